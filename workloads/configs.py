@@ -1,0 +1,327 @@
+"""Seeded synthetic workloads for the CSA hot path, in the byte layouts the C ABI consumes.
+
+Every array is drawn from ``numpy.random.Generator(PCG64)`` seeded through ``SeedSequence``; large
+arrays are drawn in fixed-size chunks, each with its own spawned child seed, so the bytes do not
+depend on how many threads fill them.  Nothing here computes scores, selections or attention: the
+one piece of linear algebra (the planted direction of the long-context workload) builds an input,
+it does not evaluate the method.
+
+Layouts (little-endian, C order), shared with ``include/csa.h``:
+
+* ``q``            [Q][H][512]   bf16 bits (uint16) or float32
+* ``sink``         [H]           float32
+* ``qI``           [Q][HI][128]  fp8 e4m3fn codes (uint8) or float32;  ``qI_scale`` [Q][HI][4] E8M0
+* ``w``            [Q][HI]       float32 (already carries softmax_scale * HI**-0.5)
+* ``ik_keys``      [P][64][128]  fp8 codes or float32;  ``ik_scales`` [P][4][64] E8M0 (block-major)
+* ``kv_pool``      [P][64][row_bytes]  KV rows (see workloads.codec)
+* ``win_rows``     [B][Wr][row_bytes]  window source (a 128-slot ring at decode, raw rows at prefill)
+* ``page_table``   [B][max_pages] int32, -1 for unused entries; entry c of request b lives in page
+                   ``page_table[b][c >> 6]``, slot ``c & 63``
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+from . import codec
+
+PAGE = 64
+DI = 128
+WINDOW = 128
+TOPK = 512
+COMPRESS = 4
+
+DT_F32, DT_BF16, DT_FP8 = 0, 1, 2
+KV_F32, KV_BF16, KV_FP8 = codec.KV_F32, codec.KV_BF16, codec.KV_FP8
+
+_CHUNK = 1 << 20  # values per independently seeded chunk
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _normal_rows(ss: np.random.SeedSequence, n_rows: int, dim: int, transform, out: np.ndarray):
+    """Fill ``out[i] = transform(N(0,1) rows)`` chunk by chunk with spawned seeds (thread-parallel)."""
+    rows_per_chunk = max(1, _CHUNK // dim)
+    n_chunks = (n_rows + rows_per_chunk - 1) // rows_per_chunk
+    if n_chunks == 0:
+        return out
+    kids = ss.spawn(n_chunks)
+
+    def work(i):
+        lo = i * rows_per_chunk
+        hi = min(n_rows, lo + rows_per_chunk)
+        g = np.random.Generator(np.random.PCG64(kids[i]))
+        x = g.standard_normal((hi - lo, dim), dtype=np.float32)
+        out[lo:hi] = transform(x, lo, hi)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(n_chunks)))
+    return out
+
+
+@dataclass
+class Workload:
+    name: str
+    kind: str                 # "decode" or "prefill"
+    B: int
+    Q: int
+    H: int
+    HI: int
+    q_dt: int
+    out_dt: int
+    idx_dt: int
+    kv_fmt: int
+    win_fmt: int
+    q: np.ndarray
+    sink: np.ndarray
+    qI: np.ndarray
+    qI_scale: np.ndarray | None
+    w: np.ndarray
+    ik_keys: np.ndarray
+    ik_scales: np.ndarray | None
+    kv_pool: np.ndarray
+    win_rows: np.ndarray
+    page_table: np.ndarray
+    q_req: np.ndarray
+    n_vis: np.ndarray
+    ctx_len: np.ndarray | None = None      # decode: raw context length per request (incl. current)
+    positions: np.ndarray | None = None    # prefill: raw position of each query
+    topk: int = TOPK
+    window: int = WINDOW
+    softmax_scale: float = 1.0 / math.sqrt(512.0)
+    planted: list = field(default_factory=list)   # long-context workload: planted entries per request
+    notes: str = ""
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.kv_pool.shape[0])
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.page_table.shape[1])
+
+    @property
+    def win_rows_per_req(self) -> int:
+        return int(self.win_rows.shape[1])
+
+    @property
+    def max_n_vis(self) -> int:
+        return int(self.n_vis.max()) if self.n_vis.size else 0
+
+    @property
+    def row_bytes(self) -> int:
+        return codec.ROW_BYTES[self.kv_fmt]
+
+
+def _encode_q(x: np.ndarray, dt: int) -> np.ndarray:
+    return x.astype(np.float32) if dt == DT_F32 else codec.bf16_encode(x)
+
+
+def _page_table(rng: np.random.Generator, n_entries: list[int]):
+    pages = [max(1, -(-n // PAGE)) for n in n_entries]
+    total = int(sum(pages))
+    perm = rng.permutation(total).astype(np.int32)
+    maxp = max(pages) if pages else 1
+    pt = np.full((len(n_entries), maxp), -1, dtype=np.int32)
+    off = 0
+    for b, p in enumerate(pages):
+        pt[b, :p] = perm[off:off + p]
+        off += p
+    return pt, total
+
+
+def _indexer_pool(ss, total_pages: int, idx_dt: int, override=None):
+    """Indexer keys [P][64][128] and E8M0 scales [P][4][64] (block-major within a page)."""
+    n = total_pages * PAGE
+    if idx_dt == DT_F32:
+        keys = np.empty((n, DI), dtype=np.float32)
+        _normal_rows(ss, n, DI, lambda x, lo, hi: x, keys)
+        if override is not None:
+            override(keys, None)
+        return keys.reshape(total_pages, PAGE, DI), None
+    codes = np.empty((n, DI), dtype=np.uint8)
+    scales = np.empty((n, DI // 32), dtype=np.uint8)
+
+    def tf(x, lo, hi):
+        c, e = codec.quantize_fp8_e8m0_blocks(x, 32)
+        scales[lo:hi] = e
+        return c
+
+    _normal_rows(ss, n, DI, tf, codes)
+    if override is not None:
+        override(codes, scales)
+    sc = scales.reshape(total_pages, PAGE, 4).transpose(0, 2, 1).copy()   # [P][4][64]
+    return codes.reshape(total_pages, PAGE, DI), sc
+
+
+def _kv_rows(ss, n_rows: int, fmt: int) -> np.ndarray:
+    out = np.empty((n_rows, codec.ROW_BYTES[fmt]), dtype=np.uint8)
+    _normal_rows(ss, n_rows, 512, lambda x, lo, hi: codec.pack_kv_rows(x, fmt), out)
+    return out
+
+
+def _indexer_queries(g: np.random.Generator, Q: int, HI: int, idx_dt: int):
+    x = g.standard_normal((Q, HI, DI), dtype=np.float32)
+    if idx_dt == DT_F32:
+        return x, x, None
+    codes, e = codec.quantize_fp8_e8m0_blocks(x, 32)
+    return x, codes, e
+
+
+def make_decode(name: str, ctx_len, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_BF16,
+                idx_dt=DT_FP8, kv_fmt=KV_FP8, win_fmt=None, seed: int = 0,
+                planted_frac: float = 0.0, topk: int = TOPK) -> Workload:
+    """One query per request at the end of a context of ``ctx_len[b]`` raw tokens.
+
+    Sub-streams, spawned in this order: page permutation, q, sink, indexer q, w, indexer key pool,
+    KV pool, window ring, planted entries.
+    """
+    win_fmt = kv_fmt if win_fmt is None else win_fmt
+    ctx_len = np.asarray(ctx_len, dtype=np.int32)
+    B = int(ctx_len.shape[0])
+    n_c = [int(t) // COMPRESS for t in ctx_len]
+    ss = np.random.SeedSequence(seed).spawn(9)
+    g = [np.random.Generator(np.random.PCG64(s)) for s in ss]
+
+    page_table, total_pages = _page_table(g[0], n_c)
+    q_f = g[1].standard_normal((B, H, 512), dtype=np.float32)
+    sink = g[2].standard_normal(H, dtype=np.float32)
+    qI_f, qI, qI_s = _indexer_queries(g[3], B, HI, idx_dt)
+    w = (g[4].standard_normal((B, HI), dtype=np.float32) * np.float32(DI ** -0.5 * HI ** -0.5)).astype(np.float32)
+
+    planted = []
+    key_override = None
+    if planted_frac > 0:
+        pg = g[8]
+        for b in range(B):
+            n_plant = int(round(planted_frac * n_c[b]))
+            planted.append(np.sort(pg.choice(n_c[b], size=n_plant, replace=False)).astype(np.int64))
+
+        def key_override(codes, scales):
+            # planted indexer key = alpha * u_b + 0.25 * N(0, I), where u_b is the unit vector whose
+            # dot product with each head's indexer query has the sign of that head's weight.
+            for b in range(B):
+                Qb = qI_f[b].astype(np.float64)                     # [HI,128]
+                s = np.sign(w[b]).astype(np.float64)
+                s[s == 0] = 1.0
+                u = Qb.T @ np.linalg.solve(Qb @ Qb.T, s)
+                u /= np.linalg.norm(u)
+                n = planted[b]
+                noise = pg.standard_normal((n.size, DI)).astype(np.float32)
+                kv = (3.0 * math.sqrt(DI) * u[None, :] + 0.25 * noise).astype(np.float32)
+                rows = page_table[b, n // PAGE].astype(np.int64) * PAGE + (n % PAGE)
+                if scales is None:
+                    codes[rows] = kv
+                else:
+                    c, e = codec.quantize_fp8_e8m0_blocks(kv, 32)
+                    codes[rows] = c
+                    scales[rows] = e
+
+    ik_keys, ik_scales = _indexer_pool(ss[5], total_pages, idx_dt, key_override)
+    kv_pool = _kv_rows(ss[6], total_pages * PAGE, kv_fmt)
+    if planted_frac > 0:
+        for b in range(B):
+            n = planted[b]
+            d = q_f[b].astype(np.float64).sum(axis=0)
+            d /= np.linalg.norm(d)
+            x = (2.0 * math.sqrt(512) * d[None, :] + g[8].standard_normal((n.size, 512))).astype(np.float32)
+            rows = page_table[b, n // PAGE].astype(np.int64) * PAGE + (n % PAGE)
+            kv_pool[rows] = codec.pack_kv_rows(x, kv_fmt)
+    kv_pool = kv_pool.reshape(total_pages, PAGE, -1)
+    win = _kv_rows(ss[7], B * WINDOW, win_fmt).reshape(B, WINDOW, -1)
+
+    return Workload(
+        name=name, kind="decode", B=B, Q=B, H=H, HI=HI, q_dt=q_dt, out_dt=out_dt, idx_dt=idx_dt,
+        kv_fmt=kv_fmt, win_fmt=win_fmt, q=_encode_q(q_f, q_dt), sink=sink, qI=qI, qI_scale=qI_s,
+        w=w, ik_keys=ik_keys, ik_scales=ik_scales, kv_pool=kv_pool, win_rows=win,
+        page_table=page_table, q_req=np.arange(B, dtype=np.int32),
+        n_vis=np.asarray(n_c, dtype=np.int32), ctx_len=ctx_len, topk=topk, planted=planted)
+
+
+def make_prefill(name: str, T: int, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_BF16,
+                 idx_dt=DT_FP8, kv_fmt=KV_BF16, seed: int = 0, q_start: int = 0,
+                 q_count: int | None = None, topk: int = TOPK) -> Workload:
+    """Causal prefill of one request with ``T`` raw tokens; queries are positions
+    ``q_start .. q_start+q_count-1``.  Query t sees compressed entries ``c < (t+1)//4`` and the raw
+    window ``[t-127, t]``.
+
+    Sub-streams, spawned in this order: page permutation, q, sink, indexer q, w, indexer key pool,
+    compressed KV pool, raw KV rows.
+    """
+    q_count = T - q_start if q_count is None else q_count
+    n_c = T // COMPRESS
+    ss = np.random.SeedSequence(seed).spawn(8)
+    g = [np.random.Generator(np.random.PCG64(s)) for s in ss]
+    page_table, total_pages = _page_table(g[0], [n_c])
+    Q = q_count
+    q = np.empty((Q, H * 512), dtype=np.float32 if q_dt == DT_F32 else np.uint16)
+    _normal_rows(ss[1], Q, H * 512, lambda x, lo, hi: _encode_q(x, q_dt), q)
+    q = q.reshape(Q, H, 512)
+    sink = g[2].standard_normal(H, dtype=np.float32)
+    _, qI, qI_s = _indexer_queries(g[3], Q, HI, idx_dt)
+    w = (g[4].standard_normal((Q, HI), dtype=np.float32) * np.float32(DI ** -0.5 * HI ** -0.5)).astype(np.float32)
+    ik_keys, ik_scales = _indexer_pool(ss[5], total_pages, idx_dt)
+    kv_pool = _kv_rows(ss[6], total_pages * PAGE, kv_fmt).reshape(total_pages, PAGE, -1)
+    raw = _kv_rows(ss[7], T, kv_fmt).reshape(1, T, -1)
+    pos = np.arange(q_start, q_start + Q, dtype=np.int32)
+    return Workload(
+        name=name, kind="prefill", B=1, Q=Q, H=H, HI=HI, q_dt=q_dt, out_dt=out_dt, idx_dt=idx_dt,
+        kv_fmt=kv_fmt, win_fmt=kv_fmt, q=q, sink=sink, qI=qI, qI_scale=qI_s, w=w,
+        ik_keys=ik_keys, ik_scales=ik_scales, kv_pool=kv_pool, win_rows=raw,
+        page_table=page_table, q_req=np.zeros(Q, dtype=np.int32),
+        n_vis=((pos + 1) // COMPRESS).astype(np.int32), positions=pos, topk=topk)
+
+
+# ------------------------------------------------------------------------------------------------
+# The five named workloads.  Sizes default to the full configurations; the parity tests pass
+# smaller sizes of the same recipe.
+# ------------------------------------------------------------------------------------------------
+
+def tiny_decode(seed: int = 0) -> Workload:
+    """B=1, T=4096 (1024 compressed entries, 128-token window), H=16, HI=16, everything fp32."""
+    return make_decode("tiny_decode", [4096], H=16, HI=16, q_dt=DT_F32, out_dt=DT_F32,
+                       idx_dt=DT_F32, kv_fmt=KV_F32, seed=seed)
+
+
+def batched_decode(seed: int = 0, B: int = 32, T: int = 65536, H: int = 64, HI: int = 64) -> Workload:
+    """B=32 requests at T=65536 (16384 compressed entries in 256 pages of 64), FP8-nope/BF16-rope
+    KV with per-64 fp32 scales, FP8 indexer with E8M0 per-32 scales, bf16 q, H=HI=64."""
+    return make_decode("batched_decode", [T] * B, H=H, HI=HI, seed=seed)
+
+
+def long_decode(seed: int = 0, B: int = 8, T: int = 1 << 20, H: int = 64, HI: int = 64) -> Workload:
+    """B=8 requests at T=1,048,576 (262,144 compressed entries), formats as batched_decode, with 1%
+    planted high-similarity entries per request."""
+    return make_decode("long_decode", [T] * B, H=H, HI=HI, seed=seed, planted_frac=0.01)
+
+
+def causal_prefill(seed: int = 0, T: int = 8192, H: int = 64, HI: int = 64, q_start: int = 0,
+                   q_count: int | None = None) -> Workload:
+    """One request, T=8192 query positions, bf16 q and KV rows, FP8 indexer."""
+    return make_prefill("causal_prefill", T, H=H, HI=HI, seed=seed, q_start=q_start, q_count=q_count)
+
+
+RAGGED_EMPTY_ROWS = (3, 17, 42, 63)
+
+
+def ragged_lengths(seed: int = 0, B: int = 64, empty=RAGGED_EMPTY_ROWS, lo: int = 512,
+                   hi: int = 131072) -> np.ndarray:
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed).spawn(10)[9]))
+    T = np.clip(np.round(np.exp(g.normal(math.log(8192.0), 1.2, size=B))), lo, hi).astype(np.int32)
+    for r in empty:
+        if r < B:
+            T[r] = 0
+    return T
+
+
+def ragged_decode(seed: int = 0, B: int = 64, H: int = 8, HI: int = 64, hi: int = 131072) -> Workload:
+    """B=64 lognormal contexts in [512, 131072] (rows 3, 17, 42, 63 empty), H=8 (padded to 16
+    inside the kernels), bf16 q and KV rows, FP8 indexer."""
+    T = ragged_lengths(seed, B, hi=hi)
+    return make_decode("ragged_decode", T, H=H, HI=HI, kv_fmt=KV_BF16, seed=seed)
