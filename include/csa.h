@@ -1,0 +1,221 @@
+/*
+ * csa.h - C ABI of the compressed-sparse-attention (CSA) hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The path computes, for each query token:
+ *   (1) indexer scores of every visible 4:1-compressed entry,
+ *         s[c] = sum_h w[h] * max(0, qI[h] . kI[c])
+ *       with FP8 E4M3FN indexer queries/keys carrying one E8M0 scale per 32 elements;
+ *   (2) the indices of the top-k scores (k = 512 in the model);
+ *   (3) sparse multi-query attention over [sliding-window rows ++ selected compressed rows]:
+ *         out[h] = sum_j e^{S[h,j]} v_j / (sum_j e^{S[h,j]} + e^{sink[h]}),  S = scale * q[h] . v_j
+ *       where K and V are the same single-head 512-dim rows and invalid index slots are skipped.
+ *
+ * Sources (pages as titled; the section is named on each declaration):
+ *   [P1] "DeepSeek-V4 全面解读：架构设计与 inference/encoding 源码深度解析" (wangjunjian.com)
+ *   [P2] "DeepSeek-V4 in SGLang 深度理解分析" (kenforever1.github.io)
+ *   [P3] "tilelang量化内核拆解DeepSeek-V4.1-Flash-NVFP4的fp4_gemm与sparse_attn实现" (wzjinhao.cn)
+ *
+ * Conventions shared by every entry point
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library never allocates,
+ *     frees or retains them; work is enqueued on `stream` and nothing is synchronised.  Keep the
+ *     buffers alive until the stream work has completed.
+ *   - Scratch memory ("ws") is caller-provided and sized by the matching *_workspace_bytes query.
+ *     Its contents on entry do not matter; the entry point initialises what it uses.
+ *   - Arguments are validated on the host before anything is launched; on error nothing is written
+ *     and nothing is enqueued.  Device-resident *values* (indices, page ids, lengths, request ids)
+ *     are data: out-of-range values are masked exactly like the -1 slot, never dereferenced.
+ *   - Every device pointer must be 16-byte aligned (CSA_ERR_ALIGN otherwise).
+ *   - Layouts are C order.  D = 512 (448 "nope" dims then 64 "rope" dims, rope last as in [P1]
+ *     section 2.11 step 8), DI = 128 indexer dims, a page holds 64 consecutive compressed entries.
+ *   - Calls on different streams may run concurrently; calls that share a workspace must not.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_NULL = -1,        /* a required pointer is NULL                                      */
+  CSA_ERR_SHAPE = -2,       /* a size is out of its documented range                            */
+  CSA_ERR_DTYPE = -3,       /* unknown or unsupported dtype / format code                       */
+  CSA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                                 */
+  CSA_ERR_WORKSPACE = -5,   /* ws is NULL or smaller than the *_workspace_bytes query            */
+  CSA_ERR_UNSUPPORTED = -6, /* a valid combination this build does not implement                */
+  CSA_ERR_HIP = -7          /* a HIP launch failed; csa_last_hip_error() holds the hipError_t   */
+} csa_status;
+
+/* Element types of q, out and the indexer operands. */
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3FN = 2 } csa_dtype;
+
+/* KV row formats (one 512-dim row each).
+ *   CSA_KV_F32               2048 B: 512 x fp32
+ *   CSA_KV_BF16              1024 B: 512 x bf16
+ *   CSA_KV_FP8NOPE_BF16ROPE   608 B: [0,448) e4m3fn nope | [448,576) 64 x bf16 rope |
+ *                                   [576,604) 7 x fp32 scale, one per 64 nope dims | [604,608) pad
+ *     value of nope dim i = fp8(byte i) * scale[i / 64]            ([P2] concept 5)          */
+typedef enum { CSA_KV_F32 = 0, CSA_KV_BF16 = 1, CSA_KV_FP8NOPE_BF16ROPE = 2 } csa_kv_format;
+
+/* Paged compressed KV pool.  Entry c of request r lives in row
+ *   page_table[r * max_pages + (c >> 6)] * 64 + (c & 63)   of `rows` ([num_pages][64][row bytes]).
+ * A page id outside [0, num_pages) masks the entry.                                          */
+typedef struct {
+  const void* rows;
+  int32_t fmt;              /* csa_kv_format */
+  int32_t num_pages;
+  const int32_t* page_table;/* [n_req][max_pages] */
+  int32_t max_pages;
+  int32_t reserved;
+} csa_paged_kv;
+
+/* Paged indexer key cache (same page mapping as csa_paged_kv).
+ *   dt = CSA_FP8_E4M3FN: keys [num_pages][64][128] e4m3fn bytes; scales [num_pages][4][64] E8M0
+ *        bytes, scales[p][b][s] scaling dims [32b, 32b+32) of slot s (value 2^(e-127)).
+ *   dt = CSA_F32: keys [num_pages][64][128] fp32; scales must be NULL.                          */
+typedef struct {
+  const void* keys;
+  const uint8_t* scales;
+  int32_t dt;               /* csa_dtype: CSA_FP8_E4M3FN or CSA_F32 */
+  int32_t num_pages;
+  const int32_t* page_table;/* [n_req][max_pages] */
+  int32_t max_pages;
+  int32_t reserved;
+} csa_paged_idx;
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_indexer_logits - indexer scores ([P1] section 2.10 forward steps 5-8; [P2] concept 3 and
+ * algorithm 2, the FP8 "paged MQA logits" pass).
+ *
+ *   qI        [Q][HI][128] e4m3fn bytes (qI_dt = CSA_FP8_E4M3FN) or fp32 (CSA_F32)
+ *   qI_scale  [Q][HI][4] E8M0 bytes, one per 32 dims (NULL for CSA_F32)
+ *   w         [Q][HI] fp32 head weights (the caller folds softmax_scale * HI^-0.5 into them)
+ *   keys      paged indexer keys; the key dtype must equal qI_dt
+ *   q_req     [Q] request id of each query (row of the page table), n_req requests
+ *   n_vis     [Q] visible compressed entries of each query (decode: T/4; causal prefill at raw
+ *             position t: (t+1)/4).  Clamped to [0, min(max_n_vis, 64*max_pages)].
+ *   logits    [Q][ld] fp32 out: s[c] for c < n_vis[q], -INFINITY for n_vis[q] <= c < max_n_vis;
+ *             columns >= max_n_vis are not written.
+ * Ranges: 1 <= Q, 1 <= HI <= 64, 0 <= max_n_vis <= ld, n_req >= 1.
+ * ------------------------------------------------------------------------------------------- */
+csa_status csa_indexer_logits(const void* qI, const uint8_t* qI_scale, int32_t qI_dt,
+                              const float* w, const csa_paged_idx* keys,
+                              const int32_t* q_req, int32_t n_req, const int32_t* n_vis,
+                              int32_t Q, int32_t HI, int64_t max_n_vis,
+                              float* logits, int64_t ld, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_topk - per-query top-k selection over the visible prefix of each logits row ([P1] section
+ * 2.10 steps 9-10 with the visibility mask applied first; [P2] concept 3, top-512).
+ *
+ *   logits    [Q][ld] fp32; only columns c < n_vis[q] (clamped to [0, max_n_vis]) are candidates
+ *   idx       [Q][ld_idx] int32 out, first k columns written:
+ *               n_vis <= k : 0, 1, ..., n_vis-1, then -1 padding;
+ *               n_vis  > k : the k candidates with the largest scores, equal scores ordered by
+ *                            ascending index, written in ascending index order.
+ *             NaN scores rank below -INFINITY; -0.0 equals +0.0.
+ *   ws        >= csa_topk_workspace_bytes(Q, max_n_vis, k) bytes
+ * Ranges: 1 <= Q, 1 <= k <= 2048, 0 <= max_n_vis <= ld, ld_idx >= k.
+ * ------------------------------------------------------------------------------------------- */
+size_t csa_topk_workspace_bytes(int32_t Q, int64_t max_n_vis, int32_t k);
+csa_status csa_topk(const float* logits, int64_t ld, const int32_t* n_vis, int32_t Q,
+                    int64_t max_n_vis, int32_t k, int32_t* idx, int64_t ld_idx,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_sparse_attn - index-gathered multi-query attention with a per-head sink ([P1] section 3.7,
+ * sparse_attn_kernel: gather by index, online softmax, sink added to the denominator after the
+ * loop; [P3] sparse_attn section: running max starts at -1e30 so an all-invalid row gives 0).
+ *
+ *   q         [Q][H][512], q_dt CSA_BF16 (BF16 matrix-core path, fp32 accumulation) or CSA_F32
+ *             (fp32 path)
+ *   sink      [H] fp32 (not multiplied by softmax_scale)
+ *   win_rows  [n_req][win_rows_per_req][row bytes of win_fmt]: the window source (a 128-slot ring
+ *             at decode, the raw rows of the request at prefill); may be NULL when n_win == 0
+ *   comp      the paged compressed KV (may be NULL when n_comp == 0)
+ *   q_req     [Q] request id of each query
+ *   idx       [Q][ld_idx] int32: columns [0, n_win) index the window source of the query's request,
+ *             columns [n_win, n_win+n_comp) index compressed entries.  Negative or out-of-range
+ *             values (and unmapped pages) are invalid slots.  Duplicates count once per slot.
+ *   out       [Q][H][512], out_dt CSA_BF16 or CSA_F32; a query with no valid slot gets exact 0.
+ *   ws        >= csa_sparse_attn_workspace_bytes(Q, H, n_win + n_comp) bytes (split-K partials)
+ * Ranges: 1 <= Q, 1 <= H <= 128, 0 <= n_win, 0 <= n_comp, 1 <= n_win + n_comp <= 4096,
+ *         ld_idx >= n_win + n_comp, softmax_scale finite.
+ * ------------------------------------------------------------------------------------------- */
+size_t csa_sparse_attn_workspace_bytes(int32_t Q, int32_t H, int32_t n_idx);
+csa_status csa_sparse_attn(const void* q, int32_t q_dt, int32_t Q, int32_t H, const float* sink,
+                           const void* win_rows, int32_t win_fmt, int64_t win_rows_per_req,
+                           const csa_paged_kv* comp, const int32_t* q_req, int32_t n_req,
+                           const int32_t* idx, int64_t ld_idx, int32_t n_win, int32_t n_comp,
+                           float softmax_scale, void* out, int32_t out_dt,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_decode - one decode step of B requests (one query each) through the whole path: indexer
+ * scores -> top-k -> [window ++ top-k] -> sparse attention ([P1] section 2.11 forward steps 3-7).
+ *
+ *   ctx_len   [B] raw context length T_b including the current token (device).  The query sees
+ *             n_vis = T_b / 4 compressed entries and the last min(T_b, 128) raw tokens, which live
+ *             in ring slots (position % 128) of win_ring ([P1] section 2.8, decode ring buffer).
+ *   max_ctx   host-side upper bound of ctx_len (sizes the workspace); larger values are clamped.
+ *   win_ring  [B][128][row bytes of win_fmt]
+ *   idx_out   optional [B][128 + k] int32: the index list attended ([window slots ++ top-k]);
+ *             NULL to keep it in the workspace only.
+ *   Other arguments as in the primitives above (q_req is the identity).
+ * Ranges: 1 <= B, 1 <= H <= 128, 1 <= HI <= 64, 1 <= k <= 2048, 0 <= max_ctx <= 2^31-1.
+ * ------------------------------------------------------------------------------------------- */
+size_t csa_decode_workspace_bytes(int32_t B, int32_t H, int32_t HI, int64_t max_ctx, int32_t k);
+csa_status csa_decode(int32_t B, int32_t H, int32_t HI, int32_t k,
+                      const void* q, int32_t q_dt, const float* sink,
+                      const void* qI, const uint8_t* qI_scale, int32_t qI_dt, const float* w,
+                      const csa_paged_idx* keys, const csa_paged_kv* comp,
+                      const void* win_ring, int32_t win_fmt,
+                      const int32_t* ctx_len, int64_t max_ctx,
+                      float softmax_scale, void* out, int32_t out_dt, int32_t* idx_out,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_prefill - causal prefill of one request: Q queries at raw positions pos0 .. pos0+Q-1.
+ * Query t sees compressed entries c < (t+1)/4 and raw rows [t-127, t] of raw_rows ([P1] section
+ * 2.8, causal window at prefill; section 2.10 causal mask).  Page tables have one row.
+ *
+ *   raw_rows  [T][row bytes of raw_fmt], the request's raw KV rows (window source)
+ *   idx_out   optional [Q][128 + k] int32 as in csa_decode
+ * Ranges: 1 <= Q, 0 <= pos0, pos0 + Q <= T, 1 <= H <= 128, 1 <= HI <= 64, 1 <= k <= 2048.
+ * ------------------------------------------------------------------------------------------- */
+size_t csa_prefill_workspace_bytes(int32_t Q, int32_t H, int32_t HI, int64_t T, int32_t k);
+csa_status csa_prefill(int32_t Q, int32_t H, int32_t HI, int32_t k,
+                       const void* q, int32_t q_dt, const float* sink,
+                       const void* qI, const uint8_t* qI_scale, int32_t qI_dt, const float* w,
+                       const csa_paged_idx* keys, const csa_paged_kv* comp,
+                       const void* raw_rows, int32_t raw_fmt, int64_t T, int64_t pos0,
+                       float softmax_scale, void* out, int32_t out_dt, int32_t* idx_out,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Diagnostics.
+ *   csa_status_string   static text of a status code.
+ *   csa_last_hip_error  hipError_t of the last CSA_ERR_HIP on the calling thread (0 if none).
+ *   csa_profile_enable  on != 0: every kernel the entry points launch is bracketed by a pair of
+ *                       hipEvents recorded on the caller's stream (adds no synchronisation).
+ *   csa_profile_collect synchronises the recorded events and returns, for the kernel named
+ *                       `kernel` (e.g. "indexer_fp8"), the summed duration in ms and the number
+ *                       of launches since the last reset; unknown names return 0 launches.
+ *   csa_profile_reset   forgets all recorded events.
+ * Profiling state is process-wide and not thread-safe; enable it only from one host thread.
+ * ------------------------------------------------------------------------------------------- */
+const char* csa_status_string(int32_t status);
+int32_t csa_last_hip_error(void);
+csa_status csa_profile_enable(int32_t on);
+csa_status csa_profile_collect(const char* kernel, double* total_ms, int64_t* launches);
+csa_status csa_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */

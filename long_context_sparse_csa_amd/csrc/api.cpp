@@ -1,0 +1,419 @@
+// C ABI of the CSA hot path: argument validation, workspace layout and launch sequencing.
+// Every check runs on the host before anything is enqueued; kernels never see an argument that
+// could send them out of bounds (device-resident values are masked inside the kernels).
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/csa.h"
+#include "csa_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip = 0;
+
+struct ProfRec {
+  std::string name;
+  hipEvent_t start, stop;
+};
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+
+constexpr int kWin = 128;
+constexpr int kHistBins = 4096;
+constexpr int64_t kMaxEntries = (int64_t)1 << 30;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+bool kv_fmt_ok(int f) { return f == CSA_KV_F32 || f == CSA_KV_BF16 || f == CSA_KV_FP8NOPE_BF16ROPE; }
+
+csa_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return CSA_OK;
+  g_last_hip = (int32_t)e;
+  return CSA_ERR_HIP;
+}
+
+// ---- workspace carving ------------------------------------------------------------------------
+struct Carver {
+  uint8_t* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base((uint8_t*)b) {}
+  template <class T>
+  T* take(size_t bytes) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += align256(bytes);
+    return p;
+  }
+};
+
+struct TopkWs {
+  uint32_t* hist;
+  uint32_t* counters;
+  int32_t* sel;
+  uint2* cand;
+};
+
+TopkWs carve_topk(Carver& c, int32_t Q, int64_t max_n_vis, int32_t k) {
+  TopkWs w;
+  w.hist = c.take<uint32_t>((size_t)Q * kHistBins * 4);
+  w.counters = c.take<uint32_t>((size_t)Q * 4 * 4);
+  w.sel = c.take<int32_t>((size_t)Q * k * 4);
+  w.cand = c.take<uint2>((size_t)Q * (size_t)(max_n_vis > 0 ? max_n_vis : 1) * 8);
+  return w;
+}
+
+int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
+
+struct PathWs {
+  int32_t* n_vis;
+  int32_t* q_req;
+  int32_t* idx;
+  float* logits;
+  int64_t ld;
+  TopkWs tk;
+  float* part;
+};
+
+PathWs carve_path(Carver& c, int32_t rows, int32_t H, int64_t max_n_vis, int32_t k) {
+  PathWs w;
+  w.n_vis = c.take<int32_t>((size_t)rows * 4);
+  w.q_req = c.take<int32_t>((size_t)rows * 4);
+  w.idx = c.take<int32_t>((size_t)rows * (kWin + k) * 4);
+  w.ld = round64(max_n_vis > 0 ? max_n_vis : 1);
+  w.logits = c.take<float>((size_t)rows * (size_t)w.ld * 4);
+  w.tk = carve_topk(c, rows, max_n_vis, k);
+  w.part = c.take<float>(csa::attn_partial_bytes(rows, H, kWin + k));
+  return w;
+}
+
+csa_status check_idx_struct(const csa_paged_idx* k, int32_t dt) {
+  if (!k || !k->keys || !k->page_table) return CSA_ERR_NULL;
+  if (k->dt != dt) return CSA_ERR_DTYPE;
+  if (dt == CSA_FP8_E4M3FN && !k->scales) return CSA_ERR_NULL;
+  if (dt == CSA_F32 && k->scales) return CSA_ERR_DTYPE;
+  if (k->num_pages < 1 || k->max_pages < 1) return CSA_ERR_SHAPE;
+  if (!aligned(k->keys, 16) || !aligned(k->page_table, 4) || (k->scales && !aligned(k->scales, 4))) return CSA_ERR_ALIGN;
+  return CSA_OK;
+}
+
+csa_status check_kv_struct(const csa_paged_kv* c) {
+  if (!c || !c->rows || !c->page_table) return CSA_ERR_NULL;
+  if (!kv_fmt_ok(c->fmt)) return CSA_ERR_DTYPE;
+  if (c->num_pages < 1 || c->max_pages < 1) return CSA_ERR_SHAPE;
+  if (!aligned(c->rows, 16) || !aligned(c->page_table, 4)) return CSA_ERR_ALIGN;
+  return CSA_OK;
+}
+
+csa_status check_indexer_inputs(const void* qI, const uint8_t* qI_scale, int32_t qI_dt, const float* w, int32_t HI) {
+  if (!qI || !w) return CSA_ERR_NULL;
+  if (qI_dt != CSA_F32 && qI_dt != CSA_FP8_E4M3FN) return CSA_ERR_DTYPE;
+  if (qI_dt == CSA_FP8_E4M3FN && !qI_scale) return CSA_ERR_NULL;
+  if (HI < 1 || HI > 64) return CSA_ERR_SHAPE;
+  if (!aligned(qI, 16) || !aligned(w, 4)) return CSA_ERR_ALIGN;
+  return CSA_OK;
+}
+
+csa_status check_attn_common(const void* q, int32_t q_dt, int32_t H, const float* sink, const void* out,
+                             int32_t out_dt, float scale) {
+  if (!q || !sink || !out) return CSA_ERR_NULL;
+  if ((q_dt != CSA_F32 && q_dt != CSA_BF16) || (out_dt != CSA_F32 && out_dt != CSA_BF16)) return CSA_ERR_DTYPE;
+  if (H < 1 || H > 128) return CSA_ERR_SHAPE;
+  if (!std::isfinite(scale)) return CSA_ERR_SHAPE;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(sink, 4)) return CSA_ERR_ALIGN;
+  return CSA_OK;
+}
+
+#define CSA_TRY(x)                      \
+  do {                                  \
+    csa_status _s = (x);                \
+    if (_s != CSA_OK) return _s;        \
+  } while (0)
+
+#define CSA_HIP(x)                      \
+  do {                                  \
+    hipError_t _e = (x);                \
+    if (_e != hipSuccess) return hip_status(_e); \
+  } while (0)
+
+}  // namespace
+
+namespace csa {
+
+ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
+  if (!g_prof_on) return;
+  ProfRec r;
+  r.name = name;
+  if (hipEventCreate(&r.start) != hipSuccess) return;
+  if (hipEventCreate(&r.stop) != hipSuccess) {
+    (void)hipEventDestroy(r.start);
+    return;
+  }
+  (void)hipEventRecord(r.start, s);
+  g_prof.push_back(r);
+  slot = (int)g_prof.size() - 1;
+}
+
+ProfScope::~ProfScope() {
+  if (slot >= 0) (void)hipEventRecord(g_prof[slot].stop, stream);
+}
+
+}  // namespace csa
+
+extern "C" {
+
+const char* csa_status_string(int32_t s) {
+  switch (s) {
+    case CSA_OK: return "ok";
+    case CSA_ERR_NULL: return "required pointer is NULL";
+    case CSA_ERR_SHAPE: return "size out of range";
+    case CSA_ERR_DTYPE: return "unknown or unsupported dtype/format";
+    case CSA_ERR_ALIGN: return "pointer not aligned";
+    case CSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case CSA_ERR_UNSUPPORTED: return "unsupported combination";
+    case CSA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t csa_last_hip_error(void) { return g_last_hip; }
+
+csa_status csa_profile_enable(int32_t on) {
+  g_prof_on = on != 0;
+  return CSA_OK;
+}
+
+csa_status csa_profile_reset(void) {
+  for (auto& r : g_prof) {
+    (void)hipEventSynchronize(r.stop);
+    (void)hipEventDestroy(r.start);
+    (void)hipEventDestroy(r.stop);
+  }
+  g_prof.clear();
+  return CSA_OK;
+}
+
+csa_status csa_profile_collect(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel || !total_ms || !launches) return CSA_ERR_NULL;
+  double tot = 0.0;
+  int64_t n = 0;
+  for (auto& r : g_prof) {
+    if (r.name != kernel) continue;
+    hipError_t e = hipEventSynchronize(r.stop);
+    if (e != hipSuccess) return hip_status(e);
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.start, r.stop);
+    if (e != hipSuccess) return hip_status(e);
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return CSA_OK;
+}
+
+// ------------------------------------------------------------------------------------------------
+csa_status csa_indexer_logits(const void* qI, const uint8_t* qI_scale, int32_t qI_dt, const float* w,
+                              const csa_paged_idx* keys, const int32_t* q_req, int32_t n_req,
+                              const int32_t* n_vis, int32_t Q, int32_t HI, int64_t max_n_vis,
+                              float* logits, int64_t ld, hipStream_t stream) {
+  CSA_TRY(check_indexer_inputs(qI, qI_scale, qI_dt, w, HI));
+  CSA_TRY(check_idx_struct(keys, qI_dt));
+  if (!q_req || !n_vis || !logits) return CSA_ERR_NULL;
+  if (Q < 1 || Q > 65535 || n_req < 1) return CSA_ERR_SHAPE;
+  if (max_n_vis < 0 || max_n_vis > kMaxEntries || ld < max_n_vis) return CSA_ERR_SHAPE;
+  if (!aligned(q_req, 4) || !aligned(n_vis, 4) || !aligned(logits, 4)) return CSA_ERR_ALIGN;
+  csa::IndexerArgs a{};
+  a.qI = qI; a.qI_scale = qI_scale; a.dt = qI_dt; a.w = w;
+  a.keys = keys->keys; a.kscale = keys->scales; a.num_pages = keys->num_pages;
+  a.page_table = keys->page_table; a.max_pages = keys->max_pages;
+  a.q_req = q_req; a.n_req = n_req; a.n_vis = n_vis; a.Q = Q; a.HI = HI;
+  a.max_n_vis = max_n_vis; a.logits = logits; a.ld = ld; a.hist = nullptr;
+  return hip_status(csa::launch_indexer(a, stream));
+}
+
+size_t csa_topk_workspace_bytes(int32_t Q, int64_t max_n_vis, int32_t k) {
+  if (Q < 1 || k < 1 || max_n_vis < 0) return 0;
+  Carver c(nullptr);
+  carve_topk(c, Q, max_n_vis, k);
+  return c.off;
+}
+
+csa_status csa_topk(const float* logits, int64_t ld, const int32_t* n_vis, int32_t Q, int64_t max_n_vis,
+                    int32_t k, int32_t* idx, int64_t ld_idx, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!logits || !n_vis || !idx) return CSA_ERR_NULL;
+  if (Q < 1 || Q > 65535 || k < 1 || k > 2048) return CSA_ERR_SHAPE;
+  if (max_n_vis < 0 || max_n_vis > kMaxEntries || ld < max_n_vis || ld_idx < k) return CSA_ERR_SHAPE;
+  if (!aligned(logits, 4) || !aligned(n_vis, 4) || !aligned(idx, 4)) return CSA_ERR_ALIGN;
+  const size_t need = csa_topk_workspace_bytes(Q, max_n_vis, k);
+  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return CSA_ERR_ALIGN;
+  Carver c(ws);
+  TopkWs w = carve_topk(c, Q, max_n_vis, k);
+  csa::PrepArgs p{};
+  p.zero_ptr = w.hist;
+  p.zero_words = (int64_t)((uint8_t*)w.sel - (uint8_t*)w.hist) / 4;   // hist + counters
+  p.mode = 0;
+  CSA_HIP(csa::launch_prep(p, stream));
+  csa::TopkArgs t{};
+  t.logits = logits; t.ld = ld; t.n_vis = n_vis; t.Q = Q; t.max_n_vis = max_n_vis; t.k = k;
+  t.idx = idx; t.ld_idx = ld_idx; t.hist = w.hist; t.counters = w.counters; t.sel = w.sel;
+  t.cand = w.cand; t.cand_cap = max_n_vis > 0 ? max_n_vis : 1;
+  CSA_HIP(csa::launch_topk_hist(t, stream));
+  return hip_status(csa::launch_topk_select(t, stream));
+}
+
+size_t csa_sparse_attn_workspace_bytes(int32_t Q, int32_t H, int32_t n_idx) {
+  if (Q < 1 || H < 1 || n_idx < 1) return 0;
+  return csa::attn_partial_bytes(Q, H, n_idx);
+}
+
+csa_status csa_sparse_attn(const void* q, int32_t q_dt, int32_t Q, int32_t H, const float* sink,
+                           const void* win_rows, int32_t win_fmt, int64_t win_rows_per_req,
+                           const csa_paged_kv* comp, const int32_t* q_req, int32_t n_req, const int32_t* idx,
+                           int64_t ld_idx, int32_t n_win, int32_t n_comp, float softmax_scale, void* out,
+                           int32_t out_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  CSA_TRY(check_attn_common(q, q_dt, H, sink, out, out_dt, softmax_scale));
+  if (!q_req || !idx) return CSA_ERR_NULL;
+  if (Q < 1 || Q > 65535 || n_req < 1 || n_win < 0 || n_comp < 0) return CSA_ERR_SHAPE;
+  const int32_t n_idx = n_win + n_comp;
+  if (n_idx < 1 || n_idx > 4096 || ld_idx < n_idx) return CSA_ERR_SHAPE;
+  if (n_win > 0) {
+    if (!win_rows) return CSA_ERR_NULL;
+    if (!kv_fmt_ok(win_fmt)) return CSA_ERR_DTYPE;
+    if (win_rows_per_req < 0 || win_rows_per_req > kMaxEntries) return CSA_ERR_SHAPE;
+    if (!aligned(win_rows, 16)) return CSA_ERR_ALIGN;
+  }
+  if (n_comp > 0) CSA_TRY(check_kv_struct(comp));
+  if (!aligned(q_req, 4) || !aligned(idx, 4)) return CSA_ERR_ALIGN;
+  const size_t need = csa_sparse_attn_workspace_bytes(Q, H, n_idx);
+  if (need > 0 && (!ws || ws_bytes < need)) return CSA_ERR_WORKSPACE;
+  if (need > 0 && !aligned(ws, 16)) return CSA_ERR_ALIGN;
+  csa::AttnArgs a{};
+  a.q = q; a.q_dt = q_dt; a.Q = Q; a.H = H; a.sink = sink;
+  a.win = n_win > 0 ? (const uint8_t*)win_rows : nullptr; a.win_fmt = n_win > 0 ? win_fmt : 0;
+  a.win_rows_per_req = win_rows_per_req;
+  if (n_comp > 0) {
+    a.comp = (const uint8_t*)comp->rows; a.comp_fmt = comp->fmt; a.comp_num_pages = comp->num_pages;
+    a.page_table = comp->page_table; a.max_pages = comp->max_pages;
+  }
+  a.q_req = q_req; a.n_req = n_req; a.idx = idx; a.ld_idx = ld_idx; a.n_win = n_win; a.n_comp = n_comp;
+  a.softmax_scale = softmax_scale; a.out = out; a.out_dt = out_dt;
+  a.n_split = csa::plan_attn_split(Q, H, n_idx, q_dt);
+  a.part = (float*)ws;
+  return hip_status(csa::launch_attention(a, stream));
+}
+
+// ------------------------------------------------------------------------------------------------
+static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_t k, const void* q, int32_t q_dt,
+                           const float* sink, const void* qI, const uint8_t* qI_scale, int32_t qI_dt,
+                           const float* w, const csa_paged_idx* keys, const csa_paged_kv* comp,
+                           const void* win, int32_t win_fmt, int64_t win_rows_per_req, const int32_t* ctx_len,
+                           int64_t max_ctx, int64_t pos0, int64_t max_n_vis, float softmax_scale, void* out,
+                           int32_t out_dt, int32_t* idx_out, void* ws, size_t ws_bytes, size_t need,
+                           hipStream_t stream) {
+  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return CSA_ERR_ALIGN;
+  if (idx_out && !aligned(idx_out, 4)) return CSA_ERR_ALIGN;
+  Carver c(ws);
+  PathWs pw = carve_path(c, rows, H, max_n_vis, k);
+  int32_t* idx = idx_out ? idx_out : pw.idx;
+  const int64_t ld_idx = kWin + k;
+
+  csa::PrepArgs p{};
+  p.zero_ptr = pw.tk.hist;
+  p.zero_words = (int64_t)((uint8_t*)pw.tk.sel - (uint8_t*)pw.tk.hist) / 4;
+  p.mode = mode; p.rows = rows; p.ctx_len = ctx_len; p.max_ctx = max_ctx; p.pos0 = pos0;
+  p.idx = idx; p.ld_idx = ld_idx; p.n_vis_out = pw.n_vis; p.q_req_out = pw.q_req;
+  CSA_HIP(csa::launch_prep(p, stream));
+
+  csa::IndexerArgs ia{};
+  ia.qI = qI; ia.qI_scale = qI_scale; ia.dt = qI_dt; ia.w = w;
+  ia.keys = keys->keys; ia.kscale = keys->scales; ia.num_pages = keys->num_pages;
+  ia.page_table = keys->page_table; ia.max_pages = keys->max_pages;
+  ia.q_req = pw.q_req; ia.n_req = mode == 1 ? rows : 1; ia.n_vis = pw.n_vis; ia.Q = rows; ia.HI = HI;
+  ia.max_n_vis = max_n_vis; ia.logits = pw.logits; ia.ld = pw.ld; ia.hist = pw.tk.hist;
+  CSA_HIP(csa::launch_indexer(ia, stream));
+
+  csa::TopkArgs t{};
+  t.logits = pw.logits; t.ld = pw.ld; t.n_vis = pw.n_vis; t.Q = rows; t.max_n_vis = max_n_vis; t.k = k;
+  t.idx = idx + kWin; t.ld_idx = ld_idx; t.hist = pw.tk.hist; t.counters = pw.tk.counters; t.sel = pw.tk.sel;
+  t.cand = pw.tk.cand; t.cand_cap = max_n_vis > 0 ? max_n_vis : 1;
+  CSA_HIP(csa::launch_topk_select(t, stream));
+
+  csa::AttnArgs a{};
+  a.q = q; a.q_dt = q_dt; a.Q = rows; a.H = H; a.sink = sink;
+  a.win = (const uint8_t*)win; a.win_fmt = win_fmt; a.win_rows_per_req = win_rows_per_req;
+  a.comp = (const uint8_t*)comp->rows; a.comp_fmt = comp->fmt; a.comp_num_pages = comp->num_pages;
+  a.page_table = comp->page_table; a.max_pages = comp->max_pages;
+  a.q_req = pw.q_req; a.n_req = mode == 1 ? rows : 1; a.idx = idx; a.ld_idx = ld_idx; a.n_win = kWin; a.n_comp = k;
+  a.softmax_scale = softmax_scale; a.out = out; a.out_dt = out_dt;
+  a.n_split = csa::plan_attn_split(rows, H, kWin + k, q_dt);
+  a.part = pw.part;
+  return hip_status(csa::launch_attention(a, stream));
+}
+
+static csa_status check_path(int32_t rows, int32_t H, int32_t HI, int32_t k, const void* q, int32_t q_dt,
+                             const float* sink, const void* qI, const uint8_t* qI_scale, int32_t qI_dt,
+                             const float* w, const csa_paged_idx* keys, const csa_paged_kv* comp, const void* win,
+                             int32_t win_fmt, float scale, void* out, int32_t out_dt) {
+  CSA_TRY(check_attn_common(q, q_dt, H, sink, out, out_dt, scale));
+  CSA_TRY(check_indexer_inputs(qI, qI_scale, qI_dt, w, HI));
+  CSA_TRY(check_idx_struct(keys, qI_dt));
+  CSA_TRY(check_kv_struct(comp));
+  if (!win) return CSA_ERR_NULL;
+  if (!kv_fmt_ok(win_fmt)) return CSA_ERR_DTYPE;
+  if (!aligned(win, 16)) return CSA_ERR_ALIGN;
+  if (rows < 1 || rows > 65535 || k < 1 || k > 2048) return CSA_ERR_SHAPE;
+  if (comp->max_pages != keys->max_pages) return CSA_ERR_SHAPE;
+  return CSA_OK;
+}
+
+size_t csa_decode_workspace_bytes(int32_t B, int32_t H, int32_t HI, int64_t max_ctx, int32_t k) {
+  if (B < 1 || H < 1 || HI < 1 || k < 1 || max_ctx < 0) return 0;
+  Carver c(nullptr);
+  carve_path(c, B, H, max_ctx / 4, k);
+  return c.off;
+}
+
+csa_status csa_decode(int32_t B, int32_t H, int32_t HI, int32_t k, const void* q, int32_t q_dt, const float* sink,
+                      const void* qI, const uint8_t* qI_scale, int32_t qI_dt, const float* w,
+                      const csa_paged_idx* keys, const csa_paged_kv* comp, const void* win_ring, int32_t win_fmt,
+                      const int32_t* ctx_len, int64_t max_ctx, float softmax_scale, void* out, int32_t out_dt,
+                      int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  CSA_TRY(check_path(B, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys, comp, win_ring, win_fmt,
+                     softmax_scale, out, out_dt));
+  if (!ctx_len) return CSA_ERR_NULL;
+  if (!aligned(ctx_len, 4)) return CSA_ERR_ALIGN;
+  if (max_ctx < 0 || max_ctx > INT32_MAX) return CSA_ERR_SHAPE;
+  const int64_t max_n_vis = std::min<int64_t>(max_ctx / 4, (int64_t)keys->max_pages * 64);
+  const size_t need = csa_decode_workspace_bytes(B, H, HI, max_ctx, k);
+  return run_path(1, B, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys, comp, win_ring, win_fmt, kWin,
+                  ctx_len, max_ctx, 0, max_n_vis, softmax_scale, out, out_dt, idx_out, ws, ws_bytes, need, stream);
+}
+
+size_t csa_prefill_workspace_bytes(int32_t Q, int32_t H, int32_t HI, int64_t T, int32_t k) {
+  if (Q < 1 || H < 1 || HI < 1 || k < 1 || T < 0) return 0;
+  Carver c(nullptr);
+  carve_path(c, Q, H, T / 4, k);
+  return c.off;
+}
+
+csa_status csa_prefill(int32_t Q, int32_t H, int32_t HI, int32_t k, const void* q, int32_t q_dt, const float* sink,
+                       const void* qI, const uint8_t* qI_scale, int32_t qI_dt, const float* w,
+                       const csa_paged_idx* keys, const csa_paged_kv* comp, const void* raw_rows, int32_t raw_fmt,
+                       int64_t T, int64_t pos0, float softmax_scale, void* out, int32_t out_dt, int32_t* idx_out,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  CSA_TRY(check_path(Q, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys, comp, raw_rows, raw_fmt,
+                     softmax_scale, out, out_dt));
+  if (T < 1 || T > INT32_MAX || pos0 < 0 || pos0 + Q > T) return CSA_ERR_SHAPE;
+  const int64_t max_n_vis = std::min<int64_t>((pos0 + Q) / 4, (int64_t)keys->max_pages * 64);
+  const size_t need = csa_prefill_workspace_bytes(Q, H, HI, T, k);
+  return run_path(2, Q, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys, comp, raw_rows, raw_fmt, T,
+                  nullptr, 0, pos0, max_n_vis, softmax_scale, out, out_dt, idx_out, ws, ws_bytes, need, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,79 @@
+// Device-side helpers shared by the CSA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kD = 512;         // head dim: 448 nope + 64 rope
+constexpr int kNope = 448;
+constexpr int kDI = 128;        // indexer dim
+constexpr int kPage = 64;       // compressed entries per page
+constexpr int kWin = 128;       // sliding window
+constexpr int kHistBins = 4096; // top-k coarse histogram: top 12 bits of the order key
+constexpr int kHistShift = 20;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;   // finite running-max start: an all-invalid row yields 0
+
+enum RowFmt : int { kRowF32 = 0, kRowBF16 = 1, kRowFP8 = 2 };
+
+__host__ __device__ constexpr int row_bytes(int fmt) {
+  return fmt == kRowF32 ? 2048 : (fmt == kRowBF16 ? 1024 : 608);
+}
+
+// Order-preserving map float -> uint32 (larger float -> larger key).  -0.0 is folded onto +0.0 so
+// equal scores tie; NaN maps to 0, below -inf.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (f != f) return 0u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);   // v_cvt_pk_bf16_f32: RNE
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// 4 e4m3fn bytes of `w` -> 4 floats (hardware conversion, OCP e4m3fn on gfx950).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
+  v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  v2f b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  o[0] = a[0]; o[1] = a[1]; o[2] = b[0]; o[3] = b[1];
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+template <int I, int N>
+struct static_for {
+  template <class F>
+  __device__ __forceinline__ static void run(F&& f) {
+    if constexpr (I < N) {
+      f(std::integral_constant<int, I>{});
+      static_for<I + 1, N>::run(f);
+    }
+  }
+};
+
+}  // namespace csa

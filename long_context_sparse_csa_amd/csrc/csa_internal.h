@@ -1,0 +1,99 @@
+// Internal host-side interface between the C ABI layer (api.cpp) and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa {
+
+// Records hipEvents around a launch when profiling is on (see csa_profile_enable).
+struct ProfScope {
+  ProfScope(const char* name, hipStream_t s);
+  ~ProfScope();
+  int slot;
+  hipStream_t stream;
+};
+
+struct IndexerArgs {
+  const void* qI;             // [Q][HI][128] fp8 bytes or fp32
+  const uint8_t* qI_scale;    // [Q][HI][4] E8M0 (fp8 only)
+  int dt;                     // 0 = f32, 2 = fp8
+  const float* w;             // [Q][HI]
+  const void* keys;           // [P][64][128]
+  const uint8_t* kscale;      // [P][4][64]
+  int num_pages;
+  const int32_t* page_table;  // [n_req][max_pages]
+  int max_pages;
+  const int32_t* q_req;       // [Q]
+  int n_req;
+  const int32_t* n_vis;       // [Q]
+  int Q, HI;
+  int64_t max_n_vis;
+  float* logits;              // [Q][ld]
+  int64_t ld;
+  uint32_t* hist;             // optional [Q][4096] coarse histogram of the written scores
+};
+hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
+
+struct TopkArgs {
+  const float* logits;
+  int64_t ld;
+  const int32_t* n_vis;
+  int Q;
+  int64_t max_n_vis;
+  int k;
+  int32_t* idx;
+  int64_t ld_idx;
+  uint32_t* hist;       // [Q][4096], filled by the indexer or by launch_topk_hist
+  uint32_t* counters;   // [Q][4], zero on entry
+  int32_t* sel;         // [Q][k]
+  uint2* cand;          // [Q][cand_cap]
+  int64_t cand_cap;
+};
+hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
+hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
+
+// Zero histograms / counters and write window indices (decode ring or causal prefill window).
+struct PrepArgs {
+  uint32_t* zero_ptr;        // words to clear
+  int64_t zero_words;
+  int mode;                  // 0: none, 1: decode ring, 2: causal prefill
+  int rows;                  // B (decode) or Q (prefill)
+  const int32_t* ctx_len;    // decode: [B]
+  int64_t max_ctx;           // decode: clamp of ctx_len
+  int64_t pos0;              // prefill: position of query 0
+  int32_t* idx;              // [rows][ld_idx] window part written to columns [0,128)
+  int64_t ld_idx;
+  int32_t* n_vis_out;        // [rows]
+  int32_t* q_req_out;        // optional [rows]: request id of each row (decode: row, prefill: 0)
+};
+hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
+
+struct AttnArgs {
+  const void* q;             // [Q][H][512]
+  int q_dt;                  // 0 f32, 1 bf16
+  int Q, H;
+  const float* sink;
+  const uint8_t* win;
+  int win_fmt;
+  int64_t win_rows_per_req;
+  const uint8_t* comp;
+  int comp_fmt;
+  int comp_num_pages;
+  const int32_t* page_table;
+  int max_pages;
+  const int32_t* q_req;
+  int n_req;
+  const int32_t* idx;
+  int64_t ld_idx;
+  int n_win, n_comp;
+  float softmax_scale;
+  void* out;
+  int out_dt;                // 0 f32, 1 bf16
+  float* part;               // split-K partials (may be null when n_split == 1)
+  int n_split;               // chosen by plan_attn_split
+};
+int plan_attn_split(int Q, int H, int n_idx, int q_dt);
+size_t attn_partial_bytes(int Q, int H, int n_idx);
+hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
+
+}  // namespace csa

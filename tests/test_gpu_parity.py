@@ -1,0 +1,217 @@
+"""GPU parity of the HIP path against the CPU oracle, at sizes the oracle finishes in seconds that
+still span several tiles, pages and blocks with ragged tails.  Every call goes through the C ABI."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import csa_oracle as O
+from tests.helpers import BF16_TOL, F32_TOL, check_attention, check_topk_row
+from workloads import configs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import long_context_sparse_csa_amd as csa
+    csa.lib()
+    return "cuda"
+
+
+def _run():
+    from workloads import run, torch_io
+    return run, torch_io
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+# ------------------------------------------------------------------------------------ indexer
+@pytest.mark.parametrize("HI,idx_dt", [(64, configs.DT_FP8), (40, configs.DT_FP8), (16, configs.DT_FP8),
+                                        (16, configs.DT_F32), (64, configs.DT_F32)])
+def test_indexer_scores(dev, HI, idx_dt):
+    run, tio = _run()
+    ctx = [4096, 1000, 257, 0, 6000, 3]
+    wl = configs.make_decode("idx", ctx, H=16, HI=HI, idx_dt=idx_dt, seed=11)
+    _say(f"indexer HI={HI} dt={idx_dt} ctx={ctx}")
+    d = tio.to_device(wl, dev)
+    logits = run.indexer(wl, d).cpu().numpy()
+    for qi in range(wl.Q):
+        nv = int(wl.n_vis[qi])
+        ref = O.query_scores(wl, qi)
+        got = logits[qi, :nv].astype(np.float64)
+        bound = _fp32_score_bound(wl, qi)
+        err = np.abs(got - ref)
+        assert np.all(err <= bound), f"query {qi}: max err {err.max():.3e}, worst ratio {(err / bound).max():.2f}"
+        if nv:
+            _say(f"query {qi}: max err {err.max():.2e}, max err/bound {(err / bound).max():.3f}")
+        assert np.all(np.isneginf(logits[qi, nv:wl.max_n_vis])), f"query {qi}: tail not -inf"
+
+
+def _fp32_score_bound(wl, qi):
+    """Forward error bound of the score computed in fp32 from exact fp8 products: each head logit sums
+    128 products (error <= 128 u sum|q_d k_d|), the weighted head sum adds HI more roundings.  u=2^-24."""
+    nv = int(wl.n_vis[qi])
+    if nv == 0:
+        return np.zeros(0)
+    u = 2.0 ** -24
+    qh = O.indexer_q_values(wl.qI[qi], None if wl.qI_scale is None else wl.qI_scale[qi], wl.idx_dt)
+    r = int(wl.q_req[qi])
+    ent = np.arange(nv)
+    pages = wl.page_table[r][ent // 64]
+    k = np.empty((nv, 128))
+    for p in np.unique(pages):
+        sel = pages == p
+        k[sel] = O.indexer_key_values(wl.ik_keys, wl.ik_scales, wl.idx_dt, int(p), (ent % 64)[sel])
+    absdot = np.abs(k) @ np.abs(qh).T                       # [nv, HI]
+    logit = k @ qh.T
+    w = np.abs(wl.w[qi].astype(np.float64))
+    return 2 * (128 * u * (absdot @ w) + (wl.HI + 2) * u * (np.maximum(logit, 0) @ w)) + 1e-30
+
+
+# ------------------------------------------------------------------------------------ top-k
+def _topk_cases(rng):
+    cases = []
+    for n_vis in [0, 1, 511, 512, 513, 777, 5000, 70000]:
+        cases.append(rng.standard_normal(n_vis).astype(np.float32))
+    ties = rng.integers(0, 7, size=9000).astype(np.float32)                # heavy ties at the threshold
+    cases.append(ties)
+    flat = np.full(6000, 1.5, np.float32)                                   # every score equal
+    cases.append(flat)
+    mixed = rng.standard_normal(3000).astype(np.float32)
+    mixed[::7] = -np.inf
+    mixed[5::11] = np.nan
+    mixed[3::13] = -0.0
+    mixed[4::17] = 0.0
+    cases.append(mixed)
+    few = np.full(2000, -np.inf, np.float32)                                # fewer finite than k
+    few[rng.choice(2000, 100, replace=False)] = rng.standard_normal(100).astype(np.float32)
+    cases.append(few)
+    return cases
+
+
+@pytest.mark.parametrize("k", [512, 1, 100, 2048])
+def test_topk_exact(dev, k):
+    run, _ = _run()
+    rng = np.random.default_rng(5 + k)
+    cases = _topk_cases(rng)
+    n = [len(c) for c in cases]
+    max_n = max(n)
+    ld = (max_n + 63) // 64 * 64
+    L = np.full((len(cases), ld), 7.0, np.float32)      # junk beyond n_vis must be ignored
+    for i, c in enumerate(cases):
+        L[i, :len(c)] = c
+    _say(f"topk k={k} n_vis={n}")
+    idx = run.topk(torch.from_numpy(L).to(dev), torch.tensor(n, dtype=torch.int32, device=dev), max_n, k)
+    idx = idx.cpu().numpy()
+    for i, c in enumerate(cases):
+        ref = O.topk_select(c.astype(np.float64), len(c), k)
+        if len(c) > k:
+            ref = np.sort(ref)
+        assert idx[i].tolist() == ref.tolist(), f"case {i} (n_vis={len(c)}) differs"
+
+
+# ------------------------------------------------------------------------------------ sparse attention
+@pytest.mark.parametrize("kv_fmt,q_dt", [(configs.KV_FP8, configs.DT_BF16), (configs.KV_BF16, configs.DT_BF16),
+                                          (configs.KV_F32, configs.DT_F32), (configs.KV_FP8, configs.DT_F32)])
+@pytest.mark.parametrize("H", [64, 8, 80])
+def test_sparse_attn_explicit_indices(dev, kv_fmt, q_dt, H):
+    run, tio = _run()
+    ctx = [3000, 700, 0, 5000]
+    out_dt = configs.DT_F32 if q_dt == configs.DT_F32 else configs.DT_BF16
+    wl = configs.make_decode("attn", ctx, H=H, HI=16, q_dt=q_dt, out_dt=out_dt, kv_fmt=kv_fmt, seed=21)
+    rng = np.random.default_rng(H + kv_fmt)
+    n_win, n_comp = 128, 300
+    limit = wl.max_pages * 64
+    idx = np.empty((wl.Q, n_win + n_comp), np.int32)
+    idx[:, :n_win] = rng.integers(-5, 140, size=(wl.Q, n_win))
+    idx[:, n_win:] = rng.integers(-3, limit + 10, size=(wl.Q, n_comp))
+    idx[0, n_win + 5] = idx[0, n_win + 6]           # duplicate slot
+    idx[1, :] = -1                                  # a query with no valid slot
+    idx[1, 3] = 200                                 # out-of-range window index
+    _say(f"sparse_attn kv_fmt={kv_fmt} q_dt={q_dt} H={H}")
+    d = tio.to_device(wl, dev)
+    out = tio.out_to_numpy(run.sparse_attn(wl, d, torch.from_numpy(idx).to(dev), n_win, n_comp))
+    tol = F32_TOL if q_dt == configs.DT_F32 else BF16_TOL
+    for qi in range(wl.Q):
+        ref = O.attend(wl, qi, idx[qi, :n_win], idx[qi, n_win:])
+        check_attention(out[qi], ref, tol, f"query {qi}")
+    assert np.all(out[1] == 0.0)
+
+
+# ------------------------------------------------------------------------------------ whole path
+def _check_decode(wl, out, idx, tol, empty_rows=()):
+    k = wl.topk
+    errs = []
+    for qi in range(wl.Q):
+        nv = int(wl.n_vis[qi])
+        scores = O.query_scores(wl, qi)
+        win = O.query_window(wl, qi)
+        assert idx[qi, :128].tolist() == win.tolist(), f"query {qi}: window indices differ"
+        check_topk_row(idx[qi, 128:], scores, nv, k, f"query {qi}")
+        ref = O.attend(wl, qi, idx[qi, :128], idx[qi, 128:])   # oracle on the GPU's own index set
+        errs.append(check_attention(out[qi], ref, tol, f"query {qi}"))
+    for r in empty_rows:
+        assert np.all(out[r] == 0.0), f"row {r} must be exact zero"
+    return max(errs)
+
+
+def test_decode_tiny_fp32(dev):
+    run, tio = _run()
+    wl = configs.tiny_decode()
+    _say("decode tiny fp32 (B=1, T=4096, H=16)")
+    out, idx = run.decode(wl, tio.to_device(wl, dev))
+    err = _check_decode(wl, tio.out_to_numpy(out), idx.cpu().numpy(), F32_TOL)
+    _say(f"max err {err:.2e}")
+
+
+def test_decode_batched_small(dev):
+    run, tio = _run()
+    wl = configs.batched_decode(B=4, T=65536)
+    _say("decode batched small (B=4, T=65536, H=64, fp8)")
+    out, idx = run.decode(wl, tio.to_device(wl, dev))
+    err = _check_decode(wl, tio.out_to_numpy(out), idx.cpu().numpy(), BF16_TOL)
+    _say(f"max err {err:.2e}")
+
+
+def test_decode_long_planted_small(dev):
+    run, tio = _run()
+    wl = configs.make_decode("long_small", [262144, 262144], H=64, HI=64, seed=0, planted_frac=0.01)
+    _say("decode long planted small (B=2, T=262144)")
+    out, idx = run.decode(wl, tio.to_device(wl, dev))
+    idx = idx.cpu().numpy()
+    _check_decode(wl, tio.out_to_numpy(out), idx, BF16_TOL)
+    for b in range(wl.B):
+        assert set(idx[b, 128:].tolist()) <= set(wl.planted[b].tolist())
+
+
+def test_decode_ragged_small(dev):
+    run, tio = _run()
+    ctx = [0, 100, 2000, 2047, 2048, 2052, 9000, 0, 131, 4]
+    wl = configs.make_decode("ragged_small", ctx, H=8, HI=64, kv_fmt=configs.KV_BF16, seed=4)
+    _say(f"decode ragged small ctx={ctx}")
+    out, idx = run.decode(wl, tio.to_device(wl, dev))
+    _check_decode(wl, tio.out_to_numpy(out), idx.cpu().numpy(), BF16_TOL, empty_rows=(0, 7))
+
+
+def test_prefill_small(dev):
+    run, tio = _run()
+    wl = configs.causal_prefill(T=2560)
+    _say("prefill small (T=2560, H=64)")
+    out, idx = run.prefill(wl, tio.to_device(wl, dev))
+    out, idx = tio.out_to_numpy(out), idx.cpu().numpy()
+    sample = sorted(set([0, 1, 2, 3, 4, 127, 128, 129, 2045, 2046, 2047, 2048, 2049, 2559] +
+                        np.random.default_rng(0).choice(2560, 24, replace=False).tolist()))
+    for t in sample:
+        nv = int(wl.n_vis[t])
+        scores = O.query_scores(wl, t)
+        assert idx[t, :128].tolist() == O.window_prefill(t).tolist()
+        check_topk_row(idx[t, 128:], scores, nv, wl.topk, f"t={t}")
+        ref = O.attend(wl, t, idx[t, :128], idx[t, 128:])
+        check_attention(out[t], ref, BF16_TOL, f"t={t}")

@@ -1,0 +1,91 @@
+"""Drive the CSA library on a workload (argument marshalling only; the work runs in libcsa.so)."""
+from __future__ import annotations
+
+import torch
+
+import long_context_sparse_csa_amd as csa
+
+from .configs import WINDOW, Workload
+from .torch_io import empty_out
+
+
+def _keys(wl: Workload, d):
+    return csa.paged_idx(d.ik_keys, d.ik_scales, wl.idx_dt, d.page_table)
+
+
+def _comp(wl: Workload, d):
+    return csa.paged_kv(d.kv_pool, wl.kv_fmt, d.page_table)
+
+
+def decode_workspace(wl: Workload, device="cuda"):
+    n = csa.csa_decode_workspace_bytes(wl.B, wl.H, wl.HI, int(wl.ctx_len.max()), wl.topk)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device), n
+
+
+def decode(wl: Workload, d, out=None, idx=None, ws=None, stream=None):
+    """One csa_decode call; returns (out [B,H,512], idx [B, 128+k])."""
+    dev = d.q.device
+    out = empty_out(wl, dev) if out is None else out
+    idx = torch.empty((wl.B, WINDOW + wl.topk), dtype=torch.int32, device=dev) if idx is None else idx
+    if ws is None:
+        ws, nbytes = decode_workspace(wl, dev)
+    else:
+        ws, nbytes = ws
+    keys, comp = _keys(wl, d), _comp(wl, d)
+    csa.csa_decode(wl.B, wl.H, wl.HI, wl.topk, d.q, wl.q_dt, d.sink, d.qI, d.qI_scale, wl.idx_dt, d.w, keys, comp,
+                   d.win_rows, wl.win_fmt, d.ctx_len, int(wl.ctx_len.max()), wl.softmax_scale, out, wl.out_dt, idx,
+                   ws, nbytes, stream)
+    return out, idx
+
+
+def prefill_workspace(wl: Workload, device="cuda"):
+    T = int(wl.win_rows.shape[1])
+    n = csa.csa_prefill_workspace_bytes(wl.Q, wl.H, wl.HI, T, wl.topk)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device), n
+
+
+def prefill(wl: Workload, d, out=None, idx=None, ws=None, stream=None):
+    dev = d.q.device
+    out = empty_out(wl, dev) if out is None else out
+    idx = torch.empty((wl.Q, WINDOW + wl.topk), dtype=torch.int32, device=dev) if idx is None else idx
+    if ws is None:
+        ws, nbytes = prefill_workspace(wl, dev)
+    else:
+        ws, nbytes = ws
+    T = int(wl.win_rows.shape[1])
+    keys, comp = _keys(wl, d), _comp(wl, d)
+    csa.csa_prefill(wl.Q, wl.H, wl.HI, wl.topk, d.q, wl.q_dt, d.sink, d.qI, d.qI_scale, wl.idx_dt, d.w, keys, comp,
+                    d.win_rows[0], wl.win_fmt, T, int(wl.positions[0]), wl.softmax_scale, out, wl.out_dt, idx, ws,
+                    nbytes, stream)
+    return out, idx
+
+
+def indexer(wl: Workload, d, stream=None):
+    """csa_indexer_logits over every query; returns logits [Q, ld]."""
+    max_n_vis = wl.max_n_vis
+    ld = max(64, (max_n_vis + 63) // 64 * 64)
+    logits = torch.empty((wl.Q, ld), dtype=torch.float32, device=d.q.device)
+    csa.csa_indexer_logits(d.qI, d.qI_scale, wl.idx_dt, d.w, _keys(wl, d), d.q_req, wl.B, d.n_vis, wl.Q, wl.HI,
+                           max_n_vis, logits, ld, stream)
+    return logits
+
+
+def topk(logits: torch.Tensor, n_vis: torch.Tensor, max_n_vis: int, k: int, stream=None):
+    Q, ld = logits.shape
+    n = csa.csa_topk_workspace_bytes(Q, max_n_vis, k)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=logits.device)
+    idx = torch.empty((Q, k), dtype=torch.int32, device=logits.device)
+    csa.csa_topk(logits, ld, n_vis, Q, max_n_vis, k, idx, k, ws, n, stream)
+    return idx
+
+
+def sparse_attn(wl: Workload, d, idx: torch.Tensor, n_win: int, n_comp: int, stream=None):
+    """csa_sparse_attn over explicit [window ++ compressed] index lists."""
+    out = empty_out(wl, d.q.device)
+    n = csa.csa_sparse_attn_workspace_bytes(wl.Q, wl.H, n_win + n_comp)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=d.q.device)
+    win = d.win_rows
+    csa.csa_sparse_attn(d.q, wl.q_dt, wl.Q, wl.H, d.sink, win, wl.win_fmt, int(wl.win_rows.shape[1]),
+                        _comp(wl, d), d.q_req, wl.B, idx, idx.shape[1], n_win, n_comp, wl.softmax_scale, out,
+                        wl.out_dt, ws, n, stream)
+    return out
