@@ -1,0 +1,228 @@
+"""Throughput of the CSA decode hot path (indexer -> top-512 -> sparse attention) on one MI355X.
+
+One step = one csa_decode call over a batch of synthetic queries already resident in HBM.  Default
+workload: batched decode, B=32 requests at 65,536 raw tokens (16,384 compressed entries each in
+pages of 64), H=64 query heads of 512 dims, FP8-nope/BF16-rope KV with per-64 fp32 scales, FP8
+indexer q/k (dim 128, E8M0 per 32), top-512, window 128.  Inputs are rotated over several device
+copies so the 256 MB Infinity Cache cannot serve repeated steps.
+
+Prints ONE JSON line (rank 0).  `roofline` is the indexer kernel's algorithmic HBM bytes per launch
+over its average launch duration, measured with HIP events on the launch stream during a second
+timed pass; `cpu_baseline` is the fp64 oracle timed on this host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KEY_BYTES = 132            # 128 FP8 + 4 E8M0 per indexer key
+ROW_BYTES = {0: 2048, 1: 1024, 2: 608}
+DOMINANT = "indexer_fp8"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", default="batched", choices=["batched", "long", "ragged", "tiny", "prefill"])
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = enough to exceed 1 GB)")
+    return p.parse_args()
+
+
+def make_workload(name):
+    from workloads import configs
+    return {"batched": configs.batched_decode, "long": configs.long_decode, "ragged": configs.ragged_decode,
+            "tiny": configs.tiny_decode, "prefill": configs.causal_prefill}[name]()
+
+
+def algorithmic_bytes(wl, idx_np):
+    """Bytes the method must move once per step (indexer keys of every visible entry, page table,
+    q, qI, w, sink, every valid gathered row, output) and the indexer kernel's share of them."""
+    Q, H, HI = wl.Q, wl.H, wl.HI
+    n_vis = wl.n_vis.astype("int64")
+    pages = (n_vis + 63) // 64
+    q_bytes = Q * H * 512 * (4 if wl.q_dt == 0 else 2)
+    qi_bytes = Q * HI * (128 * 4 if wl.idx_dt == 0 else 128 + 4)
+    w_bytes = Q * HI * 4
+    key_bytes = int(n_vis.sum()) * (512 if wl.idx_dt == 0 else KEY_BYTES)
+    pt_bytes = int(pages.sum()) * 4
+    indexer = key_bytes + pt_bytes + qi_bytes + w_bytes
+    valid_rows = 0
+    for qi in range(Q):
+        row = idx_np[qi]
+        valid_rows += int((row[:128] >= 0).sum()) + int((row[128:] >= 0).sum())
+    # window and compressed rows share a format in the configured workloads
+    attn = valid_rows * ROW_BYTES[wl.kv_fmt] + q_bytes + H * 4 + Q * H * 512 * (4 if wl.out_dt == 0 else 2)
+    return indexer + attn, indexer
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("indexer.hip", "csa_device.h"):
+        h.update(open(os.path.join(ROOT, "long_context_sparse_csa_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config):
+    """HBM bytes per indexer launch from the committed rocprofv3 PMC summary, if it was taken on the
+    current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"indexer_fp8_{config}_traffic.json")
+    try:
+        d = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, target_s):
+    """Time the oracle (as it stands) on a bounded sample of the workload's queries."""
+    import numpy as np
+    from oracle import csa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # noqa: BLE001
+        cores = 1
+    order = list(range(wl.Q))
+    done, t0 = 0, time.perf_counter()
+    outs = {}
+    while time.perf_counter() - t0 < target_s:
+        qi = order[done % len(order)]
+        out, top, _ = O.run_query(wl, qi)
+        outs[qi] = (out, top)
+        done += 1
+        if done >= 4 * len(order):
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "query-tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} queries of the {wl.name} workload ({el:.1f} s, fp64 numpy)"}, outs
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import long_context_sparse_csa_amd as csa
+    from workloads import run, torch_io
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    csa.lib()
+    dev = "cuda"
+    t_gen = time.perf_counter()
+    wl = make_workload(args.config)
+    gen_s = time.perf_counter() - t_gen
+    base = torch_io.to_device(wl, dev)
+    decode = wl.kind == "decode"
+    runner = run.decode if decode else run.prefill
+    out, idx = runner(wl, base)
+    torch.cuda.synchronize()
+    idx_np = idx.cpu().numpy()
+    total_bytes, idx_bytes = algorithmic_bytes(wl, idx_np)
+
+    # input copies at distinct addresses so repeated steps miss the Infinity Cache
+    # the bytes a step touches (not the allocation) decide whether the 256 MB Infinity Cache could
+    # serve a repeat: rotate until the rotation touches >= 1 GB
+    n_copies = args.copies or max(2, math.ceil(1.0e9 / max(total_bytes, 1)))
+    copies = [base]
+    for _ in range(n_copies - 1):
+        c = type(base)()
+        for k, v in vars(base).items():
+            setattr(c, k, v.clone() if isinstance(v, torch.Tensor) else v)
+        copies.append(c)
+    ws = (run.decode_workspace if decode else run.prefill_workspace)(wl, dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        runner(wl, copies[i % n_copies], out=out, idx=idx, ws=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    value = wl.Q / (ms_per_step / 1e3)
+
+    # second pass: per-kernel HIP events on the launch stream
+    csa.csa_profile_reset()
+    csa.csa_profile_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    csa.csa_profile_enable(False)
+    kernels = {}
+    for name in ("prep", "indexer_fp8", "indexer_f32", "topk_hist", "topk_collect", "topk_finish", "attn_bf16",
+                 "attn_combine", "attn_f32"):
+        tot, n = csa.csa_profile_collect(name)
+        if n:
+            kernels[name] = round(tot / n * 1e3, 3)
+    csa.csa_profile_reset()
+    dom = DOMINANT if DOMINANT in kernels else max(kernels, key=kernels.get)
+    dom_us = kernels[dom]
+    achieved = idx_bytes / (dom_us * 1e-6) / 1e9
+    traffic = measured_traffic(args.config)
+
+    res = {
+        "metric": "decode query-tokens/s for indexer+top512+sparse_attn; achieved HBM TB/s",
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3fn indexer, bf16 matrix-core attention, fp32 accumulate",
+        "data": "synthetic (seeded N(0,1) q/kv/indexer, quantised as the workload states)",
+        "config": {"workload": wl.name, "B": wl.B, "Q": wl.Q, "H": wl.H, "HI": wl.HI,
+                   "context": int(wl.ctx_len.max()) if decode else int(wl.win_rows.shape[1]),
+                   "compressed_entries": int(wl.max_n_vis), "topk": wl.topk, "window": wl.window,
+                   "kv_format": {0: "f32", 1: "bf16", 2: "fp8nope_bf16rope"}[wl.kv_fmt],
+                   "input_copies": n_copies},
+        "achieved_hbm_tbs": round(total_bytes / (ms_per_step * 1e-3) / 1e12, 3),
+        "step_hbm_frac": round(total_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_bytes_per_step": int(total_bytes),
+        "kernel_us": kernels,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": int(idx_bytes),
+                     "traffic": traffic},
+        "wall_s_timed": round(wall, 4),
+        "gen_s": round(gen_s, 1),
+    }
+    if not args.no_cpu:
+        cb, outs = cpu_baseline(wl, args.cpu_seconds)
+        res["cpu_baseline"] = cb
+        o = torch_io.out_to_numpy(out)
+        errs = [float(np.abs(o[qi] - ref[0]).max()) for qi, ref in outs.items()]
+        res["parity_max_abs_vs_oracle"] = max(errs) if errs else None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

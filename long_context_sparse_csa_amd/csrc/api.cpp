@@ -60,7 +60,7 @@ struct TopkWs {
 TopkWs carve_topk(Carver& c, int32_t Q, int64_t max_n_vis, int32_t k) {
   TopkWs w;
   w.hist = c.take<uint32_t>((size_t)Q * kHistBins * 4);
-  w.counters = c.take<uint32_t>((size_t)Q * 4 * 4);
+  w.counters = c.take<uint32_t>((size_t)Q * 8 * 4);
   w.sel = c.take<int32_t>((size_t)Q * k * 4);
   w.cand = c.take<uint2>((size_t)Q * (size_t)(max_n_vis > 0 ? max_n_vis : 1) * 8);
   return w;
@@ -253,6 +253,12 @@ csa_status csa_topk(const float* logits, int64_t ld, const int32_t* n_vis, int32
   if (!aligned(ws, 16)) return CSA_ERR_ALIGN;
   Carver c(ws);
   TopkWs w = carve_topk(c, Q, max_n_vis, k);
+  if (csa::topk_single_ok(max_n_vis, k) && ld % 4 == 0 && aligned(logits, 16)) {
+    csa::TopkArgs t{};
+    t.logits = logits; t.ld = ld; t.n_vis = n_vis; t.Q = Q; t.max_n_vis = max_n_vis; t.k = k;
+    t.idx = idx; t.ld_idx = ld_idx; t.win_mode = 0;
+    return hip_status(csa::launch_topk_single(t, stream));
+  }
   csa::PrepArgs p{};
   p.zero_ptr = w.hist;
   p.zero_words = (int64_t)((uint8_t*)w.sel - (uint8_t*)w.hist) / 4;   // hist + counters
@@ -302,7 +308,8 @@ csa_status csa_sparse_attn(const void* q, int32_t q_dt, int32_t Q, int32_t H, co
   }
   a.q_req = q_req; a.n_req = n_req; a.idx = idx; a.ld_idx = ld_idx; a.n_win = n_win; a.n_comp = n_comp;
   a.softmax_scale = softmax_scale; a.out = out; a.out_dt = out_dt;
-  a.n_split = csa::plan_attn_split(Q, H, n_idx, q_dt);
+  a.n_split = csa::attn_uses_matrix_cores(q_dt, a.win_fmt, a.comp_fmt, n_win, n_comp)
+                  ? csa::plan_attn_split(Q, H, n_idx, q_dt) : 1;
   a.part = (float*)ws;
   return hip_status(csa::launch_attention(a, stream));
 }
@@ -322,27 +329,34 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   PathWs pw = carve_path(c, rows, H, max_n_vis, k);
   int32_t* idx = idx_out ? idx_out : pw.idx;
   const int64_t ld_idx = kWin + k;
+  // Short rows: the indexer and a one-block-per-query selection derive visibility from ctx_len /
+  // pos0 themselves, so no preparation launch and no zeroed histogram are needed.
+  const bool single = csa::topk_single_ok(max_n_vis, k);
 
-  csa::PrepArgs p{};
-  p.zero_ptr = pw.tk.hist;
-  p.zero_words = (int64_t)((uint8_t*)pw.tk.sel - (uint8_t*)pw.tk.hist) / 4;
-  p.mode = mode; p.rows = rows; p.ctx_len = ctx_len; p.max_ctx = max_ctx; p.pos0 = pos0;
-  p.idx = idx; p.ld_idx = ld_idx; p.n_vis_out = pw.n_vis; p.q_req_out = pw.q_req;
-  CSA_HIP(csa::launch_prep(p, stream));
+  if (!single) {
+    csa::PrepArgs p{};
+    p.zero_ptr = pw.tk.hist;
+    p.zero_words = (int64_t)((uint8_t*)pw.tk.sel - (uint8_t*)pw.tk.hist) / 4;
+    p.mode = mode; p.rows = rows; p.ctx_len = ctx_len; p.max_ctx = max_ctx; p.pos0 = pos0;
+    p.idx = idx; p.ld_idx = ld_idx; p.n_vis_out = pw.n_vis; p.q_req_out = pw.q_req;
+    CSA_HIP(csa::launch_prep(p, stream));
+  }
 
   csa::IndexerArgs ia{};
   ia.qI = qI; ia.qI_scale = qI_scale; ia.dt = qI_dt; ia.w = w;
   ia.keys = keys->keys; ia.kscale = keys->scales; ia.num_pages = keys->num_pages;
   ia.page_table = keys->page_table; ia.max_pages = keys->max_pages;
   ia.q_req = pw.q_req; ia.n_req = mode == 1 ? rows : 1; ia.n_vis = pw.n_vis; ia.Q = rows; ia.HI = HI;
-  ia.max_n_vis = max_n_vis; ia.logits = pw.logits; ia.ld = pw.ld; ia.hist = pw.tk.hist;
+  ia.max_n_vis = max_n_vis; ia.logits = pw.logits; ia.ld = pw.ld; ia.hist = single ? nullptr : pw.tk.hist;
+  ia.vis_mode = single ? mode : 0; ia.ctx_len = ctx_len; ia.max_ctx = max_ctx; ia.pos0 = pos0;
   CSA_HIP(csa::launch_indexer(ia, stream));
 
   csa::TopkArgs t{};
   t.logits = pw.logits; t.ld = pw.ld; t.n_vis = pw.n_vis; t.Q = rows; t.max_n_vis = max_n_vis; t.k = k;
   t.idx = idx + kWin; t.ld_idx = ld_idx; t.hist = pw.tk.hist; t.counters = pw.tk.counters; t.sel = pw.tk.sel;
   t.cand = pw.tk.cand; t.cand_cap = max_n_vis > 0 ? max_n_vis : 1;
-  CSA_HIP(csa::launch_topk_select(t, stream));
+  t.win_mode = single ? mode : 0; t.ctx_len = ctx_len; t.max_ctx = max_ctx; t.pos0 = pos0;
+  CSA_HIP(single ? csa::launch_topk_single(t, stream) : csa::launch_topk_select(t, stream));
 
   csa::AttnArgs a{};
   a.q = q; a.q_dt = q_dt; a.Q = rows; a.H = H; a.sink = sink;
@@ -351,8 +365,9 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   a.page_table = comp->page_table; a.max_pages = comp->max_pages;
   a.q_req = pw.q_req; a.n_req = mode == 1 ? rows : 1; a.idx = idx; a.ld_idx = ld_idx; a.n_win = kWin; a.n_comp = k;
   a.softmax_scale = softmax_scale; a.out = out; a.out_dt = out_dt;
-  a.n_split = csa::plan_attn_split(rows, H, kWin + k, q_dt);
+  a.n_split = csa::attn_uses_matrix_cores(q_dt, win_fmt, comp->fmt, kWin, k) ? csa::plan_attn_split(rows, H, kWin + k, q_dt) : 1;
   a.part = pw.part;
+  a.req_mode = mode;
   return hip_status(csa::launch_attention(a, stream));
 }
 

@@ -7,27 +7,31 @@
 // query with no valid slot outputs exact zeros.  K and V are the same 512-dim rows.
 //
 // BF16 matrix-core kernel (q bf16): a block owns one query, up to 64 heads (one wave per 16 heads)
-// and a contiguous range of 32-slot tiles.  Per tile the block gathers the 32 rows once (coalesced:
-// one 16-B lane chunk per 8 dims of a row, FP8 nope dequantised with its fp32 block scale), writes
-// them to LDS twice as bf16 - row-major for S^T = K.q^T and transposed for O^T = V^T.P^T - and each
-// wave runs 2x16 + 32 v_mfma_f32_16x16x32_bf16.  Computing S transposed leaves each lane holding 8
-// scores of its own head, which are exactly the P^T operand of the P.V product once the key order
-// inside the 32-wide K step is permuted (slot 8g+4mt+i <-> key 16mt+4g+i); the transposed V tile is
-// written in that slot order.  Softmax runs in base 2 with log2(e) folded into the scale.
+// and a contiguous range of 32-slot tiles.  All slots of the range are resolved to row addresses
+// up front; per tile the block gathers the 32 rows once (coalesced: one 16-B lane chunk per 8 dims
+// of a row, FP8 nope dequantised with its fp32 block scale) into one row-major bf16 LDS tile while
+// the next tile's rows are already in flight, and each wave runs 2x16 + 32
+// v_mfma_f32_16x16x32_bf16.  Computing S transposed (S^T = K.q^T) leaves each lane holding 8 scores
+// of its own head, which are exactly the P^T operand of O^T = V^T.P^T once the key order inside the
+// 32-wide K step is permuted (slot 8g+4mt+i <-> key 16mt+4g+i); the V^T operand is read from the
+// same row-major tile with gfx950's transposing LDS load (ds_read_b64_tr_b16), so no transposed
+// copy is ever written.  Softmax runs in base 2 with log2(e) folded into the scale.
 // Large queries-by-heads grids run unsplit; small ones split the slot range across blocks and a
 // combine kernel merges the (max, sum, acc) partials, sink included.
 //
 // fp32 kernel (q f32): one block per (query, head); scores, softmax and P.V in fp32 with natural
 // exp, for bit-accurate-ish comparisons against the fp64 definition.
+#include <cstdlib>
+
 #include "csa_device.h"
 #include "csa_internal.h"
 
 namespace csa {
 
 constexpr int kTile = 32;
-constexpr int kKrStride = 520;   // bf16 per row of the row-major tile (1040 B, 16-B aligned)
-constexpr int kVtStride = 36;    // bf16 per row of the transposed tile (72 B)
+constexpr int kKrStride = 528;   // bf16 per row of the row-major tile (1056 B, 16-B aligned)
 constexpr int kMaxSplit = 8;
+constexpr float kRescaleLog2 = 8.f;
 
 struct RowSrc {
   const uint8_t* p;
@@ -105,41 +109,123 @@ __device__ __forceinline__ void store4(void* out, int out_dt, int64_t off, float
   }
 }
 
+// Slot codes: -1 invalid, else (row << 3) | (fmt << 1) | src, src 0 = window, 1 = compressed.
+__device__ __forceinline__ int32_t slot_code(const AttnArgs& a, int q, int r, int s) {
+  if (r < 0 || r >= a.n_req || s >= a.n_win + a.n_comp) return -1;
+  const int v = a.idx[(int64_t)q * a.ld_idx + s];
+  if (v < 0) return -1;
+  if (s < a.n_win) {
+    if (a.win == nullptr || v >= a.win_rows_per_req) return -1;
+    return (int32_t)((((int64_t)r * a.win_rows_per_req + v) << 3) | (a.win_fmt << 1));
+  }
+  if (a.comp == nullptr || (int64_t)v >= (int64_t)a.max_pages * kPage) return -1;
+  const int pg = a.page_table[(int64_t)r * a.max_pages + (v >> 6)];
+  if ((unsigned)pg >= (unsigned)a.comp_num_pages) return -1;
+  return (int32_t)((((int64_t)pg * kPage + (v & 63)) << 3) | (a.comp_fmt << 1) | 1);
+}
+
+__device__ __forceinline__ const uint8_t* code_row(const AttnArgs& a, int32_t code) {
+  const int fmt = (code >> 1) & 3;
+  const int64_t row = (int64_t)(code >> 3);
+  return ((code & 1) ? a.comp : a.win) + row * row_bytes(fmt);
+}
+
+// One 16-byte chunk per lane per row, loaded without branches so a whole tile of loads is in
+// flight at once.  Lane dc covers dims [8dc, 8dc+8): BF16 rows give the 8 values directly; FP8 rows
+// give 8 nope codes (the first 8 of 16 bytes loaded at 8dc; lanes >= 56 load 8 bf16 rope values)
+// plus the fp32 scale of their 64-dim block.  Invalid slots load from a valid dummy address and
+// are zeroed at conversion.
+struct RawChunk {
+  uint4 x;
+  uint32_t sc;
+};
+
+template <int WF, int CF>
+__device__ __forceinline__ RawChunk load_raw(const AttnArgs& a, int32_t code, int dc) {
+  const bool comp = (code & 1) != 0;
+  const int fmt = comp ? CF : WF;
+  const int64_t row = (int64_t)(code >> 3);
+  const uint8_t* base = comp ? a.comp : a.win;
+  const int rb = comp ? row_bytes(CF) : row_bytes(WF);
+  const uint8_t* rp = code >= 0 ? base + row * rb : (const uint8_t*)a.q;
+  const int off = fmt == kRowFP8 ? (dc < kNope / 8 ? 8 * dc : 16 * dc - kNope) : 16 * dc;
+  RawChunk r;
+  r.x = *(const uint4*)(rp + off);
+  if constexpr (WF == kRowFP8 || CF == kRowFP8) {
+    const int so = 576 + 4 * ((dc >> 3) < 6 ? (dc >> 3) : 6);
+    r.sc = *(const uint32_t*)(rp + so);
+  } else {
+    r.sc = 0u;
+  }
+  return r;
+}
+
+template <int WF, int CF>
+__device__ __forceinline__ void raw_to_bf16(const RawChunk& r, int32_t code, int dc, uint32_t* w) {
+  const int fmt = (code & 1) ? CF : WF;
+  if (code < 0) {
+    w[0] = w[1] = w[2] = w[3] = 0u;
+    return;
+  }
+  if ((WF == kRowFP8 || CF == kRowFP8) && fmt == kRowFP8 && dc < kNope / 8) {
+    float v[8];
+    fp8x4_to_f32(r.x.x, v);
+    fp8x4_to_f32(r.x.y, v + 4);
+    const float sc = __uint_as_float(r.sc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(v[2 * e] * sc, v[2 * e + 1] * sc);
+  } else {
+    w[0] = r.x.x; w[1] = r.x.y; w[2] = r.x.z; w[3] = r.x.w;
+  }
+}
+
+constexpr int kMaxSlots = 4096;
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+
+// ds_read_b64_tr_b16 (gfx950).  Measured lane semantics: inside each group of 16 lanes, lane d
+// receives element (d & 3) of the 4-element chunks addressed by lanes d/4, d/4+4, d/4+8, d/4+12.
+__device__ __forceinline__ v4s lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)((__attribute__((address_space(3))) uint16_t*)p));
+}
+
+template <int WF, int CF>
 __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
-  const int nw = blockDim.x >> 6;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int nw = 4;   // all four waves gather; waves whose 16 heads are all padding skip compute
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int q = blockIdx.x / a.n_split, split = blockIdx.x % a.n_split;
   const int Hpad = (a.H + 15) & ~15;
   const int h = blockIdx.y * 64 + wave * 16 + n;   // this lane's head
   const bool h_ok = h < a.H;
+  const bool computes = blockIdx.y * 64 + wave * 16 < Hpad;
 
   __shared__ __align__(16) uint16_t Kr[kTile * kKrStride];
-  __shared__ __align__(16) uint16_t Vt[kD * kVtStride];
-  __shared__ const uint8_t* rowp[kTile];
-  __shared__ int rowf[kTile];
-  __shared__ int nvalid;
+  __shared__ int32_t codes[kMaxSlots];
+  __shared__ int tile_valid;
 
   const int n_idx = a.n_win + a.n_comp;
   const int n_tiles = (n_idx + kTile - 1) / kTile;
   const int tps = (n_tiles + a.n_split - 1) / a.n_split;
   const int t_begin = split * tps;
   const int t_end = min(n_tiles, t_begin + tps);
-  const int r = a.q_req[q];
+  const int r = a.req_mode == 1 ? q : (a.req_mode == 2 ? 0 : a.q_req[q]);
+  const int s_begin = t_begin * kTile;
+  const int s_count = max(0, (t_end - t_begin) * kTile);
+
+  // every slot of this block's range resolved once: idx -> page -> row, all in parallel
+  for (int i = tid; i < s_count; i += 64 * nw) codes[i] = slot_code(a, q, r, s_begin + i);
 
   // q^T operand: lane holds q[h][32ks + 8g .. +8] for the 16 K-steps of 32 dims
   v8bf qf[16];
   {
     const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)q * a.H + (h_ok ? h : 0)) * kD;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      if (h_ok) {
-        qf[ks] = *(const v8bf*)(qrow + 32 * ks + 8 * g);
-      } else {
-        qf[ks] = v8bf{};
-      }
-    }
+    for (int ks = 0; ks < 16; ++ks) qf[ks] = h_ok ? *(const v8bf*)(qrow + 32 * ks + 8 * g) : v8bf{};
   }
+  __syncthreads();
 
   const float sc = a.softmax_scale * kLog2e;
   float m = kNegBig, lsum = 0.f;
@@ -147,45 +233,39 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int dt = 0; dt < 32; ++dt) acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int t = t_begin; t < t_end; ++t) {
-    __syncthreads();
-    RowSrc rs{nullptr, 0};
-    if (tid < kTile) {
-      rs = resolve_slot(a, q, r, t * kTile + tid);
-      rowp[tid] = rs.p;
-      rowf[tid] = rs.fmt;
-    }
-    if (wave == 0) {
-      const unsigned long long b = __ballot(tid < kTile && rs.p != nullptr);
-      if (lane == 0) nvalid = __popcll(b);
-    }
-    __syncthreads();
-    if (nvalid == 0) continue;
+  // raw rows of the next tile live in registers: wave w gathers rows w, w+4, ..., one 16-B chunk
+  // (8 dims) per lane, so each load instruction reads whole rows contiguously
+  constexpr int kRowsPerWave = kTile / nw;
+  RawChunk raw[kRowsPerWave];
+  auto fetch = [&](int t) {
+    const int base = (t - t_begin) * kTile;
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) raw[i] = load_raw<WF, CF>(a, codes[base + wave + nw * i], lane);
+  };
+  if (t_begin < t_end) fetch(t_begin);
 
-    // gather: rows (2pr, 2pr+1), lane = dim chunk; bf16 into Kr (row-major) and Vt (transposed)
-    for (int pr = wave; pr < kTile / 2; pr += nw) {
-      const int j0 = 2 * pr;
-      float v0[8], v1[8];
-      load_chunk8(rowp[j0], rowf[j0], lane, v0);
-      load_chunk8(rowp[j0 + 1], rowf[j0 + 1], lane, v1);
-      uint32_t w0[4], w1[4];
+  // transposed-read addresses of the P.V operand: source lane s = lane%16 of group g points at
+  // key row 4g + s/4 (slots 8g..8g+3) or 16 + 4g + s/4 (slots 8g+4..8g+7), dims 4*(s%4) .. +3
+  const uint16_t* tr_lo = &Kr[(4 * g + (n >> 2)) * kKrStride + 4 * (n & 3)];
+  const uint16_t* tr_hi = tr_lo + 16 * kKrStride;
+
+  for (int t = t_begin; t < t_end; ++t) {
+    const int base = (t - t_begin) * kTile;
+    __syncthreads();   // the previous tile's readers are done with Kr
+    if (wave == 0) {
+      const unsigned long long b = __ballot(lane < kTile && codes[base + (lane & 31)] >= 0);
+      if (lane == 0) tile_valid = __popcll(b);
+    }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        w0[e] = pack_bf16x2(v0[2 * e], v0[2 * e + 1]);
-        w1[e] = pack_bf16x2(v1[2 * e], v1[2 * e + 1]);
-      }
-      *(uint4*)&Kr[j0 * kKrStride + 8 * lane] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
-      *(uint4*)&Kr[(j0 + 1) * kKrStride + 8 * lane] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
-      const int slot = 8 * ((j0 & 15) >> 2) + 4 * (j0 >> 4) + (j0 & 3);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = (w0[e] & 0xFFFFu) | (w1[e] << 16);      // dim 8*lane + 2e
-        const uint32_t hi = (w0[e] >> 16) | (w1[e] & 0xFFFF0000u);  // dim 8*lane + 2e + 1
-        *(uint32_t*)&Vt[(8 * lane + 2 * e) * kVtStride + slot] = lo;
-        *(uint32_t*)&Vt[(8 * lane + 2 * e + 1) * kVtStride + slot] = hi;
-      }
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int j = wave + nw * i;
+      uint32_t w[4];
+      raw_to_bf16<WF, CF>(raw[i], codes[base + j], lane, w);
+      *(uint4*)&Kr[j * kKrStride + 8 * lane] = make_uint4(w[0], w[1], w[2], w[3]);
     }
     __syncthreads();
+    if (t + 1 < t_end) fetch(t + 1);      // global latency of the next tile overlaps this compute
+    if (tile_valid == 0 || !computes) continue;
 
     // S^T[key][head] for keys 0..15 (s0) and 16..31 (s1)
     v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = v4f{0.f, 0.f, 0.f, 0.f};
@@ -199,40 +279,44 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
     float sv[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sv[i] = rowp[4 * g + i] != nullptr ? s0[i] * sc : -INFINITY;
-      sv[4 + i] = rowp[16 + 4 * g + i] != nullptr ? s1[i] * sc : -INFINITY;
+      sv[i] = codes[base + 4 * g + i] >= 0 ? s0[i] * sc : -INFINITY;
+      sv[4 + i] = codes[base + 16 + 4 * g + i] >= 0 ? s1[i] * sc : -INFINITY;
     }
     float tmax = sv[0];
 #pragma unroll
     for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, sv[e]);
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m, tmax);
-    const float alpha = exp2f(m - m_new);
+    // lazy rescaling: the reference max moves only when a head's max grows by more than 2^8, so
+    // the accumulators are touched rarely; p = 2^(S - m) then stays below 256
+    const bool grow = tmax > m + kRescaleLog2;
+    if (__any(grow)) {
+      const float m_new = grow ? tmax : m;
+      const float alpha = exp2f(m - m_new);
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 32; ++dt) acc[dt] *= alpha;
+      m = m_new;
+    }
     float p[8], psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = exp2f(sv[e] - m_new);
+      p[e] = exp2f(sv[e] - m);
       psum += p[e];
     }
-    lsum = lsum * alpha + psum;
-    if (__any(m_new != m)) {
-#pragma unroll
-      for (int dt = 0; dt < 32; ++dt) acc[dt] *= alpha;
-    }
-    m = m_new;
+    lsum += psum;
     v8bf pf;
 #pragma unroll
     for (int e = 0; e < 8; ++e) pf[e] = (__bf16)p[e];
 
-    // O^T[d][head] += V^T[d][slot] . P^T[slot][head]
+    // O^T[d][head] += V^T[d][slot] . P^T[slot][head]; V^T comes from the row-major tile through
+    // the transposing LDS read (slot 8g+4mt+i <-> key 16mt+4g+i, matching P's register order)
 #pragma unroll
     for (int dt = 0; dt < 32; ++dt) {
-      const uint16_t* vp = &Vt[(16 * dt + n) * kVtStride + 8 * g];
-      const uint2 lo = *(const uint2*)vp;
-      const uint2 hi = *(const uint2*)(vp + 4);
-      const uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-      acc[dt] = mma_bf16(__builtin_bit_cast(v8bf, vv), pf, acc[dt]);
+      const v4s lo = lds_read_tr16(tr_lo + 16 * dt);
+      const v4s hi = lds_read_tr16(tr_hi + 16 * dt);
+      const v8bf vv = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      acc[dt] = mma_bf16(vv, pf, acc[dt]);
     }
   }
 
@@ -264,35 +348,45 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
 }
 
 // Merge split-K partials: out = sum_s acc_s 2^(m_s-M) / (sum_s l_s 2^(m_s-M) + 2^(sink-M)).
+// Every partial is loaded up front (the split loop is unrolled to its maximum and predicated).
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   const int q = blockIdx.x / a.H, h = blockIdx.x % a.H;
   const int Hpad = (a.H + 15) & ~15;
   const float* ml = a.part + (int64_t)a.Q * a.n_split * Hpad * kD;
+  const int d = threadIdx.x * 4;
+  float2 mls[kMaxSplit];
+  float4 x[kMaxSplit];
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    const int sc = s < a.n_split ? s : 0;
+    const int64_t prow = ((int64_t)q * a.n_split + sc) * Hpad + h;
+    mls[s] = *(const float2*)(ml + prow * 2);
+    x[s] = *(const float4*)(a.part + prow * kD + d);
+  }
   const float sk = a.sink[h] * kLog2e;
   float M = sk;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, ml[(((int64_t)q * a.n_split + s) * Hpad + h) * 2]);
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s)
+    if (s < a.n_split) M = fmaxf(M, mls[s].x);
   float den = exp2f(sk - M);
-  float w[kMaxSplit];
-  for (int s = 0; s < a.n_split; ++s) {
-    const int64_t prow = ((int64_t)q * a.n_split + s) * Hpad + h;
-    w[s] = exp2f(ml[prow * 2] - M);
-    den += w[s] * ml[prow * 2 + 1];
+  float o[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < kMaxSplit; ++s) {
+    if (s < a.n_split) {
+      const float w = exp2f(mls[s].x - M);
+      den = fmaf(w, mls[s].y, den);
+      o[0] = fmaf(w, x[s].x, o[0]);
+      o[1] = fmaf(w, x[s].y, o[1]);
+      o[2] = fmaf(w, x[s].z, o[2]);
+      o[3] = fmaf(w, x[s].w, o[3]);
+    }
   }
   const float inv = 1.f / den;
-  const int d = threadIdx.x * 4;
-  float o[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < a.n_split; ++s) {
-    const int64_t prow = ((int64_t)q * a.n_split + s) * Hpad + h;
-    const float4 x = *(const float4*)(a.part + prow * kD + d);
-    o[0] = fmaf(w[s], x.x, o[0]);
-    o[1] = fmaf(w[s], x.y, o[1]);
-    o[2] = fmaf(w[s], x.z, o[2]);
-    o[3] = fmaf(w[s], x.w, o[3]);
-  }
   store4(a.out, a.out_dt, ((int64_t)q * a.H + h) * kD + d, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
 }
 
 // fp32 path: block = (query, head); all arithmetic in fp32.
+template <bool QBF16>
 __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const int q = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -300,11 +394,17 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   __shared__ float red[4 * kD];
   __shared__ float s_stat[4];
   const int n_idx = a.n_win + a.n_comp;
-  const int r = a.q_req[q];
-  const float* qrow = (const float*)a.q + ((int64_t)q * a.H + h) * kD;
+  const int r = a.req_mode == 1 ? q : (a.req_mode == 2 ? 0 : a.q_req[q]);
   float qv[8];
+  if constexpr (QBF16) {
+    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)q * a.H + h) * kD;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) qv[e] = qrow[8 * lane + e];
+    for (int e = 0; e < 8; ++e) qv[e] = bf16_bits_to_f32(qrow[8 * lane + e]);
+  } else {
+    const float* qrow = (const float*)a.q + ((int64_t)q * a.H + h) * kD;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[e] = qrow[8 * lane + e];
+  }
 
   float lmax = -INFINITY;
   for (int j = wave; j < n_idx; j += 4) {
@@ -354,6 +454,14 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 
 int plan_attn_split(int Q, int H, int n_idx, int q_dt) {
   if (q_dt == 0) return 1;
+  static const int forced = [] {
+    const char* e = getenv("CSA_ATTN_SPLIT");   // tuning override: fixed split count
+    return e ? atoi(e) : 0;
+  }();
+  if (forced > 0) {
+    const int n_tiles = (n_idx + kTile - 1) / kTile;
+    return forced < kMaxSplit ? (forced < n_tiles ? forced : n_tiles) : (kMaxSplit < n_tiles ? kMaxSplit : n_tiles);
+  }
   const int hchunks = (((H + 15) & ~15) + 63) / 64;
   const int n_tiles = (n_idx + kTile - 1) / kTile;
   const int blocks = Q * hchunks;
@@ -372,23 +480,35 @@ size_t attn_partial_bytes(int Q, int H, int n_idx) {
   return (size_t)Q * s * Hpad * (kD + 2) * sizeof(float);
 }
 
+bool attn_uses_matrix_cores(int q_dt, int win_fmt, int comp_fmt, int n_win, int n_comp) {
+  if (q_dt != 1) return false;
+  const bool w_ok = n_win == 0 || win_fmt == kRowBF16 || win_fmt == kRowFP8;
+  const bool c_ok = n_comp == 0 || comp_fmt == kRowBF16 || comp_fmt == kRowFP8;
+  return w_ok && c_ok;
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  const int n_idx = a.n_win + a.n_comp;
-  if (a.q_dt == 0) {
+  if (!attn_uses_matrix_cores(a.q_dt, a.win_fmt, a.comp_fmt, a.n_win, a.n_comp)) {
     ProfScope p("attn_f32", s);
-    hipLaunchKernelGGL(attn_f32_kernel, dim3((unsigned)a.Q, (unsigned)a.H), dim3(256), 0, s, a);
+    if (a.q_dt == 1) hipLaunchKernelGGL(attn_f32_kernel<true>, dim3((unsigned)a.Q, (unsigned)a.H), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(attn_f32_kernel<false>, dim3((unsigned)a.Q, (unsigned)a.H), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   const int Hpad = (a.H + 15) & ~15;
   const int hchunks = (Hpad + 63) / 64;
-  const int waves = Hpad >= 64 ? 4 : Hpad / 16;
+  // a source with no slots takes the other source's format (its loads are never issued)
+  const int wf = a.n_win > 0 ? a.win_fmt : a.comp_fmt;
+  const int cf = a.n_comp > 0 ? a.comp_fmt : wf;
   {
     ProfScope p("attn_bf16", s);
-    hipLaunchKernelGGL(attn_bf16_kernel, dim3((unsigned)(a.Q * a.n_split), (unsigned)hchunks), dim3(64 * waves), 0, s, a);
+    const dim3 grid((unsigned)(a.Q * a.n_split), (unsigned)hchunks);
+    if (wf == kRowFP8 && cf == kRowFP8) hipLaunchKernelGGL((attn_bf16_kernel<kRowFP8, kRowFP8>), grid, dim3(256), 0, s, a);
+    else if (wf == kRowFP8) hipLaunchKernelGGL((attn_bf16_kernel<kRowFP8, kRowBF16>), grid, dim3(256), 0, s, a);
+    else if (cf == kRowFP8) hipLaunchKernelGGL((attn_bf16_kernel<kRowBF16, kRowFP8>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<kRowBF16, kRowBF16>), grid, dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  (void)n_idx;
   ProfScope p("attn_combine", s);
   hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.Q * a.H)), dim3(128), 0, s, a);
   return hipGetLastError();

@@ -31,6 +31,12 @@ struct IndexerArgs {
   float* logits;              // [Q][ld]
   int64_t ld;
   uint32_t* hist;             // optional [Q][4096] coarse histogram of the written scores
+  // 0: q_req / n_vis arrays; 1: decode (request q, n_vis = clamp(ctx_len[q], 0, max_ctx)/4);
+  // 2: causal prefill of request 0 (n_vis = (pos0 + q + 1)/4)
+  int vis_mode;
+  const int32_t* ctx_len;
+  int64_t max_ctx;
+  int64_t pos0;
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
 
@@ -44,13 +50,21 @@ struct TopkArgs {
   int32_t* idx;
   int64_t ld_idx;
   uint32_t* hist;       // [Q][4096], filled by the indexer or by launch_topk_hist
-  uint32_t* counters;   // [Q][4], zero on entry
+  uint32_t* counters;   // [Q][8]: [0],[1] append cursors (zero on entry), [4..6] threshold record
   int32_t* sel;         // [Q][k]
   uint2* cand;          // [Q][cand_cap]
   int64_t cand_cap;
+  // single-block path only: 0 = n_vis array; 1 = decode (n_vis = ctx_len/4, also writes the ring
+  // window into idx[-128..-1]); 2 = causal prefill from pos0 (also writes the raw window)
+  int win_mode;
+  const int32_t* ctx_len;
+  int64_t max_ctx;
+  int64_t pos0;
 };
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
+hipError_t launch_topk_single(const TopkArgs& a, hipStream_t s);
+bool topk_single_ok(int64_t max_n_vis, int k);
 
 // Zero histograms / counters and write window indices (decode ring or causal prefill window).
 struct PrepArgs {
@@ -91,8 +105,11 @@ struct AttnArgs {
   int out_dt;                // 0 f32, 1 bf16
   float* part;               // split-K partials (may be null when n_split == 1)
   int n_split;               // chosen by plan_attn_split
+  int req_mode;              // 0: q_req array; 1: request = query (decode); 2: request 0 (prefill)
 };
 int plan_attn_split(int Q, int H, int n_idx, int q_dt);
+// true when the BF16 matrix-core kernel serves this call (bf16 q, BF16/FP8 rows); else the fp32 kernel
+bool attn_uses_matrix_cores(int q_dt, int win_fmt, int comp_fmt, int n_win, int n_comp);
 size_t attn_partial_bytes(int Q, int H, int n_idx);
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s);
 

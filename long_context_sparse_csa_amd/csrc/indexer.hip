@@ -15,6 +15,8 @@
 // 2-step reduce-scatter over the four lane groups leaves lane l with the full score of slot
 // 4*(l%16) + l/16.  Keys stream straight from HBM into VGPRs (no LDS): each lane loads 2 x 16 B per
 // key group, and each page is read exactly once.
+#include <cstdlib>
+
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -24,6 +26,9 @@ template <int HG, int KG>
 __device__ __forceinline__ v4f mma_fp8_scaled(const v8i& a, const v8i& b, int sa, int sb, v4f c) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, HG, sa, KG, sb);
 }
+
+// max(x, 0) in one v_med3_f32 (MFMA results are never signalling NaNs, so no canonicalisation)
+__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, INFINITY); }
 
 __device__ __forceinline__ v8i load_k_operand(const uint8_t* row, int g) {
   uint4 lo = *(const uint4*)(row + 16 * g);
@@ -35,8 +40,18 @@ __device__ __forceinline__ v8i load_k_operand(const uint8_t* row, int g) {
 }
 
 __device__ __forceinline__ int64_t visible_count(const IndexerArgs& a, int q, int& r) {
-  r = a.q_req[q];
-  int64_t nv = a.n_vis[q];
+  int64_t nv;
+  if (a.vis_mode == 1) {
+    r = q;
+    int64_t T = a.ctx_len[q];
+    nv = (T < 0 ? 0 : (T > a.max_ctx ? a.max_ctx : T)) / 4;
+  } else if (a.vis_mode == 2) {
+    r = 0;
+    nv = (a.pos0 + q + 1) / 4;
+  } else {
+    r = a.q_req[q];
+    nv = a.n_vis[q];
+  }
   int64_t lim = a.max_n_vis < (int64_t)a.max_pages * kPage ? a.max_n_vis : (int64_t)a.max_pages * kPage;
   nv = nv < 0 ? 0 : (nv > lim ? lim : nv);
   if (r < 0 || r >= a.n_req) nv = 0;
@@ -55,22 +70,23 @@ __device__ __forceinline__ void flush_hist(uint32_t* lhist, uint32_t* ghist, int
 }
 
 template <int NHG, bool HIST>
-__global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a, int pages_per_wg) {
+__global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a, int pages_per_wave) {
   const int q = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
 
-  const int64_t c_begin = (int64_t)blockIdx.x * pages_per_wg * kPage;
+  const int64_t c_begin = (int64_t)blockIdx.x * 4 * pages_per_wave * kPage;
   if (c_begin >= a.max_n_vis) return;
   int r;
   const int64_t nv = visible_count(a, q, r);
   if constexpr (HIST) {
     for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0u;
-    __syncthreads();
   }
 
-  // A operand: the query's indexer heads, resident in VGPRs for the whole block.
+  // A operand: the query's indexer heads, resident in VGPRs.  Loads are unconditional (clamped
+  // addresses, padded heads zeroed by select) so nothing waits before the first key page.
   const uint8_t* qb = (const uint8_t*)a.qI + (int64_t)q * a.HI * kDI;
   v8i qa[NHG];
   int qsc = 0;
@@ -78,69 +94,114 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a, int pag
 #pragma unroll
   for (int hg = 0; hg < NHG; ++hg) {
     const int h = 16 * hg + n;
-    if (h < a.HI) {
-      qa[hg] = load_k_operand(qb + h * kDI, g);
-      qsc |= (int)a.qI_scale[((int64_t)q * a.HI + h) * 4 + g] << (8 * hg);
-    } else {
-      qa[hg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      qsc |= 127 << (8 * hg);
-    }
+    const int hc = h < a.HI ? h : a.HI - 1;
+    const v8i v = load_k_operand(qb + hc * kDI, g);
+    const int sb = (int)a.qI_scale[((int64_t)q * a.HI + hc) * 4 + g];
+    const bool ok = h < a.HI;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qa[hg][e] = ok ? v[e] : 0;
+    qsc |= (ok ? sb : 127) << (8 * hg);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hh = 16 * hg + 4 * g + i;
-      wv[hg][i] = hh < a.HI ? a.w[(int64_t)q * a.HI + hh] : 0.f;
+      const float x = a.w[(int64_t)q * a.HI + (hh < a.HI ? hh : a.HI - 1)];
+      wv[hg][i] = hh < a.HI ? x : 0.f;
     }
   }
 
   const uint8_t* keys = (const uint8_t*)a.keys;
   const int32_t* pt = a.page_table + (int64_t)(r < 0 ? 0 : r) * a.max_pages;
   float* lrow = a.logits + (int64_t)q * a.ld;
+  const int64_t p_first = (c_begin >> 6) + (int64_t)wave * pages_per_wave;   // this wave's first page
+  const int64_t vis_pages = (nv + kPage - 1) / kPage;
 
-  for (int pl = wave; pl < pages_per_wg; pl += 4) {
-    const int64_t c0 = c_begin + (int64_t)pl * kPage;
-    if (c0 >= a.max_n_vis) break;
-    float score = -INFINITY;
-    if (c0 < nv) {
-      const int page = pt[c0 >> 6];
-      if ((unsigned)page < (unsigned)a.num_pages) {
-        const uint8_t* kp = keys + (int64_t)page * (kPage * kDI);
-        const int ksc = *(const int*)(a.kscale + (int64_t)page * 256 + 4 * lane);
-        v8i kb[4];
+  // page ids of this wave's pages, one per lane, then broadcast as needed
+  int my_pid = -1;
+  {
+    const int64_t pp = p_first + lane;
+    if (lane < pages_per_wave && pp < vis_pages) my_pid = pt[pp];
+  }
+
+  // key page p -> operands; invalid pages read page 0 (always mapped memory) and are masked later
+  auto page_ok = [&](int i) {
+    const int pid = __shfl(my_pid, i);
+    return (unsigned)pid < (unsigned)a.num_pages;
+  };
+  auto load_page = [&](int i, v8i* kb, int& ksc) {
+    int pid = __shfl(my_pid, i);
+    pid = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
+    const uint8_t* kp = keys + (int64_t)pid * (kPage * kDI);
+    ksc = *(const int*)(a.kscale + (int64_t)pid * 256 + 4 * lane);
 #pragma unroll
-        for (int kg = 0; kg < 4; ++kg) kb[kg] = load_k_operand(kp + (4 * n + kg) * kDI, g);
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
-        static_for<0, NHG>::run([&](auto HGc) {
-          constexpr int HG = decltype(HGc)::value;
-          static_for<0, 4>::run([&](auto KGc) {
-            constexpr int KG = decltype(KGc)::value;
-            v4f acc = mma_fp8_scaled<HG, KG>(qa[HG], kb[KG], qsc, ksc, v4f{0.f, 0.f, 0.f, 0.f});
-            float s = part[KG];
+    for (int kg = 0; kg < 4; ++kg) kb[kg] = load_k_operand(kp + (4 * n + kg) * kDI, g);
+  };
+
+  int n_pages = pages_per_wave;
+  {
+    const int64_t rem = (a.max_n_vis + kPage - 1) / kPage - p_first;
+    if (rem < n_pages) n_pages = rem < 0 ? 0 : (int)rem;
+  }
+
+  auto compute_page = [&](int i, const v8i* kb, int ksc) {
+    const int64_t c0 = (p_first + i) * kPage;
+    const bool live = c0 < nv && page_ok(i);
+    v4f acc[NHG][4];
+    static_for<0, NHG>::run([&](auto HGc) {
+      constexpr int HG = decltype(HGc)::value;
+      static_for<0, 4>::run([&](auto KGc) {
+        constexpr int KG = decltype(KGc)::value;
+        acc[HG][KG] = mma_fp8_scaled<HG, KG>(qa[HG], kb[KG], qsc, ksc, v4f{0.f, 0.f, 0.f, 0.f});
+      });
+    });
+    float part[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s = fmaf(wv[HG][i], fmaxf(acc[i], 0.f), s);
-            part[KG] = s;
-          });
-        });
-        // reduce-scatter over the 4 lane groups: lane (n, g) ends with the score of slot 4n+g
-        const bool b5 = (lane & 32) != 0;
-        float keep0 = b5 ? part[2] : part[0], keep1 = b5 ? part[3] : part[1];
-        const float send0 = b5 ? part[0] : part[2], send1 = b5 ? part[1] : part[3];
-        keep0 += __shfl_xor(send0, 32);
-        keep1 += __shfl_xor(send1, 32);
-        const bool b4 = (lane & 16) != 0;
-        const float keep = b4 ? keep1 : keep0, send = b4 ? keep0 : keep1;
-        score = keep + __shfl_xor(send, 16);
-      }
+    for (int kg = 0; kg < 4; ++kg) {
+      float sacc = 0.f;
+#pragma unroll
+      for (int hg = 0; hg < NHG; ++hg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sacc = fmaf(wv[hg][e], relu(acc[hg][kg][e]), sacc);
+      part[kg] = sacc;
     }
+    // reduce-scatter over the 4 lane groups: lane (n, g) ends with the score of slot 4n+g
+    const bool b5 = (lane & 32) != 0;
+    float keep0 = b5 ? part[2] : part[0], keep1 = b5 ? part[3] : part[1];
+    const float send0 = b5 ? part[0] : part[2], send1 = b5 ? part[1] : part[3];
+    keep0 += __shfl_xor(send0, 32);
+    keep1 += __shfl_xor(send1, 32);
+    const bool b4 = (lane & 16) != 0;
+    const float keep = b4 ? keep1 : keep0, send = b4 ? keep0 : keep1;
+    const float score = keep + __shfl_xor(send, 16);
     const int64_t c = c0 + 4 * n + g;
     if (c < a.max_n_vis) {
-      const float v = c < nv ? score : -INFINITY;
+      const float v = (live && c < nv) ? score : -INFINITY;
       lrow[c] = v;
       if constexpr (HIST) {
         if (c < nv) atomicAdd(&lhist[order_key(v) >> kHistShift], 1u);
       }
     }
+  };
+
+  // ping-pong page buffers: the next page's loads are in flight while the current one computes
+  v8i kb0[4], kb1[4];
+  int ksc0 = 0, ksc1 = 0;
+  if (n_pages > 0) load_page(0, kb0, ksc0);
+  for (int i = 0; i < n_pages; i += 2) {
+    if (i + 1 < n_pages) load_page(i + 1, kb1, ksc1);
+    compute_page(i, kb0, ksc0);
+    if (i + 1 < n_pages) {
+      if (i + 2 < n_pages) load_page(i + 2, kb0, ksc0);
+      compute_page(i + 1, kb1, ksc1);
+    }
   }
-  flush_hist<HIST>(lhist, a.hist + (int64_t)q * kHistBins, tid);
+  if constexpr (HIST) {
+    __syncthreads();
+    uint32_t* gh = a.hist + (int64_t)q * kHistBins;
+    for (int i = tid; i < kHistBins; i += 256) {
+      const uint32_t v = lhist[i];
+      if (v) atomicAdd(&gh[i], v);
+    }
+  }
 }
 
 // fp32 indexer (unquantised queries and keys): 4 threads per entry, heads split between them.
@@ -203,13 +264,19 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
     else hipLaunchKernelGGL(indexer_f32_kernel<false>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  const int pages_per_wg = 8;
-  dim3 grid((unsigned)((a.max_n_vis + pages_per_wg * kPage - 1) / (pages_per_wg * kPage)), (unsigned)a.Q);
+  // 4 pages (256 entries) per wave with one page in flight ahead; 4 waves per block
+  static const int ppw_env = [] {
+    const char* e = getenv("CSA_IDX_PAGES_PER_WAVE");   // tuning override
+    return e ? atoi(e) : 0;
+  }();
+  const int pages_per_wave = ppw_env > 0 && ppw_env <= 64 ? ppw_env : 4;
+  const int per_block = 4 * pages_per_wave * kPage;
+  dim3 grid((unsigned)((a.max_n_vis + per_block - 1) / per_block), (unsigned)a.Q);
   const int nhg = (a.HI + 15) / 16;
   ProfScope p("indexer_fp8", s);
 #define CSA_IDX_LAUNCH(N)                                                                              \
-  if (hist) hipLaunchKernelGGL((indexer_fp8_kernel<N, true>), grid, dim3(256), 0, s, a, pages_per_wg); \
-  else hipLaunchKernelGGL((indexer_fp8_kernel<N, false>), grid, dim3(256), 0, s, a, pages_per_wg);
+  if (hist) hipLaunchKernelGGL((indexer_fp8_kernel<N, true>), grid, dim3(256), 0, s, a, pages_per_wave); \
+  else hipLaunchKernelGGL((indexer_fp8_kernel<N, false>), grid, dim3(256), 0, s, a, pages_per_wave);
   switch (nhg) {
     case 1: CSA_IDX_LAUNCH(1) break;
     case 2: CSA_IDX_LAUNCH(2) break;

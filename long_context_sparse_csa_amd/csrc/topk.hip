@@ -7,12 +7,14 @@
 // Radix select on the order-preserving uint32 image of each fp32 score:
 //   1. a 4096-bin histogram of the top 12 key bits (fused into the indexer at decode, or
 //      topk_hist_kernel);
-//   2. topk_select_kernel, many blocks per query: every block finds the threshold bin b* from the
+//   2. topk_collect_kernel, many blocks per query: every block finds the threshold bin b* from the
 //      histogram, appends entries above b* to the selected list and entries in b* to a candidate
 //      list (wave-aggregated atomics);
-//   3. the last block of each query (a done-counter with device-scope fences; no block ever waits
-//      on another) resolves b* exactly: 10+10 more key bits, then, only if scores tie at the k-th
-//      place, the ascending-index digits; it merges both lists and bitonic-sorts the k indices.
+//   3. topk_finish_kernel, one block per query, resolves b* exactly: 10+10 more key bits, then,
+//      only if scores tie at the k-th place, the ascending-index digits; it emits the k indices in
+//      ascending order through an LDS bitmap and a popcount scan.
+// The two passes are separate launches: no block ever reads another block's plain stores within
+// a launch, so no device-scope fence (an L2 write-back on this part) is needed.
 #include "csa_device.h"
 #include "csa_internal.h"
 
@@ -24,6 +26,39 @@ constexpr int kCandLds = 4096;      // candidates resolved from LDS; more fall b
 __device__ __forceinline__ int64_t clamp_nv(const TopkArgs& a, int q) {
   int64_t nv = a.n_vis[q];
   return nv < 0 ? 0 : (nv > a.max_n_vis ? a.max_n_vis : nv);
+}
+
+// Visible count of row q: from the n_vis array, or derived (decode: ctx_len/4, prefill: (t+1)/4).
+__device__ __forceinline__ int64_t topk_row_count(const TopkArgs& a, int q) {
+  int64_t nv;
+  if (a.win_mode == 1) {
+    int64_t T = a.ctx_len[q];
+    T = T < 0 ? 0 : (T > a.max_ctx ? a.max_ctx : T);
+    nv = T / 4;
+  } else if (a.win_mode == 2) {
+    nv = (a.pos0 + q + 1) / 4;
+  } else {
+    nv = a.n_vis[q];
+  }
+  return nv < 0 ? 0 : (nv > a.max_n_vis ? a.max_n_vis : nv);
+}
+
+// Window part of the index list: decode ring slots of positions T-128..T-1, or prefill positions
+// t-127..t; -1 before position 0.  Written to columns [-128, 0) relative to a.idx.
+__device__ __forceinline__ void write_window(const TopkArgs& a, int q) {
+  const int j = threadIdx.x;
+  if (j >= kWin) return;
+  int32_t v;
+  if (a.win_mode == 1) {
+    int64_t T = a.ctx_len[q];
+    T = T < 0 ? 0 : (T > a.max_ctx ? a.max_ctx : T);
+    const int64_t p = T - kWin + j;
+    v = p >= 0 ? (int32_t)(p % kWin) : -1;
+  } else {
+    const int64_t p = a.pos0 + q - (kWin - 1) + j;
+    v = p >= 0 ? (int32_t)p : -1;
+  }
+  a.idx[(int64_t)q * a.ld_idx - kWin + j] = v;
 }
 
 // Exclusive prefix sum over the 256 threads of a block; *total receives the block sum.
@@ -48,7 +83,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return before + inc - v;
 }
 
-// Append `flag`ged values with one atomic per wave; returns this lane's slot (or -1).
+// Append `flag`ged values with one atomic per wave (an LDS counter); returns this lane's slot or -1.
 __device__ __forceinline__ int64_t wave_append(bool flag, uint32_t* counter) {
   const unsigned long long m = __ballot(flag);
   if (m == 0ull) return -1;
@@ -72,7 +107,16 @@ __global__ __launch_bounds__(256) void topk_hist_kernel(TopkArgs a) {
   __syncthreads();
   const int64_t end = begin + kSelChunk < nv ? begin + kSelChunk : nv;
   const float* row = a.logits + (int64_t)q * a.ld;
-  for (int64_t c = begin + tid; c < end; c += 256) atomicAdd(&lh[order_key(row[c]) >> kHistShift], 1u);
+  constexpr int kPer = kSelChunk / 256;
+  float vals[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t c = begin + j * 256 + tid;
+    vals[j] = row[c < end ? c : begin];
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (begin + j * 256 + tid < end) atomicAdd(&lh[order_key(vals[j]) >> kHistShift], 1u);
   __syncthreads();
   uint32_t* gh = a.hist + (int64_t)q * kHistBins;
   for (int i = tid; i < kHistBins; i += 256)
@@ -111,98 +155,154 @@ __device__ void find_digit(const uint32_t* bins, int nb, uint32_t need, uint32_t
   __syncthreads();
 }
 
-__global__ __launch_bounds__(256) void topk_select_kernel(TopkArgs a) {
+// Threshold bin b* of query q from its coarse histogram (descending scan, 16 bins per thread).
+// Returns b* (or -1 when the histogram holds fewer than k entries), the count above it and in it.
+__device__ void threshold_bin(const uint32_t* gh, uint32_t k, uint32_t* s_wave, int* s_digit,
+                              uint32_t* s_before, uint32_t* s_at) {
+  const int tid = threadIdx.x;
+  uint32_t c[16];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    c[j] = gh[kHistBins - 1 - (tid * 16 + j)];
+    sum += c[j];
+  }
+  if (tid == 0) { *s_digit = -1; *s_before = 0; *s_at = 0; }
+  __syncthreads();
+  uint32_t total;
+  const uint32_t pre = block_exclusive_scan(sum, s_wave, &total);
+  if (pre < k && pre + sum >= k) {
+    uint32_t acc = pre;
+    for (int j = 0; j < 16; ++j) {
+      if (acc + c[j] >= k) {
+        *s_digit = kHistBins - 1 - (tid * 16 + j);
+        *s_before = acc;
+        *s_at = c[j];
+        break;
+      }
+      acc += c[j];
+    }
+  }
+  __syncthreads();
+}
+
+// Pass 1 (many blocks per query): entries above the threshold bin go to `sel`, entries in it to
+// `cand`.  Block 0 of each query records (b*, count above, count in b*) for pass 2.
+__global__ __launch_bounds__(256) void topk_collect_kernel(TopkArgs a) {
   const int q = blockIdx.y, tid = threadIdx.x;
+  const int64_t nv = clamp_nv(a, q);
+  const int k = a.k;
+  if (nv <= k) return;
+  const int64_t begin = (int64_t)blockIdx.x * kSelChunk;
+  if (begin >= nv && blockIdx.x != 0) return;
+  __shared__ uint32_t s_wave[4];
+  __shared__ int s_digit;
+  __shared__ uint32_t s_before, s_at;
+  threshold_bin(a.hist + (int64_t)q * kHistBins, (uint32_t)k, s_wave, &s_digit, &s_before, &s_at);
+  const int bstar = s_digit;
+  const uint32_t above = s_before;
+  uint32_t* ctr = a.counters + (int64_t)q * 8;
+  if (blockIdx.x == 0 && tid == 0) {
+    ctr[4] = (uint32_t)bstar;
+    ctr[5] = above;
+    ctr[6] = s_at;
+  }
+  if (bstar < 0) return;
+  // compact into LDS first (LDS atomics), then reserve global space with one atomic per list
+  __shared__ int32_t l_above[2048];
+  __shared__ uint2 l_cand[kSelChunk];
+  __shared__ uint32_t s_na, s_nc, s_ga, s_gc;
+  if (tid == 0) { s_na = 0u; s_nc = 0u; }
+  __syncthreads();
+  const int64_t end = begin + kSelChunk < nv ? begin + kSelChunk : nv;
+  const float* row = a.logits + (int64_t)q * a.ld;
+  // all of this thread's scores are loaded before any is examined (one memory latency, not 16)
+  constexpr int kPer = kSelChunk / 256;
+  float vals[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t c = begin + j * 256 + tid;
+    vals[j] = row[c < end ? c : begin];
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t c = begin + j * 256 + tid;
+    const bool ok = c < end;
+    const uint32_t key = ok ? order_key(vals[j]) : 0u;
+    const int bin = (int)(key >> kHistShift);
+    const int64_t pa = wave_append(ok && bin > bstar, &s_na);
+    if (pa >= 0 && pa < 2048) l_above[pa] = (int32_t)c;
+    const int64_t pc = wave_append(ok && bin == bstar, &s_nc);
+    if (pc >= 0 && pc < kSelChunk) l_cand[pc] = make_uint2(key, (uint32_t)c);
+  }
+  __syncthreads();
+  const uint32_t na = s_na < 2048u ? s_na : 2048u, nc = s_nc < (uint32_t)kSelChunk ? s_nc : (uint32_t)kSelChunk;
+  if (tid == 0) {
+    s_ga = na ? atomicAdd(&ctr[0], na) : 0u;
+    s_gc = nc ? atomicAdd(&ctr[1], nc) : 0u;
+  }
+  __syncthreads();
+  uint2* cand = a.cand + (int64_t)q * a.cand_cap;
+  int32_t* sel = a.sel + (int64_t)q * k;
+  for (uint32_t i = tid; i < na; i += 256) {
+    const uint32_t p = s_ga + i;
+    if (p < above) sel[p] = l_above[i];
+  }
+  for (uint32_t i = tid; i < nc; i += 256) {
+    const int64_t p = (int64_t)s_gc + i;
+    if (p < a.cand_cap) cand[p] = l_cand[i];
+  }
+}
+
+constexpr int kBitmapWords = 8192;   // ascending emission through an LDS bitmap for n_vis <= 2^18
+
+// Pass 2 (one block per query): resolve the exact threshold inside b* (10+10 more key bits, then
+// the ascending index digits only if scores tie at the k-th place) and emit the k indices in
+// ascending order.
+__global__ __launch_bounds__(256) void topk_finish_kernel(TopkArgs a) {
+  const int q = blockIdx.x, tid = threadIdx.x;
   const int64_t nv = clamp_nv(a, q);
   const int k = a.k;
   int32_t* out = a.idx + (int64_t)q * a.ld_idx;
   if (nv <= k) {
-    if (blockIdx.x == 0)
-      for (int i = tid; i < k; i += 256) out[i] = i < nv ? i : -1;
+    for (int i = tid; i < k; i += 256) out[i] = i < nv ? i : -1;
     return;
   }
-
   __shared__ uint32_t s_wave[4];
   __shared__ int s_digit;
-  __shared__ uint32_t s_before, s_at;
-  __shared__ int s_last;
+  __shared__ uint32_t s_before, s_at, s_cursor;
   __shared__ uint32_t rh[2048];
   __shared__ uint2 lc[kCandLds];
-  __shared__ int sk[2048];
-  __shared__ uint32_t s_cursor;
-
-  // ---- 1. threshold bin b* from the coarse histogram (descending scan, 16 bins per thread)
-  const uint32_t* gh = a.hist + (int64_t)q * kHistBins;
-  {
-    uint32_t c[16];
-    uint32_t sum = 0;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      c[j] = gh[kHistBins - 1 - (tid * 16 + j)];
-      sum += c[j];
-    }
-    if (tid == 0) { s_digit = -1; s_before = 0; s_at = 0; }
-    __syncthreads();
-    uint32_t total;
-    const uint32_t pre = block_exclusive_scan(sum, s_wave, &total);
-    if (pre < (uint32_t)k && pre + sum >= (uint32_t)k) {
-      uint32_t acc = pre;
-      for (int j = 0; j < 16; ++j) {
-        if (acc + c[j] >= (uint32_t)k) {
-          s_digit = kHistBins - 1 - (tid * 16 + j);
-          s_before = acc;
-          s_at = c[j];
-          break;
-        }
-        acc += c[j];
-      }
-    }
-    __syncthreads();
-  }
-  const int bstar = s_digit;              // -1 only if the histogram does not cover k entries
-  const uint32_t above = s_before;
-  const uint32_t n_b = s_at;
-
-  // ---- 2. scan this block's chunk
-  uint2* cand = a.cand + (int64_t)q * a.cand_cap;
-  int32_t* sel = a.sel + (int64_t)q * k;
-  uint32_t* ctr = a.counters + (int64_t)q * 4;
-  const int64_t begin = (int64_t)blockIdx.x * kSelChunk;
-  const int64_t end = begin + kSelChunk < nv ? begin + kSelChunk : nv;
-  const float* row = a.logits + (int64_t)q * a.ld;
-  if (bstar >= 0) {
-    for (int64_t base = begin; base < end; base += 256) {
-      const int64_t c = base + tid;
-      const bool ok = c < end;
-      const uint32_t key = ok ? order_key(row[c]) : 0u;
-      const int bin = (int)(key >> kHistShift);
-      const int64_t pa = wave_append(ok && bin > bstar, &ctr[0]);
-      if (pa >= 0 && pa < (int64_t)above) sel[pa] = (int32_t)c;
-      const int64_t pc = wave_append(ok && bin == bstar, &ctr[1]);
-      if (pc >= 0 && pc < a.cand_cap) cand[pc] = make_uint2(key, (uint32_t)c);
-    }
-  }
-
-  // ---- 3. the last block of this query finishes the selection
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&ctr[2], 1u) == gridDim.x - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
+  __shared__ uint32_t bm[kBitmapWords];     // bitmap, or (n_vis > 2^18) the sort buffer
+  const uint32_t* ctr = a.counters + (int64_t)q * 8;
+  const int bstar = (int)ctr[4];
+  const uint32_t above = ctr[5];
+  const uint32_t n_b = ctr[6];
   if (bstar < 0) {   // inconsistent histogram: emit an empty (all -1) selection rather than guess
     for (int i = tid; i < k; i += 256) out[i] = -1;
     return;
   }
+  const uint2* cand = a.cand + (int64_t)q * a.cand_cap;
+  const int32_t* sel = a.sel + (int64_t)q * k;
   const uint32_t n_cand = n_b < (uint64_t)a.cand_cap ? n_b : (uint32_t)a.cand_cap;
   const bool in_lds = n_cand <= (uint32_t)kCandLds;
-  if (in_lds)
-    for (uint32_t i = tid; i < n_cand; i += 256) lc[i] = cand[i];
+  if (in_lds) {
+    constexpr int kPer = kCandLds / 256;
+    uint2 tmp[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t i = j * 256 + tid;
+      tmp[j] = cand[i < n_cand ? i : 0];
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t i = j * 256 + tid;
+      if (i < n_cand) lc[i] = tmp[j];
+    }
+  }
   const uint2* src = in_lds ? lc : cand;
   __syncthreads();
 
-  // key digits: bits [19,10] then [9,0]
   uint32_t prefix = (uint32_t)bstar;
   int pbits = 12;
   uint32_t need = (uint32_t)k - above;
@@ -226,7 +326,6 @@ __global__ __launch_bounds__(256) void topk_select_kernel(TopkArgs a) {
   }
   const uint32_t T = prefix;
 
-  // ties at the threshold key: keep the `need` lowest indices (3 ascending digits 11/11/10 bits)
   uint32_t idx_thr = 0xFFFFFFFFu;
   if (need < eq_at) {
     uint32_t ipre = 0;
@@ -253,7 +352,48 @@ __global__ __launch_bounds__(256) void topk_select_kernel(TopkArgs a) {
     idx_thr = ipre;
   }
 
-  // ---- merge: entries above b* (written by every block) + resolved candidates, then sort
+  if (nv <= (int64_t)kBitmapWords * 32) {
+    // ascending emission: set one bit per selected index, then a block-wide popcount scan
+    const int words = (int)((nv + 31) / 32);
+    for (int i = tid; i < words; i += 256) bm[i] = 0u;
+    __syncthreads();
+    {
+      int32_t cs[8];   // above < k <= 2048: at most 8 per thread, loaded together
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t i = j * 256 + tid;
+        cs[j] = sel[i < above ? i : 0];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j * 256 + tid < (int)above) atomicOr(&bm[cs[j] >> 5], 1u << (cs[j] & 31));
+    }
+    for (uint32_t i = tid; i < n_cand; i += 256) {
+      const uint2 x = src[i];
+      if (x.x > T || (x.x == T && x.y <= idx_thr)) atomicOr(&bm[x.y >> 5], 1u << (x.y & 31));
+    }
+    __syncthreads();
+    const int per = (words + 255) / 256;
+    const int w0 = tid * per, w1 = min(words, w0 + per);
+    uint32_t cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(bm[w]);
+    uint32_t total;
+    uint32_t pos = block_exclusive_scan(cnt, s_wave, &total);
+    for (int w = w0; w < w1; ++w) {
+      uint32_t b = bm[w];
+      while (b) {
+        const int bit = __ffs((int)b) - 1;
+        b &= b - 1u;
+        if (pos < (uint32_t)k) out[pos] = w * 32 + bit;
+        ++pos;
+      }
+    }
+    for (int i = (int)total + tid; i < k; i += 256) out[i] = -1;   // only if the histogram was short
+    return;
+  }
+
+  // n_vis > 2^18: merge into the sort buffer and bitonic-sort the k indices
+  int* sk = (int*)bm;
   int K2 = 1;
   while (K2 < k) K2 <<= 1;
   for (int i = tid; i < K2; i += 256) sk[i] = (i < (int)above) ? sel[i] : 0x7FFFFFFF;
@@ -282,6 +422,184 @@ __global__ __launch_bounds__(256) void topk_select_kernel(TopkArgs a) {
   for (int i = tid; i < k; i += 256) out[i] = sk[i] == 0x7FFFFFFF ? -1 : sk[i];
 }
 
+// ---- single-block selection for short rows (n_vis <= kSingleMax): one block per query keeps the
+// whole row in LDS, so no global histogram, no zeroed workspace and no second launch are needed.
+// Threshold search: 12-bit coarse histogram, then two 10-bit refinements of the order key; equal
+// keys at the threshold are resolved in index order during the emission scan.
+constexpr int kSingleThreads = 1024;
+constexpr int kSingleMax = 16384;
+constexpr int kSinglePer = kSingleMax / kSingleThreads;   // 16 entries per thread, in index order
+
+__device__ __forceinline__ uint32_t block1024_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t inc = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t t = __shfl_up(inc, off);
+    if (lane >= off) inc += t;
+  }
+  if (lane == 63) s_wave[wave] = inc;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < kSingleThreads / 64; ++w) {
+    const uint32_t x = s_wave[w];
+    before += w < wave ? x : 0u;
+    all += x;
+  }
+  __syncthreads();
+  *total = all;
+  return before + inc - v;
+}
+
+// Digit (scanning `nb` bins from the top) where the running count first reaches `need`.
+__device__ void single_find_desc(const uint32_t* bins, int nb, uint32_t need, uint32_t* s_wave, int* s_digit,
+                                 uint32_t* s_before, uint32_t* s_at) {
+  const int tid = threadIdx.x;
+  const int per = nb / kSingleThreads;   // 4 (4096 bins) or 1 (1024 bins)
+  uint32_t c[4] = {0u, 0u, 0u, 0u};
+  uint32_t sum = 0;
+  for (int j = 0; j < per; ++j) {
+    c[j] = bins[nb - 1 - (tid * per + j)];
+    sum += c[j];
+  }
+  uint32_t total;
+  const uint32_t pre = block1024_exclusive_scan(sum, s_wave, &total);
+  if (pre < need && pre + sum >= need) {
+    uint32_t acc = pre;
+    for (int j = 0; j < per; ++j) {
+      if (acc + c[j] >= need) {
+        *s_digit = nb - 1 - (tid * per + j);
+        *s_before = acc;
+        *s_at = c[j];
+        break;
+      }
+      acc += c[j];
+    }
+  }
+  __syncthreads();
+}
+
+// LDS position of entry c: one pad word per 16 entries, so a thread's 16 consecutive entries start
+// 17 words after its neighbour's and every wave-wide access touches 64 distinct banks
+__device__ __forceinline__ int kpos(int c) { return c + (c >> 4); }
+
+__global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a) {
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const int64_t nv = topk_row_count(a, q);
+  const int k = a.k;
+  int32_t* out = a.idx + (int64_t)q * a.ld_idx;
+  if (a.win_mode) write_window(a, q);
+  if (nv <= k) {
+    for (int i = tid; i < k; i += kSingleThreads) out[i] = i < nv ? i : -1;
+    return;
+  }
+  constexpr int kCopies = 4;                       // histogram copies, picked by wave, to spread atomics
+  __shared__ uint32_t keys[kSingleMax + kSingleMax / 16];
+  __shared__ uint32_t bins[kCopies * kHistBins];
+  __shared__ uint32_t s_wave[kSingleThreads / 64];
+  __shared__ int s_digit;
+  __shared__ uint32_t s_before, s_at;
+
+  const float* row = a.logits + (int64_t)q * a.ld;
+  const int c0 = tid * kSinglePer;          // this thread owns entries [c0, c0+16)
+  const int kp0 = kpos(c0);
+  uint32_t* hist = bins + (tid >> 6) % kCopies * kHistBins;
+  {
+    float v[kSinglePer];
+#pragma unroll
+    for (int j = 0; j < kSinglePer; j += 4) {
+      const int c = c0 + j;
+      // rows are 16-byte aligned and ld is a multiple of 4; the tail past n_vis is never counted
+      const float4 x = *(const float4*)(row + (c < nv ? c : 0));
+      v[j] = x.x; v[j + 1] = x.y; v[j + 2] = x.z; v[j + 3] = x.w;
+    }
+#pragma unroll
+    for (int j = 0; j < kSinglePer; ++j) keys[kp0 + j] = c0 + j < nv ? order_key(v[j]) : 0u;
+  }
+  for (int i = tid; i < kCopies * kHistBins; i += kSingleThreads) bins[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kSinglePer; ++j)
+    if (c0 + j < nv) atomicAdd(&hist[keys[kp0 + j] >> kHistShift], 1u);
+  __syncthreads();
+  for (int i = tid; i < kHistBins; i += kSingleThreads) {
+    uint32_t t = 0;
+#pragma unroll
+    for (int cpy = 0; cpy < kCopies; ++cpy) t += bins[cpy * kHistBins + i];
+    bins[i] = t;
+  }
+  if (tid == 0) { s_digit = 0; s_before = 0; s_at = 0; }
+  __syncthreads();
+  single_find_desc(bins, kHistBins, (uint32_t)k, s_wave, &s_digit, &s_before, &s_at);
+  uint32_t prefix = (uint32_t)s_digit;
+  int pbits = 12;
+  uint32_t need = (uint32_t)k - s_before;
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int i = tid; i < kCopies * 1024; i += kSingleThreads) bins[i] = 0u;
+    __syncthreads();
+    const int shift = 32 - pbits - 10;
+    uint32_t* h2 = bins + (tid >> 6) % kCopies * 1024;
+#pragma unroll
+    for (int j = 0; j < kSinglePer; ++j) {
+      const uint32_t key = keys[kp0 + j];
+      if (c0 + j < nv && (key >> (32 - pbits)) == prefix) atomicAdd(&h2[(key >> shift) & 1023u], 1u);
+    }
+    __syncthreads();
+    {
+      const int i = tid;   // 1024 bins, one per thread
+      uint32_t t = 0;
+#pragma unroll
+      for (int cpy = 0; cpy < kCopies; ++cpy) t += bins[cpy * 1024 + i];
+      __syncthreads();
+      bins[i] = t;
+    }
+    if (tid == 0) { s_digit = 0; s_before = 0; s_at = 0; }
+    __syncthreads();
+    single_find_desc(bins, 1024, need, s_wave, &s_digit, &s_before, &s_at);
+    prefix = (prefix << 10) | (uint32_t)s_digit;
+    pbits += 10;
+    need -= s_before;
+  }
+  const uint32_t T = prefix;     // exact k-th key; `need` of the entries equal to it are taken
+  uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int j = 0; j < kSinglePer; ++j) {
+    const uint32_t key = keys[kp0 + j];
+    const bool ok = c0 + j < nv;
+    n_gt += ok && key > T;
+    n_eq += ok && key == T;
+  }
+  uint32_t tot;
+  const uint32_t eq_before = block1024_exclusive_scan(n_eq, s_wave, &tot);
+  uint32_t take_eq = eq_before < need ? (need - eq_before < n_eq ? need - eq_before : n_eq) : 0u;
+  const uint32_t pos0 = block1024_exclusive_scan(n_gt + take_eq, s_wave, &tot);
+  uint32_t pos = pos0;
+#pragma unroll
+  for (int j = 0; j < kSinglePer; ++j) {
+    const uint32_t key = keys[kp0 + j];
+    const bool ok = c0 + j < nv;
+    bool take = ok && key > T;
+    if (ok && key == T && take_eq) {
+      take = true;
+      --take_eq;
+    }
+    if (take) {
+      if (pos < (uint32_t)k) out[pos] = c0 + j;
+      ++pos;
+    }
+  }
+  for (int i = (int)tot + tid; i < k; i += kSingleThreads) out[i] = -1;   // only on inconsistent input
+}
+
+hipError_t launch_topk_single(const TopkArgs& a, hipStream_t s) {
+  ProfScope p("topk_single", s);
+  hipLaunchKernelGGL(topk_single_kernel, dim3((unsigned)a.Q), dim3(kSingleThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+bool topk_single_ok(int64_t max_n_vis, int k) { return max_n_vis <= kSingleMax && k <= kSingleMax; }
+
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s) {
   if (a.max_n_vis <= a.k) return hipSuccess;
   dim3 grid((unsigned)((a.max_n_vis + kSelChunk - 1) / kSelChunk), (unsigned)a.Q);
@@ -293,9 +611,14 @@ hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s) {
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s) {
   int64_t chunks = (a.max_n_vis + kSelChunk - 1) / kSelChunk;
   if (chunks < 1) chunks = 1;
-  dim3 grid((unsigned)chunks, (unsigned)a.Q);
-  ProfScope p("topk_select", s);
-  hipLaunchKernelGGL(topk_select_kernel, grid, dim3(256), 0, s, a);
+  if (a.max_n_vis > a.k) {
+    ProfScope p("topk_collect", s);
+    hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)chunks, (unsigned)a.Q), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  ProfScope p("topk_finish", s);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.Q), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
