@@ -38,6 +38,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = enough to exceed 1 GB)")
+    p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                   help="after timing, run 3 plain device copies of MB megabytes (a known-size reference "
+                        "for hardware traffic counters)")
     return p.parse_args()
 
 
@@ -221,6 +224,15 @@ def main():
         o = torch_io.out_to_numpy(out)
         errs = [float(np.abs(o[qi] - ref[0]).max()) for qi, ref in outs.items()]
         res["parity_max_abs_vs_oracle"] = max(errs) if errs else None
+    if args.calibrate_copy > 0:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calibration_copy_bytes"] = n
     print(json.dumps(res), flush=True)
 
 

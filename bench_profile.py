@@ -1,0 +1,89 @@
+"""Turn rocprofv3 outputs of bench.py runs into the short summaries kept under profiles/.
+
+  python bench_profile.py trace   <kernel_trace.csv> <out.txt> "<command>"
+  python bench_profile.py traffic <fetch_counter_collection.csv> <write_counter_collection.csv>
+                                  <copy_bytes> <config> <out.json> "<command>"
+
+`traffic` scales the per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each csa kernel by what the same
+counters read for the plain device copy of `copy_bytes` bytes that bench.py --calibrate-copy runs
+(each copy reads and writes copy_bytes), and records the indexer kernel source hash so bench.py can
+tell whether the figure still describes the current kernel.
+"""
+import collections
+import csv
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def _short(name):
+    return name.split("(")[0].replace("void ", "").strip()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("indexer.hip", "csa_device.h"):
+        h.update(open(os.path.join(ROOT, "long_context_sparse_csa_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def trace(path, out, cmd):
+    rows = list(csv.DictReader(open(path)))
+    st = collections.OrderedDict()
+    for r in sorted(rows, key=lambda r: int(r["Start_Timestamp"])):
+        n = _short(r["Kernel_Name"])
+        st.setdefault(n, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [f"command: {cmd}", "", f"{'kernel':58s} {'calls':>6s} {'avg_us':>9s} {'med_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for n, v in st.items():
+        s = sorted(v)
+        lines.append(f"{n[:58]:58s} {len(v):6d} {sum(v)/len(v):9.2f} {s[len(s)//2]:9.2f} {s[0]:9.2f} {s[-1]:9.2f}")
+    open(out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def _counter(path, counter):
+    vals = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            vals[_short(r["Kernel_Name"])].append(float(r["Counter_Value"]))
+    return vals
+
+
+def traffic(fetch_csv, write_csv, copy_bytes, config, out, cmd):
+    copy_bytes = int(copy_bytes)
+    f = _counter(fetch_csv, "FETCH_SIZE")
+    w = _counter(write_csv, "WRITE_SIZE")
+    copy_k = [k for k in f if "copyBuffer" in k or "copy" in k.lower()]
+    # the calibration copies are the largest copy dispatches of the run
+    fc = max(max(f[k]) for k in copy_k)
+    wc = max(max(w[k]) for k in copy_k if k in w)
+    f_scale = copy_bytes / (fc * 1024.0)
+    w_scale = copy_bytes / (wc * 1024.0)
+    res = {"command": cmd, "config": config, "copy_bytes": copy_bytes,
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4), "kernels": {}}
+    for k in f:
+        if "csa::" not in k:
+            continue
+        fb = sum(f[k]) / len(f[k]) * 1024.0 * f_scale
+        wb = sum(w.get(k, [0.0])) / max(1, len(w.get(k, []))) * 1024.0 * w_scale
+        res["kernels"][k] = {"fetch_bytes": int(fb), "write_bytes": int(wb), "dispatches": len(f[k])}
+    idx = [k for k in res["kernels"] if "indexer_fp8" in k]
+    if idx:
+        k = idx[0]
+        res["bytes_per_launch"] = res["kernels"][k]["fetch_bytes"] + res["kernels"][k]["write_bytes"]
+        res["kernel"] = k
+    res["kernel_source_sha256_16"] = kernel_source_hash()
+    open(out, "w").write(json.dumps(res, indent=1) + "\n")
+    print(json.dumps(res, indent=1))
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "trace":
+        trace(*sys.argv[2:5])
+    elif sys.argv[1] == "traffic":
+        traffic(*sys.argv[2:8])
+    else:
+        sys.exit(__doc__)

@@ -19,6 +19,9 @@ HIPCC_FLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-shared",
     # keep the compiler from emitting packed-fp32 VALU ops (see the design notes)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the accumulation-register form made the compiler copy
+    # the 128 attention accumulators between register files on every tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
 

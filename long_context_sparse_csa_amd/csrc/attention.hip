@@ -30,6 +30,7 @@ namespace csa {
 
 constexpr int kTile = 32;
 constexpr int kKrStride = 528;   // bf16 per row of the row-major tile (1056 B, 16-B aligned)
+constexpr int kQStride = 520;    // bf16 per row of the staged q tile (1040 B)
 constexpr int kMaxSplit = 8;
 constexpr float kRescaleLog2 = 8.f;
 
@@ -192,7 +193,7 @@ __device__ __forceinline__ v4s lds_read_tr16(const uint16_t* p) {
 
 template <int WF, int CF>
 __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int nw = 4;   // all four waves gather; waves whose 16 heads are all padding skip compute
+  constexpr int nw = 4;   // all four waves gather and compute (padded heads have zero q)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -200,11 +201,10 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   const int Hpad = (a.H + 15) & ~15;
   const int h = blockIdx.y * 64 + wave * 16 + n;   // this lane's head
   const bool h_ok = h < a.H;
-  const bool computes = blockIdx.y * 64 + wave * 16 < Hpad;
 
   __shared__ __align__(16) uint16_t Kr[kTile * kKrStride];
+  __shared__ __align__(16) uint16_t Qs[64 * kQStride];   // this block's 64 heads of q, bf16
   __shared__ int32_t codes[kMaxSlots];
-  __shared__ int tile_valid;
 
   const int n_idx = a.n_win + a.n_comp;
   const int n_tiles = (n_idx + kTile - 1) / kTile;
@@ -218,13 +218,19 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   // every slot of this block's range resolved once: idx -> page -> row, all in parallel
   for (int i = tid; i < s_count; i += 64 * nw) codes[i] = slot_code(a, q, r, s_begin + i);
 
-  // q^T operand: lane holds q[h][32ks + 8g .. +8] for the 16 K-steps of 32 dims
-  v8bf qf[16];
+  // q of the block's heads staged in LDS (rows of padded heads are zero): keeps the 128
+  // accumulator registers per lane free of spills to the accumulation file
   {
-    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)q * a.H + (h_ok ? h : 0)) * kD;
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qf[ks] = h_ok ? *(const v8bf*)(qrow + 32 * ks + 8 * g) : v8bf{};
+    const int h_base = blockIdx.y * 64;
+    for (int i = tid; i < 64 * (kD / 8); i += 64 * nw) {
+      const int hh = i / (kD / 8), c = i % (kD / 8);
+      const int hg = h_base + hh;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (hg < a.H) v = *(const uint4*)((const uint16_t*)a.q + ((int64_t)q * a.H + hg) * kD + 8 * c);
+      *(uint4*)&Qs[hh * kQStride + 8 * c] = v;
+    }
   }
+  const uint16_t* qs_row = &Qs[(wave * 16 + n) * kQStride + 8 * g];
   __syncthreads();
 
   const float sc = a.softmax_scale * kLog2e;
@@ -252,10 +258,6 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   for (int t = t_begin; t < t_end; ++t) {
     const int base = (t - t_begin) * kTile;
     __syncthreads();   // the previous tile's readers are done with Kr
-    if (wave == 0) {
-      const unsigned long long b = __ballot(lane < kTile && codes[base + (lane & 31)] >= 0);
-      if (lane == 0) tile_valid = __popcll(b);
-    }
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       const int j = wave + nw * i;
@@ -265,7 +267,8 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
     }
     __syncthreads();
     if (t + 1 < t_end) fetch(t + 1);      // global latency of the next tile overlaps this compute
-    if (tile_valid == 0 || !computes) continue;
+    // every wave computes every tile (an all-invalid tile adds exact zeros): a single path through
+    // the loop lets the accumulators stay in the MFMA accumulation registers
 
     // S^T[key][head] for keys 0..15 (s0) and 16..31 (s1)
     v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = v4f{0.f, 0.f, 0.f, 0.f};
@@ -273,8 +276,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
     for (int ks = 0; ks < 16; ++ks) {
       const v8bf k0 = *(const v8bf*)&Kr[n * kKrStride + 32 * ks + 8 * g];
       const v8bf k1 = *(const v8bf*)&Kr[(16 + n) * kKrStride + 32 * ks + 8 * g];
-      s0 = mma_bf16(k0, qf[ks], s0);
-      s1 = mma_bf16(k1, qf[ks], s1);
+      const v8bf qk = *(const v8bf*)(qs_row + 32 * ks);
+      s0 = mma_bf16(k0, qk, s0);
+      s1 = mma_bf16(k1, qk, s1);
     }
     float sv[8];
 #pragma unroll
@@ -290,7 +294,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
     // lazy rescaling: the reference max moves only when a head's max grows by more than 2^8, so
     // the accumulators are touched rarely; p = 2^(S - m) then stays below 256
     const bool grow = tmax > m + kRescaleLog2;
-    if (__any(grow)) {
+    if (__builtin_expect(__any(grow), 0)) {
+      // an opaque statement keeps the compiler from if-converting this rare path into every tile
+      __asm__ volatile("" ::: "memory");
       const float m_new = grow ? tmax : m;
       const float alpha = exp2f(m - m_new);
       lsum *= alpha;
