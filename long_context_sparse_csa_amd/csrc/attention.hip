@@ -163,21 +163,25 @@ __device__ __forceinline__ RawChunk load_raw(const AttnArgs& a, int32_t code, in
 
 template <int WF, int CF>
 __device__ __forceinline__ void raw_to_bf16(const RawChunk& r, int32_t code, int dc, uint32_t* w) {
-  const int fmt = (code & 1) ? CF : WF;
-  if (code < 0) {
-    w[0] = w[1] = w[2] = w[3] = 0u;
-    return;
-  }
-  if ((WF == kRowFP8 || CF == kRowFP8) && fmt == kRowFP8 && dc < kNope / 8) {
+  // branch-free: the FP8 conversion is always computed and selected per lane (nope lanes of FP8
+  // rows take it, rope lanes and BF16 rows keep the raw bits, invalid slots become zero)
+  const bool ok = code >= 0;
+  uint32_t x[4] = {r.x.x, r.x.y, r.x.z, r.x.w};
+  if constexpr (WF == kRowFP8 || CF == kRowFP8) {
+    const int fmt = (code & 1) ? CF : WF;
+    const bool fp8_lane = fmt == kRowFP8 && dc < kNope / 8;
     float v[8];
     fp8x4_to_f32(r.x.x, v);
     fp8x4_to_f32(r.x.y, v + 4);
     const float sc = __uint_as_float(r.sc);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(v[2 * e] * sc, v[2 * e + 1] * sc);
-  } else {
-    w[0] = r.x.x; w[1] = r.x.y; w[2] = r.x.z; w[3] = r.x.w;
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t c = pack_bf16x2(v[2 * e] * sc, v[2 * e + 1] * sc);
+      x[e] = fp8_lane ? c : x[e];
+    }
   }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) w[e] = ok ? x[e] : 0u;
 }
 
 constexpr int kMaxSlots = 4096;
@@ -311,9 +315,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
       psum += p[e];
     }
     lsum += psum;
-    v8bf pf;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pf[e] = (__bf16)p[e];
+    const uint4 pw = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                pack_bf16x2(p[6], p[7]));
+    const v8bf pf = __builtin_bit_cast(v8bf, pw);
 
     // O^T[d][head] += V^T[d][slot] . P^T[slot][head]; V^T comes from the row-major tile through
     // the transposing LDS read (slot 8g+4mt+i <-> key 16mt+4g+i, matching P's register order)

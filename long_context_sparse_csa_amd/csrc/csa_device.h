@@ -42,8 +42,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);   // v_cvt_pk_bf16_f32: RNE
 }
 
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// Two floats -> two RNE bf16 in one dword (a single v_cvt_pk_bf16_f32), lo in bits [0,16).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const v2f x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf));
 }
 
 // 4 e4m3fn bytes of `w` -> 4 floats (hardware conversion, OCP e4m3fn on gfx950).
