@@ -6,18 +6,20 @@
 // "tilelang量化内核拆解…" (sparse_attn section) fixes the running-max start at the finite -1e30, so a
 // query with no valid slot outputs exact zeros.  K and V are the same 512-dim rows.
 //
-// BF16 matrix-core kernel (q bf16): a block owns one query, up to 64 heads (one wave per 16 heads)
-// and a contiguous range of 32-slot tiles.  All slots of the range are resolved to row addresses
-// up front; per tile the block gathers the 32 rows once (coalesced: one 16-B lane chunk per 8 dims
-// of a row, FP8 nope dequantised with its fp32 block scale) into one row-major bf16 LDS tile while
-// the next tile's rows are already in flight, and each wave runs 2x16 + 32
-// v_mfma_f32_16x16x32_bf16.  Computing S transposed (S^T = K.q^T) leaves each lane holding 8 scores
-// of its own head, which are exactly the P^T operand of O^T = V^T.P^T once the key order inside the
-// 32-wide K step is permuted (slot 8g+4mt+i <-> key 16mt+4g+i); the V^T operand is read from the
-// same row-major tile with gfx950's transposing LDS load (ds_read_b64_tr_b16), so no transposed
-// copy is ever written.  Softmax runs in base 2 with log2(e) folded into the scale.
-// Large queries-by-heads grids run unsplit; small ones split the slot range across blocks and a
-// combine kernel merges the (max, sum, acc) partials, sink included.
+// BF16 matrix-core kernel (q bf16): a block owns one query, up to 64 heads (four head groups of
+// 16) and a contiguous range of 32-slot tiles.  All slots of the range are resolved to row
+// addresses up front.  Per tile the four waves gather the 32 rows once (coalesced: one 16-B lane
+// chunk per 8 dims of a row, FP8 nope dequantised with its fp32 block scale) into one of two
+// row-major bf16 LDS tiles, so the next tile is dequantised while the matrix cores work on this
+// one.  Wave w computes the scores of head group w (q in registers) with v_mfma_f32_16x16x32_bf16,
+// computing S transposed (S^T = K.q^T) so each lane holds 8 scores of its own head; once the key
+// order inside the 32-wide K step is permuted (slot 8g+4mt+i <-> key 16mt+4g+i) these are exactly
+// the P^T operand of O^T = V^T.P^T.  The four P^T operands are exchanged through LDS and wave w
+// then accumulates output dims [128w, 128w+128) of all 64 heads, reading V^T from the same
+// row-major tile with gfx950's transposing LDS load (ds_read_b64_tr_b16): each V fragment feeds
+// four MFMAs and no transposed copy is ever written.  Softmax runs in base 2 with log2(e) folded
+// into the scale.  Large queries-by-heads grids run unsplit; small ones split the slot range
+// across blocks and a combine kernel merges the (max, sum, acc) partials, sink included.
 //
 // fp32 kernel (q f32): one block per (query, head); scores, softmax and P.V in fp32 with natural
 // exp, for bit-accurate-ish comparisons against the fp64 definition.
@@ -30,7 +32,6 @@ namespace csa {
 
 constexpr int kTile = 32;
 constexpr int kKrStride = 528;   // bf16 per row of the row-major tile (1056 B, 16-B aligned)
-constexpr int kQStride = 520;    // bf16 per row of the staged q tile (1040 B)
 constexpr int kMaxSplit = 8;
 constexpr float kRescaleLog2 = 8.f;
 
@@ -110,78 +111,120 @@ __device__ __forceinline__ void store4(void* out, int out_dt, int64_t off, float
   }
 }
 
-// Slot codes: -1 invalid, else (row << 3) | (fmt << 1) | src, src 0 = window, 1 = compressed.
-__device__ __forceinline__ int32_t slot_code(const AttnArgs& a, int q, int r, int s) {
-  if (r < 0 || r >= a.n_req || s >= a.n_win + a.n_comp) return -1;
-  const int v = a.idx[(int64_t)q * a.ld_idx + s];
-  if (v < 0) return -1;
-  if (s < a.n_win) {
-    if (a.win == nullptr || v >= a.win_rows_per_req) return -1;
-    return (int32_t)((((int64_t)r * a.win_rows_per_req + v) << 3) | (a.win_fmt << 1));
-  }
-  if (a.comp == nullptr || (int64_t)v >= (int64_t)a.max_pages * kPage) return -1;
-  const int pg = a.page_table[(int64_t)r * a.max_pages + (v >> 6)];
-  if ((unsigned)pg >= (unsigned)a.comp_num_pages) return -1;
-  return (int32_t)((((int64_t)pg * kPage + (v & 63)) << 3) | (a.comp_fmt << 1) | 1);
-}
+// Slot codes: the absolute address of the slot's row (rows are 16-B aligned) with bit 1 set for a
+// compressed row (the row format follows from that bit and the kernel's template arguments).
+// Invalid slots get the address of kZeroRow, which dequantises to zeros, so V needs no masking; a
+// 32-bit mask per tile marks the valid slots for the scores.
+typedef const __attribute__((address_space(1))) uint8_t* gbytes;
+constexpr uint64_t kCodeComp = 2;
+constexpr uint64_t kCodeAddrMask = ~(uint64_t)15;
 
-__device__ __forceinline__ const uint8_t* code_row(const AttnArgs& a, int32_t code) {
-  const int fmt = (code >> 1) & 3;
-  const int64_t row = (int64_t)(code >> 3);
-  return ((code & 1) ? a.comp : a.win) + row * row_bytes(fmt);
+__device__ __attribute__((aligned(256))) const uint8_t kZeroRow[1024] = {};
+
+// Slots [s_begin, s_begin + s_count) of query q are resolved into `codes` and `vmask`, four per
+// thread per pass: all index loads, then all page-table loads, are issued before any is used.
+// s_count is a whole number of tiles, and each wave covers 64 consecutive slots per pass.
+__device__ __forceinline__ void resolve_codes(const AttnArgs& a, int q, int r, int s_begin, int s_count,
+                                              uint64_t* codes, uint32_t* vmask, int tid) {
+  const int n_idx = a.n_win + a.n_comp;
+  const bool r_ok = r >= 0 && r < a.n_req;
+  const int rr = r_ok ? r : 0;
+  const bool has_win = a.win != nullptr;
+  const bool has_pt = a.comp != nullptr && a.page_table != nullptr && a.max_pages > 0;
+  const int64_t n_entries = (int64_t)a.max_pages * kPage;
+  const int32_t* idx_row = a.idx + (int64_t)q * a.ld_idx;
+  const uint64_t zero = (uint64_t)(uintptr_t)kZeroRow;
+  const int64_t win_rb = row_bytes(a.win_fmt), comp_rb = row_bytes(a.comp_fmt);
+  for (int b = 0; b < s_count; b += 4 * 256) {
+    int v[4], pg[4];
+    bool in[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = b + tid + 256 * k;
+      in[k] = r_ok && i < s_count && s_begin + i < n_idx;
+      v[k] = idx_row[in[k] ? s_begin + i : 0];
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) pg[k] = -1;
+    if (has_pt) {
+      const int32_t* pt_row = a.page_table + (int64_t)rr * a.max_pages;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int s = s_begin + b + tid + 256 * k;
+        const bool pv = in[k] && s >= a.n_win && v[k] >= 0 && v[k] < n_entries;
+        pg[k] = pt_row[pv ? (v[k] >> 6) : 0];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = b + tid + 256 * k;
+      const int s = s_begin + i;
+      uint64_t c = zero;
+      bool ok = false;
+      if (in[k] && v[k] >= 0) {
+        if (s < a.n_win) {
+          ok = has_win && v[k] < a.win_rows_per_req;
+          if (ok) c = (uint64_t)(uintptr_t)(a.win + ((int64_t)rr * a.win_rows_per_req + v[k]) * win_rb);
+        } else {
+          ok = has_pt && v[k] < n_entries && (unsigned)pg[k] < (unsigned)a.comp_num_pages;
+          if (ok) c = (uint64_t)(uintptr_t)(a.comp + ((int64_t)pg[k] * kPage + (v[k] & 63)) * comp_rb) | kCodeComp;
+        }
+      }
+      const uint64_t bal = __ballot(ok);
+      const int i0 = b + 256 * k + (tid & ~63);   // first slot of this wave's 64 (two tiles)
+      if (i < s_count) codes[i] = c;
+      if ((tid & 63) == 0 && i0 < s_count) {
+        vmask[i0 / kTile] = (uint32_t)bal;
+        if (i0 + kTile < s_count) vmask[i0 / kTile + 1] = (uint32_t)(bal >> 32);
+      }
+    }
+  }
 }
 
 // One 16-byte chunk per lane per row, loaded without branches so a whole tile of loads is in
 // flight at once.  Lane dc covers dims [8dc, 8dc+8): BF16 rows give the 8 values directly; FP8 rows
 // give 8 nope codes (the first 8 of 16 bytes loaded at 8dc; lanes >= 56 load 8 bf16 rope values)
-// plus the fp32 scale of their 64-dim block.  Invalid slots load from a valid dummy address and
-// are zeroed at conversion.
+// plus the fp32 scale of their 64-dim block.  `code` is wave-uniform, so the row address is scalar.
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 struct RawChunk {
-  uint4 x;
+  v4u x;
   uint32_t sc;
 };
 
 template <int WF, int CF>
-__device__ __forceinline__ RawChunk load_raw(const AttnArgs& a, int32_t code, int dc) {
-  const bool comp = (code & 1) != 0;
-  const int fmt = comp ? CF : WF;
-  const int64_t row = (int64_t)(code >> 3);
-  const uint8_t* base = comp ? a.comp : a.win;
-  const int rb = comp ? row_bytes(CF) : row_bytes(WF);
-  const uint8_t* rp = code >= 0 ? base + row * rb : (const uint8_t*)a.q;
+__device__ __forceinline__ RawChunk load_raw(uint64_t code, int dc) {
+  const int fmt = (code & kCodeComp) ? CF : WF;
+  const gbytes rp = (gbytes)(uintptr_t)(code & kCodeAddrMask);
   const int off = fmt == kRowFP8 ? (dc < kNope / 8 ? 8 * dc : 16 * dc - kNope) : 16 * dc;
   RawChunk r;
-  r.x = *(const uint4*)(rp + off);
+  r.x = *(const __attribute__((address_space(1))) v4u*)(rp + off);
   if constexpr (WF == kRowFP8 || CF == kRowFP8) {
     const int so = 576 + 4 * ((dc >> 3) < 6 ? (dc >> 3) : 6);
-    r.sc = *(const uint32_t*)(rp + so);
+    r.sc = *(const __attribute__((address_space(1))) uint32_t*)(rp + so);
   } else {
     r.sc = 0u;
   }
   return r;
 }
 
+// Raw chunk -> 8 bf16 (4 dwords).  Branch-free: the FP8 conversion is always computed and selected
+// per lane (nope lanes of FP8 rows take it; rope lanes and BF16 rows keep the raw bits).
 template <int WF, int CF>
-__device__ __forceinline__ void raw_to_bf16(const RawChunk& r, int32_t code, int dc, uint32_t* w) {
-  // branch-free: the FP8 conversion is always computed and selected per lane (nope lanes of FP8
-  // rows take it, rope lanes and BF16 rows keep the raw bits, invalid slots become zero)
-  const bool ok = code >= 0;
-  uint32_t x[4] = {r.x.x, r.x.y, r.x.z, r.x.w};
+__device__ __forceinline__ void raw_to_bf16(const RawChunk& r, uint64_t code, int dc, uint32_t* w) {
+  w[0] = r.x[0]; w[1] = r.x[1]; w[2] = r.x[2]; w[3] = r.x[3];
   if constexpr (WF == kRowFP8 || CF == kRowFP8) {
-    const int fmt = (code & 1) ? CF : WF;
+    const int fmt = (code & kCodeComp) ? CF : WF;
     const bool fp8_lane = fmt == kRowFP8 && dc < kNope / 8;
     float v[8];
-    fp8x4_to_f32(r.x.x, v);
-    fp8x4_to_f32(r.x.y, v + 4);
+    fp8x4_to_f32(r.x[0], v);
+    fp8x4_to_f32(r.x[1], v + 4);
     const float sc = __uint_as_float(r.sc);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t c = pack_bf16x2(v[2 * e] * sc, v[2 * e + 1] * sc);
-      x[e] = fp8_lane ? c : x[e];
+      w[e] = fp8_lane ? c : w[e];
     }
   }
-#pragma unroll
-  for (int e = 0; e < 4; ++e) w[e] = ok ? x[e] : 0u;
 }
 
 constexpr int kMaxSlots = 4096;
@@ -197,18 +240,20 @@ __device__ __forceinline__ v4s lds_read_tr16(const uint16_t* p) {
 
 template <int WF, int CF>
 __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int nw = 4;   // all four waves gather and compute (padded heads have zero q)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int q = blockIdx.x / a.n_split, split = blockIdx.x % a.n_split;
   const int Hpad = (a.H + 15) & ~15;
-  const int h = blockIdx.y * 64 + wave * 16 + n;   // this lane's head
-  const bool h_ok = h < a.H;
+  const int h_base = blockIdx.y * 64;
 
-  __shared__ __align__(16) uint16_t Kr[kTile * kKrStride];
-  __shared__ __align__(16) uint16_t Qs[64 * kQStride];   // this block's 64 heads of q, bf16
-  __shared__ int32_t codes[kMaxSlots];
+  __shared__ __align__(16) uint16_t Kr[2][kTile * kKrStride];   // double-buffered bf16 row tile
+  __shared__ __align__(16) uint4 Ps[4][64];                      // P^T operand of each head group
+  __shared__ __align__(16) int Fl[4];                            // head group rescaled this tile
+  __shared__ float As[64];                                       // its per-head rescale factors
+  __shared__ float Ms[64], Ls[64];
+  __shared__ __align__(16) uint64_t codes[kMaxSlots];
+  __shared__ uint32_t vmask[kMaxSlots / kTile];
 
   const int n_idx = a.n_win + a.n_comp;
   const int n_tiles = (n_idx + kTile - 1) / kTile;
@@ -219,76 +264,78 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   const int s_begin = t_begin * kTile;
   const int s_count = max(0, (t_end - t_begin) * kTile);
 
-  // every slot of this block's range resolved once: idx -> page -> row, all in parallel
-  for (int i = tid; i < s_count; i += 64 * nw) codes[i] = slot_code(a, q, r, s_begin + i);
-
-  // q of the block's heads staged in LDS (rows of padded heads are zero): keeps the 128
-  // accumulator registers per lane free of spills to the accumulation file
+  // q of this wave's 16 heads stays in registers as the QK B operand: lane (n, g) holds dims
+  // 32ks + 8g .. +7 of head h_base + 16 wave + n.  Padded heads read head 0's row; their results are
+  // never written.
+  v8bf qreg[16];
   {
-    const int h_base = blockIdx.y * 64;
-    for (int i = tid; i < 64 * (kD / 8); i += 64 * nw) {
-      const int hh = i / (kD / 8), c = i % (kD / 8);
-      const int hg = h_base + hh;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (hg < a.H) v = *(const uint4*)((const uint16_t*)a.q + ((int64_t)q * a.H + hg) * kD + 8 * c);
-      *(uint4*)&Qs[hh * kQStride + 8 * c] = v;
-    }
+    const int hq = h_base + 16 * wave + n;
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)q * a.H + (hq < a.H ? hq : 0)) * kD + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) qreg[ks] = *(const v8bf*)(qp + 32 * ks);
   }
-  const uint16_t* qs_row = &Qs[(wave * 16 + n) * kQStride + 8 * g];
+  resolve_codes(a, q, r, s_begin, s_count, codes, vmask, tid);
+  __syncthreads();
+
+  // wave w gathers rows 8w .. 8w+7 of a tile, one 16-B chunk (8 dims) per lane, so each load
+  // instruction reads a whole row contiguously; the raw chunks of the next tile and their
+  // (wave-uniform) codes sit in registers
+  constexpr int kRowsPerWave = kTile / 4;
+  RawChunk raw[kRowsPerWave];
+  uint64_t rc[kRowsPerWave];
+  auto fetch = [&](int t) {
+    const int base = (t - t_begin) * kTile + kRowsPerWave * wave;
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; i += 2) {
+      const uint4 c = *(const uint4*)&codes[base + i];
+      rc[i] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.y) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.x);
+      rc[i + 1] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.w) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.z);
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) raw[i] = load_raw<WF, CF>(rc[i], lane);
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      uint32_t w[4];
+      raw_to_bf16<WF, CF>(raw[i], rc[i], lane, w);
+      *(uint4*)&Kr[buf][(kRowsPerWave * wave + i) * kKrStride + 8 * lane] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  };
+  if (t_begin < t_end) {
+    fetch(t_begin);
+    stage(0);
+    if (t_begin + 1 < t_end) fetch(t_begin + 1);
+  }
   __syncthreads();
 
   const float sc = a.softmax_scale * kLog2e;
-  float m = kNegBig, lsum = 0.f;
-  v4f acc[32];
+  float m = kNegBig, lsum = 0.f;   // softmax state of head h_base + 16 wave + n
+  v4f acc[4][8];                   // O^T[128 wave + 16 dt + 4 g + i][h_base + 16 hg + n]
 #pragma unroll
-  for (int dt = 0; dt < 32; ++dt) acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // raw rows of the next tile live in registers: wave w gathers rows w, w+4, ..., one 16-B chunk
-  // (8 dims) per lane, so each load instruction reads whole rows contiguously
-  constexpr int kRowsPerWave = kTile / nw;
-  RawChunk raw[kRowsPerWave];
-  auto fetch = [&](int t) {
-    const int base = (t - t_begin) * kTile;
+  for (int hg = 0; hg < 4; ++hg)
 #pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) raw[i] = load_raw<WF, CF>(a, codes[base + wave + nw * i], lane);
-  };
-  if (t_begin < t_end) fetch(t_begin);
-
-  // transposed-read addresses of the P.V operand: source lane s = lane%16 of group g points at
-  // key row 4g + s/4 (slots 8g..8g+3) or 16 + 4g + s/4 (slots 8g+4..8g+7), dims 4*(s%4) .. +3
-  const uint16_t* tr_lo = &Kr[(4 * g + (n >> 2)) * kKrStride + 4 * (n & 3)];
-  const uint16_t* tr_hi = tr_lo + 16 * kKrStride;
+    for (int dt = 0; dt < 8; ++dt) acc[hg][dt] = v4f{0.f, 0.f, 0.f, 0.f};
 
   for (int t = t_begin; t < t_end; ++t) {
-    const int base = (t - t_begin) * kTile;
-    __syncthreads();   // the previous tile's readers are done with Kr
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      const int j = wave + nw * i;
-      uint32_t w[4];
-      raw_to_bf16<WF, CF>(raw[i], codes[base + j], lane, w);
-      *(uint4*)&Kr[j * kKrStride + 8 * lane] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-    __syncthreads();
-    if (t + 1 < t_end) fetch(t + 1);      // global latency of the next tile overlaps this compute
-    // every wave computes every tile (an all-invalid tile adds exact zeros): a single path through
-    // the loop lets the accumulators stay in the MFMA accumulation registers
+    const int buf = (t - t_begin) & 1;
+    const uint16_t* K = Kr[buf];
 
-    // S^T[key][head] for keys 0..15 (s0) and 16..31 (s1)
+    // S^T[key][head] of this wave's head group for keys 0..15 (s0) and 16..31 (s1)
     v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
-      const v8bf k0 = *(const v8bf*)&Kr[n * kKrStride + 32 * ks + 8 * g];
-      const v8bf k1 = *(const v8bf*)&Kr[(16 + n) * kKrStride + 32 * ks + 8 * g];
-      const v8bf qk = *(const v8bf*)(qs_row + 32 * ks);
-      s0 = mma_bf16(k0, qk, s0);
-      s1 = mma_bf16(k1, qk, s1);
+      const v8bf k0 = *(const v8bf*)&K[n * kKrStride + 32 * ks + 8 * g];
+      const v8bf k1 = *(const v8bf*)&K[(16 + n) * kKrStride + 32 * ks + 8 * g];
+      s0 = mma_bf16(k0, qreg[ks], s0);
+      s1 = mma_bf16(k1, qreg[ks], s1);
     }
+    const uint32_t vm = vmask[t - t_begin];
     float sv[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sv[i] = codes[base + 4 * g + i] >= 0 ? s0[i] * sc : -INFINITY;
-      sv[4 + i] = codes[base + 16 + 4 * g + i] >= 0 ? s1[i] * sc : -INFINITY;
+      sv[i] = (vm >> (4 * g + i)) & 1u ? s0[i] * sc : -INFINITY;
+      sv[4 + i] = (vm >> (16 + 4 * g + i)) & 1u ? s1[i] * sc : -INFINITY;
     }
     float tmax = sv[0];
 #pragma unroll
@@ -298,61 +345,103 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
     // lazy rescaling: the reference max moves only when a head's max grows by more than 2^8, so
     // the accumulators are touched rarely; p = 2^(S - m) then stays below 256
     const bool grow = tmax > m + kRescaleLog2;
+    float alpha = 1.f;
+    int fl = 0;
     if (__builtin_expect(__any(grow), 0)) {
       // an opaque statement keeps the compiler from if-converting this rare path into every tile
       __asm__ volatile("" ::: "memory");
       const float m_new = grow ? tmax : m;
-      const float alpha = exp2f(m - m_new);
+      alpha = exp2f(m - m_new);
       lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 32; ++dt) acc[dt] *= alpha;
       m = m_new;
+      fl = 1;
     }
     float p[8], psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      p[e] = exp2f(sv[e] - m);
+      p[e] = __builtin_amdgcn_exp2f(sv[e] - m);
       psum += p[e];
     }
     lsum += psum;
-    const uint4 pw = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+    // slot 8g+4mt+i of the K step <-> key 16mt+4g+i: these 8 values are exactly this lane's part of
+    // the P^T operand, for every wave that multiplies this head group
+    Ps[wave][lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                                 pack_bf16x2(p[6], p[7]));
-    const v8bf pf = __builtin_bit_cast(v8bf, pw);
+    if (g == 0) As[16 * wave + n] = alpha;
+    if (lane == 0) Fl[wave] = fl;
+    __syncthreads();
 
-    // O^T[d][head] += V^T[d][slot] . P^T[slot][head]; V^T comes from the row-major tile through
-    // the transposing LDS read (slot 8g+4mt+i <-> key 16mt+4g+i, matching P's register order)
+    const int4 f4 = *(const int4*)Fl;
+    if (__builtin_expect((f4.x | f4.y | f4.z | f4.w) != 0, 0)) {
+      __asm__ volatile("" ::: "memory");
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-      const v4s lo = lds_read_tr16(tr_lo + 16 * dt);
-      const v4s hi = lds_read_tr16(tr_hi + 16 * dt);
-      const v8bf vv = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[dt] = mma_bf16(vv, pf, acc[dt]);
+      for (int hg = 0; hg < 4; ++hg) {
+        const float al = As[16 * hg + n];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[hg][dt] *= al;
+      }
     }
+    v8bf pf[4];
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) pf[hg] = __builtin_bit_cast(v8bf, Ps[hg][lane]);
+
+    // O^T[d][head] += V^T[d][slot] . P^T[slot][head] over this wave's 128 dims, all head groups;
+    // V^T comes from the row-major tile through the transposing LDS read: source lane s of group g
+    // points at key row 4g + s/4 (slots 8g..8g+3) or 16 + 4g + s/4 (slots 8g+4..8g+7), dims
+    // 4(s%4) .. +3
+    const uint16_t* tr_lo = &K[(4 * g + (n >> 2)) * kKrStride + 4 * (n & 3) + 128 * wave];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const v4s lo = lds_read_tr16(tr_lo + 16 * dt);
+      const v4s hi = lds_read_tr16(tr_lo + 16 * kKrStride + 16 * dt);
+      const v8bf vv = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int hg = 0; hg < 4; ++hg) acc[hg][dt] = mma_bf16(vv, pf[hg], acc[hg][dt]);
+    }
+    // the next tile is dequantised into the other buffer while the matrix cores run.  Unconditional
+    // so that the conversion shares a basic block with the MFMAs: past the end it re-stages and
+    // re-fetches the block's last tile, whose codes are valid, into the buffer nobody reads again.
+    stage(buf ^ 1);
+    fetch(min(t + 2, t_end - 1));
+    __syncthreads();
   }
 
   float ltot = lsum + __shfl_xor(lsum, 16);
   ltot += __shfl_xor(ltot, 32);
-  if (a.n_split == 1) {
-    if (!h_ok) return;
-    const float sk = a.sink[h] * kLog2e;
-    const float M = fmaxf(m, sk);
-    const float f = exp2f(m - M);
-    const float inv = f / (ltot * f + exp2f(sk - M));
-    const int64_t ob = ((int64_t)q * a.H + h) * kD;
+  if (g == 0) {
+    Ms[16 * wave + n] = m;
+    Ls[16 * wave + n] = ltot;
+  }
+  __syncthreads();
+  const int dbase = 128 * wave + 4 * g;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt)
-      store4(a.out, a.out_dt, ob + 16 * dt + 4 * g, acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv,
-             acc[dt][3] * inv);
-  } else {
-    if (h >= Hpad) return;
-    const int64_t prow = ((int64_t)q * a.n_split + split) * Hpad + h;
-    float* pa = a.part + prow * kD;
+  for (int hg = 0; hg < 4; ++hg) {
+    const int h = h_base + 16 * hg + n;
+    const float mh = Ms[16 * hg + n], lh = Ls[16 * hg + n];
+    if (a.n_split == 1) {
+      const bool h_ok = h < a.H;
+      const float sk = a.sink[h_ok ? h : 0] * kLog2e;
+      const float M = fmaxf(mh, sk);
+      const float f = exp2f(mh - M);
+      const float inv = f / (lh * f + exp2f(sk - M));
+      if (h_ok) {
+        const int64_t ob = ((int64_t)q * a.H + h) * kD + dbase;
 #pragma unroll
-    for (int dt = 0; dt < 32; ++dt) *(float4*)(pa + 16 * dt + 4 * g) = make_float4(acc[dt][0], acc[dt][1], acc[dt][2], acc[dt][3]);
-    float* pml = a.part + (int64_t)a.Q * a.n_split * Hpad * kD + prow * 2;
-    if (g == 0) {
-      pml[0] = m;
-      pml[1] = ltot;
+        for (int dt = 0; dt < 8; ++dt)
+          store4(a.out, a.out_dt, ob + 16 * dt, acc[hg][dt][0] * inv, acc[hg][dt][1] * inv, acc[hg][dt][2] * inv,
+                 acc[hg][dt][3] * inv);
+      }
+    } else if (h_base + 16 * hg < Hpad) {
+      const int64_t prow = ((int64_t)q * a.n_split + split) * Hpad + h;
+      float* pa = a.part + prow * kD + dbase;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *(float4*)(pa + 16 * dt) = make_float4(acc[hg][dt][0], acc[hg][dt][1], acc[hg][dt][2], acc[hg][dt][3]);
+      if (hg == wave && g == 0) {
+        float* pml = a.part + (int64_t)a.Q * a.n_split * Hpad * kD + prow * 2;
+        pml[0] = mh;
+        pml[1] = lh;
+      }
     }
   }
 }
