@@ -243,7 +243,9 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int q = blockIdx.x / a.n_split, split = blockIdx.x % a.n_split;
+  // queries vary fastest in the block index, so with Q a multiple of 8 every split of a query (and
+  // the combine blocks that read its partials) runs on the same XCD and shares its L2
+  const int q = blockIdx.x % a.Q, split = blockIdx.x / a.Q;
   const int Hpad = (a.H + 15) & ~15;
   const int h_base = blockIdx.y * 64;
 
@@ -449,7 +451,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
 // Merge split-K partials: out = sum_s acc_s 2^(m_s-M) / (sum_s l_s 2^(m_s-M) + 2^(sink-M)).
 // Every partial is loaded up front (the split loop is unrolled to its maximum and predicated).
 __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
-  const int q = blockIdx.x / a.H, h = blockIdx.x % a.H;
+  const int q = blockIdx.x % a.Q, h = blockIdx.x / a.Q;
   const int Hpad = (a.H + 15) & ~15;
   const float* ml = a.part + (int64_t)a.Q * a.n_split * Hpad * kD;
   const int d = threadIdx.x * 4;

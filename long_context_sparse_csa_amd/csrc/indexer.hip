@@ -71,13 +71,13 @@ __device__ __forceinline__ void flush_hist(uint32_t* lhist, uint32_t* ghist, int
 
 template <int NHG, bool HIST>
 __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a, int pages_per_wave) {
-  const int q = blockIdx.y;
+  const int q = blockIdx.x;   // queries vary fastest: a row's blocks share one XCD (and its L2)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
 
-  const int64_t c_begin = (int64_t)blockIdx.x * 4 * pages_per_wave * kPage;
+  const int64_t c_begin = (int64_t)blockIdx.y * 4 * pages_per_wave * kPage;
   if (c_begin >= a.max_n_vis) return;
   int r;
   const int64_t nv = visible_count(a, q, r);
@@ -207,14 +207,14 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a, int pag
 // fp32 indexer (unquantised queries and keys): 4 threads per entry, heads split between them.
 template <bool HIST>
 __global__ __launch_bounds__(256) void indexer_f32_kernel(IndexerArgs a) {
-  const int q = blockIdx.y;
+  const int q = blockIdx.x;   // queries vary fastest: a row's blocks share one XCD (and its L2)
   const int tid = threadIdx.x;
   __shared__ float qs[64 * kDI];
   __shared__ float ks[kPage * (kDI + 1)];
   __shared__ float ws[64];
   __shared__ uint32_t lhist[HIST ? kHistBins : 1];
 
-  const int64_t c0 = (int64_t)blockIdx.x * kPage;
+  const int64_t c0 = (int64_t)blockIdx.y * kPage;
   if (c0 >= a.max_n_vis) return;
   int r;
   const int64_t nv = visible_count(a, q, r);
@@ -258,7 +258,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
   if (a.max_n_vis <= 0) return hipSuccess;
   const bool hist = a.hist != nullptr;
   if (a.dt == 0) {
-    dim3 grid((unsigned)((a.max_n_vis + kPage - 1) / kPage), (unsigned)a.Q);
+    dim3 grid((unsigned)a.Q, (unsigned)((a.max_n_vis + kPage - 1) / kPage));
     ProfScope p("indexer_f32", s);
     if (hist) hipLaunchKernelGGL(indexer_f32_kernel<true>, grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL(indexer_f32_kernel<false>, grid, dim3(256), 0, s, a);
@@ -271,7 +271,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
   }();
   const int pages_per_wave = ppw_env > 0 && ppw_env <= 64 ? ppw_env : 4;
   const int per_block = 4 * pages_per_wave * kPage;
-  dim3 grid((unsigned)((a.max_n_vis + per_block - 1) / per_block), (unsigned)a.Q);
+  dim3 grid((unsigned)a.Q, (unsigned)((a.max_n_vis + per_block - 1) / per_block));
   const int nhg = (a.HI + 15) / 16;
   ProfScope p("indexer_fp8", s);
 #define CSA_IDX_LAUNCH(N)                                                                              \

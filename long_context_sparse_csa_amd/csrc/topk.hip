@@ -423,69 +423,64 @@ __global__ __launch_bounds__(256) void topk_finish_kernel(TopkArgs a) {
 }
 
 // ---- single-block selection for short rows (n_vis <= kSingleMax): one block per query keeps the
-// whole row in LDS, so no global histogram, no zeroed workspace and no second launch are needed.
-// Threshold search: 12-bit coarse histogram, then two 10-bit refinements of the order key; equal
-// keys at the threshold are resolved in index order during the emission scan.
+// row in registers (16 consecutive entries per thread), so no global histogram, no zeroed
+// workspace and no second launch are needed.  Every barrier-separated phase costs on the order
+// of a microsecond at 16 waves, and a predicated LDS instruction costs its issue slot even when
+// few lanes are active, so the phases are few, the scans are done by a single wave and sparse
+// passes skip instructions no lane needs:
+//   1. three radix levels (12 + 10 + 10 key bits) give the exact k-th largest key T and how many
+//      keys equal to T are taken;
+//   2. one scan of the per-thread (greater, equal) counts, packed in one word, emits the k indices
+//      in ascending order, equal keys at T in index order.
 constexpr int kSingleThreads = 1024;
 constexpr int kSingleMax = 16384;
 constexpr int kSinglePer = kSingleMax / kSingleThreads;   // 16 entries per thread, in index order
 
-__device__ __forceinline__ uint32_t block1024_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t t = __shfl_up(inc, off);
-    if (lane >= off) inc += t;
-  }
-  if (lane == 63) s_wave[wave] = inc;
-  __syncthreads();
-  uint32_t before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kSingleThreads / 64; ++w) {
-    const uint32_t x = s_wave[w];
-    before += w < wave ? x : 0u;
-    all += x;
-  }
-  __syncthreads();
-  *total = all;
-  return before + inc - v;
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (VALU only, no LDS crossbar):
+// shifts by 1, 2, 4, 8 inside each row of 16 lanes, then row 0's and row 2's totals broadcast into
+// rows 1 and 3, then the total of rows 0-1 into rows 2 and 3.  Lanes without a source add 0.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
 }
 
-// Digit (scanning `nb` bins from the top) where the running count first reaches `need`.
-__device__ void single_find_desc(const uint32_t* bins, int nb, uint32_t need, uint32_t* s_wave, int* s_digit,
-                                 uint32_t* s_before, uint32_t* s_at) {
-  const int tid = threadIdx.x;
-  const int per = nb / kSingleThreads;   // 4 (4096 bins) or 1 (1024 bins)
-  uint32_t c[4] = {0u, 0u, 0u, 0u};
+// One wave scans `nb` bins (64 to 4096, a multiple of 256) from the top and finds the bin where
+// the running count first reaches `need` (1 <= need <= total): *digit, *before (count strictly
+// above it).  Two rounds, no serial search: per-lane sums and a shuffle scan pick the lane whose
+// range crosses `need`, then the 64 lanes read that range's bins one each and a second scan picks
+// the bin.  Lanes of other waves do nothing; the caller puts barriers around it.
+__device__ __forceinline__ void wave_find_desc(const uint32_t* bins, int nb, uint32_t need, uint32_t* digit,
+                                               uint32_t* before) {
+  const int lane = threadIdx.x & 63;
+  const int per = nb / 64;              // bins per lane: lane l owns [nb - per (l+1), nb - per l)
+  const int hi = nb - per * lane;       // exclusive top of this lane's range
   uint32_t sum = 0;
-  for (int j = 0; j < per; ++j) {
-    c[j] = bins[nb - 1 - (tid * per + j)];
-    sum += c[j];
+  for (int j = 0; j < per; j += 4) {
+    const uint4 c = *(const uint4*)&bins[hi - per + j];
+    sum += c.x + c.y + c.z + c.w;
   }
-  uint32_t total;
-  const uint32_t pre = block1024_exclusive_scan(sum, s_wave, &total);
-  if (pre < need && pre + sum >= need) {
-    uint32_t acc = pre;
-    for (int j = 0; j < per; ++j) {
-      if (acc + c[j] >= need) {
-        *s_digit = nb - 1 - (tid * per + j);
-        *s_before = acc;
-        *s_at = c[j];
-        break;
-      }
-      acc += c[j];
-    }
+  const uint32_t inc = wave_inclusive_scan(sum);
+  const uint64_t cross = __ballot(inc - sum < need && inc >= need);
+  const int x = cross ? __ffsll((long long)cross) - 1 : 63;
+  const uint32_t pre_x = __shfl(inc - sum, x);
+  const int top = nb - per * x;         // lane j looks at bin top - 1 - j
+  const uint32_t c = lane < per ? bins[top - 1 - lane] : 0u;
+  const uint32_t cinc = wave_inclusive_scan(c);
+  const uint64_t hit = __ballot(lane < per && pre_x + cinc >= need);
+  const int y = hit ? __ffsll((long long)hit) - 1 : 0;
+  if (lane == y) {
+    *digit = (uint32_t)(top - 1 - y);
+    *before = pre_x + cinc - c;
   }
-  __syncthreads();
 }
-
-// LDS position of entry c: one pad word per 16 entries, so a thread's 16 consecutive entries start
-// 17 words after its neighbour's and every wave-wide access touches 64 distinct banks
-__device__ __forceinline__ int kpos(int c) { return c + (c >> 4); }
 
 __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a) {
-  const int q = blockIdx.x, tid = threadIdx.x;
+  const int q = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
   const int64_t nv = topk_row_count(a, q);
   const int k = a.k;
   int32_t* out = a.idx + (int64_t)q * a.ld_idx;
@@ -494,93 +489,96 @@ __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a)
     for (int i = tid; i < k; i += kSingleThreads) out[i] = i < nv ? i : -1;
     return;
   }
-  constexpr int kCopies = 4;                       // histogram copies, picked by wave, to spread atomics
-  __shared__ uint32_t keys[kSingleMax + kSingleMax / 16];
-  __shared__ uint32_t bins[kCopies * kHistBins];
-  __shared__ uint32_t s_wave[kSingleThreads / 64];
-  __shared__ int s_digit;
-  __shared__ uint32_t s_before, s_at;
+  __shared__ __align__(16) uint32_t bins[kHistBins];
+  __shared__ __align__(16) uint32_t scan[kSingleThreads];
+  __shared__ uint32_t s_digit, s_before;
 
   const float* row = a.logits + (int64_t)q * a.ld;
   const int c0 = tid * kSinglePer;          // this thread owns entries [c0, c0+16)
-  const int kp0 = kpos(c0);
-  uint32_t* hist = bins + (tid >> 6) % kCopies * kHistBins;
+  uint32_t key[kSinglePer];
   {
     float v[kSinglePer];
 #pragma unroll
     for (int j = 0; j < kSinglePer; j += 4) {
       const int c = c0 + j;
-      // rows are 16-byte aligned and ld is a multiple of 4; the tail past n_vis is never counted
+      // rows are 16-byte aligned and ld is a multiple of 4; entries past n_vis are never counted
       const float4 x = *(const float4*)(row + (c < nv ? c : 0));
       v[j] = x.x; v[j + 1] = x.y; v[j + 2] = x.z; v[j + 3] = x.w;
     }
+    // cleared while the loads are in flight
+    for (int i = tid; i < kHistBins; i += kSingleThreads) bins[i] = 0u;
 #pragma unroll
-    for (int j = 0; j < kSinglePer; ++j) keys[kp0 + j] = c0 + j < nv ? order_key(v[j]) : 0u;
+    for (int j = 0; j < kSinglePer; ++j) key[j] = order_key(v[j]);   // entries past n_vis are never counted
   }
-  for (int i = tid; i < kCopies * kHistBins; i += kSingleThreads) bins[i] = 0u;
   __syncthreads();
+  // level 1: top 12 key bits of every entry (all lanes active: one LDS atomic instruction covers 64)
 #pragma unroll
   for (int j = 0; j < kSinglePer; ++j)
-    if (c0 + j < nv) atomicAdd(&hist[keys[kp0 + j] >> kHistShift], 1u);
+    if (c0 + j < nv) atomicAdd(&bins[key[j] >> kHistShift], 1u);
   __syncthreads();
-  for (int i = tid; i < kHistBins; i += kSingleThreads) {
-    uint32_t t = 0;
-#pragma unroll
-    for (int cpy = 0; cpy < kCopies; ++cpy) t += bins[cpy * kHistBins + i];
-    bins[i] = t;
-  }
-  if (tid == 0) { s_digit = 0; s_before = 0; s_at = 0; }
+  if (wave == 0) wave_find_desc(bins, kHistBins, (uint32_t)k, &s_digit, &s_before);
   __syncthreads();
-  single_find_desc(bins, kHistBins, (uint32_t)k, s_wave, &s_digit, &s_before, &s_at);
-  uint32_t prefix = (uint32_t)s_digit;
-  int pbits = 12;
+  uint32_t prefix = s_digit;
   uint32_t need = (uint32_t)k - s_before;
-  for (int pass = 0; pass < 2; ++pass) {
-    for (int i = tid; i < kCopies * 1024; i += kSingleThreads) bins[i] = 0u;
+  // levels 2 and 3: ten more key bits each, counting only entries with the current prefix
+#pragma unroll 1
+  for (int lvl = 0; lvl < 2; ++lvl) {
+    const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
+    for (int i = tid; i < 1024; i += kSingleThreads) bins[i] = 0u;
     __syncthreads();
-    const int shift = 32 - pbits - 10;
-    uint32_t* h2 = bins + (tid >> 6) % kCopies * 1024;
+    // few entries share the prefix: an atomic instruction is issued only where some lane needs it
 #pragma unroll
     for (int j = 0; j < kSinglePer; ++j) {
-      const uint32_t key = keys[kp0 + j];
-      if (c0 + j < nv && (key >> (32 - pbits)) == prefix) atomicAdd(&h2[(key >> shift) & 1023u], 1u);
+      const bool hit = c0 + j < nv && (key[j] >> (shift + 10)) == prefix;
+      if (__any(hit) && hit) atomicAdd(&bins[(key[j] >> shift) & 1023u], 1u);
     }
     __syncthreads();
-    {
-      const int i = tid;   // 1024 bins, one per thread
-      uint32_t t = 0;
-#pragma unroll
-      for (int cpy = 0; cpy < kCopies; ++cpy) t += bins[cpy * 1024 + i];
-      __syncthreads();
-      bins[i] = t;
-    }
-    if (tid == 0) { s_digit = 0; s_before = 0; s_at = 0; }
+    if (wave == 0) wave_find_desc(bins, 1024, need, &s_digit, &s_before);
     __syncthreads();
-    single_find_desc(bins, 1024, need, s_wave, &s_digit, &s_before, &s_at);
-    prefix = (prefix << 10) | (uint32_t)s_digit;
-    pbits += 10;
+    prefix = (prefix << 10) | s_digit;
     need -= s_before;
   }
-  const uint32_t T = prefix;     // exact k-th key; `need` of the entries equal to it are taken
+  const uint32_t T = prefix;   // exact k-th largest key; the first `need` entries equal to it are taken
   uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
   for (int j = 0; j < kSinglePer; ++j) {
-    const uint32_t key = keys[kp0 + j];
     const bool ok = c0 + j < nv;
-    n_gt += ok && key > T;
-    n_eq += ok && key == T;
+    n_gt += ok && key[j] > T;
+    n_eq += ok && key[j] == T;
   }
-  uint32_t tot;
-  const uint32_t eq_before = block1024_exclusive_scan(n_eq, s_wave, &tot);
+  // exclusive scan of (n_gt << 16 | n_eq) over threads by wave 0 (both totals stay below 2^16)
+  scan[tid] = (n_gt << 16) | n_eq;
+  __syncthreads();
+  if (wave == 0) {
+    const int lane = tid;
+    uint32_t c[16], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) {
+      const uint4 x = *(const uint4*)&scan[16 * lane + j];
+      c[j] = x.x; c[j + 1] = x.y; c[j + 2] = x.z; c[j + 3] = x.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) sum += c[j];
+    uint32_t run = wave_inclusive_scan(sum) - sum;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t x = c[j];
+      c[j] = run;
+      run += x;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; j += 4) *(uint4*)&scan[16 * lane + j] = make_uint4(c[j], c[j + 1], c[j + 2], c[j + 3]);
+  }
+  __syncthreads();
+  const uint32_t pre = scan[tid];
+  const uint32_t eq_before = pre & 0xFFFFu;
+  uint32_t pos = (pre >> 16) + (eq_before < need ? eq_before : need);
   uint32_t take_eq = eq_before < need ? (need - eq_before < n_eq ? need - eq_before : n_eq) : 0u;
-  const uint32_t pos0 = block1024_exclusive_scan(n_gt + take_eq, s_wave, &tot);
-  uint32_t pos = pos0;
 #pragma unroll
   for (int j = 0; j < kSinglePer; ++j) {
-    const uint32_t key = keys[kp0 + j];
     const bool ok = c0 + j < nv;
-    bool take = ok && key > T;
-    if (ok && key == T && take_eq) {
+    bool take = ok && key[j] > T;
+    if (ok && key[j] == T && take_eq) {
       take = true;
       --take_eq;
     }
@@ -589,7 +587,6 @@ __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a)
       ++pos;
     }
   }
-  for (int i = (int)tot + tid; i < k; i += kSingleThreads) out[i] = -1;   // only on inconsistent input
 }
 
 hipError_t launch_topk_single(const TopkArgs& a, hipStream_t s) {
