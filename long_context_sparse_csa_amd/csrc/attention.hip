@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   __shared__ __align__(16) uint4 Ps[4][64];                      // P^T operand of each head group
   __shared__ __align__(16) int Fl[4];                            // head group rescaled this tile
   __shared__ float As[64];                                       // its per-head rescale factors
-  __shared__ float Ms[64], Ls[64];
+  __shared__ float Ms[64], Ls[64], Xs[4][64];
   __shared__ __align__(16) uint64_t codes[kMaxSlots];
   __shared__ uint32_t vmask[kMaxSlots / kTile];
 
@@ -416,11 +416,11 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   }
   __syncthreads();
   const int dbase = 128 * wave + 4 * g;
+  if (a.n_split == 1) {
 #pragma unroll
-  for (int hg = 0; hg < 4; ++hg) {
-    const int h = h_base + 16 * hg + n;
-    const float mh = Ms[16 * hg + n], lh = Ls[16 * hg + n];
-    if (a.n_split == 1) {
+    for (int hg = 0; hg < 4; ++hg) {
+      const int h = h_base + 16 * hg + n;
+      const float mh = Ms[16 * hg + n], lh = Ls[16 * hg + n];
       const bool h_ok = h < a.H;
       const float sk = a.sink[h_ok ? h : 0] * kLog2e;
       const float M = fmaxf(mh, sk);
@@ -433,36 +433,60 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
           store4(a.out, a.out_dt, ob + 16 * dt, acc[hg][dt][0] * inv, acc[hg][dt][1] * inv, acc[hg][dt][2] * inv,
                  acc[hg][dt][3] * inv);
       }
-    } else if (h_base + 16 * hg < Hpad) {
-      const int64_t prow = ((int64_t)q * a.n_split + split) * Hpad + h;
-      float* pa = a.part + prow * kD + dbase;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        *(float4*)(pa + 16 * dt) = make_float4(acc[hg][dt][0], acc[hg][dt][1], acc[hg][dt][2], acc[hg][dt][3]);
-      if (hg == wave && g == 0) {
-        float* pml = a.part + (int64_t)a.Q * a.n_split * Hpad * kD + prow * 2;
-        pml[0] = mh;
-        pml[1] = lh;
-      }
     }
+    return;
+  }
+  // split-K partial of each head: m, l, amax = max |acc| over the 512 dims (fp32) and acc / amax
+  // as fp16 (|value| <= 1, so the only loss is fp16's 11-bit rounding relative to amax)
+#pragma unroll
+  for (int hg = 0; hg < 4; ++hg) {
+    float mx = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[hg][dt][i]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (g == 0) Xs[wave][16 * hg + n] = mx;
+  }
+  __syncthreads();
+  uint16_t* p16 = (uint16_t*)a.part;
+  float* pml = (float*)((uint8_t*)a.part + (size_t)a.Q * a.n_split * Hpad * kD * sizeof(uint16_t));
+#pragma unroll
+  for (int hg = 0; hg < 4; ++hg) {
+    if (h_base + 16 * hg >= Hpad) continue;
+    const int h = h_base + 16 * hg + n;
+    const int hl = 16 * hg + n;
+    const float amax = fmaxf(fmaxf(Xs[0][hl], Xs[1][hl]), fmaxf(Xs[2][hl], Xs[3][hl]));
+    const float f = amax > 0.f ? 1.f / amax : 0.f;
+    const int64_t prow = ((int64_t)q * a.n_split + split) * Hpad + h;
+    uint16_t* pa = p16 + prow * kD + dbase;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      *(uint2*)(pa + 16 * dt) = make_uint2(pack_f16x2(acc[hg][dt][0] * f, acc[hg][dt][1] * f),
+                                           pack_f16x2(acc[hg][dt][2] * f, acc[hg][dt][3] * f));
+    if (hg == wave && g == 0) *(float4*)(pml + prow * 4) = make_float4(Ms[hl], Ls[hl], amax, 0.f);
   }
 }
 
-// Merge split-K partials: out = sum_s acc_s 2^(m_s-M) / (sum_s l_s 2^(m_s-M) + 2^(sink-M)).
+// Merge split-K partials: out = sum_s 2^(m_s-M) amax_s o_s / (sum_s 2^(m_s-M) l_s + 2^(sink-M)),
+// o_s the fp16 partial (acc_s / amax_s).  Block = one query, four heads; thread = 8 dims of a head.
 // Every partial is loaded up front (the split loop is unrolled to its maximum and predicated).
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
-  const int q = blockIdx.x % a.Q, h = blockIdx.x / a.Q;
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  const int q = blockIdx.x % a.Q, h = (blockIdx.x / a.Q) * 4 + (threadIdx.x >> 6);
+  if (h >= a.H) return;
   const int Hpad = (a.H + 15) & ~15;
-  const float* ml = a.part + (int64_t)a.Q * a.n_split * Hpad * kD;
-  const int d = threadIdx.x * 4;
-  float2 mls[kMaxSplit];
-  float4 x[kMaxSplit];
+  const int d = (threadIdx.x & 63) * 8;
+  const uint16_t* p16 = (const uint16_t*)a.part;
+  const float* ml = (const float*)((const uint8_t*)a.part + (size_t)a.Q * a.n_split * Hpad * kD * sizeof(uint16_t));
+  float4 mls[kMaxSplit];
+  uint4 x[kMaxSplit];
 #pragma unroll
   for (int s = 0; s < kMaxSplit; ++s) {
     const int sc = s < a.n_split ? s : 0;
     const int64_t prow = ((int64_t)q * a.n_split + sc) * Hpad + h;
-    mls[s] = *(const float2*)(ml + prow * 2);
-    x[s] = *(const float4*)(a.part + prow * kD + d);
+    mls[s] = *(const float4*)(ml + prow * 4);
+    x[s] = *(const uint4*)(p16 + prow * kD + d);
   }
   const float sk = a.sink[h] * kLog2e;
   float M = sk;
@@ -470,20 +494,26 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
   for (int s = 0; s < kMaxSplit; ++s)
     if (s < a.n_split) M = fmaxf(M, mls[s].x);
   float den = exp2f(sk - M);
-  float o[4] = {0.f, 0.f, 0.f, 0.f};
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < kMaxSplit; ++s) {
     if (s < a.n_split) {
       const float w = exp2f(mls[s].x - M);
       den = fmaf(w, mls[s].y, den);
-      o[0] = fmaf(w, x[s].x, o[0]);
-      o[1] = fmaf(w, x[s].y, o[1]);
-      o[2] = fmaf(w, x[s].z, o[2]);
-      o[3] = fmaf(w, x[s].w, o[3]);
+      const float wa = w * mls[s].z;
+      const uint32_t xs[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const v2f v = unpack_f16x2(xs[e]);
+        o[2 * e] = fmaf(wa, v[0], o[2 * e]);
+        o[2 * e + 1] = fmaf(wa, v[1], o[2 * e + 1]);
+      }
     }
   }
   const float inv = 1.f / den;
-  store4(a.out, a.out_dt, ((int64_t)q * a.H + h) * kD + d, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+  const int64_t ob = ((int64_t)q * a.H + h) * kD + d;
+  store4(a.out, a.out_dt, ob, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
+  store4(a.out, a.out_dt, ob + 4, o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
 }
 
 // fp32 path: block = (query, head); all arithmetic in fp32.
@@ -578,7 +608,7 @@ size_t attn_partial_bytes(int Q, int H, int n_idx) {
   const int s = plan_attn_split(Q, H, n_idx, 1);
   if (s <= 1) return 0;
   const size_t Hpad = (size_t)((H + 15) & ~15);
-  return (size_t)Q * s * Hpad * (kD + 2) * sizeof(float);
+  return (size_t)Q * s * Hpad * (kD * sizeof(uint16_t) + 4 * sizeof(float));   // fp16 rows + (m, l, amax)
 }
 
 bool attn_uses_matrix_cores(int q_dt, int win_fmt, int comp_fmt, int n_win, int n_comp) {
@@ -611,7 +641,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   ProfScope p("attn_combine", s);
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.Q * a.H)), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.Q * ((a.H + 3) / 4))), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -50,6 +50,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2bf));
 }
 
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// Two floats -> two RNE fp16 in one dword, lo in bits [0,16); and back.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  const v2f x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, v2h));
+}
+__device__ __forceinline__ v2f unpack_f16x2(uint32_t w) {
+  return __builtin_convertvector(__builtin_bit_cast(v2h, w), v2f);
+}
+
 // 4 e4m3fn bytes of `w` -> 4 floats (hardware conversion, OCP e4m3fn on gfx950).
 __device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
   v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
