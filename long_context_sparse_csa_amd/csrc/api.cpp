@@ -76,6 +76,7 @@ struct PathWs {
   int64_t ld;
   TopkWs tk;
   float* part;
+  int32_t* rows;     // [rows][k] compressed KV rows of the selection (single-block top-k only)
 };
 
 PathWs carve_path(Carver& c, int32_t rows, int32_t H, int64_t max_n_vis, int32_t k) {
@@ -87,6 +88,7 @@ PathWs carve_path(Carver& c, int32_t rows, int32_t H, int64_t max_n_vis, int32_t
   w.logits = c.take<float>((size_t)rows * (size_t)w.ld * 4);
   w.tk = carve_topk(c, rows, max_n_vis, k);
   w.part = c.take<float>(csa::attn_partial_bytes(rows, H, kWin + k));
+  w.rows = c.take<int32_t>((size_t)rows * k * 4);
   return w;
 }
 
@@ -356,6 +358,12 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   t.idx = idx + kWin; t.ld_idx = ld_idx; t.hist = pw.tk.hist; t.counters = pw.tk.counters; t.sel = pw.tk.sel;
   t.cand = pw.tk.cand; t.cand_cap = max_n_vis > 0 ? max_n_vis : 1;
   t.win_mode = single ? mode : 0; t.ctx_len = ctx_len; t.max_ctx = max_ctx; t.pos0 = pos0;
+  if (single) {
+    // the selection also resolves its rows through the page table, which it loads while the
+    // scores load, so the attention prologue saves one dependent round trip
+    t.rows = pw.rows; t.ld_rows = k; t.page_table = comp->page_table; t.max_pages = comp->max_pages;
+    t.num_pages = comp->num_pages;
+  }
   CSA_HIP(single ? csa::launch_topk_single(t, stream) : csa::launch_topk_select(t, stream));
 
   csa::AttnArgs a{};
@@ -368,6 +376,7 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   a.n_split = csa::attn_uses_matrix_cores(q_dt, win_fmt, comp->fmt, kWin, k) ? csa::plan_attn_split(rows, H, kWin + k, q_dt) : 1;
   a.part = pw.part;
   a.req_mode = mode;
+  if (single) { a.rows = pw.rows; a.ld_rows = k; }
   return hip_status(csa::launch_attention(a, stream));
 }
 

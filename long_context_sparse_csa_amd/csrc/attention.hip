@@ -133,6 +133,8 @@ __device__ __forceinline__ void resolve_codes(const AttnArgs& a, int q, int r, i
   const bool has_pt = a.comp != nullptr && a.page_table != nullptr && a.max_pages > 0;
   const int64_t n_entries = (int64_t)a.max_pages * kPage;
   const int32_t* idx_row = a.idx + (int64_t)q * a.ld_idx;
+  const int32_t* rows_row = a.rows ? a.rows + (int64_t)q * a.ld_rows - a.n_win : nullptr;
+  const bool rows_in = a.rows != nullptr && a.comp != nullptr;   // compressed rows arrive resolved
   const uint64_t zero = (uint64_t)(uintptr_t)kZeroRow;
   const int64_t win_rb = row_bytes(a.win_fmt), comp_rb = row_bytes(a.comp_fmt);
   for (int b = 0; b < s_count; b += 4 * 256) {
@@ -142,11 +144,12 @@ __device__ __forceinline__ void resolve_codes(const AttnArgs& a, int q, int r, i
     for (int k = 0; k < 4; ++k) {
       const int i = b + tid + 256 * k;
       in[k] = r_ok && i < s_count && s_begin + i < n_idx;
-      v[k] = idx_row[in[k] ? s_begin + i : 0];
+      const int s = in[k] ? s_begin + i : 0;
+      v[k] = (rows_in && s >= a.n_win) ? rows_row[s] : idx_row[s];
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) pg[k] = -1;
-    if (has_pt) {
+    if (has_pt && !rows_in) {
       const int32_t* pt_row = a.page_table + (int64_t)rr * a.max_pages;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -165,6 +168,9 @@ __device__ __forceinline__ void resolve_codes(const AttnArgs& a, int q, int r, i
         if (s < a.n_win) {
           ok = has_win && v[k] < a.win_rows_per_req;
           if (ok) c = (uint64_t)(uintptr_t)(a.win + ((int64_t)rr * a.win_rows_per_req + v[k]) * win_rb);
+        } else if (rows_in) {
+          ok = (int64_t)v[k] < (int64_t)a.comp_num_pages * kPage;
+          if (ok) c = (uint64_t)(uintptr_t)(a.comp + (int64_t)v[k] * comp_rb) | kCodeComp;
         } else {
           ok = has_pt && v[k] < n_entries && (unsigned)pg[k] < (unsigned)a.comp_num_pages;
           if (ok) c = (uint64_t)(uintptr_t)(a.comp + ((int64_t)pg[k] * kPage + (v[k] & 63)) * comp_rb) | kCodeComp;
@@ -416,24 +422,52 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   }
   __syncthreads();
   const int dbase = 128 * wave + 4 * g;
+  // 16-bit output rows (bf16 results, fp16 partials) are staged in the idle row tiles, 1056 B per
+  // head, so that every wave then stores whole 1 KB rows with one instruction each
+  constexpr int kStage = kKrStride;
+  uint16_t* stg = &Kr[0][0];
+  static_assert(64 * kStage <= 2 * kTile * kKrStride, "staging fits the two row tiles");
+  auto store_rows = [&](uint16_t* base, int64_t row_stride, int nrows) {
+    // wave w writes staged rows 16w .. 16w+15 (those below nrows) to base + row * row_stride
+    for (int i = 0; i < 16; ++i) {
+      const int rr = 16 * wave + i;
+      if (rr < nrows) *(uint4*)(base + rr * row_stride + 8 * lane) = *(const uint4*)&stg[rr * kStage + 8 * lane];
+    }
+  };
   if (a.n_split == 1) {
+    float inv[4];
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg) {
       const int h = h_base + 16 * hg + n;
       const float mh = Ms[16 * hg + n], lh = Ls[16 * hg + n];
-      const bool h_ok = h < a.H;
-      const float sk = a.sink[h_ok ? h : 0] * kLog2e;
+      const float sk = a.sink[h < a.H ? h : 0] * kLog2e;
       const float M = fmaxf(mh, sk);
       const float f = exp2f(mh - M);
-      const float inv = f / (lh * f + exp2f(sk - M));
-      if (h_ok) {
+      inv[hg] = f / (lh * f + exp2f(sk - M));
+    }
+    const int nrows = min(64, a.H - h_base);
+    if (a.out_dt == 0) {
+#pragma unroll
+      for (int hg = 0; hg < 4; ++hg) {
+        const int h = h_base + 16 * hg + n;
+        if (h >= a.H) continue;
         const int64_t ob = ((int64_t)q * a.H + h) * kD + dbase;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt)
-          store4(a.out, a.out_dt, ob + 16 * dt, acc[hg][dt][0] * inv, acc[hg][dt][1] * inv, acc[hg][dt][2] * inv,
-                 acc[hg][dt][3] * inv);
+          store4(a.out, 0, ob + 16 * dt, acc[hg][dt][0] * inv[hg], acc[hg][dt][1] * inv[hg], acc[hg][dt][2] * inv[hg],
+                 acc[hg][dt][3] * inv[hg]);
       }
+      return;
     }
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg)
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *(uint2*)&stg[(16 * hg + n) * kStage + dbase + 16 * dt] =
+            make_uint2(pack_bf16x2(acc[hg][dt][0] * inv[hg], acc[hg][dt][1] * inv[hg]),
+                       pack_bf16x2(acc[hg][dt][2] * inv[hg], acc[hg][dt][3] * inv[hg]));
+    __syncthreads();
+    store_rows((uint16_t*)a.out + ((int64_t)q * a.H + h_base) * kD, kD, nrows);
     return;
   }
   // split-K partial of each head: m, l, amax = max |acc| over the 512 dims (fp32) and acc / amax
@@ -450,23 +484,22 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
     if (g == 0) Xs[wave][16 * hg + n] = mx;
   }
   __syncthreads();
-  uint16_t* p16 = (uint16_t*)a.part;
+  const int64_t prow0 = ((int64_t)q * a.n_split + split) * Hpad + h_base;   // partial row of head h_base
   float* pml = (float*)((uint8_t*)a.part + (size_t)a.Q * a.n_split * Hpad * kD * sizeof(uint16_t));
 #pragma unroll
   for (int hg = 0; hg < 4; ++hg) {
-    if (h_base + 16 * hg >= Hpad) continue;
-    const int h = h_base + 16 * hg + n;
     const int hl = 16 * hg + n;
     const float amax = fmaxf(fmaxf(Xs[0][hl], Xs[1][hl]), fmaxf(Xs[2][hl], Xs[3][hl]));
     const float f = amax > 0.f ? 1.f / amax : 0.f;
-    const int64_t prow = ((int64_t)q * a.n_split + split) * Hpad + h;
-    uint16_t* pa = p16 + prow * kD + dbase;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
-      *(uint2*)(pa + 16 * dt) = make_uint2(pack_f16x2(acc[hg][dt][0] * f, acc[hg][dt][1] * f),
-                                           pack_f16x2(acc[hg][dt][2] * f, acc[hg][dt][3] * f));
-    if (hg == wave && g == 0) *(float4*)(pml + prow * 4) = make_float4(Ms[hl], Ls[hl], amax, 0.f);
+      *(uint2*)&stg[hl * kStage + dbase + 16 * dt] = make_uint2(pack_f16x2(acc[hg][dt][0] * f, acc[hg][dt][1] * f),
+                                                              pack_f16x2(acc[hg][dt][2] * f, acc[hg][dt][3] * f));
+    if (hg == wave && g == 0 && h_base + hl < Hpad)
+      *(float4*)(pml + (prow0 + hl) * 4) = make_float4(Ms[hl], Ls[hl], amax, 0.f);
   }
+  __syncthreads();
+  store_rows((uint16_t*)a.part + prow0 * kD, kD, min(64, Hpad - h_base));
 }
 
 // Merge split-K partials: out = sum_s 2^(m_s-M) amax_s o_s / (sum_s 2^(m_s-M) l_s + 2^(sink-M)),

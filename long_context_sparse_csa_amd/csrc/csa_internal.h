@@ -60,6 +60,13 @@ struct TopkArgs {
   const int32_t* ctx_len;
   int64_t max_ctx;
   int64_t pos0;
+  // single-block path only, optional: also write each selected entry's compressed KV row
+  // (page_table[request][idx >> 6] * 64 + (idx & 63), -1 if unmapped) to rows[q * ld_rows + j]
+  int32_t* rows;
+  int64_t ld_rows;
+  const int32_t* page_table;
+  int max_pages;
+  int num_pages;
 };
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
@@ -106,6 +113,10 @@ struct AttnArgs {
   float* part;               // split-K partials (may be null when n_split == 1)
   int n_split;               // chosen by plan_attn_split
   int req_mode;              // 0: q_req array; 1: request = query (decode); 2: request 0 (prefill)
+  // optional: compressed slot j of query q is row rows[q * ld_rows + j] of the pool (< 0 invalid),
+  // already resolved through the page table; null = resolve idx through the page table
+  const int32_t* rows;
+  int64_t ld_rows;
 };
 int plan_attn_split(int Q, int H, int n_idx, int q_dt);
 // true when the BF16 matrix-core kernel serves this call (bf16 q, BF16/FP8 rows); else the fp32 kernel

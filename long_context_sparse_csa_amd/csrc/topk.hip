@@ -485,9 +485,20 @@ __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a)
   const int k = a.k;
   int32_t* out = a.idx + (int64_t)q * a.ld_idx;
   if (a.win_mode) write_window(a, q);
+  const int r = a.win_mode == 1 ? q : 0;   // request of this query (decode: q; prefill: 0)
+  const int32_t* pt = a.rows ? a.page_table + (int64_t)r * a.max_pages : nullptr;
+  auto row_of = [&](int c, int pg) { return (unsigned)pg < (unsigned)a.num_pages ? pg * kPage + (c & (kPage - 1)) : -1; };
   if (nv <= k) {
-    for (int i = tid; i < k; i += kSingleThreads) out[i] = i < nv ? i : -1;
+    for (int i = tid; i < k; i += kSingleThreads) {
+      out[i] = i < nv ? i : -1;
+      if (a.rows) a.rows[(int64_t)q * a.ld_rows + i] = i < nv ? row_of(i, pt[i >> 6]) : -1;
+    }
     return;
+  }
+  __shared__ int32_t pt_lds[kSingleMax / kPage];
+  if (a.rows) {
+    // the request's page ids, loaded alongside the scores (rows >= 1: nv > k >= 1)
+    for (int p = tid; p < (int)((nv + kPage - 1) / kPage); p += kSingleThreads) pt_lds[p] = pt[p];
   }
   __shared__ __align__(16) uint32_t bins[kHistBins];
   __shared__ __align__(16) uint32_t scan[kSingleThreads];
@@ -583,7 +594,10 @@ __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a)
       --take_eq;
     }
     if (take) {
-      if (pos < (uint32_t)k) out[pos] = c0 + j;
+      if (pos < (uint32_t)k) {
+        out[pos] = c0 + j;
+        if (a.rows) a.rows[(int64_t)q * a.ld_rows + pos] = row_of(c0 + j, pt_lds[(c0 + j) >> 6]);
+      }
       ++pos;
     }
   }
