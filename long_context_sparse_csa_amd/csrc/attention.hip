@@ -121,9 +121,10 @@ constexpr uint64_t kCodeAddrMask = ~(uint64_t)15;
 
 __device__ __attribute__((aligned(256))) const uint8_t kZeroRow[1024] = {};
 
-// Slots [s_begin, s_begin + s_count) of query q are resolved into `codes` and `vmask`, four per
-// thread per pass: all index loads, then all page-table loads, are issued before any is used.
-// s_count is a whole number of tiles, and each wave covers 64 consecutive slots per pass.
+// Slots [s_begin, s_begin + s_count) of query q are resolved into `codes` and `vmask` by NT
+// threads, four per thread per pass: all index loads, then all page-table loads, are issued before
+// any is used.  s_count is a whole number of tiles, and each wave covers 64 consecutive slots per pass.
+template <int NT>
 __device__ __forceinline__ void resolve_codes(const AttnArgs& a, int q, int r, int s_begin, int s_count,
                                               uint64_t* codes, uint32_t* vmask, int tid) {
   const int n_idx = a.n_win + a.n_comp;
@@ -137,12 +138,12 @@ __device__ __forceinline__ void resolve_codes(const AttnArgs& a, int q, int r, i
   const bool rows_in = a.rows != nullptr && a.comp != nullptr;   // compressed rows arrive resolved
   const uint64_t zero = (uint64_t)(uintptr_t)kZeroRow;
   const int64_t win_rb = row_bytes(a.win_fmt), comp_rb = row_bytes(a.comp_fmt);
-  for (int b = 0; b < s_count; b += 4 * 256) {
+  for (int b = 0; b < s_count; b += 4 * NT) {
     int v[4], pg[4];
     bool in[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int i = b + tid + 256 * k;
+      const int i = b + tid + NT * k;
       in[k] = r_ok && i < s_count && s_begin + i < n_idx;
       const int s = in[k] ? s_begin + i : 0;
       v[k] = (rows_in && s >= a.n_win) ? rows_row[s] : idx_row[s];
@@ -153,14 +154,14 @@ __device__ __forceinline__ void resolve_codes(const AttnArgs& a, int q, int r, i
       const int32_t* pt_row = a.page_table + (int64_t)rr * a.max_pages;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const int s = s_begin + b + tid + 256 * k;
+        const int s = s_begin + b + tid + NT * k;
         const bool pv = in[k] && s >= a.n_win && v[k] >= 0 && v[k] < n_entries;
         pg[k] = pt_row[pv ? (v[k] >> 6) : 0];
       }
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int i = b + tid + 256 * k;
+      const int i = b + tid + NT * k;
       const int s = s_begin + i;
       uint64_t c = zero;
       bool ok = false;
@@ -177,7 +178,7 @@ __device__ __forceinline__ void resolve_codes(const AttnArgs& a, int q, int r, i
         }
       }
       const uint64_t bal = __ballot(ok);
-      const int i0 = b + 256 * k + (tid & ~63);   // first slot of this wave's 64 (two tiles)
+      const int i0 = b + NT * k + (tid & ~63);   // first slot of this wave's 64 (two tiles)
       if (i < s_count) codes[i] = c;
       if ((tid & 63) == 0 && i0 < s_count) {
         vmask[i0 / kTile] = (uint32_t)bal;
@@ -187,50 +188,53 @@ __device__ __forceinline__ void resolve_codes(const AttnArgs& a, int q, int r, i
   }
 }
 
-// One 16-byte chunk per lane per row, loaded without branches so a whole tile of loads is in
-// flight at once.  Lane dc covers dims [8dc, 8dc+8): BF16 rows give the 8 values directly; FP8 rows
-// give 8 nope codes (the first 8 of 16 bytes loaded at 8dc; lanes >= 56 load 8 bf16 rope values)
-// plus the fp32 scale of their 64-dim block.  `code` is wave-uniform, so the row address is scalar.
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+// Two 8-byte loads per lane per row, without branches, so a whole tile of loads is in flight at
+// once.  Lane dc covers dims [8dc, 8dc+8).  BF16 rows: the two halves of the lane's 16 bytes.  FP8
+// rows: nope lanes (dc < 56) take their 8 e4m3fn codes and, in the second load, the 8-byte aligned
+// pair of fp32 block scales that holds the scale of their 64-dim block; rope lanes (dc >= 56) take
+// the two halves of 8 bf16 values.  The code is wave-uniform, so the row address is scalar.
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef const __attribute__((address_space(1))) v2u* gv2u;
 struct RawChunk {
-  v4u x;
-  uint32_t sc;
+  v2u lo, hi;
 };
 
 template <int WF, int CF>
 __device__ __forceinline__ RawChunk load_raw(uint64_t code, int dc) {
   const int fmt = (code & kCodeComp) ? CF : WF;
   const gbytes rp = (gbytes)(uintptr_t)(code & kCodeAddrMask);
-  const int off = fmt == kRowFP8 ? (dc < kNope / 8 ? 8 * dc : 16 * dc - kNope) : 16 * dc;
-  RawChunk r;
-  r.x = *(const __attribute__((address_space(1))) v4u*)(rp + off);
-  if constexpr (WF == kRowFP8 || CF == kRowFP8) {
-    const int so = 576 + 4 * ((dc >> 3) < 6 ? (dc >> 3) : 6);
-    r.sc = *(const __attribute__((address_space(1))) uint32_t*)(rp + so);
-  } else {
-    r.sc = 0u;
+  int o0 = 16 * dc, o1 = 16 * dc + 8;
+  if (fmt == kRowFP8) {
+    const bool nope = dc < kNope / 8;
+    o0 = nope ? 8 * dc : 16 * dc - kNope;
+    o1 = nope ? 576 + 8 * (dc >> 4) : 16 * dc - kNope + 8;
   }
+  RawChunk r;
+  r.lo = *(gv2u)(rp + o0);
+  r.hi = *(gv2u)(rp + o1);
   return r;
 }
 
 // Raw chunk -> 8 bf16 (4 dwords).  Branch-free: the FP8 conversion is always computed and selected
 // per lane (nope lanes of FP8 rows take it; rope lanes and BF16 rows keep the raw bits).
 template <int WF, int CF>
-__device__ __forceinline__ void raw_to_bf16(const RawChunk& r, uint64_t code, int dc, uint32_t* w) {
-  w[0] = r.x[0]; w[1] = r.x[1]; w[2] = r.x[2]; w[3] = r.x[3];
+__device__ __forceinline__ uint4 raw_to_bf16(const RawChunk& r, uint64_t code, int dc) {
+  uint4 w = make_uint4(r.lo[0], r.lo[1], r.hi[0], r.hi[1]);
   if constexpr (WF == kRowFP8 || CF == kRowFP8) {
     const int fmt = (code & kCodeComp) ? CF : WF;
     const bool fp8_lane = fmt == kRowFP8 && dc < kNope / 8;
     float v[8];
-    fp8x4_to_f32(r.x[0], v);
-    fp8x4_to_f32(r.x[1], v + 4);
-    const float sc = __uint_as_float(r.sc);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t c = pack_bf16x2(v[2 * e] * sc, v[2 * e + 1] * sc);
-      w[e] = fp8_lane ? c : w[e];
-    }
+    fp8x4_to_f32(r.lo[0], v);
+    fp8x4_to_f32(r.lo[1], v + 4);
+    const float sc = __uint_as_float((dc >> 3) & 1 ? r.hi[1] : r.hi[0]);
+    const uint32_t c0 = pack_bf16x2(v[0] * sc, v[1] * sc), c1 = pack_bf16x2(v[2] * sc, v[3] * sc);
+    const uint32_t c2 = pack_bf16x2(v[4] * sc, v[5] * sc), c3 = pack_bf16x2(v[6] * sc, v[7] * sc);
+    w.x = fp8_lane ? c0 : w.x;
+    w.y = fp8_lane ? c1 : w.y;
+    w.z = fp8_lane ? c2 : w.z;
+    w.w = fp8_lane ? c3 : w.w;
   }
+  return w;
 }
 
 constexpr int kMaxSlots = 4096;
@@ -244,8 +248,10 @@ __device__ __forceinline__ v4s lds_read_tr16(const uint16_t* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)((__attribute__((address_space(3))) uint16_t*)p));
 }
 
+constexpr int kAttnThreads = 512;   // waves 0-3 consume (matrix cores), waves 4-7 produce (gathers)
+
 template <int WF, int CF>
-__global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -267,158 +273,169 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   const int n_tiles = (n_idx + kTile - 1) / kTile;
   const int tps = (n_tiles + a.n_split - 1) / a.n_split;
   const int t_begin = split * tps;
-  const int t_end = min(n_tiles, t_begin + tps);
+  const int nt = max(0, min(n_tiles, t_begin + tps) - t_begin);   // tiles of this block
   const int r = a.req_mode == 1 ? q : (a.req_mode == 2 ? 0 : a.q_req[q]);
   const int s_begin = t_begin * kTile;
-  const int s_count = max(0, (t_end - t_begin) * kTile);
 
-  // q of this wave's 16 heads stays in registers as the QK B operand: lane (n, g) holds dims
-  // 32ks + 8g .. +7 of head h_base + 16 wave + n.  Padded heads read head 0's row; their results are
-  // never written.
+  // consumers: q of this wave's 16 heads stays in registers as the QK B operand: lane (n, g) holds
+  // dims 32ks + 8g .. +7 of head h_base + 16 wave + n.  Padded heads read head 0's row; their
+  // results are never written.
   v8bf qreg[16];
-  {
+  if (wave < 4) {
     const int hq = h_base + 16 * wave + n;
     const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)q * a.H + (hq < a.H ? hq : 0)) * kD + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) qreg[ks] = *(const v8bf*)(qp + 32 * ks);
   }
-  resolve_codes(a, q, r, s_begin, s_count, codes, vmask, tid);
+  resolve_codes<kAttnThreads>(a, q, r, s_begin, nt * kTile, codes, vmask, tid);
   __syncthreads();
 
-  // wave w gathers rows 8w .. 8w+7 of a tile, one 16-B chunk (8 dims) per lane, so each load
-  // instruction reads a whole row contiguously; the raw chunks of the next tile and their
-  // (wave-uniform) codes sit in registers
-  constexpr int kRowsPerWave = kTile / 4;
-  RawChunk raw[kRowsPerWave];
-  uint64_t rc[kRowsPerWave];
-  auto fetch = [&](int t) {
-    const int base = (t - t_begin) * kTile + kRowsPerWave * wave;
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; i += 2) {
-      const uint4 c = *(const uint4*)&codes[base + i];
-      rc[i] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.y) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.x);
-      rc[i + 1] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.w) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.z);
-    }
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) raw[i] = load_raw<WF, CF>(rc[i], lane);
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) {
-      uint32_t w[4];
-      raw_to_bf16<WF, CF>(raw[i], rc[i], lane, w);
-      *(uint4*)&Kr[buf][(kRowsPerWave * wave + i) * kKrStride + 8 * lane] = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  };
-  if (t_begin < t_end) {
-    fetch(t_begin);
-    stage(0);
-    if (t_begin + 1 < t_end) fetch(t_begin + 1);
-  }
-  __syncthreads();
-
-  const float sc = a.softmax_scale * kLog2e;
-  float m = kNegBig, lsum = 0.f;   // softmax state of head h_base + 16 wave + n
+  float m = kNegBig, lsum = 0.f;   // consumer softmax state of head h_base + 16 wave + n
   v4f acc[4][8];                   // O^T[128 wave + 16 dt + 4 g + i][h_base + 16 hg + n]
 #pragma unroll
   for (int hg = 0; hg < 4; ++hg)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[hg][dt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int t = t_begin; t < t_end; ++t) {
-    const int buf = (t - t_begin) & 1;
-    const uint16_t* K = Kr[buf];
-
-    // S^T[key][head] of this wave's head group for keys 0..15 (s0) and 16..31 (s1)
-    v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = v4f{0.f, 0.f, 0.f, 0.f};
+  if (wave >= 4) {
+    // ---- producers: wave 4+p gathers rows 8p .. 8p+7 of every tile, one 16-B chunk (8 dims) per
+    // lane, two tiles ahead in registers, and dequantises the next tile into the free LDS buffer
+    // while the consumers work on the current one
+    const int pw = wave - 4;
+    RawChunk raw0[8], raw1[8];
+    uint64_t rc0[8], rc1[8];
+    auto fetch = [&](int k, RawChunk* raw, uint64_t* rc) {
+      const int base = k * kTile + 8 * pw;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      const v8bf k0 = *(const v8bf*)&K[n * kKrStride + 32 * ks + 8 * g];
-      const v8bf k1 = *(const v8bf*)&K[(16 + n) * kKrStride + 32 * ks + 8 * g];
-      s0 = mma_bf16(k0, qreg[ks], s0);
-      s1 = mma_bf16(k1, qreg[ks], s1);
-    }
-    const uint32_t vm = vmask[t - t_begin];
-    float sv[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sv[i] = (vm >> (4 * g + i)) & 1u ? s0[i] * sc : -INFINITY;
-      sv[4 + i] = (vm >> (16 + 4 * g + i)) & 1u ? s1[i] * sc : -INFINITY;
-    }
-    float tmax = sv[0];
-#pragma unroll
-    for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, sv[e]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    // lazy rescaling: the reference max moves only when a head's max grows by more than 2^8, so
-    // the accumulators are touched rarely; p = 2^(S - m) then stays below 256
-    const bool grow = tmax > m + kRescaleLog2;
-    float alpha = 1.f;
-    int fl = 0;
-    if (__builtin_expect(__any(grow), 0)) {
-      // an opaque statement keeps the compiler from if-converting this rare path into every tile
-      __asm__ volatile("" ::: "memory");
-      const float m_new = grow ? tmax : m;
-      alpha = exp2f(m - m_new);
-      lsum *= alpha;
-      m = m_new;
-      fl = 1;
-    }
-    float p[8], psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(sv[e] - m);
-      psum += p[e];
-    }
-    lsum += psum;
-    // slot 8g+4mt+i of the K step <-> key 16mt+4g+i: these 8 values are exactly this lane's part of
-    // the P^T operand, for every wave that multiplies this head group
-    Ps[wave][lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                                pack_bf16x2(p[6], p[7]));
-    if (g == 0) As[16 * wave + n] = alpha;
-    if (lane == 0) Fl[wave] = fl;
-    __syncthreads();
-
-    const int4 f4 = *(const int4*)Fl;
-    if (__builtin_expect((f4.x | f4.y | f4.z | f4.w) != 0, 0)) {
-      __asm__ volatile("" ::: "memory");
-#pragma unroll
-      for (int hg = 0; hg < 4; ++hg) {
-        const float al = As[16 * hg + n];
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt) acc[hg][dt] *= al;
+      for (int i = 0; i < 8; i += 2) {
+        const uint4 c = *(const uint4*)&codes[base + i];
+        rc[i] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.y) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.x);
+        rc[i + 1] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.w) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.z);
       }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) raw[i] = load_raw<WF, CF>(rc[i], lane);
+    };
+    auto stage = [&](int buf, const RawChunk* raw, const uint64_t* rc) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *(uint4*)&Kr[buf][(8 * pw + i) * kKrStride + 8 * lane] = raw_to_bf16<WF, CF>(raw[i], rc[i], lane);
+    };
+    if (nt > 0) fetch(0, raw0, rc0);
+    if (nt > 1) fetch(1, raw1, rc1);
+    if (nt > 0) {
+      stage(0, raw0, rc0);
+      if (nt > 2) fetch(2, raw0, rc0);
     }
-    v8bf pf[4];
-#pragma unroll
-    for (int hg = 0; hg < 4; ++hg) pf[hg] = __builtin_bit_cast(v8bf, Ps[hg][lane]);
-
-    // O^T[d][head] += V^T[d][slot] . P^T[slot][head] over this wave's 128 dims, all head groups;
-    // V^T comes from the row-major tile through the transposing LDS read: source lane s of group g
-    // points at key row 4g + s/4 (slots 8g..8g+3) or 16 + 4g + s/4 (slots 8g+4..8g+7), dims
-    // 4(s%4) .. +3
-    const uint16_t* tr_lo = &K[(4 * g + (n >> 2)) * kKrStride + 4 * (n & 3) + 128 * wave];
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const v4s lo = lds_read_tr16(tr_lo + 16 * dt);
-      const v4s hi = lds_read_tr16(tr_lo + 16 * kKrStride + 16 * dt);
-      const v8bf vv = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int hg = 0; hg < 4; ++hg) acc[hg][dt] = mma_bf16(vv, pf[hg], acc[hg][dt]);
-    }
-    // the next tile is dequantised into the other buffer while the matrix cores run.  Unconditional
-    // so that the conversion shares a basic block with the MFMAs: past the end it re-stages and
-    // re-fetches the block's last tile, whose codes are valid, into the buffer nobody reads again.
-    stage(buf ^ 1);
-    fetch(min(t + 2, t_end - 1));
     __syncthreads();
-  }
+    // iteration k: consumers read buffer k & 1 (tile k); tile k+1 goes into the other buffer.  The
+    // raw registers alternate: tile j sits in raw(j & 1).
+    for (int k = 0; k < nt; k += 2) {
+      if (k + 1 < nt) {
+        stage(1, raw1, rc1);
+        if (k + 3 < nt) fetch(k + 3, raw1, rc1);
+      }
+      __syncthreads();
+      __syncthreads();
+      if (k + 1 >= nt) break;
+      if (k + 2 < nt) {
+        stage(0, raw0, rc0);
+        if (k + 4 < nt) fetch(k + 4, raw0, rc0);
+      }
+      __syncthreads();
+      __syncthreads();
+    }
+  } else {
+    // ---- consumers
+    __syncthreads();
+    const float sc = a.softmax_scale * kLog2e;
+    for (int k = 0; k < nt; ++k) {
+      const uint16_t* K = Kr[k & 1];
 
-  float ltot = lsum + __shfl_xor(lsum, 16);
-  ltot += __shfl_xor(ltot, 32);
-  if (g == 0) {
-    Ms[16 * wave + n] = m;
-    Ls[16 * wave + n] = ltot;
+      // S^T[key][head] of this wave's head group for keys 0..15 (s0) and 16..31 (s1)
+      v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const v8bf k0 = *(const v8bf*)&K[n * kKrStride + 32 * ks + 8 * g];
+        const v8bf k1 = *(const v8bf*)&K[(16 + n) * kKrStride + 32 * ks + 8 * g];
+        s0 = mma_bf16(k0, qreg[ks], s0);
+        s1 = mma_bf16(k1, qreg[ks], s1);
+      }
+      const uint32_t vm = vmask[k];
+      float sv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = (vm >> (4 * g + i)) & 1u ? s0[i] * sc : -INFINITY;
+        sv[4 + i] = (vm >> (16 + 4 * g + i)) & 1u ? s1[i] * sc : -INFINITY;
+      }
+      float tmax = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, sv[e]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      // lazy rescaling: the reference max moves only when a head's max grows by more than 2^8, so
+      // the accumulators are touched rarely; p = 2^(S - m) then stays below 256
+      const bool grow = tmax > m + kRescaleLog2;
+      float alpha = 1.f;
+      int fl = 0;
+      if (__builtin_expect(__any(grow), 0)) {
+        // an opaque statement keeps the compiler from if-converting this rare path into every tile
+        __asm__ volatile("" ::: "memory");
+        const float m_new = grow ? tmax : m;
+        alpha = exp2f(m - m_new);
+        lsum *= alpha;
+        m = m_new;
+        fl = 1;
+      }
+      float p[8], psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(sv[e] - m);
+        psum += p[e];
+      }
+      lsum += psum;
+      // slot 8g+4mt+i of the K step <-> key 16mt+4g+i: these 8 values are exactly this lane's part
+      // of the P^T operand, for every wave that multiplies this head group
+      Ps[wave][lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                  pack_bf16x2(p[6], p[7]));
+      if (g == 0) As[16 * wave + n] = alpha;
+      if (lane == 0) Fl[wave] = fl;
+      __syncthreads();
+
+      const int4 f4 = *(const int4*)Fl;
+      if (__builtin_expect((f4.x | f4.y | f4.z | f4.w) != 0, 0)) {
+        __asm__ volatile("" ::: "memory");
+#pragma unroll
+        for (int hg = 0; hg < 4; ++hg) {
+          const float al = As[16 * hg + n];
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) acc[hg][dt] *= al;
+        }
+      }
+      v8bf pf[4];
+#pragma unroll
+      for (int hg = 0; hg < 4; ++hg) pf[hg] = __builtin_bit_cast(v8bf, Ps[hg][lane]);
+
+      // O^T[d][head] += V^T[d][slot] . P^T[slot][head] over this wave's 128 dims, all head groups;
+      // V^T comes from the row-major tile through the transposing LDS read: source lane s of group
+      // g points at key row 4g + s/4 (slots 8g..8g+3) or 16 + 4g + s/4 (slots 8g+4..8g+7), dims
+      // 4(s%4) .. +3
+      const uint16_t* tr_lo = &K[(4 * g + (n >> 2)) * kKrStride + 4 * (n & 3) + 128 * wave];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const v4s lo = lds_read_tr16(tr_lo + 16 * dt);
+        const v4s hi = lds_read_tr16(tr_lo + 16 * kKrStride + 16 * dt);
+        const v8bf vv = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int hg = 0; hg < 4; ++hg) acc[hg][dt] = mma_bf16(vv, pf[hg], acc[hg][dt]);
+      }
+      __syncthreads();
+    }
+    float ltot = lsum + __shfl_xor(lsum, 16);
+    ltot += __shfl_xor(ltot, 32);
+    if (g == 0) {
+      Ms[16 * wave + n] = m;
+      Ls[16 * wave + n] = ltot;
+    }
   }
   __syncthreads();
   const int dbase = 128 * wave + 4 * g;
@@ -428,75 +445,82 @@ __global__ __launch_bounds__(256, 1) void attn_bf16_kernel(AttnArgs a) {
   uint16_t* stg = &Kr[0][0];
   static_assert(64 * kStage <= 2 * kTile * kKrStride, "staging fits the two row tiles");
   auto store_rows = [&](uint16_t* base, int64_t row_stride, int nrows) {
-    // wave w writes staged rows 16w .. 16w+15 (those below nrows) to base + row * row_stride
-    for (int i = 0; i < 16; ++i) {
-      const int rr = 16 * wave + i;
+    // wave w writes staged rows 8w .. 8w+7 (those below nrows) to base + row * row_stride
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int rr = 8 * wave + i;
       if (rr < nrows) *(uint4*)(base + rr * row_stride + 8 * lane) = *(const uint4*)&stg[rr * kStage + 8 * lane];
     }
   };
   if (a.n_split == 1) {
-    float inv[4];
-#pragma unroll
-    for (int hg = 0; hg < 4; ++hg) {
-      const int h = h_base + 16 * hg + n;
-      const float mh = Ms[16 * hg + n], lh = Ls[16 * hg + n];
-      const float sk = a.sink[h < a.H ? h : 0] * kLog2e;
-      const float M = fmaxf(mh, sk);
-      const float f = exp2f(mh - M);
-      inv[hg] = f / (lh * f + exp2f(sk - M));
-    }
-    const int nrows = min(64, a.H - h_base);
-    if (a.out_dt == 0) {
+    if (wave < 4) {
+      float inv[4];
 #pragma unroll
       for (int hg = 0; hg < 4; ++hg) {
         const int h = h_base + 16 * hg + n;
-        if (h >= a.H) continue;
-        const int64_t ob = ((int64_t)q * a.H + h) * kD + dbase;
-#pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          store4(a.out, 0, ob + 16 * dt, acc[hg][dt][0] * inv[hg], acc[hg][dt][1] * inv[hg], acc[hg][dt][2] * inv[hg],
-                 acc[hg][dt][3] * inv[hg]);
+        const float mh = Ms[16 * hg + n], lh = Ls[16 * hg + n];
+        const float sk = a.sink[h < a.H ? h : 0] * kLog2e;
+        const float M = fmaxf(mh, sk);
+        const float f = exp2f(mh - M);
+        inv[hg] = f / (lh * f + exp2f(sk - M));
       }
-      return;
+      if (a.out_dt == 0) {
+#pragma unroll
+        for (int hg = 0; hg < 4; ++hg) {
+          const int h = h_base + 16 * hg + n;
+          if (h >= a.H) continue;
+          const int64_t ob = ((int64_t)q * a.H + h) * kD + dbase;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+            store4(a.out, 0, ob + 16 * dt, acc[hg][dt][0] * inv[hg], acc[hg][dt][1] * inv[hg],
+                   acc[hg][dt][2] * inv[hg], acc[hg][dt][3] * inv[hg]);
+        }
+      } else {
+#pragma unroll
+        for (int hg = 0; hg < 4; ++hg)
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt)
+            *(uint2*)&stg[(16 * hg + n) * kStage + dbase + 16 * dt] =
+                make_uint2(pack_bf16x2(acc[hg][dt][0] * inv[hg], acc[hg][dt][1] * inv[hg]),
+                           pack_bf16x2(acc[hg][dt][2] * inv[hg], acc[hg][dt][3] * inv[hg]));
+      }
     }
-#pragma unroll
-    for (int hg = 0; hg < 4; ++hg)
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        *(uint2*)&stg[(16 * hg + n) * kStage + dbase + 16 * dt] =
-            make_uint2(pack_bf16x2(acc[hg][dt][0] * inv[hg], acc[hg][dt][1] * inv[hg]),
-                       pack_bf16x2(acc[hg][dt][2] * inv[hg], acc[hg][dt][3] * inv[hg]));
+    if (a.out_dt == 0) return;
     __syncthreads();
-    store_rows((uint16_t*)a.out + ((int64_t)q * a.H + h_base) * kD, kD, nrows);
+    store_rows((uint16_t*)a.out + ((int64_t)q * a.H + h_base) * kD, kD, min(64, a.H - h_base));
     return;
   }
   // split-K partial of each head: m, l, amax = max |acc| over the 512 dims (fp32) and acc / amax
   // as fp16 (|value| <= 1, so the only loss is fp16's 11-bit rounding relative to amax)
+  if (wave < 4) {
 #pragma unroll
-  for (int hg = 0; hg < 4; ++hg) {
-    float mx = 0.f;
+    for (int hg = 0; hg < 4; ++hg) {
+      float mx = 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+      for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[hg][dt][i]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (g == 0) Xs[wave][16 * hg + n] = mx;
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[hg][dt][i]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (g == 0) Xs[wave][16 * hg + n] = mx;
+    }
   }
   __syncthreads();
   const int64_t prow0 = ((int64_t)q * a.n_split + split) * Hpad + h_base;   // partial row of head h_base
-  float* pml = (float*)((uint8_t*)a.part + (size_t)a.Q * a.n_split * Hpad * kD * sizeof(uint16_t));
+  if (wave < 4) {
+    float* pml = (float*)((uint8_t*)a.part + (size_t)a.Q * a.n_split * Hpad * kD * sizeof(uint16_t));
 #pragma unroll
-  for (int hg = 0; hg < 4; ++hg) {
-    const int hl = 16 * hg + n;
-    const float amax = fmaxf(fmaxf(Xs[0][hl], Xs[1][hl]), fmaxf(Xs[2][hl], Xs[3][hl]));
-    const float f = amax > 0.f ? 1.f / amax : 0.f;
+    for (int hg = 0; hg < 4; ++hg) {
+      const int hl = 16 * hg + n;
+      const float amax = fmaxf(fmaxf(Xs[0][hl], Xs[1][hl]), fmaxf(Xs[2][hl], Xs[3][hl]));
+      const float f = amax > 0.f ? 1.f / amax : 0.f;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-      *(uint2*)&stg[hl * kStage + dbase + 16 * dt] = make_uint2(pack_f16x2(acc[hg][dt][0] * f, acc[hg][dt][1] * f),
-                                                              pack_f16x2(acc[hg][dt][2] * f, acc[hg][dt][3] * f));
-    if (hg == wave && g == 0 && h_base + hl < Hpad)
-      *(float4*)(pml + (prow0 + hl) * 4) = make_float4(Ms[hl], Ls[hl], amax, 0.f);
+      for (int dt = 0; dt < 8; ++dt)
+        *(uint2*)&stg[hl * kStage + dbase + 16 * dt] = make_uint2(pack_f16x2(acc[hg][dt][0] * f, acc[hg][dt][1] * f),
+                                                                pack_f16x2(acc[hg][dt][2] * f, acc[hg][dt][3] * f));
+      if (hg == wave && g == 0 && h_base + hl < Hpad)
+        *(float4*)(pml + (prow0 + hl) * 4) = make_float4(Ms[hl], Ls[hl], amax, 0.f);
+    }
   }
   __syncthreads();
   store_rows((uint16_t*)a.part + prow0 * kD, kD, min(64, Hpad - h_base));
@@ -666,10 +690,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   {
     ProfScope p("attn_bf16", s);
     const dim3 grid((unsigned)(a.Q * a.n_split), (unsigned)hchunks);
-    if (wf == kRowFP8 && cf == kRowFP8) hipLaunchKernelGGL((attn_bf16_kernel<kRowFP8, kRowFP8>), grid, dim3(256), 0, s, a);
-    else if (wf == kRowFP8) hipLaunchKernelGGL((attn_bf16_kernel<kRowFP8, kRowBF16>), grid, dim3(256), 0, s, a);
-    else if (cf == kRowFP8) hipLaunchKernelGGL((attn_bf16_kernel<kRowBF16, kRowFP8>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<kRowBF16, kRowBF16>), grid, dim3(256), 0, s, a);
+    if (wf == kRowFP8 && cf == kRowFP8) hipLaunchKernelGGL((attn_bf16_kernel<kRowFP8, kRowFP8>), grid, dim3(kAttnThreads), 0, s, a);
+    else if (wf == kRowFP8) hipLaunchKernelGGL((attn_bf16_kernel<kRowFP8, kRowBF16>), grid, dim3(kAttnThreads), 0, s, a);
+    else if (cf == kRowFP8) hipLaunchKernelGGL((attn_bf16_kernel<kRowBF16, kRowFP8>), grid, dim3(kAttnThreads), 0, s, a);
+    else hipLaunchKernelGGL((attn_bf16_kernel<kRowBF16, kRowBF16>), grid, dim3(kAttnThreads), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
