@@ -249,6 +249,10 @@ __device__ __forceinline__ v4s lds_read_tr16(const uint16_t* p) {
 }
 
 constexpr int kAttnThreads = 512;   // waves 0-3 consume (matrix cores), waves 4-7 produce (gathers)
+#ifndef CSA_ATTN_DEPTH
+#define CSA_ATTN_DEPTH 4
+#endif
+constexpr int kDepth = CSA_ATTN_DEPTH;   // tiles of row gathers in flight per producer wave
 
 template <int WF, int CF>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) {
@@ -261,10 +265,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   const int Hpad = (a.H + 15) & ~15;
   const int h_base = blockIdx.y * 64;
 
-  __shared__ __align__(16) uint16_t Kr[2][kTile * kKrStride];   // double-buffered bf16 row tile
-  __shared__ __align__(16) uint4 Ps[4][64];                      // P^T operand of each head group
-  __shared__ __align__(16) int Fl[4];                            // head group rescaled this tile
-  __shared__ float As[64];                                       // its per-head rescale factors
+  __shared__ __align__(16) uint16_t Kr[3][kTile * kKrStride];   // ring of three bf16 row tiles
+  __shared__ __align__(16) uint4 Ps[2][4][64];                   // P^T operand of each head group
+  __shared__ __align__(16) int Fl[2][4];                         // head group rescaled this tile
+  __shared__ float As[2][64];                                    // its per-head rescale factors
   __shared__ float Ms[64], Ls[64], Xs[4][64];
   __shared__ __align__(16) uint64_t codes[kMaxSlots];
   __shared__ uint32_t vmask[kMaxSlots / kTile];
@@ -299,60 +303,64 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
 
   if (wave >= 4) {
     // ---- producers: wave 4+p gathers rows 8p .. 8p+7 of every tile, one 16-B chunk (8 dims) per
-    // lane, two tiles ahead in registers, and dequantises the next tile into the free LDS buffer
-    // while the consumers work on the current one
+    // lane, kDepth tiles ahead in registers.  During iteration k (between barriers k-1 and k) they
+    // dequantise tile k+1 into ring buffer (k+1) % 3, whose last reader (the P.V of tile k-2)
+    // finished before barrier k-1.
     const int pw = wave - 4;
-    RawChunk raw0[8], raw1[8];
-    uint64_t rc0[8], rc1[8];
-    auto fetch = [&](int k, RawChunk* raw, uint64_t* rc) {
+    RawChunk raw[kDepth][8];
+    uint64_t rc[kDepth][8];
+    auto fetch = [&](int k, RawChunk* rw, uint64_t* c8) {
       const int base = k * kTile + 8 * pw;
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
         const uint4 c = *(const uint4*)&codes[base + i];
-        rc[i] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.y) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.x);
-        rc[i + 1] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.w) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.z);
+        c8[i] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.y) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.x);
+        c8[i + 1] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.w) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.z);
       }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) raw[i] = load_raw<WF, CF>(rc[i], lane);
+      for (int i = 0; i < 8; ++i) rw[i] = load_raw<WF, CF>(c8[i], lane);
     };
-    auto stage = [&](int buf, const RawChunk* raw, const uint64_t* rc) {
+    auto stage = [&](int buf, const RawChunk* rw, const uint64_t* c8) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        *(uint4*)&Kr[buf][(8 * pw + i) * kKrStride + 8 * lane] = raw_to_bf16<WF, CF>(raw[i], rc[i], lane);
+        *(uint4*)&Kr[buf][(8 * pw + i) * kKrStride + 8 * lane] = raw_to_bf16<WF, CF>(rw[i], c8[i], lane);
     };
-    if (nt > 0) fetch(0, raw0, rc0);
-    if (nt > 1) fetch(1, raw1, rc1);
+    // tile j lives in raw slot j % kDepth from its fetch until it is staged
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j)
+      if (j < nt) fetch(j, raw[j], rc[j]);
     if (nt > 0) {
-      stage(0, raw0, rc0);
-      if (nt > 2) fetch(2, raw0, rc0);
+      stage(0, raw[0], rc[0]);
+      if (kDepth < nt) fetch(kDepth, raw[0], rc[0]);
     }
     __syncthreads();
-    // iteration k: consumers read buffer k & 1 (tile k); tile k+1 goes into the other buffer.  The
-    // raw registers alternate: tile j sits in raw(j & 1).
-    for (int k = 0; k < nt; k += 2) {
-      if (k + 1 < nt) {
-        stage(1, raw1, rc1);
-        if (k + 3 < nt) fetch(k + 3, raw1, rc1);
+    int buf = 1;   // (k + 1) % 3
+    for (int k = 0; k < nt; k += kDepth) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        if (k + u < nt) {
+          constexpr int kDepthC = kDepth;
+          const int sl = (u + 1) % kDepthC;
+          if (k + u + 1 < nt) {
+            stage(buf, raw[sl], rc[sl]);
+            if (k + u + 1 + kDepth < nt) fetch(k + u + 1 + kDepth, raw[sl], rc[sl]);
+          }
+          buf = buf == 2 ? 0 : buf + 1;
+          __syncthreads();
+        }
       }
-      __syncthreads();
-      __syncthreads();
-      if (k + 1 >= nt) break;
-      if (k + 2 < nt) {
-        stage(0, raw0, rc0);
-        if (k + 4 < nt) fetch(k + 4, raw0, rc0);
-      }
-      __syncthreads();
-      __syncthreads();
     }
   } else {
-    // ---- consumers
+    // ---- consumers, software-pipelined over tiles: iteration k runs the softmax of tile k (whose
+    // scores the previous iteration computed), publishes P^T, waits at barrier k, then issues the
+    // scores of tile k+1 and the P.V of tile k back to back on the matrix cores
     __syncthreads();
     const float sc = a.softmax_scale * kLog2e;
-    for (int k = 0; k < nt; ++k) {
-      const uint16_t* K = Kr[k & 1];
-
-      // S^T[key][head] of this wave's head group for keys 0..15 (s0) and 16..31 (s1)
-      v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = v4f{0.f, 0.f, 0.f, 0.f};
+    // S^T[key][head] of this wave's head group for keys 0..15 (s0) and 16..31 (s1)
+    v4f s0, s1;
+    auto qk = [&](const uint16_t* K) {
+      s0 = v4f{0.f, 0.f, 0.f, 0.f};
+      s1 = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
         const v8bf k0 = *(const v8bf*)&K[n * kKrStride + 32 * ks + 8 * g];
@@ -360,6 +368,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
         s0 = mma_bf16(k0, qreg[ks], s0);
         s1 = mma_bf16(k1, qreg[ks], s1);
       }
+    };
+    qk(Kr[0]);
+    int cur = 0;   // k % 3
+    for (int k = 0; k < nt; ++k) {
+      const int pb = k & 1;
       const uint32_t vm = vmask[k];
       float sv[8];
 #pragma unroll
@@ -395,25 +408,29 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
       lsum += psum;
       // slot 8g+4mt+i of the K step <-> key 16mt+4g+i: these 8 values are exactly this lane's part
       // of the P^T operand, for every wave that multiplies this head group
-      Ps[wave][lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                                  pack_bf16x2(p[6], p[7]));
-      if (g == 0) As[16 * wave + n] = alpha;
-      if (lane == 0) Fl[wave] = fl;
+      Ps[pb][wave][lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                                      pack_bf16x2(p[6], p[7]));
+      if (g == 0) As[pb][16 * wave + n] = alpha;
+      if (lane == 0) Fl[pb][wave] = fl;
       __syncthreads();
 
-      const int4 f4 = *(const int4*)Fl;
+      const int nxt = cur == 2 ? 0 : cur + 1;
+      // scores of tile k+1 (past the last tile this reads a stale buffer; the result is unused)
+      qk(Kr[nxt]);
+      const uint16_t* K = Kr[cur];
+      const int4 f4 = *(const int4*)Fl[pb];
       if (__builtin_expect((f4.x | f4.y | f4.z | f4.w) != 0, 0)) {
         __asm__ volatile("" ::: "memory");
 #pragma unroll
         for (int hg = 0; hg < 4; ++hg) {
-          const float al = As[16 * hg + n];
+          const float al = As[pb][16 * hg + n];
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) acc[hg][dt] *= al;
         }
       }
       v8bf pf[4];
 #pragma unroll
-      for (int hg = 0; hg < 4; ++hg) pf[hg] = __builtin_bit_cast(v8bf, Ps[hg][lane]);
+      for (int hg = 0; hg < 4; ++hg) pf[hg] = __builtin_bit_cast(v8bf, Ps[pb][hg][lane]);
 
       // O^T[d][head] += V^T[d][slot] . P^T[slot][head] over this wave's 128 dims, all head groups;
       // V^T comes from the row-major tile through the transposing LDS read: source lane s of group
@@ -428,7 +445,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
 #pragma unroll
         for (int hg = 0; hg < 4; ++hg) acc[hg][dt] = mma_bf16(vv, pf[hg], acc[hg][dt]);
       }
-      __syncthreads();
+      cur = nxt;
     }
     float ltot = lsum + __shfl_xor(lsum, 16);
     ltot += __shfl_xor(ltot, 32);
@@ -443,7 +460,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   // head, so that every wave then stores whole 1 KB rows with one instruction each
   constexpr int kStage = kKrStride;
   uint16_t* stg = &Kr[0][0];
-  static_assert(64 * kStage <= 2 * kTile * kKrStride, "staging fits the two row tiles");
+  static_assert(64 * kStage <= 3 * kTile * kKrStride, "staging fits the row tiles");
   auto store_rows = [&](uint16_t* base, int64_t row_stride, int nrows) {
     // wave w writes staged rows 8w .. 8w+7 (those below nrows) to base + row * row_stride
 #pragma unroll
