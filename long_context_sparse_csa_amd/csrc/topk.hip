@@ -428,13 +428,20 @@ __global__ __launch_bounds__(256) void topk_finish_kernel(TopkArgs a) {
 // of a microsecond at 16 waves, and a predicated LDS instruction costs its issue slot even when
 // few lanes are active, so the phases are few, the scans are done by a single wave and sparse
 // passes skip instructions no lane needs:
-//   1. three radix levels (12 + 10 + 10 key bits) give the exact k-th largest key T and how many
-//      keys equal to T are taken;
-//   2. one scan of the per-thread (greater, equal) counts, packed in one word, emits the k indices
-//      in ascending order, equal keys at T in index order.
+//   1. a 12-bit histogram of every key gives the threshold bin b* and the count above it;
+//   2. the entries of b* (normally a few hundred) are appended to an LDS candidate list, and one
+//      wave resolves the remaining 20 key bits among them (two 10-bit levels, no block barrier),
+//      giving the exact k-th largest key T and how many keys equal to T are taken; a bin with more
+//      than kCandMax entries (heavily tied scores) takes two block-wide levels instead;
+//   3. one scan of the per-thread (greater, equal) counts, packed in one word, places the k
+//      indices in ascending order (equal keys at T in index order) in LDS, from where they are
+//      written with coalesced stores.
 constexpr int kSingleThreads = 1024;
 constexpr int kSingleMax = 16384;
 constexpr int kSinglePer = kSingleMax / kSingleThreads;   // 16 entries per thread, in index order
+constexpr int kCandMax = 2048;      // entries of the threshold bin resolved by one wave; more take
+                                    // the block-wide path
+constexpr int kSingleMaxK = 2048;   // largest k
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves (VALU only, no LDS crossbar):
 // shifts by 1, 2, 4, 8 inside each row of 16 lanes, then row 0's and row 2's totals broadcast into
@@ -480,7 +487,7 @@ __device__ __forceinline__ void wave_find_desc(const uint32_t* bins, int nb, uin
 }
 
 __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a) {
-  const int q = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
+  const int q = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t nv = topk_row_count(a, q);
   const int k = a.k;
   int32_t* out = a.idx + (int64_t)q * a.ld_idx;
@@ -502,7 +509,10 @@ __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a)
   }
   __shared__ __align__(16) uint32_t bins[kHistBins];
   __shared__ __align__(16) uint32_t scan[kSingleThreads];
-  __shared__ uint32_t s_digit, s_before;
+  __shared__ __align__(16) uint32_t key_lds[kSingleMax];   // order keys of the row, by entry
+  __shared__ uint32_t cand_idx[kCandMax];
+  __shared__ int32_t sel[kSingleMaxK];
+  __shared__ uint32_t s_digit, s_before, s_ncand, s_T, s_need;
 
   const float* row = a.logits + (int64_t)q * a.ld;
   const int c0 = tid * kSinglePer;          // this thread owns entries [c0, c0+16)
@@ -518,8 +528,12 @@ __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a)
     }
     // cleared while the loads are in flight
     for (int i = tid; i < kHistBins; i += kSingleThreads) bins[i] = 0u;
+    if (tid == 0) s_ncand = 0u;
 #pragma unroll
     for (int j = 0; j < kSinglePer; ++j) key[j] = order_key(v[j]);   // entries past n_vis are never counted
+#pragma unroll
+    for (int j = 0; j < kSinglePer; j += 4)
+      *(uint4*)&key_lds[c0 + j] = make_uint4(key[j], key[j + 1], key[j + 2], key[j + 3]);
   }
   __syncthreads();
   // level 1: top 12 key bits of every entry (all lanes active: one LDS atomic instruction covers 64)
@@ -529,39 +543,98 @@ __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a)
   __syncthreads();
   if (wave == 0) wave_find_desc(bins, kHistBins, (uint32_t)k, &s_digit, &s_before);
   __syncthreads();
-  uint32_t prefix = s_digit;
-  uint32_t need = (uint32_t)k - s_before;
-  // levels 2 and 3: ten more key bits each, counting only entries with the current prefix
-#pragma unroll 1
-  for (int lvl = 0; lvl < 2; ++lvl) {
-    const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
-    for (int i = tid; i < 1024; i += kSingleThreads) bins[i] = 0u;
-    __syncthreads();
-    // few entries share the prefix: an atomic instruction is issued only where some lane needs it
+  const uint32_t bstar = s_digit;
+  const uint32_t need1 = (uint32_t)k - s_before;   // entries still to take from bin b* (>= 1)
+  // the entries of bin b* become candidates: their indices are appended to LDS with one atomic per
+  // wave, a lane's after those of the lanes below it
+  {
+    uint32_t hm = 0;   // bit j: entry c0 + j is in b*
 #pragma unroll
-    for (int j = 0; j < kSinglePer; ++j) {
-      const bool hit = c0 + j < nv && (key[j] >> (shift + 10)) == prefix;
-      if (__any(hit) && hit) atomicAdd(&bins[(key[j] >> shift) & 1023u], 1u);
+    for (int j = 0; j < kSinglePer; ++j) hm |= (c0 + j < nv && (key[j] >> kHistShift) == bstar) ? (1u << j) : 0u;
+    const uint32_t hits = __popc(hm);
+    const uint32_t incl = wave_inclusive_scan(hits);
+    uint32_t base = 0;
+    if (lane == 63 && incl) base = atomicAdd(&s_ncand, incl);
+    base = (uint32_t)__shfl((int)base, 63);
+    uint32_t pos = base + incl - hits;
+    while (hm) {
+      const int j = __ffs((int)hm) - 1;
+      hm &= hm - 1u;
+      if (pos < (uint32_t)kCandMax) cand_idx[pos] = (uint32_t)(c0 + j);
+      ++pos;
     }
-    __syncthreads();
-    if (wave == 0) wave_find_desc(bins, 1024, need, &s_digit, &s_before);
-    __syncthreads();
-    prefix = (prefix << 10) | s_digit;
-    need -= s_before;
   }
-  const uint32_t T = prefix;   // exact k-th largest key; the first `need` entries equal to it are taken
-  uint32_t n_gt = 0, n_eq = 0;
+  __syncthreads();
+  const uint32_t n_cand = s_ncand;
+  if (n_cand <= (uint32_t)kCandMax) {
+    // wave 0 alone resolves the 20 low key bits among the candidates (two 10-bit levels in a
+    // wave-private histogram); LDS operations of one wave complete in order
+    if (wave == 0) {
+      uint32_t prefix = bstar, need = need1;
+#pragma unroll 1
+      for (int lvl = 0; lvl < 2; ++lvl) {
+        const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
+#pragma unroll
+        for (int i = 0; i < 1024; i += 256) *(uint4*)&bins[i + 4 * lane] = make_uint4(0u, 0u, 0u, 0u);
+        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+        __builtin_amdgcn_wave_barrier();
+        for (uint32_t i = lane; i < n_cand; i += 64) {
+          const uint32_t kk = key_lds[cand_idx[i]];
+          if ((kk >> (shift + 10)) == prefix) atomicAdd(&bins[(kk >> shift) & 1023u], 1u);
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        wave_find_desc(bins, 1024, need, &s_digit, &s_before);
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+        prefix = (prefix << 10) | s_digit;
+        need -= s_before;
+      }
+      if (lane == 0) {
+        s_T = prefix;
+        s_need = need;
+      }
+    }
+  } else {
+    // many entries share b* (heavily tied scores): levels 2 and 3 over the whole block, ten more
+    // key bits each, counting only entries with the current prefix
+    uint32_t prefix = bstar, need = need1;
+#pragma unroll 1
+    for (int lvl = 0; lvl < 2; ++lvl) {
+      const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
+      for (int i = tid; i < 1024; i += kSingleThreads) bins[i] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kSinglePer; ++j) {
+        const bool hit = c0 + j < nv && (key[j] >> (shift + 10)) == prefix;
+        if (__any(hit) && hit) atomicAdd(&bins[(key[j] >> shift) & 1023u], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) wave_find_desc(bins, 1024, need, &s_digit, &s_before);
+      __syncthreads();
+      prefix = (prefix << 10) | s_digit;
+      need -= s_before;
+    }
+    if (tid == 0) {
+      s_T = prefix;
+      s_need = need;
+    }
+  }
+  __syncthreads();
+  const uint32_t T = s_T;        // exact k-th largest key
+  const uint32_t need = s_need;  // the first `need` entries equal to T (in index order) are taken
+  uint32_t gm = 0, em = 0;       // bit j: entry c0 + j is above T / equal to T
 #pragma unroll
   for (int j = 0; j < kSinglePer; ++j) {
     const bool ok = c0 + j < nv;
-    n_gt += ok && key[j] > T;
-    n_eq += ok && key[j] == T;
+    gm |= (ok && key[j] > T) ? (1u << j) : 0u;
+    em |= (ok && key[j] == T) ? (1u << j) : 0u;
   }
+  const uint32_t n_gt = __popc(gm), n_eq = __popc(em);
   // exclusive scan of (n_gt << 16 | n_eq) over threads by wave 0 (both totals stay below 2^16)
   scan[tid] = (n_gt << 16) | n_eq;
   __syncthreads();
   if (wave == 0) {
-    const int lane = tid;
     uint32_t c[16], sum = 0;
 #pragma unroll
     for (int j = 0; j < 16; j += 4) {
@@ -585,21 +658,25 @@ __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a)
   const uint32_t eq_before = pre & 0xFFFFu;
   uint32_t pos = (pre >> 16) + (eq_before < need ? eq_before : need);
   uint32_t take_eq = eq_before < need ? (need - eq_before < n_eq ? need - eq_before : n_eq) : 0u;
-#pragma unroll
-  for (int j = 0; j < kSinglePer; ++j) {
-    const bool ok = c0 + j < nv;
-    bool take = ok && key[j] > T;
-    if (ok && key[j] == T && take_eq) {
-      take = true;
-      --take_eq;
-    }
-    if (take) {
-      if (pos < (uint32_t)k) {
-        out[pos] = c0 + j;
-        if (a.rows) a.rows[(int64_t)q * a.ld_rows + pos] = row_of(c0 + j, pt_lds[(c0 + j) >> 6]);
-      }
-      ++pos;
-    }
+  // the taken entries: all above T, and the lowest-index take_eq of those equal to T
+  uint32_t tm = gm;
+  for (uint32_t t = 0; t < take_eq; ++t) {
+    const uint32_t low = em & (0u - em);
+    tm |= low;
+    em ^= low;
+  }
+  // selected entries land in LDS in ascending index order, then go out in coalesced stores
+  while (tm) {
+    const int j = __ffs((int)tm) - 1;
+    tm &= tm - 1u;
+    if (pos < (uint32_t)k) sel[pos] = c0 + j;
+    ++pos;
+  }
+  __syncthreads();
+  for (int i = tid; i < k; i += kSingleThreads) {
+    const int c = sel[i];
+    out[i] = c;
+    if (a.rows) a.rows[(int64_t)q * a.ld_rows + i] = row_of(c, pt_lds[c >> 6]);
   }
 }
 
