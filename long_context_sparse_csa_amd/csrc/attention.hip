@@ -254,6 +254,61 @@ constexpr int kAttnThreads = 512;   // waves 0-3 consume (matrix cores), waves 4
 #endif
 constexpr int kDepth = CSA_ATTN_DEPTH;   // tiles of row gathers in flight per producer wave
 
+// Producer side of the matrix-core kernels (waves 4-7 of a block): wave 4+p gathers rows 8p ..
+// 8p+7 of every 32-slot tile, one 16-B chunk (8 dims) per lane, kDepth tiles ahead in registers,
+// and dequantises tile j into ring buffer j % 3 just before barrier j, for j < nt.  The consumers
+// read tile j after barrier j and are done with it before barrier j + 2, so the buffer is free
+// again when tile j + 3 is staged.  The producers pass `nbar` >= nt + 1 barriers in all.
+template <int WF, int CF>
+__device__ __forceinline__ void produce_tiles(const uint64_t* codes, uint16_t (*Kr)[kTile * kKrStride], int nt,
+                                              int nbar, int lane, int wave) {
+  const int pw = wave - 4;
+  RawChunk raw[kDepth][8];
+  uint64_t rc[kDepth][8];
+  auto fetch = [&](int k, RawChunk* rw, uint64_t* c8) {
+    const int base = k * kTile + 8 * pw;
+#pragma unroll
+    for (int i = 0; i < 8; i += 2) {
+      const uint4 c = *(const uint4*)&codes[base + i];
+      c8[i] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.y) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.x);
+      c8[i + 1] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.w) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.z);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rw[i] = load_raw<WF, CF>(c8[i], lane);
+  };
+  auto stage = [&](int buf, const RawChunk* rw, const uint64_t* c8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *(uint4*)&Kr[buf][(8 * pw + i) * kKrStride + 8 * lane] = raw_to_bf16<WF, CF>(rw[i], c8[i], lane);
+  };
+  // tile j lives in raw slot j % kDepth from its fetch until it is staged
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j)
+    if (j < nt) fetch(j, raw[j], rc[j]);
+  if (nt > 0) {
+    stage(0, raw[0], rc[0]);
+    if (kDepth < nt) fetch(kDepth, raw[0], rc[0]);
+  }
+  __syncthreads();
+  int buf = 1;   // (k + 1) % 3
+  for (int k = 0; k < nt; k += kDepth) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      if (k + u < nt) {
+        constexpr int kDepthC = kDepth;
+        const int sl = (u + 1) % kDepthC;
+        if (k + u + 1 < nt) {
+          stage(buf, raw[sl], rc[sl]);
+          if (k + u + 1 + kDepth < nt) fetch(k + u + 1 + kDepth, raw[sl], rc[sl]);
+        }
+        buf = buf == 2 ? 0 : buf + 1;
+        __syncthreads();
+      }
+    }
+  }
+  for (int j = nt + 1; j < nbar; ++j) __syncthreads();
+}
+
 template <int WF, int CF>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -302,54 +357,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
     for (int dt = 0; dt < 8; ++dt) acc[hg][dt] = v4f{0.f, 0.f, 0.f, 0.f};
 
   if (wave >= 4) {
-    // ---- producers: wave 4+p gathers rows 8p .. 8p+7 of every tile, one 16-B chunk (8 dims) per
-    // lane, kDepth tiles ahead in registers.  During iteration k (between barriers k-1 and k) they
-    // dequantise tile k+1 into ring buffer (k+1) % 3, whose last reader (the P.V of tile k-2)
-    // finished before barrier k-1.
-    const int pw = wave - 4;
-    RawChunk raw[kDepth][8];
-    uint64_t rc[kDepth][8];
-    auto fetch = [&](int k, RawChunk* rw, uint64_t* c8) {
-      const int base = k * kTile + 8 * pw;
-#pragma unroll
-      for (int i = 0; i < 8; i += 2) {
-        const uint4 c = *(const uint4*)&codes[base + i];
-        c8[i] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.y) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.x);
-        c8[i + 1] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.w) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.z);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) rw[i] = load_raw<WF, CF>(c8[i], lane);
-    };
-    auto stage = [&](int buf, const RawChunk* rw, const uint64_t* c8) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *(uint4*)&Kr[buf][(8 * pw + i) * kKrStride + 8 * lane] = raw_to_bf16<WF, CF>(rw[i], c8[i], lane);
-    };
-    // tile j lives in raw slot j % kDepth from its fetch until it is staged
-#pragma unroll
-    for (int j = 0; j < kDepth; ++j)
-      if (j < nt) fetch(j, raw[j], rc[j]);
-    if (nt > 0) {
-      stage(0, raw[0], rc[0]);
-      if (kDepth < nt) fetch(kDepth, raw[0], rc[0]);
-    }
-    __syncthreads();
-    int buf = 1;   // (k + 1) % 3
-    for (int k = 0; k < nt; k += kDepth) {
-#pragma unroll
-      for (int u = 0; u < kDepth; ++u) {
-        if (k + u < nt) {
-          constexpr int kDepthC = kDepth;
-          const int sl = (u + 1) % kDepthC;
-          if (k + u + 1 < nt) {
-            stage(buf, raw[sl], rc[sl]);
-            if (k + u + 1 + kDepth < nt) fetch(k + u + 1 + kDepth, raw[sl], rc[sl]);
-          }
-          buf = buf == 2 ? 0 : buf + 1;
-          __syncthreads();
-        }
-      }
-    }
+    // ---- producers: tile j staged before barrier j; the consumers wait at nt + 1 barriers
+    produce_tiles<WF, CF>(codes, Kr, nt, nt + 1, lane, wave);
   } else {
     // ---- consumers, software-pipelined over tiles: iteration k runs the softmax of tile k (whose
     // scores the previous iteration computed), publishes P^T, waits at barrier k, then issues the
@@ -543,6 +552,162 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   store_rows((uint16_t*)a.part + prow0 * kD, kD, min(64, Hpad - h_base));
 }
 
+// 16-head variant for small query batches: a block owns one query, one head group of 16 and a
+// range of tiles, so with one block per (query, head group) no key split (and no combine) is
+// needed.  Producers are the same as in the 64-head kernel.  Consumer c computes the partial
+// scores of key block c & 1 over dims [256 (c >> 1), +256), the four partials meet in LDS, and
+// every consumer runs the same softmax on the summed scores, so P^T and the rescale factors never
+// cross waves.  Consumer c then accumulates output dims [128c, 128c+128).  One barrier per tile:
+// iteration k runs the softmax and P.V of tile k and the partial scores of tile k+1.
+template <int WF, int CF>
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int q = blockIdx.x % a.Q, split = blockIdx.x / a.Q;
+  const int Hpad = (a.H + 15) & ~15;
+  const int h_base = blockIdx.y * 16;
+  const int h = h_base + n;   // this lane's head
+
+  __shared__ __align__(16) uint16_t Kr[3][kTile * kKrStride];   // ring of three bf16 row tiles
+  __shared__ __align__(16) v4f Sp[2][4][64];                     // partial scores [tile & 1][consumer]
+  __shared__ float Xs[4][16];
+  __shared__ __align__(16) uint64_t codes[kMaxSlots];
+  __shared__ uint32_t vmask[kMaxSlots / kTile];
+
+  const int n_idx = a.n_win + a.n_comp;
+  const int n_tiles = (n_idx + kTile - 1) / kTile;
+  const int tps = (n_tiles + a.n_split - 1) / a.n_split;
+  const int t_begin = split * tps;
+  const int nt = max(0, min(n_tiles, t_begin + tps) - t_begin);
+  const int r = a.req_mode == 1 ? q : (a.req_mode == 2 ? 0 : a.q_req[q]);
+
+  const int kb = wave & 1, dh = wave >> 1;   // consumer roles (waves 0-3)
+  // q as the QK B operand: lane (n, g) holds dims 256 dh + 32ks + 8g .. +7 of head h (padded heads
+  // read head 0's row; their results are never written)
+  v8bf qop[8];
+  if (wave < 4) {
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)q * a.H + (h < a.H ? h : 0)) * kD + 256 * dh + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qop[ks] = *(const v8bf*)(qp + 32 * ks);
+  }
+  resolve_codes<kAttnThreads>(a, q, r, t_begin * kTile, nt * kTile, codes, vmask, tid);
+  __syncthreads();
+
+  float m = kNegBig, lsum = 0.f;   // softmax state of head h (identical in the four consumers)
+  v4f acc[8];                      // O^T[128 wave + 16 dt + 4 g + i][head h]
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  if (wave >= 4) {
+    produce_tiles<WF, CF>(codes, Kr, nt, nt + 2, lane, wave);
+  } else {
+    const float sc = a.softmax_scale * kLog2e;
+    // partial S^T[key 16 kb + 4g + i][head h] over this consumer's 256 dims
+    auto qk = [&](const uint16_t* K) {
+      v4f x = v4f{0.f, 0.f, 0.f, 0.f};
+      const uint16_t* kp = &K[(16 * kb + n) * kKrStride + 256 * dh + 8 * g];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) x = mma_bf16(*(const v8bf*)(kp + 32 * ks), qop[ks], x);
+      return x;
+    };
+    __syncthreads();                             // barrier 0: tile 0 staged
+    if (nt > 0) Sp[0][wave][lane] = qk(Kr[0]);
+    __syncthreads();                             // barrier 1: tile 1 staged, scores of tile 0 posted
+    int cur = 0;                                 // k % 3
+    for (int k = 0; k < nt; ++k) {
+      const int pb = k & 1;
+      const v4f s0 = Sp[pb][0][lane] + Sp[pb][2][lane];
+      const v4f s1 = Sp[pb][1][lane] + Sp[pb][3][lane];
+      const uint32_t vm = vmask[k];
+      float sv[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[i] = (vm >> (4 * g + i)) & 1u ? s0[i] * sc : -INFINITY;
+        sv[4 + i] = (vm >> (16 + 4 * g + i)) & 1u ? s1[i] * sc : -INFINITY;
+      }
+      float tmax = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, sv[e]);
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      // lazy rescaling as in the 64-head kernel; alpha is this lane's own head's
+      const bool grow = tmax > m + kRescaleLog2;
+      if (__builtin_expect(__any(grow), 0)) {
+        __asm__ volatile("" ::: "memory");
+        const float m_new = grow ? tmax : m;
+        const float alpha = exp2f(m - m_new);
+        lsum *= alpha;
+        m = m_new;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+      }
+      float p[8], psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p[e] = __builtin_amdgcn_exp2f(sv[e] - m);
+        psum += p[e];
+      }
+      lsum += psum;
+      // slot 8g+4mt+i of the K step <-> key 16mt+4g+i: this lane's part of the P^T operand
+      const v8bf pf = __builtin_bit_cast(v8bf, make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                                          pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])));
+      const uint16_t* K = Kr[cur];
+      const uint16_t* tr_lo = &K[(4 * g + (n >> 2)) * kKrStride + 4 * (n & 3) + 128 * wave];
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const v4s lo = lds_read_tr16(tr_lo + 16 * dt);
+        const v4s hi = lds_read_tr16(tr_lo + 16 * kKrStride + 16 * dt);
+        const v8bf vv = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[dt] = mma_bf16(vv, pf, acc[dt]);
+      }
+      cur = cur == 2 ? 0 : cur + 1;
+      if (k + 1 < nt) Sp[pb ^ 1][wave][lane] = qk(Kr[cur]);
+      __syncthreads();                           // barrier k + 2
+    }
+  }
+  float ltot = lsum + __shfl_xor(lsum, 16);
+  ltot += __shfl_xor(ltot, 32);
+  const int dbase = 128 * wave + 4 * g;
+  if (a.n_split == 1) {
+    if (wave >= 4 || h >= a.H) return;
+    const float sk = a.sink[h] * kLog2e;
+    const float M = fmaxf(m, sk);
+    const float f = exp2f(m - M);
+    const float inv = f / (ltot * f + exp2f(sk - M));
+    const int64_t ob = ((int64_t)q * a.H + h) * kD + dbase;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+      store4(a.out, a.out_dt, ob + 16 * dt, acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
+    return;
+  }
+  // split-K partial: m, l, amax = max |acc| over the head's 512 dims (fp32), acc / amax as fp16
+  if (wave < 4) {
+    float mx = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[dt][i]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (g == 0) Xs[wave][n] = mx;
+  }
+  __syncthreads();
+  if (wave >= 4) return;
+  const float amax = fmaxf(fmaxf(Xs[0][n], Xs[1][n]), fmaxf(Xs[2][n], Xs[3][n]));
+  const float f = amax > 0.f ? 1.f / amax : 0.f;
+  const int64_t prow = ((int64_t)q * a.n_split + split) * Hpad + h;
+  uint16_t* pa = (uint16_t*)a.part + prow * kD + dbase;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    *(uint2*)(pa + 16 * dt) = make_uint2(pack_f16x2(acc[dt][0] * f, acc[dt][1] * f),
+                                         pack_f16x2(acc[dt][2] * f, acc[dt][3] * f));
+  if (wave == 0 && g == 0) {
+    float* pml = (float*)((uint8_t*)a.part + (size_t)a.Q * a.n_split * Hpad * kD * sizeof(uint16_t));
+    *(float4*)(pml + prow * 4) = make_float4(m, ltot, amax, 0.f);
+  }
+}
+
 // Merge split-K partials: out = sum_s 2^(m_s-M) amax_s o_s / (sum_s 2^(m_s-M) l_s + 2^(sink-M)),
 // o_s the fp16 partial (acc_s / amax_s).  Block = one query, four heads; thread = 8 dims of a head.
 // Every partial is loaded up front (the split loop is unrolled to its maximum and predicated).
@@ -657,18 +822,32 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
+// Heads per block of the matrix-core kernels: 16 when the heads fit one group of 16 (no padded
+// head groups), else 64, where each dequantised K tile serves four head groups.  At 64 heads and
+// small batches the 16-head kernel (split or not) measured no faster than the 64-head one with a
+// key split: its per-tile cost is dequantisation and LDS latency, repeated for every head group.
+int attn_head_block(int Q, int H) {
+  (void)Q;
+  static const int forced = [] {
+    const char* e = getenv("CSA_ATTN_HEADS");   // tuning override: 16 or 64
+    return e ? atoi(e) : 0;
+  }();
+  if (forced == 16 || forced == 64) return forced;
+  return (H + 15) / 16 == 1 ? 16 : 64;
+}
+
 int plan_attn_split(int Q, int H, int n_idx, int q_dt) {
   if (q_dt == 0) return 1;
   static const int forced = [] {
     const char* e = getenv("CSA_ATTN_SPLIT");   // tuning override: fixed split count
     return e ? atoi(e) : 0;
   }();
+  const int n_tiles = (n_idx + kTile - 1) / kTile;
   if (forced > 0) {
-    const int n_tiles = (n_idx + kTile - 1) / kTile;
     return forced < kMaxSplit ? (forced < n_tiles ? forced : n_tiles) : (kMaxSplit < n_tiles ? kMaxSplit : n_tiles);
   }
-  const int hchunks = (((H + 15) & ~15) + 63) / 64;
-  const int n_tiles = (n_idx + kTile - 1) / kTile;
+  const int hb = attn_head_block(Q, H);
+  const int hchunks = (((H + 15) & ~15) + hb - 1) / hb;
   const int blocks = Q * hchunks;
   int s = (256 + blocks - 1) / blocks;
   const int max_s = n_tiles / 2 > 1 ? n_tiles / 2 : 1;
@@ -700,17 +879,25 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   const int Hpad = (a.H + 15) & ~15;
-  const int hchunks = (Hpad + 63) / 64;
+  const int hb = attn_head_block(a.Q, a.H);
+  const int hchunks = (Hpad + hb - 1) / hb;
   // a source with no slots takes the other source's format (its loads are never issued)
   const int wf = a.n_win > 0 ? a.win_fmt : a.comp_fmt;
   const int cf = a.n_comp > 0 ? a.comp_fmt : wf;
   {
     ProfScope p("attn_bf16", s);
     const dim3 grid((unsigned)(a.Q * a.n_split), (unsigned)hchunks);
-    if (wf == kRowFP8 && cf == kRowFP8) hipLaunchKernelGGL((attn_bf16_kernel<kRowFP8, kRowFP8>), grid, dim3(kAttnThreads), 0, s, a);
-    else if (wf == kRowFP8) hipLaunchKernelGGL((attn_bf16_kernel<kRowFP8, kRowBF16>), grid, dim3(kAttnThreads), 0, s, a);
-    else if (cf == kRowFP8) hipLaunchKernelGGL((attn_bf16_kernel<kRowBF16, kRowFP8>), grid, dim3(kAttnThreads), 0, s, a);
-    else hipLaunchKernelGGL((attn_bf16_kernel<kRowBF16, kRowBF16>), grid, dim3(kAttnThreads), 0, s, a);
+#define CSA_ATTN_LAUNCH(K)                                                                                    \
+  if (wf == kRowFP8 && cf == kRowFP8) hipLaunchKernelGGL((K<kRowFP8, kRowFP8>), grid, dim3(kAttnThreads), 0, s, a); \
+  else if (wf == kRowFP8) hipLaunchKernelGGL((K<kRowFP8, kRowBF16>), grid, dim3(kAttnThreads), 0, s, a);           \
+  else if (cf == kRowFP8) hipLaunchKernelGGL((K<kRowBF16, kRowFP8>), grid, dim3(kAttnThreads), 0, s, a);           \
+  else hipLaunchKernelGGL((K<kRowBF16, kRowBF16>), grid, dim3(kAttnThreads), 0, s, a);
+    if (hb == 16) {
+      CSA_ATTN_LAUNCH(attn_bf16_h16_kernel)
+    } else {
+      CSA_ATTN_LAUNCH(attn_bf16_kernel)
+    }
+#undef CSA_ATTN_LAUNCH
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
