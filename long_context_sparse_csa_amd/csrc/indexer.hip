@@ -69,8 +69,11 @@ __device__ __forceinline__ void flush_hist(uint32_t* lhist, uint32_t* ghist, int
   }
 }
 
+constexpr int kPagesPerWave = 4;   // pages scored by one wave, all of them loaded up front but one
+
 template <int NHG, bool HIST>
-__global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a, int pages_per_wave) {
+__global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
+  constexpr int pages_per_wave = kPagesPerWave;
   const int q = blockIdx.x;   // queries vary fastest: a row's blocks share one XCD (and its L2)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -136,12 +139,6 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a, int pag
     for (int kg = 0; kg < 4; ++kg) kb[kg] = load_k_operand(kp + (4 * n + kg) * kDI, g);
   };
 
-  int n_pages = pages_per_wave;
-  {
-    const int64_t rem = (a.max_n_vis + kPage - 1) / kPage - p_first;
-    if (rem < n_pages) n_pages = rem < 0 ? 0 : (int)rem;
-  }
-
   auto compute_page = [&](int i, const v8i* kb, int ksc) {
     const int64_t c0 = (p_first + i) * kPage;
     const bool live = c0 < nv && page_ok(i);
@@ -182,18 +179,20 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a, int pag
     }
   };
 
-  // ping-pong page buffers: the next page's loads are in flight while the current one computes
-  v8i kb0[4], kb1[4];
-  int ksc0 = 0, ksc1 = 0;
-  if (n_pages > 0) load_page(0, kb0, ksc0);
-  for (int i = 0; i < n_pages; i += 2) {
-    if (i + 1 < n_pages) load_page(i + 1, kb1, ksc1);
-    compute_page(i, kb0, ksc0);
-    if (i + 1 < n_pages) {
-      if (i + 2 < n_pages) load_page(i + 2, kb0, ksc0);
-      compute_page(i + 1, kb1, ksc1);
-    }
-  }
+  // Three page buffers, straight-line code: pages 0-2 are loaded up front and page 3 as soon as
+  // page 0 is scored, so up to three pages are in flight and every wait is for exactly the page
+  // about to be scored.  Pages past the wave's range load page 0 (always mapped) and store nothing.
+  static_assert(pages_per_wave == 4, "the schedule below scores four pages");
+  v8i kb0[4], kb1[4], kb2[4];
+  int ksc0 = 0, ksc1 = 0, ksc2 = 0;
+  load_page(0, kb0, ksc0);
+  load_page(1, kb1, ksc1);
+  load_page(2, kb2, ksc2);
+  compute_page(0, kb0, ksc0);
+  load_page(3, kb0, ksc0);
+  compute_page(1, kb1, ksc1);
+  compute_page(2, kb2, ksc2);
+  compute_page(3, kb0, ksc0);
   if constexpr (HIST) {
     __syncthreads();
     uint32_t* gh = a.hist + (int64_t)q * kHistBins;
@@ -264,19 +263,14 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
     else hipLaunchKernelGGL(indexer_f32_kernel<false>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  // 4 pages (256 entries) per wave with one page in flight ahead; 4 waves per block
-  static const int ppw_env = [] {
-    const char* e = getenv("CSA_IDX_PAGES_PER_WAVE");   // tuning override
-    return e ? atoi(e) : 0;
-  }();
-  const int pages_per_wave = ppw_env > 0 && ppw_env <= 64 ? ppw_env : 4;
-  const int per_block = 4 * pages_per_wave * kPage;
+  // four pages (256 entries) per wave, four waves per block
+  const int per_block = 4 * kPagesPerWave * kPage;
   dim3 grid((unsigned)a.Q, (unsigned)((a.max_n_vis + per_block - 1) / per_block));
   const int nhg = (a.HI + 15) / 16;
   ProfScope p("indexer_fp8", s);
 #define CSA_IDX_LAUNCH(N)                                                                              \
-  if (hist) hipLaunchKernelGGL((indexer_fp8_kernel<N, true>), grid, dim3(256), 0, s, a, pages_per_wave); \
-  else hipLaunchKernelGGL((indexer_fp8_kernel<N, false>), grid, dim3(256), 0, s, a, pages_per_wave);
+  if (hist) hipLaunchKernelGGL((indexer_fp8_kernel<N, true>), grid, dim3(256), 0, s, a); \
+  else hipLaunchKernelGGL((indexer_fp8_kernel<N, false>), grid, dim3(256), 0, s, a);
   switch (nhg) {
     case 1: CSA_IDX_LAUNCH(1) break;
     case 2: CSA_IDX_LAUNCH(2) break;
