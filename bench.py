@@ -208,7 +208,7 @@ def main():
     torch.cuda.synchronize()
     csa.csa_profile_enable(False)
     kernels = {}
-    for name in ("prep", "indexer_fp8", "indexer_f32", "topk_single", "topk_hist", "topk_collect", "topk_finish",
+    for name in ("prep", "indexer_fp8", "indexer_fp8_prefill", "indexer_f32", "topk_single", "topk_hist", "topk_collect", "topk_finish",
                  "attn_bf16",
                  "attn_combine", "attn_f32"):
         tot, n = csa.csa_profile_collect(name)

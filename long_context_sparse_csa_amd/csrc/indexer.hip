@@ -13,8 +13,9 @@
 // is slot 4n+kg, so lane l's scale dword is word l of the page's [4 blocks][64 slots] scale array
 // and the key group picks the byte (opsel).  The epilogue applies ReLU and the head weights, then a
 // 2-step reduce-scatter over the four lane groups leaves lane l with the full score of slot
-// 4*(l%16) + l/16.  Keys stream straight from HBM into VGPRs (no LDS): each lane loads 2 x 16 B per
-// key group, and each page is read exactly once.
+// 4*(l%16) + l/16.  Decode: keys stream straight from HBM into VGPRs (no LDS), each lane loads
+// 2 x 16 B per key group, and each page is read exactly once.  Causal prefill, where all queries
+// share one request's keys, stages key pages in LDS per block of queries instead (see below).
 #include <cstdlib>
 
 #include "csa_device.h"
@@ -27,8 +28,10 @@ __device__ __forceinline__ v4f mma_fp8_scaled(const v8i& a, const v8i& b, int sa
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, HG, sa, KG, sb);
 }
 
-// max(x, 0) in one v_med3_f32 (MFMA results are never signalling NaNs, so no canonicalisation)
-__device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, INFINITY); }
+// max(x, 0) as one integer max on the bit pattern: every negative float (and -0) is a negative
+// integer, every other float keeps its bits.  A float max costs two instructions here, because the
+// compiler first quiets possible signalling NaNs of the matrix-core result.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 __device__ __forceinline__ v8i load_k_operand(const uint8_t* row, int g) {
   uint4 lo = *(const uint4*)(row + 16 * g);
@@ -69,6 +72,74 @@ __device__ __forceinline__ void flush_hist(uint32_t* lhist, uint32_t* ghist, int
   }
 }
 
+// The query's indexer heads as scaled-MFMA A operands (padded heads zeroed), their E8M0 block
+// scales packed one byte per head group, and the head weights of this lane's output rows.
+template <int NHG>
+__device__ __forceinline__ void load_query(const IndexerArgs& a, int q, int n, int g, v8i* qa, int& qsc,
+                                           float (*wv)[4]) {
+  const uint8_t* qb = (const uint8_t*)a.qI + (int64_t)q * a.HI * kDI;
+  qsc = 0;
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+    const int h = 16 * hg + n;
+    const int hc = h < a.HI ? h : a.HI - 1;
+    const v8i v = load_k_operand(qb + hc * kDI, g);
+    const int sb = (int)a.qI_scale[((int64_t)q * a.HI + hc) * 4 + g];
+    const bool ok = h < a.HI;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qa[hg][e] = ok ? v[e] : 0;
+    qsc |= (ok ? sb : 127) << (8 * hg);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 16 * hg + 4 * g + i;
+      const float x = a.w[(int64_t)q * a.HI + (hh < a.HI ? hh : a.HI - 1)];
+      wv[hg][i] = hh < a.HI ? x : 0.f;
+    }
+  }
+}
+
+// Score of one page (64 entries) for one query: 4 x NHG scaled MFMAs, ReLU and head weights, then
+// a reduce-scatter over the four lane groups leaves lane (n, g) with the score of slot 4n + g.
+// The reduce-scatter uses the cross-half lane swaps (v_permlane32_swap: upper half of the first
+// operand <-> lower half of the second; v_permlane16_swap: odd 16-lane rows of the first <-> even
+// rows of the second), so the sum of the two swapped registers holds, in each half (row), the
+// total of the value that half (row) keeps: three swaps and three adds, no LDS round trip.
+__device__ __forceinline__ float swap_sum32(float keep_lo, float keep_hi) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(keep_lo), __float_as_uint(keep_hi), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap_sum16(float keep_even, float keep_odd) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(keep_even), __float_as_uint(keep_odd), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int NHG>
+__device__ __forceinline__ float score_page(const v8i* qa, int qsc, const float (*wv)[4], const v8i* kb, int ksc) {
+  v4f acc[NHG][4];
+  static_for<0, NHG>::run([&](auto HGc) {
+    constexpr int HG = decltype(HGc)::value;
+    static_for<0, 4>::run([&](auto KGc) {
+      constexpr int KG = decltype(KGc)::value;
+      acc[HG][KG] = mma_fp8_scaled<HG, KG>(qa[HG], kb[KG], qsc, ksc, v4f{0.f, 0.f, 0.f, 0.f});
+    });
+  });
+  float part[4];
+#pragma unroll
+  for (int kg = 0; kg < 4; ++kg) {
+    float sacc = 0.f;
+#pragma unroll
+    for (int hg = 0; hg < NHG; ++hg)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sacc = fmaf(wv[hg][e], relu(acc[hg][kg][e]), sacc);
+    part[kg] = sacc;
+  }
+  // lanes 0-31 keep key groups 0 and 1, lanes 32-63 key groups 2 and 3; then even rows keep the
+  // first of the pair and odd rows the second
+  const float k0 = swap_sum32(part[0], part[2]);
+  const float k1 = swap_sum32(part[1], part[3]);
+  return swap_sum16(k0, k1);
+}
+
 // Pages (64 entries each) scored by one wave.  Measured on the batched and long-context decode
 // workloads: 2 pages per wave is 15% slower than 4; 8 matches 4 on the first and is 4% faster on
 // the second.
@@ -93,27 +164,10 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
 
   // A operand: the query's indexer heads, resident in VGPRs.  Loads are unconditional (clamped
   // addresses, padded heads zeroed by select) so nothing waits before the first key page.
-  const uint8_t* qb = (const uint8_t*)a.qI + (int64_t)q * a.HI * kDI;
   v8i qa[NHG];
-  int qsc = 0;
+  int qsc;
   float wv[NHG][4];
-#pragma unroll
-  for (int hg = 0; hg < NHG; ++hg) {
-    const int h = 16 * hg + n;
-    const int hc = h < a.HI ? h : a.HI - 1;
-    const v8i v = load_k_operand(qb + hc * kDI, g);
-    const int sb = (int)a.qI_scale[((int64_t)q * a.HI + hc) * 4 + g];
-    const bool ok = h < a.HI;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qa[hg][e] = ok ? v[e] : 0;
-    qsc |= (ok ? sb : 127) << (8 * hg);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int hh = 16 * hg + 4 * g + i;
-      const float x = a.w[(int64_t)q * a.HI + (hh < a.HI ? hh : a.HI - 1)];
-      wv[hg][i] = hh < a.HI ? x : 0.f;
-    }
-  }
+  load_query<NHG>(a, q, n, g, qa, qsc, wv);
 
   const uint8_t* keys = (const uint8_t*)a.keys;
   const int32_t* pt = a.page_table + (int64_t)(r < 0 ? 0 : r) * a.max_pages;
@@ -145,33 +199,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   auto compute_page = [&](int i, const v8i* kb, int ksc) {
     const int64_t c0 = (p_first + i) * kPage;
     const bool live = c0 < nv && page_ok(i);
-    v4f acc[NHG][4];
-    static_for<0, NHG>::run([&](auto HGc) {
-      constexpr int HG = decltype(HGc)::value;
-      static_for<0, 4>::run([&](auto KGc) {
-        constexpr int KG = decltype(KGc)::value;
-        acc[HG][KG] = mma_fp8_scaled<HG, KG>(qa[HG], kb[KG], qsc, ksc, v4f{0.f, 0.f, 0.f, 0.f});
-      });
-    });
-    float part[4];
-#pragma unroll
-    for (int kg = 0; kg < 4; ++kg) {
-      float sacc = 0.f;
-#pragma unroll
-      for (int hg = 0; hg < NHG; ++hg)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sacc = fmaf(wv[hg][e], relu(acc[hg][kg][e]), sacc);
-      part[kg] = sacc;
-    }
-    // reduce-scatter over the 4 lane groups: lane (n, g) ends with the score of slot 4n+g
-    const bool b5 = (lane & 32) != 0;
-    float keep0 = b5 ? part[2] : part[0], keep1 = b5 ? part[3] : part[1];
-    const float send0 = b5 ? part[0] : part[2], send1 = b5 ? part[1] : part[3];
-    keep0 += __shfl_xor(send0, 32);
-    keep1 += __shfl_xor(send1, 32);
-    const bool b4 = (lane & 16) != 0;
-    const float keep = b4 ? keep1 : keep0, send = b4 ? keep0 : keep1;
-    const float score = keep + __shfl_xor(send, 16);
+    const float score = score_page<NHG>(qa, qsc, wv, kb, ksc);
     const int64_t c = c0 + 4 * n + g;
     if (c < a.max_n_vis) {
       const float v = (live && c < nv) ? score : -INFINITY;
@@ -201,6 +229,113 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
     for (int i = tid; i < kHistBins; i += 256) {
       const uint32_t v = lhist[i];
       if (v) atomicAdd(&gh[i], v);
+    }
+  }
+}
+
+// Causal prefill: every query scores the keys of request 0, so keys are shared across queries.  A
+// block stages kPfPages key pages (48 KB) and their scale words in LDS once and scores kPfQueries
+// consecutive queries against them (four per wave), instead of every query streaming every page.
+// The staged layout is the operand order, [page][key group kg][half][lane][16 B]: lane (n, g)'s
+// operand for key group kg is row 4n + kg, bytes 16g .. (half 0) and 64 + 16g .. (half 1), so every
+// LDS read of an operand half is 64 lanes x 16 contiguous bytes.  Staging uses direct global-to-LDS
+// loads (each lane fetches the chunk that belongs at its 16-byte slot), so no registers hold keys
+// in transit.  The kernel is bound by the matrix-core / VALU pair of each page score (16 scaled
+// MFMAs and 128 ReLU/weight operations), and one wave alone leaves both units half idle, so the
+// block is sized for three waves per SIMD: about 160 VGPRs and 50 KB of LDS (measured on the 8192-token
+// causal prefill: 8 pages at two waves per SIMD, with next-query prefetch and double-buffered key
+// operands, is 18% slower).  Query blocks are issued heaviest (latest) first.  Only the visible
+// prefix of each row is written: the selection reads nothing past it.
+constexpr int kPfPages = 6;
+constexpr int kPfQueries = 16;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef const __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// entries visible to causal-prefill query q: those with index < floor((pos0 + q + 1) / 4)
+__device__ __forceinline__ int64_t prefill_visible(const IndexerArgs& a, int q) {
+  const int64_t lim = min<int64_t>(a.max_n_vis, (int64_t)a.max_pages * kPage);
+  const int64_t nv = (a.pos0 + q + 1) / 4;
+  return a.n_req < 1 ? 0 : (nv > lim ? lim : nv);
+}
+
+template <int NHG>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void indexer_fp8_prefill_kernel(
+    IndexerArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int nbx = (a.Q + kPfQueries - 1) / kPfQueries;
+  const int q0 = (nbx - 1 - (int)blockIdx.x) * kPfQueries;       // heaviest query blocks first
+  const int64_t p0 = (int64_t)blockIdx.y * kPfPages;
+  if (p0 * kPage >= a.max_n_vis) return;
+  __shared__ __align__(16) uint8_t kl[kPfPages][4][2][64][16];   // [page][kg][half][lane] operand bytes
+  __shared__ __align__(16) uint32_t sl[kPfPages][64];             // scale word of lane l = word l
+  __shared__ int pid_s[kPfPages];
+
+  const int qw = q0 + 4 * wave;                                   // this wave's first query
+  const int nq = min(4, a.Q - qw);                                // its query count (may be <= 0)
+  const int qlast = min(q0 + kPfQueries, a.Q) - 1;
+  const int64_t nv_last = prefill_visible(a, qlast);              // the largest prefix of the block
+  if (p0 * kPage >= nv_last) return;   // no query of the block sees these pages
+
+  if (tid < kPfPages) {
+    const int64_t pp = p0 + tid;
+    int pid = -1;
+    if (pp * kPage < nv_last) pid = a.page_table[pp];
+    pid_s[tid] = pid;
+  }
+  __syncthreads();
+  // wave w stages pages w and w + 4: eight 1 KB loads per page (load j fills key group j / 2,
+  // half j % 2: lane L takes row 4 (L % 16) + kg, bytes 16 (L / 16) + 64 half), then the page's
+  // 256 scale bytes
+  const uint8_t* keys = (const uint8_t*)a.keys;
+  for (int pg = wave; pg < kPfPages; pg += 4) {
+    int pid = pid_s[pg];
+    pid = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
+    const uint8_t* kp = keys + (int64_t)pid * (kPage * kDI) + (4 * n) * kDI + 16 * g;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint8_t* src = kp + (j >> 1) * kDI + 64 * (j & 1);
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)&kl[pg][j >> 1][j & 1][0][0], 16, 0, 0);
+    }
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(a.kscale + (int64_t)pid * 256 + 4 * lane),
+                                     (lds_ptr_t)&sl[pg][0], 4, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // bit i: staged page i is mapped (wave-uniform)
+  uint32_t live_bits = 0;
+#pragma unroll
+  for (int i = 0; i < kPfPages; ++i) live_bits |= ((unsigned)pid_s[i] < (unsigned)a.num_pages ? 1u : 0u) << i;
+  live_bits = __builtin_amdgcn_readfirstlane(live_bits);
+
+  for (int j = 0; j < nq; ++j) {
+    const int q = qw + j;
+    const int64_t nv = prefill_visible(a, q);
+    float* lrow = a.logits + (int64_t)q * a.ld;
+    // pages of this block holding visible entries of q (wave-uniform)
+    const int64_t vis_end = nv - p0 * kPage;
+    const int np = vis_end <= 0 ? 0 : (int)min<int64_t>((vis_end + kPage - 1) / kPage, kPfPages);
+    if (np == 0) continue;
+    v8i qa[NHG];
+    int qsc;
+    float wv[NHG][4];
+    load_query<NHG>(a, q, n, g, qa, qsc, wv);
+    for (int pi = 0; pi < np; ++pi) {
+      v8i kb[4];
+      const int ksc = (int)sl[pi][lane];
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg) {
+        const uint4 lo = *(const uint4*)&kl[pi][kg][0][lane][0];
+        const uint4 hi = *(const uint4*)&kl[pi][kg][1][lane][0];
+        kb[kg][0] = (int)lo.x; kb[kg][1] = (int)lo.y; kb[kg][2] = (int)lo.z; kb[kg][3] = (int)lo.w;
+        kb[kg][4] = (int)hi.x; kb[kg][5] = (int)hi.y; kb[kg][6] = (int)hi.z; kb[kg][7] = (int)hi.w;
+      }
+      const bool live = (live_bits >> pi) & 1u;
+      const float score = score_page<NHG>(qa, qsc, wv, kb, ksc);
+      const int64_t c = (p0 + pi) * kPage + 4 * n + g;
+      if (c < a.max_n_vis) lrow[c] = (live && c < nv) ? score : -INFINITY;
     }
   }
 }
@@ -265,10 +400,23 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
     else hipLaunchKernelGGL(indexer_f32_kernel<false>, grid, dim3(256), 0, s, a);
     return hipGetLastError();
   }
+  const int nhg = (a.HI + 15) / 16;
+  if (a.vis_mode == 2 && !hist) {
+    // causal prefill: keys shared by all queries, staged once per block of queries
+    dim3 grid((unsigned)((a.Q + kPfQueries - 1) / kPfQueries),
+              (unsigned)((a.max_n_vis + kPfPages * kPage - 1) / (kPfPages * kPage)));
+    ProfScope p("indexer_fp8_prefill", s);
+    switch (nhg) {
+      case 1: hipLaunchKernelGGL((indexer_fp8_prefill_kernel<1>), grid, dim3(256), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((indexer_fp8_prefill_kernel<2>), grid, dim3(256), 0, s, a); break;
+      case 3: hipLaunchKernelGGL((indexer_fp8_prefill_kernel<3>), grid, dim3(256), 0, s, a); break;
+      default: hipLaunchKernelGGL((indexer_fp8_prefill_kernel<4>), grid, dim3(256), 0, s, a); break;
+    }
+    return hipGetLastError();
+  }
   // kPagesPerWave pages per wave, four waves per block
   const int per_block = 4 * kPagesPerWave * kPage;
   dim3 grid((unsigned)a.Q, (unsigned)((a.max_n_vis + per_block - 1) / per_block));
-  const int nhg = (a.HI + 15) / 16;
   ProfScope p("indexer_fp8", s);
 #define CSA_IDX_LAUNCH(N)                                                                              \
   if (hist) hipLaunchKernelGGL((indexer_fp8_kernel<N, true>), grid, dim3(256), 0, s, a); \

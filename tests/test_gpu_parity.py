@@ -220,3 +220,24 @@ def test_prefill_small(dev):
         check_topk_row(idx[t, 128:], scores, nv, wl.topk, f"t={t}")
         ref = O.attend(wl, t, idx[t, :128], idx[t, 128:])
         check_attention(out[t], ref, BF16_TOL, f"t={t}")
+
+
+def test_prefill_chunk_ragged(dev):
+    """A prefill chunk that starts mid-sequence, with a query count that is not a multiple of the
+    indexer's query block, a visible prefix that ends mid-page, and 40 indexer heads (padded to
+    48 inside the matrix-core kernels)."""
+    run, tio = _run()
+    wl = configs.causal_prefill(T=4100, HI=40, q_start=2003, q_count=1013, seed=5)
+    _say("prefill chunk (T=4100, q 2003..3015, HI=40)")
+    out, idx = run.prefill(wl, tio.to_device(wl, dev))
+    out, idx = tio.out_to_numpy(out), idx.cpu().numpy()
+    sample = sorted(set([0, 1, 2, 3, 14, 15, 16, 17, 252, 253, 1008, 1009, 1010, 1011, 1012] +
+                        np.random.default_rng(1).choice(wl.Q, 16, replace=False).tolist()))
+    for i in sample:
+        t = int(wl.positions[i])
+        nv = int(wl.n_vis[i])
+        scores = O.query_scores(wl, i)
+        assert idx[i, :128].tolist() == O.window_prefill(t).tolist()
+        check_topk_row(idx[i, 128:], scores, nv, wl.topk, f"t={t}")
+        ref = O.attend(wl, i, idx[i, :128], idx[i, 128:])
+        check_attention(out[i], ref, BF16_TOL, f"t={t}")
