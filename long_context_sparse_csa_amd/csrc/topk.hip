@@ -436,9 +436,8 @@ __global__ __launch_bounds__(256) void topk_finish_kernel(TopkArgs a) {
 //   3. one scan of the per-thread (greater, equal) counts, packed in one word, places the k
 //      indices in ascending order (equal keys at T in index order) in LDS, from where they are
 //      written with coalesced stores.
-constexpr int kSingleThreads = 1024;
-constexpr int kSingleMax = 16384;
-constexpr int kSinglePer = kSingleMax / kSingleThreads;   // 16 entries per thread, in index order
+constexpr int kSinglePer = 16;      // entries per thread, in index order
+constexpr int kSingleMax = 1024 * kSinglePer;   // longest row: 1024 threads
 constexpr int kCandMax = 2048;      // entries of the threshold bin resolved by one wave; more take
                                     // the block-wide path
 constexpr int kSingleMaxK = 2048;   // largest k
@@ -486,7 +485,11 @@ __device__ __forceinline__ void wave_find_desc(const uint32_t* bins, int nb, uin
   }
 }
 
-__global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a) {
+// NT threads cover rows of up to 16 NT entries; short rows take a small block so that several
+// rows share a CU (LDS: 16 KB of bins + 4 B per entry + 8 KB of candidates / selected indices).
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
+  constexpr int kRowMax = NT * kSinglePer;
   const int q = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t nv = topk_row_count(a, q);
   const int k = a.k;
@@ -496,22 +499,24 @@ __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a)
   const int32_t* pt = a.rows ? a.page_table + (int64_t)r * a.max_pages : nullptr;
   auto row_of = [&](int c, int pg) { return (unsigned)pg < (unsigned)a.num_pages ? pg * kPage + (c & (kPage - 1)) : -1; };
   if (nv <= k) {
-    for (int i = tid; i < k; i += kSingleThreads) {
+    for (int i = tid; i < k; i += NT) {
       out[i] = i < nv ? i : -1;
       if (a.rows) a.rows[(int64_t)q * a.ld_rows + i] = i < nv ? row_of(i, pt[i >> 6]) : -1;
     }
     return;
   }
-  __shared__ int32_t pt_lds[kSingleMax / kPage];
+  __shared__ int32_t pt_lds[kRowMax / kPage];
   if (a.rows) {
     // the request's page ids, loaded alongside the scores (rows >= 1: nv > k >= 1)
-    for (int p = tid; p < (int)((nv + kPage - 1) / kPage); p += kSingleThreads) pt_lds[p] = pt[p];
+    for (int p = tid; p < (int)((nv + kPage - 1) / kPage); p += NT) pt_lds[p] = pt[p];
   }
   __shared__ __align__(16) uint32_t bins[kHistBins];
-  __shared__ __align__(16) uint32_t scan[kSingleThreads];
-  __shared__ __align__(16) uint32_t key_lds[kSingleMax];   // order keys of the row, by entry
-  __shared__ uint32_t cand_idx[kCandMax];
-  __shared__ int32_t sel[kSingleMaxK];
+  __shared__ __align__(16) uint32_t scan[NT];
+  __shared__ __align__(16) uint32_t key_lds[kRowMax];   // order keys of the row, by entry
+  // candidate indices while the threshold is resolved, then the selected indices
+  __shared__ uint32_t cand_sel[kCandMax > kSingleMaxK ? kCandMax : kSingleMaxK];
+  uint32_t* cand_idx = cand_sel;
+  int32_t* sel = (int32_t*)cand_sel;
   __shared__ uint32_t s_digit, s_before, s_ncand, s_T, s_need;
 
   const float* row = a.logits + (int64_t)q * a.ld;
@@ -527,7 +532,7 @@ __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a)
       v[j] = x.x; v[j + 1] = x.y; v[j + 2] = x.z; v[j + 3] = x.w;
     }
     // cleared while the loads are in flight
-    for (int i = tid; i < kHistBins; i += kSingleThreads) bins[i] = 0u;
+    for (int i = tid; i < kHistBins; i += NT) bins[i] = 0u;
     if (tid == 0) s_ncand = 0u;
 #pragma unroll
     for (int j = 0; j < kSinglePer; ++j) key[j] = order_key(v[j]);   // entries past n_vis are never counted
@@ -602,7 +607,7 @@ __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a)
 #pragma unroll 1
     for (int lvl = 0; lvl < 2; ++lvl) {
       const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
-      for (int i = tid; i < 1024; i += kSingleThreads) bins[i] = 0u;
+      for (int i = tid; i < 1024; i += NT) bins[i] = 0u;
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < kSinglePer; ++j) {
@@ -635,23 +640,21 @@ __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a)
   scan[tid] = (n_gt << 16) | n_eq;
   __syncthreads();
   if (wave == 0) {
-    uint32_t c[16], sum = 0;
+    constexpr int SPL = NT / 64;   // thread counts per lane
+    uint32_t c[SPL], sum = 0;
 #pragma unroll
-    for (int j = 0; j < 16; j += 4) {
-      const uint4 x = *(const uint4*)&scan[16 * lane + j];
-      c[j] = x.x; c[j + 1] = x.y; c[j + 2] = x.z; c[j + 3] = x.w;
-    }
+    for (int j = 0; j < SPL; ++j) c[j] = scan[SPL * lane + j];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) sum += c[j];
+    for (int j = 0; j < SPL; ++j) sum += c[j];
     uint32_t run = wave_inclusive_scan(sum) - sum;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < SPL; ++j) {
       const uint32_t x = c[j];
       c[j] = run;
       run += x;
     }
 #pragma unroll
-    for (int j = 0; j < 16; j += 4) *(uint4*)&scan[16 * lane + j] = make_uint4(c[j], c[j + 1], c[j + 2], c[j + 3]);
+    for (int j = 0; j < SPL; ++j) scan[SPL * lane + j] = c[j];
   }
   __syncthreads();
   const uint32_t pre = scan[tid];
@@ -673,7 +676,7 @@ __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a)
     ++pos;
   }
   __syncthreads();
-  for (int i = tid; i < k; i += kSingleThreads) {
+  for (int i = tid; i < k; i += NT) {
     const int c = sel[i];
     out[i] = c;
     if (a.rows) a.rows[(int64_t)q * a.ld_rows + i] = row_of(c, pt_lds[c >> 6]);
@@ -682,7 +685,12 @@ __global__ __launch_bounds__(kSingleThreads) void topk_single_kernel(TopkArgs a)
 
 hipError_t launch_topk_single(const TopkArgs& a, hipStream_t s) {
   ProfScope p("topk_single", s);
-  hipLaunchKernelGGL(topk_single_kernel, dim3((unsigned)a.Q), dim3(kSingleThreads), 0, s, a);
+  if (a.max_n_vis <= 128 * kSinglePer)
+    hipLaunchKernelGGL(topk_single_kernel<128>, dim3((unsigned)a.Q), dim3(128), 0, s, a);
+  else if (a.max_n_vis <= 256 * kSinglePer)
+    hipLaunchKernelGGL(topk_single_kernel<256>, dim3((unsigned)a.Q), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(topk_single_kernel<1024>, dim3((unsigned)a.Q), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

@@ -76,15 +76,25 @@ def _fp32_score_bound(wl, qi):
 
 
 # ------------------------------------------------------------------------------------ top-k
-def _topk_cases(rng, long_row=True):
-    cases = []
-    for n_vis in [0, 1, 511, 512, 513, 777, 5000] + ([70000] if long_row else []):
-        cases.append(rng.standard_normal(n_vis).astype(np.float32))
-    ties = rng.integers(0, 7, size=9000).astype(np.float32)                # heavy ties at the threshold
+# Row lengths per selection path: rows longer than 16,384 entries take the multi-launch selection;
+# shorter rows take one block per query, of 1024, 256 or 128 threads for rows of up to 16,384,
+# 4,096 or 2,048 entries (the longest row of the call decides).
+_TOPK_LENGTHS = {
+    "multi_block": ([0, 1, 511, 512, 513, 777, 5000, 70000], 9000),
+    "single_1024": ([0, 1, 511, 512, 513, 777, 5000, 16384], 9000),
+    "single_256": ([0, 1, 511, 512, 513, 777, 2049, 4096], 4000),
+    "single_128": ([0, 1, 511, 512, 513, 777, 1500, 2048], 2000),
+}
+
+
+def _topk_cases(rng, size_class):
+    lengths, m = _TOPK_LENGTHS[size_class]
+    cases = [rng.standard_normal(n_vis).astype(np.float32) for n_vis in lengths]
+    ties = rng.integers(0, 7, size=m).astype(np.float32)                   # heavy ties at the threshold
     cases.append(ties)
-    flat = np.full(6000, 1.5, np.float32)                                   # every score equal
+    flat = np.full(m * 2 // 3, 1.5, np.float32)                             # every score equal
     cases.append(flat)
-    mixed = rng.standard_normal(3000).astype(np.float32)
+    mixed = rng.standard_normal(m // 3).astype(np.float32)
     mixed[::7] = -np.inf
     mixed[5::11] = np.nan
     mixed[3::13] = -0.0
@@ -96,16 +106,15 @@ def _topk_cases(rng, long_row=True):
     return cases
 
 
-@pytest.mark.parametrize("long_row", [True, False], ids=["multi_block", "single_block"])
+@pytest.mark.parametrize("size_class", list(_TOPK_LENGTHS))
 @pytest.mark.parametrize("k", [512, 1, 100, 2048])
-def test_topk_exact(dev, k, long_row):
-    """Exact selection on ties, NaN, -inf, +-0 and all-equal rows.  Without the 70,000-entry row every
-    row fits the one-block-per-query selection (<= 16,384 entries), whose threshold bin is resolved
-    by one wave when it holds at most 2,048 entries (the tied rows) and block-wide otherwise (the
-    all-equal row)."""
+def test_topk_exact(dev, k, size_class):
+    """Exact selection on ties, NaN, -inf, +-0 and all-equal rows, for every selection path.  In the
+    one-block-per-query paths the threshold bin is resolved by one wave when it holds at most 2,048
+    entries (the tied rows) and block-wide otherwise (the all-equal rows)."""
     run, _ = _run()
     rng = np.random.default_rng(5 + k)
-    cases = _topk_cases(rng, long_row)
+    cases = _topk_cases(rng, size_class)
     n = [len(c) for c in cases]
     max_n = max(n)
     ld = (max_n + 63) // 64 * 64
