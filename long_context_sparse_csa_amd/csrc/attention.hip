@@ -8,18 +8,20 @@
 //
 // BF16 matrix-core kernel (q bf16): a block owns one query, up to 64 heads (four head groups of
 // 16) and a contiguous range of 32-slot tiles.  All slots of the range are resolved to row
-// addresses up front.  Per tile the four waves gather the 32 rows once (coalesced: one 16-B lane
-// chunk per 8 dims of a row, FP8 nope dequantised with its fp32 block scale) into one of two
-// row-major bf16 LDS tiles, so the next tile is dequantised while the matrix cores work on this
-// one.  Wave w computes the scores of head group w (q in registers) with v_mfma_f32_16x16x32_bf16,
-// computing S transposed (S^T = K.q^T) so each lane holds 8 scores of its own head; once the key
+// addresses up front.  Eight waves in two roles share each SIMD: score wave w keeps q of head group
+// w in registers, gathers rows 8w .. 8w+7 of every tile (coalesced: one 16-B lane chunk per 8 dims
+// of a row, FP8 nope dequantised with its fp32 block scale) two tiles ahead into a ring of four
+// row-major bf16 LDS tiles, computes the scores with v_mfma_f32_16x16x32_bf16 and runs the online
+// softmax; value wave 4 + w accumulates output dims [128w, 128w+128) of all 64 heads.  Scores are
+// computed transposed (S^T = K.q^T) so each lane holds 8 scores of its own head; once the key
 // order inside the 32-wide K step is permuted (slot 8g+4mt+i <-> key 16mt+4g+i) these are exactly
-// the P^T operand of O^T = V^T.P^T.  The four P^T operands are exchanged through LDS and wave w
-// then accumulates output dims [128w, 128w+128) of all 64 heads, reading V^T from the same
-// row-major tile with gfx950's transposing LDS load (ds_read_b64_tr_b16): each V fragment feeds
-// four MFMAs and no transposed copy is ever written.  Softmax runs in base 2 with log2(e) folded
-// into the scale.  Large queries-by-heads grids run unsplit; small ones split the slot range
-// across blocks and a combine kernel merges the (max, sum, acc) partials, sink included.
+// the P^T operand of O^T = V^T.P^T, which the value waves read from LDS.  They read V^T from the
+// same row-major tile with gfx950's transposing LDS load (ds_read_b64_tr_b16): each V fragment
+// feeds four MFMAs and no transposed copy is ever written.  The two roles run a tile apart (the
+// scores and softmax of tile p overlap P.V of tile p - 2 on the same SIMD), one barrier per tile.
+// Softmax runs in base 2 with log2(e) folded into the scale.  Large queries-by-heads grids run
+// unsplit; small ones split the slot range across blocks and a combine kernel merges the
+// (max, sum, acc) partials, sink included.
 //
 // fp32 kernel (q f32): one block per (query, head); scores, softmax and P.V in fp32 with natural
 // exp, for bit-accurate-ish comparisons against the fp64 definition.
@@ -237,7 +239,7 @@ __device__ __forceinline__ uint4 raw_to_bf16(const RawChunk& r, uint64_t code, i
   return w;
 }
 
-constexpr int kMaxSlots = 4096;
+constexpr int kMaxSlots = 1024;   // slots of one block: longer index lists are split
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
@@ -253,6 +255,10 @@ constexpr int kAttnThreads = 512;   // waves 0-3 consume (matrix cores), waves 4
 #define CSA_ATTN_DEPTH 4
 #endif
 constexpr int kDepth = CSA_ATTN_DEPTH;   // tiles of row gathers in flight per producer wave
+#ifndef CSA_SCORE_DEPTH
+#define CSA_SCORE_DEPTH 2
+#endif
+constexpr int kScoreDepth = CSA_SCORE_DEPTH;   // the same for the score waves of the 64-head kernel
 
 // Producer side of the matrix-core kernels (waves 4-7 of a block): wave 4+p gathers rows 8p ..
 // 8p+7 of every 32-slot tile, one 16-B chunk (8 dims) per lane, kDepth tiles ahead in registers,
@@ -320,7 +326,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   const int Hpad = (a.H + 15) & ~15;
   const int h_base = blockIdx.y * 64;
 
-  __shared__ __align__(16) uint16_t Kr[3][kTile * kKrStride];   // ring of three bf16 row tiles
+  __shared__ __align__(16) uint16_t Kr[4][kTile * kKrStride];   // ring of four bf16 row tiles
   __shared__ __align__(16) uint4 Ps[2][4][64];                   // P^T operand of each head group
   __shared__ __align__(16) int Fl[2][4];                         // head group rescaled this tile
   __shared__ float As[2][64];                                    // its per-head rescale factors
@@ -336,9 +342,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   const int r = a.req_mode == 1 ? q : (a.req_mode == 2 ? 0 : a.q_req[q]);
   const int s_begin = t_begin * kTile;
 
-  // consumers: q of this wave's 16 heads stays in registers as the QK B operand: lane (n, g) holds
-  // dims 32ks + 8g .. +7 of head h_base + 16 wave + n.  Padded heads read head 0's row; their
-  // results are never written.
+  // score waves: q of this wave's 16 heads stays in registers as the QK B operand: lane (n, g)
+  // holds dims 32ks + 8g .. +7 of head h_base + 16 wave + n.  Padded heads read head 0's row;
+  // their results are never written.
   v8bf qreg[16];
   if (wave < 4) {
     const int hq = h_base + 16 * wave + n;
@@ -349,27 +355,56 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   resolve_codes<kAttnThreads>(a, q, r, s_begin, nt * kTile, codes, vmask, tid);
   __syncthreads();
 
-  float m = kNegBig, lsum = 0.f;   // consumer softmax state of head h_base + 16 wave + n
-  v4f acc[4][8];                   // O^T[128 wave + 16 dt + 4 g + i][h_base + 16 hg + n]
+  float m = kNegBig, lsum = 0.f;   // score-wave softmax state of head h_base + 16 wave + n
+  v4f acc[4][8];                   // value waves: O^T[128 dw + 16 dt + 4 g + i][h_base + 16 hg + n]
 #pragma unroll
   for (int hg = 0; hg < 4; ++hg)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) acc[hg][dt] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  if (wave >= 4) {
-    // ---- producers: tile j staged before barrier j; the consumers wait at nt + 1 barriers
-    produce_tiles<WF, CF>(codes, Kr, nt, nt + 1, lane, wave);
-  } else {
-    // ---- consumers, software-pipelined over tiles: iteration k runs the softmax of tile k (whose
-    // scores the previous iteration computed), publishes P^T, waits at barrier k, then issues the
-    // scores of tile k+1 and the P.V of tile k back to back on the matrix cores
-    __syncthreads();
-    const float sc = a.softmax_scale * kLog2e;
-    // S^T[key][head] of this wave's head group for keys 0..15 (s0) and 16..31 (s1)
-    v4f s0, s1;
-    auto qk = [&](const uint16_t* K) {
-      s0 = v4f{0.f, 0.f, 0.f, 0.f};
-      s1 = v4f{0.f, 0.f, 0.f, 0.f};
+  // Phase p (ending at barrier p) of the tile loop: the score waves issue the scores of tile p on
+  // the matrix cores, run the softmax of tile p - 1 (its scores were computed in phase p - 1) and
+  // publish its P^T, then stage tile p + 1 into the ring slot of tile p - 3, which nobody reads
+  // after phase p - 1; the value waves accumulate P.V of tile p - 2.
+  if (wave < 4) {
+    const int pw = wave;   // staged rows 8pw .. 8pw+7 of every tile
+    // codes of this wave's rows, entry 8t + i = row 8pw + i of tile t, in VGPRs: lane l of word j
+    // holds entry 64j + l, so a fetch picks them with scalar lane reads instead of an LDS round trip
+    uint32_t cw_lo[kMaxSlots / 4 / 64], cw_hi[kMaxSlots / 4 / 64];
+#pragma unroll
+    for (int j = 0; j < kMaxSlots / 4 / 64; ++j) {
+      const int e = 64 * j + lane;                 // entry: tile e / 8, row e % 8
+      const int sidx = (e >> 3) * kTile + 8 * pw + (e & 7);
+      const uint64_t c = e < 8 * nt ? codes[sidx] : 0ull;
+      cw_lo[j] = (uint32_t)c;
+      cw_hi[j] = (uint32_t)(c >> 32);
+    }
+    RawChunk raw[kScoreDepth][8];
+    uint64_t rc[kScoreDepth][8];
+    auto fetch = [&](int k, RawChunk* rw, uint64_t* c8) {
+      const int j = k >> 3;                        // word of tile k's entries (wave-uniform)
+      uint32_t lo = cw_lo[0], hi = cw_hi[0];
+#pragma unroll
+      for (int jj = 1; jj < kMaxSlots / 4 / 64; ++jj) {
+        lo = j == jj ? cw_lo[jj] : lo;
+        hi = j == jj ? cw_hi[jj] : hi;
+      }
+      const int l0 = (8 * k) & 63;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        c8[i] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, l0 + i) << 32) |
+                (uint32_t)__builtin_amdgcn_readlane(lo, l0 + i);   // zero-extended: the lane read is an int
+#pragma unroll
+      for (int i = 0; i < 8; ++i) rw[i] = load_raw<WF, CF>(c8[i], lane);
+    };
+    auto stage = [&](uint16_t* K, const RawChunk* rw, const uint64_t* c8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        *(uint4*)&K[(8 * pw + i) * kKrStride + 8 * lane] = raw_to_bf16<WF, CF>(rw[i], c8[i], lane);
+    };
+    // S^T[key][head] of this wave's head group for keys 0..15 (s[0]) and 16..31 (s[1])
+    auto scores = [&](const uint16_t* K, v4f* sv) {
+      v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) {
         const v8bf k0 = *(const v8bf*)&K[n * kKrStride + 32 * ks + 8 * g];
@@ -377,23 +412,23 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
         s0 = mma_bf16(k0, qreg[ks], s0);
         s1 = mma_bf16(k1, qreg[ks], s1);
       }
+      sv[0] = s0;
+      sv[1] = s1;
     };
-    qk(Kr[0]);
-    int cur = 0;   // k % 3
-    for (int k = 0; k < nt; ++k) {
-      const int pb = k & 1;
-      const uint32_t vm = vmask[k];
-      float sv[8];
+    const float sc = a.softmax_scale * kLog2e;
+    // softmax of tile t with valid-slot mask vm (vm = 0: no slot, the state is left unchanged)
+    auto softmax = [&](int t, uint32_t vm, const v4f* sv) {
+      const int pb = t & 1;
+      float x[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sv[i] = (vm >> (4 * g + i)) & 1u ? s0[i] * sc : -INFINITY;
-        sv[4 + i] = (vm >> (16 + 4 * g + i)) & 1u ? s1[i] * sc : -INFINITY;
+        x[i] = (vm >> (4 * g + i)) & 1u ? sv[0][i] * sc : -INFINITY;
+        x[4 + i] = (vm >> (16 + 4 * g + i)) & 1u ? sv[1][i] * sc : -INFINITY;
       }
-      float tmax = sv[0];
+      float tmax = x[0];
 #pragma unroll
-      for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, sv[e]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
+      tmax = row_group_max(tmax);
       // lazy rescaling: the reference max moves only when a head's max grows by more than 2^8, so
       // the accumulators are touched rarely; p = 2^(S - m) then stays below 256
       const bool grow = tmax > m + kRescaleLog2;
@@ -408,68 +443,101 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
         m = m_new;
         fl = 1;
       }
-      float p[8], psum = 0.f;
+      float pr[8], psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(sv[e] - m);
-        psum += p[e];
+        pr[e] = __builtin_amdgcn_exp2f(x[e] - m);
+        psum += pr[e];
       }
       lsum += psum;
       // slot 8g+4mt+i of the K step <-> key 16mt+4g+i: these 8 values are exactly this lane's part
-      // of the P^T operand, for every wave that multiplies this head group
-      Ps[pb][wave][lane] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                                      pack_bf16x2(p[6], p[7]));
+      // of the P^T operand, for every value wave
+      Ps[pb][wave][lane] = make_uint4(pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]),
+                                      pack_bf16x2(pr[4], pr[5]), pack_bf16x2(pr[6], pr[7]));
       if (g == 0) As[pb][16 * wave + n] = alpha;
       if (lane == 0) Fl[pb][wave] = fl;
-      __syncthreads();
-
-      const int nxt = cur == 2 ? 0 : cur + 1;
-      // scores of tile k+1 (past the last tile this reads a stale buffer; the result is unused)
-      qk(Kr[nxt]);
-      const uint16_t* K = Kr[cur];
-      const int4 f4 = *(const int4*)Fl[pb];
-      if (__builtin_expect((f4.x | f4.y | f4.z | f4.w) != 0, 0)) {
-        __asm__ volatile("" ::: "memory");
+    };
+    // tile j lives in raw slot j % kScoreDepth from its fetch until it is staged
 #pragma unroll
-        for (int hg = 0; hg < 4; ++hg) {
-          const float al = As[pb][16 * hg + n];
+    for (int j = 0; j < kScoreDepth; ++j)
+      if (j < nt) fetch(j, raw[j], rc[j]);
+    if (nt > 0) {
+      stage(Kr[0], raw[0], rc[0]);
+      if (kScoreDepth < nt) fetch(kScoreDepth, raw[0], rc[0]);
+    }
+    __syncthreads();
+    v4f sv[2][2];   // scores of the tiles of even and odd index
+    for (int p0 = 0; p0 <= nt; p0 += kScoreDepth) {
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) acc[hg][dt] *= al;
+      for (int u = 0; u < kScoreDepth; ++u) {
+        const int p = p0 + u;
+        if (p <= nt) {
+          constexpr int kDepthC = kScoreDepth;
+          const int sl = (u + 1) % kDepthC;   // raw slot of tile p + 1
+          // p = nt scores a stale tile (never used); p = 0 runs a softmax over no slot (a no-op)
+          scores(Kr[p & 3], sv[u & 1]);
+          softmax(p - 1, p >= 1 ? vmask[p - 1] : 0u, sv[(u + 1) & 1]);
+          // staging last keeps its LDS writes out of the way of this phase's operand reads
+          if (p + 1 < nt) {
+            stage(Kr[(p + 1) & 3], raw[sl], rc[sl]);
+            if (p + 1 + kScoreDepth < nt) fetch(p + 1 + kScoreDepth, raw[sl], rc[sl]);
+          }
+          __syncthreads();
         }
       }
-      v8bf pf[4];
-#pragma unroll
-      for (int hg = 0; hg < 4; ++hg) pf[hg] = __builtin_bit_cast(v8bf, Ps[pb][hg][lane]);
-
-      // O^T[d][head] += V^T[d][slot] . P^T[slot][head] over this wave's 128 dims, all head groups;
-      // V^T comes from the row-major tile through the transposing LDS read: source lane s of group
-      // g points at key row 4g + s/4 (slots 8g..8g+3) or 16 + 4g + s/4 (slots 8g+4..8g+7), dims
-      // 4(s%4) .. +3
-      const uint16_t* tr_lo = &K[(4 * g + (n >> 2)) * kKrStride + 4 * (n & 3) + 128 * wave];
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        const v4s lo = lds_read_tr16(tr_lo + 16 * dt);
-        const v4s hi = lds_read_tr16(tr_lo + 16 * kKrStride + 16 * dt);
-        const v8bf vv = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int hg = 0; hg < 4; ++hg) acc[hg][dt] = mma_bf16(vv, pf[hg], acc[hg][dt]);
-      }
-      cur = nxt;
     }
-    float ltot = lsum + __shfl_xor(lsum, 16);
-    ltot += __shfl_xor(ltot, 32);
+    __syncthreads();   // phase nt + 1: the value waves finish tile nt - 1
+    const float ltot = row_group_sum(lsum);
     if (g == 0) {
       Ms[16 * wave + n] = m;
       Ls[16 * wave + n] = ltot;
     }
+  } else {
+    const int dw = wave - 4;   // output dims [128 dw, 128 dw + 128)
+    __syncthreads();
+    for (int p = 0; p <= nt + 1; ++p) {
+      if (p >= 2) {
+        const int t = p - 2;
+        const int pb = t & 1;
+        const uint16_t* K = Kr[t & 3];
+        const int4 f4 = *(const int4*)Fl[pb];
+        if (__builtin_expect((f4.x | f4.y | f4.z | f4.w) != 0, 0)) {
+          __asm__ volatile("" ::: "memory");
+#pragma unroll
+          for (int hg = 0; hg < 4; ++hg) {
+            const float al = As[pb][16 * hg + n];
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) acc[hg][dt] *= al;
+          }
+        }
+        v8bf pf[4];
+#pragma unroll
+        for (int hg = 0; hg < 4; ++hg) pf[hg] = __builtin_bit_cast(v8bf, Ps[pb][hg][lane]);
+        // O^T[d][head] += V^T[d][slot] . P^T[slot][head] over this wave's 128 dims, all head
+        // groups; V^T comes from the row-major tile through the transposing LDS read: source lane s
+        // of group g points at key row 4g + s/4 (slots 8g..8g+3) or 16 + 4g + s/4 (slots
+        // 8g+4..8g+7), dims 4(s%4) .. +3
+        const uint16_t* tr_lo = &K[(4 * g + (n >> 2)) * kKrStride + 4 * (n & 3) + 128 * dw];
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const v4s lo = lds_read_tr16(tr_lo + 16 * dt);
+          const v4s hi = lds_read_tr16(tr_lo + 16 * kKrStride + 16 * dt);
+          const v8bf vv = __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int hg = 0; hg < 4; ++hg) acc[hg][dt] = mma_bf16(vv, pf[hg], acc[hg][dt]);
+        }
+      }
+      __syncthreads();
+    }
   }
   __syncthreads();
-  const int dbase = 128 * wave + 4 * g;
+  const int dw = wave - 4;   // value waves: output dims [128 dw, 128 dw + 128)
+  const int dbase = 128 * dw + 4 * g;
   // 16-bit output rows (bf16 results, fp16 partials) are staged in the idle row tiles, 1056 B per
   // head, so that every wave then stores whole 1 KB rows with one instruction each
   constexpr int kStage = kKrStride;
   uint16_t* stg = &Kr[0][0];
-  static_assert(64 * kStage <= 3 * kTile * kKrStride, "staging fits the row tiles");
+  static_assert(64 * kStage <= 4 * kTile * kKrStride, "staging fits the row tiles");
   auto store_rows = [&](uint16_t* base, int64_t row_stride, int nrows) {
     // wave w writes staged rows 8w .. 8w+7 (those below nrows) to base + row * row_stride
 #pragma unroll
@@ -479,7 +547,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
     }
   };
   if (a.n_split == 1) {
-    if (wave < 4) {
+    if (wave >= 4) {
       float inv[4];
 #pragma unroll
       for (int hg = 0; hg < 4; ++hg) {
@@ -518,7 +586,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   }
   // split-K partial of each head: m, l, amax = max |acc| over the 512 dims (fp32) and acc / amax
   // as fp16 (|value| <= 1, so the only loss is fp16's 11-bit rounding relative to amax)
-  if (wave < 4) {
+  if (wave >= 4) {
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg) {
       float mx = 0.f;
@@ -526,14 +594,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[hg][dt][i]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      if (g == 0) Xs[wave][16 * hg + n] = mx;
+      mx = row_group_max(mx);
+      if (g == 0) Xs[dw][16 * hg + n] = mx;
     }
   }
   __syncthreads();
   const int64_t prow0 = ((int64_t)q * a.n_split + split) * Hpad + h_base;   // partial row of head h_base
-  if (wave < 4) {
+  if (wave >= 4) {
     float* pml = (float*)((uint8_t*)a.part + (size_t)a.Q * a.n_split * Hpad * kD * sizeof(uint16_t));
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg) {
@@ -544,7 +611,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
       for (int dt = 0; dt < 8; ++dt)
         *(uint2*)&stg[hl * kStage + dbase + 16 * dt] = make_uint2(pack_f16x2(acc[hg][dt][0] * f, acc[hg][dt][1] * f),
                                                                 pack_f16x2(acc[hg][dt][2] * f, acc[hg][dt][3] * f));
-      if (hg == wave && g == 0 && h_base + hl < Hpad)
+      if (hg == dw && g == 0 && h_base + hl < Hpad)
         *(float4*)(pml + (prow0 + hl) * 4) = make_float4(Ms[hl], Ls[hl], amax, 0.f);
     }
   }
@@ -843,8 +910,11 @@ int plan_attn_split(int Q, int H, int n_idx, int q_dt) {
     return e ? atoi(e) : 0;
   }();
   const int n_tiles = (n_idx + kTile - 1) / kTile;
+  // a block holds at most kMaxSlots slots (n_idx <= 4096 keeps this within kMaxSplit)
+  const int min_s = (n_tiles + kMaxSlots / kTile - 1) / (kMaxSlots / kTile);
   if (forced > 0) {
-    return forced < kMaxSplit ? (forced < n_tiles ? forced : n_tiles) : (kMaxSplit < n_tiles ? kMaxSplit : n_tiles);
+    const int f = forced < kMaxSplit ? (forced < n_tiles ? forced : n_tiles) : (kMaxSplit < n_tiles ? kMaxSplit : n_tiles);
+    return f > min_s ? f : min_s;
   }
   const int hb = attn_head_block(Q, H);
   const int hchunks = (((H + 15) & ~15) + hb - 1) / hb;
@@ -853,6 +923,7 @@ int plan_attn_split(int Q, int H, int n_idx, int q_dt) {
   const int max_s = n_tiles / 2 > 1 ? n_tiles / 2 : 1;
   if (s > max_s) s = max_s;
   if (s > kMaxSplit) s = kMaxSplit;
+  if (s < min_s) s = min_s;
   if (s < 1) s = 1;
   return s;
 }

@@ -80,6 +80,25 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Max / sum over lanes l, l^16, l^32, l^48 (the four 16-lane rows), broadcast to all four, with
+// the cross-row lane swaps (v_permlane32_swap: upper half of the first operand <-> lower half of
+// the second; v_permlane16_swap: odd rows of the first <-> even rows of the second) instead of
+// LDS-routed shuffles.  Swapping a value with itself leaves the two halves (rows) side by side in
+// the two results.
+__device__ __forceinline__ float row_group_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float row_group_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int I, int N>
 struct static_for {
   template <class F>
