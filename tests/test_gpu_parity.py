@@ -135,9 +135,17 @@ def test_topk_exact(dev, k, size_class):
 @pytest.mark.parametrize("kv_fmt,q_dt", [(configs.KV_FP8, configs.DT_BF16), (configs.KV_BF16, configs.DT_BF16),
                                           (configs.KV_F32, configs.DT_F32), (configs.KV_FP8, configs.DT_F32)])
 @pytest.mark.parametrize("H", [64, 8, 80])
-def test_sparse_attn_explicit_indices(dev, kv_fmt, q_dt, H):
+@pytest.mark.parametrize("batch", ["q4", "q24"])
+def test_sparse_attn_explicit_indices(dev, kv_fmt, q_dt, H, batch):
+    """Explicit index lists with invalid, duplicate and out-of-range slots.  Four queries take the
+    16-head blocks; 24 queries with 64 or 80 heads take the 64-head blocks with the key range
+    split across blocks and merged by the combine kernel (80 heads: a second, mostly padded, head
+    block)."""
     run, tio = _run()
     ctx = [3000, 700, 0, 5000]
+    if batch == "q24":
+        ctx += [64, 1, 128, 4096, 9000, 256, 2048, 333, 0, 7000, 1500, 640, 12000, 5, 900, 4000, 2500, 60,
+                10000, 800]
     out_dt = configs.DT_F32 if q_dt == configs.DT_F32 else configs.DT_BF16
     wl = configs.make_decode("attn", ctx, H=H, HI=16, q_dt=q_dt, out_dt=out_dt, kv_fmt=kv_fmt, seed=21)
     rng = np.random.default_rng(H + kv_fmt)
@@ -192,6 +200,22 @@ def test_decode_batched_small(dev):
     out, idx = run.decode(wl, tio.to_device(wl, dev))
     err = _check_decode(wl, tio.out_to_numpy(out), idx.cpu().numpy(), BF16_TOL)
     _say(f"max err {err:.2e}")
+
+
+def test_decode_batched_full(dev):
+    """The batched decode workload at its full size (B=32, 65,536-token contexts, 64 heads, FP8 KV),
+    in the launch configuration the benchmark times; three queries are checked against the oracle."""
+    run, tio = _run()
+    wl = configs.batched_decode()
+    _say("decode batched full (B=32, T=65536, H=64, fp8)")
+    out, idx = run.decode(wl, tio.to_device(wl, dev))
+    out, idx = tio.out_to_numpy(out), idx.cpu().numpy()
+    for qi in (0, 13, 31):
+        nv = int(wl.n_vis[qi])
+        assert idx[qi, :128].tolist() == O.query_window(wl, qi).tolist()
+        check_topk_row(idx[qi, 128:], O.query_scores(wl, qi), nv, wl.topk, f"query {qi}")
+        ref = O.attend(wl, qi, idx[qi, :128], idx[qi, 128:])
+        check_attention(out[qi], ref, BF16_TOL, f"query {qi}")
 
 
 def test_decode_long_planted_small(dev):
