@@ -696,8 +696,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs
       float tmax = sv[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, sv[e]);
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      tmax = row_group_max(tmax);
       // lazy rescaling as in the 64-head kernel; alpha is this lane's own head's
       const bool grow = tmax > m + kRescaleLog2;
       if (__builtin_expect(__any(grow), 0)) {
@@ -733,8 +732,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs
       __syncthreads();                           // barrier k + 2
     }
   }
-  float ltot = lsum + __shfl_xor(lsum, 16);
-  ltot += __shfl_xor(ltot, 32);
+  const float ltot = row_group_sum(lsum);
   const int dbase = 128 * wave + 4 * g;
   if (a.n_split == 1) {
     if (wave >= 4 || h >= a.H) return;
@@ -755,8 +753,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[dt][i]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = row_group_max(mx);
     if (g == 0) Xs[wave][n] = mx;
   }
   __syncthreads();

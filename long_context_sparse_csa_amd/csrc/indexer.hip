@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   const int64_t p_first = (c_begin >> 6) + (int64_t)wave * pages_per_wave;   // this wave's first page
   const int64_t vis_pages = (nv + kPage - 1) / kPage;
 
-  // page ids of this wave's pages, one per lane, then broadcast as needed
+  // page ids of this wave's pages, one per lane, then read into scalars as needed
   int my_pid = -1;
   {
     const int64_t pp = p_first + lane;
@@ -184,11 +184,11 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
 
   // key page p -> operands; invalid pages read page 0 (always mapped memory) and are masked later
   auto page_ok = [&](int i) {
-    const int pid = __shfl(my_pid, i);
+    const int pid = __builtin_amdgcn_readlane(my_pid, i);
     return (unsigned)pid < (unsigned)a.num_pages;
   };
   auto load_page = [&](int i, v8i* kb, int& ksc) {
-    int pid = __shfl(my_pid, i);
+    int pid = __builtin_amdgcn_readlane(my_pid, i);
     pid = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
     const uint8_t* kp = keys + (int64_t)pid * (kPage * kDI);
     ksc = *(const int*)(a.kscale + (int64_t)pid * 256 + 4 * lane);

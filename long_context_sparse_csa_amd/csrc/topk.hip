@@ -61,15 +61,23 @@ __device__ __forceinline__ void write_window(const TopkArgs& a, int q) {
   a.idx[(int64_t)q * a.ld_idx - kWin + j] = v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (VALU only, no LDS crossbar):
+// shifts by 1, 2, 4, 8 inside each row of 16 lanes, then row 0's and row 2's totals broadcast into
+// rows 1 and 3, then the total of rows 0-1 into rows 2 and 3.  Lanes without a source add 0.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // Exclusive prefix sum over the 256 threads of a block; *total receives the block sum.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    uint32_t t = __shfl_up(inc, off);
-    if (lane >= off) inc += t;
-  }
+  const uint32_t inc = wave_inclusive_scan(v);
   if (lane == 63) s_wave[wave] = inc;
   __syncthreads();
   uint32_t before = 0, all = 0;
@@ -91,7 +99,7 @@ __device__ __forceinline__ int64_t wave_append(bool flag, uint32_t* counter) {
   const int leader = __ffsll((long long)m) - 1;
   uint32_t base = 0;
   if (lane == leader) base = atomicAdd(counter, (uint32_t)__popcll(m));
-  base = __shfl(base, leader);
+  base = __builtin_amdgcn_readlane(base, leader);
   if (!flag) return -1;
   const unsigned long long below = m & ((1ull << lane) - 1ull);
   return (int64_t)base + __popcll(below);
@@ -429,11 +437,11 @@ __global__ __launch_bounds__(256) void topk_finish_kernel(TopkArgs a) {
 // few lanes are active, so the phases are few, the scans are done by a single wave and sparse
 // passes skip instructions no lane needs:
 //   1. a 12-bit histogram of every key gives the threshold bin b* and the count above it;
-//   2. the entries of b* (normally a few hundred) are appended to an LDS candidate list, and one
-//      wave resolves the remaining 20 key bits among them (two 10-bit levels, no block barrier),
+//   2. the keys of b*'s entries (normally a few hundred) are appended to an LDS candidate list, and
+//      one wave resolves their remaining 20 bits (two 10-bit levels, no block barrier),
 //      giving the exact k-th largest key T and how many keys equal to T are taken; a bin with more
 //      than kCandMax entries (heavily tied scores) takes two block-wide levels instead;
-//   3. one scan of the per-thread (greater, equal) counts, packed in one word, places the k
+//   3. one block scan of the per-thread (greater, equal) counts, packed in one word, places the k
 //      indices in ascending order (equal keys at T in index order) in LDS, from where they are
 //      written with coalesced stores.
 constexpr int kSinglePer = 16;      // entries per thread, in index order
@@ -441,19 +449,6 @@ constexpr int kSingleMax = 1024 * kSinglePer;   // longest row: 1024 threads
 constexpr int kCandMax = 2048;      // entries of the threshold bin resolved by one wave; more take
                                     // the block-wide path
 constexpr int kSingleMaxK = 2048;   // largest k
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (VALU only, no LDS crossbar):
-// shifts by 1, 2, 4, 8 inside each row of 16 lanes, then row 0's and row 2's totals broadcast into
-// rows 1 and 3, then the total of rows 0-1 into rows 2 and 3.  Lanes without a source add 0.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return x;
-}
 
 // One wave scans `nb` bins (64 to 4096, a multiple of 256) from the top and finds the bin where
 // the running count first reaches `need` (1 <= need <= total): *digit, *before (count strictly
@@ -473,7 +468,7 @@ __device__ __forceinline__ void wave_find_desc(const uint32_t* bins, int nb, uin
   const uint32_t inc = wave_inclusive_scan(sum);
   const uint64_t cross = __ballot(inc - sum < need && inc >= need);
   const int x = cross ? __ffsll((long long)cross) - 1 : 63;
-  const uint32_t pre_x = __shfl(inc - sum, x);
+  const uint32_t pre_x = __builtin_amdgcn_readlane(inc - sum, x);
   const int top = nb - per * x;         // lane j looks at bin top - 1 - j
   const uint32_t c = lane < per ? bins[top - 1 - lane] : 0u;
   const uint32_t cinc = wave_inclusive_scan(c);
@@ -486,7 +481,7 @@ __device__ __forceinline__ void wave_find_desc(const uint32_t* bins, int nb, uin
 }
 
 // NT threads cover rows of up to 16 NT entries; short rows take a small block so that several
-// rows share a CU (LDS: 16 KB of bins + 4 B per entry + 8 KB of candidates / selected indices).
+// rows share a CU (LDS: 16 KB of bins + 8 KB of candidate keys / selected indices + 4 B per thread).
 template <int NT>
 __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
   constexpr int kRowMax = NT * kSinglePer;
@@ -511,11 +506,11 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
     for (int p = tid; p < (int)((nv + kPage - 1) / kPage); p += NT) pt_lds[p] = pt[p];
   }
   __shared__ __align__(16) uint32_t bins[kHistBins];
-  __shared__ __align__(16) uint32_t scan[NT];
-  __shared__ __align__(16) uint32_t key_lds[kRowMax];   // order keys of the row, by entry
-  // candidate indices while the threshold is resolved, then the selected indices
+  __shared__ __align__(16) uint32_t scan[NT / 64];   // per-wave totals of the final scan
+  // order keys of the threshold bin's entries while the threshold is resolved, then the selected
+  // indices
   __shared__ uint32_t cand_sel[kCandMax > kSingleMaxK ? kCandMax : kSingleMaxK];
-  uint32_t* cand_idx = cand_sel;
+  uint32_t* cand_key = cand_sel;
   int32_t* sel = (int32_t*)cand_sel;
   __shared__ uint32_t s_digit, s_before, s_ncand, s_T, s_need;
 
@@ -536,9 +531,6 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
     if (tid == 0) s_ncand = 0u;
 #pragma unroll
     for (int j = 0; j < kSinglePer; ++j) key[j] = order_key(v[j]);   // entries past n_vis are never counted
-#pragma unroll
-    for (int j = 0; j < kSinglePer; j += 4)
-      *(uint4*)&key_lds[c0 + j] = make_uint4(key[j], key[j + 1], key[j + 2], key[j + 3]);
   }
   __syncthreads();
   // level 1: top 12 key bits of every entry (all lanes active: one LDS atomic instruction covers 64)
@@ -550,7 +542,7 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
   __syncthreads();
   const uint32_t bstar = s_digit;
   const uint32_t need1 = (uint32_t)k - s_before;   // entries still to take from bin b* (>= 1)
-  // the entries of bin b* become candidates: their indices are appended to LDS with one atomic per
+  // the entries of bin b* become candidates: their keys are appended to LDS with one atomic per
   // wave, a lane's after those of the lanes below it
   {
     uint32_t hm = 0;   // bit j: entry c0 + j is in b*
@@ -560,12 +552,12 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
     const uint32_t incl = wave_inclusive_scan(hits);
     uint32_t base = 0;
     if (lane == 63 && incl) base = atomicAdd(&s_ncand, incl);
-    base = (uint32_t)__shfl((int)base, 63);
+    base = __builtin_amdgcn_readlane(base, 63);
     uint32_t pos = base + incl - hits;
     while (hm) {
       const int j = __ffs((int)hm) - 1;
       hm &= hm - 1u;
-      if (pos < (uint32_t)kCandMax) cand_idx[pos] = (uint32_t)(c0 + j);
+      if (pos < (uint32_t)kCandMax) cand_key[pos] = key[j];
       ++pos;
     }
   }
@@ -583,9 +575,19 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
         for (int i = 0; i < 1024; i += 256) *(uint4*)&bins[i + 4 * lane] = make_uint4(0u, 0u, 0u, 0u);
         __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
         __builtin_amdgcn_wave_barrier();
-        for (uint32_t i = lane; i < n_cand; i += 64) {
-          const uint32_t kk = key_lds[cand_idx[i]];
-          if ((kk >> (shift + 10)) == prefix) atomicAdd(&bins[(kk >> shift) & 1023u], 1u);
+        // four candidates per lane per pass: their reads are all in flight before the first atomic
+        for (uint32_t i0 = 0; i0 < n_cand; i0 += 256) {
+          uint32_t kk[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t i = i0 + 64 * u + lane;
+            kk[u] = cand_key[i < n_cand ? i : 0];
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t i = i0 + 64 * u + lane;
+            if (i < n_cand && (kk[u] >> (shift + 10)) == prefix) atomicAdd(&bins[(kk[u] >> shift) & 1023u], 1u);
+          }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
@@ -636,28 +638,15 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
     em |= (ok && key[j] == T) ? (1u << j) : 0u;
   }
   const uint32_t n_gt = __popc(gm), n_eq = __popc(em);
-  // exclusive scan of (n_gt << 16 | n_eq) over threads by wave 0 (both totals stay below 2^16)
-  scan[tid] = (n_gt << 16) | n_eq;
+  // exclusive scan of (n_gt << 16 | n_eq) over threads (both totals stay below 2^16): a DPP scan
+  // inside each wave, the wave totals through LDS, one barrier
+  const uint32_t mine = (n_gt << 16) | n_eq;
+  const uint32_t incl = wave_inclusive_scan(mine);
+  if (lane == 63) scan[wave] = incl;
   __syncthreads();
-  if (wave == 0) {
-    constexpr int SPL = NT / 64;   // thread counts per lane
-    uint32_t c[SPL], sum = 0;
+  uint32_t pre = incl - mine;
 #pragma unroll
-    for (int j = 0; j < SPL; ++j) c[j] = scan[SPL * lane + j];
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) sum += c[j];
-    uint32_t run = wave_inclusive_scan(sum) - sum;
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) {
-      const uint32_t x = c[j];
-      c[j] = run;
-      run += x;
-    }
-#pragma unroll
-    for (int j = 0; j < SPL; ++j) scan[SPL * lane + j] = c[j];
-  }
-  __syncthreads();
-  const uint32_t pre = scan[tid];
+  for (int w = 0; w < NT / 64; ++w) pre += w < wave ? scan[w] : 0u;
   const uint32_t eq_before = pre & 0xFFFFu;
   uint32_t pos = (pre >> 16) + (eq_before < need ? eq_before : need);
   uint32_t take_eq = eq_before < need ? (need - eq_before < n_eq ? need - eq_before : n_eq) : 0u;
