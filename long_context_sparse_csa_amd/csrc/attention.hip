@@ -123,13 +123,10 @@ constexpr uint64_t kCodeAddrMask = ~(uint64_t)15;
 
 __device__ __attribute__((aligned(256))) const uint8_t kZeroRow[1024] = {};
 
-// Slots [s_begin, s_begin + s_count) of query q are resolved into `codes` and `vmask` by NT
-// threads, four per thread per pass: all index loads, then all page-table loads, are issued before
-// any is used.  s_count is a whole number of tiles, and each wave covers 64 consecutive slots per pass.
-template <int NT>
-__device__ __forceinline__ void resolve_codes(const AttnArgs& a, int q, int r, int s_begin, int s_count,
-                                              uint64_t* codes, uint32_t* vmask, int tid) {
-  const int n_idx = a.n_win + a.n_comp;
+// Codes of four slots of query q (absolute slot indices s[k]; in[k] = the slot exists): all index
+// loads, then all page-table loads, are issued before any is used.  ok[k] = the slot has a row.
+__device__ __forceinline__ void slot_codes4(const AttnArgs& a, int q, int r, const int* s, const bool* in,
+                                            uint64_t* code, bool* ok) {
   const bool r_ok = r >= 0 && r < a.n_req;
   const int rr = r_ok ? r : 0;
   const bool has_win = a.win != nullptr;
@@ -140,48 +137,69 @@ __device__ __forceinline__ void resolve_codes(const AttnArgs& a, int q, int r, i
   const bool rows_in = a.rows != nullptr && a.comp != nullptr;   // compressed rows arrive resolved
   const uint64_t zero = (uint64_t)(uintptr_t)kZeroRow;
   const int64_t win_rb = row_bytes(a.win_fmt), comp_rb = row_bytes(a.comp_fmt);
+  int v[4], pg[4];
+  bool live[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    live[k] = r_ok && in[k];
+    const int sk = live[k] ? s[k] : 0;
+    v[k] = (rows_in && sk >= a.n_win) ? rows_row[sk] : idx_row[sk];
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pg[k] = -1;
+  if (has_pt && !rows_in) {
+    const int32_t* pt_row = a.page_table + (int64_t)rr * a.max_pages;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool pv = live[k] && s[k] >= a.n_win && v[k] >= 0 && v[k] < n_entries;
+      pg[k] = pt_row[pv ? (v[k] >> 6) : 0];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint64_t c = zero;
+    bool o = false;
+    if (live[k] && v[k] >= 0) {
+      if (s[k] < a.n_win) {
+        o = has_win && v[k] < a.win_rows_per_req;
+        if (o) c = (uint64_t)(uintptr_t)(a.win + ((int64_t)rr * a.win_rows_per_req + v[k]) * win_rb);
+      } else if (rows_in) {
+        o = (int64_t)v[k] < (int64_t)a.comp_num_pages * kPage;
+        if (o) c = (uint64_t)(uintptr_t)(a.comp + (int64_t)v[k] * comp_rb) | kCodeComp;
+      } else {
+        o = has_pt && v[k] < n_entries && (unsigned)pg[k] < (unsigned)a.comp_num_pages;
+        if (o) c = (uint64_t)(uintptr_t)(a.comp + ((int64_t)pg[k] * kPage + (v[k] & 63)) * comp_rb) | kCodeComp;
+      }
+    }
+    code[k] = c;
+    ok[k] = o;
+  }
+}
+
+// Slots [s_begin, s_begin + s_count) of query q are resolved into `codes` and `vmask` by NT
+// threads, four per thread per pass.  s_count is a whole number of tiles, and each wave covers 64
+// consecutive slots per pass.
+template <int NT>
+__device__ __forceinline__ void resolve_codes(const AttnArgs& a, int q, int r, int s_begin, int s_count,
+                                              uint64_t* codes, uint32_t* vmask, int tid) {
+  const int n_idx = a.n_win + a.n_comp;
   for (int b = 0; b < s_count; b += 4 * NT) {
-    int v[4], pg[4];
-    bool in[4];
+    int sl[4];
+    bool in[4], ok[4];
+    uint64_t c[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int i = b + tid + NT * k;
-      in[k] = r_ok && i < s_count && s_begin + i < n_idx;
-      const int s = in[k] ? s_begin + i : 0;
-      v[k] = (rows_in && s >= a.n_win) ? rows_row[s] : idx_row[s];
+      sl[k] = s_begin + i;
+      in[k] = i < s_count && s_begin + i < n_idx;
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) pg[k] = -1;
-    if (has_pt && !rows_in) {
-      const int32_t* pt_row = a.page_table + (int64_t)rr * a.max_pages;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int s = s_begin + b + tid + NT * k;
-        const bool pv = in[k] && s >= a.n_win && v[k] >= 0 && v[k] < n_entries;
-        pg[k] = pt_row[pv ? (v[k] >> 6) : 0];
-      }
-    }
+    slot_codes4(a, q, r, sl, in, c, ok);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int i = b + tid + NT * k;
-      const int s = s_begin + i;
-      uint64_t c = zero;
-      bool ok = false;
-      if (in[k] && v[k] >= 0) {
-        if (s < a.n_win) {
-          ok = has_win && v[k] < a.win_rows_per_req;
-          if (ok) c = (uint64_t)(uintptr_t)(a.win + ((int64_t)rr * a.win_rows_per_req + v[k]) * win_rb);
-        } else if (rows_in) {
-          ok = (int64_t)v[k] < (int64_t)a.comp_num_pages * kPage;
-          if (ok) c = (uint64_t)(uintptr_t)(a.comp + (int64_t)v[k] * comp_rb) | kCodeComp;
-        } else {
-          ok = has_pt && v[k] < n_entries && (unsigned)pg[k] < (unsigned)a.comp_num_pages;
-          if (ok) c = (uint64_t)(uintptr_t)(a.comp + ((int64_t)pg[k] * kPage + (v[k] & 63)) * comp_rb) | kCodeComp;
-        }
-      }
-      const uint64_t bal = __ballot(ok);
+      const uint64_t bal = __ballot(ok[k]);
       const int i0 = b + NT * k + (tid & ~63);   // first slot of this wave's 64 (two tiles)
-      if (i < s_count) codes[i] = c;
+      if (i < s_count) codes[i] = c[k];
       if ((tid & 63) == 0 && i0 < s_count) {
         vmask[i0 / kTile] = (uint32_t)bal;
         if (i0 + kTile < s_count) vmask[i0 / kTile + 1] = (uint32_t)(bal >> 32);
@@ -331,8 +349,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   __shared__ __align__(16) int Fl[2][4];                         // head group rescaled this tile
   __shared__ float As[2][64];                                    // its per-head rescale factors
   __shared__ float Ms[64], Ls[64], Xs[4][64];
-  __shared__ __align__(16) uint64_t codes[kMaxSlots];
-  __shared__ uint32_t vmask[kMaxSlots / kTile];
+  __shared__ uint32_t vmask[kMaxSlots / kTile];                  // valid slots of each tile
 
   const int n_idx = a.n_win + a.n_comp;
   const int n_tiles = (n_idx + kTile - 1) / kTile;
@@ -352,9 +369,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) qreg[ks] = *(const v8bf*)(qp + 32 * ks);
   }
-  resolve_codes<kAttnThreads>(a, q, r, s_begin, nt * kTile, codes, vmask, tid);
-  __syncthreads();
-
   float m = kNegBig, lsum = 0.f;   // score-wave softmax state of head h_base + 16 wave + n
   v4f acc[4][8];                   // value waves: O^T[128 dw + 16 dt + 4 g + i][h_base + 16 hg + n]
 #pragma unroll
@@ -368,16 +382,31 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   // after phase p - 1; the value waves accumulate P.V of tile p - 2.
   if (wave < 4) {
     const int pw = wave;   // staged rows 8pw .. 8pw+7 of every tile
-    // codes of this wave's rows, entry 8t + i = row 8pw + i of tile t, in VGPRs: lane l of word j
-    // holds entry 64j + l, so a fetch picks them with scalar lane reads instead of an LDS round trip
-    uint32_t cw_lo[kMaxSlots / 4 / 64], cw_hi[kMaxSlots / 4 / 64];
+    // Each score wave resolves the slots of its own rows, entry 8t + i = row 8pw + i of tile t,
+    // straight into VGPRs (lane l of word j holds entry 64j + l), so its first gathers wait for no
+    // other wave; a fetch picks the codes with scalar lane reads.  Its byte of every tile's
+    // valid-slot mask goes to LDS (read by the softmax, after the next barrier).
+    constexpr int kWords = kMaxSlots / 4 / 64;
+    uint32_t cw_lo[kWords], cw_hi[kWords];
+    {
+      int sl[kWords];
+      bool in[kWords], ok[kWords];
+      uint64_t c[kWords];
 #pragma unroll
-    for (int j = 0; j < kMaxSlots / 4 / 64; ++j) {
-      const int e = 64 * j + lane;                 // entry: tile e / 8, row e % 8
-      const int sidx = (e >> 3) * kTile + 8 * pw + (e & 7);
-      const uint64_t c = e < 8 * nt ? codes[sidx] : 0ull;
-      cw_lo[j] = (uint32_t)c;
-      cw_hi[j] = (uint32_t)(c >> 32);
+      for (int j = 0; j < kWords; ++j) {
+        const int e = 64 * j + lane;               // entry: tile e / 8, row e % 8
+        sl[j] = s_begin + (e >> 3) * kTile + 8 * pw + (e & 7);
+        in[j] = e < 8 * nt && sl[j] < n_idx;
+      }
+      slot_codes4(a, q, r, sl, in, c, ok);
+#pragma unroll
+      for (int j = 0; j < kWords; ++j) {
+        cw_lo[j] = (uint32_t)c[j];
+        cw_hi[j] = (uint32_t)(c[j] >> 32);
+        const uint64_t bal = __ballot(ok[j]);
+        const int t = 8 * j + lane;                // lanes 0..7 write the bytes of tiles 8j .. 8j+7
+        if (lane < 8 && t < nt) ((uint8_t*)vmask)[4 * t + pw] = (uint8_t)(bal >> (8 * lane));
+      }
     }
     RawChunk raw[kScoreDepth][8];
     uint64_t rc[kScoreDepth][8];
