@@ -257,6 +257,55 @@ __device__ __forceinline__ uint4 raw_to_bf16(const RawChunk& r, uint64_t code, i
   return w;
 }
 
+// Row gathers shared by both roles of the 64-head kernel: a wave owns rows rb .. rb+3 of every
+// 32-slot tile of its block's range, entry 4t + i = row rb + i of tile t.  Their codes are resolved
+// into VGPRs (lane l of word j holds entry 64j + l: two words cover the 32 tiles of a block), and
+// the wave's nibble of each tile's valid-slot mask goes to byte `vm_slot` of that tile's 8 mask
+// bytes in LDS.
+__device__ __forceinline__ void gather_codes(const AttnArgs& a, int q, int r, int s_begin, int nt, int n_idx,
+                                             int rb, int lane, uint32_t* cw_lo, uint32_t* cw_hi, uint8_t* vm8,
+                                             int vm_slot) {
+  int sl[4];
+  bool in[4], ok[4];
+  uint64_t c[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = 64 * j + lane;                   // entry: tile e / 4, row e % 4
+    sl[j] = s_begin + (e >> 2) * kTile + rb + (e & 3);
+    in[j] = j < 2 && e < 4 * nt && sl[j] < n_idx;
+  }
+  slot_codes4(a, q, r, sl, in, c, ok);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    cw_lo[j] = (uint32_t)c[j];
+    cw_hi[j] = (uint32_t)(c[j] >> 32);
+    const uint64_t bal = __ballot(ok[j]);
+    const int t = 16 * j + lane;                   // lanes 0..15 write the nibbles of tiles 16j .. 16j+15
+    if (lane < 16 && t < nt) vm8[8 * t + vm_slot] = (uint8_t)((bal >> (4 * lane)) & 0xFu);
+  }
+}
+
+// Issue the loads of the wave's four rows of tile k (codes picked from VGPRs with lane reads).
+template <int WF, int CF>
+__device__ __forceinline__ void gather_fetch(int k, const uint32_t* cw_lo, const uint32_t* cw_hi, int lane,
+                                             RawChunk* rw, uint64_t* c4) {
+  const uint32_t lo = (k >> 4) ? cw_lo[1] : cw_lo[0], hi = (k >> 4) ? cw_hi[1] : cw_hi[0];
+  const int l0 = (4 * k) & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    c4[i] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, l0 + i) << 32) |
+            (uint32_t)__builtin_amdgcn_readlane(lo, l0 + i);   // zero-extended: the lane read is an int
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rw[i] = load_raw<WF, CF>(c4[i], lane);
+}
+
+// Write the wave's four rows of a tile into the LDS tile K (dequantised to bf16).
+template <int WF, int CF>
+__device__ __forceinline__ void gather_stage(uint16_t* K, int rb, const RawChunk* rw, const uint64_t* c4, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *(uint4*)&K[(rb + i) * kKrStride + 8 * lane] = raw_to_bf16<WF, CF>(rw[i], c4[i], lane);
+}
+
 constexpr int kMaxSlots = 1024;   // slots of one block: longer index lists are split
 
 typedef short v4s __attribute__((ext_vector_type(4)));
@@ -349,7 +398,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   __shared__ __align__(16) int Fl[2][4];                         // head group rescaled this tile
   __shared__ float As[2][64];                                    // its per-head rescale factors
   __shared__ float Ms[64], Ls[64], Xs[4][64];
-  __shared__ uint32_t vmask[kMaxSlots / kTile];                  // valid slots of each tile
+  // valid slots of each tile: byte w holds rows 8w .. 8w+3 (score wave w), byte 4 + w rows
+  // 8w+4 .. 8w+7 (value wave w), one bit per row in the low nibble
+  __shared__ __align__(8) uint8_t vm8[kMaxSlots / kTile][8];
 
   const int n_idx = a.n_win + a.n_comp;
   const int n_tiles = (n_idx + kTile - 1) / kTile;
@@ -381,56 +432,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   // publish its P^T, then stage tile p + 1 into the ring slot of tile p - 3, which nobody reads
   // after phase p - 1; the value waves accumulate P.V of tile p - 2.
   if (wave < 4) {
-    const int pw = wave;   // staged rows 8pw .. 8pw+7 of every tile
-    // Each score wave resolves the slots of its own rows, entry 8t + i = row 8pw + i of tile t,
-    // straight into VGPRs (lane l of word j holds entry 64j + l), so its first gathers wait for no
-    // other wave; a fetch picks the codes with scalar lane reads.  Its byte of every tile's
-    // valid-slot mask goes to LDS (read by the softmax, after the next barrier).
-    constexpr int kWords = kMaxSlots / 4 / 64;
-    uint32_t cw_lo[kWords], cw_hi[kWords];
-    {
-      int sl[kWords];
-      bool in[kWords], ok[kWords];
-      uint64_t c[kWords];
-#pragma unroll
-      for (int j = 0; j < kWords; ++j) {
-        const int e = 64 * j + lane;               // entry: tile e / 8, row e % 8
-        sl[j] = s_begin + (e >> 3) * kTile + 8 * pw + (e & 7);
-        in[j] = e < 8 * nt && sl[j] < n_idx;
-      }
-      slot_codes4(a, q, r, sl, in, c, ok);
-#pragma unroll
-      for (int j = 0; j < kWords; ++j) {
-        cw_lo[j] = (uint32_t)c[j];
-        cw_hi[j] = (uint32_t)(c[j] >> 32);
-        const uint64_t bal = __ballot(ok[j]);
-        const int t = 8 * j + lane;                // lanes 0..7 write the bytes of tiles 8j .. 8j+7
-        if (lane < 8 && t < nt) ((uint8_t*)vmask)[4 * t + pw] = (uint8_t)(bal >> (8 * lane));
-      }
-    }
-    RawChunk raw[kScoreDepth][8];
-    uint64_t rc[kScoreDepth][8];
-    auto fetch = [&](int k, RawChunk* rw, uint64_t* c8) {
-      const int j = k >> 3;                        // word of tile k's entries (wave-uniform)
-      uint32_t lo = cw_lo[0], hi = cw_hi[0];
-#pragma unroll
-      for (int jj = 1; jj < kMaxSlots / 4 / 64; ++jj) {
-        lo = j == jj ? cw_lo[jj] : lo;
-        hi = j == jj ? cw_hi[jj] : hi;
-      }
-      const int l0 = (8 * k) & 63;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        c8[i] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, l0 + i) << 32) |
-                (uint32_t)__builtin_amdgcn_readlane(lo, l0 + i);   // zero-extended: the lane read is an int
-#pragma unroll
-      for (int i = 0; i < 8; ++i) rw[i] = load_raw<WF, CF>(c8[i], lane);
-    };
-    auto stage = [&](uint16_t* K, const RawChunk* rw, const uint64_t* c8) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *(uint4*)&K[(8 * pw + i) * kKrStride + 8 * lane] = raw_to_bf16<WF, CF>(rw[i], c8[i], lane);
-    };
+    const int rb = 8 * wave;   // gathered rows rb .. rb+3 of every tile
+    uint32_t cw_lo[2], cw_hi[2];
+    gather_codes(a, q, r, s_begin, nt, n_idx, rb, lane, cw_lo, cw_hi, &vm8[0][0], wave);
+    RawChunk raw[kScoreDepth][4];
+    uint64_t rc[kScoreDepth][4];
+    auto fetch = [&](int t, RawChunk* rw, uint64_t* c4) { gather_fetch<WF, CF>(t, cw_lo, cw_hi, lane, rw, c4); };
+    auto stage = [&](uint16_t* K, const RawChunk* rw, const uint64_t* c4) { gather_stage<WF, CF>(K, rb, rw, c4, lane); };
     // S^T[key][head] of this wave's head group for keys 0..15 (s[0]) and 16..31 (s[1])
     auto scores = [&](const uint16_t* K, v4f* sv) {
       v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = v4f{0.f, 0.f, 0.f, 0.f};
@@ -505,7 +513,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
           const int sl = (u + 1) % kDepthC;   // raw slot of tile p + 1
           // p = nt scores a stale tile (never used); p = 0 runs a softmax over no slot (a no-op)
           scores(Kr[p & 3], sv[u & 1]);
-          softmax(p - 1, p >= 1 ? vmask[p - 1] : 0u, sv[(u + 1) & 1]);
+          uint32_t vm = 0u;
+          if (p >= 1) {
+            const uint2 mb = *(const uint2*)&vm8[p - 1][0];
+            vm = mb.x | (mb.y << 4);
+          }
+          softmax(p - 1, vm, sv[(u + 1) & 1]);
           // staging last keeps its LDS writes out of the way of this phase's operand reads
           if (p + 1 < nt) {
             stage(Kr[(p + 1) & 3], raw[sl], rc[sl]);
@@ -523,6 +536,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
     }
   } else {
     const int dw = wave - 4;   // output dims [128 dw, 128 dw + 128)
+    const int rb = 8 * dw + 4;   // gathered rows rb .. rb+3 of every tile
+    uint32_t cw_lo[2], cw_hi[2];
+    gather_codes(a, q, r, s_begin, nt, n_idx, rb, lane, cw_lo, cw_hi, &vm8[0][0], 4 + dw);
+    // one tile of gathers in flight: the value waves' own work is the shorter of the two roles, so
+    // they can wait for a gather without lengthening the phase
+    RawChunk raw[4];
+    uint64_t rc[4];
+    if (nt > 0) {
+      gather_fetch<WF, CF>(0, cw_lo, cw_hi, lane, raw, rc);
+      gather_stage<WF, CF>(Kr[0], rb, raw, rc, lane);
+      if (nt > 1) gather_fetch<WF, CF>(1, cw_lo, cw_hi, lane, raw, rc);
+    }
     __syncthreads();
     for (int p = 0; p <= nt + 1; ++p) {
       if (p >= 2) {
@@ -555,6 +580,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
 #pragma unroll
           for (int hg = 0; hg < 4; ++hg) acc[hg][dt] = mma_bf16(vv, pf[hg], acc[hg][dt]);
         }
+      }
+      if (p + 1 < nt) {
+        gather_stage<WF, CF>(Kr[(p + 1) & 3], rb, raw, rc, lane);
+        if (p + 2 < nt) gather_fetch<WF, CF>(p + 2, cw_lo, cw_hi, lane, raw, rc);
       }
       __syncthreads();
     }
