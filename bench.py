@@ -35,8 +35,8 @@ DOMINANT = "indexer_fp8"
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--config", default="batched", choices=["batched", "long", "ragged", "tiny", "prefill"])
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     p.add_argument("--no-cpu", action="store_true")

@@ -467,19 +467,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
       for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, x[e]);
       tmax = row_group_max(tmax);
       // lazy rescaling: the reference max moves only when a head's max grows by more than 2^8, so
-      // the accumulators are touched rarely; p = 2^(S - m) then stays below 256
+      // the value waves rescale their accumulators rarely; p = 2^(S - m) then stays below 256.  The
+      // update is branch-free here (alpha = 1 when the max stays), so the whole softmax is one basic
+      // block that the compiler can interleave with the matrix-core work of the next tile.
       const bool grow = tmax > m + kRescaleLog2;
-      float alpha = 1.f;
-      int fl = 0;
-      if (__builtin_expect(__any(grow), 0)) {
-        // an opaque statement keeps the compiler from if-converting this rare path into every tile
-        __asm__ volatile("" ::: "memory");
-        const float m_new = grow ? tmax : m;
-        alpha = exp2f(m - m_new);
-        lsum *= alpha;
-        m = m_new;
-        fl = 1;
-      }
+      const float m_new = grow ? tmax : m;
+      const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+      lsum *= alpha;
+      m = m_new;
+      const int fl = __ballot(grow) != 0ull;
       float pr[8], psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
