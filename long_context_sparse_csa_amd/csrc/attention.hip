@@ -7,21 +7,22 @@
 // query with no valid slot outputs exact zeros.  K and V are the same 512-dim rows.
 //
 // BF16 matrix-core kernel (q bf16): a block owns one query, up to 64 heads (four head groups of
-// 16) and a contiguous range of 32-slot tiles.  All slots of the range are resolved to row
-// addresses up front.  Eight waves in two roles share each SIMD: score wave w keeps q of head group
-// w in registers, gathers rows 8w .. 8w+7 of every tile (coalesced: one 16-B lane chunk per 8 dims
-// of a row, FP8 nope dequantised with its fp32 block scale) two tiles ahead into a ring of four
-// row-major bf16 LDS tiles, computes the scores with v_mfma_f32_16x16x32_bf16 and runs the online
-// softmax; value wave 4 + w accumulates output dims [128w, 128w+128) of all 64 heads.  Scores are
-// computed transposed (S^T = K.q^T) so each lane holds 8 scores of its own head; once the key
-// order inside the 32-wide K step is permuted (slot 8g+4mt+i <-> key 16mt+4g+i) these are exactly
-// the P^T operand of O^T = V^T.P^T, which the value waves read from LDS.  They read V^T from the
-// same row-major tile with gfx950's transposing LDS load (ds_read_b64_tr_b16): each V fragment
-// feeds four MFMAs and no transposed copy is ever written.  The two roles run a tile apart (the
-// scores and softmax of tile p overlap P.V of tile p - 2 on the same SIMD), one barrier per tile.
-// Softmax runs in base 2 with log2(e) folded into the scale.  Large queries-by-heads grids run
-// unsplit; small ones split the slot range across blocks and a combine kernel merges the
-// (max, sum, acc) partials, sink included.
+// 16) and a contiguous range of 32-slot tiles (at most 1024 slots; longer lists are split).  Eight
+// waves in two roles share each SIMD.  Score wave w holds q of head groups w and w ^ 1 over one
+// half of the dims, so each K fragment it reads feeds two MFMAs and every K element is read by two
+// waves; the partial scores of group w ^ 1 go to wave w ^ 1 through LDS, and wave w runs the online
+// softmax of group w.  Value wave 4 + w accumulates output dims [128w, 128w+128) of all 64 heads.
+// Every wave resolves and gathers four rows of each tile (coalesced: one 16-B lane chunk per 8 dims
+// of a row, FP8 nope dequantised with its fp32 block scale) into a ring of four row-major bf16 LDS
+// tiles.  Scores are computed transposed (S^T = K.q^T) so each lane holds 8 scores of its own head;
+// once the key order inside the 32-wide K step is permuted (slot 8g+4mt+i <-> key 16mt+4g+i) these
+// are exactly the P^T operand of O^T = V^T.P^T, which the value waves read from LDS.  They read V^T
+// from the same row-major tile with gfx950's transposing LDS load (ds_read_b64_tr_b16): each V
+// fragment feeds four MFMAs and no transposed copy is ever written.  The roles run a tile apart
+// (the scores of tile p, the softmax of tile p - 1 and P.V of tile p - 2 share one phase), one
+// barrier per tile.  Softmax runs in base 2 with log2(e) folded into the scale.  Large
+// queries-by-heads grids run unsplit; small ones split the slot range across blocks and a combine
+// kernel merges the (max, sum, acc) partials, sink included.
 //
 // fp32 kernel (q f32): one block per (query, head); scores, softmax and P.V in fp32 with natural
 // exp, for bit-accurate-ish comparisons against the fp64 definition.
@@ -395,6 +396,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
 
   __shared__ __align__(16) uint16_t Kr[4][kTile * kKrStride];   // ring of four bf16 row tiles
   __shared__ __align__(16) uint4 Ps[2][4][64];                   // P^T operand of each head group
+  __shared__ __align__(16) v4f Sx[2][4][2][64];                  // partial scores for the partner wave
   __shared__ __align__(16) int Fl[2][4];                         // head group rescaled this tile
   __shared__ float As[2][64];                                    // its per-head rescale factors
   __shared__ float Ms[64], Ls[64], Xs[4][64];
@@ -410,15 +412,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   const int r = a.req_mode == 1 ? q : (a.req_mode == 2 ? 0 : a.q_req[q]);
   const int s_begin = t_begin * kTile;
 
-  // score waves: q of this wave's 16 heads stays in registers as the QK B operand: lane (n, g)
-  // holds dims 32ks + 8g .. +7 of head h_base + 16 wave + n.  Padded heads read head 0's row;
-  // their results are never written.
-  v8bf qreg[16];
+  // score waves: wave w computes the scores of head groups w and w ^ 1 over dims [256 (w & 1),
+  // +256), so every K fragment it reads feeds two MFMAs and each K element is read by two waves
+  // instead of four; the partial scores of head group w ^ 1 go to wave w ^ 1 through LDS.  q stays
+  // in registers as the QK B operand: qo[ks] / qx[ks] hold dims 256 (w & 1) + 32ks + 8g .. +7 of
+  // head n of group w / w ^ 1.  Padded heads read head 0's row; their results are never written.
+  v8bf qo[8], qx[8];
   if (wave < 4) {
-    const int hq = h_base + 16 * wave + n;
-    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)q * a.H + (hq < a.H ? hq : 0)) * kD + 8 * g;
+    const int ho = h_base + 16 * wave + n, hx = h_base + 16 * (wave ^ 1) + n;
+    const int d0 = 256 * (wave & 1) + 8 * g;
+    const uint16_t* qpo = (const uint16_t*)a.q + ((int64_t)q * a.H + (ho < a.H ? ho : 0)) * kD + d0;
+    const uint16_t* qpx = (const uint16_t*)a.q + ((int64_t)q * a.H + (hx < a.H ? hx : 0)) * kD + d0;
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) qreg[ks] = *(const v8bf*)(qp + 32 * ks);
+    for (int ks = 0; ks < 8; ++ks) {
+      qo[ks] = *(const v8bf*)(qpo + 32 * ks);
+      qx[ks] = *(const v8bf*)(qpx + 32 * ks);
+    }
   }
   float m = kNegBig, lsum = 0.f;   // score-wave softmax state of head h_base + 16 wave + n
   v4f acc[4][8];                   // value waves: O^T[128 dw + 16 dt + 4 g + i][h_base + 16 hg + n]
@@ -439,28 +448,35 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
     uint64_t rc[kScoreDepth][4];
     auto fetch = [&](int t, RawChunk* rw, uint64_t* c4) { gather_fetch<WF, CF>(t, cw_lo, cw_hi, lane, rw, c4); };
     auto stage = [&](uint16_t* K, const RawChunk* rw, const uint64_t* c4) { gather_stage<WF, CF>(K, rb, rw, c4, lane); };
-    // S^T[key][head] of this wave's head group for keys 0..15 (s[0]) and 16..31 (s[1])
-    auto scores = [&](const uint16_t* K, v4f* sv) {
-      v4f s0 = v4f{0.f, 0.f, 0.f, 0.f}, s1 = v4f{0.f, 0.f, 0.f, 0.f};
+    // partial S^T[key][head] over this wave's 256 dims for keys 0..15 ([0]) and 16..31 ([1]), of
+    // head group w (so) and w ^ 1 (sx)
+    const int dk = 256 * (wave & 1);
+    auto scores = [&](const uint16_t* K, v4f* so, v4f* sx) {
+      v4f o0 = v4f{0.f, 0.f, 0.f, 0.f}, o1 = o0, x0 = o0, x1 = o0;
 #pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const v8bf k0 = *(const v8bf*)&K[n * kKrStride + 32 * ks + 8 * g];
-        const v8bf k1 = *(const v8bf*)&K[(16 + n) * kKrStride + 32 * ks + 8 * g];
-        s0 = mma_bf16(k0, qreg[ks], s0);
-        s1 = mma_bf16(k1, qreg[ks], s1);
+      for (int ks = 0; ks < 8; ++ks) {
+        const v8bf k0 = *(const v8bf*)&K[n * kKrStride + dk + 32 * ks + 8 * g];
+        const v8bf k1 = *(const v8bf*)&K[(16 + n) * kKrStride + dk + 32 * ks + 8 * g];
+        o0 = mma_bf16(k0, qo[ks], o0);
+        x0 = mma_bf16(k0, qx[ks], x0);
+        o1 = mma_bf16(k1, qo[ks], o1);
+        x1 = mma_bf16(k1, qx[ks], x1);
       }
-      sv[0] = s0;
-      sv[1] = s1;
+      so[0] = o0;
+      so[1] = o1;
+      sx[0] = x0;
+      sx[1] = x1;
     };
     const float sc = a.softmax_scale * kLog2e;
-    // softmax of tile t with valid-slot mask vm (vm = 0: no slot, the state is left unchanged)
-    auto softmax = [&](int t, uint32_t vm, const v4f* sv) {
+    // softmax of tile t with valid-slot mask vm (vm = 0: no slot, the state is left unchanged); the
+    // scores are this wave's partial plus the partner's, published at the end of the previous phase
+    auto softmax = [&](int t, uint32_t vm, const v4f* sv, const v4f& y0, const v4f& y1) {
       const int pb = t & 1;
       float x[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        x[i] = (vm >> (4 * g + i)) & 1u ? sv[0][i] * sc : -INFINITY;
-        x[4 + i] = (vm >> (16 + 4 * g + i)) & 1u ? sv[1][i] * sc : -INFINITY;
+        x[i] = (vm >> (4 * g + i)) & 1u ? (sv[0][i] + y0[i]) * sc : -INFINITY;
+        x[4 + i] = (vm >> (16 + 4 * g + i)) & 1u ? (sv[1][i] + y1[i]) * sc : -INFINITY;
       }
       float tmax = x[0];
 #pragma unroll
@@ -499,7 +515,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
       if (kScoreDepth < nt) fetch(kScoreDepth, raw[0], rc[0]);
     }
     __syncthreads();
-    v4f sv[2][2];   // scores of the tiles of even and odd index
+    v4f sv[2][2];   // own partial scores of the tiles of even and odd index
     for (int p0 = 0; p0 <= nt; p0 += kScoreDepth) {
 #pragma unroll
       for (int u = 0; u < kScoreDepth; ++u) {
@@ -508,13 +524,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
           constexpr int kDepthC = kScoreDepth;
           const int sl = (u + 1) % kDepthC;   // raw slot of tile p + 1
           // p = nt scores a stale tile (never used); p = 0 runs a softmax over no slot (a no-op)
-          scores(Kr[p & 3], sv[u & 1]);
+          // the partner's partial scores of tile p - 1 (published before the last barrier), read
+          // before this tile's operands so their latency hides behind the matrix-core work
+          const v4f y0 = Sx[(p - 1) & 1][wave ^ 1][0][lane], y1 = Sx[(p - 1) & 1][wave ^ 1][1][lane];
+          v4f sxp[2];
+          scores(Kr[p & 3], sv[u & 1], sxp);
           uint32_t vm = 0u;
           if (p >= 1) {
             const uint2 mb = *(const uint2*)&vm8[p - 1][0];
             vm = mb.x | (mb.y << 4);
           }
-          softmax(p - 1, vm, sv[(u + 1) & 1]);
+          softmax(p - 1, vm, sv[(u + 1) & 1], y0, y1);
+          // the partner's partial scores of tile p, read by it in the next phase (tile p + 2 reuses
+          // the buffer after the barrier that follows that read)
+          Sx[p & 1][wave][0][lane] = sxp[0];
+          Sx[p & 1][wave][1][lane] = sxp[1];
           // staging last keeps its LDS writes out of the way of this phase's operand reads
           if (p + 1 < nt) {
             stage(Kr[(p + 1) & 3], raw[sl], rc[sl]);
