@@ -34,7 +34,7 @@ WINDOW = 128
 COMPRESS = 4
 
 KV_F32, KV_BF16, KV_FP8 = 0, 1, 2
-DT_F32, DT_BF16, DT_FP8 = 0, 1, 2
+DT_F32, DT_BF16, DT_FP8, DT_FP4 = 0, 1, 2, 3
 
 
 # ------------------------------------------------------------------------------------------------
@@ -61,6 +61,32 @@ _FP8_TABLE = np.array([fp8_e4m3fn_value(c) for c in range(256)], dtype=np.float6
 
 def fp8_decode(codes: np.ndarray) -> np.ndarray:
     return _FP8_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def fp4_e2m1_value(code: int) -> float:
+    """Value of one FP4 E2M1 nibble ([P1] section 3.5, fp4_quant_kernel: the FP4 indexer format,
+    largest value 6.0): 1 sign, 2 exponent (bias 1), 1 mantissa bit; exponent 0 is subnormal
+    (m * 0.5); no infinities or NaN."""
+    code = int(code) & 0xF
+    sign = -1.0 if code & 0x8 else 1.0
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    if e == 0:
+        return sign * m * 0.5
+    return sign * (1.0 + m / 2.0) * 2.0 ** (e - 1)
+
+
+_FP4_TABLE = np.array([fp4_e2m1_value(c) for c in range(16)], dtype=np.float64)
+
+
+def fp4_decode_packed(packed: np.ndarray) -> np.ndarray:
+    """Two E2M1 values per byte ([P1] section 3.5: float4_e2m1fn_x2), element 2i in the low nibble
+    and 2i+1 in the high nibble: [..., n] bytes -> [..., 2n] values."""
+    b = np.asarray(packed, dtype=np.uint8)
+    out = np.empty((*b.shape[:-1], 2 * b.shape[-1]), dtype=np.float64)
+    out[..., 0::2] = _FP4_TABLE[b & np.uint8(0xF)]
+    out[..., 1::2] = _FP4_TABLE[b >> np.uint8(4)]
+    return out
 
 
 def e8m0_decode(codes: np.ndarray) -> np.ndarray:
@@ -106,10 +132,11 @@ def q_values(q: np.ndarray, dt: int) -> np.ndarray:
 
 
 def indexer_q_values(qI: np.ndarray, qI_scale, dt: int) -> np.ndarray:
-    """Indexer query [..., HI, 128]: fp8 value times the E8M0 scale of its 32-element block."""
+    """Indexer query [..., HI, 128]: fp8 (or fp4, two per byte) value times the E8M0 scale of its
+    32-element block."""
     if dt == DT_F32:
         return np.asarray(qI, dtype=np.float64)
-    v = fp8_decode(qI)
+    v = fp4_decode_packed(qI) if dt == DT_FP4 else fp8_decode(qI)
     s = e8m0_decode(qI_scale)                                  # [..., HI, 4]
     return (v.reshape(*v.shape[:-1], 4, 32) * s[..., None]).reshape(v.shape)
 
@@ -119,7 +146,8 @@ def indexer_key_values(ik_keys: np.ndarray, ik_scales, dt: int, page: int, slots
     slots = np.arange(PAGE) if slots is None else np.asarray(slots)
     if dt == DT_F32:
         return np.asarray(ik_keys[page][slots], dtype=np.float64)
-    v = fp8_decode(ik_keys[page][slots])                      # [n,128]
+    raw = ik_keys[page][slots]
+    v = fp4_decode_packed(raw) if dt == DT_FP4 else fp8_decode(raw)   # [n,128]
     s = e8m0_decode(ik_scales[page][:, slots]).T              # [n,4]
     return (v.reshape(-1, 4, 32) * s[:, :, None]).reshape(-1, DI)
 

@@ -124,3 +124,56 @@ def test_pack_rows_round_trip_error_bound():
             assert np.all(np.abs(v[:, :448] - x[:, :448])[big] <= np.abs(x[:, :448])[big] * 2.0 ** -4)
         else:
             assert np.all(np.abs(v - x) <= np.abs(x) * tol)
+
+
+# ----------------------------------------------------------------------------- FP4 E2M1 (MXFP4)
+
+# The eight E2M1 magnitudes of the OCP microscaling FP4 format, codes 0..7; code | 8 is the negation.
+_E2M1_MAGNITUDES = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_fp4_all_codes_match_format_table():
+    for code in range(16):
+        ref = _E2M1_MAGNITUDES[code & 7] * (-1.0 if code & 8 else 1.0)
+        assert O.fp4_e2m1_value(code) == ref
+    assert max(abs(O.fp4_e2m1_value(c)) for c in range(16)) == 6.0    # fp4_max of the quantiser
+
+
+def test_fp4_packed_nibble_order():
+    # byte 0x5A: low nibble 0xA = -1.0 (element 0), high nibble 0x5 = 3.0 (element 1)
+    v = O.fp4_decode_packed(np.array([[0x5A, 0x0F, 0x70]], dtype=np.uint8))
+    assert v.tolist() == [[-1.0, 3.0, -6.0, 0.0, 0.0, 6.0]]
+
+
+def test_fp4_encoder_rounds_to_nearest_even_and_saturates():
+    grid = np.array(_E2M1_MAGNITUDES + [-m for m in _E2M1_MAGNITUDES[1:]] + [0.0])   # 16 values
+    codes = codec.fp4_e2m1_encode(grid)
+    packed = (codes[0::2] | (codes[1::2] << np.uint8(4))).astype(np.uint8)
+    assert np.array_equal(O.fp4_decode_packed(packed[None, :])[0], grid)
+    # ties go to the even code: 0.25 -> 0, 0.75 -> 1.0, 1.25 -> 1.0, 1.75 -> 2.0, 2.5 -> 2.0, 3.5 -> 4.0, 5 -> 4.0
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -5.0])
+    got = [O.fp4_e2m1_value(c) for c in codec.fp4_e2m1_encode(ties)]
+    assert got == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, -4.0]
+    # off-tie points go to the nearest value; beyond 6 saturates
+    got = [O.fp4_e2m1_value(c) for c in codec.fp4_e2m1_encode(np.array([0.26, 2.6, 4.9, 5.1, 7.0, -100.0]))]
+    assert got == [0.5, 3.0, 4.0, 6.0, 6.0, -6.0]
+
+
+@pytest.mark.parametrize("amax,code", [(6.0, 127), (6.01, 128), (3.0, 126), (12.0, 128), (0.0, 1), (1e-40, 1)])
+def test_fp4_scale_rule(amax, code):
+    """Power-of-two scale 2^ceil(log2(max(amax, 6*2^-126) / 6)) (fp4_quant_kernel)."""
+    assert int(codec.e8m0_exponent_fp4(np.array([amax], np.float32))[0]) == code
+
+
+def test_fp4_block_quantiser_picks_nearest_grid_value():
+    rng = np.random.default_rng(7)
+    x = (rng.standard_normal((40, 128)) * rng.uniform(0.01, 50, size=(40, 1))).astype(np.float32)
+    packed, e = codec.quantize_fp4_e8m0_blocks(x, 32)
+    assert packed.shape == (40, 64) and e.shape == (40, 4)
+    vals = O.fp4_decode_packed(packed) * np.repeat(O.e8m0_decode(e), 32, axis=1)
+    scale = np.repeat(O.e8m0_decode(e), 32, axis=1)
+    cand = np.array(_E2M1_MAGNITUDES + [-m for m in _E2M1_MAGNITUDES[1:]])
+    nearest_err = np.abs(x[..., None] - cand * scale[..., None]).min(axis=-1)
+    assert np.allclose(np.abs(vals - x), nearest_err, rtol=0, atol=1e-6 * np.abs(x).max())
+    # the block maximum lands within one grid step of the top value
+    assert np.all(np.abs(x).reshape(40, 4, 32).max(axis=-1) <= 6.0 * O.e8m0_decode(e) * (1 + 1e-7))

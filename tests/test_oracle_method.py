@@ -242,6 +242,29 @@ def test_scores_use_page_table_and_block_scales():
         assert s[c] == pytest.approx(ref, rel=1e-12, abs=1e-12)
 
 
+def test_fp4_scores_use_page_table_nibbles_and_block_scales():
+    """FP4 indexer (two E2M1 values per byte, element 2i in the low nibble, E8M0 per 32): scores from
+    the paged byte layout equal scores from keys and queries unpacked nibble by nibble here."""
+    wl = configs.make_decode("t4", [1000], H=4, HI=8, idx_dt=configs.DT_FP4, seed=4)
+    assert wl.ik_keys.shape[-1] == 64 and wl.qI.shape[-1] == 64
+    s = O.query_scores(wl, 0)
+
+    def unpack(row):
+        out = []
+        for byte in row:
+            out += [O.fp4_e2m1_value(int(byte) & 0xF), O.fp4_e2m1_value(int(byte) >> 4)]
+        return np.array(out)
+
+    qh = np.stack([unpack(wl.qI[0, h]) * np.repeat([2.0 ** (int(x) - 127) for x in wl.qI_scale[0, h]], 32)
+                   for h in range(8)])
+    for c in [0, 63, 64, 130, 249]:
+        p = wl.page_table[0, c // 64]
+        slot = c % 64
+        k = unpack(wl.ik_keys[p, slot]) * np.repeat([2.0 ** (int(wl.ik_scales[p, b, slot]) - 127) for b in range(4)], 32)
+        ref = sum(float(wl.w[0, h]) * max(0.0, float(qh[h] @ k)) for h in range(8))
+        assert s[c] == pytest.approx(ref, rel=1e-12, abs=1e-12)
+
+
 def test_long_context_planted_entries_win():
     """Reduced long-context recipe (T=262144, 655 planted entries): every planted entry outscores every other entry, so
     the top-512 set is a subset of the planted set."""

@@ -14,6 +14,10 @@ Formats (all little-endian):
 * E8M0: one byte, value ``2**(e - 127)``; the power-of-two scale of "fast_round_scale"
   (same page, section 3.3): ``2**ceil(log2(max(amax, 1e-4) / 448))``.
 * BF16: the upper 16 bits of an fp32, round-to-nearest-even.
+* FP4 E2M1 (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte, element 2i in the low nibble
+  ("float4_e2m1fn_x2"); block 32 with a power-of-two E8M0 scale ``2**ceil(log2(max(amax,
+  6*2**-126) / 6))`` (page "DeepSeek-V4 全面解读", section 3.5, fp4_quant_kernel).  Rounding is
+  round-to-nearest-even on the E2M1 grid with saturation to +-6; the pages do not state it.
 """
 from __future__ import annotations
 
@@ -82,6 +86,52 @@ def quantize_fp8_e8m0_blocks(x: np.ndarray, block: int = 32):
     inv = np.ldexp(np.float32(1.0), 127 - e.astype(np.int32)).astype(np.float32)   # exact 1/scale
     codes = fp8_e4m3fn_encode(xb * inv[..., None])
     return codes.reshape(x.shape), e
+
+
+FP4_MAX = 6.0
+FP4_AMAX_FLOOR = 6.0 * 2.0 ** -126
+_FP4_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float64)   # codes 0..7
+
+
+def fp4_e2m1_encode(x: np.ndarray) -> np.ndarray:
+    """Round values to FP4 E2M1 nibble codes (0..15): nearest grid magnitude, ties to the even code,
+    saturating at 6."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), FP4_MAX)
+    d = np.abs(a[..., None] - _FP4_GRID)                      # distance to every magnitude
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best                                          # one or two nearest codes
+    even = cand & (np.arange(8) % 2 == 0)
+    code = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1)).astype(np.uint8)
+    sign = (np.signbit(x) & (code != 0)).astype(np.uint8) << np.uint8(3)
+    return code | sign
+
+
+def e8m0_exponent_fp4(amax: np.ndarray) -> np.ndarray:
+    """Biased E8M0 code of ``2**ceil(log2(max(amax, 6*2**-126) / 6))`` (exact, on the fp32 bits)."""
+    a = np.maximum(np.asarray(amax, dtype=np.float32), np.float32(FP4_AMAX_FLOOR))
+    v = (a.astype(np.float64) / FP4_MAX).astype(np.float32)
+    bits = v.view(np.uint32)
+    e = ((bits >> np.uint32(23)) & np.uint32(0xFF)).astype(np.int64) - 127
+    e = e + ((bits & np.uint32(0x7FFFFF)) != 0)
+    return (e + 127).astype(np.uint8)
+
+
+def quantize_fp4_e8m0_blocks(x: np.ndarray, block: int = 32):
+    """Quantise the last axis of ``x`` to FP4 E2M1 in blocks of ``block`` with E8M0 scales.
+
+    Returns (packed codes uint8 [..., n/2], element 2i in the low nibble; scale codes uint8
+    [..., n_blocks]).
+    """
+    x = np.asarray(x, dtype=np.float32)
+    n = x.shape[-1]
+    assert n % block == 0 and n % 2 == 0
+    xb = x.reshape(*x.shape[:-1], n // block, block)
+    e = e8m0_exponent_fp4(np.abs(xb).max(axis=-1))
+    inv = np.ldexp(1.0, 127 - e.astype(np.int64))           # exact 1/scale
+    codes = fp4_e2m1_encode(xb.astype(np.float64) * inv[..., None]).reshape(*x.shape)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << np.uint8(4))).astype(np.uint8)
+    return packed, e
 
 
 def quantize_fp8_f32_blocks(x: np.ndarray, block: int = 64):

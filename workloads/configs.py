@@ -35,7 +35,7 @@ WINDOW = 128
 TOPK = 512
 COMPRESS = 4
 
-DT_F32, DT_BF16, DT_FP8 = 0, 1, 2
+DT_F32, DT_BF16, DT_FP8, DT_FP4 = 0, 1, 2, 3
 KV_F32, KV_BF16, KV_FP8 = codec.KV_F32, codec.KV_BF16, codec.KV_FP8
 
 _CHUNK = 1 << 20  # values per independently seeded chunk
@@ -137,7 +137,8 @@ def _page_table(rng: np.random.Generator, n_entries: list[int]):
 
 
 def _indexer_pool(ss, total_pages: int, idx_dt: int, override=None):
-    """Indexer keys [P][64][128] and E8M0 scales [P][4][64] (block-major within a page)."""
+    """Indexer keys [P][64][128] (fp8; fp4: [P][64][64], two values per byte) and E8M0 scales
+    [P][4][64] (block-major within a page)."""
     n = total_pages * PAGE
     if idx_dt == DT_F32:
         keys = np.empty((n, DI), dtype=np.float32)
@@ -145,11 +146,13 @@ def _indexer_pool(ss, total_pages: int, idx_dt: int, override=None):
         if override is not None:
             override(keys, None)
         return keys.reshape(total_pages, PAGE, DI), None
-    codes = np.empty((n, DI), dtype=np.uint8)
+    width = DI // 2 if idx_dt == DT_FP4 else DI
+    quant = codec.quantize_fp4_e8m0_blocks if idx_dt == DT_FP4 else codec.quantize_fp8_e8m0_blocks
+    codes = np.empty((n, width), dtype=np.uint8)
     scales = np.empty((n, DI // 32), dtype=np.uint8)
 
     def tf(x, lo, hi):
-        c, e = codec.quantize_fp8_e8m0_blocks(x, 32)
+        c, e = quant(x, 32)
         scales[lo:hi] = e
         return c
 
@@ -157,7 +160,7 @@ def _indexer_pool(ss, total_pages: int, idx_dt: int, override=None):
     if override is not None:
         override(codes, scales)
     sc = scales.reshape(total_pages, PAGE, 4).transpose(0, 2, 1).copy()   # [P][4][64]
-    return codes.reshape(total_pages, PAGE, DI), sc
+    return codes.reshape(total_pages, PAGE, width), sc
 
 
 def _kv_rows(ss, n_rows: int, fmt: int) -> np.ndarray:
@@ -170,7 +173,10 @@ def _indexer_queries(g: np.random.Generator, Q: int, HI: int, idx_dt: int):
     x = g.standard_normal((Q, HI, DI), dtype=np.float32)
     if idx_dt == DT_F32:
         return x, x, None
-    codes, e = codec.quantize_fp8_e8m0_blocks(x, 32)
+    if idx_dt == DT_FP4:
+        codes, e = codec.quantize_fp4_e8m0_blocks(x, 32)
+    else:
+        codes, e = codec.quantize_fp8_e8m0_blocks(x, 32)
     return x, codes, e
 
 
@@ -219,7 +225,8 @@ def make_decode(name: str, ctx_len, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_
                 if scales is None:
                     codes[rows] = kv
                 else:
-                    c, e = codec.quantize_fp8_e8m0_blocks(kv, 32)
+                    quant = codec.quantize_fp4_e8m0_blocks if idx_dt == DT_FP4 else codec.quantize_fp8_e8m0_blocks
+                    c, e = quant(kv, 32)
                     codes[rows] = c
                     scales[rows] = e
 
