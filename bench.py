@@ -27,9 +27,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KEY_BYTES = 132            # 128 FP8 + 4 E8M0 per indexer key
+# indexer bytes per key (and per query head): FP8 128 + 4 E8M0 scales; FP4 64 + 4; fp32 512
+IDX_BYTES = {0: 512, 2: 132, 3: 68}
 ROW_BYTES = {0: 2048, 1: 1024, 2: 608}
-DOMINANT = "indexer_fp8"
+IDX_NAME = {0: "f32", 2: "fp8", 3: "fp4"}
 
 
 def parse():
@@ -40,6 +41,8 @@ def parse():
     p.add_argument("--config", default="batched", choices=["batched", "long", "ragged", "tiny", "prefill"])
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--indexer", default="fp8", choices=["fp8", "fp4"],
+                   help="indexer q/k format: FP8 E4M3FN or MXFP4 E2M1, both with E8M0 scales per 32")
     p.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = enough to exceed 1 GB)")
     p.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
                    help="after timing, run 3 plain device copies of MB megabytes (a known-size reference "
@@ -47,10 +50,13 @@ def parse():
     return p.parse_args()
 
 
-def make_workload(name):
+def make_workload(name, indexer):
     from workloads import configs
+    if name == "tiny":
+        return configs.tiny_decode()
+    idx_dt = configs.DT_FP4 if indexer == "fp4" else configs.DT_FP8
     return {"batched": configs.batched_decode, "long": configs.long_decode, "ragged": configs.ragged_decode,
-            "tiny": configs.tiny_decode, "prefill": configs.causal_prefill}[name]()
+            "prefill": configs.causal_prefill}[name](idx_dt=idx_dt)
 
 
 def algorithmic_bytes(wl, idx_np):
@@ -60,9 +66,9 @@ def algorithmic_bytes(wl, idx_np):
     n_vis = wl.n_vis.astype("int64")
     pages = (n_vis + 63) // 64
     q_bytes = Q * H * 512 * (4 if wl.q_dt == 0 else 2)
-    qi_bytes = Q * HI * (128 * 4 if wl.idx_dt == 0 else 128 + 4)
+    qi_bytes = Q * HI * IDX_BYTES[wl.idx_dt]
     w_bytes = Q * HI * 4
-    key_bytes = int(n_vis.sum()) * (512 if wl.idx_dt == 0 else KEY_BYTES)
+    key_bytes = int(n_vis.sum()) * IDX_BYTES[wl.idx_dt]
     pt_bytes = int(pages.sum()) * 4
     indexer = key_bytes + pt_bytes + qi_bytes + w_bytes
     valid_rows = 0
@@ -81,10 +87,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config):
+def measured_traffic(kernel, config):
     """HBM bytes per indexer launch from the committed rocprofv3 PMC summary, if it was taken on the
     current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"indexer_fp8_{config}_traffic.json")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{config}_traffic.json")
     try:
         d = json.load(open(path))
     except (OSError, ValueError):
@@ -160,7 +166,7 @@ def main():
     csa.lib()
     dev = "cuda"
     t_gen = time.perf_counter()
-    wl = make_workload(args.config)
+    wl = make_workload(args.config, args.indexer)
     gen_s = time.perf_counter() - t_gen
     base = torch_io.to_device(wl, dev)
     decode = wl.kind == "decode"
@@ -208,19 +214,19 @@ def main():
     torch.cuda.synchronize()
     csa.csa_profile_enable(False)
     kernels = {}
-    for name in ("prep", "indexer_fp8", "indexer_fp8_prefill", "indexer_f32", "topk_single", "topk_hist", "topk_collect", "topk_finish",
-                 "attn_bf16",
-                 "attn_combine", "attn_f32"):
+    for name in ("prep", "indexer_fp8", "indexer_fp8_prefill", "indexer_fp4", "indexer_fp4_prefill", "indexer_f32",
+                 "topk_single", "topk_hist", "topk_collect", "topk_finish", "attn_bf16", "attn_combine", "attn_f32"):
         tot, n = csa.csa_profile_collect(name)
         if n:
             kernels[name] = round(tot / n * 1e3, 3)
     csa.csa_profile_reset()
-    dom = DOMINANT if DOMINANT in kernels else max(kernels, key=kernels.get)
+    dominant = f"indexer_{IDX_NAME[wl.idx_dt]}"
+    dom = dominant if dominant in kernels else max(kernels, key=kernels.get)
     dom_us = kernels[dom]
     if dom.startswith("indexer"):
         dom_us = indexer_launch_us(wl, copies, stream, args.steps)
     achieved = idx_bytes / (dom_us * 1e-6) / 1e9
-    traffic = measured_traffic(args.config)
+    traffic = measured_traffic(dom, args.config)
 
     res = {
         "metric": "decode query-tokens/s for indexer+top512+sparse_attn; achieved HBM TB/s",
@@ -233,7 +239,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8-e4m3fn indexer, bf16 matrix-core attention, fp32 accumulate",
+        "dtype": {0: "fp32 indexer and attention", 2: "fp8-e4m3fn indexer, bf16 matrix-core attention, fp32 accumulate",
+                  3: "mxfp4-e2m1 indexer, bf16 matrix-core attention, fp32 accumulate"}[wl.idx_dt],
         "data": "synthetic (seeded N(0,1) q/kv/indexer, quantised as the workload states)",
         "config": {"workload": wl.name, "B": wl.B, "Q": wl.Q, "H": wl.H, "HI": wl.HI,
                    "context": int(wl.ctx_len.max()) if decode else int(wl.win_rows.shape[1]),

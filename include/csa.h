@@ -52,7 +52,10 @@ typedef enum {
 } csa_status;
 
 /* Element types of q, out and the indexer operands. */
-typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3FN = 2 } csa_dtype;
+/* CSA_FP4_E2M1 packs two E2M1 codes per byte: element 2i in bits [0,4), element 2i+1 in bits
+ * [4,8) (code = sign bit 3 | exponent bits 2..1 | mantissa bit 0, magnitudes 0, 0.5, 1, 1.5, 2, 3,
+ * 4, 6), as the block FP4 quantiser of [P1] section 3.5 writes them.  Indexer operands only.    */
+typedef enum { CSA_F32 = 0, CSA_BF16 = 1, CSA_FP8_E4M3FN = 2, CSA_FP4_E2M1 = 3 } csa_dtype;
 
 /* KV row formats (one 512-dim row each).
  *   CSA_KV_F32               2048 B: 512 x fp32
@@ -77,11 +80,13 @@ typedef struct {
 /* Paged indexer key cache (same page mapping as csa_paged_kv).
  *   dt = CSA_FP8_E4M3FN: keys [num_pages][64][128] e4m3fn bytes; scales [num_pages][4][64] E8M0
  *        bytes, scales[p][b][s] scaling dims [32b, 32b+32) of slot s (value 2^(e-127)).
+ *   dt = CSA_FP4_E2M1: keys [num_pages][64][64] bytes, two E2M1 codes per byte; scales as for
+ *        CSA_FP8_E4M3FN (one E8M0 byte per 32 dims).
  *   dt = CSA_F32: keys [num_pages][64][128] fp32; scales must be NULL.                          */
 typedef struct {
   const void* keys;
   const uint8_t* scales;
-  int32_t dt;               /* csa_dtype: CSA_FP8_E4M3FN or CSA_F32 */
+  int32_t dt;               /* csa_dtype: CSA_FP8_E4M3FN, CSA_FP4_E2M1 or CSA_F32 */
   int32_t num_pages;
   const int32_t* page_table;/* [n_req][max_pages] */
   int32_t max_pages;
@@ -92,7 +97,8 @@ typedef struct {
  * csa_indexer_logits - indexer scores ([P1] section 2.10 forward steps 5-8; [P2] concept 3 and
  * algorithm 2, the FP8 "paged MQA logits" pass).
  *
- *   qI        [Q][HI][128] e4m3fn bytes (qI_dt = CSA_FP8_E4M3FN) or fp32 (CSA_F32)
+ *   qI        [Q][HI][128] e4m3fn bytes (qI_dt = CSA_FP8_E4M3FN), [Q][HI][64] bytes of packed
+ *             E2M1 pairs (CSA_FP4_E2M1) or [Q][HI][128] fp32 (CSA_F32)
  *   qI_scale  [Q][HI][4] E8M0 bytes, one per 32 dims (NULL for CSA_F32)
  *   w         [Q][HI] fp32 head weights (the caller folds softmax_scale * HI^-0.5 into them)
  *   keys      paged indexer keys; the key dtype must equal qI_dt

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcsa.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "csa.h")
 
-CSA_F32, CSA_BF16, CSA_FP8_E4M3FN = 0, 1, 2
+CSA_F32, CSA_BF16, CSA_FP8_E4M3FN, CSA_FP4_E2M1 = 0, 1, 2, 3
 CSA_KV_F32, CSA_KV_BF16, CSA_KV_FP8NOPE_BF16ROPE = 0, 1, 2
 STATUS = {0: "CSA_OK", -1: "CSA_ERR_NULL", -2: "CSA_ERR_SHAPE", -3: "CSA_ERR_DTYPE", -4: "CSA_ERR_ALIGN",
           -5: "CSA_ERR_WORKSPACE", -6: "CSA_ERR_UNSUPPORTED", -7: "CSA_ERR_HIP"}

@@ -95,7 +95,7 @@ PathWs carve_path(Carver& c, int32_t rows, int32_t H, int64_t max_n_vis, int32_t
 csa_status check_idx_struct(const csa_paged_idx* k, int32_t dt) {
   if (!k || !k->keys || !k->page_table) return CSA_ERR_NULL;
   if (k->dt != dt) return CSA_ERR_DTYPE;
-  if (dt == CSA_FP8_E4M3FN && !k->scales) return CSA_ERR_NULL;
+  if ((dt == CSA_FP8_E4M3FN || dt == CSA_FP4_E2M1) && !k->scales) return CSA_ERR_NULL;
   if (dt == CSA_F32 && k->scales) return CSA_ERR_DTYPE;
   if (k->num_pages < 1 || k->max_pages < 1) return CSA_ERR_SHAPE;
   if (!aligned(k->keys, 16) || !aligned(k->page_table, 4) || (k->scales && !aligned(k->scales, 4))) return CSA_ERR_ALIGN;
@@ -112,8 +112,8 @@ csa_status check_kv_struct(const csa_paged_kv* c) {
 
 csa_status check_indexer_inputs(const void* qI, const uint8_t* qI_scale, int32_t qI_dt, const float* w, int32_t HI) {
   if (!qI || !w) return CSA_ERR_NULL;
-  if (qI_dt != CSA_F32 && qI_dt != CSA_FP8_E4M3FN) return CSA_ERR_DTYPE;
-  if (qI_dt == CSA_FP8_E4M3FN && !qI_scale) return CSA_ERR_NULL;
+  if (qI_dt != CSA_F32 && qI_dt != CSA_FP8_E4M3FN && qI_dt != CSA_FP4_E2M1) return CSA_ERR_DTYPE;
+  if (qI_dt != CSA_F32 && !qI_scale) return CSA_ERR_NULL;
   if (HI < 1 || HI > 64) return CSA_ERR_SHAPE;
   if (!aligned(qI, 16) || !aligned(w, 4)) return CSA_ERR_ALIGN;
   return CSA_OK;

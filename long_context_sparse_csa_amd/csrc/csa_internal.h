@@ -16,7 +16,7 @@ struct ProfScope {
 struct IndexerArgs {
   const void* qI;             // [Q][HI][128] fp8 bytes or fp32
   const uint8_t* qI_scale;    // [Q][HI][4] E8M0 (fp8 only)
-  int dt;                     // 0 = f32, 2 = fp8
+  int dt;                     // 0 = f32, 2 = fp8 e4m3fn, 3 = fp4 e2m1 (two per byte)
   const float* w;             // [Q][HI]
   const void* keys;           // [P][64][128]
   const uint8_t* kscale;      // [P][4][64]

@@ -3,7 +3,7 @@
 // Score of compressed entry c for one query ([P1] "DeepSeek-V4 全面解读" section 2.10, forward steps
 // 5-8; [P2] "DeepSeek-V4 in SGLang 深度理解分析" concept 3 / algorithm 2):
 //     s[c] = sum_h w[h] * max(0, qI[h] . kI[c])
-// with FP8 E4M3FN operands that carry one E8M0 scale per 32 elements.
+// with FP8 E4M3FN or FP4 E2M1 operands that carry one E8M0 scale per 32 elements.
 //
 // FP8 path: one v_mfma_scale_f32_16x16x128_f8f6f4 covers 16 heads x 16 entries x all 128 dims, and
 // its per-lane E8M0 scale operands are exactly the stored per-32 block scales, so dequantisation
@@ -16,6 +16,13 @@
 // 4*(l%16) + l/16.  Decode: keys stream straight from HBM into VGPRs (no LDS), each lane loads
 // 2 x 16 B per key group, and each page is read exactly once.  Causal prefill, where all queries
 // share one request's keys, stages key pages in LDS per block of queries instead (see below).
+//
+// FP4 path (two E2M1 codes per byte, element 2i in the low nibble): the same instruction with both
+// operand formats set to FP4 reads four registers per lane, and lane l = m + 16*g's 32 codes all
+// fall in scale block g (measured on gfx950).  Lane (m, g) therefore loads the one contiguous
+// 16-byte chunk of row m that holds elements [32g, 32g+32), and the scale operands are exactly the
+// FP8 path's.  A and B use the same lane layout, so codes pair up element by element.  Rows are
+// 64 bytes, a key page 4 KB: half the FP8 key traffic, at the same matrix-core cost per page.
 #include <cstdlib>
 
 #include "csa_device.h"
@@ -23,9 +30,14 @@
 
 namespace csa {
 
-template <int HG, int KG>
-__device__ __forceinline__ v4f mma_fp8_scaled(const v8i& a, const v8i& b, int sa, int sb, v4f c) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, HG, sa, KG, sb);
+// bytes of one 128-dim operand row
+template <bool FP4>
+constexpr int kRowB = FP4 ? kDI / 2 : kDI;
+
+template <int HG, int KG, bool FP4>
+__device__ __forceinline__ v4f mma_scaled(const v8i& a, const v8i& b, int sa, int sb, v4f c) {
+  constexpr int fmt = FP4 ? 4 : 0;   // operand format code: 0 = fp8 e4m3, 4 = fp4 e2m1
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, fmt, fmt, HG, sa, KG, sb);
 }
 
 // max(x, 0) as one integer max on the bit pattern: every negative float (and -0) is a negative
@@ -33,12 +45,17 @@ __device__ __forceinline__ v4f mma_fp8_scaled(const v8i& a, const v8i& b, int sa
 // compiler first quiets possible signalling NaNs of the matrix-core result.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+template <bool FP4>
 __device__ __forceinline__ v8i load_k_operand(const uint8_t* row, int g) {
-  uint4 lo = *(const uint4*)(row + 16 * g);
-  uint4 hi = *(const uint4*)(row + 64 + 16 * g);
+  const uint4 lo = *(const uint4*)(row + 16 * g);
   v8i r;
   r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+  if constexpr (FP4) {
+    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  } else {
+    const uint4 hi = *(const uint4*)(row + 64 + 16 * g);
+    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+  }
   return r;
 }
 
@@ -74,16 +91,16 @@ __device__ __forceinline__ void flush_hist(uint32_t* lhist, uint32_t* ghist, int
 
 // The query's indexer heads as scaled-MFMA A operands (padded heads zeroed), their E8M0 block
 // scales packed one byte per head group, and the head weights of this lane's output rows.
-template <int NHG>
+template <int NHG, bool FP4>
 __device__ __forceinline__ void load_query(const IndexerArgs& a, int q, int n, int g, v8i* qa, int& qsc,
                                            float (*wv)[4]) {
-  const uint8_t* qb = (const uint8_t*)a.qI + (int64_t)q * a.HI * kDI;
+  const uint8_t* qb = (const uint8_t*)a.qI + (int64_t)q * a.HI * kRowB<FP4>;
   qsc = 0;
 #pragma unroll
   for (int hg = 0; hg < NHG; ++hg) {
     const int h = 16 * hg + n;
     const int hc = h < a.HI ? h : a.HI - 1;
-    const v8i v = load_k_operand(qb + hc * kDI, g);
+    const v8i v = load_k_operand<FP4>(qb + hc * kRowB<FP4>, g);
     const int sb = (int)a.qI_scale[((int64_t)q * a.HI + hc) * 4 + g];
     const bool ok = h < a.HI;
 #pragma unroll
@@ -113,14 +130,14 @@ __device__ __forceinline__ float swap_sum16(float keep_even, float keep_odd) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int NHG>
+template <int NHG, bool FP4>
 __device__ __forceinline__ float score_page(const v8i* qa, int qsc, const float (*wv)[4], const v8i* kb, int ksc) {
   v4f acc[NHG][4];
   static_for<0, NHG>::run([&](auto HGc) {
     constexpr int HG = decltype(HGc)::value;
     static_for<0, 4>::run([&](auto KGc) {
       constexpr int KG = decltype(KGc)::value;
-      acc[HG][KG] = mma_fp8_scaled<HG, KG>(qa[HG], kb[KG], qsc, ksc, v4f{0.f, 0.f, 0.f, 0.f});
+      acc[HG][KG] = mma_scaled<HG, KG, FP4>(qa[HG], kb[KG], qsc, ksc, v4f{0.f, 0.f, 0.f, 0.f});
     });
   });
   float part[4];
@@ -145,7 +162,7 @@ __device__ __forceinline__ float score_page(const v8i* qa, int qsc, const float 
 // the second.
 constexpr int kPagesPerWave = 8;
 
-template <int NHG, bool HIST>
+template <int NHG, bool HIST, bool FP4>
 __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   constexpr int pages_per_wave = kPagesPerWave;
   const int q = blockIdx.x;   // queries vary fastest: a row's blocks share one XCD (and its L2)
@@ -167,7 +184,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   v8i qa[NHG];
   int qsc;
   float wv[NHG][4];
-  load_query<NHG>(a, q, n, g, qa, qsc, wv);
+  load_query<NHG, FP4>(a, q, n, g, qa, qsc, wv);
 
   const uint8_t* keys = (const uint8_t*)a.keys;
   const int32_t* pt = a.page_table + (int64_t)(r < 0 ? 0 : r) * a.max_pages;
@@ -190,16 +207,16 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   auto load_page = [&](int i, v8i* kb, int& ksc) {
     int pid = __builtin_amdgcn_readlane(my_pid, i);
     pid = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
-    const uint8_t* kp = keys + (int64_t)pid * (kPage * kDI);
+    const uint8_t* kp = keys + (int64_t)pid * (kPage * kRowB<FP4>);
     ksc = *(const int*)(a.kscale + (int64_t)pid * 256 + 4 * lane);
 #pragma unroll
-    for (int kg = 0; kg < 4; ++kg) kb[kg] = load_k_operand(kp + (4 * n + kg) * kDI, g);
+    for (int kg = 0; kg < 4; ++kg) kb[kg] = load_k_operand<FP4>(kp + (4 * n + kg) * kRowB<FP4>, g);
   };
 
   auto compute_page = [&](int i, const v8i* kb, int ksc) {
     const int64_t c0 = (p_first + i) * kPage;
     const bool live = c0 < nv && page_ok(i);
-    const float score = score_page<NHG>(qa, qsc, wv, kb, ksc);
+    const float score = score_page<NHG, FP4>(qa, qsc, wv, kb, ksc);
     const int64_t c = c0 + 4 * n + g;
     if (c < a.max_n_vis) {
       const float v = (live && c < nv) ? score : -INFINITY;
@@ -259,9 +276,11 @@ __device__ __forceinline__ int64_t prefill_visible(const IndexerArgs& a, int q) 
   return a.n_req < 1 ? 0 : (nv > lim ? lim : nv);
 }
 
-template <int NHG>
+template <int NHG, bool FP4>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void indexer_fp8_prefill_kernel(
     IndexerArgs a) {
+  constexpr int kHalves = FP4 ? 1 : 2;                            // 16-byte chunks per lane operand
+  constexpr int kRow = kRowB<FP4>;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -269,7 +288,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   const int q0 = (nbx - 1 - (int)blockIdx.x) * kPfQueries;       // heaviest query blocks first
   const int64_t p0 = (int64_t)blockIdx.y * kPfPages;
   if (p0 * kPage >= a.max_n_vis) return;
-  __shared__ __align__(16) uint8_t kl[kPfPages][4][2][64][16];   // [page][kg][half][lane] operand bytes
+  __shared__ __align__(16) uint8_t kl[kPfPages][4][kHalves][64][16];   // [page][kg][half][lane] operand bytes
   __shared__ __align__(16) uint32_t sl[kPfPages][64];             // scale word of lane l = word l
   __shared__ int pid_s[kPfPages];
 
@@ -286,18 +305,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     pid_s[tid] = pid;
   }
   __syncthreads();
-  // wave w stages pages w and w + 4: eight 1 KB loads per page (load j fills key group j / 2,
-  // half j % 2: lane L takes row 4 (L % 16) + kg, bytes 16 (L / 16) + 64 half), then the page's
-  // 256 scale bytes
+  // wave w stages pages w and w + 4: 4 x kHalves 1 KB loads per page (load j fills key group
+  // j / kHalves, half j % kHalves: lane L takes row 4 (L % 16) + kg, bytes 16 (L / 16) + 64 half),
+  // then the page's 256 scale bytes
   const uint8_t* keys = (const uint8_t*)a.keys;
   for (int pg = wave; pg < kPfPages; pg += 4) {
     int pid = pid_s[pg];
     pid = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
-    const uint8_t* kp = keys + (int64_t)pid * (kPage * kDI) + (4 * n) * kDI + 16 * g;
+    const uint8_t* kp = keys + (int64_t)pid * (kPage * kRow) + (4 * n) * kRow + 16 * g;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint8_t* src = kp + (j >> 1) * kDI + 64 * (j & 1);
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)&kl[pg][j >> 1][j & 1][0][0], 16, 0, 0);
+    for (int j = 0; j < 4 * kHalves; ++j) {
+      const int kg = j / kHalves, half = j % kHalves;
+      const uint8_t* src = kp + kg * kRow + 64 * half;
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)&kl[pg][kg][half][0][0], 16, 0, 0);
     }
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)(a.kscale + (int64_t)pid * 256 + 4 * lane),
                                      (lds_ptr_t)&sl[pg][0], 4, 0, 0);
@@ -321,19 +341,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     v8i qa[NHG];
     int qsc;
     float wv[NHG][4];
-    load_query<NHG>(a, q, n, g, qa, qsc, wv);
+    load_query<NHG, FP4>(a, q, n, g, qa, qsc, wv);
     for (int pi = 0; pi < np; ++pi) {
       v8i kb[4];
       const int ksc = (int)sl[pi][lane];
 #pragma unroll
       for (int kg = 0; kg < 4; ++kg) {
         const uint4 lo = *(const uint4*)&kl[pi][kg][0][lane][0];
-        const uint4 hi = *(const uint4*)&kl[pi][kg][1][lane][0];
         kb[kg][0] = (int)lo.x; kb[kg][1] = (int)lo.y; kb[kg][2] = (int)lo.z; kb[kg][3] = (int)lo.w;
-        kb[kg][4] = (int)hi.x; kb[kg][5] = (int)hi.y; kb[kg][6] = (int)hi.z; kb[kg][7] = (int)hi.w;
+        if constexpr (FP4) {
+          kb[kg][4] = 0; kb[kg][5] = 0; kb[kg][6] = 0; kb[kg][7] = 0;
+        } else {
+          const uint4 hi = *(const uint4*)&kl[pi][kg][kHalves - 1][lane][0];
+          kb[kg][4] = (int)hi.x; kb[kg][5] = (int)hi.y; kb[kg][6] = (int)hi.z; kb[kg][7] = (int)hi.w;
+        }
       }
       const bool live = (live_bits >> pi) & 1u;
-      const float score = score_page<NHG>(qa, qsc, wv, kb, ksc);
+      const float score = score_page<NHG, FP4>(qa, qsc, wv, kb, ksc);
       const int64_t c = (p0 + pi) * kPage + 4 * n + g;
       if (c < a.max_n_vis) lrow[c] = (live && c < nv) ? score : -INFINITY;
     }
@@ -401,32 +425,40 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   const int nhg = (a.HI + 15) / 16;
+  const bool fp4 = a.dt == 3;
   if (a.vis_mode == 2 && !hist) {
     // causal prefill: keys shared by all queries, staged once per block of queries
     dim3 grid((unsigned)((a.Q + kPfQueries - 1) / kPfQueries),
               (unsigned)((a.max_n_vis + kPfPages * kPage - 1) / (kPfPages * kPage)));
-    ProfScope p("indexer_fp8_prefill", s);
+    ProfScope p(fp4 ? "indexer_fp4_prefill" : "indexer_fp8_prefill", s);
+#define CSA_PF_LAUNCH(N)                                                                    \
+  if (fp4) hipLaunchKernelGGL((indexer_fp8_prefill_kernel<N, true>), grid, dim3(256), 0, s, a); \
+  else hipLaunchKernelGGL((indexer_fp8_prefill_kernel<N, false>), grid, dim3(256), 0, s, a);
     switch (nhg) {
-      case 1: hipLaunchKernelGGL((indexer_fp8_prefill_kernel<1>), grid, dim3(256), 0, s, a); break;
-      case 2: hipLaunchKernelGGL((indexer_fp8_prefill_kernel<2>), grid, dim3(256), 0, s, a); break;
-      case 3: hipLaunchKernelGGL((indexer_fp8_prefill_kernel<3>), grid, dim3(256), 0, s, a); break;
-      default: hipLaunchKernelGGL((indexer_fp8_prefill_kernel<4>), grid, dim3(256), 0, s, a); break;
+      case 1: CSA_PF_LAUNCH(1) break;
+      case 2: CSA_PF_LAUNCH(2) break;
+      case 3: CSA_PF_LAUNCH(3) break;
+      default: CSA_PF_LAUNCH(4) break;
     }
+#undef CSA_PF_LAUNCH
     return hipGetLastError();
   }
   // kPagesPerWave pages per wave, four waves per block
   const int per_block = 4 * kPagesPerWave * kPage;
   dim3 grid((unsigned)a.Q, (unsigned)((a.max_n_vis + per_block - 1) / per_block));
-  ProfScope p("indexer_fp8", s);
-#define CSA_IDX_LAUNCH(N)                                                                              \
-  if (hist) hipLaunchKernelGGL((indexer_fp8_kernel<N, true>), grid, dim3(256), 0, s, a); \
-  else hipLaunchKernelGGL((indexer_fp8_kernel<N, false>), grid, dim3(256), 0, s, a);
+  ProfScope p(fp4 ? "indexer_fp4" : "indexer_fp8", s);
+#define CSA_IDX_LAUNCH(N, F)                                                                        \
+  if (hist) hipLaunchKernelGGL((indexer_fp8_kernel<N, true, F>), grid, dim3(256), 0, s, a); \
+  else hipLaunchKernelGGL((indexer_fp8_kernel<N, false, F>), grid, dim3(256), 0, s, a);
+#define CSA_IDX_FMT(N) \
+  if (fp4) { CSA_IDX_LAUNCH(N, true) } else { CSA_IDX_LAUNCH(N, false) }
   switch (nhg) {
-    case 1: CSA_IDX_LAUNCH(1) break;
-    case 2: CSA_IDX_LAUNCH(2) break;
-    case 3: CSA_IDX_LAUNCH(3) break;
-    default: CSA_IDX_LAUNCH(4) break;
+    case 1: CSA_IDX_FMT(1) break;
+    case 2: CSA_IDX_FMT(2) break;
+    case 3: CSA_IDX_FMT(3) break;
+    default: CSA_IDX_FMT(4) break;
   }
+#undef CSA_IDX_FMT
 #undef CSA_IDX_LAUNCH
   return hipGetLastError();
 }

@@ -60,6 +60,9 @@ def _indexer(**kw):
     (dict(qI=None), -1), (dict(w=None), -1), (dict(qs=None), -1), (dict(logits=None), -1),
     (dict(keys=_idx(keys=None)), -1), (dict(keys=_idx(scales=None)), -1),
     (dict(dt=1), -3), (dict(keys=_idx(dt=0)), -3), (dict(dt=0, keys=_idx(dt=0)), -3),   # f32 keys with scales
+    (dict(dt=4, keys=_idx(dt=4)), -3), (dict(dt=B.CSA_FP4_E2M1), -3),                   # unknown / key dtype differs
+    (dict(dt=B.CSA_FP4_E2M1, keys=_idx(dt=B.CSA_FP4_E2M1), qs=None), -1),
+    (dict(dt=B.CSA_FP4_E2M1, keys=_idx(dt=B.CSA_FP4_E2M1, scales=None)), -1),
     (dict(HI=0), -2), (dict(HI=65), -2), (dict(Q=0), -2), (dict(n_req=0), -2), (dict(ld=100), -2),
     (dict(max_n_vis=-1), -2), (dict(keys=_idx(num_pages=0)), -2),
     (dict(qI=MISALIGNED), -4), (dict(logits=FAKE + 2), -4), (dict(keys=_idx(keys=MISALIGNED)), -4),

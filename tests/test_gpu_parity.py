@@ -34,6 +34,7 @@ def _say(msg):
 
 # ------------------------------------------------------------------------------------ indexer
 @pytest.mark.parametrize("HI,idx_dt", [(64, configs.DT_FP8), (40, configs.DT_FP8), (16, configs.DT_FP8),
+                                        (64, configs.DT_FP4), (40, configs.DT_FP4), (16, configs.DT_FP4),
                                         (16, configs.DT_F32), (64, configs.DT_F32)])
 def test_indexer_scores(dev, HI, idx_dt):
     run, tio = _run()
@@ -218,6 +219,23 @@ def test_decode_batched_full(dev):
         check_attention(out[qi], ref, BF16_TOL, f"query {qi}")
 
 
+def test_decode_fp4_indexer(dev):
+    """Whole decode path with the MXFP4 indexer (E2M1 pairs, E8M0 per 32): 4 requests at 65,536
+    tokens plus a ragged batch whose contexts end mid-page, with 40 indexer heads."""
+    run, tio = _run()
+    wl = configs.batched_decode(B=4, T=65536, idx_dt=configs.DT_FP4)
+    _say("decode batched small, fp4 indexer (B=4, T=65536, H=64)")
+    out, idx = run.decode(wl, tio.to_device(wl, dev))
+    err = _check_decode(wl, tio.out_to_numpy(out), idx.cpu().numpy(), BF16_TOL)
+    _say(f"max err {err:.2e}")
+    ctx = [0, 100, 2000, 2047, 2052, 9000, 131, 4]
+    wl = configs.make_decode("ragged_fp4", ctx, H=8, HI=40, kv_fmt=configs.KV_BF16, idx_dt=configs.DT_FP4,
+                             seed=6)
+    _say(f"decode ragged, fp4 indexer ctx={ctx}")
+    out, idx = run.decode(wl, tio.to_device(wl, dev))
+    _check_decode(wl, tio.out_to_numpy(out), idx.cpu().numpy(), BF16_TOL, empty_rows=(0,))
+
+
 def test_decode_long_planted_small(dev):
     run, tio = _run()
     wl = configs.make_decode("long_small", [262144, 262144], H=64, HI=64, seed=0, planted_frac=0.01)
@@ -255,13 +273,14 @@ def test_prefill_small(dev):
         check_attention(out[t], ref, BF16_TOL, f"t={t}")
 
 
-def test_prefill_chunk_ragged(dev):
+@pytest.mark.parametrize("idx_dt", [configs.DT_FP8, configs.DT_FP4])
+def test_prefill_chunk_ragged(dev, idx_dt):
     """A prefill chunk that starts mid-sequence, with a query count that is not a multiple of the
     indexer's query block, a visible prefix that ends mid-page, and 40 indexer heads (padded to
-    48 inside the matrix-core kernels)."""
+    48 inside the matrix-core kernels); FP8 and MXFP4 indexer operands."""
     run, tio = _run()
-    wl = configs.causal_prefill(T=4100, HI=40, q_start=2003, q_count=1013, seed=5)
-    _say("prefill chunk (T=4100, q 2003..3015, HI=40)")
+    wl = configs.causal_prefill(T=4100, HI=40, q_start=2003, q_count=1013, seed=5, idx_dt=idx_dt)
+    _say(f"prefill chunk (T=4100, q 2003..3015, HI=40, idx_dt={idx_dt})")
     out, idx = run.prefill(wl, tio.to_device(wl, dev))
     out, idx = tio.out_to_numpy(out), idx.cpu().numpy()
     sample = sorted(set([0, 1, 2, 3, 14, 15, 16, 17, 252, 253, 1008, 1009, 1010, 1011, 1012] +

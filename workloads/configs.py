@@ -296,22 +296,25 @@ def tiny_decode(seed: int = 0) -> Workload:
                        idx_dt=DT_F32, kv_fmt=KV_F32, seed=seed)
 
 
-def batched_decode(seed: int = 0, B: int = 32, T: int = 65536, H: int = 64, HI: int = 64) -> Workload:
+def batched_decode(seed: int = 0, B: int = 32, T: int = 65536, H: int = 64, HI: int = 64,
+                   idx_dt: int = DT_FP8) -> Workload:
     """B=32 requests at T=65536 (16384 compressed entries in 256 pages of 64), FP8-nope/BF16-rope
-    KV with per-64 fp32 scales, FP8 indexer with E8M0 per-32 scales, bf16 q, H=HI=64."""
-    return make_decode("batched_decode", [T] * B, H=H, HI=HI, seed=seed)
+    KV with per-64 fp32 scales, FP8 (or FP4) indexer with E8M0 per-32 scales, bf16 q, H=HI=64."""
+    return make_decode("batched_decode", [T] * B, H=H, HI=HI, seed=seed, idx_dt=idx_dt)
 
 
-def long_decode(seed: int = 0, B: int = 8, T: int = 1 << 20, H: int = 64, HI: int = 64) -> Workload:
+def long_decode(seed: int = 0, B: int = 8, T: int = 1 << 20, H: int = 64, HI: int = 64,
+                idx_dt: int = DT_FP8) -> Workload:
     """B=8 requests at T=1,048,576 (262,144 compressed entries), formats as batched_decode, with 1%
     planted high-similarity entries per request."""
-    return make_decode("long_decode", [T] * B, H=H, HI=HI, seed=seed, planted_frac=0.01)
+    return make_decode("long_decode", [T] * B, H=H, HI=HI, seed=seed, planted_frac=0.01, idx_dt=idx_dt)
 
 
 def causal_prefill(seed: int = 0, T: int = 8192, H: int = 64, HI: int = 64, q_start: int = 0,
-                   q_count: int | None = None) -> Workload:
-    """One request, T=8192 query positions, bf16 q and KV rows, FP8 indexer."""
-    return make_prefill("causal_prefill", T, H=H, HI=HI, seed=seed, q_start=q_start, q_count=q_count)
+                   q_count: int | None = None, idx_dt: int = DT_FP8) -> Workload:
+    """One request, T=8192 query positions, bf16 q and KV rows, FP8 (or FP4) indexer."""
+    return make_prefill("causal_prefill", T, H=H, HI=HI, seed=seed, q_start=q_start, q_count=q_count,
+                        idx_dt=idx_dt)
 
 
 RAGGED_EMPTY_ROWS = (3, 17, 42, 63)
@@ -327,8 +330,9 @@ def ragged_lengths(seed: int = 0, B: int = 64, empty=RAGGED_EMPTY_ROWS, lo: int 
     return T
 
 
-def ragged_decode(seed: int = 0, B: int = 64, H: int = 8, HI: int = 64, hi: int = 131072) -> Workload:
+def ragged_decode(seed: int = 0, B: int = 64, H: int = 8, HI: int = 64, hi: int = 131072,
+                  idx_dt: int = DT_FP8) -> Workload:
     """B=64 lognormal contexts in [512, 131072] (rows 3, 17, 42, 63 empty), H=8 (padded to 16
-    inside the kernels), bf16 q and KV rows, FP8 indexer."""
+    inside the kernels), bf16 q and KV rows, FP8 (or FP4) indexer."""
     T = ragged_lengths(seed, B, hi=hi)
-    return make_decode("ragged_decode", T, H=H, HI=HI, kv_fmt=KV_BF16, seed=seed)
+    return make_decode("ragged_decode", T, H=H, HI=HI, kv_fmt=KV_BF16, seed=seed, idx_dt=idx_dt)
