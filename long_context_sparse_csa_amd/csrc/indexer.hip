@@ -157,14 +157,18 @@ __device__ __forceinline__ float score_page(const v8i* qa, int qsc, const float 
   return swap_sum16(k0, k1);
 }
 
-// Pages (64 entries each) scored by one wave.  Measured on the batched and long-context decode
-// workloads: 2 pages per wave is 15% slower than 4; 8 matches 4 on the first and is 4% faster on
-// the second.
-constexpr int kPagesPerWave = 8;
+// Pages (64 entries each) scored by one wave, and page buffers in flight per wave.  Measured on the
+// batched and long-context decode workloads with FP8 keys: 2 pages per wave is 15% slower than 4;
+// 8 matches 4 on the first and is 4% faster on the second.
+template <bool FP4>
+constexpr int kPagesPerWave = FP4 ? 8 : 8;
+template <bool FP4>
+constexpr int kPageBufs = FP4 ? 3 : 3;
 
 template <int NHG, bool HIST, bool FP4>
 __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
-  constexpr int pages_per_wave = kPagesPerWave;
+  constexpr int pages_per_wave = kPagesPerWave<FP4>;
+  constexpr int nbuf = kPageBufs<FP4> < pages_per_wave ? kPageBufs<FP4> : pages_per_wave;
   const int q = blockIdx.x;   // queries vary fastest: a row's blocks share one XCD (and its L2)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -227,18 +231,18 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
     }
   };
 
-  // Three page buffers, straight-line code: the first three pages are loaded up front and page
-  // i + 3 as soon as page i is scored, so up to three pages are in flight and every wait is for
+  // nbuf page buffers, straight-line code: the first nbuf pages are loaded up front and page
+  // i + nbuf as soon as page i is scored, so up to nbuf pages are in flight and every wait is for
   // exactly the page about to be scored.  Pages past the wave's range load page 0 (always mapped)
   // and store nothing.
-  v8i kb[3][4];
-  int ksc[3] = {0, 0, 0};
+  v8i kb[nbuf][4];
+  int ksc[nbuf];
 #pragma unroll
-  for (int i = 0; i < 3 && i < pages_per_wave; ++i) load_page(i, kb[i], ksc[i]);
+  for (int i = 0; i < nbuf; ++i) load_page(i, kb[i], ksc[i]);
 #pragma unroll
   for (int i = 0; i < pages_per_wave; ++i) {
-    compute_page(i, kb[i % 3], ksc[i % 3]);
-    if (i + 3 < pages_per_wave) load_page(i + 3, kb[i % 3], ksc[i % 3]);
+    compute_page(i, kb[i % nbuf], ksc[i % nbuf]);
+    if (i + nbuf < pages_per_wave) load_page(i + nbuf, kb[i % nbuf], ksc[i % nbuf]);
   }
   if constexpr (HIST) {
     __syncthreads();
@@ -444,7 +448,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   // kPagesPerWave pages per wave, four waves per block
-  const int per_block = 4 * kPagesPerWave * kPage;
+  const int per_block = 4 * (fp4 ? kPagesPerWave<true> : kPagesPerWave<false>) * kPage;
   dim3 grid((unsigned)a.Q, (unsigned)((a.max_n_vis + per_block - 1) / per_block));
   ProfScope p(fp4 ? "indexer_fp4" : "indexer_fp8", s);
 #define CSA_IDX_LAUNCH(N, F)                                                                        \
