@@ -289,6 +289,27 @@ def attend(wl, qi: int, win_idx, comp_idx) -> np.ndarray:
     return sparse_attention(qv, rows, valid, wl.sink, wl.softmax_scale)
 
 
+def compressed_visible(n_tokens: int, ratio: int) -> int:
+    """Compressed entries a query can see when ``n_tokens`` raw tokens (positions 0..n_tokens-1) are
+    at or before it: entry c summarises raw tokens [c*ratio, (c+1)*ratio) and is visible once all of
+    them are ([P1] section 2.8, get_compress_topk_idxs: causal by compression ratio at prefill, the
+    entries up to the current position at decode; section 2.10 for the C4 case)."""
+    return max(int(n_tokens), 0) // int(ratio)
+
+
+def dense_compressed_indices(n_vis: int) -> np.ndarray:
+    """Index list of a layer without an indexer: every visible compressed entry, in order ([P1]
+    section 2.8 get_compress_topk_idxs; section 2.11, the attention forward's branch without an
+    indexer)."""
+    return np.arange(int(n_vis), dtype=np.int64)
+
+
+def run_query_dense(wl, qi: int) -> np.ndarray:
+    """Attention of a layer without an indexer for query ``qi``: [window ++ all visible compressed
+    entries] through the same sparse attention."""
+    return attend(wl, qi, query_window(wl, qi), dense_compressed_indices(int(wl.n_vis[qi])))
+
+
 def run_query(wl, qi: int):
     """Whole path for one query: scores -> top-k -> [window ++ top-k] -> sparse attention.
 

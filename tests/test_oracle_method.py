@@ -226,6 +226,40 @@ def test_decode_path_top_equals_all_when_short():
     np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
 
 
+@pytest.mark.parametrize("ratio", [1, 3, 4, 128])
+def test_compressed_visible_brute_force(ratio):
+    """Entry c is visible when every raw token it summarises ([c*ratio, (c+1)*ratio)) is among the
+    first n tokens; counted token by token."""
+    for n in list(range(0, 300, 7)) + [ratio * 5 - 1, ratio * 5, ratio * 5 + 1]:
+        brute = sum(1 for c in range(n + 1) if all(c * ratio + i < n for i in range(ratio)))
+        assert O.compressed_visible(n, ratio) == brute
+
+
+def test_dense_compressed_layer_equals_dense_sdpa():
+    """A layer without an indexer at ratio 128: the query attends the window ring and all 37 visible
+    compressed entries, which equals dense attention over rows read straight from the pool."""
+    T = 128 * 37 + 5
+    wl = configs.make_decode("hca", [T], H=4, HI=4, seed=9, ratio=128)
+    assert int(wl.n_vis[0]) == O.compressed_visible(T, 128) == 37
+    out = O.run_query_dense(wl, 0)
+    rows = [O.kv_row_values(wl.win_rows[0, p % 128], wl.win_fmt) for p in range(T - 128, T)]
+    rows += [O.kv_row_values(wl.kv_pool[wl.page_table[0, c // 64], c % 64], wl.kv_fmt) for c in range(37)]
+    ref = _sdpa_with_sink(O.q_values(wl.q[0], wl.q_dt), np.array(rows), wl.sink.astype(np.float64),
+                          wl.softmax_scale)
+    np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_dense_compressed_prefill_is_causal():
+    """Prefill at ratio 128: query t sees floor((t+1)/128) entries, so the query at the last token of
+    a block sees that block's entry and the one before it does not."""
+    wl = configs.make_prefill("hca_p", 1024, H=2, HI=2, seed=1, q_start=120, q_count=300, ratio=128)
+    for i, t in enumerate(wl.positions):
+        assert int(wl.n_vis[i]) == O.compressed_visible(int(t) + 1, 128)
+    i = int(np.nonzero(wl.positions == 255)[0][0])
+    assert int(wl.n_vis[i]) == 2 and int(wl.n_vis[i - 1]) == 1
+    np.testing.assert_array_equal(O.dense_compressed_indices(2), [0, 1])
+
+
 def test_scores_use_page_table_and_block_scales():
     """Scores computed from the paged byte layout equal scores from keys decoded entry by entry with
     the scale bytes read at [page][block][slot]."""

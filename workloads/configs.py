@@ -96,6 +96,7 @@ class Workload:
     window: int = WINDOW
     softmax_scale: float = 1.0 / math.sqrt(512.0)
     planted: list = field(default_factory=list)   # long-context workload: planted entries per request
+    ratio: int = COMPRESS                          # raw tokens per compressed entry
     notes: str = ""
 
     @property
@@ -182,7 +183,7 @@ def _indexer_queries(g: np.random.Generator, Q: int, HI: int, idx_dt: int):
 
 def make_decode(name: str, ctx_len, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_BF16,
                 idx_dt=DT_FP8, kv_fmt=KV_FP8, win_fmt=None, seed: int = 0,
-                planted_frac: float = 0.0, topk: int = TOPK) -> Workload:
+                planted_frac: float = 0.0, topk: int = TOPK, ratio: int = COMPRESS) -> Workload:
     """One query per request at the end of a context of ``ctx_len[b]`` raw tokens.
 
     Sub-streams, spawned in this order: page permutation, q, sink, indexer q, w, indexer key pool,
@@ -191,7 +192,7 @@ def make_decode(name: str, ctx_len, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_
     win_fmt = kv_fmt if win_fmt is None else win_fmt
     ctx_len = np.asarray(ctx_len, dtype=np.int32)
     B = int(ctx_len.shape[0])
-    n_c = [int(t) // COMPRESS for t in ctx_len]
+    n_c = [int(t) // ratio for t in ctx_len]
     ss = np.random.SeedSequence(seed).spawn(9)
     g = [np.random.Generator(np.random.PCG64(s)) for s in ss]
 
@@ -248,12 +249,12 @@ def make_decode(name: str, ctx_len, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_
         kv_fmt=kv_fmt, win_fmt=win_fmt, q=_encode_q(q_f, q_dt), sink=sink, qI=qI, qI_scale=qI_s,
         w=w, ik_keys=ik_keys, ik_scales=ik_scales, kv_pool=kv_pool, win_rows=win,
         page_table=page_table, q_req=np.arange(B, dtype=np.int32),
-        n_vis=np.asarray(n_c, dtype=np.int32), ctx_len=ctx_len, topk=topk, planted=planted)
+        n_vis=np.asarray(n_c, dtype=np.int32), ctx_len=ctx_len, topk=topk, planted=planted, ratio=ratio)
 
 
 def make_prefill(name: str, T: int, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_BF16,
                  idx_dt=DT_FP8, kv_fmt=KV_BF16, seed: int = 0, q_start: int = 0,
-                 q_count: int | None = None, topk: int = TOPK) -> Workload:
+                 q_count: int | None = None, topk: int = TOPK, ratio: int = COMPRESS) -> Workload:
     """Causal prefill of one request with ``T`` raw tokens; queries are positions
     ``q_start .. q_start+q_count-1``.  Query t sees compressed entries ``c < (t+1)//4`` and the raw
     window ``[t-127, t]``.
@@ -262,7 +263,7 @@ def make_prefill(name: str, T: int, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_
     compressed KV pool, raw KV rows.
     """
     q_count = T - q_start if q_count is None else q_count
-    n_c = T // COMPRESS
+    n_c = T // ratio
     ss = np.random.SeedSequence(seed).spawn(8)
     g = [np.random.Generator(np.random.PCG64(s)) for s in ss]
     page_table, total_pages = _page_table(g[0], [n_c])
@@ -282,7 +283,7 @@ def make_prefill(name: str, T: int, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_
         kv_fmt=kv_fmt, win_fmt=kv_fmt, q=q, sink=sink, qI=qI, qI_scale=qI_s, w=w,
         ik_keys=ik_keys, ik_scales=ik_scales, kv_pool=kv_pool, win_rows=raw,
         page_table=page_table, q_req=np.zeros(Q, dtype=np.int32),
-        n_vis=((pos + 1) // COMPRESS).astype(np.int32), positions=pos, topk=topk)
+        n_vis=((pos + 1) // ratio).astype(np.int32), positions=pos, topk=topk, ratio=ratio)
 
 
 # ------------------------------------------------------------------------------------------------
