@@ -38,7 +38,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="batched", choices=["batched", "long", "ragged", "tiny", "prefill"])
+    p.add_argument("--config", default="batched", choices=["batched", "long", "ragged", "tiny", "prefill", "dense"],
+                   help="dense: a layer without an indexer (window ++ all 8,192 compressed entries at 1M tokens)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--indexer", default="fp8", choices=["fp8", "fp4"],
@@ -54,6 +55,8 @@ def make_workload(name, indexer):
     from workloads import configs
     if name == "tiny":
         return configs.tiny_decode()
+    if name == "dense":
+        return configs.dense_decode()
     idx_dt = configs.DT_FP4 if indexer == "fp4" else configs.DT_FP8
     return {"batched": configs.batched_decode, "long": configs.long_decode, "ragged": configs.ragged_decode,
             "prefill": configs.causal_prefill}[name](idx_dt=idx_dt)
@@ -71,10 +74,15 @@ def algorithmic_bytes(wl, idx_np):
     key_bytes = int(n_vis.sum()) * IDX_BYTES[wl.idx_dt]
     pt_bytes = int(pages.sum()) * 4
     indexer = key_bytes + pt_bytes + qi_bytes + w_bytes
-    valid_rows = 0
-    for qi in range(Q):
-        row = idx_np[qi]
-        valid_rows += int((row[:128] >= 0).sum()) + int((row[128:] >= 0).sum())
+    if idx_np is None:   # dense compressed lists: every visible entry plus the window
+        T = wl.ctx_len.astype("int64")
+        valid_rows = int((T.clip(0, 128) + n_vis).sum())
+        indexer = 0
+    else:
+        valid_rows = 0
+        for qi in range(Q):
+            row = idx_np[qi]
+            valid_rows += int((row[:128] >= 0).sum()) + int((row[128:] >= 0).sum())
     # window and compressed rows share a format in the configured workloads
     attn = valid_rows * ROW_BYTES[wl.kv_fmt] + q_bytes + H * 4 + Q * H * 512 * (4 if wl.out_dt == 0 else 2)
     return indexer + attn, indexer
@@ -100,7 +108,7 @@ def measured_traffic(kernel, config):
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, target_s):
+def cpu_baseline(wl, target_s, dense=False):
     """Time the oracle (as it stands) on a bounded sample of the workload's queries."""
     import numpy as np
     from oracle import csa_oracle as O
@@ -114,7 +122,10 @@ def cpu_baseline(wl, target_s):
     outs = {}
     while time.perf_counter() - t0 < target_s:
         qi = order[done % len(order)]
-        out, top, _ = O.run_query(wl, qi)
+        if dense:
+            out, top = O.run_query_dense(wl, qi), None
+        else:
+            out, top, _ = O.run_query(wl, qi)
         outs[qi] = (out, top)
         done += 1
         if done >= 4 * len(order):
@@ -170,10 +181,15 @@ def main():
     gen_s = time.perf_counter() - t_gen
     base = torch_io.to_device(wl, dev)
     decode = wl.kind == "decode"
-    runner = run.decode if decode else run.prefill
+    dense = args.config == "dense"
+    if dense:
+        def runner(wl, d, out=None, idx=None, ws=None, stream=None):
+            return run.hca_decode(wl, d, out=out, ws=ws, stream=stream), None
+    else:
+        runner = run.decode if decode else run.prefill
     out, idx = runner(wl, base)
     torch.cuda.synchronize()
-    idx_np = idx.cpu().numpy()
+    idx_np = None if dense else idx.cpu().numpy()
     total_bytes, idx_bytes = algorithmic_bytes(wl, idx_np)
 
     # input copies at distinct addresses so repeated steps miss the Infinity Cache
@@ -186,7 +202,7 @@ def main():
         for k, v in vars(base).items():
             setattr(c, k, v.clone() if isinstance(v, torch.Tensor) else v)
         copies.append(c)
-    ws = (run.decode_workspace if decode else run.prefill_workspace)(wl, dev)
+    ws = (run.hca_decode_workspace if dense else run.decode_workspace if decode else run.prefill_workspace)(wl, dev)
     stream = torch.cuda.current_stream()
 
     def step(i):
@@ -220,16 +236,19 @@ def main():
         if n:
             kernels[name] = round(tot / n * 1e3, 3)
     csa.csa_profile_reset()
-    dominant = f"indexer_{IDX_NAME[wl.idx_dt]}"
+    dominant = "attn_bf16" if dense else f"indexer_{IDX_NAME[wl.idx_dt]}"
     dom = dominant if dominant in kernels else max(kernels, key=kernels.get)
     dom_us = kernels[dom]
     if dom.startswith("indexer"):
         dom_us = indexer_launch_us(wl, copies, stream, args.steps)
-    achieved = idx_bytes / (dom_us * 1e-6) / 1e9
+    # without an indexer the attention moves every byte of the step but q/out's share of the sink
+    dom_bytes = total_bytes if dense else idx_bytes
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     traffic = measured_traffic(dom, args.config)
 
     res = {
-        "metric": "decode query-tokens/s for indexer+top512+sparse_attn; achieved HBM TB/s",
+        "metric": ("decode query-tokens/s for window+all compressed entries (no indexer); achieved HBM TB/s"
+                   if dense else "decode query-tokens/s for indexer+top512+sparse_attn; achieved HBM TB/s"),
         "value": round(value, 1),
         "unit": "query-tokens/s",
         "n_gpus": 1,
@@ -253,13 +272,13 @@ def main():
         "kernel_us": kernels,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": int(idx_bytes), "launch_us": round(dom_us, 3),
+                     "bytes_per_launch": int(dom_bytes), "launch_us": round(dom_us, 3),
                      "traffic": traffic},
         "wall_s_timed": round(wall, 4),
         "gen_s": round(gen_s, 1),
     }
     if not args.no_cpu:
-        cb, outs = cpu_baseline(wl, args.cpu_seconds)
+        cb, outs = cpu_baseline(wl, args.cpu_seconds, dense)
         res["cpu_baseline"] = cb
         o = torch_io.out_to_numpy(out)
         errs = [float(np.abs(o[qi] - ref[0]).max()) for qi, ref in outs.items()]

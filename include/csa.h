@@ -150,7 +150,7 @@ csa_status csa_topk(const float* logits, int64_t ld, const int32_t* n_vis, int32
  *             values (and unmapped pages) are invalid slots.  Duplicates count once per slot.
  *   out       [Q][H][512], out_dt CSA_BF16 or CSA_F32; a query with no valid slot gets exact 0.
  *   ws        >= csa_sparse_attn_workspace_bytes(Q, H, n_win + n_comp) bytes (split-K partials)
- * Ranges: 1 <= Q, 1 <= H <= 128, 0 <= n_win, 0 <= n_comp, 1 <= n_win + n_comp <= 4096,
+ * Ranges: 1 <= Q, 1 <= H <= 128, 0 <= n_win, 0 <= n_comp, 1 <= n_win + n_comp <= 16384,
  *         ld_idx >= n_win + n_comp, softmax_scale finite.
  * ------------------------------------------------------------------------------------------- */
 size_t csa_sparse_attn_workspace_bytes(int32_t Q, int32_t H, int32_t n_idx);
@@ -202,6 +202,37 @@ csa_status csa_prefill(int32_t Q, int32_t H, int32_t HI, int32_t k,
                        const void* raw_rows, int32_t raw_fmt, int64_t T, int64_t pos0,
                        float softmax_scale, void* out, int32_t out_dt, int32_t* idx_out,
                        void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * csa_hca_decode / csa_hca_prefill - attention layers whose compressed cache has no indexer (the
+ * heavily compressed C128 layers of [P1]'s hybrid CSA/HCA design; [P1] section 2.8
+ * get_compress_topk_idxs and the attention forward's branch without an indexer, [P2] concept 2).
+ * Each query attends [window ++ every visible compressed entry]: with `ratio` raw tokens per
+ * compressed entry, decode sees n_vis = T_b / ratio entries and prefill query t sees (t+1) / ratio.
+ * The window is as in csa_decode (ring of the last 128 tokens) and csa_prefill (raw rows
+ * [t-127, t]).  The attention, its precision and its output are those of csa_sparse_attn.
+ *
+ *   comp      paged compressed KV; entry c of request r lives at page_table[r][c >> 6], slot c & 63
+ *   ratio     raw tokens per compressed entry (128 for C128; any value >= 1)
+ *   ws        >= csa_hca_decode_workspace_bytes(B, H, max_ctx, ratio) (decode) or
+ *             csa_hca_prefill_workspace_bytes(Q, H, T, ratio) (prefill) bytes: the index lists
+ *             and split-K partials.  The workspace functions return 0 for arguments out of range.
+ *   Other arguments as in csa_decode / csa_prefill (no indexer inputs, no top-k).
+ * Ranges: as csa_decode / csa_prefill, plus 1 <= ratio and 128 + min(max_ctx / ratio,
+ *         64 * comp->max_pages) <= 16384 (decode; prefill with (pos0 + Q) / ratio).
+ * ------------------------------------------------------------------------------------------- */
+size_t csa_hca_decode_workspace_bytes(int32_t B, int32_t H, int64_t max_ctx, int32_t ratio);
+csa_status csa_hca_decode(int32_t B, int32_t H, const void* q, int32_t q_dt, const float* sink,
+                          const csa_paged_kv* comp, const void* win_ring, int32_t win_fmt,
+                          const int32_t* ctx_len, int64_t max_ctx, int32_t ratio,
+                          float softmax_scale, void* out, int32_t out_dt,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+size_t csa_hca_prefill_workspace_bytes(int32_t Q, int32_t H, int64_t T, int32_t ratio);
+csa_status csa_hca_prefill(int32_t Q, int32_t H, const void* q, int32_t q_dt, const float* sink,
+                           const csa_paged_kv* comp, const void* raw_rows, int32_t raw_fmt,
+                           int64_t T, int64_t pos0, int32_t ratio,
+                           float softmax_scale, void* out, int32_t out_dt,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Diagnostics.

@@ -49,6 +49,12 @@ _SIGS = {
     "csa_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I64, _I32]),
     "csa_prefill": (_I32, [_I32, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _I32, _P, ctypes.POINTER(PagedIdx),
                            ctypes.POINTER(PagedKV), _P, _I32, _I64, _I64, _F32, _P, _I32, _P, _P, _SZ, _P]),
+    "csa_hca_decode_workspace_bytes": (_SZ, [_I32, _I32, _I64, _I32]),
+    "csa_hca_decode": (_I32, [_I32, _I32, _P, _I32, _P, ctypes.POINTER(PagedKV), _P, _I32, _P, _I64, _I32, _F32,
+                              _P, _I32, _P, _SZ, _P]),
+    "csa_hca_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I64, _I32]),
+    "csa_hca_prefill": (_I32, [_I32, _I32, _P, _I32, _P, ctypes.POINTER(PagedKV), _P, _I32, _I64, _I64, _I32,
+                               _F32, _P, _I32, _P, _SZ, _P]),
     "csa_status_string": (ctypes.c_char_p, [_I32]),
     "csa_last_hip_error": (_I32, []),
     "csa_profile_enable": (_I32, [_I32]),
@@ -162,6 +168,28 @@ def csa_prefill(Q, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys: PagedI
         Q, H, HI, k, _ptr(q), q_dt, _ptr(sink), _ptr(qI), _ptr(qI_scale), qI_dt, _ptr(w), ctypes.byref(keys),
         ctypes.byref(comp), _ptr(raw_rows), raw_fmt, T, pos0, softmax_scale, _ptr(out), out_dt, _ptr(idx_out),
         _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def csa_hca_decode_workspace_bytes(B, H, max_ctx, ratio) -> int:
+    return int(lib().csa_hca_decode_workspace_bytes(B, H, max_ctx, ratio))
+
+
+def csa_hca_decode(B, H, q, q_dt, sink, comp: PagedKV, win_ring, win_fmt, ctx_len, max_ctx, ratio, softmax_scale,
+                   out, out_dt, ws, ws_bytes, stream=None):
+    _check("csa_hca_decode", lib().csa_hca_decode(
+        B, H, _ptr(q), q_dt, _ptr(sink), ctypes.byref(comp), _ptr(win_ring), win_fmt, _ptr(ctx_len), max_ctx, ratio,
+        softmax_scale, _ptr(out), out_dt, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def csa_hca_prefill_workspace_bytes(Q, H, T, ratio) -> int:
+    return int(lib().csa_hca_prefill_workspace_bytes(Q, H, T, ratio))
+
+
+def csa_hca_prefill(Q, H, q, q_dt, sink, comp: PagedKV, raw_rows, raw_fmt, T, pos0, ratio, softmax_scale, out, out_dt,
+                    ws, ws_bytes, stream=None):
+    _check("csa_hca_prefill", lib().csa_hca_prefill(
+        Q, H, _ptr(q), q_dt, _ptr(sink), ctypes.byref(comp), _ptr(raw_rows), raw_fmt, T, pos0, ratio, softmax_scale,
+        _ptr(out), out_dt, _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def csa_status_string(status: int) -> str:

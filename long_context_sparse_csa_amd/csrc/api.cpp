@@ -26,6 +26,7 @@ std::vector<ProfRec> g_prof;
 constexpr int kWin = 128;
 constexpr int kHistBins = 4096;
 constexpr int64_t kMaxEntries = (int64_t)1 << 30;
+constexpr int32_t kMaxSlotsPerQuery = 16384;   // attention index-list length (window + compressed)
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -264,7 +265,7 @@ csa_status csa_topk(const float* logits, int64_t ld, const int32_t* n_vis, int32
   csa::PrepArgs p{};
   p.zero_ptr = w.hist;
   p.zero_words = (int64_t)((uint8_t*)w.sel - (uint8_t*)w.hist) / 4;   // hist + counters
-  p.mode = 0;
+  p.mode = 0; p.ratio = 4;
   CSA_HIP(csa::launch_prep(p, stream));
   csa::TopkArgs t{};
   t.logits = logits; t.ld = ld; t.n_vis = n_vis; t.Q = Q; t.max_n_vis = max_n_vis; t.k = k;
@@ -288,7 +289,7 @@ csa_status csa_sparse_attn(const void* q, int32_t q_dt, int32_t Q, int32_t H, co
   if (!q_req || !idx) return CSA_ERR_NULL;
   if (Q < 1 || Q > 65535 || n_req < 1 || n_win < 0 || n_comp < 0) return CSA_ERR_SHAPE;
   const int32_t n_idx = n_win + n_comp;
-  if (n_idx < 1 || n_idx > 4096 || ld_idx < n_idx) return CSA_ERR_SHAPE;
+  if (n_idx < 1 || n_idx > kMaxSlotsPerQuery || ld_idx < n_idx) return CSA_ERR_SHAPE;
   if (n_win > 0) {
     if (!win_rows) return CSA_ERR_NULL;
     if (!kv_fmt_ok(win_fmt)) return CSA_ERR_DTYPE;
@@ -341,6 +342,7 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
     p.zero_words = (int64_t)((uint8_t*)pw.tk.sel - (uint8_t*)pw.tk.hist) / 4;
     p.mode = mode; p.rows = rows; p.ctx_len = ctx_len; p.max_ctx = max_ctx; p.pos0 = pos0;
     p.idx = idx; p.ld_idx = ld_idx; p.n_vis_out = pw.n_vis; p.q_req_out = pw.q_req;
+    p.ratio = 4;
     CSA_HIP(csa::launch_prep(p, stream));
   }
 
@@ -438,6 +440,120 @@ csa_status csa_prefill(int32_t Q, int32_t H, int32_t HI, int32_t k, const void* 
   const size_t need = csa_prefill_workspace_bytes(Q, H, HI, T, k);
   return run_path(2, Q, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys, comp, raw_rows, raw_fmt, T,
                   nullptr, 0, pos0, max_n_vis, softmax_scale, out, out_dt, idx_out, ws, ws_bytes, need, stream);
+}
+
+}  // extern "C"
+
+// ---- layers without an indexer ([P1] section 2.8 get_compress_topk_idxs, and the attention
+// forward's "no indexer" branch): every visible compressed entry is attended, plus the window.
+namespace {
+
+struct HcaWs {
+  int32_t* n_vis;
+  int32_t* q_req;
+  int32_t* idx;
+  float* part;
+};
+
+HcaWs carve_hca(Carver& c, int32_t rows, int32_t H, int64_t n_comp) {
+  HcaWs w;
+  w.n_vis = c.take<int32_t>((size_t)rows * 4);
+  w.q_req = c.take<int32_t>((size_t)rows * 4);
+  w.idx = c.take<int32_t>((size_t)rows * (size_t)(kWin + n_comp) * 4);
+  w.part = c.take<float>(csa::attn_partial_bytes(rows, H, (int)(kWin + n_comp)));
+  return w;
+}
+
+csa_status run_hca(int mode, int32_t rows, int32_t H, const void* q, int32_t q_dt, const float* sink,
+                   const csa_paged_kv* comp, const void* win, int32_t win_fmt, int64_t win_rows_per_req,
+                   const int32_t* ctx_len, int64_t max_ctx, int64_t pos0, int32_t ratio, int64_t n_comp,
+                   float softmax_scale, void* out, int32_t out_dt, void* ws, size_t ws_bytes, hipStream_t stream) {
+  Carver c(ws);
+  HcaWs w = carve_hca(c, rows, H, n_comp);
+  if (!ws || ws_bytes < c.off) return CSA_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return CSA_ERR_ALIGN;
+  const int64_t ld_idx = kWin + n_comp;
+  csa::PrepArgs p{};
+  p.mode = mode; p.rows = rows; p.ctx_len = ctx_len; p.max_ctx = max_ctx; p.pos0 = pos0;
+  p.idx = w.idx; p.ld_idx = ld_idx; p.n_vis_out = w.n_vis; p.q_req_out = w.q_req;
+  p.ratio = ratio; p.comp_cols = n_comp;
+  CSA_HIP(csa::launch_prep(p, stream));
+
+  csa::AttnArgs a{};
+  a.q = q; a.q_dt = q_dt; a.Q = rows; a.H = H; a.sink = sink;
+  a.win = (const uint8_t*)win; a.win_fmt = win_fmt; a.win_rows_per_req = win_rows_per_req;
+  const int nc = (int)n_comp;
+  if (nc > 0) {
+    a.comp = (const uint8_t*)comp->rows; a.comp_fmt = comp->fmt; a.comp_num_pages = comp->num_pages;
+    a.page_table = comp->page_table; a.max_pages = comp->max_pages;
+  }
+  a.q_req = w.q_req; a.n_req = mode == 1 ? rows : 1; a.idx = w.idx; a.ld_idx = ld_idx; a.n_win = kWin;
+  a.n_comp = nc; a.softmax_scale = softmax_scale; a.out = out; a.out_dt = out_dt;
+  a.n_split = csa::attn_uses_matrix_cores(q_dt, win_fmt, a.comp_fmt, kWin, nc)
+                  ? csa::plan_attn_split(rows, H, kWin + nc, q_dt) : 1;
+  a.part = w.part;
+  a.req_mode = mode;
+  return hip_status(csa::launch_attention(a, stream));
+}
+
+csa_status check_hca(int32_t rows, int32_t H, const void* q, int32_t q_dt, const float* sink,
+                     const csa_paged_kv* comp, const void* win, int32_t win_fmt, int32_t ratio, float scale,
+                     void* out, int32_t out_dt) {
+  CSA_TRY(check_attn_common(q, q_dt, H, sink, out, out_dt, scale));
+  CSA_TRY(check_kv_struct(comp));
+  if (!win) return CSA_ERR_NULL;
+  if (!kv_fmt_ok(win_fmt)) return CSA_ERR_DTYPE;
+  if (!aligned(win, 16)) return CSA_ERR_ALIGN;
+  if (rows < 1 || rows > 65535 || ratio < 1) return CSA_ERR_SHAPE;
+  return CSA_OK;
+}
+
+int64_t hca_cols(int64_t n_vis_max, const csa_paged_kv* comp) {
+  return std::min<int64_t>(n_vis_max, (int64_t)comp->max_pages * 64);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t csa_hca_decode_workspace_bytes(int32_t B, int32_t H, int64_t max_ctx, int32_t ratio) {
+  if (B < 1 || H < 1 || max_ctx < 0 || ratio < 1 || max_ctx / ratio + kWin > kMaxSlotsPerQuery) return 0;
+  Carver c(nullptr);
+  carve_hca(c, B, H, max_ctx / ratio);
+  return c.off;
+}
+
+csa_status csa_hca_decode(int32_t B, int32_t H, const void* q, int32_t q_dt, const float* sink,
+                          const csa_paged_kv* comp, const void* win_ring, int32_t win_fmt, const int32_t* ctx_len,
+                          int64_t max_ctx, int32_t ratio, float softmax_scale, void* out, int32_t out_dt, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+  CSA_TRY(check_hca(B, H, q, q_dt, sink, comp, win_ring, win_fmt, ratio, softmax_scale, out, out_dt));
+  if (!ctx_len) return CSA_ERR_NULL;
+  if (!aligned(ctx_len, 4)) return CSA_ERR_ALIGN;
+  if (max_ctx < 0 || max_ctx > INT32_MAX) return CSA_ERR_SHAPE;
+  const int64_t n_comp = hca_cols(max_ctx / ratio, comp);
+  if (kWin + n_comp > kMaxSlotsPerQuery) return CSA_ERR_SHAPE;
+  return run_hca(1, B, H, q, q_dt, sink, comp, win_ring, win_fmt, kWin, ctx_len, max_ctx, 0, ratio, n_comp,
+                 softmax_scale, out, out_dt, ws, ws_bytes, stream);
+}
+
+size_t csa_hca_prefill_workspace_bytes(int32_t Q, int32_t H, int64_t T, int32_t ratio) {
+  if (Q < 1 || H < 1 || T < 0 || ratio < 1 || T / ratio + kWin > kMaxSlotsPerQuery) return 0;
+  Carver c(nullptr);
+  carve_hca(c, Q, H, T / ratio);
+  return c.off;
+}
+
+csa_status csa_hca_prefill(int32_t Q, int32_t H, const void* q, int32_t q_dt, const float* sink,
+                           const csa_paged_kv* comp, const void* raw_rows, int32_t raw_fmt, int64_t T, int64_t pos0,
+                           int32_t ratio, float softmax_scale, void* out, int32_t out_dt, void* ws, size_t ws_bytes,
+                           hipStream_t stream) {
+  CSA_TRY(check_hca(Q, H, q, q_dt, sink, comp, raw_rows, raw_fmt, ratio, softmax_scale, out, out_dt));
+  if (T < 1 || T > INT32_MAX || pos0 < 0 || pos0 + Q > T) return CSA_ERR_SHAPE;
+  const int64_t n_comp = hca_cols((pos0 + Q) / ratio, comp);
+  if (kWin + n_comp > kMaxSlotsPerQuery) return CSA_ERR_SHAPE;
+  return run_hca(2, Q, H, q, q_dt, sink, comp, raw_rows, raw_fmt, T, nullptr, 0, pos0, ratio, n_comp,
+                 softmax_scale, out, out_dt, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

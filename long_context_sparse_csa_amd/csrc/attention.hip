@@ -35,7 +35,7 @@ namespace csa {
 
 constexpr int kTile = 32;
 constexpr int kKrStride = 528;   // bf16 per row of the row-major tile (1056 B, 16-B aligned)
-constexpr int kMaxSplit = 8;
+constexpr int kMaxSplit = 32;   // key-range splits of one query: with kMaxSlots, 32,768 slots
 constexpr float kRescaleLog2 = 8.f;
 
 struct RowSrc {
@@ -851,50 +851,106 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs
 }
 
 // Merge split-K partials: out = sum_s 2^(m_s-M) amax_s o_s / (sum_s 2^(m_s-M) l_s + 2^(sink-M)),
-// o_s the fp16 partial (acc_s / amax_s).  Block = one query, four heads; thread = 8 dims of a head.
-// Every partial is loaded up front (the split loop is unrolled to its maximum and predicated).
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  const int q = blockIdx.x % a.Q, h = (blockIdx.x / a.Q) * 4 + (threadIdx.x >> 6);
-  if (h >= a.H) return;
+// o_s the fp16 partial (acc_s / amax_s).  A thread owns 8 dims of one head and merges groups of
+// kCombineGroup splits, every partial of a group loaded up front (the group loop is unrolled and
+// predicated); a later group rescales what the earlier ones summed when it raises the max.
+constexpr int kCombineGroup = 8;
+
+// merges split groups starting at s_first, every s_step splits, into (M, den, o)
+__device__ __forceinline__ void merge_split_groups(const AttnArgs& a, int q, int h, int d, int s_first, int s_step,
+                                                   float& M, float& den, float* o) {
   const int Hpad = (a.H + 15) & ~15;
-  const int d = (threadIdx.x & 63) * 8;
   const uint16_t* p16 = (const uint16_t*)a.part;
   const float* ml = (const float*)((const uint8_t*)a.part + (size_t)a.Q * a.n_split * Hpad * kD * sizeof(uint16_t));
-  float4 mls[kMaxSplit];
-  uint4 x[kMaxSplit];
+#pragma unroll 1
+  for (int s0 = s_first; s0 < a.n_split; s0 += s_step) {
+    float4 mls[kCombineGroup];
+    uint4 x[kCombineGroup];
 #pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s) {
-    const int sc = s < a.n_split ? s : 0;
-    const int64_t prow = ((int64_t)q * a.n_split + sc) * Hpad + h;
-    mls[s] = *(const float4*)(ml + prow * 4);
-    x[s] = *(const uint4*)(p16 + prow * kD + d);
-  }
-  const float sk = a.sink[h] * kLog2e;
-  float M = sk;
+    for (int i = 0; i < kCombineGroup; ++i) {
+      const int sc = s0 + i < a.n_split ? s0 + i : s0;
+      const int64_t prow = ((int64_t)q * a.n_split + sc) * Hpad + h;
+      mls[i] = *(const float4*)(ml + prow * 4);
+      x[i] = *(const uint4*)(p16 + prow * kD + d);
+    }
+    float Mg = M;
 #pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s)
-    if (s < a.n_split) M = fmaxf(M, mls[s].x);
-  float den = exp2f(sk - M);
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < kCombineGroup; ++i)
+      if (s0 + i < a.n_split) Mg = fmaxf(Mg, mls[i].x);
+    const float r = exp2f(M - Mg);
+    den *= r;
 #pragma unroll
-  for (int s = 0; s < kMaxSplit; ++s) {
-    if (s < a.n_split) {
-      const float w = exp2f(mls[s].x - M);
-      den = fmaf(w, mls[s].y, den);
-      const float wa = w * mls[s].z;
-      const uint32_t xs[4] = {x[s].x, x[s].y, x[s].z, x[s].w};
+    for (int e = 0; e < 8; ++e) o[e] *= r;
+    M = Mg;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const v2f v = unpack_f16x2(xs[e]);
-        o[2 * e] = fmaf(wa, v[0], o[2 * e]);
-        o[2 * e + 1] = fmaf(wa, v[1], o[2 * e + 1]);
+    for (int i = 0; i < kCombineGroup; ++i) {
+      if (s0 + i < a.n_split) {
+        const float w = exp2f(mls[i].x - M);
+        den = fmaf(w, mls[i].y, den);
+        const float wa = w * mls[i].z;
+        const uint32_t xs[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const v2f v = unpack_f16x2(xs[e]);
+          o[2 * e] = fmaf(wa, v[0], o[2 * e]);
+          o[2 * e + 1] = fmaf(wa, v[1], o[2 * e + 1]);
+        }
       }
     }
   }
+}
+
+__device__ __forceinline__ void store_merged(const AttnArgs& a, int q, int h, int d, float den, const float* o) {
   const float inv = 1.f / den;
   const int64_t ob = ((int64_t)q * a.H + h) * kD + d;
   store4(a.out, a.out_dt, ob, o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv);
   store4(a.out, a.out_dt, ob + 4, o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv);
+}
+
+// Block = one query, four heads (a wave per head); used up to kCombineGroup splits.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+  const int q = blockIdx.x % a.Q, h = (blockIdx.x / a.Q) * 4 + (threadIdx.x >> 6);
+  if (h >= a.H) return;
+  const int d = (threadIdx.x & 63) * 8;
+  float M = a.sink[h] * kLog2e, den = 1.f;   // den holds 2^(sink - M) plus the merged splits' terms
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  merge_split_groups(a, q, h, d, 0, kCombineGroup, M, den, o);
+  store_merged(a, q, h, d, den, o);
+}
+
+// More splits (long index lists): block = one (query, head); wave w merges split groups w, w + 4,
+// ..., so four group chains run side by side, and wave 0 merges the four states through LDS.  Only
+// wave 0 starts from the sink term; the others start empty (max -1e30, nothing summed).
+__global__ __launch_bounds__(256) void attn_combine_wide_kernel(AttnArgs a) {
+  const int q = blockIdx.x % a.Q, h = blockIdx.x / a.Q;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int d = lane * 8;
+  __shared__ float sm[4], sden[4];
+  __shared__ float so[4][8][64];   // [wave][dim e][lane]: conflict-free writes and reads
+  const float sk = a.sink[h] * kLog2e;
+  float M = wave == 0 ? sk : kNegBig, den = wave == 0 ? 1.f : 0.f;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  merge_split_groups(a, q, h, d, wave * kCombineGroup, 4 * kCombineGroup, M, den, o);
+  if (lane == 0) {
+    sm[wave] = M;
+    sden[wave] = den;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) so[wave][e][lane] = o[e];
+  __syncthreads();
+  if (wave != 0) return;
+  const float Mt = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+  float f[4], dt = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    f[w] = exp2f(sm[w] - Mt);
+    dt = fmaf(sden[w], f[w], dt);
+  }
+  float ot[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    ot[e] = (so[0][e][lane] * f[0] + so[1][e][lane] * f[1]) + (so[2][e][lane] * f[2] + so[3][e][lane] * f[3]);
+  store_merged(a, q, h, d, dt, ot);
 }
 
 // fp32 path: block = (query, head); all arithmetic in fp32.
@@ -964,22 +1020,23 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
-// Heads per block of the matrix-core kernels: 16 when the heads fit one group of 16 (no padded
-// head groups), else 64, where each dequantised K tile serves four head groups.  At 64 heads and
-// small batches the 16-head kernel (split or not) measured no faster than the 64-head one with a
-// key split: its per-tile cost is dequantisation and LDS latency, repeated for every head group.
-// Heads per block: 64 (one block per query and key range, q read once per range) unless the heads
-// fit one group of 16, or the batch is small: with few queries, 16-head blocks fill the GPU with
+// Heads per block of the matrix-core kernels: 64 (one block per query and key range, q read once
+// per range, each dequantised tile serving four head groups) unless the heads fit one group of 16,
+// or the batch is small and its lists short: with few queries, 16-head blocks fill the GPU with
 // four times as many blocks per key range, so each range can stay longer (measured on decode with
 // 64 heads and 640 slots: 8 queries take 13.8 us in 16-head blocks against 19.0 us in 64-head
-// blocks; 32 queries take 22.5 against 20.8).
-int attn_head_block(int Q, int H) {
+// blocks; 32 queries take 22.5 against 20.8).  Long lists have key ranges enough to fill the GPU
+// with 64-head blocks, and 16-head blocks would gather every row four times (8 queries of 8,320
+// slots: 27.7 us in 64-head blocks, 80.1 us in 16-head blocks).
+constexpr int kSmallBatchSlots = 2048;
+
+int attn_head_block(int Q, int H, int n_idx) {
   static const int forced = [] {
     const char* e = getenv("CSA_ATTN_HEADS");   // tuning override: 16 or 64
     return e ? atoi(e) : 0;
   }();
   if (forced == 16 || forced == 64) return forced;
-  return ((H + 15) / 16 == 1 || Q <= 16) ? 16 : 64;
+  return ((H + 15) / 16 == 1 || (Q <= 16 && n_idx <= kSmallBatchSlots)) ? 16 : 64;
 }
 
 int plan_attn_split(int Q, int H, int n_idx, int q_dt) {
@@ -989,13 +1046,13 @@ int plan_attn_split(int Q, int H, int n_idx, int q_dt) {
     return e ? atoi(e) : 0;
   }();
   const int n_tiles = (n_idx + kTile - 1) / kTile;
-  // a block holds at most kMaxSlots slots (n_idx <= 4096 keeps this within kMaxSplit)
+  // a block holds at most kMaxSlots slots (n_idx <= kMaxSplit * kMaxSlots keeps this within kMaxSplit)
   const int min_s = (n_tiles + kMaxSlots / kTile - 1) / (kMaxSlots / kTile);
   if (forced > 0) {
     const int f = forced < kMaxSplit ? (forced < n_tiles ? forced : n_tiles) : (kMaxSplit < n_tiles ? kMaxSplit : n_tiles);
     return f > min_s ? f : min_s;
   }
-  const int hb = attn_head_block(Q, H);
+  const int hb = attn_head_block(Q, H, n_idx);
   const int hchunks = (((H + 15) & ~15) + hb - 1) / hb;
   const int blocks = Q * hchunks;
   int s = (256 + blocks - 1) / blocks;
@@ -1029,7 +1086,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   const int Hpad = (a.H + 15) & ~15;
-  const int hb = attn_head_block(a.Q, a.H);
+  const int hb = attn_head_block(a.Q, a.H, a.n_win + a.n_comp);
   const int hchunks = (Hpad + hb - 1) / hb;
   // a source with no slots takes the other source's format (its loads are never issued)
   const int wf = a.n_win > 0 ? a.win_fmt : a.comp_fmt;
@@ -1052,7 +1109,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   ProfScope p("attn_combine", s);
-  hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.Q * ((a.H + 3) / 4))), dim3(256), 0, s, a);
+  if (a.n_split <= kCombineGroup)
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.Q * ((a.H + 3) / 4))), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(attn_combine_wide_kernel, dim3((unsigned)(a.Q * a.H)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

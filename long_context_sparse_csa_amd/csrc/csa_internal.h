@@ -86,6 +86,8 @@ struct PrepArgs {
   int64_t ld_idx;
   int32_t* n_vis_out;        // [rows]
   int32_t* q_req_out;        // optional [rows]: request id of each row (decode: row, prefill: 0)
+  int ratio;                 // raw tokens per compressed entry: n_vis = T / ratio or (t + 1) / ratio
+  int64_t comp_cols;         // > 0: also write compressed columns [128, 128 + comp_cols) as j < n_vis ? j : -1
 };
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
 

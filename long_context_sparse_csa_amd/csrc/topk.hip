@@ -707,7 +707,19 @@ hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// ---- preparation: clear counters/histograms, window indices, visible counts, request ids
+// ---- preparation: clear counters/histograms, window indices, visible counts, request ids, and
+// (layers without an indexer) the dense compressed index lists
+// visible compressed entries of row rrow: every entry whose `ratio` raw tokens are all at or before
+// the row's position (decode: T tokens, the current one included; prefill: position t)
+__device__ __forceinline__ int64_t prep_visible(const PrepArgs& a, int rrow) {
+  if (a.mode == 1) {
+    int64_t T = a.ctx_len[rrow];
+    T = T < 0 ? 0 : (T > a.max_ctx ? a.max_ctx : T);
+    return T / a.ratio;
+  }
+  return (a.pos0 + rrow + 1) / a.ratio;
+}
+
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * 256;
@@ -716,29 +728,33 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   for (int64_t i = gid; i < (int64_t)a.rows * kWin; i += stride) {
     const int rrow = (int)(i / kWin), j = (int)(i % kWin);
     int32_t v;
-    int64_t nvis;
     if (a.mode == 1) {   // decode: ring slot of position T-128+j
       int64_t T = a.ctx_len[rrow];
       T = T < 0 ? 0 : (T > a.max_ctx ? a.max_ctx : T);
       const int64_t p = T - kWin + j;
       v = p >= 0 ? (int32_t)(p % kWin) : -1;
-      nvis = T / 4;
     } else {             // causal prefill: raw position t-127+j
       const int64_t t = a.pos0 + rrow;
       const int64_t p = t - (kWin - 1) + j;
       v = p >= 0 ? (int32_t)p : -1;
-      nvis = (t + 1) / 4;
     }
     a.idx[(int64_t)rrow * a.ld_idx + j] = v;
     if (j == 0) {
-      a.n_vis_out[rrow] = (int32_t)nvis;
+      a.n_vis_out[rrow] = (int32_t)prep_visible(a, rrow);
       if (a.q_req_out) a.q_req_out[rrow] = a.mode == 1 ? rrow : 0;
     }
+  }
+  // dense compressed list: entry j while visible, then -1 (row-major, so stores coalesce)
+  for (int64_t i = gid; i < (int64_t)a.rows * a.comp_cols; i += stride) {
+    const int rrow = (int)(i / a.comp_cols);
+    const int64_t j = i % a.comp_cols;
+    a.idx[(int64_t)rrow * a.ld_idx + kWin + j] = j < prep_visible(a, rrow) ? (int32_t)j : -1;
   }
 }
 
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
   int64_t work = a.zero_words > (int64_t)a.rows * kWin ? a.zero_words : (int64_t)a.rows * kWin;
+  if ((int64_t)a.rows * a.comp_cols > work) work = (int64_t)a.rows * a.comp_cols;
   int64_t blocks = (work + 255) / 256;
   if (blocks < 1) blocks = 1;
   if (blocks > 2048) blocks = 2048;

@@ -158,6 +158,51 @@ def test_prefill_rejects(kw, status):
     assert _prefill(**kw) == status
 
 
+def _hca_decode(**kw):
+    a = dict(B=2, H=64, q=FAKE, q_dt=1, sink=FAKE, comp=_kv(), win=FAKE, win_fmt=2, ctx=FAKE, max_ctx=65536,
+             ratio=128, scale=0.044, out=FAKE, out_dt=1, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return csa.lib().csa_hca_decode(a["B"], a["H"], a["q"], a["q_dt"], a["sink"], ctypes.byref(a["comp"]), a["win"],
+                                    a["win_fmt"], a["ctx"], a["max_ctx"], a["ratio"], a["scale"], a["out"],
+                                    a["out_dt"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(ctx=None), -1), (dict(win=None), -1), (dict(sink=None), -1),
+    (dict(comp=_kv(page_table=None)), -1), (dict(win_fmt=5), -3), (dict(q_dt=2), -3),
+    (dict(B=0), -2), (dict(H=129), -2), (dict(ratio=0), -2), (dict(max_ctx=-1), -2),
+    (dict(ratio=4, comp=_kv(max_pages=1024), max_ctx=1 << 20), -2),        # 128 + 65,536 slots per query
+    (dict(ws=None), -5), (dict(ws_bytes=100), -5), (dict(ws=FAKE + 8), -4), (dict(ctx=FAKE + 2), -4),
+])
+def test_hca_decode_rejects(kw, status):
+    assert _hca_decode(**kw) == status
+
+
+def _hca_prefill(**kw):
+    a = dict(Q=16, H=64, q=FAKE, q_dt=1, sink=FAKE, comp=_kv(), raw=FAKE, raw_fmt=1, T=4096, pos0=0, ratio=128,
+             scale=0.044, out=FAKE, out_dt=1, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return csa.lib().csa_hca_prefill(a["Q"], a["H"], a["q"], a["q_dt"], a["sink"], ctypes.byref(a["comp"]), a["raw"],
+                                     a["raw_fmt"], a["T"], a["pos0"], a["ratio"], a["scale"], a["out"], a["out_dt"],
+                                     a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(raw=None), -1), (dict(out=None), -1), (dict(pos0=4090), -2), (dict(T=0), -2), (dict(ratio=-3), -2),
+    (dict(ws_bytes=8), -5), (dict(scale=float("inf")), -2),
+])
+def test_hca_prefill_rejects(kw, status):
+    assert _hca_prefill(**kw) == status
+
+
+def test_hca_workspace_queries():
+    n = csa.csa_hca_decode_workspace_bytes(8, 64, 1 << 20, 128)
+    assert n >= 8 * (128 + 8192) * 4                                   # the index lists
+    assert csa.csa_hca_decode_workspace_bytes(8, 64, 1 << 20, 4) == 0   # 262,144 slots: out of range
+    assert csa.csa_hca_decode_workspace_bytes(8, 64, 1 << 20, 0) == 0
+    assert csa.csa_hca_prefill_workspace_bytes(8192, 64, 8192, 128) >= 8192 * (128 + 64) * 4
+
+
 def test_profile_toggle_without_launches():
     csa.csa_profile_enable(True)
     assert csa.csa_profile_collect("indexer_fp8") == (0.0, 0)

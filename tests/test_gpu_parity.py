@@ -293,3 +293,67 @@ def test_prefill_chunk_ragged(dev, idx_dt):
         check_topk_row(idx[i, 128:], scores, nv, wl.topk, f"t={t}")
         ref = O.attend(wl, i, idx[i, :128], idx[i, 128:])
         check_attention(out[i], ref, BF16_TOL, f"t={t}")
+
+
+# ------------------------------------------------------------------------------------ no indexer
+def test_hca_decode_ragged(dev):
+    """Layers without an indexer at ratio 128: window ring ++ every visible compressed entry, over
+    contexts with 0, 37, 130 and 512 visible entries, an empty context and a context shorter than
+    the window."""
+    run, tio = _run()
+    ctx = [128 * 37 + 5, 0, 100, 128 * 130 + 127, 1 << 16]
+    wl = configs.make_decode("hca_ragged", ctx, H=64, HI=4, seed=12, ratio=128)
+    _say(f"hca decode ragged ctx={ctx} ratio=128")
+    out = tio.out_to_numpy(run.hca_decode(wl, tio.to_device(wl, dev)))
+    for qi in range(wl.Q):
+        err = check_attention(out[qi], O.run_query_dense(wl, qi), BF16_TOL, f"query {qi}")
+        _say(f"query {qi} (n_vis {int(wl.n_vis[qi])}): max err {err:.2e}")
+    assert np.all(out[1] == 0.0)
+
+
+def test_hca_decode_million_tokens(dev):
+    """Two requests at 1,048,576 tokens (8,192 compressed entries each): 8,320-slot lists, split over
+    more key ranges than one merge group holds."""
+    run, tio = _run()
+    wl = configs.dense_decode(B=2)
+    _say("hca decode (B=2, T=1048576, ratio 128, fp8 rows)")
+    out = tio.out_to_numpy(run.hca_decode(wl, tio.to_device(wl, dev)))
+    for qi in range(wl.Q):
+        err = check_attention(out[qi], O.run_query_dense(wl, qi), BF16_TOL, f"query {qi}")
+        _say(f"query {qi}: max err {err:.2e}")
+
+
+def test_hca_prefill_chunk(dev):
+    """Prefill without an indexer at ratio 128: a chunk starting mid-sequence; query t attends raw
+    rows [t-127, t] and compressed entries c < (t+1)/128."""
+    run, tio = _run()
+    wl = configs.make_prefill("hca_prefill", 4100, H=64, HI=4, seed=13, q_start=2003, q_count=1013, ratio=128)
+    _say("hca prefill chunk (T=4100, q 2003..3015, ratio 128)")
+    out = tio.out_to_numpy(run.hca_prefill(wl, tio.to_device(wl, dev)))
+    sample = sorted(set([0, 1, 45, 46, 47, 172, 173, 174, 1012] +
+                        np.random.default_rng(2).choice(wl.Q, 12, replace=False).tolist()))
+    for i in sample:
+        check_attention(out[i], O.run_query_dense(wl, i), BF16_TOL, f"t={int(wl.positions[i])}")
+
+
+@pytest.mark.parametrize("H", [64, 8])
+def test_sparse_attn_long_lists(dev, H):
+    """Explicit index lists of 9,128 slots (invalid, out-of-range and duplicate slots included):
+    enough key ranges that the split partials merge in several groups."""
+    run, tio = _run()
+    wl = configs.make_decode("attn_long", [1 << 20, 40000, 3 << 18], H=H, HI=4, seed=23, ratio=32)
+    rng = np.random.default_rng(H)
+    n_win, n_comp = 128, 9000
+    limit = wl.max_pages * 64
+    idx = np.empty((wl.Q, n_win + n_comp), np.int32)
+    idx[:, :n_win] = rng.integers(-5, 140, size=(wl.Q, n_win))
+    idx[:, n_win:] = rng.integers(-3, limit + 10, size=(wl.Q, n_comp))
+    idx[0, n_win + 7] = idx[0, n_win + 8000]
+    _say(f"sparse_attn long lists H={H} n_comp={n_comp}")
+    d = tio.to_device(wl, dev)
+    out = tio.out_to_numpy(run.sparse_attn(wl, d, torch.from_numpy(idx).to(dev), n_win, n_comp))
+    for qi in range(wl.Q):
+        ref = O.attend(wl, qi, idx[qi, :n_win], idx[qi, n_win:])
+        err = check_attention(out[qi], ref, BF16_TOL, f"query {qi}")
+        _say(f"query {qi}: max err {err:.2e}")
+

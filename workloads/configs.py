@@ -318,6 +318,13 @@ def causal_prefill(seed: int = 0, T: int = 8192, H: int = 64, HI: int = 64, q_st
                         idx_dt=idx_dt)
 
 
+def dense_decode(seed: int = 0, B: int = 8, T: int = 1 << 20, H: int = 64, ratio: int = 128) -> Workload:
+    """A layer without an indexer (heavily compressed, ratio 128): B=8 requests at T=1,048,576, so
+    each query attends 128 window rows and all 8,192 compressed rows; FP8-nope/BF16-rope rows, bf16
+    q.  The indexer arrays the generator also draws are not used on this path."""
+    return make_decode("dense_decode", [T] * B, H=H, HI=16, seed=seed, ratio=ratio)
+
+
 RAGGED_EMPTY_ROWS = (3, 17, 42, 63)
 
 

@@ -89,3 +89,33 @@ def sparse_attn(wl: Workload, d, idx: torch.Tensor, n_win: int, n_comp: int, str
                         _comp(wl, d), d.q_req, wl.B, idx, idx.shape[1], n_win, n_comp, wl.softmax_scale, out,
                         wl.out_dt, ws, n, stream)
     return out
+
+
+def hca_decode_workspace(wl: Workload, device="cuda"):
+    n = csa.csa_hca_decode_workspace_bytes(wl.B, wl.H, int(wl.ctx_len.max()), wl.ratio)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device), n
+
+
+def hca_decode(wl: Workload, d, out=None, ws=None, stream=None):
+    """One csa_hca_decode call (window ++ every visible compressed entry); returns out [B,H,512]."""
+    dev = d.q.device
+    out = empty_out(wl, dev) if out is None else out
+    ws, nbytes = hca_decode_workspace(wl, dev) if ws is None else ws
+    csa.csa_hca_decode(wl.B, wl.H, d.q, wl.q_dt, d.sink, _comp(wl, d), d.win_rows, wl.win_fmt, d.ctx_len,
+                       int(wl.ctx_len.max()), wl.ratio, wl.softmax_scale, out, wl.out_dt, ws, nbytes, stream)
+    return out
+
+
+def hca_prefill_workspace(wl: Workload, device="cuda"):
+    n = csa.csa_hca_prefill_workspace_bytes(wl.Q, wl.H, int(wl.win_rows.shape[1]), wl.ratio)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device), n
+
+
+def hca_prefill(wl: Workload, d, out=None, ws=None, stream=None):
+    dev = d.q.device
+    out = empty_out(wl, dev) if out is None else out
+    ws, nbytes = hca_prefill_workspace(wl, dev) if ws is None else ws
+    T = int(wl.win_rows.shape[1])
+    csa.csa_hca_prefill(wl.Q, wl.H, d.q, wl.q_dt, d.sink, _comp(wl, d), d.win_rows[0], wl.win_fmt, T,
+                        int(wl.positions[0]), wl.ratio, wl.softmax_scale, out, wl.out_dt, ws, nbytes, stream)
+    return out
