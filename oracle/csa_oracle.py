@@ -182,15 +182,25 @@ def topk_select(s: np.ndarray, n_vis: int, k: int) -> np.ndarray:
     return order[:k].astype(np.int64)
 
 
-def window_decode(ctx_len: int, window: int = WINDOW) -> np.ndarray:
+def window_decode(ctx_len: int, window: int = WINDOW, ring: int = WINDOW) -> np.ndarray:
     """Ring-slot indices of the sliding window at decode ([P1] section 2.8, get_window_topk_idxs:
     a ring buffer at decode, -1 for absent positions).
 
     With ``ctx_len`` raw tokens (the current one included), slot j of the list holds position
-    ``p = ctx_len - window + j``; it is valid when p >= 0 and lives in ring slot ``p % window``.
+    ``p = ctx_len - window + j``; it is valid when p >= 0 and lives in ring slot ``p % ring`` (a
+    ring of ``window`` slots for one query per request; multi-query decode keeps ``ring`` >=
+    window + queries - 1 slots so the earliest query's window is still held).
     """
     p = ctx_len - window + np.arange(window)
-    return np.where(p >= 0, p % window, -1).astype(np.int64)
+    return np.where(p >= 0, p % ring, -1).astype(np.int64)
+
+
+def decode_tokens_seen(ctx_len: int, queries: int, j: int) -> int:
+    """Raw tokens at or before query j of a request decoding ``queries`` tokens at once (the last
+    ``queries`` of its ``ctx_len`` tokens, as in multi-token prediction / speculative decoding,
+    [P1] sections 2.17 and [P2]'s NextN variant): query j sits at position ctx_len - queries + j
+    and causally sees the tokens up to it."""
+    return max(int(ctx_len) - (int(queries) - 1 - int(j)), 0)
 
 
 def window_prefill(t: int, window: int = WINDOW) -> np.ndarray:
@@ -252,7 +262,9 @@ def query_scores(wl, qi: int) -> np.ndarray:
 
 def query_window(wl, qi: int) -> np.ndarray:
     if wl.kind == "decode":
-        return window_decode(int(wl.ctx_len[wl.q_req[qi]]), wl.window)
+        S = wl.q_per_req
+        seen = decode_tokens_seen(int(wl.ctx_len[wl.q_req[qi]]), S, qi % S)
+        return window_decode(seen, wl.window, wl.ring)
     return window_prefill(int(wl.positions[qi]), wl.window)
 
 

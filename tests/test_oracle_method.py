@@ -260,6 +260,42 @@ def test_dense_compressed_prefill_is_causal():
     np.testing.assert_array_equal(O.dense_compressed_indices(2), [0, 1])
 
 
+@pytest.mark.parametrize("T,S", [(5000, 2), (5000, 4), (130, 3), (3, 4), (128, 2), (129, 4)])
+def test_multi_query_window_against_simulated_ring(T, S):
+    """S queries per request (the last S of T tokens): write tokens 0..T-1 one by one into a ring of
+    128 + S - 1 slots, then every valid slot of query j's window must hold exactly the positions
+    [p-127, p] (p = T - S + j), in order, with -1 for positions before 0."""
+    R = 128 + S - 1
+    ring = np.full(R, -1)
+    for pos in range(T):
+        ring[pos % R] = pos
+    for j in range(S):
+        p = T - S + j
+        win = O.window_decode(O.decode_tokens_seen(T, S, j), 128, R)
+        expect = np.arange(p - 127, p + 1)
+        for slot, e in zip(win, expect):
+            if e < 0:
+                assert slot == -1
+            else:
+                assert slot >= 0 and ring[slot] == e
+
+
+def test_multi_query_visibility_and_single_query_reduction():
+    """Query j of S sees the compressed entries whose 4 tokens are all at or before position
+    T - S + j; with S = 1 the workload is the plain one-query decode."""
+    wl = configs.make_decode("mq", [4099, 7, 20000], H=2, HI=2, seed=4, q_per_req=3)
+    assert wl.Q == 9 and wl.win_rows.shape[1] == 130
+    for q in range(wl.Q):
+        T = int(wl.ctx_len[q // 3])
+        p = T - 3 + q % 3
+        assert int(wl.q_req[q]) == q // 3
+        assert int(wl.n_vis[q]) == sum(1 for c in range(p + 2) if 4 * c + 3 <= p)
+    one = configs.make_decode("mq1", [4099, 7], H=2, HI=2, seed=4, q_per_req=1)
+    ref = configs.make_decode("mq1", [4099, 7], H=2, HI=2, seed=4)
+    assert one.Q == 2 and np.array_equal(one.q, ref.q) and np.array_equal(one.n_vis, [1024, 1])
+    np.testing.assert_array_equal(O.query_window(one, 0), O.window_decode(4099))
+
+
 def test_scores_use_page_table_and_block_scales():
     """Scores computed from the paged byte layout equal scores from keys decoded entry by entry with
     the scale bytes read at [page][block][slot]."""

@@ -97,6 +97,8 @@ class Workload:
     softmax_scale: float = 1.0 / math.sqrt(512.0)
     planted: list = field(default_factory=list)   # long-context workload: planted entries per request
     ratio: int = COMPRESS                          # raw tokens per compressed entry
+    q_per_req: int = 1                             # decode: queries per request (the last tokens)
+    ring: int = WINDOW                             # decode: window ring slots per request
     notes: str = ""
 
     @property
@@ -183,8 +185,11 @@ def _indexer_queries(g: np.random.Generator, Q: int, HI: int, idx_dt: int):
 
 def make_decode(name: str, ctx_len, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_BF16,
                 idx_dt=DT_FP8, kv_fmt=KV_FP8, win_fmt=None, seed: int = 0,
-                planted_frac: float = 0.0, topk: int = TOPK, ratio: int = COMPRESS) -> Workload:
-    """One query per request at the end of a context of ``ctx_len[b]`` raw tokens.
+                planted_frac: float = 0.0, topk: int = TOPK, ratio: int = COMPRESS,
+                q_per_req: int = 1) -> Workload:
+    """``q_per_req`` queries per request: the last tokens of a context of ``ctx_len[b]`` raw tokens
+    (query b*q_per_req + j sits at position ctx_len[b] - q_per_req + j).  The window ring holds
+    128 + q_per_req - 1 slots, so the earliest query's window is still in it.
 
     Sub-streams, spawned in this order: page permutation, q, sink, indexer q, w, indexer key pool,
     KV pool, window ring, planted entries.
@@ -192,15 +197,20 @@ def make_decode(name: str, ctx_len, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_
     win_fmt = kv_fmt if win_fmt is None else win_fmt
     ctx_len = np.asarray(ctx_len, dtype=np.int32)
     B = int(ctx_len.shape[0])
+    S = int(q_per_req)
+    Q = B * S
+    ring = WINDOW + S - 1
     n_c = [int(t) // ratio for t in ctx_len]
+    # visible entries of each query: every entry whose tokens are all at or before its position
+    n_vis = [max(int(ctx_len[q // S]) - (S - 1 - q % S), 0) // ratio for q in range(Q)]
     ss = np.random.SeedSequence(seed).spawn(9)
     g = [np.random.Generator(np.random.PCG64(s)) for s in ss]
 
     page_table, total_pages = _page_table(g[0], n_c)
-    q_f = g[1].standard_normal((B, H, 512), dtype=np.float32)
+    q_f = g[1].standard_normal((Q, H, 512), dtype=np.float32)
     sink = g[2].standard_normal(H, dtype=np.float32)
-    qI_f, qI, qI_s = _indexer_queries(g[3], B, HI, idx_dt)
-    w = (g[4].standard_normal((B, HI), dtype=np.float32) * np.float32(DI ** -0.5 * HI ** -0.5)).astype(np.float32)
+    qI_f, qI, qI_s = _indexer_queries(g[3], Q, HI, idx_dt)
+    w = (g[4].standard_normal((Q, HI), dtype=np.float32) * np.float32(DI ** -0.5 * HI ** -0.5)).astype(np.float32)
 
     planted = []
     key_override = None
@@ -214,8 +224,9 @@ def make_decode(name: str, ctx_len, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_
             # planted indexer key = alpha * u_b + 0.25 * N(0, I), where u_b is the unit vector whose
             # dot product with each head's indexer query has the sign of that head's weight.
             for b in range(B):
-                Qb = qI_f[b].astype(np.float64)                     # [HI,128]
-                s = np.sign(w[b]).astype(np.float64)
+                qb = b * S + S - 1                                   # the request's last query
+                Qb = qI_f[qb].astype(np.float64)                    # [HI,128]
+                s = np.sign(w[qb]).astype(np.float64)
                 s[s == 0] = 1.0
                 u = Qb.T @ np.linalg.solve(Qb @ Qb.T, s)
                 u /= np.linalg.norm(u)
@@ -236,20 +247,21 @@ def make_decode(name: str, ctx_len, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_
     if planted_frac > 0:
         for b in range(B):
             n = planted[b]
-            d = q_f[b].astype(np.float64).sum(axis=0)
+            d = q_f[b * S + S - 1].astype(np.float64).sum(axis=0)
             d /= np.linalg.norm(d)
             x = (2.0 * math.sqrt(512) * d[None, :] + g[8].standard_normal((n.size, 512))).astype(np.float32)
             rows = page_table[b, n // PAGE].astype(np.int64) * PAGE + (n % PAGE)
             kv_pool[rows] = codec.pack_kv_rows(x, kv_fmt)
     kv_pool = kv_pool.reshape(total_pages, PAGE, -1)
-    win = _kv_rows(ss[7], B * WINDOW, win_fmt).reshape(B, WINDOW, -1)
+    win = _kv_rows(ss[7], B * ring, win_fmt).reshape(B, ring, -1)
 
     return Workload(
-        name=name, kind="decode", B=B, Q=B, H=H, HI=HI, q_dt=q_dt, out_dt=out_dt, idx_dt=idx_dt,
+        name=name, kind="decode", B=B, Q=Q, H=H, HI=HI, q_dt=q_dt, out_dt=out_dt, idx_dt=idx_dt,
         kv_fmt=kv_fmt, win_fmt=win_fmt, q=_encode_q(q_f, q_dt), sink=sink, qI=qI, qI_scale=qI_s,
         w=w, ik_keys=ik_keys, ik_scales=ik_scales, kv_pool=kv_pool, win_rows=win,
-        page_table=page_table, q_req=np.arange(B, dtype=np.int32),
-        n_vis=np.asarray(n_c, dtype=np.int32), ctx_len=ctx_len, topk=topk, planted=planted, ratio=ratio)
+        page_table=page_table, q_req=(np.arange(Q) // S).astype(np.int32),
+        n_vis=np.asarray(n_vis, dtype=np.int32), ctx_len=ctx_len, topk=topk, planted=planted, ratio=ratio,
+        q_per_req=S, ring=ring)
 
 
 def make_prefill(name: str, T: int, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_BF16,
