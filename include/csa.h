@@ -186,6 +186,30 @@ csa_status csa_decode(int32_t B, int32_t H, int32_t HI, int32_t k,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * csa_decode_multi - a decode step that takes the last S tokens of each of B requests at once
+ * (multi-token prediction / speculative decoding: [P1] section 2.17 MTPBlock, [P2]'s NextN
+ * variant), through the same path as csa_decode.  Query b*S + j sits at position T_b - S + j and
+ * sees what a one-query decode with context T_b - (S - 1 - j) would: n_vis = (T_b - S + j + 1) / 4
+ * compressed entries and the 128 raw tokens up to its position.
+ *
+ *   q, qI, qI_scale, w, out   B*S query rows, request-major (row b*S + j)
+ *   win_ring   [B][ring_slots][row bytes of win_fmt]: raw token p of request b in slot p % ring_slots;
+ *              ring_slots >= 128 + S - 1 keeps the earliest query's window in the ring
+ *   idx_out    optional [B*S][128 + k] int32
+ *   Other arguments as in csa_decode; S = 1 with ring_slots = 128 is exactly csa_decode.
+ * Ranges: 1 <= S <= 16, B*S <= 65535, 128 + S - 1 <= ring_slots <= 2^20, others as csa_decode.
+ * ------------------------------------------------------------------------------------------- */
+size_t csa_decode_multi_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t HI, int64_t max_ctx, int32_t k);
+csa_status csa_decode_multi(int32_t B, int32_t S, int32_t H, int32_t HI, int32_t k,
+                            const void* q, int32_t q_dt, const float* sink,
+                            const void* qI, const uint8_t* qI_scale, int32_t qI_dt, const float* w,
+                            const csa_paged_idx* keys, const csa_paged_kv* comp,
+                            const void* win_ring, int32_t win_fmt, int32_t ring_slots,
+                            const int32_t* ctx_len, int64_t max_ctx,
+                            float softmax_scale, void* out, int32_t out_dt, int32_t* idx_out,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * csa_prefill - causal prefill of one request: Q queries at raw positions pos0 .. pos0+Q-1.
  * Query t sees compressed entries c < (t+1)/4 and raw rows [t-127, t] of raw_rows ([P1] section
  * 2.8, causal window at prefill; section 2.10 causal mask).  Page tables have one row.

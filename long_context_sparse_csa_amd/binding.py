@@ -46,6 +46,10 @@ _SIGS = {
     "csa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I64, _I32]),
     "csa_decode": (_I32, [_I32, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _I32, _P, ctypes.POINTER(PagedIdx),
                           ctypes.POINTER(PagedKV), _P, _I32, _P, _I64, _F32, _P, _I32, _P, _P, _SZ, _P]),
+    "csa_decode_multi_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I64, _I32]),
+    "csa_decode_multi": (_I32, [_I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _I32, _P,
+                                ctypes.POINTER(PagedIdx), ctypes.POINTER(PagedKV), _P, _I32, _I32, _P, _I64, _F32,
+                                _P, _I32, _P, _P, _SZ, _P]),
     "csa_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I64, _I32]),
     "csa_prefill": (_I32, [_I32, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _I32, _P, ctypes.POINTER(PagedIdx),
                            ctypes.POINTER(PagedKV), _P, _I32, _I64, _I64, _F32, _P, _I32, _P, _P, _SZ, _P]),
@@ -156,6 +160,19 @@ def csa_decode(B, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys: PagedId
         B, H, HI, k, _ptr(q), q_dt, _ptr(sink), _ptr(qI), _ptr(qI_scale), qI_dt, _ptr(w), ctypes.byref(keys),
         ctypes.byref(comp), _ptr(win_ring), win_fmt, _ptr(ctx_len), max_ctx, softmax_scale, _ptr(out), out_dt,
         _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def csa_decode_multi_workspace_bytes(B, S, H, HI, max_ctx, k) -> int:
+    return int(lib().csa_decode_multi_workspace_bytes(B, S, H, HI, max_ctx, k))
+
+
+def csa_decode_multi(B, S, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys: PagedIdx, comp: PagedKV, win_ring,
+                     win_fmt, ring_slots, ctx_len, max_ctx, softmax_scale, out, out_dt, idx_out, ws, ws_bytes,
+                     stream=None):
+    _check("csa_decode_multi", lib().csa_decode_multi(
+        B, S, H, HI, k, _ptr(q), q_dt, _ptr(sink), _ptr(qI), _ptr(qI_scale), qI_dt, _ptr(w), ctypes.byref(keys),
+        ctypes.byref(comp), _ptr(win_ring), win_fmt, ring_slots, _ptr(ctx_len), max_ctx, softmax_scale, _ptr(out),
+        out_dt, _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def csa_prefill_workspace_bytes(Q, H, HI, T, k) -> int:

@@ -27,6 +27,7 @@ constexpr int kWin = 128;
 constexpr int kHistBins = 4096;
 constexpr int64_t kMaxEntries = (int64_t)1 << 30;
 constexpr int32_t kMaxSlotsPerQuery = 16384;   // attention index-list length (window + compressed)
+constexpr int32_t kMaxQueriesPerReq = 16;      // multi-query decode: tokens decoded together
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -324,7 +325,7 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
                            const void* win, int32_t win_fmt, int64_t win_rows_per_req, const int32_t* ctx_len,
                            int64_t max_ctx, int64_t pos0, int64_t max_n_vis, float softmax_scale, void* out,
                            int32_t out_dt, int32_t* idx_out, void* ws, size_t ws_bytes, size_t need,
-                           hipStream_t stream) {
+                           hipStream_t stream, int32_t S = 1, int32_t ring = kWin) {
   if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return CSA_ERR_ALIGN;
   if (idx_out && !aligned(idx_out, 4)) return CSA_ERR_ALIGN;
@@ -342,7 +343,7 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
     p.zero_words = (int64_t)((uint8_t*)pw.tk.sel - (uint8_t*)pw.tk.hist) / 4;
     p.mode = mode; p.rows = rows; p.ctx_len = ctx_len; p.max_ctx = max_ctx; p.pos0 = pos0;
     p.idx = idx; p.ld_idx = ld_idx; p.n_vis_out = pw.n_vis; p.q_req_out = pw.q_req;
-    p.ratio = 4;
+    p.ratio = 4; p.q_per_req = S; p.ring = ring;
     CSA_HIP(csa::launch_prep(p, stream));
   }
 
@@ -350,9 +351,9 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   ia.qI = qI; ia.qI_scale = qI_scale; ia.dt = qI_dt; ia.w = w;
   ia.keys = keys->keys; ia.kscale = keys->scales; ia.num_pages = keys->num_pages;
   ia.page_table = keys->page_table; ia.max_pages = keys->max_pages;
-  ia.q_req = pw.q_req; ia.n_req = mode == 1 ? rows : 1; ia.n_vis = pw.n_vis; ia.Q = rows; ia.HI = HI;
+  ia.q_req = pw.q_req; ia.n_req = mode == 1 ? rows / S : 1; ia.n_vis = pw.n_vis; ia.Q = rows; ia.HI = HI;
   ia.max_n_vis = max_n_vis; ia.logits = pw.logits; ia.ld = pw.ld; ia.hist = single ? nullptr : pw.tk.hist;
-  ia.vis_mode = single ? mode : 0; ia.ctx_len = ctx_len; ia.max_ctx = max_ctx; ia.pos0 = pos0;
+  ia.vis_mode = single ? mode : 0; ia.ctx_len = ctx_len; ia.max_ctx = max_ctx; ia.pos0 = pos0; ia.q_per_req = S;
   CSA_HIP(csa::launch_indexer(ia, stream));
 
   csa::TopkArgs t{};
@@ -360,6 +361,7 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   t.idx = idx + kWin; t.ld_idx = ld_idx; t.hist = pw.tk.hist; t.counters = pw.tk.counters; t.sel = pw.tk.sel;
   t.cand = pw.tk.cand; t.cand_cap = max_n_vis > 0 ? max_n_vis : 1;
   t.win_mode = single ? mode : 0; t.ctx_len = ctx_len; t.max_ctx = max_ctx; t.pos0 = pos0;
+  t.q_per_req = S; t.ring = ring;
   if (single) {
     // the selection also resolves its rows through the page table, which it loads while the
     // scores load, so the attention prologue saves one dependent round trip
@@ -373,11 +375,12 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   a.win = (const uint8_t*)win; a.win_fmt = win_fmt; a.win_rows_per_req = win_rows_per_req;
   a.comp = (const uint8_t*)comp->rows; a.comp_fmt = comp->fmt; a.comp_num_pages = comp->num_pages;
   a.page_table = comp->page_table; a.max_pages = comp->max_pages;
-  a.q_req = pw.q_req; a.n_req = mode == 1 ? rows : 1; a.idx = idx; a.ld_idx = ld_idx; a.n_win = kWin; a.n_comp = k;
+  a.q_req = pw.q_req; a.n_req = mode == 1 ? rows / S : 1; a.idx = idx; a.ld_idx = ld_idx; a.n_win = kWin; a.n_comp = k;
   a.softmax_scale = softmax_scale; a.out = out; a.out_dt = out_dt;
   a.n_split = csa::attn_uses_matrix_cores(q_dt, win_fmt, comp->fmt, kWin, k) ? csa::plan_attn_split(rows, H, kWin + k, q_dt) : 1;
   a.part = pw.part;
   a.req_mode = mode;
+  a.q_per_req = S;
   if (single) { a.rows = pw.rows; a.ld_rows = k; }
   return hip_status(csa::launch_attention(a, stream));
 }
@@ -419,6 +422,33 @@ csa_status csa_decode(int32_t B, int32_t H, int32_t HI, int32_t k, const void* q
   const size_t need = csa_decode_workspace_bytes(B, H, HI, max_ctx, k);
   return run_path(1, B, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys, comp, win_ring, win_fmt, kWin,
                   ctx_len, max_ctx, 0, max_n_vis, softmax_scale, out, out_dt, idx_out, ws, ws_bytes, need, stream);
+}
+
+size_t csa_decode_multi_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t HI, int64_t max_ctx, int32_t k) {
+  if (B < 1 || S < 1 || S > kMaxQueriesPerReq || H < 1 || HI < 1 || k < 1 || max_ctx < 0) return 0;
+  Carver c(nullptr);
+  carve_path(c, B * S, H, max_ctx / 4, k);
+  return c.off;
+}
+
+csa_status csa_decode_multi(int32_t B, int32_t S, int32_t H, int32_t HI, int32_t k, const void* q, int32_t q_dt,
+                            const float* sink, const void* qI, const uint8_t* qI_scale, int32_t qI_dt, const float* w,
+                            const csa_paged_idx* keys, const csa_paged_kv* comp, const void* win_ring,
+                            int32_t win_fmt, int32_t ring_slots, const int32_t* ctx_len, int64_t max_ctx,
+                            float softmax_scale, void* out, int32_t out_dt, int32_t* idx_out, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  if (S < 1 || S > kMaxQueriesPerReq || B < 1 || (int64_t)B * S > 65535) return CSA_ERR_SHAPE;
+  CSA_TRY(check_path(B * S, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys, comp, win_ring, win_fmt,
+                     softmax_scale, out, out_dt));
+  if (!ctx_len) return CSA_ERR_NULL;
+  if (!aligned(ctx_len, 4)) return CSA_ERR_ALIGN;
+  if (max_ctx < 0 || max_ctx > INT32_MAX) return CSA_ERR_SHAPE;
+  if (ring_slots < kWin + S - 1 || ring_slots > (1 << 20)) return CSA_ERR_SHAPE;
+  const int64_t max_n_vis = std::min<int64_t>(max_ctx / 4, (int64_t)keys->max_pages * 64);
+  const size_t need = csa_decode_multi_workspace_bytes(B, S, H, HI, max_ctx, k);
+  return run_path(1, B * S, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys, comp, win_ring, win_fmt,
+                  ring_slots, ctx_len, max_ctx, 0, max_n_vis, softmax_scale, out, out_dt, idx_out, ws, ws_bytes, need,
+                  stream, S, ring_slots);
 }
 
 size_t csa_prefill_workspace_bytes(int32_t Q, int32_t H, int32_t HI, int64_t T, int32_t k) {

@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   const int tps = (n_tiles + a.n_split - 1) / a.n_split;
   const int t_begin = split * tps;
   const int nt = max(0, min(n_tiles, t_begin + tps) - t_begin);   // tiles of this block
-  const int r = a.req_mode == 1 ? q : (a.req_mode == 2 ? 0 : a.q_req[q]);
+  const int r = a.req_mode == 1 ? q / a.q_per_req : (a.req_mode == 2 ? 0 : a.q_req[q]);
   const int s_begin = t_begin * kTile;
 
   // score waves: wave w computes the scores of head groups w and w ^ 1 over dims [256 (w & 1),
@@ -725,7 +725,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs
   const int tps = (n_tiles + a.n_split - 1) / a.n_split;
   const int t_begin = split * tps;
   const int nt = max(0, min(n_tiles, t_begin + tps) - t_begin);
-  const int r = a.req_mode == 1 ? q : (a.req_mode == 2 ? 0 : a.q_req[q]);
+  const int r = a.req_mode == 1 ? q / a.q_per_req : (a.req_mode == 2 ? 0 : a.q_req[q]);
 
   const int kb = wave & 1, dh = wave >> 1;   // consumer roles (waves 0-3)
   // q as the QK B operand: lane (n, g) holds dims 256 dh + 32ks + 8g .. +7 of head h (padded heads
@@ -962,7 +962,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   __shared__ float red[4 * kD];
   __shared__ float s_stat[4];
   const int n_idx = a.n_win + a.n_comp;
-  const int r = a.req_mode == 1 ? q : (a.req_mode == 2 ? 0 : a.q_req[q]);
+  const int r = a.req_mode == 1 ? q / a.q_per_req : (a.req_mode == 2 ? 0 : a.q_req[q]);
   float qv[8];
   if constexpr (QBF16) {
     const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)q * a.H + h) * kD;

@@ -99,6 +99,17 @@ __device__ __forceinline__ float row_group_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Decode with S queries per request: query q is token j = q % S of request r = q / S, one of the
+// last S tokens of that request's T = ctx_len[r] (clamped to [0, max_ctx]); it sits at position
+// T - S + j and sees the T - (S - 1 - j) tokens up to it (0 if that is negative).
+__device__ __forceinline__ int64_t decode_seen(const int32_t* ctx_len, int64_t max_ctx, int S, int q, int& r) {
+  r = q / S;
+  int64_t T = ctx_len[r];
+  T = T < 0 ? 0 : (T > max_ctx ? max_ctx : T);
+  T -= S - 1 - (q - r * S);
+  return T < 0 ? 0 : T;
+}
+
 template <int I, int N>
 struct static_for {
   template <class F>

@@ -37,6 +37,7 @@ struct IndexerArgs {
   const int32_t* ctx_len;
   int64_t max_ctx;
   int64_t pos0;
+  int q_per_req = 1;          // decode: queries per request (query q belongs to request q / q_per_req)
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
 
@@ -60,6 +61,8 @@ struct TopkArgs {
   const int32_t* ctx_len;
   int64_t max_ctx;
   int64_t pos0;
+  int q_per_req = 1;    // decode: queries per request (the last q_per_req tokens of each request)
+  int ring = 128;       // decode: window ring slots per request (slot = position % ring)
   // single-block path only, optional: also write each selected entry's compressed KV row
   // (page_table[request][idx >> 6] * 64 + (idx & 63), -1 if unmapped) to rows[q * ld_rows + j]
   int32_t* rows;
@@ -87,6 +90,8 @@ struct PrepArgs {
   int32_t* n_vis_out;        // [rows]
   int32_t* q_req_out;        // optional [rows]: request id of each row (decode: row, prefill: 0)
   int ratio;                 // raw tokens per compressed entry: n_vis = T / ratio or (t + 1) / ratio
+  int q_per_req = 1;         // decode: queries per request (row = request * q_per_req + token)
+  int ring = 128;            // decode: window ring slots per request (slot = position % ring)
   int64_t comp_cols;         // > 0: also write compressed columns [128, 128 + comp_cols) as j < n_vis ? j : -1
 };
 hipError_t launch_prep(const PrepArgs& a, hipStream_t s);
@@ -114,7 +119,8 @@ struct AttnArgs {
   int out_dt;                // 0 f32, 1 bf16
   float* part;               // split-K partials (may be null when n_split == 1)
   int n_split;               // chosen by plan_attn_split
-  int req_mode;              // 0: q_req array; 1: request = query (decode); 2: request 0 (prefill)
+  int req_mode;              // 0: q_req array; 1: request = query / q_per_req (decode); 2: request 0 (prefill)
+  int q_per_req = 1;
   // optional: compressed slot j of query q is row rows[q * ld_rows + j] of the pool (< 0 invalid),
   // already resolved through the page table; null = resolve idx through the page table
   const int32_t* rows;

@@ -62,9 +62,7 @@ __device__ __forceinline__ v8i load_k_operand(const uint8_t* row, int g) {
 __device__ __forceinline__ int64_t visible_count(const IndexerArgs& a, int q, int& r) {
   int64_t nv;
   if (a.vis_mode == 1) {
-    r = q;
-    int64_t T = a.ctx_len[q];
-    nv = (T < 0 ? 0 : (T > a.max_ctx ? a.max_ctx : T)) / 4;
+    nv = decode_seen(a.ctx_len, a.max_ctx, a.q_per_req, q, r) / 4;
   } else if (a.vis_mode == 2) {
     r = 0;
     nv = (a.pos0 + q + 1) / 4;

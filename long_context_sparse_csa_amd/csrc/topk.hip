@@ -32,9 +32,8 @@ __device__ __forceinline__ int64_t clamp_nv(const TopkArgs& a, int q) {
 __device__ __forceinline__ int64_t topk_row_count(const TopkArgs& a, int q) {
   int64_t nv;
   if (a.win_mode == 1) {
-    int64_t T = a.ctx_len[q];
-    T = T < 0 ? 0 : (T > a.max_ctx ? a.max_ctx : T);
-    nv = T / 4;
+    int r;
+    nv = decode_seen(a.ctx_len, a.max_ctx, a.q_per_req, q, r) / 4;
   } else if (a.win_mode == 2) {
     nv = (a.pos0 + q + 1) / 4;
   } else {
@@ -43,17 +42,17 @@ __device__ __forceinline__ int64_t topk_row_count(const TopkArgs& a, int q) {
   return nv < 0 ? 0 : (nv > a.max_n_vis ? a.max_n_vis : nv);
 }
 
-// Window part of the index list: decode ring slots of positions T-128..T-1, or prefill positions
-// t-127..t; -1 before position 0.  Written to columns [-128, 0) relative to a.idx.
+// Window part of the index list: decode ring slots (position % ring) of the 128 positions up to
+// the query's, or prefill positions t-127..t; -1 before position 0.  Written to columns [-128, 0)
+// relative to a.idx.
 __device__ __forceinline__ void write_window(const TopkArgs& a, int q) {
   const int j = threadIdx.x;
   if (j >= kWin) return;
   int32_t v;
   if (a.win_mode == 1) {
-    int64_t T = a.ctx_len[q];
-    T = T < 0 ? 0 : (T > a.max_ctx ? a.max_ctx : T);
-    const int64_t p = T - kWin + j;
-    v = p >= 0 ? (int32_t)(p % kWin) : -1;
+    int r;
+    const int64_t p = decode_seen(a.ctx_len, a.max_ctx, a.q_per_req, q, r) - kWin + j;
+    v = p >= 0 ? (int32_t)(p % a.ring) : -1;
   } else {
     const int64_t p = a.pos0 + q - (kWin - 1) + j;
     v = p >= 0 ? (int32_t)p : -1;
@@ -490,7 +489,7 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
   const int k = a.k;
   int32_t* out = a.idx + (int64_t)q * a.ld_idx;
   if (a.win_mode) write_window(a, q);
-  const int r = a.win_mode == 1 ? q : 0;   // request of this query (decode: q; prefill: 0)
+  const int r = a.win_mode == 1 ? q / a.q_per_req : 0;   // request of this query (prefill: 0)
   const int32_t* pt = a.rows ? a.page_table + (int64_t)r * a.max_pages : nullptr;
   auto row_of = [&](int c, int pg) { return (unsigned)pg < (unsigned)a.num_pages ? pg * kPage + (c & (kPage - 1)) : -1; };
   if (nv <= k) {
@@ -713,9 +712,8 @@ hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s) {
 // the row's position (decode: T tokens, the current one included; prefill: position t)
 __device__ __forceinline__ int64_t prep_visible(const PrepArgs& a, int rrow) {
   if (a.mode == 1) {
-    int64_t T = a.ctx_len[rrow];
-    T = T < 0 ? 0 : (T > a.max_ctx ? a.max_ctx : T);
-    return T / a.ratio;
+    int r;
+    return decode_seen(a.ctx_len, a.max_ctx, a.q_per_req, rrow, r) / a.ratio;
   }
   return (a.pos0 + rrow + 1) / a.ratio;
 }
@@ -728,11 +726,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
   for (int64_t i = gid; i < (int64_t)a.rows * kWin; i += stride) {
     const int rrow = (int)(i / kWin), j = (int)(i % kWin);
     int32_t v;
-    if (a.mode == 1) {   // decode: ring slot of position T-128+j
-      int64_t T = a.ctx_len[rrow];
-      T = T < 0 ? 0 : (T > a.max_ctx ? a.max_ctx : T);
-      const int64_t p = T - kWin + j;
-      v = p >= 0 ? (int32_t)(p % kWin) : -1;
+    if (a.mode == 1) {   // decode: ring slot of the j-th of the 128 positions up to the row's
+      int r;
+      const int64_t p = decode_seen(a.ctx_len, a.max_ctx, a.q_per_req, rrow, r) - kWin + j;
+      v = p >= 0 ? (int32_t)(p % a.ring) : -1;
     } else {             // causal prefill: raw position t-127+j
       const int64_t t = a.pos0 + rrow;
       const int64_t p = t - (kWin - 1) + j;
@@ -741,7 +738,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     a.idx[(int64_t)rrow * a.ld_idx + j] = v;
     if (j == 0) {
       a.n_vis_out[rrow] = (int32_t)prep_visible(a, rrow);
-      if (a.q_req_out) a.q_req_out[rrow] = a.mode == 1 ? rrow : 0;
+      if (a.q_req_out) a.q_req_out[rrow] = a.mode == 1 ? rrow / a.q_per_req : 0;
     }
   }
   // dense compressed list: entry j while visible, then -1 (row-major, so stores coalesce)

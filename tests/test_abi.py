@@ -140,6 +140,35 @@ def test_decode_rejects(kw, status):
     assert _decode(**kw) == status
 
 
+def _decode_multi(**kw):
+    a = dict(B=2, S=3, H=64, HI=64, k=512, q=FAKE, q_dt=1, sink=FAKE, qI=FAKE, qs=FAKE, qI_dt=2, w=FAKE, keys=_idx(),
+             comp=_kv(), win=FAKE, win_fmt=2, ring=130, ctx=FAKE, max_ctx=65536, scale=0.044, out=FAKE, out_dt=1,
+             idx_out=None, ws=FAKE, ws_bytes=1 << 40)
+    a.update(kw)
+    return csa.lib().csa_decode_multi(a["B"], a["S"], a["H"], a["HI"], a["k"], a["q"], a["q_dt"], a["sink"], a["qI"],
+                                      a["qs"], a["qI_dt"], a["w"], ctypes.byref(a["keys"]), ctypes.byref(a["comp"]),
+                                      a["win"], a["win_fmt"], a["ring"], a["ctx"], a["max_ctx"], a["scale"], a["out"],
+                                      a["out_dt"], a["idx_out"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(ctx=None), -1), (dict(win=None), -1), (dict(qI_dt=0), -3),
+    (dict(S=0), -2), (dict(S=17), -2), (dict(ring=129), -2), (dict(S=1, ring=127), -2), (dict(B=30000), -2),
+    (dict(max_ctx=-1), -2), (dict(k=0), -2), (dict(ws=None), -5), (dict(ws_bytes=64), -5),
+    (dict(ctx=FAKE + 1), -4),
+])
+def test_decode_multi_rejects(kw, status):
+    assert _decode_multi(**kw) == status
+
+
+def test_decode_multi_workspace_matches_one_query_decode():
+    assert csa.csa_decode_multi_workspace_bytes(32, 1, 64, 64, 65536, 512) == \
+        csa.csa_decode_workspace_bytes(32, 64, 64, 65536, 512)
+    assert csa.csa_decode_multi_workspace_bytes(8, 4, 64, 64, 65536, 512) == \
+        csa.csa_decode_workspace_bytes(32, 64, 64, 65536, 512)
+    assert csa.csa_decode_multi_workspace_bytes(8, 0, 64, 64, 65536, 512) == 0
+
+
 def _prefill(**kw):
     a = dict(Q=16, H=64, HI=64, k=512, q=FAKE, q_dt=1, sink=FAKE, qI=FAKE, qs=FAKE, qI_dt=2, w=FAKE, keys=_idx(),
              comp=_kv(), raw=FAKE, raw_fmt=1, T=256, pos0=0, scale=0.044, out=FAKE, out_dt=1, idx_out=None,

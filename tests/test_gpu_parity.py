@@ -236,6 +236,31 @@ def test_decode_fp4_indexer(dev):
     _check_decode(wl, tio.out_to_numpy(out), idx.cpu().numpy(), BF16_TOL, empty_rows=(0,))
 
 
+@pytest.mark.parametrize("idx_dt", [configs.DT_FP8, configs.DT_FP4])
+def test_decode_multi_query(dev, idx_dt):
+    """Three queries per request (the last three tokens decoded together): contexts shorter than
+    the query count, around the 512-entry selection threshold and past the 128-token window."""
+    run, tio = _run()
+    ctx = [65536, 4099, 2, 2049, 20000, 130]
+    wl = configs.make_decode("multi", ctx, H=64, HI=64, seed=31, q_per_req=3, idx_dt=idx_dt)
+    _say(f"decode multi-query S=3 ctx={ctx} idx_dt={idx_dt}")
+    out, idx = run.decode(wl, tio.to_device(wl, dev))
+    err = _check_decode(wl, tio.out_to_numpy(out), idx.cpu().numpy(), BF16_TOL)
+    _say(f"max err {err:.2e}")
+
+
+def test_decode_multi_query_long_rows(dev):
+    """Two queries per request on rows longer than the one-block selection takes (the histogram /
+    collect / finish path and its preparation launch)."""
+    run, tio = _run()
+    ctx = [262144, 100003]
+    wl = configs.make_decode("multi_long", ctx, H=16, HI=64, seed=32, q_per_req=2)
+    _say(f"decode multi-query S=2 ctx={ctx}")
+    out, idx = run.decode(wl, tio.to_device(wl, dev))
+    err = _check_decode(wl, tio.out_to_numpy(out), idx.cpu().numpy(), BF16_TOL)
+    _say(f"max err {err:.2e}")
+
+
 def test_decode_long_planted_small(dev):
     run, tio = _run()
     wl = configs.make_decode("long_small", [262144, 262144], H=64, HI=64, seed=0, planted_frac=0.01)

@@ -18,23 +18,32 @@ def _comp(wl: Workload, d):
 
 
 def decode_workspace(wl: Workload, device="cuda"):
-    n = csa.csa_decode_workspace_bytes(wl.B, wl.H, wl.HI, int(wl.ctx_len.max()), wl.topk)
+    if wl.q_per_req > 1:
+        n = csa.csa_decode_multi_workspace_bytes(wl.B, wl.q_per_req, wl.H, wl.HI, int(wl.ctx_len.max()), wl.topk)
+    else:
+        n = csa.csa_decode_workspace_bytes(wl.B, wl.H, wl.HI, int(wl.ctx_len.max()), wl.topk)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device), n
 
 
 def decode(wl: Workload, d, out=None, idx=None, ws=None, stream=None):
-    """One csa_decode call; returns (out [B,H,512], idx [B, 128+k])."""
+    """One csa_decode call (csa_decode_multi with several queries per request); returns
+    (out [Q,H,512], idx [Q, 128+k])."""
     dev = d.q.device
     out = empty_out(wl, dev) if out is None else out
-    idx = torch.empty((wl.B, WINDOW + wl.topk), dtype=torch.int32, device=dev) if idx is None else idx
+    idx = torch.empty((wl.Q, WINDOW + wl.topk), dtype=torch.int32, device=dev) if idx is None else idx
     if ws is None:
         ws, nbytes = decode_workspace(wl, dev)
     else:
         ws, nbytes = ws
     keys, comp = _keys(wl, d), _comp(wl, d)
-    csa.csa_decode(wl.B, wl.H, wl.HI, wl.topk, d.q, wl.q_dt, d.sink, d.qI, d.qI_scale, wl.idx_dt, d.w, keys, comp,
-                   d.win_rows, wl.win_fmt, d.ctx_len, int(wl.ctx_len.max()), wl.softmax_scale, out, wl.out_dt, idx,
-                   ws, nbytes, stream)
+    if wl.q_per_req > 1:
+        csa.csa_decode_multi(wl.B, wl.q_per_req, wl.H, wl.HI, wl.topk, d.q, wl.q_dt, d.sink, d.qI, d.qI_scale,
+                             wl.idx_dt, d.w, keys, comp, d.win_rows, wl.win_fmt, wl.ring, d.ctx_len,
+                             int(wl.ctx_len.max()), wl.softmax_scale, out, wl.out_dt, idx, ws, nbytes, stream)
+    else:
+        csa.csa_decode(wl.B, wl.H, wl.HI, wl.topk, d.q, wl.q_dt, d.sink, d.qI, d.qI_scale, wl.idx_dt, d.w, keys,
+                       comp, d.win_rows, wl.win_fmt, d.ctx_len, int(wl.ctx_len.max()), wl.softmax_scale, out,
+                       wl.out_dt, idx, ws, nbytes, stream)
     return out, idx
 
 
