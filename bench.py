@@ -42,6 +42,8 @@ def parse():
                    help="dense: a layer without an indexer (window ++ all 8,192 compressed entries at 1M tokens)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--queries-per-request", type=int, default=1, metavar="S",
+                   help="batched/long decode: decode the last S tokens of each request together")
     p.add_argument("--indexer", default="fp8", choices=["fp8", "fp4"],
                    help="indexer q/k format: FP8 E4M3FN or MXFP4 E2M1, both with E8M0 scales per 32")
     p.add_argument("--copies", type=int, default=0, help="input copies to rotate (0 = enough to exceed 1 GB)")
@@ -51,33 +53,45 @@ def parse():
     return p.parse_args()
 
 
-def make_workload(name, indexer):
+def make_workload(name, indexer, S=1):
     from workloads import configs
     if name == "tiny":
         return configs.tiny_decode()
     if name == "dense":
         return configs.dense_decode()
     idx_dt = configs.DT_FP4 if indexer == "fp4" else configs.DT_FP8
+    if S > 1:
+        return {"batched": configs.batched_decode, "long": configs.long_decode}[name](idx_dt=idx_dt, q_per_req=S)
     return {"batched": configs.batched_decode, "long": configs.long_decode, "ragged": configs.ragged_decode,
             "prefill": configs.causal_prefill}[name](idx_dt=idx_dt)
 
 
 def algorithmic_bytes(wl, idx_np):
     """Bytes the method must move once per step (indexer keys of every visible entry, page table,
-    q, qI, w, sink, every valid gathered row, output) and the indexer kernel's share of them."""
-    Q, H, HI = wl.Q, wl.H, wl.HI
+    q, qI, w, sink, every valid gathered row, output) and the indexer kernel's share of them.  With
+    several queries per request, a request's keys, page-table row and gathered rows count once for
+    all of its queries (the largest visible prefix; the union of the selected rows)."""
+    Q, H, HI, S = wl.Q, wl.H, wl.HI, wl.q_per_req
     n_vis = wl.n_vis.astype("int64")
-    pages = (n_vis + 63) // 64
+    req_vis = n_vis.reshape(-1, S).max(axis=1) if wl.kind == "decode" else n_vis
+    pages = (req_vis + 63) // 64
     q_bytes = Q * H * 512 * (4 if wl.q_dt == 0 else 2)
     qi_bytes = Q * HI * IDX_BYTES[wl.idx_dt]
     w_bytes = Q * HI * 4
-    key_bytes = int(n_vis.sum()) * IDX_BYTES[wl.idx_dt]
+    key_bytes = int(req_vis.sum()) * IDX_BYTES[wl.idx_dt]
     pt_bytes = int(pages.sum()) * 4
     indexer = key_bytes + pt_bytes + qi_bytes + w_bytes
     if idx_np is None:   # dense compressed lists: every visible entry plus the window
         T = wl.ctx_len.astype("int64")
         valid_rows = int((T.clip(0, 128) + n_vis).sum())
         indexer = 0
+    elif S > 1:
+        import numpy as np
+        valid_rows = 0
+        for b in range(Q // S):
+            rows = idx_np[b * S:(b + 1) * S]
+            valid_rows += np.unique(rows[:, :128][rows[:, :128] >= 0]).size
+            valid_rows += np.unique(rows[:, 128:][rows[:, 128:] >= 0]).size
     else:
         valid_rows = 0
         for qi in range(Q):
@@ -177,7 +191,7 @@ def main():
     csa.lib()
     dev = "cuda"
     t_gen = time.perf_counter()
-    wl = make_workload(args.config, args.indexer)
+    wl = make_workload(args.config, args.indexer, args.queries_per_request)
     gen_s = time.perf_counter() - t_gen
     base = torch_io.to_device(wl, dev)
     decode = wl.kind == "decode"
@@ -239,7 +253,9 @@ def main():
     dominant = "attn_bf16" if dense else f"indexer_{IDX_NAME[wl.idx_dt]}"
     dom = dominant if dominant in kernels else max(kernels, key=kernels.get)
     dom_us = kernels[dom]
-    if dom.startswith("indexer"):
+    if dom.startswith("indexer") and wl.q_per_req == 1:
+        # back-to-back launches of the same kernel through csa_indexer_logits (with several queries
+        # per request only the fused step shares key pages, so its event-pair time is used instead)
         dom_us = indexer_launch_us(wl, copies, stream, args.steps)
     # without an indexer the attention moves every byte of the step but q/out's share of the sink
     dom_bytes = total_bytes if dense else idx_bytes
@@ -261,7 +277,8 @@ def main():
         "dtype": {0: "fp32 indexer and attention", 2: "fp8-e4m3fn indexer, bf16 matrix-core attention, fp32 accumulate",
                   3: "mxfp4-e2m1 indexer, bf16 matrix-core attention, fp32 accumulate"}[wl.idx_dt],
         "data": "synthetic (seeded N(0,1) q/kv/indexer, quantised as the workload states)",
-        "config": {"workload": wl.name, "B": wl.B, "Q": wl.Q, "H": wl.H, "HI": wl.HI,
+        "config": {"workload": wl.name, "B": wl.B, "Q": wl.Q, "queries_per_request": wl.q_per_req, "H": wl.H,
+                   "HI": wl.HI,
                    "context": int(wl.ctx_len.max()) if decode else int(wl.win_rows.shape[1]),
                    "compressed_entries": int(wl.max_n_vis), "topk": wl.topk, "window": wl.window,
                    "kv_format": {0: "f32", 1: "bf16", 2: "fp8nope_bf16rope"}[wl.kv_fmt],

@@ -162,37 +162,50 @@ template <bool FP4>
 constexpr int kPagesPerWave = FP4 ? 8 : 8;
 template <bool FP4>
 constexpr int kPageBufs = FP4 ? 3 : 3;
+constexpr int kMaxSharedQueries = 4;   // multi-query decode: queries scored per key page
 
-template <int NHG, bool HIST, bool FP4>
+// NQ > 1 (multi-query decode): the block scores the NQ queries of one request, the last NQ tokens
+// of its context, so each key page is read from HBM once for all of them instead of once per
+// query.  Page buffers drop to two to make room for the extra query operands.
+template <bool FP4, int NQ>
+constexpr int kDecodeBufs = NQ > 1 ? 2 : kPageBufs<FP4>;
+
+template <int NHG, bool HIST, bool FP4, int NQ>
 __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   constexpr int pages_per_wave = kPagesPerWave<FP4>;
-  constexpr int nbuf = kPageBufs<FP4> < pages_per_wave ? kPageBufs<FP4> : pages_per_wave;
-  const int q = blockIdx.x;   // queries vary fastest: a row's blocks share one XCD (and its L2)
+  constexpr int nbuf = kDecodeBufs<FP4, NQ> < pages_per_wave ? kDecodeBufs<FP4, NQ> : pages_per_wave;
+  const int q0 = blockIdx.x * NQ;   // queries vary fastest: a row's blocks share one XCD (and its L2)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  __shared__ uint32_t lhist[HIST ? kHistBins : 1];
+  __shared__ uint32_t lhist[HIST ? NQ : 1][HIST ? kHistBins : 1];
 
   const int64_t c_begin = (int64_t)blockIdx.y * 4 * pages_per_wave * kPage;
   if (c_begin >= a.max_n_vis) return;
   int r;
-  const int64_t nv = visible_count(a, q, r);
+  int64_t nv[NQ];
+  int64_t nv_max = 0;
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) {
+    nv[j] = visible_count(a, q0 + j, r);   // one request: every j gives the same r
+    nv_max = nv[j] > nv_max ? nv[j] : nv_max;
+  }
   if constexpr (HIST) {
-    for (int i = tid; i < kHistBins; i += 256) lhist[i] = 0u;
+    for (int i = tid; i < NQ * kHistBins; i += 256) lhist[i / kHistBins][i % kHistBins] = 0u;
   }
 
-  // A operand: the query's indexer heads, resident in VGPRs.  Loads are unconditional (clamped
+  // A operands: the queries' indexer heads, resident in VGPRs.  Loads are unconditional (clamped
   // addresses, padded heads zeroed by select) so nothing waits before the first key page.
-  v8i qa[NHG];
-  int qsc;
-  float wv[NHG][4];
-  load_query<NHG, FP4>(a, q, n, g, qa, qsc, wv);
+  v8i qa[NQ][NHG];
+  int qsc[NQ];
+  float wv[NQ][NHG][4];
+#pragma unroll
+  for (int j = 0; j < NQ; ++j) load_query<NHG, FP4>(a, q0 + j, n, g, qa[j], qsc[j], wv[j]);
 
   const uint8_t* keys = (const uint8_t*)a.keys;
   const int32_t* pt = a.page_table + (int64_t)(r < 0 ? 0 : r) * a.max_pages;
-  float* lrow = a.logits + (int64_t)q * a.ld;
   const int64_t p_first = (c_begin >> 6) + (int64_t)wave * pages_per_wave;   // this wave's first page
-  const int64_t vis_pages = (nv + kPage - 1) / kPage;
+  const int64_t vis_pages = (nv_max + kPage - 1) / kPage;
 
   // page ids of this wave's pages, one per lane, then read into scalars as needed
   int my_pid = -1;
@@ -217,14 +230,17 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
 
   auto compute_page = [&](int i, const v8i* kb, int ksc) {
     const int64_t c0 = (p_first + i) * kPage;
-    const bool live = c0 < nv && page_ok(i);
-    const float score = score_page<NHG, FP4>(qa, qsc, wv, kb, ksc);
+    const bool mapped = page_ok(i);
     const int64_t c = c0 + 4 * n + g;
-    if (c < a.max_n_vis) {
-      const float v = (live && c < nv) ? score : -INFINITY;
-      lrow[c] = v;
-      if constexpr (HIST) {
-        if (c < nv) atomicAdd(&lhist[order_key(v) >> kHistShift], 1u);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      const float score = score_page<NHG, FP4>(qa[j], qsc[j], wv[j], kb, ksc);
+      if (c < a.max_n_vis) {
+        const float v = (mapped && c0 < nv[j] && c < nv[j]) ? score : -INFINITY;
+        a.logits[(int64_t)(q0 + j) * a.ld + c] = v;
+        if constexpr (HIST) {
+          if (c < nv[j]) atomicAdd(&lhist[j][order_key(v) >> kHistShift], 1u);
+        }
       }
     }
   };
@@ -244,10 +260,13 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   }
   if constexpr (HIST) {
     __syncthreads();
-    uint32_t* gh = a.hist + (int64_t)q * kHistBins;
-    for (int i = tid; i < kHistBins; i += 256) {
-      const uint32_t v = lhist[i];
-      if (v) atomicAdd(&gh[i], v);
+#pragma unroll
+    for (int j = 0; j < NQ; ++j) {
+      uint32_t* gh = a.hist + (int64_t)(q0 + j) * kHistBins;
+      for (int i = tid; i < kHistBins; i += 256) {
+        const uint32_t v = lhist[j][i];
+        if (v) atomicAdd(&gh[i], v);
+      }
     }
   }
 }
@@ -445,15 +464,24 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
 #undef CSA_PF_LAUNCH
     return hipGetLastError();
   }
-  // kPagesPerWave pages per wave, four waves per block
+  // kPagesPerWave pages per wave, four waves per block; a multi-query decode (2 to 4 queries per
+  // request, derived visibility) gives each block all queries of one request
+  const int nq = (a.vis_mode == 1 && a.q_per_req >= 2 && a.q_per_req <= kMaxSharedQueries) ? a.q_per_req : 1;
   const int per_block = 4 * (fp4 ? kPagesPerWave<true> : kPagesPerWave<false>) * kPage;
-  dim3 grid((unsigned)a.Q, (unsigned)((a.max_n_vis + per_block - 1) / per_block));
+  dim3 grid((unsigned)(a.Q / nq), (unsigned)((a.max_n_vis + per_block - 1) / per_block));
   ProfScope p(fp4 ? "indexer_fp4" : "indexer_fp8", s);
-#define CSA_IDX_LAUNCH(N, F)                                                                        \
-  if (hist) hipLaunchKernelGGL((indexer_fp8_kernel<N, true, F>), grid, dim3(256), 0, s, a); \
-  else hipLaunchKernelGGL((indexer_fp8_kernel<N, false, F>), grid, dim3(256), 0, s, a);
+#define CSA_IDX_LAUNCH(N, F, NQ)                                                                    \
+  if (hist) hipLaunchKernelGGL((indexer_fp8_kernel<N, true, F, NQ>), grid, dim3(256), 0, s, a); \
+  else hipLaunchKernelGGL((indexer_fp8_kernel<N, false, F, NQ>), grid, dim3(256), 0, s, a);
+#define CSA_IDX_NQ(N, F)                          \
+  switch (nq) {                                   \
+    case 2: CSA_IDX_LAUNCH(N, F, 2) break;        \
+    case 3: CSA_IDX_LAUNCH(N, F, 3) break;        \
+    case 4: CSA_IDX_LAUNCH(N, F, 4) break;        \
+    default: CSA_IDX_LAUNCH(N, F, 1) break;       \
+  }
 #define CSA_IDX_FMT(N) \
-  if (fp4) { CSA_IDX_LAUNCH(N, true) } else { CSA_IDX_LAUNCH(N, false) }
+  if (fp4) { CSA_IDX_NQ(N, true) } else { CSA_IDX_NQ(N, false) }
   switch (nhg) {
     case 1: CSA_IDX_FMT(1) break;
     case 2: CSA_IDX_FMT(2) break;
@@ -461,6 +489,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
     default: CSA_IDX_FMT(4) break;
   }
 #undef CSA_IDX_FMT
+#undef CSA_IDX_NQ
 #undef CSA_IDX_LAUNCH
   return hipGetLastError();
 }

@@ -310,17 +310,18 @@ def tiny_decode(seed: int = 0) -> Workload:
 
 
 def batched_decode(seed: int = 0, B: int = 32, T: int = 65536, H: int = 64, HI: int = 64,
-                   idx_dt: int = DT_FP8) -> Workload:
+                   idx_dt: int = DT_FP8, q_per_req: int = 1) -> Workload:
     """B=32 requests at T=65536 (16384 compressed entries in 256 pages of 64), FP8-nope/BF16-rope
     KV with per-64 fp32 scales, FP8 (or FP4) indexer with E8M0 per-32 scales, bf16 q, H=HI=64."""
-    return make_decode("batched_decode", [T] * B, H=H, HI=HI, seed=seed, idx_dt=idx_dt)
+    return make_decode("batched_decode", [T] * B, H=H, HI=HI, seed=seed, idx_dt=idx_dt, q_per_req=q_per_req)
 
 
 def long_decode(seed: int = 0, B: int = 8, T: int = 1 << 20, H: int = 64, HI: int = 64,
-                idx_dt: int = DT_FP8) -> Workload:
+                idx_dt: int = DT_FP8, q_per_req: int = 1) -> Workload:
     """B=8 requests at T=1,048,576 (262,144 compressed entries), formats as batched_decode, with 1%
     planted high-similarity entries per request."""
-    return make_decode("long_decode", [T] * B, H=H, HI=HI, seed=seed, planted_frac=0.01, idx_dt=idx_dt)
+    return make_decode("long_decode", [T] * B, H=H, HI=HI, seed=seed, planted_frac=0.01, idx_dt=idx_dt,
+                       q_per_req=q_per_req)
 
 
 def causal_prefill(seed: int = 0, T: int = 8192, H: int = 64, HI: int = 64, q_start: int = 0,
