@@ -331,3 +331,100 @@ def run_query(wl, qi: int):
     top = topk_select(s, int(wl.n_vis[qi]), wl.topk)
     out = attend(wl, qi, query_window(wl, qi), top)
     return out, top, s
+
+
+# ------------------------------------------------------------------------------------------------
+# Compressor: the step that writes the compressed cache the path reads ([P1] section 2.9; [P2]
+# concept 2).  Token projections (the kv and gate linear maps of the hidden state) are inputs: they
+# are plain matrix products outside the step.  Readings (also in the design notes): with overlap
+# (ratio 4) each token's 2D-wide projection splits into an overlapping half [0, D), lent to the
+# next window, and a normal half [D, 2D); the learned position embedding `ape` [ratio, coff*D] is
+# added to the gate scores per position inside the window before the halves are placed; the first
+# window has no previous window, so its borrowed positions are absent.
+# ------------------------------------------------------------------------------------------------
+
+def compressor_window(kv_tok: np.ndarray, score_tok: np.ndarray, ape: np.ndarray, entry: int, ratio: int,
+                      overlap: bool, D: int):
+    """Positions of compressed entry ``entry``: (kv [P, D], score [P, D]) for its window of ``ratio``
+    tokens ([P1] section 2.9, overlap_transform: the current window's normal half in place, the
+    previous window's overlapping half shifted in front).  ``kv_tok`` / ``score_tok`` are indexed
+    by raw token position ([T, coff*D])."""
+    r = ratio
+    cur = np.arange(entry * r, (entry + 1) * r)
+    s_cur = np.asarray(score_tok[cur], np.float64) + np.asarray(ape, np.float64)
+    if not overlap:
+        return np.asarray(kv_tok[cur], np.float64)[:, :D], s_cur[:, :D]
+    kv = [np.asarray(kv_tok[cur], np.float64)[:, D:2 * D]]
+    sc = [s_cur[:, D:2 * D]]
+    if entry > 0:
+        prev = cur - r
+        kv.insert(0, np.asarray(kv_tok[prev], np.float64)[:, :D])
+        sc.insert(0, (np.asarray(score_tok[prev], np.float64) + np.asarray(ape, np.float64))[:, :D])
+    return np.concatenate(kv), np.concatenate(sc)
+
+
+def gated_pool(kv: np.ndarray, score: np.ndarray) -> np.ndarray:
+    """Softmax of the gate scores over the window positions, per feature, then the weighted sum of
+    the kv rows ([P1] section 2.9 forward step 5)."""
+    s = np.asarray(score, np.float64)
+    e = np.exp(s - s.max(axis=0, keepdims=True))
+    return (e * np.asarray(kv, np.float64)).sum(axis=0) / e.sum(axis=0)
+
+
+def rms_norm(x: np.ndarray, weight: np.ndarray, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * weight ([P1] section 2.9 step 6: RMSNorm)."""
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(weight, np.float64)
+
+
+def rope_pairs(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """Rotary embedding on consecutive pairs (x[2i], x[2i+1]) read as complex numbers and multiplied
+    by cos + i sin ([P1] section 2.6 apply_rotary_emb: the last dimension split into (-1, 2) pairs,
+    complex multiplication by freqs_cis)."""
+    x = np.asarray(x, np.float64)
+    a, b = x[..., 0::2], x[..., 1::2]
+    c, s = np.asarray(cos, np.float64), np.asarray(sin, np.float64)
+    out = np.empty_like(x)
+    out[..., 0::2] = a * c - b * s
+    out[..., 1::2] = a * s + b * c
+    return out
+
+
+def hadamard_rotate(x: np.ndarray) -> np.ndarray:
+    """Walsh-Hadamard transform of the last dimension scaled by n^-1/2 ([P1] section 2.7
+    rotate_activation), by the butterfly definition H_2n = [[H_n, H_n], [H_n, -H_n]]."""
+    y = np.array(x, dtype=np.float64, copy=True)
+    n = y.shape[-1]
+    h = 1
+    while h < n:
+        y = y.reshape(*y.shape[:-1], n // (2 * h), 2, h)
+        a, b = y[..., 0, :].copy(), y[..., 1, :].copy()
+        y[..., 0, :], y[..., 1, :] = a + b, a - b
+        y = y.reshape(*y.shape[:-3], n)
+        h *= 2
+    return y / math.sqrt(n)
+
+
+def compress_entries(kv_tok, score_tok, ape, norm_w, eps, rope_cos, rope_sin, c_begin: int, c_count: int,
+                     ratio: int, rope_dims: int = 64, rotate: bool = False) -> np.ndarray:
+    """Compressed rows of entries c_begin .. c_begin+c_count-1 before quantisation ([P1] section 2.9
+    forward steps 4-7): overlap placement (ratio 4), gated softmax pooling, RMSNorm, RoPE on the
+    last ``rope_dims`` dims with the angles of each entry (rope_cos/rope_sin [c_count, rope_dims/2]),
+    then for ``rotate`` the Hadamard rotation of the whole row (the indexer's key compressor)."""
+    D = int(np.asarray(norm_w).shape[0])
+    overlap = ratio == 4
+    out = np.empty((c_count, D))
+    for i in range(c_count):
+        kv, sc = compressor_window(kv_tok, score_tok, ape, c_begin + i, ratio, overlap, D)
+        y = rms_norm(gated_pool(kv, sc), norm_w, eps)
+        y[D - rope_dims:] = rope_pairs(y[D - rope_dims:], rope_cos[i], rope_sin[i])
+        out[i] = hadamard_rotate(y) if rotate else y
+    return out
+
+
+def compressor_reference(ci, c_begin: int, c_count: int, rotate: bool = False) -> np.ndarray:
+    """compress_entries on a workload's stored projections (bf16 or fp32 rows)."""
+    kv = q_values(ci.kv_tok, ci.proj_dt)
+    sc = q_values(ci.score_tok, ci.proj_dt)
+    return compress_entries(kv, sc, ci.ape, ci.norm_w, ci.eps, ci.rope_cos[c_begin:c_begin + c_count],
+                            ci.rope_sin[c_begin:c_begin + c_count], c_begin, c_count, ci.ratio, rotate=rotate)

@@ -357,3 +357,55 @@ def ragged_decode(seed: int = 0, B: int = 64, H: int = 8, HI: int = 64, hi: int 
     inside the kernels), bf16 q and KV rows, FP8 (or FP4) indexer."""
     T = ragged_lengths(seed, B, hi=hi)
     return make_decode("ragged_decode", T, H=H, HI=HI, kv_fmt=KV_BF16, seed=seed, idx_dt=idx_dt)
+
+
+# ------------------------------------------------------------------------------------------------
+# Compressor inputs: token projections of one request and the compressor's parameters.
+# ------------------------------------------------------------------------------------------------
+COMPRESS_ROPE_THETA = 160000.0   # base frequency of the compressed entries' rotary embedding
+
+
+@dataclass
+class CompressorInputs:
+    name: str
+    T: int                    # raw tokens with projections (positions 0 .. T-1)
+    ratio: int                # 4 (overlapping windows, two halves per token) or 128
+    D: int                    # compressed row width: 512 (KV) or 128 (indexer keys)
+    proj_dt: int              # DT_BF16 or DT_F32 projections
+    kv_tok: np.ndarray        # [T, coff*D] (bf16 bits as uint16, or float32)
+    score_tok: np.ndarray     # [T, coff*D]
+    ape: np.ndarray           # [ratio, coff*D] float32
+    norm_w: np.ndarray        # [D] float32
+    eps: float
+    rope_cos: np.ndarray      # [T // ratio, 32] float32: angles of entry c at position c * ratio
+    rope_sin: np.ndarray
+
+    @property
+    def coff(self) -> int:
+        return 2 if self.ratio == 4 else 1
+
+    @property
+    def n_entries(self) -> int:
+        return self.T // self.ratio
+
+
+def make_compressor(name: str, T: int, ratio: int, D: int = 512, proj_dt: int = DT_BF16,
+                    seed: int = 0) -> CompressorInputs:
+    """Seeded compressor inputs.  Sub-streams in this order: kv projections, gate projections, ape,
+    norm weight.  Projections are N(0,1) (the gate scores also N(0,1), so the window softmax is
+    neither flat nor one-hot); ape ~ N(0, 0.5); norm weight ~ 1 + N(0, 0.1).  The rotary angles of
+    entry c are (c * ratio) * theta^(-2i/64), i < 32, in float32."""
+    coff = 2 if ratio == 4 else 1
+    ss = np.random.SeedSequence(seed).spawn(4)
+    g = [np.random.Generator(np.random.PCG64(s)) for s in ss]
+    kv = g[0].standard_normal((T, coff * D), dtype=np.float32)
+    sc = g[1].standard_normal((T, coff * D), dtype=np.float32)
+    ape = (g[2].standard_normal((ratio, coff * D), dtype=np.float32) * np.float32(0.5)).astype(np.float32)
+    w = (1.0 + 0.1 * g[3].standard_normal(D, dtype=np.float32)).astype(np.float32)
+    n_c = T // ratio
+    freqs = (1.0 / (np.float32(COMPRESS_ROPE_THETA) ** (np.arange(0, 64, 2, dtype=np.float32) / np.float32(64))))
+    ang = np.outer(np.arange(n_c, dtype=np.float32) * np.float32(ratio), freqs.astype(np.float32)).astype(np.float32)
+    enc = codec.bf16_encode if proj_dt == DT_BF16 else (lambda x: x.astype(np.float32))
+    return CompressorInputs(name=name, T=T, ratio=ratio, D=D, proj_dt=proj_dt, kv_tok=enc(kv), score_tok=enc(sc),
+                            ape=ape, norm_w=w, eps=1e-6, rope_cos=np.cos(ang).astype(np.float32),
+                            rope_sin=np.sin(ang).astype(np.float32))
