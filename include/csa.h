@@ -259,6 +259,48 @@ csa_status csa_hca_prefill(int32_t Q, int32_t H, const void* q, int32_t q_dt, co
                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * csa_compress_kv / csa_compress_index_keys - the compressor that fills the caches this path
+ * reads ([P1] section 2.9 Compressor, 2.6 apply_rotary_emb, 2.7 rotate_activation; [P2] concept
+ * 2).  Entries c_begin .. c_begin+c_count-1 of one request are computed and written to page
+ * page_table_row[c >> 6], slot c & 63 (unmapped pages are skipped).
+ *
+ *   kv_proj, score_proj  the token projections of the kv and gate linear maps (computed by the
+ *             caller): row (p - tok0) at ptr + row * ld_proj holds raw token p, coff * D
+ *             elements, proj_dt CSA_BF16 or CSA_F32.  coff = 2 at ratio 4 (each token's
+ *             overlapping half [0, D) serves the next window, its normal half [D, 2D) its own
+ *             window), 1 at ratio 128.  Entry c pools tokens [c*ratio, (c+1)*ratio) and, at ratio 4
+ *             with c > 0, the overlapping halves of tokens [(c-1)*4, c*4); those rows must lie in
+ *             [tok0, tok0 + n_tok).
+ *   ape       [ratio][coff * D] fp32 position embedding added to the gate scores
+ *   norm_w    [D] fp32 RMSNorm weight; eps its epsilon
+ *   rope_cos, rope_sin  [c_count][32] fp32: the rotary angles of each entry (row i: entry
+ *             c_begin + i); pairs (2j, 2j+1) of the last 64 features are rotated by angle j
+ *   Per entry and feature: softmax over the window positions of (score + ape), weighted sum of
+ *   kv; RMSNorm over the D features; rotary embedding.
+ * csa_compress_kv: D = 512; pool_rows [num_pages][64][row bytes] in pool_fmt (csa_kv_format):
+ *   FP8NOPE_BF16ROPE rows quantise the 448 nope features per 64 with scale max(amax,1e-4)/448.
+ * csa_compress_index_keys: D = 128, then the scaled Hadamard rotation of the row, then key_dt
+ *   CSA_FP8_E4M3FN (keys [P][64][128]) or CSA_FP4_E2M1 (keys [P][64][64]) with one E8M0 scale
+ *   per 32 features in scales [P][4][64]: 2^ceil(log2(max(amax,1e-4)/448)) for FP8,
+ *   2^ceil(log2(max(amax,6*2^-126)/6)) for FP4.
+ * Ranges: ratio 4 or 128; ld_proj >= coff * D and even; c_begin + c_count <= 64 * max_pages;
+ *         eps >= 0.  Projections 4-byte (bf16) / 8-byte (fp32) aligned; outputs 16-byte aligned.
+ * ------------------------------------------------------------------------------------------- */
+csa_status csa_compress_kv(const void* kv_proj, const void* score_proj, int32_t proj_dt, int64_t ld_proj,
+                           int64_t tok0, int64_t n_tok, int32_t ratio, const float* ape, const float* norm_w,
+                           float eps, const float* rope_cos, const float* rope_sin,
+                           int64_t c_begin, int32_t c_count, void* pool_rows, int32_t pool_fmt,
+                           int32_t num_pages, const int32_t* page_table_row, int32_t max_pages,
+                           hipStream_t stream);
+csa_status csa_compress_index_keys(const void* kv_proj, const void* score_proj, int32_t proj_dt,
+                                   int64_t ld_proj, int64_t tok0, int64_t n_tok, int32_t ratio,
+                                   const float* ape, const float* norm_w, float eps,
+                                   const float* rope_cos, const float* rope_sin,
+                                   int64_t c_begin, int32_t c_count, void* keys, uint8_t* scales,
+                                   int32_t key_dt, int32_t num_pages, const int32_t* page_table_row,
+                                   int32_t max_pages, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Diagnostics.
  *   csa_status_string   static text of a status code.
  *   csa_last_hip_error  hipError_t of the last CSA_ERR_HIP on the calling thread (0 if none).

@@ -59,6 +59,10 @@ _SIGS = {
     "csa_hca_prefill_workspace_bytes": (_SZ, [_I32, _I32, _I64, _I32]),
     "csa_hca_prefill": (_I32, [_I32, _I32, _P, _I32, _P, ctypes.POINTER(PagedKV), _P, _I32, _I64, _I64, _I32,
                                _F32, _P, _I32, _P, _SZ, _P]),
+    "csa_compress_kv": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P, _F32, _P, _P, _I64, _I32, _P, _I32, _I32,
+                               _P, _I32, _P]),
+    "csa_compress_index_keys": (_I32, [_P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P, _F32, _P, _P, _I64, _I32, _P, _P,
+                                       _I32, _I32, _P, _I32, _P]),
     "csa_status_string": (ctypes.c_char_p, [_I32]),
     "csa_last_hip_error": (_I32, []),
     "csa_profile_enable": (_I32, [_I32]),
@@ -207,6 +211,23 @@ def csa_hca_prefill(Q, H, q, q_dt, sink, comp: PagedKV, raw_rows, raw_fmt, T, po
     _check("csa_hca_prefill", lib().csa_hca_prefill(
         Q, H, _ptr(q), q_dt, _ptr(sink), ctypes.byref(comp), _ptr(raw_rows), raw_fmt, T, pos0, ratio, softmax_scale,
         _ptr(out), out_dt, _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def csa_compress_kv(kv_proj, score_proj, proj_dt, ld_proj, tok0, n_tok, ratio, ape, norm_w, eps, rope_cos, rope_sin,
+                    c_begin, c_count, pool_rows, pool_fmt, num_pages, page_table_row, max_pages, stream=None):
+    _check("csa_compress_kv", lib().csa_compress_kv(
+        _ptr(kv_proj), _ptr(score_proj), proj_dt, ld_proj, tok0, n_tok, ratio, _ptr(ape), _ptr(norm_w), eps,
+        _ptr(rope_cos), _ptr(rope_sin), c_begin, c_count, _ptr(pool_rows), pool_fmt, num_pages, _ptr(page_table_row),
+        max_pages, _stream(stream)))
+
+
+def csa_compress_index_keys(kv_proj, score_proj, proj_dt, ld_proj, tok0, n_tok, ratio, ape, norm_w, eps, rope_cos,
+                            rope_sin, c_begin, c_count, keys, scales, key_dt, num_pages, page_table_row, max_pages,
+                            stream=None):
+    _check("csa_compress_index_keys", lib().csa_compress_index_keys(
+        _ptr(kv_proj), _ptr(score_proj), proj_dt, ld_proj, tok0, n_tok, ratio, _ptr(ape), _ptr(norm_w), eps,
+        _ptr(rope_cos), _ptr(rope_sin), c_begin, c_count, _ptr(keys), _ptr(scales), key_dt, num_pages,
+        _ptr(page_table_row), max_pages, _stream(stream)))
 
 
 def csa_status_string(status: int) -> str:

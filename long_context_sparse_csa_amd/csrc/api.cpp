@@ -546,6 +546,68 @@ int64_t hca_cols(int64_t n_vis_max, const csa_paged_kv* comp) {
 
 extern "C" {
 
+// ---- compressor ([P1] section 2.9): writes compressed entries into the caches
+namespace {
+csa_status compress_common(const void* kv_proj, const void* score_proj, int32_t proj_dt, int64_t ld_proj,
+                           int64_t tok0, int64_t n_tok, int32_t ratio, int32_t D, const float* ape,
+                           const float* norm_w, float eps, const float* rope_cos, const float* rope_sin,
+                           int64_t c_begin, int32_t c_count, int32_t num_pages, const int32_t* page_table_row,
+                           int32_t max_pages, csa::CompressArgs& a) {
+  if (!kv_proj || !score_proj || !ape || !norm_w || !rope_cos || !rope_sin || !page_table_row) return CSA_ERR_NULL;
+  if (proj_dt != CSA_F32 && proj_dt != CSA_BF16) return CSA_ERR_DTYPE;
+  if (ratio != 4 && ratio != 128) return CSA_ERR_SHAPE;
+  const int coff = ratio == 4 ? 2 : 1;
+  if (ld_proj < (int64_t)coff * D || ld_proj % 2 != 0 || !std::isfinite(eps) || eps < 0.f) return CSA_ERR_SHAPE;
+  if (c_begin < 0 || c_count < 0 || n_tok < 0 || tok0 < 0 || num_pages < 1 || max_pages < 1) return CSA_ERR_SHAPE;
+  if (c_begin + c_count > (int64_t)max_pages * 64) return CSA_ERR_SHAPE;
+  if (c_count > 0) {
+    // every token the entries pool must have a projection row
+    const int64_t first = (ratio == 4 && c_begin > 0) ? (c_begin - 1) * ratio : c_begin * ratio;
+    if (first < tok0 || (c_begin + c_count) * ratio > tok0 + n_tok) return CSA_ERR_SHAPE;
+  }
+  const size_t pair = proj_dt == CSA_BF16 ? 4 : 8;
+  if (!aligned(kv_proj, pair) || !aligned(score_proj, pair) || !aligned(ape, 4) || !aligned(norm_w, 4) ||
+      !aligned(rope_cos, 4) || !aligned(rope_sin, 4) || !aligned(page_table_row, 4))
+    return CSA_ERR_ALIGN;
+  a.kv = kv_proj; a.score = score_proj; a.proj_dt = proj_dt == CSA_BF16 ? 1 : 0; a.ld = ld_proj; a.tok0 = tok0;
+  a.ratio = ratio; a.D = D; a.ape = ape; a.norm_w = norm_w; a.eps = eps; a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin; a.c_begin = c_begin; a.c_count = c_count; a.num_pages = num_pages;
+  a.page_table = page_table_row;
+  return CSA_OK;
+}
+}  // namespace
+
+csa_status csa_compress_kv(const void* kv_proj, const void* score_proj, int32_t proj_dt, int64_t ld_proj,
+                           int64_t tok0, int64_t n_tok, int32_t ratio, const float* ape, const float* norm_w,
+                           float eps, const float* rope_cos, const float* rope_sin, int64_t c_begin,
+                           int32_t c_count, void* pool_rows, int32_t pool_fmt, int32_t num_pages,
+                           const int32_t* page_table_row, int32_t max_pages, hipStream_t stream) {
+  csa::CompressArgs a{};
+  CSA_TRY(compress_common(kv_proj, score_proj, proj_dt, ld_proj, tok0, n_tok, ratio, 512, ape, norm_w, eps, rope_cos,
+                          rope_sin, c_begin, c_count, num_pages, page_table_row, max_pages, a));
+  if (!pool_rows) return CSA_ERR_NULL;
+  if (!kv_fmt_ok(pool_fmt)) return CSA_ERR_DTYPE;
+  if (!aligned(pool_rows, 16)) return CSA_ERR_ALIGN;
+  a.out = (uint8_t*)pool_rows; a.out_fmt = pool_fmt;
+  return hip_status(csa::launch_compress(a, stream));
+}
+
+csa_status csa_compress_index_keys(const void* kv_proj, const void* score_proj, int32_t proj_dt, int64_t ld_proj,
+                                   int64_t tok0, int64_t n_tok, int32_t ratio, const float* ape,
+                                   const float* norm_w, float eps, const float* rope_cos, const float* rope_sin,
+                                   int64_t c_begin, int32_t c_count, void* keys, uint8_t* scales, int32_t key_dt,
+                                   int32_t num_pages, const int32_t* page_table_row, int32_t max_pages,
+                                   hipStream_t stream) {
+  csa::CompressArgs a{};
+  CSA_TRY(compress_common(kv_proj, score_proj, proj_dt, ld_proj, tok0, n_tok, ratio, 128, ape, norm_w, eps, rope_cos,
+                          rope_sin, c_begin, c_count, num_pages, page_table_row, max_pages, a));
+  if (!keys || !scales) return CSA_ERR_NULL;
+  if (key_dt != CSA_FP8_E4M3FN && key_dt != CSA_FP4_E2M1) return CSA_ERR_DTYPE;
+  if (!aligned(keys, 16)) return CSA_ERR_ALIGN;
+  a.out = (uint8_t*)keys; a.out_fmt = key_dt; a.out_scales = scales;
+  return hip_status(csa::launch_compress(a, stream));
+}
+
 size_t csa_hca_decode_workspace_bytes(int32_t B, int32_t H, int64_t max_ctx, int32_t ratio) {
   if (B < 1 || H < 1 || max_ctx < 0 || ratio < 1 || max_ctx / ratio + kWin > kMaxSlotsPerQuery) return 0;
   Carver c(nullptr);

@@ -126,6 +126,29 @@ struct AttnArgs {
   const int32_t* rows;
   int64_t ld_rows;
 };
+struct CompressArgs {
+  const void* kv;            // token projections, row (tok - tok0) at kv + row * ld: [n_tok][coff * D]
+  const void* score;         // gate projections, same layout
+  int proj_dt;               // 0 f32, 1 bf16
+  int64_t ld;                // elements per projection row
+  int64_t tok0;              // raw position of projection row 0
+  int ratio;                 // 4 (overlapping windows, coff = 2) or 128 (coff = 1)
+  int D;                     // 512 (KV rows) or 128 (indexer keys)
+  const float* ape;          // [ratio][coff * D]
+  const float* norm_w;       // [D]
+  float eps;
+  const float* rope_cos;     // [c_count][32]
+  const float* rope_sin;
+  int64_t c_begin;
+  int c_count;
+  uint8_t* out;              // KV pool rows (D = 512) or indexer key bytes (D = 128)
+  int out_fmt;               // D = 512: row format 0/1/2; D = 128: 2 fp8, 3 fp4
+  uint8_t* out_scales;       // D = 128: [P][4][64] E8M0
+  int num_pages;
+  const int32_t* page_table; // the request's row
+};
+hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
+
 int plan_attn_split(int Q, int H, int n_idx, int q_dt);
 // true when the BF16 matrix-core kernel serves this call (bf16 q, BF16/FP8 rows); else the fp32 kernel
 bool attn_uses_matrix_cores(int q_dt, int win_fmt, int comp_fmt, int n_win, int n_comp);

@@ -128,3 +128,36 @@ def hca_prefill(wl: Workload, d, out=None, ws=None, stream=None):
     csa.csa_hca_prefill(wl.Q, wl.H, d.q, wl.q_dt, d.sink, _comp(wl, d), d.win_rows[0], wl.win_fmt, T,
                         int(wl.positions[0]), wl.ratio, wl.softmax_scale, out, wl.out_dt, ws, nbytes, stream)
     return out
+
+
+def compress(ci, kind: str, out_fmt: int, c_begin: int, c_count: int, device="cuda", tok0: int = 0,
+             n_tok: int | None = None, num_pages: int | None = None, page_row=None, seed: int = 0, stream=None):
+    """csa_compress_kv (kind "kv") or csa_compress_index_keys (kind "keys") for entries c_begin ..
+    c_begin+c_count-1 of a compressor workload, projections rows tok0 .. tok0+n_tok-1 uploaded.
+    Returns (page_row numpy, pool outputs as numpy: rows, or (keys, scales))."""
+    import numpy as np
+    n_tok = ci.T - tok0 if n_tok is None else n_tok
+    need_pages = (c_begin + c_count + 63) // 64
+    num_pages = need_pages + 3 if num_pages is None else num_pages
+    if page_row is None:
+        page_row = np.random.default_rng(seed).permutation(num_pages)[:need_pages].astype(np.int32)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)
+    proj = (lambda a: t(a.view(np.int16))) if ci.proj_dt == 1 else t
+    kv, sc = proj(ci.kv_tok[tok0:tok0 + n_tok]), proj(ci.score_tok[tok0:tok0 + n_tok])
+    ape, w = t(ci.ape), t(ci.norm_w)
+    cs, sn = t(ci.rope_cos[c_begin:c_begin + c_count]), t(ci.rope_sin[c_begin:c_begin + c_count])
+    pt = t(page_row)
+    if kind == "kv":
+        rb = {0: 2048, 1: 1024, 2: 608}[out_fmt]
+        pool = torch.zeros((num_pages, 64, rb), dtype=torch.uint8, device=device)
+        csa.csa_compress_kv(kv, sc, ci.proj_dt, ci.kv_tok.shape[1], tok0, n_tok, ci.ratio, ape, w, ci.eps, cs, sn,
+                            c_begin, c_count, pool, out_fmt, num_pages, pt, len(page_row), stream)
+        torch.cuda.synchronize()
+        return page_row, pool.cpu().numpy()
+    width = 64 if out_fmt == 3 else 128
+    keys = torch.zeros((num_pages, 64, width), dtype=torch.uint8, device=device)
+    scales = torch.zeros((num_pages, 4, 64), dtype=torch.uint8, device=device)
+    csa.csa_compress_index_keys(kv, sc, ci.proj_dt, ci.kv_tok.shape[1], tok0, n_tok, ci.ratio, ape, w, ci.eps, cs, sn,
+                                c_begin, c_count, keys, scales, out_fmt, num_pages, pt, len(page_row), stream)
+    torch.cuda.synchronize()
+    return page_row, (keys.cpu().numpy(), scales.cpu().numpy())
