@@ -38,8 +38,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--config", default="batched", choices=["batched", "long", "ragged", "tiny", "prefill", "dense"],
-                   help="dense: a layer without an indexer (window ++ all 8,192 compressed entries at 1M tokens)")
+    p.add_argument("--config", default="batched",
+                   choices=["batched", "long", "ragged", "tiny", "prefill", "dense", "compress"],
+                   help="dense: a layer without an indexer (window ++ all 8,192 compressed entries at 1M tokens); "
+                        "compress: the compressor over a 65,536-token prefill (C4 KV rows + indexer keys)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for cpu_baseline")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--queries-per-request", type=int, default=1, metavar="S",
@@ -176,11 +178,109 @@ def indexer_launch_us(wl, copies, stream, n):
     return e0.elapsed_time(e1) * 1e3 / n
 
 
+def bench_compress(args):
+    """The compressor over one 65,536-token prefill: 16,384 C4 entries into FP8 KV rows and the
+    indexer's 16,384 FP8 keys, from bf16 projections already in HBM."""
+    import numpy as np
+    import torch
+
+    import long_context_sparse_csa_amd as csa
+    from workloads import configs
+
+    dev = "cuda"
+    T = 65536
+    kv_ci = configs.make_compressor("compress_kv", T, 4, D=512, seed=1)
+    key_ci = configs.make_compressor("compress_keys", T, 4, D=128, seed=2)
+    n = T // 4
+    pages = n // 64
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    page_row = t(np.random.default_rng(0).permutation(pages).astype(np.int32))
+    ins = []
+    for ci in (kv_ci, key_ci):
+        ins.append(dict(kv=t(ci.kv_tok.view(np.int16)), sc=t(ci.score_tok.view(np.int16)), ape=t(ci.ape),
+                        w=t(ci.norm_w), cs=t(ci.rope_cos), sn=t(ci.rope_sin), ld=ci.kv_tok.shape[1]))
+    pool = torch.zeros((pages, 64, 608), dtype=torch.uint8, device=dev)
+    keys = torch.zeros((pages, 64, 128), dtype=torch.uint8, device=dev)
+    scales = torch.zeros((pages, 4, 64), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        a, b = ins
+        csa.csa_compress_kv(a["kv"], a["sc"], 1, a["ld"], 0, T, 4, a["ape"], a["w"], 1e-6, a["cs"], a["sn"], 0, n,
+                            pool, 2, pages, page_row, pages, stream)
+        csa.csa_compress_index_keys(b["kv"], b["sc"], 1, b["ld"], 0, T, 4, b["ape"], b["w"], 1e-6, b["cs"], b["sn"],
+                                    0, n, keys, scales, 2, pages, page_row, pages, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    csa.csa_profile_reset()
+    csa.csa_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    csa.csa_profile_enable(False)
+    kernels = {}
+    for name in ("compress_kv", "compress_keys"):
+        tot, cnt = csa.csa_profile_collect(name)
+        if cnt:
+            kernels[name] = round(tot / cnt * 1e3, 3)
+    csa.csa_profile_reset()
+    # algorithmic bytes: every projection element once (bf16 kv and gate, two halves per token),
+    # the per-entry parameters, the written rows / keys + scales
+    kv_bytes = T * 2 * 1024 * 2 + n * 608 + 4 * 1024 * 4 + 512 * 4 + n * 64 * 4
+    key_bytes = T * 2 * 256 * 2 + n * (128 + 4) + 4 * 256 * 4 + 128 * 4 + n * 64 * 4
+    dom_us = kernels.get("compress_kv", ms * 1e3)
+    achieved = kv_bytes / (dom_us * 1e-6) / 1e9
+    res = {
+        "metric": "compressor tokens/s (C4 KV rows + indexer keys from bf16 projections); achieved HBM TB/s",
+        "value": round(T / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 projections, fp32 pooling, fp8 outputs",
+        "data": "synthetic (seeded N(0,1) projections, random position embedding and norm weight)",
+        "config": {"workload": "compress_prefill", "tokens": T, "ratio": 4, "entries": n, "kv_format": "fp8nope_bf16rope",
+                   "key_format": "fp8_e4m3fn"},
+        "achieved_hbm_tbs": round((kv_bytes + key_bytes) / (ms * 1e-3) / 1e12, 3),
+        "algorithmic_bytes_per_step": int(kv_bytes + key_bytes),
+        "kernel_us": kernels,
+        "roofline": {"bound": "hbm", "kernel": "compress_kv", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "bytes_per_launch": int(kv_bytes),
+                     "launch_us": round(dom_us, 3), "traffic": None},
+    }
+    if not args.no_cpu:
+        from oracle import csa_oracle as O
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:  # noqa: BLE001
+            cores = 1
+        t0 = time.perf_counter()
+        done = 0
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 10.0) and done < n:
+            O.compressor_reference(kv_ci, done, 64)
+            O.compressor_reference(key_ci, done, 64, rotate=True)
+            done += 64
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": done * 4 / el, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+                               "sample": f"{done} entries of both compressors ({el:.1f} s, fp64 numpy)"}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.config == "compress":
+        bench_compress(args)
+        return
     import numpy as np
     import torch
 
