@@ -283,8 +283,8 @@ csa_status csa_hca_prefill(int32_t Q, int32_t H, const void* q, int32_t q_dt, co
  *   CSA_FP8_E4M3FN (keys [P][64][128]) or CSA_FP4_E2M1 (keys [P][64][64]) with one E8M0 scale
  *   per 32 features in scales [P][4][64]: 2^ceil(log2(max(amax,1e-4)/448)) for FP8,
  *   2^ceil(log2(max(amax,6*2^-126)/6)) for FP4.
- * Ranges: ratio 4 or 128; ld_proj >= coff * D and even; c_begin + c_count <= 64 * max_pages;
- *         eps >= 0.  Projections 4-byte (bf16) / 8-byte (fp32) aligned; outputs 16-byte aligned.
+ * Ranges: ratio 4 or 128; ld_proj >= coff * D, a multiple of 8; c_begin + c_count <= 64 *
+ *         max_pages; eps >= 0.  Projections, ape, norm_w, rope tables and outputs 16-byte aligned.
  * ------------------------------------------------------------------------------------------- */
 csa_status csa_compress_kv(const void* kv_proj, const void* score_proj, int32_t proj_dt, int64_t ld_proj,
                            int64_t tok0, int64_t n_tok, int32_t ratio, const float* ape, const float* norm_w,

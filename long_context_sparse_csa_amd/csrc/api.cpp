@@ -557,7 +557,7 @@ csa_status compress_common(const void* kv_proj, const void* score_proj, int32_t 
   if (proj_dt != CSA_F32 && proj_dt != CSA_BF16) return CSA_ERR_DTYPE;
   if (ratio != 4 && ratio != 128) return CSA_ERR_SHAPE;
   const int coff = ratio == 4 ? 2 : 1;
-  if (ld_proj < (int64_t)coff * D || ld_proj % 2 != 0 || !std::isfinite(eps) || eps < 0.f) return CSA_ERR_SHAPE;
+  if (ld_proj < (int64_t)coff * D || ld_proj % 8 != 0 || !std::isfinite(eps) || eps < 0.f) return CSA_ERR_SHAPE;
   if (c_begin < 0 || c_count < 0 || n_tok < 0 || tok0 < 0 || num_pages < 1 || max_pages < 1) return CSA_ERR_SHAPE;
   if (c_begin + c_count > (int64_t)max_pages * 64) return CSA_ERR_SHAPE;
   if (c_count > 0) {
@@ -565,9 +565,8 @@ csa_status compress_common(const void* kv_proj, const void* score_proj, int32_t 
     const int64_t first = (ratio == 4 && c_begin > 0) ? (c_begin - 1) * ratio : c_begin * ratio;
     if (first < tok0 || (c_begin + c_count) * ratio > tok0 + n_tok) return CSA_ERR_SHAPE;
   }
-  const size_t pair = proj_dt == CSA_BF16 ? 4 : 8;
-  if (!aligned(kv_proj, pair) || !aligned(score_proj, pair) || !aligned(ape, 4) || !aligned(norm_w, 4) ||
-      !aligned(rope_cos, 4) || !aligned(rope_sin, 4) || !aligned(page_table_row, 4))
+  if (!aligned(kv_proj, 16) || !aligned(score_proj, 16) || !aligned(ape, 16) || !aligned(norm_w, 16) ||
+      !aligned(rope_cos, 16) || !aligned(rope_sin, 16) || !aligned(page_table_row, 4))
     return CSA_ERR_ALIGN;
   a.kv = kv_proj; a.score = score_proj; a.proj_dt = proj_dt == CSA_BF16 ? 1 : 0; a.ld = ld_proj; a.tok0 = tok0;
   a.ratio = ratio; a.D = D; a.ape = ape; a.norm_w = norm_w; a.eps = eps; a.rope_cos = rope_cos;

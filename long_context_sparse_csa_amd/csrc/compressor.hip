@@ -12,21 +12,34 @@
 // rotation of the whole row.  The row is quantised into the cache format and written to page
 // page_table[c >> 6], slot c & 63.
 //
-// One block per entry, one thread per feature pair (2t, 2t+1): the pair is a rotary pair, and
-// consecutive threads read consecutive 4-byte (bf16) or 8-byte (fp32) pairs of a token row, so
-// every position's loads coalesce.  The kernel is HBM-bound: it reads coff * D * 2 projections per
-// token once and writes one cache row per entry.
+// A thread owns 8 consecutive features (4 rotary pairs): one 16-byte load of bf16 projections
+// (two of fp32) per window position, so a token row is read by D/8 lanes with no redundancy and
+// all positions' loads are issued before the softmax needs them.  A 512-feature entry is one wave
+// (four entries per block), a 128-feature key 16 lanes (sixteen keys per block); the row-wide
+// reductions (RMSNorm, block maxima) and the Hadamard stages across lanes are lane exchanges.  The
+// kernel is HBM-bound: it reads coff * D * 2 projections per token once and writes one cache row
+// per entry.
 #include "csa_device.h"
 #include "csa_internal.h"
 
 namespace csa {
 
-__device__ __forceinline__ v2f load_pair(const void* base, bool bf16, int64_t off) {
+// 8 projections of a row: bf16 (one 16-byte load) or fp32 (two)
+__device__ __forceinline__ void load8(const void* base, bool bf16, int64_t off, float* v) {
   if (bf16) {
-    const uint32_t w = *(const uint32_t*)((const uint16_t*)base + off);
-    return v2f{bf16_bits_to_f32(w & 0xFFFFu), bf16_bits_to_f32(w >> 16)};
+    const uint4 w = *(const uint4*)((const uint16_t*)base + off);
+    const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_bits_to_f32(x[i] & 0xFFFFu);
+      v[2 * i + 1] = bf16_bits_to_f32(x[i] >> 16);
+    }
+  } else {
+    const float4 a = *(const float4*)((const float*)base + off);
+    const float4 b = *(const float4*)((const float*)base + off + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   }
-  return *(const v2f*)((const float*)base + off);
 }
 
 // nearest E2M1 code of |x| <= 6 (larger saturates), ties to the even code; sign in bit 3
@@ -52,65 +65,101 @@ __device__ __forceinline__ uint32_t e8m0_ceil(float v) {
   return e > 254u ? 254u : e;
 }
 
+// max / sum over the L lanes of an aligned lane group
+template <int L>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int m = 1; m < L; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < L; m <<= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
 template <int D>
-__global__ __launch_bounds__(D / 2) void compress_kernel(CompressArgs a) {
-  constexpr int NT = D / 2;
+__global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
+  constexpr int L = D / 8;                 // lanes per entry
   constexpr int kRope = 64;
-  const int t = threadIdx.x;
-  const int64_t c = a.c_begin + blockIdx.x;
+  const int lane_in = threadIdx.x % L;     // features [8 lane_in, 8 lane_in + 8)
+  const int64_t ci = (int64_t)blockIdx.x * (256 / L) + threadIdx.x / L;   // entry index in the call
+  if (ci >= a.c_count) return;             // whole lane groups leave together
+  const int64_t c = a.c_begin + ci;
   const bool overlap = a.ratio == 4;
   const int coff = overlap ? 2 : 1;
   const bool bf16 = a.proj_dt == 1;
+  const int f0 = 8 * lane_in;
 
   // online softmax over the window positions, per feature
-  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.f, l1 = 0.f, s0 = 0.f, s1 = 0.f;
-  auto add = [&](int64_t tok, int half, int wpos) {
-    const int col = half * D + 2 * t;
-    const int64_t off = (tok - a.tok0) * a.ld + col;
-    const v2f k = load_pair(a.kv, bf16, off);
-    v2f s = load_pair(a.score, bf16, off);
-    s[0] += a.ape[(int64_t)wpos * coff * D + col];
-    s[1] += a.ape[(int64_t)wpos * coff * D + col + 1];
-    const float n0 = fmaxf(m0, s[0]), n1 = fmaxf(m1, s[1]);
-    const float r0 = exp2f((m0 - n0) * kLog2e), r1 = exp2f((m1 - n1) * kLog2e);
-    const float e0 = exp2f((s[0] - n0) * kLog2e), e1 = exp2f((s[1] - n1) * kLog2e);
-    l0 = fmaf(l0, r0, e0);
-    l1 = fmaf(l1, r1, e1);
-    s0 = fmaf(s0, r0, e0 * k[0]);
-    s1 = fmaf(s1, r1, e1 * k[1]);
-    m0 = n0;
-    m1 = n1;
-  };
-  if (overlap && c > 0) {
+  float m[8], l[8], acc[8];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) add((c - 1) * 4 + w, 0, w);
+  for (int e = 0; e < 8; ++e) {
+    m[e] = -INFINITY;
+    l[e] = 0.f;
+    acc[e] = 0.f;
   }
-#pragma unroll 8
-  for (int w = 0; w < a.ratio; ++w) add(c * a.ratio + w, overlap ? 1 : 0, w);
-  float y0 = s0 / l0, y1 = s1 / l1;
+  auto add = [&](int64_t tok, int half, int wpos) {
+    const int col = half * D + f0;
+    const int64_t off = (tok - a.tok0) * a.ld + col;
+    float k[8], sc[8];
+    load8(a.kv, bf16, off, k);
+    load8(a.score, bf16, off, sc);
+    const float4 p0 = *(const float4*)(a.ape + (int64_t)wpos * coff * D + col);
+    const float4 p1 = *(const float4*)(a.ape + (int64_t)wpos * coff * D + col + 4);
+    const float pe[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float s = sc[e] + pe[e];
+      const float n = fmaxf(m[e], s);
+      const float r = exp2f((m[e] - n) * kLog2e), x = exp2f((s - n) * kLog2e);
+      l[e] = fmaf(l[e], r, x);
+      acc[e] = fmaf(acc[e], r, x * k[e]);
+      m[e] = n;
+    }
+  };
+  if (overlap) {
+    if (c > 0) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) add((c - 1) * 4 + w, 0, w);
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) add(c * 4 + w, 1, w);
+  } else {
+#pragma unroll 4
+    for (int w = 0; w < a.ratio; ++w) add(c * a.ratio + w, 0, w);
+  }
+  float y[8];
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    y[e] = acc[e] / l[e];
+    ss = fmaf(y[e], y[e], ss);
+  }
 
   // RMSNorm over the D features
-  __shared__ float red[NT / 64 > 0 ? NT / 64 : 1];
-  float ss = wave_sum(y0 * y0 + y1 * y1);
-  if constexpr (NT > 64) {
-    if ((t & 63) == 0) red[t >> 6] = ss;
-    __syncthreads();
-    ss = 0.f;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) ss += red[w];
-  }
+  ss = group_sum<L>(ss);
   const float inv = 1.f / sqrtf(ss / (float)D + a.eps);
-  y0 = y0 * inv * a.norm_w[2 * t];
-  y1 = y1 * inv * a.norm_w[2 * t + 1];
+  {
+    const float4 w0 = *(const float4*)(a.norm_w + f0), w1 = *(const float4*)(a.norm_w + f0 + 4);
+    const float w[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) y[e] = y[e] * inv * w[e];
+  }
 
-  // rotary embedding of the last 64 features: pair (2t, 2t+1) times cos + i sin
-  if (2 * t >= D - kRope) {
-    const int p = t - (D - kRope) / 2;
-    const float cs = a.rope_cos[(int64_t)blockIdx.x * (kRope / 2) + p];
-    const float sn = a.rope_sin[(int64_t)blockIdx.x * (kRope / 2) + p];
-    const float r0 = y0 * cs - y1 * sn, r1 = y0 * sn + y1 * cs;
-    y0 = r0;
-    y1 = r1;
+  // rotary embedding of the last 64 features: pairs (2j, 2j+1) times cos + i sin
+  if (f0 >= D - kRope) {
+    const int p0 = (f0 - (D - kRope)) / 2;
+    const float4 cs = *(const float4*)(a.rope_cos + ci * (kRope / 2) + p0);
+    const float4 sn = *(const float4*)(a.rope_sin + ci * (kRope / 2) + p0);
+    const float cv[4] = {cs.x, cs.y, cs.z, cs.w}, sv[4] = {sn.x, sn.y, sn.z, sn.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float re = y[2 * j], im = y[2 * j + 1];
+      y[2 * j] = re * cv[j] - im * sv[j];
+      y[2 * j + 1] = re * sv[j] + im * cv[j];
+    }
   }
 
   const int pid = a.page_table[c >> 6];
@@ -120,61 +169,92 @@ __global__ __launch_bounds__(D / 2) void compress_kernel(CompressArgs a) {
   if constexpr (D == 512) {
     uint8_t* row = a.out + slot_row * row_bytes(a.out_fmt);
     if (a.out_fmt == kRowF32) {
-      if (mapped) *(v2f*)(row + 8 * t) = v2f{y0, y1};
-    } else if (a.out_fmt == kRowBF16) {
-      if (mapped) *(uint32_t*)(row + 4 * t) = pack_bf16x2(y0, y1);
-    } else if (2 * t < kNope) {
-      // e4m3fn nope with one fp32 scale per 64 features (32 threads, lane-aligned halves of a wave)
-      float amax = fmaxf(fabsf(y0), fabsf(y1));
-#pragma unroll
-      for (int m = 1; m < 32; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
-      const float sc = fmaxf(amax, 1e-4f) * (1.f / 448.f);
-      const int codes = __builtin_amdgcn_cvt_pk_fp8_f32(y0 / sc, y1 / sc, 0, false);
       if (mapped) {
-        *(uint16_t*)(row + 2 * t) = (uint16_t)(codes & 0xFFFF);
-        if ((t & 31) == 0) *(float*)(row + 576 + 4 * (t >> 5)) = sc;
+        *(float4*)(row + 4 * f0) = make_float4(y[0], y[1], y[2], y[3]);
+        *(float4*)(row + 4 * f0 + 16) = make_float4(y[4], y[5], y[6], y[7]);
       }
+    } else if (a.out_fmt == kRowBF16) {
+      if (mapped)
+        *(uint4*)(row + 2 * f0) = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                             pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
     } else {
-      if (mapped) {
-        *(uint32_t*)(row + 448 + 2 * (2 * t - kNope)) = pack_bf16x2(y0, y1);
-        if (t == NT - 1) *(uint32_t*)(row + 604) = 0u;
+      // e4m3fn nope with one fp32 scale per 64 features (8 lanes); every lane joins the exchange
+      float amax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[e]));
+      amax = group_max<8>(amax);
+      if (f0 < kNope) {
+        const float sc = fmaxf(amax, 1e-4f) * (1.f / 448.f);
+        uint32_t w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          int v = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h] / sc, y[4 * h + 1] / sc, 0, false);
+          v = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h + 2] / sc, y[4 * h + 3] / sc, v, true);
+          w[h] = (uint32_t)v;
+        }
+        if (mapped) {
+          *(uint2*)(row + f0) = make_uint2(w[0], w[1]);
+          if ((lane_in & 7) == 0) *(float*)(row + 576 + 4 * (f0 >> 6)) = sc;
+        }
+      } else if (mapped) {
+        *(uint4*)(row + 448 + 2 * (f0 - kNope)) = make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]),
+                                                             pack_bf16x2(y[4], y[5]), pack_bf16x2(y[6], y[7]));
+        if (lane_in == L - 1) *(uint32_t*)(row + 604) = 0u;
       }
     }
   } else {
-    // indexer key: Hadamard rotation over the 128 features (one wave; the butterfly of stride h
-    // pairs feature e with e ^ h: within the thread for h = 1, else lane t ^ (h / 2)), then E8M0
-    // per 32 features (16 threads) and FP8 or FP4 codes
+    // indexer key: Hadamard rotation over the 128 features (the butterfly of stride h pairs
+    // feature e with e ^ h: inside the thread for h < 8, else lane lane_in ^ (h / 8)), then E8M0
+    // per 32 features (4 lanes) and FP8 or FP4 codes
 #pragma unroll
-    for (int h = 1; h < D; h <<= 1) {
-      if (h == 1) {
-        const float u = y0 + y1, v = y0 - y1;
-        y0 = u;
-        y1 = v;
-      } else {
-        const float o0 = __shfl_xor(y0, h >> 1), o1 = __shfl_xor(y1, h >> 1);
-        const bool hi = (t & (h >> 1)) != 0;
-        y0 = hi ? o0 - y0 : y0 + o0;
-        y1 = hi ? o1 - y1 : y1 + o1;
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if ((e & h) == 0) {
+          const float u = y[e] + y[e + h], v = y[e] - y[e + h];
+          y[e] = u;
+          y[e + h] = v;
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 8; h < D; h <<= 1) {
+      const bool hi = (lane_in & (h >> 3)) != 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float o = __shfl_xor(y[e], h >> 3);
+        y[e] = hi ? o - y[e] : y[e] + o;
       }
     }
     const float hs = 0.08838834764831845f;   // 128^-1/2
-    y0 *= hs;
-    y1 *= hs;
-    float amax = fmaxf(fabsf(y0), fabsf(y1));
+    float amax = 0.f;
 #pragma unroll
-    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m));
+    for (int e = 0; e < 8; ++e) {
+      y[e] *= hs;
+      amax = fmaxf(amax, fabsf(y[e]));
+    }
+    amax = group_max<4>(amax);
     const bool fp4 = a.out_fmt == 3;
-    const uint32_t e = fp4 ? e8m0_ceil(fmaxf(amax, 6.f * 1.17549435e-38f) / 6.f)
-                           : e8m0_ceil(fmaxf(amax, 1e-4f) * (1.f / 448.f));
-    const float q = __uint_as_float((254u - e) << 23);   // 2^-(e-127), exact
+    const uint32_t ex = fp4 ? e8m0_ceil(fmaxf(amax, 6.f * 1.17549435e-38f) / 6.f)
+                            : e8m0_ceil(fmaxf(amax, 1e-4f) * (1.f / 448.f));
+    const float q = __uint_as_float((254u - ex) << 23);   // 2^-(ex-127), exact
     if (mapped) {
       if (fp4) {
-        a.out[slot_row * 64 + t] = (uint8_t)(e2m1_code(y0 * q) | (e2m1_code(y1 * q) << 4));
+        uint32_t w = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w |= e2m1_code(y[e] * q) << (4 * e);
+        *(uint32_t*)(a.out + slot_row * 64 + f0 / 2) = w;
       } else {
-        const int codes = __builtin_amdgcn_cvt_pk_fp8_f32(y0 * q, y1 * q, 0, false);
-        *(uint16_t*)(a.out + slot_row * 128 + 2 * t) = (uint16_t)(codes & 0xFFFF);
+        uint32_t w[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          int v = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h] * q, y[4 * h + 1] * q, 0, false);
+          v = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h + 2] * q, y[4 * h + 3] * q, v, true);
+          w[h] = (uint32_t)v;
+        }
+        *(uint2*)(a.out + slot_row * 128 + f0) = make_uint2(w[0], w[1]);
       }
-      if ((t & 15) == 0) a.out_scales[(int64_t)pid * 256 + (t >> 4) * kPage + (c & (kPage - 1))] = (uint8_t)e;
+      if ((lane_in & 3) == 0) a.out_scales[(int64_t)pid * 256 + (f0 >> 5) * kPage + (c & (kPage - 1))] = (uint8_t)ex;
     }
   }
 }
@@ -182,8 +262,10 @@ __global__ __launch_bounds__(D / 2) void compress_kernel(CompressArgs a) {
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   if (a.c_count <= 0) return hipSuccess;
   ProfScope p(a.D == 512 ? "compress_kv" : "compress_keys", s);
-  if (a.D == 512) hipLaunchKernelGGL(compress_kernel<512>, dim3((unsigned)a.c_count), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(compress_kernel<128>, dim3((unsigned)a.c_count), dim3(64), 0, s, a);
+  const int per_block = 256 / (a.D / 8);   // entries per block of 256 threads
+  const unsigned blocks = (unsigned)((a.c_count + per_block - 1) / per_block);
+  if (a.D == 512) hipLaunchKernelGGL(compress_kernel<512>, dim3(blocks), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(compress_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
