@@ -205,6 +205,17 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(TopkArgs a) {
   __shared__ uint32_t s_wave[4];
   __shared__ int s_digit;
   __shared__ uint32_t s_before, s_at;
+  // this thread's scores are loaded first (they do not depend on the threshold), so their memory
+  // latency overlaps the histogram's
+  const int64_t end = begin + kSelChunk < nv ? begin + kSelChunk : nv;
+  const float* row = a.logits + (int64_t)q * a.ld;
+  constexpr int kPer = kSelChunk / 256;
+  float vals[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int64_t c = begin + j * 256 + tid;
+    vals[j] = row[c < end ? c : 0];
+  }
   threshold_bin(a.hist + (int64_t)q * kHistBins, (uint32_t)k, s_wave, &s_digit, &s_before, &s_at);
   const int bstar = s_digit;
   const uint32_t above = s_before;
@@ -221,16 +232,6 @@ __global__ __launch_bounds__(256) void topk_collect_kernel(TopkArgs a) {
   __shared__ uint32_t s_na, s_nc, s_ga, s_gc;
   if (tid == 0) { s_na = 0u; s_nc = 0u; }
   __syncthreads();
-  const int64_t end = begin + kSelChunk < nv ? begin + kSelChunk : nv;
-  const float* row = a.logits + (int64_t)q * a.ld;
-  // all of this thread's scores are loaded before any is examined (one memory latency, not 16)
-  constexpr int kPer = kSelChunk / 256;
-  float vals[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int64_t c = begin + j * 256 + tid;
-    vals[j] = row[c < end ? c : begin];
-  }
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int64_t c = begin + j * 256 + tid;
