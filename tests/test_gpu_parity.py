@@ -249,6 +249,31 @@ def test_decode_multi_query(dev, idx_dt):
     _say(f"max err {err:.2e}")
 
 
+def test_decode_multi_query_unshared_blocks(dev):
+    """Five queries per request: more than one indexer block shares, so each query takes its own
+    blocks (the per-query path with the request mapping q / S)."""
+    run, tio = _run()
+    ctx = [9000, 4, 600]
+    wl = configs.make_decode("multi5", ctx, H=16, HI=40, seed=33, q_per_req=5)
+    _say(f"decode multi-query S=5 ctx={ctx}")
+    out, idx = run.decode(wl, tio.to_device(wl, dev))
+    err = _check_decode(wl, tio.out_to_numpy(out), idx.cpu().numpy(), BF16_TOL)
+    _say(f"max err {err:.2e}")
+
+
+def test_hca_decode_fp32(dev):
+    """A layer without an indexer in fp32 (q, rows and output): the fp32 attention over dense
+    lists of 128 + 300 slots."""
+    run, tio = _run()
+    ctx = [128 * 300 + 77, 128 * 5]
+    wl = configs.make_decode("hca_f32", ctx, H=8, HI=4, q_dt=configs.DT_F32, out_dt=configs.DT_F32,
+                             kv_fmt=configs.KV_F32, seed=14, ratio=128)
+    _say(f"hca decode fp32 ctx={ctx}")
+    out = tio.out_to_numpy(run.hca_decode(wl, tio.to_device(wl, dev)))
+    for qi in range(wl.Q):
+        check_attention(out[qi], O.run_query_dense(wl, qi), F32_TOL, f"query {qi}")
+
+
 def test_decode_multi_query_long_rows(dev):
     """Two queries per request on rows longer than the one-block selection takes (the histogram /
     collect / finish path and its preparation launch)."""
