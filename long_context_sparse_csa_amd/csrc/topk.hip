@@ -514,6 +514,11 @@ __device__ __forceinline__ void wave_find_desc(const uint32_t* bins, int nb, uin
   }
 }
 
+// the score of an order key (the inverse of order_key; -0.0 comes back as +0.0)
+__device__ __forceinline__ float key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
 // NT threads cover rows of up to 16 NT entries; short rows take a small block so that several
 // rows share a CU (LDS: 16 KB of bins + 8 KB of candidate keys / selected indices + 4 B per thread).
 template <int NT>
@@ -547,6 +552,7 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
   uint32_t* cand_key = cand_sel;
   int32_t* sel = (int32_t*)cand_sel;
   __shared__ uint32_t s_digit, s_before, s_ncand, s_T, s_need;
+  __shared__ uint32_t ext[2 * (NT / 64)];   // per-wave largest / smallest visible key
 
   const float* row = a.logits + (int64_t)q * a.ld;
   const int c0 = tid * kSinglePer;          // this thread owns entries [c0, c0+16)
@@ -567,98 +573,200 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
     for (int j = 0; j < kSinglePer; ++j) key[j] = order_key(v[j]);   // entries past n_vis are never counted
   }
   __syncthreads();
-  // level 1: top 12 key bits of every entry (all lanes active: one LDS atomic instruction covers 64)
-#pragma unroll
-  for (int j = 0; j < kSinglePer; ++j)
-    if (c0 + j < nv) atomicAdd(&bins[key[j] >> kHistShift], 1u);
-  __syncthreads();
-  if (wave == 0) wave_find_desc(bins, kHistBins, (uint32_t)k, &s_digit, &s_before);
-  __syncthreads();
-  const uint32_t bstar = s_digit;
-  const uint32_t need1 = (uint32_t)k - s_before;   // entries still to take from bin b* (>= 1)
-  // the entries of bin b* become candidates: their keys are appended to LDS with one atomic per
-  // wave, a lane's after those of the lanes below it
+  // row extremes of the visible keys: per wave, then across waves after the barrier
   {
-    uint32_t hm = 0;   // bit j: entry c0 + j is in b*
+    uint32_t kmx = 0u, kmn = 0xFFFFFFFFu;
 #pragma unroll
-    for (int j = 0; j < kSinglePer; ++j) hm |= (c0 + j < nv && (key[j] >> kHistShift) == bstar) ? (1u << j) : 0u;
-    const uint32_t hits = __popc(hm);
-    const uint32_t incl = wave_inclusive_scan(hits);
-    uint32_t base = 0;
-    if (lane == 63 && incl) base = atomicAdd(&s_ncand, incl);
-    base = __builtin_amdgcn_readlane(base, 63);
-    uint32_t pos = base + incl - hits;
-    while (hm) {
-      const int j = __ffs((int)hm) - 1;
-      hm &= hm - 1u;
-      if (pos < (uint32_t)kCandMax) cand_key[pos] = key[j];
-      ++pos;
+    for (int j = 0; j < kSinglePer; ++j) {
+      if (c0 + j < nv) {
+        kmx = key[j] > kmx ? key[j] : kmx;
+        kmn = key[j] < kmn ? key[j] : kmn;
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const uint32_t a1 = (uint32_t)__shfl_xor((int)kmx, m), b1 = (uint32_t)__shfl_xor((int)kmn, m);
+      kmx = a1 > kmx ? a1 : kmx;
+      kmn = b1 < kmn ? b1 : kmn;
+    }
+    if (lane == 0) {
+      ext[wave] = kmx;
+      ext[NT / 64 + wave] = kmn;
     }
   }
   __syncthreads();
-  const uint32_t n_cand = s_ncand;
-  if (n_cand <= (uint32_t)kCandMax) {
-    // wave 0 alone resolves the 20 low key bits among the candidates (two 10-bit levels in a
-    // wave-private histogram); LDS operations of one wave complete in order
-    if (wave == 0) {
-      uint32_t prefix = bstar, need = need1;
-#pragma unroll 1
-      for (int lvl = 0; lvl < 2; ++lvl) {
-        const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
+  // Level 1 on the value range: 4096 equal-width bins between the row's smallest and largest
+  // finite score.  Scores crowd a few of the fixed 12-bit key-prefix bins (the exponent and three
+  // mantissa bits), so LDS atomics collide and the threshold bin holds hundreds of entries; on the
+  // value range the bins hold a handful.  The bin index is a monotone function of the score
+  // (subtraction, multiplication by a positive scale and truncation all preserve order), so b*
+  // and the counts above it are exact.  When b* holds at most 64 entries one wave ranks them by
+  // their full keys; otherwise (ties, clusters, non-finite scores) the key-prefix levels run.
+  bool resolved = false;
+  {
+    uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
 #pragma unroll
-        for (int i = 0; i < 1024; i += 256) *(uint4*)&bins[i + 4 * lane] = make_uint4(0u, 0u, 0u, 0u);
-        __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-        __builtin_amdgcn_wave_barrier();
-        // four candidates per lane per pass: their reads are all in flight before the first atomic
-        for (uint32_t i0 = 0; i0 < n_cand; i0 += 256) {
-          uint32_t kk[4];
+    for (int w = 0; w < NT / 64; ++w) {
+      kmax = ext[w] > kmax ? ext[w] : kmax;
+      kmin = ext[NT / 64 + w] < kmin ? ext[NT / 64 + w] : kmin;
+    }
+    const float vmin = key_value(kmin), vmax = key_value(kmax);
+    const float scale = 4096.f / (vmax - vmin);
+    // every visible key is finite (NaN maps below -inf, infinities outside +-FLT_MAX) and spread
+    const bool adaptive = kmin >= order_key(-3.40282347e+38f) && kmax <= order_key(3.40282347e+38f) &&
+                          kmax > kmin && scale > 0.f && scale < 3.0e38f;
+    if (adaptive) {
+      uint32_t bin[kSinglePer];
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint32_t i = i0 + 64 * u + lane;
-            kk[u] = cand_key[i < n_cand ? i : 0];
+      for (int j = 0; j < kSinglePer; ++j) {
+        const float x = (key_value(key[j]) - vmin) * scale;
+        // x >= 0 for visible entries; entries past n_vis (never counted) are clamped too
+        const uint32_t b = x < 4095.f ? (x > 0.f ? (uint32_t)x : 0u) : 4095u;
+        bin[j] = b;
+        if (c0 + j < nv) atomicAdd(&bins[b], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) wave_find_desc(bins, kHistBins, (uint32_t)k, &s_digit, &s_before);
+      __syncthreads();
+      const uint32_t bstar = s_digit;
+      const uint32_t need1 = (uint32_t)k - s_before;
+      {
+        uint32_t hm = 0;
+#pragma unroll
+        for (int j = 0; j < kSinglePer; ++j) hm |= (c0 + j < nv && bin[j] == bstar) ? (1u << j) : 0u;
+        const uint32_t hits = __popc(hm);
+        const uint32_t incl = wave_inclusive_scan(hits);
+        uint32_t base = 0;
+        if (lane == 63 && incl) base = atomicAdd(&s_ncand, incl);
+        base = __builtin_amdgcn_readlane(base, 63);
+        uint32_t pos = base + incl - hits;
+        while (hm) {
+          const int j = __ffs((int)hm) - 1;
+          hm &= hm - 1u;
+          if (pos < 64u) cand_key[pos] = key[j];
+          ++pos;
+        }
+      }
+      __syncthreads();
+      const uint32_t n_cand = s_ncand;
+      if (n_cand <= 64u) {
+        // rank the candidates by their keys: the threshold is the key with fewer than need1 keys
+        // above it and at least need1 at or above it
+        if (wave == 0) {
+          const uint32_t mine = lane < (int)n_cand ? cand_key[lane] : 0u;
+          uint32_t gt = 0, ge = 0;
+          for (int j = 0; j < (int)n_cand; ++j) {
+            const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, j);
+            gt += o > mine ? 1u : 0u;
+            ge += o >= mine ? 1u : 0u;
           }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint32_t i = i0 + 64 * u + lane;
-            if (i < n_cand && (kk[u] >> (shift + 10)) == prefix) atomicAdd(&bins[(kk[u] >> shift) & 1023u], 1u);
+          if (lane < (int)n_cand && gt < need1 && ge >= need1) {   // every such lane holds the same key
+            s_T = mine;
+            s_need = need1 - gt;
           }
         }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
-        wave_find_desc(bins, 1024, need, &s_digit, &s_before);
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
+        resolved = true;
+      } else {
+        for (int i = tid; i < kHistBins; i += NT) bins[i] = 0u;
+        if (tid == 0) s_ncand = 0u;
+        __syncthreads();
+      }
+    }
+  }
+  if (!resolved) {
+    // level 1: top 12 key bits of every entry (all lanes active: one LDS atomic instruction covers 64)
+  #pragma unroll
+    for (int j = 0; j < kSinglePer; ++j)
+      if (c0 + j < nv) atomicAdd(&bins[key[j] >> kHistShift], 1u);
+    __syncthreads();
+    if (wave == 0) wave_find_desc(bins, kHistBins, (uint32_t)k, &s_digit, &s_before);
+    __syncthreads();
+    const uint32_t bstar = s_digit;
+    const uint32_t need1 = (uint32_t)k - s_before;   // entries still to take from bin b* (>= 1)
+    // the entries of bin b* become candidates: their keys are appended to LDS with one atomic per
+    // wave, a lane's after those of the lanes below it
+    {
+      uint32_t hm = 0;   // bit j: entry c0 + j is in b*
+  #pragma unroll
+      for (int j = 0; j < kSinglePer; ++j) hm |= (c0 + j < nv && (key[j] >> kHistShift) == bstar) ? (1u << j) : 0u;
+      const uint32_t hits = __popc(hm);
+      const uint32_t incl = wave_inclusive_scan(hits);
+      uint32_t base = 0;
+      if (lane == 63 && incl) base = atomicAdd(&s_ncand, incl);
+      base = __builtin_amdgcn_readlane(base, 63);
+      uint32_t pos = base + incl - hits;
+      while (hm) {
+        const int j = __ffs((int)hm) - 1;
+        hm &= hm - 1u;
+        if (pos < (uint32_t)kCandMax) cand_key[pos] = key[j];
+        ++pos;
+      }
+    }
+    __syncthreads();
+    const uint32_t n_cand = s_ncand;
+    if (n_cand <= (uint32_t)kCandMax) {
+      // wave 0 alone resolves the 20 low key bits among the candidates (two 10-bit levels in a
+      // wave-private histogram); LDS operations of one wave complete in order
+      if (wave == 0) {
+        uint32_t prefix = bstar, need = need1;
+  #pragma unroll 1
+        for (int lvl = 0; lvl < 2; ++lvl) {
+          const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
+  #pragma unroll
+          for (int i = 0; i < 1024; i += 256) *(uint4*)&bins[i + 4 * lane] = make_uint4(0u, 0u, 0u, 0u);
+          __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+          __builtin_amdgcn_wave_barrier();
+          // four candidates per lane per pass: their reads are all in flight before the first atomic
+          for (uint32_t i0 = 0; i0 < n_cand; i0 += 256) {
+            uint32_t kk[4];
+  #pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const uint32_t i = i0 + 64 * u + lane;
+              kk[u] = cand_key[i < n_cand ? i : 0];
+            }
+  #pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const uint32_t i = i0 + 64 * u + lane;
+              if (i < n_cand && (kk[u] >> (shift + 10)) == prefix) atomicAdd(&bins[(kk[u] >> shift) & 1023u], 1u);
+            }
+          }
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          __builtin_amdgcn_wave_barrier();
+          wave_find_desc(bins, 1024, need, &s_digit, &s_before);
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          __builtin_amdgcn_wave_barrier();
+          prefix = (prefix << 10) | s_digit;
+          need -= s_before;
+        }
+        if (lane == 0) {
+          s_T = prefix;
+          s_need = need;
+        }
+      }
+    } else {
+      // many entries share b* (heavily tied scores): levels 2 and 3 over the whole block, ten more
+      // key bits each, counting only entries with the current prefix
+      uint32_t prefix = bstar, need = need1;
+  #pragma unroll 1
+      for (int lvl = 0; lvl < 2; ++lvl) {
+        const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
+        for (int i = tid; i < 1024; i += NT) bins[i] = 0u;
+        __syncthreads();
+  #pragma unroll
+        for (int j = 0; j < kSinglePer; ++j) {
+          const bool hit = c0 + j < nv && (key[j] >> (shift + 10)) == prefix;
+          if (__any(hit) && hit) atomicAdd(&bins[(key[j] >> shift) & 1023u], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) wave_find_desc(bins, 1024, need, &s_digit, &s_before);
+        __syncthreads();
         prefix = (prefix << 10) | s_digit;
         need -= s_before;
       }
-      if (lane == 0) {
+      if (tid == 0) {
         s_T = prefix;
         s_need = need;
       }
-    }
-  } else {
-    // many entries share b* (heavily tied scores): levels 2 and 3 over the whole block, ten more
-    // key bits each, counting only entries with the current prefix
-    uint32_t prefix = bstar, need = need1;
-#pragma unroll 1
-    for (int lvl = 0; lvl < 2; ++lvl) {
-      const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
-      for (int i = tid; i < 1024; i += NT) bins[i] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int j = 0; j < kSinglePer; ++j) {
-        const bool hit = c0 + j < nv && (key[j] >> (shift + 10)) == prefix;
-        if (__any(hit) && hit) atomicAdd(&bins[(key[j] >> shift) & 1023u], 1u);
-      }
-      __syncthreads();
-      if (wave == 0) wave_find_desc(bins, 1024, need, &s_digit, &s_before);
-      __syncthreads();
-      prefix = (prefix << 10) | s_digit;
-      need -= s_before;
-    }
-    if (tid == 0) {
-      s_T = prefix;
-      s_need = need;
     }
   }
   __syncthreads();
