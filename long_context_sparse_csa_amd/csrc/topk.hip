@@ -470,11 +470,14 @@ __global__ __launch_bounds__(256) void topk_finish_kernel(TopkArgs a) {
 // of a microsecond at 16 waves, and a predicated LDS instruction costs its issue slot even when
 // few lanes are active, so the phases are few, the scans are done by a single wave and sparse
 // passes skip instructions no lane needs:
-//   1. a 12-bit histogram of every key gives the threshold bin b* and the count above it;
-//   2. the keys of b*'s entries (normally a few hundred) are appended to an LDS candidate list, and
-//      one wave resolves their remaining 20 bits (two 10-bit levels, no block barrier),
-//      giving the exact k-th largest key T and how many keys equal to T are taken; a bin with more
-//      than kCandMax entries (heavily tied scores) takes two block-wide levels instead;
+//   1. a 4096-bin histogram of the scores over the row's value range gives the threshold bin b*
+//      and the count above it; b*'s entries (normally a handful) go to an LDS candidate list and
+//      one wave ranks them by their full keys, giving the exact k-th largest key T and how many
+//      keys equal to T are taken;
+//   2. when b* holds more than 64 entries (ties, clusters) or a score is not finite, the levels run
+//      on key prefixes instead: a 12-bit histogram of every key gives b*, and the keys of its
+//      entries are resolved by one wave (two 10-bit levels of the remaining 20 bits, no block
+//      barrier), or by two block-wide levels when more than kCandMax entries share b*;
 //   3. one block scan of the per-thread (greater, equal) counts, packed in one word, places the k
 //      indices in ascending order (equal keys at T in index order) in LDS, from where they are
 //      written with coalesced stores.
