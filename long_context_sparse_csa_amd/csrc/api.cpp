@@ -381,6 +381,7 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   a.part = pw.part;
   a.req_mode = mode;
   a.q_per_req = S;
+  if (mode == 2) { a.trim_ratio = 4; a.pos0 = pos0; }   // selection pads past min(n_vis, k) with -1
   if (single) { a.rows = pw.rows; a.ld_rows = k; }
   return hip_status(csa::launch_attention(a, stream));
 }
@@ -523,6 +524,7 @@ csa_status run_hca(int mode, int32_t rows, int32_t H, const void* q, int32_t q_d
                   ? csa::plan_attn_split(rows, H, kWin + nc, q_dt) : 1;
   a.part = w.part;
   a.req_mode = mode;
+  if (mode == 2) { a.trim_ratio = ratio; a.pos0 = pos0; }   // dense lists stop at the visible count
   return hip_status(csa::launch_attention(a, stream));
 }
 

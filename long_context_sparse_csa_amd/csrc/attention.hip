@@ -309,6 +309,21 @@ __device__ __forceinline__ void gather_stage(uint16_t* K, int rb, const RawChunk
 
 constexpr int kMaxSlots = 1024;   // slots of one block: longer index lists are split
 
+// Tiles of a block's range.  A causal prefill's lists end with invalid slots past the visible
+// prefix (the selection pads with -1 when fewer than k entries are visible, and dense lists stop
+// at the visible count), so an unsplit block stops after the last tile that can hold a valid
+// slot: n_win + min(n_comp, (t + 1) / ratio) slots for the query at position t.  Early prefill
+// positions see few entries, so this skips about a tenth of the 8,192-query prefill's tiles.
+__device__ __forceinline__ int attn_block_tiles(const AttnArgs& a, int q, int n_tiles, int t_begin, int tps) {
+  int nt = max(0, min(n_tiles, t_begin + tps) - t_begin);
+  if (a.trim_ratio > 0 && a.req_mode == 2 && a.n_split == 1) {
+    const int64_t vis = (a.pos0 + q + 1) / a.trim_ratio;
+    const int64_t n_eff = a.n_win + (vis < a.n_comp ? vis : a.n_comp);
+    nt = min(nt, (int)((n_eff + kTile - 1) / kTile));
+  }
+  return nt;
+}
+
 typedef short v4s __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s lds_v4s;
 
@@ -408,7 +423,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   const int n_tiles = (n_idx + kTile - 1) / kTile;
   const int tps = (n_tiles + a.n_split - 1) / a.n_split;
   const int t_begin = split * tps;
-  const int nt = max(0, min(n_tiles, t_begin + tps) - t_begin);   // tiles of this block
+  const int nt = attn_block_tiles(a, q, n_tiles, t_begin, tps);   // tiles of this block
   const int r = a.req_mode == 1 ? q / a.q_per_req : (a.req_mode == 2 ? 0 : a.q_req[q]);
   const int s_begin = t_begin * kTile;
 
@@ -724,7 +739,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs
   const int n_tiles = (n_idx + kTile - 1) / kTile;
   const int tps = (n_tiles + a.n_split - 1) / a.n_split;
   const int t_begin = split * tps;
-  const int nt = max(0, min(n_tiles, t_begin + tps) - t_begin);
+  const int nt = attn_block_tiles(a, q, n_tiles, t_begin, tps);
   const int r = a.req_mode == 1 ? q / a.q_per_req : (a.req_mode == 2 ? 0 : a.q_req[q]);
 
   const int kb = wave & 1, dh = wave >> 1;   // consumer roles (waves 0-3)

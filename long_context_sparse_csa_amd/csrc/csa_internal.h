@@ -121,6 +121,10 @@ struct AttnArgs {
   int n_split;               // chosen by plan_attn_split
   int req_mode;              // 0: q_req array; 1: request = query / q_per_req (decode); 2: request 0 (prefill)
   int q_per_req = 1;
+  // causal prefill (req_mode 2) from a fused path: compressed slots at or past
+  // min(n_comp, (pos0 + q + 1) / trim_ratio) are known to be invalid (0: no such knowledge)
+  int trim_ratio = 0;
+  int64_t pos0 = 0;
   // optional: compressed slot j of query q is row rows[q * ld_rows + j] of the pool (< 0 invalid),
   // already resolved through the page table; null = resolve idx through the page table
   const int32_t* rows;
