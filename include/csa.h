@@ -9,6 +9,10 @@
  *   (3) sparse multi-query attention over [sliding-window rows ++ selected compressed rows]:
  *         out[h] = sum_j e^{S[h,j]} v_j / (sum_j e^{S[h,j]} + e^{sink[h]}),  S = scale * q[h] . v_j
  *       where K and V are the same single-head 512-dim rows and invalid index slots are skipped.
+ * Around that path the library also provides: MXFP4 (E2M1) indexer operands (CSA_FP4_E2M1),
+ * decode steps that take several tokens of each request at once (csa_decode_multi), layers whose
+ * compressed cache has no indexer and is attended whole (csa_hca_decode / csa_hca_prefill), and
+ * the compressor that writes both caches (csa_compress_kv / csa_compress_index_keys).
  *
  * Sources (pages as titled; the section is named on each declaration):
  *   [P1] "DeepSeek-V4 全面解读：架构设计与 inference/encoding 源码深度解析" (wangjunjian.com)
