@@ -354,6 +354,7 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   ia.q_req = pw.q_req; ia.n_req = mode == 1 ? rows / S : 1; ia.n_vis = pw.n_vis; ia.Q = rows; ia.HI = HI;
   ia.max_n_vis = max_n_vis; ia.logits = pw.logits; ia.ld = pw.ld; ia.hist = single ? nullptr : pw.tk.hist;
   ia.vis_mode = single ? mode : 0; ia.ctx_len = ctx_len; ia.max_ctx = max_ctx; ia.pos0 = pos0; ia.q_per_req = S;
+  ia.visible_only = true;
   CSA_HIP(csa::launch_indexer(ia, stream));
 
   csa::TopkArgs t{};

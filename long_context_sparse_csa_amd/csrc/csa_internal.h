@@ -38,6 +38,9 @@ struct IndexerArgs {
   int64_t max_ctx;
   int64_t pos0;
   int q_per_req = 1;          // decode: queries per request (query q belongs to request q / q_per_req)
+  // true inside the fused paths: only columns c < n_vis of each row are written (the selection
+  // reads nothing else); false for csa_indexer_logits, which also fills [n_vis, max_n_vis) with -inf
+  bool visible_only = false;
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
 

@@ -190,6 +190,9 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
     nv[j] = visible_count(a, q0 + j, r);   // one request: every j gives the same r
     nv_max = nv[j] > nv_max ? nv[j] : nv_max;
   }
+  // inside a fused path the selection reads only the visible prefix of each row, so a block (or
+  // a wave, below) past it has nothing to do; short rows of a ragged batch then cost nothing
+  if (a.visible_only && c_begin >= nv_max) return;
   if constexpr (HIST) {
     for (int i = tid; i < NQ * kHistBins; i += 256) lhist[i / kHistBins][i % kHistBins] = 0u;
   }
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const float score = score_page<NHG, FP4>(qa[j], qsc[j], wv[j], kb, ksc);
-      if (c < a.max_n_vis) {
+      if (c < (a.visible_only ? nv[j] : a.max_n_vis)) {
         const float v = (mapped && c0 < nv[j] && c < nv[j]) ? score : -INFINITY;
         a.logits[(int64_t)(q0 + j) * a.ld + c] = v;
         if constexpr (HIST) {
@@ -249,14 +252,16 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   // i + nbuf as soon as page i is scored, so up to nbuf pages are in flight and every wait is for
   // exactly the page about to be scored.  Pages past the wave's range load page 0 (always mapped)
   // and store nothing.
-  v8i kb[nbuf][4];
-  int ksc[nbuf];
+  if (!(a.visible_only && p_first * kPage >= nv_max)) {
+    v8i kb[nbuf][4];
+    int ksc[nbuf];
 #pragma unroll
-  for (int i = 0; i < nbuf; ++i) load_page(i, kb[i], ksc[i]);
+    for (int i = 0; i < nbuf; ++i) load_page(i, kb[i], ksc[i]);
 #pragma unroll
-  for (int i = 0; i < pages_per_wave; ++i) {
-    compute_page(i, kb[i % nbuf], ksc[i % nbuf]);
-    if (i + nbuf < pages_per_wave) load_page(i + nbuf, kb[i % nbuf], ksc[i % nbuf]);
+    for (int i = 0; i < pages_per_wave; ++i) {
+      compute_page(i, kb[i % nbuf], ksc[i % nbuf]);
+      if (i + nbuf < pages_per_wave) load_page(i + nbuf, kb[i % nbuf], ksc[i % nbuf]);
+    }
   }
   if constexpr (HIST) {
     __syncthreads();
