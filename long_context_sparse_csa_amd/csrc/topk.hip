@@ -481,8 +481,8 @@ __global__ __launch_bounds__(256) void topk_finish_kernel(TopkArgs a) {
 //   3. one block scan of the per-thread (greater, equal) counts, packed in one word, places the k
 //      indices in ascending order (equal keys at T in index order) in LDS, from where they are
 //      written with coalesced stores.
-constexpr int kSinglePer = 16;      // entries per thread, in index order
-constexpr int kSingleMax = 1024 * kSinglePer;   // longest row: 1024 threads
+constexpr int kSinglePer = 16;      // entries per thread, in index order (32 for the longest rows)
+constexpr int kSingleMax = 1024 * 32;   // longest row: 1024 threads of 32 entries
 constexpr int kCandMax = 2048;      // entries of the threshold bin resolved by one wave; more take
                                     // the block-wide path
 constexpr int kSingleMaxK = 2048;   // largest k
@@ -524,9 +524,9 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 
 // NT threads cover rows of up to 16 NT entries; short rows take a small block so that several
 // rows share a CU (LDS: 16 KB of bins + 8 KB of candidate keys / selected indices + 4 B per thread).
-template <int NT>
+template <int NT, int PER>
 __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
-  constexpr int kRowMax = NT * kSinglePer;
+  constexpr int kRowMax = NT * PER;
   const int q = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t nv = topk_row_count(a, q);
   const int k = a.k;
@@ -558,12 +558,12 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
   __shared__ uint32_t ext[2 * (NT / 64)];   // per-wave largest / smallest visible key
 
   const float* row = a.logits + (int64_t)q * a.ld;
-  const int c0 = tid * kSinglePer;          // this thread owns entries [c0, c0+16)
-  uint32_t key[kSinglePer];
+  const int c0 = tid * PER;          // this thread owns entries [c0, c0+PER)
+  uint32_t key[PER];
   {
-    float v[kSinglePer];
+    float v[PER];
 #pragma unroll
-    for (int j = 0; j < kSinglePer; j += 4) {
+    for (int j = 0; j < PER; j += 4) {
       const int c = c0 + j;
       // rows are 16-byte aligned and ld is a multiple of 4; entries past n_vis are never counted
       const float4 x = *(const float4*)(row + (c < nv ? c : 0));
@@ -573,14 +573,14 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
     for (int i = tid; i < kHistBins; i += NT) bins[i] = 0u;
     if (tid == 0) s_ncand = 0u;
 #pragma unroll
-    for (int j = 0; j < kSinglePer; ++j) key[j] = order_key(v[j]);   // entries past n_vis are never counted
+    for (int j = 0; j < PER; ++j) key[j] = order_key(v[j]);   // entries past n_vis are never counted
   }
   __syncthreads();
   // row extremes of the visible keys: per wave, then across waves after the barrier
   {
     uint32_t kmx = 0u, kmn = 0xFFFFFFFFu;
 #pragma unroll
-    for (int j = 0; j < kSinglePer; ++j) {
+    for (int j = 0; j < PER; ++j) {
       if (c0 + j < nv) {
         kmx = key[j] > kmx ? key[j] : kmx;
         kmn = key[j] < kmn ? key[j] : kmn;
@@ -619,9 +619,9 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
     const bool adaptive = kmin >= order_key(-3.40282347e+38f) && kmax <= order_key(3.40282347e+38f) &&
                           kmax > kmin && scale > 0.f && scale < 3.0e38f;
     if (adaptive) {
-      uint32_t bin[kSinglePer];
+      uint32_t bin[PER];
 #pragma unroll
-      for (int j = 0; j < kSinglePer; ++j) {
+      for (int j = 0; j < PER; ++j) {
         const float x = (key_value(key[j]) - vmin) * scale;
         // x >= 0 for visible entries; entries past n_vis (never counted) are clamped too
         const uint32_t b = x < 4095.f ? (x > 0.f ? (uint32_t)x : 0u) : 4095u;
@@ -636,7 +636,7 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
       {
         uint32_t hm = 0;
 #pragma unroll
-        for (int j = 0; j < kSinglePer; ++j) hm |= (c0 + j < nv && bin[j] == bstar) ? (1u << j) : 0u;
+        for (int j = 0; j < PER; ++j) hm |= (c0 + j < nv && bin[j] == bstar) ? (1u << j) : 0u;
         const uint32_t hits = __popc(hm);
         const uint32_t incl = wave_inclusive_scan(hits);
         uint32_t base = 0;
@@ -679,7 +679,7 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
   if (!resolved) {
     // level 1: top 12 key bits of every entry (all lanes active: one LDS atomic instruction covers 64)
   #pragma unroll
-    for (int j = 0; j < kSinglePer; ++j)
+    for (int j = 0; j < PER; ++j)
       if (c0 + j < nv) atomicAdd(&bins[key[j] >> kHistShift], 1u);
     __syncthreads();
     if (wave == 0) wave_find_desc(bins, kHistBins, (uint32_t)k, &s_digit, &s_before);
@@ -691,7 +691,7 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
     {
       uint32_t hm = 0;   // bit j: entry c0 + j is in b*
   #pragma unroll
-      for (int j = 0; j < kSinglePer; ++j) hm |= (c0 + j < nv && (key[j] >> kHistShift) == bstar) ? (1u << j) : 0u;
+      for (int j = 0; j < PER; ++j) hm |= (c0 + j < nv && (key[j] >> kHistShift) == bstar) ? (1u << j) : 0u;
       const uint32_t hits = __popc(hm);
       const uint32_t incl = wave_inclusive_scan(hits);
       uint32_t base = 0;
@@ -756,7 +756,7 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
         for (int i = tid; i < 1024; i += NT) bins[i] = 0u;
         __syncthreads();
   #pragma unroll
-        for (int j = 0; j < kSinglePer; ++j) {
+        for (int j = 0; j < PER; ++j) {
           const bool hit = c0 + j < nv && (key[j] >> (shift + 10)) == prefix;
           if (__any(hit) && hit) atomicAdd(&bins[(key[j] >> shift) & 1023u], 1u);
         }
@@ -777,7 +777,7 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
   const uint32_t need = s_need;  // the first `need` entries equal to T (in index order) are taken
   uint32_t gm = 0, em = 0;       // bit j: entry c0 + j is above T / equal to T
 #pragma unroll
-  for (int j = 0; j < kSinglePer; ++j) {
+  for (int j = 0; j < PER; ++j) {
     const bool ok = c0 + j < nv;
     gm |= (ok && key[j] > T) ? (1u << j) : 0u;
     em |= (ok && key[j] == T) ? (1u << j) : 0u;
@@ -820,11 +820,13 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
 hipError_t launch_topk_single(const TopkArgs& a, hipStream_t s) {
   ProfScope p("topk_single", s);
   if (a.max_n_vis <= 128 * kSinglePer)
-    hipLaunchKernelGGL(topk_single_kernel<128>, dim3((unsigned)a.Q), dim3(128), 0, s, a);
+    hipLaunchKernelGGL((topk_single_kernel<128, kSinglePer>), dim3((unsigned)a.Q), dim3(128), 0, s, a);
   else if (a.max_n_vis <= 256 * kSinglePer)
-    hipLaunchKernelGGL(topk_single_kernel<256>, dim3((unsigned)a.Q), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((topk_single_kernel<256, kSinglePer>), dim3((unsigned)a.Q), dim3(256), 0, s, a);
+  else if (a.max_n_vis <= 1024 * kSinglePer)
+    hipLaunchKernelGGL((topk_single_kernel<1024, kSinglePer>), dim3((unsigned)a.Q), dim3(1024), 0, s, a);
   else
-    hipLaunchKernelGGL(topk_single_kernel<1024>, dim3((unsigned)a.Q), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL((topk_single_kernel<1024, 32>), dim3((unsigned)a.Q), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 

@@ -77,11 +77,13 @@ def _fp32_score_bound(wl, qi):
 
 
 # ------------------------------------------------------------------------------------ top-k
-# Row lengths per selection path: rows longer than 16,384 entries take the multi-launch selection;
-# shorter rows take one block per query, of 1024, 256 or 128 threads for rows of up to 16,384,
-# 4,096 or 2,048 entries (the longest row of the call decides).
+# Row lengths per selection path: rows longer than 32,768 entries take the multi-launch selection;
+# shorter rows take one block per query: 1024 threads of 32 entries for rows of up to 32,768, and
+# of 16 entries with 1024, 256 or 128 threads for rows of up to 16,384, 4,096 or 2,048 entries
+# (the longest row of the call decides).
 _TOPK_LENGTHS = {
     "multi_block": ([0, 1, 511, 512, 513, 777, 5000, 70000], 9000),
+    "single_1024x32": ([0, 1, 511, 512, 513, 777, 16385, 32768], 20000),
     "single_1024": ([0, 1, 511, 512, 513, 777, 5000, 16384], 9000),
     "single_256": ([0, 1, 511, 512, 513, 777, 2049, 4096], 4000),
     "single_128": ([0, 1, 511, 512, 513, 777, 1500, 2048], 2000),
