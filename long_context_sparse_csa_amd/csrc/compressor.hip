@@ -25,8 +25,9 @@
 namespace csa {
 
 // 8 projections of a row: bf16 (one 16-byte load) or fp32 (two)
-__device__ __forceinline__ void load8(const void* base, bool bf16, int64_t off, float* v) {
-  if (bf16) {
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, int64_t off, float* v) {
+  if constexpr (BF16) {
     const uint4 w = *(const uint4*)((const uint16_t*)base + off);
     const uint32_t x[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -79,7 +80,9 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-template <int D>
+// BF16 is a template parameter so that every position's loads are straight-line code the compiler
+// can issue together (a run-time format test put a branch around each load)
+template <int D, bool BF16>
 __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   constexpr int L = D / 8;                 // lanes per entry
   constexpr int kRope = 64;
@@ -89,7 +92,6 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   const int64_t c = a.c_begin + ci;
   const bool overlap = a.ratio == 4;
   const int coff = overlap ? 2 : 1;
-  const bool bf16 = a.proj_dt == 1;
   const int f0 = 8 * lane_in;
 
   // online softmax over the window positions, per feature
@@ -104,8 +106,8 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
     const int col = half * D + f0;
     const int64_t off = (tok - a.tok0) * a.ld + col;
     float k[8], sc[8];
-    load8(a.kv, bf16, off, k);
-    load8(a.score, bf16, off, sc);
+    load8<BF16>(a.kv, off, k);
+    load8<BF16>(a.score, off, sc);
     const float4 p0 = *(const float4*)(a.ape + (int64_t)wpos * coff * D + col);
     const float4 p1 = *(const float4*)(a.ape + (int64_t)wpos * coff * D + col + 4);
     const float pe[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
@@ -264,8 +266,14 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   ProfScope p(a.D == 512 ? "compress_kv" : "compress_keys", s);
   const int per_block = 256 / (a.D / 8);   // entries per block of 256 threads
   const unsigned blocks = (unsigned)((a.c_count + per_block - 1) / per_block);
-  if (a.D == 512) hipLaunchKernelGGL(compress_kernel<512>, dim3(blocks), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(compress_kernel<128>, dim3(blocks), dim3(256), 0, s, a);
+  const bool bf16 = a.proj_dt == 1;
+  if (a.D == 512) {
+    if (bf16) hipLaunchKernelGGL((compress_kernel<512, true>), dim3(blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((compress_kernel<512, false>), dim3(blocks), dim3(256), 0, s, a);
+  } else {
+    if (bf16) hipLaunchKernelGGL((compress_kernel<128, true>), dim3(blocks), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((compress_kernel<128, false>), dim3(blocks), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
