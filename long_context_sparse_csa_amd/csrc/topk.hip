@@ -60,6 +60,21 @@ __device__ __forceinline__ void write_window(const TopkArgs& a, int q) {
   a.idx[(int64_t)q * a.ld_idx - kWin + j] = v;
 }
 
+// Largest uint32 over the 64 lanes, with DPP moves inside each 16-lane row (quad permutations
+// for strides 1 and 2, row rotations for 4 and 8) and the cross-row lane swaps for 16 and 32: no
+// LDS-routed shuffle (a chain of those measured about a microsecond per block-wide reduction).
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+  auto mx = [](uint32_t p, uint32_t q) { return p > q ? p : q; };
+  x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+  x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+  x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false));  // row_ror:4
+  x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));  // row_ror:8
+  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = mx(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return mx(r[0], r[1]);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves (VALU only, no LDS crossbar):
 // shifts by 1, 2, 4, 8 inside each row of 16 lanes, then row 0's and row 2's totals broadcast into
 // rows 1 and 3, then the total of rows 0-1 into rows 2 and 3.  Lanes without a source add 0.
@@ -586,12 +601,8 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
         kmn = key[j] < kmn ? key[j] : kmn;
       }
     }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const uint32_t a1 = (uint32_t)__shfl_xor((int)kmx, m), b1 = (uint32_t)__shfl_xor((int)kmn, m);
-      kmx = a1 > kmx ? a1 : kmx;
-      kmn = b1 < kmn ? b1 : kmn;
-    }
+    kmx = wave_umax(kmx);
+    kmn = ~wave_umax(~kmn);   // min through the max of complements
     if (lane == 0) {
       ext[wave] = kmx;
       ext[NT / 64 + wave] = kmn;
