@@ -45,16 +45,26 @@ __device__ __forceinline__ v4f mma_scaled(const v8i& a, const v8i& b, int sa, in
 // compiler first quiets possible signalling NaNs of the matrix-core result.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-template <bool FP4>
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// 16 bytes, optionally as a non-temporal load: decode keys are read exactly once, so streaming
+// them without keeping them in L2 leaves the L2 to the score rows the selection reads next
+template <bool NT>
+__device__ __forceinline__ v4u load16(const uint8_t* p) {
+  if constexpr (NT) return __builtin_nontemporal_load((const v4u*)p);
+  else return *(const v4u*)p;
+}
+
+template <bool FP4, bool NT = false>
 __device__ __forceinline__ v8i load_k_operand(const uint8_t* row, int g) {
-  const uint4 lo = *(const uint4*)(row + 16 * g);
+  const v4u lo = load16<NT>(row + 16 * g);
   v8i r;
-  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
+  r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
   if constexpr (FP4) {
     r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
   } else {
-    const uint4 hi = *(const uint4*)(row + 64 + 16 * g);
-    r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+    const v4u hi = load16<NT>(row + 64 + 16 * g);
+    r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
   }
   return r;
 }
@@ -228,7 +238,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
     const uint8_t* kp = keys + (int64_t)pid * (kPage * kRowB<FP4>);
     ksc = *(const int*)(a.kscale + (int64_t)pid * 256 + 4 * lane);
 #pragma unroll
-    for (int kg = 0; kg < 4; ++kg) kb[kg] = load_k_operand<FP4>(kp + (4 * n + kg) * kRowB<FP4>, g);
+    for (int kg = 0; kg < 4; ++kg) kb[kg] = load_k_operand<FP4, true>(kp + (4 * n + kg) * kRowB<FP4>, g);
   };
 
   auto compute_page = [&](int i, const v8i* kb, int ksc) {
