@@ -82,11 +82,18 @@ typedef struct {
 } csa_paged_kv;
 
 /* Paged indexer key cache (same page mapping as csa_paged_kv).
- *   dt = CSA_FP8_E4M3FN: keys [num_pages][64][128] e4m3fn bytes; scales [num_pages][4][64] E8M0
- *        bytes, scales[p][b][s] scaling dims [32b, 32b+32) of slot s (value 2^(e-127)).
- *   dt = CSA_FP4_E2M1: keys [num_pages][64][64] bytes, two E2M1 codes per byte; scales as for
- *        CSA_FP8_E4M3FN (one E8M0 byte per 32 dims).
- *   dt = CSA_F32: keys [num_pages][64][128] fp32; scales must be NULL.                          */
+ *   dt = CSA_FP8_E4M3FN: keys [num_pages][8192] e4m3fn bytes, one page of 64 slots x 128 dims in
+ *        operand order (below); scales [num_pages][4][64] E8M0 bytes, scales[p][b][s] scaling
+ *        dims [32b, 32b+32) of slot s (value 2^(e-127)).
+ *   dt = CSA_FP4_E2M1: keys [num_pages][4096] bytes (64 slots x 64 bytes, two E2M1 codes per
+ *        byte) in operand order; scales as for CSA_FP8_E4M3FN (one E8M0 byte per 32 dims).
+ *   dt = CSA_F32: keys [num_pages][64][128] fp32, row-major; scales must be NULL.
+ * Operand order: with R = 128 (FP8) or 64 (FP4) bytes per slot and halves = R / 64, byte b of
+ * slot s sits at page byte ((s % 4) * halves + b / 64) * 1024 + (s / 4 + 16 * ((b % 64) / 16)) * 16
+ * + b % 16.  Each kilobyte of a page is then one 16-byte chunk for each of the 64 lanes of a
+ * matrix-core operand, so the indexer reads every page with contiguous 1 KB loads.
+ * csa_compress_index_keys writes this order; pack_index_keys() in the Python package converts
+ * row-major [P][64][R] bytes to it.                                                            */
 typedef struct {
   const void* keys;
   const uint8_t* scales;
@@ -284,7 +291,8 @@ csa_status csa_hca_prefill(int32_t Q, int32_t H, const void* q, int32_t q_dt, co
  * csa_compress_kv: D = 512; pool_rows [num_pages][64][row bytes] in pool_fmt (csa_kv_format):
  *   FP8NOPE_BF16ROPE rows quantise the 448 nope features per 64 with scale max(amax,1e-4)/448.
  * csa_compress_index_keys: D = 128, then the scaled Hadamard rotation of the row, then key_dt
- *   CSA_FP8_E4M3FN (keys [P][64][128]) or CSA_FP4_E2M1 (keys [P][64][64]) with one E8M0 scale
+ *   CSA_FP8_E4M3FN (keys: 8 KB pages) or CSA_FP4_E2M1 (4 KB pages), in the operand order of
+ *   csa_paged_idx, with one E8M0 scale
  *   per 32 features in scales [P][4][64]: 2^ceil(log2(max(amax,1e-4)/448)) for FP8,
  *   2^ceil(log2(max(amax,6*2^-126)/6)) for FP4.
  * Ranges: ratio 4 or 128; ld_proj >= coff * D, a multiple of 8; c_begin + c_count <= 64 *

@@ -12,3 +12,4 @@ from .binding import (  # noqa: F401
     csa_sparse_attn_workspace_bytes, csa_status_string, csa_topk, csa_topk_workspace_bytes, lib, paged_idx,
     paged_kv,
 )
+from .layout import pack_index_keys, unpack_index_keys  # noqa: F401

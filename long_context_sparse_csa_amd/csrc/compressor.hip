@@ -82,6 +82,16 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // BF16 is a template parameter so that every position's loads are straight-line code the compiler
 // can issue together (a run-time format test put a branch around each load)
+// Byte offset of byte b of key row r (0..63) of index-key page pid in the operand-order page the
+// indexer reads (FP8: 128-byte rows, FP4: 64-byte rows): row r = 4n + kg and bytes
+// [64h + 16g, +16) form the 16-byte chunk of lane n + 16g in kilobyte kg·halves + h.
+template <bool FP4>
+__device__ __forceinline__ int64_t key_byte(int pid, int r, int b) {
+  constexpr int halves = FP4 ? 1 : 2;
+  const int kg = r & 3, n = r >> 2, h = b >> 6, g = (b >> 4) & 3;
+  return (int64_t)pid * (kPage * 64 * halves) + (kg * halves + h) * 1024 + (n + 16 * g) * 16 + (b & 15);
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
   constexpr int L = D / 8;                 // lanes per entry
@@ -166,10 +176,9 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
 
   const int pid = a.page_table[c >> 6];
   const bool mapped = (unsigned)pid < (unsigned)a.num_pages;
-  const int64_t slot_row = (int64_t)pid * kPage + (c & (kPage - 1));
 
   if constexpr (D == 512) {
-    uint8_t* row = a.out + slot_row * row_bytes(a.out_fmt);
+    uint8_t* row = a.out + ((int64_t)pid * kPage + (c & (kPage - 1))) * row_bytes(a.out_fmt);
     if (a.out_fmt == kRowF32) {
       if (mapped) {
         *(float4*)(row + 4 * f0) = make_float4(y[0], y[1], y[2], y[3]);
@@ -245,7 +254,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
         uint32_t w = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) w |= e2m1_code(y[e] * q) << (4 * e);
-        *(uint32_t*)(a.out + slot_row * 64 + f0 / 2) = w;
+        *(uint32_t*)(a.out + key_byte<true>(pid, c & (kPage - 1), f0 / 2)) = w;
       } else {
         uint32_t w[2];
 #pragma unroll
@@ -254,7 +263,7 @@ __global__ __launch_bounds__(256) void compress_kernel(CompressArgs a) {
           v = __builtin_amdgcn_cvt_pk_fp8_f32(y[4 * h + 2] * q, y[4 * h + 3] * q, v, true);
           w[h] = (uint32_t)v;
         }
-        *(uint2*)(a.out + slot_row * 128 + f0) = make_uint2(w[0], w[1]);
+        *(uint2*)(a.out + key_byte<false>(pid, c & (kPage - 1), f0)) = make_uint2(w[0], w[1]);
       }
       if ((lane_in & 3) == 0) a.out_scales[(int64_t)pid * 256 + (f0 >> 5) * kPage + (c & (kPage - 1))] = (uint8_t)ex;
     }

@@ -55,15 +55,37 @@ __device__ __forceinline__ v4u load16(const uint8_t* p) {
   else return *(const v4u*)p;
 }
 
-template <bool FP4, bool NT = false>
-__device__ __forceinline__ v8i load_k_operand(const uint8_t* row, int g) {
-  const v4u lo = load16<NT>(row + 16 * g);
+// One row-major 128-dim row (a query head) as a scaled-MFMA operand: lane (n, g) takes bytes
+// [16g, 16g+16) and, for FP8, [64+16g, 64+16g+16) of its row (the same split as the keys below)
+template <bool FP4>
+__device__ __forceinline__ v8i load_row_operand(const uint8_t* row, int g) {
+  const v4u lo = load16<false>(row + 16 * g);
   v8i r;
   r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
   if constexpr (FP4) {
     r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
   } else {
-    const v4u hi = load16<NT>(row + 64 + 16 * g);
+    const v4u hi = load16<false>(row + 64 + 16 * g);
+    r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
+  }
+  return r;
+}
+
+// Index-key pages are stored in operand order: the 16 bytes that lane L = n + 16g takes for key
+// group kg and half h (row 4n + kg, bytes [64h + 16g, +16)) sit at byte (kg·halves + h)·1024 + 16L
+// of the page, so every load instruction of a page reads one contiguous kilobyte (a row-major
+// page would touch sixteen 128-byte lines per quarter-wave instead of two).  `lane_base` is the
+// page address plus 16·lane; loads are non-temporal.
+template <bool FP4>
+__device__ __forceinline__ v8i load_key_operand(const uint8_t* lane_base, int kg) {
+  constexpr int halves = FP4 ? 1 : 2;
+  const v4u lo = load16<true>(lane_base + kg * halves * 1024);
+  v8i r;
+  r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+  if constexpr (FP4) {
+    r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
+  } else {
+    const v4u hi = load16<true>(lane_base + (kg * halves + 1) * 1024);
     r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
   }
   return r;
@@ -108,7 +130,7 @@ __device__ __forceinline__ void load_query(const IndexerArgs& a, int q, int n, i
   for (int hg = 0; hg < NHG; ++hg) {
     const int h = 16 * hg + n;
     const int hc = h < a.HI ? h : a.HI - 1;
-    const v8i v = load_k_operand<FP4>(qb + hc * kRowB<FP4>, g);
+    const v8i v = load_row_operand<FP4>(qb + hc * kRowB<FP4>, g);
     const int sb = (int)a.qI_scale[((int64_t)q * a.HI + hc) * 4 + g];
     const bool ok = h < a.HI;
 #pragma unroll
@@ -235,10 +257,10 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   auto load_page = [&](int i, v8i* kb, int& ksc) {
     int pid = __builtin_amdgcn_readlane(my_pid, i);
     pid = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
-    const uint8_t* kp = keys + (int64_t)pid * (kPage * kRowB<FP4>);
+    const uint8_t* kp = keys + (int64_t)pid * (kPage * kRowB<FP4>) + 16 * lane;
     ksc = *(const int*)(a.kscale + (int64_t)pid * 256 + 4 * lane);
 #pragma unroll
-    for (int kg = 0; kg < 4; ++kg) kb[kg] = load_k_operand<FP4, true>(kp + (4 * n + kg) * kRowB<FP4>, g);
+    for (int kg = 0; kg < 4; ++kg) kb[kg] = load_key_operand<FP4>(kp, kg);
   };
 
   auto compute_page = [&](int i, const v8i* kb, int ksc) {
@@ -341,19 +363,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     pid_s[tid] = pid;
   }
   __syncthreads();
-  // wave w stages pages w and w + 4: 4 x kHalves 1 KB loads per page (load j fills key group
-  // j / kHalves, half j % kHalves: lane L takes row 4 (L % 16) + kg, bytes 16 (L / 16) + 64 half),
-  // then the page's 256 scale bytes
+  // wave w stages pages w and w + 4: 4 x kHalves contiguous 1 KB loads per page (the page is in
+  // operand order, so load j is key group j / kHalves, half j % kHalves), then its 256 scale bytes
   const uint8_t* keys = (const uint8_t*)a.keys;
   for (int pg = wave; pg < kPfPages; pg += 4) {
     int pid = pid_s[pg];
     pid = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
-    const uint8_t* kp = keys + (int64_t)pid * (kPage * kRow) + (4 * n) * kRow + 16 * g;
+    const uint8_t* kp = keys + (int64_t)pid * (kPage * kRow) + 16 * lane;
 #pragma unroll
     for (int j = 0; j < 4 * kHalves; ++j) {
       const int kg = j / kHalves, half = j % kHalves;
-      const uint8_t* src = kp + kg * kRow + 64 * half;
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)&kl[pg][kg][half][0][0], 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(kp + 1024 * j), (lds_ptr_t)&kl[pg][kg][half][0][0], 16, 0, 0);
     }
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)(a.kscale + (int64_t)pid * 256 + 4 * lane),
                                      (lds_ptr_t)&sl[pg][0], 4, 0, 0);

@@ -6,6 +6,8 @@ from types import SimpleNamespace
 import numpy as np
 import torch
 
+import long_context_sparse_csa_amd as csa
+
 from .configs import DT_F32, Workload
 
 
@@ -23,7 +25,8 @@ def to_device(wl: Workload, device="cuda") -> SimpleNamespace:
     d.qI = _t(wl.qI, device)
     d.qI_scale = None if wl.qI_scale is None else _t(wl.qI_scale, device)
     d.w = _t(wl.w, device)
-    d.ik_keys = _t(wl.ik_keys, device)
+    # FP8 / FP4 key pages go to the device in the library's operand order
+    d.ik_keys = _t(wl.ik_keys if wl.idx_dt == DT_F32 else csa.pack_index_keys(wl.ik_keys), device)
     d.ik_scales = None if wl.ik_scales is None else _t(wl.ik_scales, device)
     d.kv_pool = _t(wl.kv_pool, device)
     d.win_rows = _t(wl.win_rows, device)
