@@ -55,6 +55,32 @@ def test_indexer_scores(dev, HI, idx_dt):
         assert np.all(np.isneginf(logits[qi, nv:wl.max_n_vis])), f"query {qi}: tail not -inf"
 
 
+@pytest.mark.parametrize("key_dt", [configs.DT_FP8, configs.DT_FP4])
+def test_indexer_reads_compressor_pages(dev, key_dt):
+    """Key pages as csa_compress_index_keys leaves them on the device feed csa_indexer_logits
+    unchanged, so the writer and the reader agree on the page order; the oracle scores the same
+    pages read back and unpacked to rows."""
+    import dataclasses
+    import long_context_sparse_csa_amd as csa
+    run, tio = _run()
+    ci = configs.make_compressor("keys_to_indexer", 300 * 4, 4, D=128, seed=7 + key_dt)
+    n = ci.n_entries
+    _say(f"compressor pages -> indexer key_dt={key_dt} entries={n}")
+    page_row, (keys_d, scales_d) = run.compress(ci, "keys", key_dt, 0, n, dev, seed=4, device_out=True)
+    base = configs.make_decode("idx_from_compressor", [4 * n + 3], H=16, HI=64, idx_dt=key_dt, seed=12)
+    wl = dataclasses.replace(base, ik_keys=csa.unpack_index_keys(keys_d.cpu().numpy()),
+                             ik_scales=scales_d.cpu().numpy(), page_table=page_row[None, :].astype(np.int32))
+    assert int(wl.n_vis[0]) == n and wl.page_table.shape == base.page_table.shape
+    d = tio.to_device(wl, dev)
+    d.ik_keys, d.ik_scales = keys_d, scales_d          # the compressor's own device pages
+    logits = run.indexer(wl, d).cpu().numpy()
+    ref = O.query_scores(wl, 0)
+    err = np.abs(logits[0, :n].astype(np.float64) - ref)
+    bound = _fp32_score_bound(wl, 0)
+    assert np.all(err <= bound), f"max err {err.max():.3e}, worst ratio {(err / bound).max():.2f}"
+    _say(f"max err {err.max():.2e}, max err/bound {(err / bound).max():.3f}")
+
+
 def _fp32_score_bound(wl, qi):
     """Forward error bound of the score computed in fp32 from exact fp8 products: each head logit sums
     128 products (error <= 128 u sum|q_d k_d|), the weighted head sum adds HI more roundings.  u=2^-24."""

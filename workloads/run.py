@@ -131,10 +131,12 @@ def hca_prefill(wl: Workload, d, out=None, ws=None, stream=None):
 
 
 def compress(ci, kind: str, out_fmt: int, c_begin: int, c_count: int, device="cuda", tok0: int = 0,
-             n_tok: int | None = None, num_pages: int | None = None, page_row=None, seed: int = 0, stream=None):
+             n_tok: int | None = None, num_pages: int | None = None, page_row=None, seed: int = 0, stream=None,
+             device_out: bool = False):
     """csa_compress_kv (kind "kv") or csa_compress_index_keys (kind "keys") for entries c_begin ..
     c_begin+c_count-1 of a compressor workload, projections rows tok0 .. tok0+n_tok-1 uploaded.
-    Returns (page_row numpy, pool outputs as numpy: rows, or (row-major keys, scales))."""
+    Returns (page_row numpy, pool outputs as numpy: rows, or (row-major keys, scales)); with
+    device_out the pool tensors stay on the device as written (key pages in the library's order)."""
     import numpy as np
     n_tok = ci.T - tok0 if n_tok is None else n_tok
     need_pages = (c_begin + c_count + 63) // 64
@@ -160,4 +162,6 @@ def compress(ci, kind: str, out_fmt: int, c_begin: int, c_count: int, device="cu
     csa.csa_compress_index_keys(kv, sc, ci.proj_dt, ci.kv_tok.shape[1], tok0, n_tok, ci.ratio, ape, w, ci.eps, cs, sn,
                                 c_begin, c_count, keys, scales, out_fmt, num_pages, pt, len(page_row), stream)
     torch.cuda.synchronize()
+    if device_out:
+        return page_row, (keys, scales)
     return page_row, (csa.unpack_index_keys(keys.cpu().numpy()), scales.cpu().numpy())
