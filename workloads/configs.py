@@ -12,7 +12,7 @@ Layouts (little-endian, C order), shared with ``include/csa.h``:
 * ``sink``         [H]           float32
 * ``qI``           [Q][HI][128]  fp8 e4m3fn codes (uint8) or float32;  ``qI_scale`` [Q][HI][4] E8M0
 * ``w``            [Q][HI]       float32 (already carries softmax_scale * HI**-0.5)
-* ``ik_keys``      [P][64][128]  fp8 codes or float32;  ``ik_scales`` [P][4][64] E8M0 (block-major)
+* ``ik_keys``      [P][64][128]  fp8 codes or float32, row-major (uploads pack fp8 / fp4 pages into the library's operand order);  ``ik_scales`` [P][4][64] E8M0 (block-major)
 * ``kv_pool``      [P][64][row_bytes]  KV rows (see workloads.codec)
 * ``win_rows``     [B][Wr][row_bytes]  window source (a 128-slot ring at decode, raw rows at prefill)
 * ``page_table``   [B][max_pages] int32, -1 for unused entries; entry c of request b lives in page
