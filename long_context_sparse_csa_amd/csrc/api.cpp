@@ -383,6 +383,7 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   a.req_mode = mode;
   a.q_per_req = S;
   if (mode == 2) { a.trim_ratio = 4; a.pos0 = pos0; }   // selection pads past min(n_vis, k) with -1
+  a.stream_rows = mode == 1 && S == 1;   // one query per request: each row is gathered once
   if (single) { a.rows = pw.rows; a.ld_rows = k; }
   return hip_status(csa::launch_attention(a, stream));
 }
@@ -526,6 +527,7 @@ csa_status run_hca(int mode, int32_t rows, int32_t H, const void* q, int32_t q_d
   a.part = w.part;
   a.req_mode = mode;
   if (mode == 2) { a.trim_ratio = ratio; a.pos0 = pos0; }   // dense lists stop at the visible count
+  a.stream_rows = mode == 1;   // decode: each request's rows belong to its one query
   return hip_status(csa::launch_attention(a, stream));
 }
 

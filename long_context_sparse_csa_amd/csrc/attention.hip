@@ -220,7 +220,9 @@ struct RawChunk {
   v2u lo, hi;
 };
 
-template <int WF, int CF>
+// NTG: non-temporal loads, for paths where no row is read by two queries (decode with one query per
+// request); a prefill re-reads each row for many queries and keeps the cached loads
+template <int WF, int CF, bool NTG>
 __device__ __forceinline__ RawChunk load_raw(uint64_t code, int dc) {
   const int fmt = (code & kCodeComp) ? CF : WF;
   const gbytes rp = (gbytes)(uintptr_t)(code & kCodeAddrMask);
@@ -231,8 +233,13 @@ __device__ __forceinline__ RawChunk load_raw(uint64_t code, int dc) {
     o1 = nope ? 576 + 8 * (dc >> 4) : 16 * dc - kNope + 8;
   }
   RawChunk r;
-  r.lo = *(gv2u)(rp + o0);
-  r.hi = *(gv2u)(rp + o1);
+  if constexpr (NTG) {
+    r.lo = __builtin_nontemporal_load((gv2u)(rp + o0));
+    r.hi = __builtin_nontemporal_load((gv2u)(rp + o1));
+  } else {
+    r.lo = *(gv2u)(rp + o0);
+    r.hi = *(gv2u)(rp + o1);
+  }
   return r;
 }
 
@@ -287,7 +294,7 @@ __device__ __forceinline__ void gather_codes(const AttnArgs& a, int q, int r, in
 }
 
 // Issue the loads of the wave's four rows of tile k (codes picked from VGPRs with lane reads).
-template <int WF, int CF>
+template <int WF, int CF, bool NTG>
 __device__ __forceinline__ void gather_fetch(int k, const uint32_t* cw_lo, const uint32_t* cw_hi, int lane,
                                              RawChunk* rw, uint64_t* c4) {
   const uint32_t lo = (k >> 4) ? cw_lo[1] : cw_lo[0], hi = (k >> 4) ? cw_hi[1] : cw_hi[0];
@@ -297,7 +304,7 @@ __device__ __forceinline__ void gather_fetch(int k, const uint32_t* cw_lo, const
     c4[i] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane(hi, l0 + i) << 32) |
             (uint32_t)__builtin_amdgcn_readlane(lo, l0 + i);   // zero-extended: the lane read is an int
 #pragma unroll
-  for (int i = 0; i < 4; ++i) rw[i] = load_raw<WF, CF>(c4[i], lane);
+  for (int i = 0; i < 4; ++i) rw[i] = load_raw<WF, CF, NTG>(c4[i], lane);
 }
 
 // Write the wave's four rows of a tile into the LDS tile K (dequantised to bf16).
@@ -348,7 +355,7 @@ constexpr int kScoreDepth = CSA_SCORE_DEPTH;   // the same for the score waves o
 // and dequantises tile j into ring buffer j % 3 just before barrier j, for j < nt.  The consumers
 // read tile j after barrier j and are done with it before barrier j + 2, so the buffer is free
 // again when tile j + 3 is staged.  The producers pass `nbar` >= nt + 1 barriers in all.
-template <int WF, int CF>
+template <int WF, int CF, bool NTG>
 __device__ __forceinline__ void produce_tiles(const uint64_t* codes, uint16_t (*Kr)[kTile * kKrStride], int nt,
                                               int nbar, int lane, int wave) {
   const int pw = wave - 4;
@@ -363,7 +370,7 @@ __device__ __forceinline__ void produce_tiles(const uint64_t* codes, uint16_t (*
       c8[i + 1] = ((uint64_t)__builtin_amdgcn_readfirstlane(c.w) << 32) | (uint32_t)__builtin_amdgcn_readfirstlane(c.z);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) rw[i] = load_raw<WF, CF>(c8[i], lane);
+    for (int i = 0; i < 8; ++i) rw[i] = load_raw<WF, CF, NTG>(c8[i], lane);
   };
   auto stage = [&](int buf, const RawChunk* rw, const uint64_t* c8) {
 #pragma unroll
@@ -398,7 +405,7 @@ __device__ __forceinline__ void produce_tiles(const uint64_t* codes, uint16_t (*
   for (int j = nt + 1; j < nbar; ++j) __syncthreads();
 }
 
-template <int WF, int CF>
+template <int WF, int CF, bool NTG>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -461,7 +468,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
     gather_codes(a, q, r, s_begin, nt, n_idx, rb, lane, cw_lo, cw_hi, &vm8[0][0], wave);
     RawChunk raw[kScoreDepth][4];
     uint64_t rc[kScoreDepth][4];
-    auto fetch = [&](int t, RawChunk* rw, uint64_t* c4) { gather_fetch<WF, CF>(t, cw_lo, cw_hi, lane, rw, c4); };
+    auto fetch = [&](int t, RawChunk* rw, uint64_t* c4) { gather_fetch<WF, CF, NTG>(t, cw_lo, cw_hi, lane, rw, c4); };
     auto stage = [&](uint16_t* K, const RawChunk* rw, const uint64_t* c4) { gather_stage<WF, CF>(K, rb, rw, c4, lane); };
     // partial S^T[key][head] over this wave's 256 dims for keys 0..15 ([0]) and 16..31 ([1]), of
     // head group w (so) and w ^ 1 (sx)
@@ -579,9 +586,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
     RawChunk raw[4];
     uint64_t rc[4];
     if (nt > 0) {
-      gather_fetch<WF, CF>(0, cw_lo, cw_hi, lane, raw, rc);
+      gather_fetch<WF, CF, NTG>(0, cw_lo, cw_hi, lane, raw, rc);
       gather_stage<WF, CF>(Kr[0], rb, raw, rc, lane);
-      if (nt > 1) gather_fetch<WF, CF>(1, cw_lo, cw_hi, lane, raw, rc);
+      if (nt > 1) gather_fetch<WF, CF, NTG>(1, cw_lo, cw_hi, lane, raw, rc);
     }
     __syncthreads();
     for (int p = 0; p <= nt + 1; ++p) {
@@ -618,7 +625,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
       }
       if (p + 1 < nt) {
         gather_stage<WF, CF>(Kr[(p + 1) & 3], rb, raw, rc, lane);
-        if (p + 2 < nt) gather_fetch<WF, CF>(p + 2, cw_lo, cw_hi, lane, raw, rc);
+        if (p + 2 < nt) gather_fetch<WF, CF, NTG>(p + 2, cw_lo, cw_hi, lane, raw, rc);
       }
       __syncthreads();
     }
@@ -719,7 +726,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
 // every consumer runs the same softmax on the summed scores, so P^T and the rescale factors never
 // cross waves.  Consumer c then accumulates output dims [128c, 128c+128).  One barrier per tile:
 // iteration k runs the softmax and P.V of tile k and the partial scores of tile k+1.
-template <int WF, int CF>
+template <int WF, int CF, bool NTG>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -760,7 +767,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs
   for (int dt = 0; dt < 8; ++dt) acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
 
   if (wave >= 4) {
-    produce_tiles<WF, CF>(codes, Kr, nt, nt + 2, lane, wave);
+    produce_tiles<WF, CF, NTG>(codes, Kr, nt, nt + 2, lane, wave);
   } else {
     const float sc = a.softmax_scale * kLog2e;
     // partial S^T[key 16 kb + 4g + i][head h] over this consumer's 256 dims
@@ -1109,17 +1116,20 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   {
     ProfScope p("attn_bf16", s);
     const dim3 grid((unsigned)(a.Q * a.n_split), (unsigned)hchunks);
-#define CSA_ATTN_LAUNCH(K)                                                                                    \
-  if (wf == kRowFP8 && cf == kRowFP8) hipLaunchKernelGGL((K<kRowFP8, kRowFP8>), grid, dim3(kAttnThreads), 0, s, a); \
-  else if (wf == kRowFP8) hipLaunchKernelGGL((K<kRowFP8, kRowBF16>), grid, dim3(kAttnThreads), 0, s, a);           \
-  else if (cf == kRowFP8) hipLaunchKernelGGL((K<kRowBF16, kRowFP8>), grid, dim3(kAttnThreads), 0, s, a);           \
-  else hipLaunchKernelGGL((K<kRowBF16, kRowBF16>), grid, dim3(kAttnThreads), 0, s, a);
+#define CSA_ATTN_FMT(K, NTG)                                                                                          \
+  if (wf == kRowFP8 && cf == kRowFP8) hipLaunchKernelGGL((K<kRowFP8, kRowFP8, NTG>), grid, dim3(kAttnThreads), 0, s, a); \
+  else if (wf == kRowFP8) hipLaunchKernelGGL((K<kRowFP8, kRowBF16, NTG>), grid, dim3(kAttnThreads), 0, s, a);           \
+  else if (cf == kRowFP8) hipLaunchKernelGGL((K<kRowBF16, kRowFP8, NTG>), grid, dim3(kAttnThreads), 0, s, a);           \
+  else hipLaunchKernelGGL((K<kRowBF16, kRowBF16, NTG>), grid, dim3(kAttnThreads), 0, s, a);
+#define CSA_ATTN_LAUNCH(K) \
+  if (a.stream_rows) { CSA_ATTN_FMT(K, true) } else { CSA_ATTN_FMT(K, false) }
     if (hb == 16) {
       CSA_ATTN_LAUNCH(attn_bf16_h16_kernel)
     } else {
       CSA_ATTN_LAUNCH(attn_bf16_kernel)
     }
 #undef CSA_ATTN_LAUNCH
+#undef CSA_ATTN_FMT
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;

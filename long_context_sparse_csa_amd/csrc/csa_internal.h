@@ -128,6 +128,9 @@ struct AttnArgs {
   // min(n_comp, (pos0 + q + 1) / trim_ratio) are known to be invalid (0: no such knowledge)
   int trim_ratio = 0;
   int64_t pos0 = 0;
+  // no row is gathered for two queries (decode, one query per request): rows are streamed with
+  // non-temporal loads
+  bool stream_rows = false;
   // optional: compressed slot j of query q is row rows[q * ld_rows + j] of the pool (< 0 invalid),
   // already resolved through the page table; null = resolve idx through the page table
   const int32_t* rows;
