@@ -276,7 +276,7 @@ def bench_compress(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "the benchmark measures one GPU; --gpus must be 1 (the path is not sharded across GPUs)"}))
         sys.exit(2)
     if args.config == "compress":
         bench_compress(args)

@@ -51,7 +51,7 @@ typedef enum {
   CSA_ERR_DTYPE = -3,       /* unknown or unsupported dtype / format code                       */
   CSA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                                 */
   CSA_ERR_WORKSPACE = -5,   /* ws is NULL or smaller than the *_workspace_bytes query            */
-  CSA_ERR_UNSUPPORTED = -6, /* a valid combination this build does not implement                */
+  CSA_ERR_UNSUPPORTED = -6, /* a valid combination the library does not implement             */
   CSA_ERR_HIP = -7          /* a HIP launch failed; csa_last_hip_error() holds the hipError_t   */
 } csa_status;
 
