@@ -52,14 +52,22 @@ def _counter(path, counter):
     return vals
 
 
+def _last_copies(path, counter, n=3):
+    rows = [r for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and "copy" in r["Kernel_Name"].lower()]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    vals = [float(r["Counter_Value"]) for r in rows[-n:]]
+    return sum(vals) / len(vals)
+
+
 def traffic(fetch_csv, write_csv, copy_bytes, config, out, cmd):
     copy_bytes = int(copy_bytes)
     f = _counter(fetch_csv, "FETCH_SIZE")
     w = _counter(write_csv, "WRITE_SIZE")
-    copy_k = [k for k in f if "copyBuffer" in k or "copy" in k.lower()]
-    # the calibration copies are the largest copy dispatches of the run
-    fc = max(max(f[k]) for k in copy_k)
-    wc = max(max(w[k]) for k in copy_k if k in w)
+    # the calibration copies are the last three copy dispatches of the run (bench.py issues them after
+    # all timed work; the workload's own input copies, some larger, come before)
+    fc = _last_copies(fetch_csv, "FETCH_SIZE")
+    wc = _last_copies(write_csv, "WRITE_SIZE")
     f_scale = copy_bytes / (fc * 1024.0)
     w_scale = copy_bytes / (wc * 1024.0)
     res = {"command": cmd, "config": config, "copy_bytes": copy_bytes,
@@ -70,9 +78,10 @@ def traffic(fetch_csv, write_csv, copy_bytes, config, out, cmd):
         fb = sum(f[k]) / len(f[k]) * 1024.0 * f_scale
         wb = sum(w.get(k, [0.0])) / max(1, len(w.get(k, []))) * 1024.0 * w_scale
         res["kernels"][k] = {"fetch_bytes": int(fb), "write_bytes": int(wb), "dispatches": len(f[k])}
+    # the last indexer kernel to appear is the one bench.py's roofline launches time back to back
     idx = [k for k in res["kernels"] if "indexer_fp8" in k]
     if idx:
-        k = idx[0]
+        k = idx[-1]
         res["bytes_per_launch"] = res["kernels"][k]["fetch_bytes"] + res["kernels"][k]["write_bytes"]
         res["kernel"] = k
     res["kernel_source_sha256_16"] = kernel_source_hash()
