@@ -33,10 +33,7 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *srcs, "-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,6 +42,25 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel: one hipcc per file), then link the library.
+    Each translation unit carries its own gfx950 code object; no device symbol crosses files."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
+    jobs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        jobs.append((obj, [hipcc(), *compile_flags, "-I", os.path.join(ROOT, "include"), "-c",
+                           os.path.join(CSRC, src), "-o", obj]))
+    with ThreadPoolExecutor(min(len(jobs), max(1, os.cpu_count() or 1))) as ex:
+        list(ex.map(lambda j: _run(j[1], verbose), jobs))
+    tmp = LIB + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *[o for o, _ in jobs], "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

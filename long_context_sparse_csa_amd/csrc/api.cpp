@@ -4,6 +4,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -19,7 +20,11 @@ thread_local int32_t g_last_hip = 0;
 struct ProfRec {
   std::string name;
   hipEvent_t start, stop;
+  bool used;   // attached to a launch
 };
+// Diagnostics only (csa_profile_*): the one piece of process-wide mutable state, guarded by a mutex
+// so that calls from several host threads may record at once.
+std::mutex g_prof_mu;
 bool g_prof_on = false;
 std::vector<ProfRec> g_prof;
 
@@ -147,22 +152,27 @@ csa_status check_attn_common(const void* q, int32_t q_dt, int32_t H, const float
 
 namespace csa {
 
-ProfScope::ProfScope(const char* name, hipStream_t s) : slot(-1), stream(s) {
+ProfScope::ProfScope(const char* name, hipStream_t) : slot(-1) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
   if (!g_prof_on) return;
   ProfRec r;
   r.name = name;
+  r.used = false;
   if (hipEventCreate(&r.start) != hipSuccess) return;
   if (hipEventCreate(&r.stop) != hipSuccess) {
     (void)hipEventDestroy(r.start);
     return;
   }
-  (void)hipEventRecord(r.start, s);
   g_prof.push_back(r);
   slot = (int)g_prof.size() - 1;
+  ev0 = r.start;
+  ev1 = r.stop;
 }
 
-ProfScope::~ProfScope() {
-  if (slot >= 0) (void)hipEventRecord(g_prof[slot].stop, stream);
+void ProfScope::mark() {
+  if (slot < 0) return;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (slot < (int)g_prof.size()) g_prof[slot].used = true;
 }
 
 }  // namespace csa
@@ -186,13 +196,15 @@ const char* csa_status_string(int32_t s) {
 int32_t csa_last_hip_error(void) { return g_last_hip; }
 
 csa_status csa_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;
   return CSA_OK;
 }
 
 csa_status csa_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
   for (auto& r : g_prof) {
-    (void)hipEventSynchronize(r.stop);
+    if (r.used) (void)hipEventSynchronize(r.stop);
     (void)hipEventDestroy(r.start);
     (void)hipEventDestroy(r.stop);
   }
@@ -202,10 +214,11 @@ csa_status csa_profile_reset(void) {
 
 csa_status csa_profile_collect(const char* kernel, double* total_ms, int64_t* launches) {
   if (!kernel || !total_ms || !launches) return CSA_ERR_NULL;
+  std::lock_guard<std::mutex> lk(g_prof_mu);
   double tot = 0.0;
   int64_t n = 0;
   for (auto& r : g_prof) {
-    if (r.name != kernel) continue;
+    if (r.name != kernel || !r.used) continue;
     hipError_t e = hipEventSynchronize(r.stop);
     if (e != hipSuccess) return hip_status(e);
     float ms = 0.f;

@@ -1103,8 +1103,8 @@ bool attn_uses_matrix_cores(int q_dt, int win_fmt, int comp_fmt, int n_win, int 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (!attn_uses_matrix_cores(a.q_dt, a.win_fmt, a.comp_fmt, a.n_win, a.n_comp)) {
     ProfScope p("attn_f32", s);
-    if (a.q_dt == 1) hipLaunchKernelGGL(attn_f32_kernel<true>, dim3((unsigned)a.Q, (unsigned)a.H), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(attn_f32_kernel<false>, dim3((unsigned)a.Q, (unsigned)a.H), dim3(256), 0, s, a);
+    if (a.q_dt == 1) CSA_LAUNCH(p, attn_f32_kernel<true>, dim3((unsigned)a.Q, (unsigned)a.H), dim3(256), s, a);
+    else CSA_LAUNCH(p, attn_f32_kernel<false>, dim3((unsigned)a.Q, (unsigned)a.H), dim3(256), s, a);
     return hipGetLastError();
   }
   const int Hpad = (a.H + 15) & ~15;
@@ -1117,10 +1117,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
     ProfScope p("attn_bf16", s);
     const dim3 grid((unsigned)(a.Q * a.n_split), (unsigned)hchunks);
 #define CSA_ATTN_FMT(K, NTG)                                                                                          \
-  if (wf == kRowFP8 && cf == kRowFP8) hipLaunchKernelGGL((K<kRowFP8, kRowFP8, NTG>), grid, dim3(kAttnThreads), 0, s, a); \
-  else if (wf == kRowFP8) hipLaunchKernelGGL((K<kRowFP8, kRowBF16, NTG>), grid, dim3(kAttnThreads), 0, s, a);           \
-  else if (cf == kRowFP8) hipLaunchKernelGGL((K<kRowBF16, kRowFP8, NTG>), grid, dim3(kAttnThreads), 0, s, a);           \
-  else hipLaunchKernelGGL((K<kRowBF16, kRowBF16, NTG>), grid, dim3(kAttnThreads), 0, s, a);
+  if (wf == kRowFP8 && cf == kRowFP8) CSA_LAUNCH(p, (K<kRowFP8, kRowFP8, NTG>), grid, dim3(kAttnThreads), s, a); \
+  else if (wf == kRowFP8) CSA_LAUNCH(p, (K<kRowFP8, kRowBF16, NTG>), grid, dim3(kAttnThreads), s, a);           \
+  else if (cf == kRowFP8) CSA_LAUNCH(p, (K<kRowBF16, kRowFP8, NTG>), grid, dim3(kAttnThreads), s, a);           \
+  else CSA_LAUNCH(p, (K<kRowBF16, kRowBF16, NTG>), grid, dim3(kAttnThreads), s, a);
 #define CSA_ATTN_LAUNCH(K) \
   if (a.stream_rows) { CSA_ATTN_FMT(K, true) } else { CSA_ATTN_FMT(K, false) }
     if (hb == 16) {
@@ -1135,9 +1135,9 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   if (e != hipSuccess || a.n_split == 1) return e;
   ProfScope p("attn_combine", s);
   if (a.n_split <= kCombineGroup)
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)(a.Q * ((a.H + 3) / 4))), dim3(256), 0, s, a);
+    CSA_LAUNCH(p, attn_combine_kernel, dim3((unsigned)(a.Q * ((a.H + 3) / 4))), dim3(256), s, a);
   else
-    hipLaunchKernelGGL(attn_combine_wide_kernel, dim3((unsigned)(a.Q * a.H)), dim3(256), 0, s, a);
+    CSA_LAUNCH(p, attn_combine_wide_kernel, dim3((unsigned)(a.Q * a.H)), dim3(256), s, a);
   return hipGetLastError();
 }
 

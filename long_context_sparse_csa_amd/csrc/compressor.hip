@@ -277,11 +277,11 @@ hipError_t launch_compress(const CompressArgs& a, hipStream_t s) {
   const unsigned blocks = (unsigned)((a.c_count + per_block - 1) / per_block);
   const bool bf16 = a.proj_dt == 1;
   if (a.D == 512) {
-    if (bf16) hipLaunchKernelGGL((compress_kernel<512, true>), dim3(blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((compress_kernel<512, false>), dim3(blocks), dim3(256), 0, s, a);
+    if (bf16) CSA_LAUNCH(p, (compress_kernel<512, true>), dim3(blocks), dim3(256), s, a);
+    else CSA_LAUNCH(p, (compress_kernel<512, false>), dim3(blocks), dim3(256), s, a);
   } else {
-    if (bf16) hipLaunchKernelGGL((compress_kernel<128, true>), dim3(blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((compress_kernel<128, false>), dim3(blocks), dim3(256), 0, s, a);
+    if (bf16) CSA_LAUNCH(p, (compress_kernel<128, true>), dim3(blocks), dim3(256), s, a);
+    else CSA_LAUNCH(p, (compress_kernel<128, false>), dim3(blocks), dim3(256), s, a);
   }
   return hipGetLastError();
 }

@@ -1,17 +1,26 @@
 // Internal host-side interface between the C ABI layer (api.cpp) and the kernel launchers.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace csa {
 
-// Records hipEvents around a launch when profiling is on (see csa_profile_enable).
+// Per-launch timing while profiling is on (see csa_profile_enable): the scope owns two events that
+// CSA_LAUNCH attaches to the kernel's own dispatch, so they bracket its execution on the GPU, not
+// its enqueue.  With profiling off both events are null and the launch is an ordinary one.
 struct ProfScope {
   ProfScope(const char* name, hipStream_t s);
-  ~ProfScope();
+  void mark();   // the scope's events were attached to a launch
   int slot;
-  hipStream_t stream;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
 };
+
+#define CSA_LAUNCH(P, K, GRID, BLOCK, S, ...)                                               \
+  do {                                                                                      \
+    (P).mark();                                                                             \
+    hipExtLaunchKernelGGL(K, GRID, BLOCK, 0, S, (P).ev0, (P).ev1, 0, __VA_ARGS__);          \
+  } while (0)
 
 struct IndexerArgs {
   const void* qI;             // [Q][HI][128] fp8 bytes or fp32

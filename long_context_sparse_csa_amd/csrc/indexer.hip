@@ -226,7 +226,10 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   // a wave, below) past it has nothing to do; short rows of a ragged batch then cost nothing
   if (a.visible_only && c_begin >= nv_max) return;
   if constexpr (HIST) {
+    // every wave adds into every part of the histogram, so all clears must land before the first
+    // add (both returns above are block-uniform, so every wave reaches this barrier)
     for (int i = tid; i < NQ * kHistBins; i += 256) lhist[i / kHistBins][i % kHistBins] = 0u;
+    __syncthreads();
   }
 
   // A operands: the queries' indexer heads, resident in VGPRs.  Loads are unconditional (clamped
@@ -476,8 +479,8 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
   if (a.dt == 0) {
     dim3 grid((unsigned)a.Q, (unsigned)((a.max_n_vis + kPage - 1) / kPage));
     ProfScope p("indexer_f32", s);
-    if (hist) hipLaunchKernelGGL(indexer_f32_kernel<true>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(indexer_f32_kernel<false>, grid, dim3(256), 0, s, a);
+    if (hist) CSA_LAUNCH(p, indexer_f32_kernel<true>, grid, dim3(256), s, a);
+    else CSA_LAUNCH(p, indexer_f32_kernel<false>, grid, dim3(256), s, a);
     return hipGetLastError();
   }
   const int nhg = (a.HI + 15) / 16;
@@ -488,8 +491,8 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
               (unsigned)((a.max_n_vis + kPfPages * kPage - 1) / (kPfPages * kPage)));
     ProfScope p(fp4 ? "indexer_fp4_prefill" : "indexer_fp8_prefill", s);
 #define CSA_PF_LAUNCH(N)                                                                    \
-  if (fp4) hipLaunchKernelGGL((indexer_fp8_prefill_kernel<N, true>), grid, dim3(256), 0, s, a); \
-  else hipLaunchKernelGGL((indexer_fp8_prefill_kernel<N, false>), grid, dim3(256), 0, s, a);
+  if (fp4) CSA_LAUNCH(p, (indexer_fp8_prefill_kernel<N, true>), grid, dim3(256), s, a); \
+  else CSA_LAUNCH(p, (indexer_fp8_prefill_kernel<N, false>), grid, dim3(256), s, a);
     switch (nhg) {
       case 1: CSA_PF_LAUNCH(1) break;
       case 2: CSA_PF_LAUNCH(2) break;
@@ -506,8 +509,8 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
   dim3 grid((unsigned)(a.Q / nq), (unsigned)((a.max_n_vis + per_block - 1) / per_block));
   ProfScope p(fp4 ? "indexer_fp4" : "indexer_fp8", s);
 #define CSA_IDX_LAUNCH(N, F, NQ)                                                                    \
-  if (hist) hipLaunchKernelGGL((indexer_fp8_kernel<N, true, F, NQ>), grid, dim3(256), 0, s, a); \
-  else hipLaunchKernelGGL((indexer_fp8_kernel<N, false, F, NQ>), grid, dim3(256), 0, s, a);
+  if (hist) CSA_LAUNCH(p, (indexer_fp8_kernel<N, true, F, NQ>), grid, dim3(256), s, a); \
+  else CSA_LAUNCH(p, (indexer_fp8_kernel<N, false, F, NQ>), grid, dim3(256), s, a);
 #define CSA_IDX_NQ(N, F)                          \
   switch (nq) {                                   \
     case 2: CSA_IDX_LAUNCH(N, F, 2) break;        \

@@ -831,13 +831,13 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
 hipError_t launch_topk_single(const TopkArgs& a, hipStream_t s) {
   ProfScope p("topk_single", s);
   if (a.max_n_vis <= 128 * kSinglePer)
-    hipLaunchKernelGGL((topk_single_kernel<128, kSinglePer>), dim3((unsigned)a.Q), dim3(128), 0, s, a);
+    CSA_LAUNCH(p, (topk_single_kernel<128, kSinglePer>), dim3((unsigned)a.Q), dim3(128), s, a);
   else if (a.max_n_vis <= 256 * kSinglePer)
-    hipLaunchKernelGGL((topk_single_kernel<256, kSinglePer>), dim3((unsigned)a.Q), dim3(256), 0, s, a);
+    CSA_LAUNCH(p, (topk_single_kernel<256, kSinglePer>), dim3((unsigned)a.Q), dim3(256), s, a);
   else if (a.max_n_vis <= 1024 * kSinglePer)
-    hipLaunchKernelGGL((topk_single_kernel<1024, kSinglePer>), dim3((unsigned)a.Q), dim3(1024), 0, s, a);
+    CSA_LAUNCH(p, (topk_single_kernel<1024, kSinglePer>), dim3((unsigned)a.Q), dim3(1024), s, a);
   else
-    hipLaunchKernelGGL((topk_single_kernel<1024, 32>), dim3((unsigned)a.Q), dim3(1024), 0, s, a);
+    CSA_LAUNCH(p, (topk_single_kernel<1024, 32>), dim3((unsigned)a.Q), dim3(1024), s, a);
   return hipGetLastError();
 }
 
@@ -847,7 +847,7 @@ hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s) {
   if (a.max_n_vis <= a.k) return hipSuccess;
   dim3 grid((unsigned)((a.max_n_vis + kSelChunk - 1) / kSelChunk), (unsigned)a.Q);
   ProfScope p("topk_hist", s);
-  hipLaunchKernelGGL(topk_hist_kernel, grid, dim3(256), 0, s, a);
+  CSA_LAUNCH(p, topk_hist_kernel, grid, dim3(256), s, a);
   return hipGetLastError();
 }
 
@@ -856,12 +856,12 @@ hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s) {
   if (chunks < 1) chunks = 1;
   if (a.max_n_vis > a.k) {
     ProfScope p("topk_collect", s);
-    hipLaunchKernelGGL(topk_collect_kernel, dim3((unsigned)chunks, (unsigned)a.Q), dim3(256), 0, s, a);
+    CSA_LAUNCH(p, topk_collect_kernel, dim3((unsigned)chunks, (unsigned)a.Q), dim3(256), s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   ProfScope p("topk_finish", s);
-  hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)a.Q), dim3(256), 0, s, a);
+  CSA_LAUNCH(p, topk_finish_kernel, dim3((unsigned)a.Q), dim3(256), s, a);
   return hipGetLastError();
 }
 
@@ -915,7 +915,7 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
   if (blocks < 1) blocks = 1;
   if (blocks > 2048) blocks = 2048;
   ProfScope p("prep", s);
-  hipLaunchKernelGGL(prep_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  CSA_LAUNCH(p, prep_kernel, dim3((unsigned)blocks), dim3(256), s, a);
   return hipGetLastError();
 }
 

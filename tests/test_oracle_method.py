@@ -356,3 +356,42 @@ def test_ragged_lengths_recipe():
     rest = np.delete(T, configs.RAGGED_EMPTY_ROWS)
     assert rest.min() >= 512 and rest.max() <= 131072
     assert (rest // 4 < 512).sum() >= 1
+
+
+def test_gather_rows_drops_negative_out_of_range_and_unmapped_slots():
+    """The oracle's reading of slots the pages leave open ([P1] section 3.7 masks only -1): a
+    negative index, an index at or past its source's length, or a compressed index on a page the
+    page table leaves unmapped (-1) or maps past the pool is dropped (zero row, not valid).  Valid
+    slots hold the stored bf16 row, decoded here by torch, with duplicates kept."""
+    wl = configs.make_decode("gather", [300, 1000], H=2, HI=2, kv_fmt=configs.KV_BF16, seed=8)
+    r = 1
+    pt = wl.page_table.copy()
+    assert pt.shape[1] >= 4 and pt[r, :4].min() >= 0
+    pt[r, 2] = -1                       # an unmapped page
+    pt[r, 3] = wl.num_pages + 5         # a page id past the pool
+    wl.page_table = pt
+    wr = wl.win_rows.shape[1]
+    limit = pt.shape[1] * 64
+    win = np.array([-1, -7, 0, 5, 5, wr - 1, wr, wr + 10])
+    comp = np.array([-1, -3, 0, 70, 70, 2 * 64 + 1, 3 * 64 + 9, limit, limit + 5, 63])
+    rows, valid = O.gather_rows(wl, r, win, comp)      # one query per request: query r is request r's
+    expect = [False, False, True, True, True, True, False, False,
+              False, False, True, True, True, False, False, False, False, True]
+    assert valid.tolist() == expect
+
+    def bf16_row(raw):
+        return torch.from_numpy(raw.view(np.int16).copy()).view(torch.bfloat16).double().numpy()
+
+    for j, ok in enumerate(expect):
+        if not ok:
+            assert np.all(rows[j] == 0.0)
+            continue
+        if j < win.size:
+            ref = bf16_row(wl.win_rows[r, win[j]])
+        else:
+            c = comp[j - win.size]
+            ref = bf16_row(wl.kv_pool[pt[r, c // 64], c % 64])
+        np.testing.assert_array_equal(rows[j], ref)
+    # an all-dropped list attends to nothing: exact zeros
+    out = O.attend(wl, r, np.array([-1, wr]), np.array([-2, limit, 2 * 64]))
+    assert np.all(out == 0.0)
