@@ -316,13 +316,15 @@ csa_status csa_compress_index_keys(const void* kv_proj, const void* score_proj, 
  * Diagnostics.
  *   csa_status_string   static text of a status code.
  *   csa_last_hip_error  hipError_t of the last CSA_ERR_HIP on the calling thread (0 if none).
- *   csa_profile_enable  on != 0: every kernel the entry points launch is bracketed by a pair of
- *                       hipEvents recorded on the caller's stream (adds no synchronisation).
+ *   csa_profile_enable  on != 0: every kernel the entry points launch carries a pair of hipEvents
+ *                       attached to its own dispatch (hipExtLaunchKernelGGL), which time the
+ *                       kernel's execution on the GPU; adds no synchronisation.
  *   csa_profile_collect synchronises the recorded events and returns, for the kernel named
  *                       `kernel` (e.g. "indexer_fp8"), the summed duration in ms and the number
  *                       of launches since the last reset; unknown names return 0 launches.
  *   csa_profile_reset   forgets all recorded events.
- * Profiling state is process-wide and not thread-safe; enable it only from one host thread.
+ * Profiling state is process-wide (a diagnostic, the library's only mutable state), guarded by a
+ * mutex.
  * ------------------------------------------------------------------------------------------- */
 const char* csa_status_string(int32_t status);
 int32_t csa_last_hip_error(void);

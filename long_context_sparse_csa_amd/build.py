@@ -24,6 +24,8 @@ HIPCC_FLAGS = [
     "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-result",
 ]
+# sources whose matrix-core accumulators may live in the accumulation registers (none at present)
+NO_VGPR_FORM: set = set()
 
 
 def hipcc() -> str:
@@ -55,7 +57,12 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src + ".o")
-        jobs.append((obj, [hipcc(), *compile_flags, "-I", os.path.join(ROOT, "include"), "-c",
+        flags = compile_flags
+        if src in NO_VGPR_FORM:
+            flags = [f for k, f in enumerate(compile_flags)
+                     if not (f == "-mllvm" and compile_flags[k + 1] == "-amdgpu-mfma-vgpr-form")
+                     and f != "-amdgpu-mfma-vgpr-form"]
+        jobs.append((obj, [hipcc(), *flags, "-I", os.path.join(ROOT, "include"), "-c",
                            os.path.join(CSRC, src), "-o", obj]))
     with ThreadPoolExecutor(min(len(jobs), max(1, os.cpu_count() or 1))) as ex:
         list(ex.map(lambda j: _run(j[1], verbose), jobs))

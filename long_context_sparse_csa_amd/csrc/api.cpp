@@ -83,19 +83,40 @@ struct PathWs {
   int64_t ld;
   TopkWs tk;
   float* part;
-  int32_t* rows;     // [rows][k] compressed KV rows of the selection (single-block top-k only)
+  int32_t* rows;     // [rows][k] compressed KV rows of the selection (one-block selections only)
+  uint2* sk_top;     // long decode rows: per-wave sketches [rows][sk_waves][8] and bounds
+  uint32_t* sk_bound;
+  int64_t sk_waves;
 };
 
-PathWs carve_path(Carver& c, int32_t rows, int32_t H, int64_t max_n_vis, int32_t k) {
-  PathWs w;
+// Which selection a fused call runs, from the visible-entry bound its workspace was sized for:
+// one block per query over the whole row (short rows), one block per query over the indexer's
+// per-wave sketches (long rows of a one-query-per-request decode), or the multi-launch histogram
+// selection (everything else).  The workspace layout depends on it, so a call and its workspace
+// query decide it from the same numbers.
+enum SelPath { kPathSingle, kPathSketch, kPathMulti };
+
+SelPath sel_path(int mode, int32_t S, int64_t n, int32_t k) {
+  if (csa::topk_single_ok(n, k)) return kPathSingle;
+  if (mode == 1 && S == 1 && csa::topk_sketch_ok(n, k)) return kPathSketch;
+  return kPathMulti;
+}
+
+PathWs carve_path(Carver& c, int32_t rows, int32_t H, int64_t max_n_vis, int32_t k, SelPath path) {
+  PathWs w{};
   w.n_vis = c.take<int32_t>((size_t)rows * 4);
   w.q_req = c.take<int32_t>((size_t)rows * 4);
   w.idx = c.take<int32_t>((size_t)rows * (kWin + k) * 4);
   w.ld = round64(max_n_vis > 0 ? max_n_vis : 1);
   w.logits = c.take<float>((size_t)rows * (size_t)w.ld * 4);
-  w.tk = carve_topk(c, rows, max_n_vis, k);
+  if (path == kPathMulti) w.tk = carve_topk(c, rows, max_n_vis, k);
   w.part = c.take<float>(csa::attn_partial_bytes(rows, H, kWin + k));
-  w.rows = c.take<int32_t>((size_t)rows * k * 4);
+  if (path != kPathMulti) w.rows = c.take<int32_t>((size_t)rows * k * 4);
+  if (path == kPathSketch) {
+    w.sk_waves = csa::topk_sketch_waves(max_n_vis > 0 ? max_n_vis : 1);
+    w.sk_top = c.take<uint2>((size_t)rows * (size_t)w.sk_waves * 8 * sizeof(uint2));
+    w.sk_bound = c.take<uint32_t>((size_t)rows * (size_t)w.sk_waves * 4);
+  }
   return w;
 }
 
@@ -167,6 +188,11 @@ ProfScope::ProfScope(const char* name, hipStream_t) : slot(-1) {
   slot = (int)g_prof.size() - 1;
   ev0 = r.start;
   ev1 = r.stop;
+}
+
+int32_t record_hip_error(hipError_t e) {
+  g_last_hip = (int32_t)e;
+  return CSA_ERR_HIP;
 }
 
 void ProfScope::mark() {
@@ -337,20 +363,29 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
                            const float* w, const csa_paged_idx* keys, const csa_paged_kv* comp,
                            const void* win, int32_t win_fmt, int64_t win_rows_per_req, const int32_t* ctx_len,
                            int64_t max_ctx, int64_t pos0, int64_t max_n_vis, float softmax_scale, void* out,
-                           int32_t out_dt, int32_t* idx_out, void* ws, size_t ws_bytes, size_t need,
+                           int32_t out_dt, int32_t* idx_out, void* ws, size_t ws_bytes, int64_t n_query,
                            hipStream_t stream, int32_t S = 1, int32_t ring = kWin) {
-  if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
+  // the workspace is laid out for n_query visible entries (what the workspace query was given);
+  // the kernels see the call's own bound max_n_vis <= n_query
+  const SelPath path = sel_path(mode, S, n_query, k);
+  Carver sizer(nullptr);
+  carve_path(sizer, rows, H, n_query, k, path);
+  if (!ws || ws_bytes < sizer.off) return CSA_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return CSA_ERR_ALIGN;
   if (idx_out && !aligned(idx_out, 4)) return CSA_ERR_ALIGN;
   Carver c(ws);
-  PathWs pw = carve_path(c, rows, H, max_n_vis, k);
+  PathWs pw = carve_path(c, rows, H, n_query, k, path);
   int32_t* idx = idx_out ? idx_out : pw.idx;
   const int64_t ld_idx = kWin + k;
   // Short rows: the indexer and a one-block-per-query selection derive visibility from ctx_len /
-  // pos0 themselves, so no preparation launch and no zeroed histogram are needed.
-  const bool single = csa::topk_single_ok(max_n_vis, k);
+  // pos0 themselves, so no preparation launch and no zeroed histogram are needed.  Long rows of a
+  // one-query-per-request decode likewise: the indexer leaves per-wave sketches and one block per
+  // query selects from them.
+  const bool single = path == kPathSingle;
+  const bool sketch = path == kPathSketch;
+  const bool one_block = single || sketch;
 
-  if (!single) {
+  if (!one_block) {
     csa::PrepArgs p{};
     p.zero_ptr = pw.tk.hist;
     p.zero_words = (int64_t)((uint8_t*)pw.tk.sel - (uint8_t*)pw.tk.hist) / 4;
@@ -365,24 +400,27 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   ia.keys = keys->keys; ia.kscale = keys->scales; ia.num_pages = keys->num_pages;
   ia.page_table = keys->page_table; ia.max_pages = keys->max_pages;
   ia.q_req = pw.q_req; ia.n_req = mode == 1 ? rows / S : 1; ia.n_vis = pw.n_vis; ia.Q = rows; ia.HI = HI;
-  ia.max_n_vis = max_n_vis; ia.logits = pw.logits; ia.ld = pw.ld; ia.hist = single ? nullptr : pw.tk.hist;
-  ia.vis_mode = single ? mode : 0; ia.ctx_len = ctx_len; ia.max_ctx = max_ctx; ia.pos0 = pos0; ia.q_per_req = S;
+  ia.max_n_vis = max_n_vis; ia.logits = pw.logits; ia.ld = pw.ld; ia.hist = one_block ? nullptr : pw.tk.hist;
+  ia.vis_mode = one_block ? mode : 0; ia.ctx_len = ctx_len; ia.max_ctx = max_ctx; ia.pos0 = pos0; ia.q_per_req = S;
   ia.visible_only = true;
+  if (sketch) { ia.sk_top = pw.sk_top; ia.sk_bound = pw.sk_bound; ia.sk_waves = pw.sk_waves; }
   CSA_HIP(csa::launch_indexer(ia, stream));
 
   csa::TopkArgs t{};
   t.logits = pw.logits; t.ld = pw.ld; t.n_vis = pw.n_vis; t.Q = rows; t.max_n_vis = max_n_vis; t.k = k;
   t.idx = idx + kWin; t.ld_idx = ld_idx; t.hist = pw.tk.hist; t.counters = pw.tk.counters; t.sel = pw.tk.sel;
   t.cand = pw.tk.cand; t.cand_cap = max_n_vis > 0 ? max_n_vis : 1;
-  t.win_mode = single ? mode : 0; t.ctx_len = ctx_len; t.max_ctx = max_ctx; t.pos0 = pos0;
+  t.win_mode = one_block ? mode : 0; t.ctx_len = ctx_len; t.max_ctx = max_ctx; t.pos0 = pos0;
   t.q_per_req = S; t.ring = ring;
-  if (single) {
+  if (one_block) {
     // the selection also resolves its rows through the page table, which it loads while the
     // scores load, so the attention prologue saves one dependent round trip
     t.rows = pw.rows; t.ld_rows = k; t.page_table = comp->page_table; t.max_pages = comp->max_pages;
     t.num_pages = comp->num_pages;
   }
-  CSA_HIP(single ? csa::launch_topk_single(t, stream) : csa::launch_topk_select(t, stream));
+  if (sketch) { t.sk_top = pw.sk_top; t.sk_bound = pw.sk_bound; t.sk_waves = pw.sk_waves; }
+  CSA_HIP(single ? csa::launch_topk_single(t, stream)
+                 : (sketch ? csa::launch_topk_sketch(t, stream) : csa::launch_topk_select(t, stream)));
 
   csa::AttnArgs a{};
   a.q = q; a.q_dt = q_dt; a.Q = rows; a.H = H; a.sink = sink;
@@ -397,7 +435,7 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   a.q_per_req = S;
   if (mode == 2) { a.trim_ratio = 4; a.pos0 = pos0; }   // selection pads past min(n_vis, k) with -1
   a.stream_rows = mode == 1 && S == 1;   // one query per request: each row is gathered once
-  if (single) { a.rows = pw.rows; a.ld_rows = k; }
+  if (one_block) { a.rows = pw.rows; a.ld_rows = k; }
   return hip_status(csa::launch_attention(a, stream));
 }
 
@@ -420,7 +458,7 @@ static csa_status check_path(int32_t rows, int32_t H, int32_t HI, int32_t k, con
 size_t csa_decode_workspace_bytes(int32_t B, int32_t H, int32_t HI, int64_t max_ctx, int32_t k) {
   if (B < 1 || H < 1 || HI < 1 || k < 1 || max_ctx < 0) return 0;
   Carver c(nullptr);
-  carve_path(c, B, H, max_ctx / 4, k);
+  carve_path(c, B, H, max_ctx / 4, k, sel_path(1, 1, max_ctx / 4, k));
   return c.off;
 }
 
@@ -435,15 +473,14 @@ csa_status csa_decode(int32_t B, int32_t H, int32_t HI, int32_t k, const void* q
   if (!aligned(ctx_len, 4)) return CSA_ERR_ALIGN;
   if (max_ctx < 0 || max_ctx > INT32_MAX) return CSA_ERR_SHAPE;
   const int64_t max_n_vis = std::min<int64_t>(max_ctx / 4, (int64_t)keys->max_pages * 64);
-  const size_t need = csa_decode_workspace_bytes(B, H, HI, max_ctx, k);
   return run_path(1, B, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys, comp, win_ring, win_fmt, kWin,
-                  ctx_len, max_ctx, 0, max_n_vis, softmax_scale, out, out_dt, idx_out, ws, ws_bytes, need, stream);
+                  ctx_len, max_ctx, 0, max_n_vis, softmax_scale, out, out_dt, idx_out, ws, ws_bytes, max_ctx / 4, stream);
 }
 
 size_t csa_decode_multi_workspace_bytes(int32_t B, int32_t S, int32_t H, int32_t HI, int64_t max_ctx, int32_t k) {
   if (B < 1 || S < 1 || S > kMaxQueriesPerReq || H < 1 || HI < 1 || k < 1 || max_ctx < 0) return 0;
   Carver c(nullptr);
-  carve_path(c, B * S, H, max_ctx / 4, k);
+  carve_path(c, B * S, H, max_ctx / 4, k, sel_path(1, S, max_ctx / 4, k));
   return c.off;
 }
 
@@ -461,16 +498,15 @@ csa_status csa_decode_multi(int32_t B, int32_t S, int32_t H, int32_t HI, int32_t
   if (max_ctx < 0 || max_ctx > INT32_MAX) return CSA_ERR_SHAPE;
   if (ring_slots < kWin + S - 1 || ring_slots > (1 << 20)) return CSA_ERR_SHAPE;
   const int64_t max_n_vis = std::min<int64_t>(max_ctx / 4, (int64_t)keys->max_pages * 64);
-  const size_t need = csa_decode_multi_workspace_bytes(B, S, H, HI, max_ctx, k);
   return run_path(1, B * S, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys, comp, win_ring, win_fmt,
-                  ring_slots, ctx_len, max_ctx, 0, max_n_vis, softmax_scale, out, out_dt, idx_out, ws, ws_bytes, need,
-                  stream, S, ring_slots);
+                  ring_slots, ctx_len, max_ctx, 0, max_n_vis, softmax_scale, out, out_dt, idx_out, ws, ws_bytes,
+                  max_ctx / 4, stream, S, ring_slots);
 }
 
 size_t csa_prefill_workspace_bytes(int32_t Q, int32_t H, int32_t HI, int64_t T, int32_t k) {
   if (Q < 1 || H < 1 || HI < 1 || k < 1 || T < 0) return 0;
   Carver c(nullptr);
-  carve_path(c, Q, H, T / 4, k);
+  carve_path(c, Q, H, T / 4, k, sel_path(2, 1, T / 4, k));
   return c.off;
 }
 
@@ -483,9 +519,8 @@ csa_status csa_prefill(int32_t Q, int32_t H, int32_t HI, int32_t k, const void* 
                      softmax_scale, out, out_dt));
   if (T < 1 || T > INT32_MAX || pos0 < 0 || pos0 + Q > T) return CSA_ERR_SHAPE;
   const int64_t max_n_vis = std::min<int64_t>((pos0 + Q) / 4, (int64_t)keys->max_pages * 64);
-  const size_t need = csa_prefill_workspace_bytes(Q, H, HI, T, k);
   return run_path(2, Q, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys, comp, raw_rows, raw_fmt, T,
-                  nullptr, 0, pos0, max_n_vis, softmax_scale, out, out_dt, idx_out, ws, ws_bytes, need, stream);
+                  nullptr, 0, pos0, max_n_vis, softmax_scale, out, out_dt, idx_out, ws, ws_bytes, T / 4, stream);
 }
 
 }  // extern "C"

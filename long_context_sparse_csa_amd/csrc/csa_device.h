@@ -17,6 +17,8 @@ constexpr int kPage = 64;       // compressed entries per page
 constexpr int kWin = 128;       // sliding window
 constexpr int kHistBins = 4096; // top-k coarse histogram: top 12 bits of the order key
 constexpr int kHistShift = 20;
+constexpr int kSketchTop = 8;       // long-row sketch: largest scores kept per wave of the indexer
+constexpr int kSketchSpan = 512;    // entries scored by one indexer wave (8 pages)
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;   // finite running-max start: an all-invalid row yields 0
@@ -97,6 +99,34 @@ __device__ __forceinline__ float row_group_sum(float x) {
   x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
   r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Largest uint32 over the 64 lanes, with DPP moves inside each 16-lane row (quad permutations
+// for strides 1 and 2, row rotations for 4 and 8) and the cross-row lane swaps for 16 and 32: no
+// LDS-routed shuffle (a chain of those measured about a microsecond per block-wide reduction).
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+  auto mx = [](uint32_t p, uint32_t q) { return p > q ? p : q; };
+  x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+  x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+  x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false));  // row_ror:4
+  x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));  // row_ror:8
+  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  x = mx(r[0], r[1]);
+  r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return mx(r[0], r[1]);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (VALU only, no LDS crossbar):
+// shifts by 1, 2, 4, 8 inside each row of 16 lanes, then row 0's and row 2's totals broadcast into
+// rows 1 and 3, then the total of rows 0-1 into rows 2 and 3.  Lanes without a source add 0.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
 }
 
 // Decode with S queries per request: query q is token j = q % S of request r = q / S, one of the

@@ -6,6 +6,9 @@
 
 namespace csa {
 
+// Records e as the calling thread's last HIP error and returns CSA_ERR_HIP.
+int32_t record_hip_error(hipError_t e);
+
 // Per-launch timing while profiling is on (see csa_profile_enable): the scope owns two events that
 // CSA_LAUNCH attaches to the kernel's own dispatch, so they bracket its execution on the GPU, not
 // its enqueue.  With profiling off both events are null and the launch is an ordinary one.
@@ -50,6 +53,11 @@ struct IndexerArgs {
   // true inside the fused paths: only columns c < n_vis of each row are written (the selection
   // reads nothing else); false for csa_indexer_logits, which also fills [n_vis, max_n_vis) with -inf
   bool visible_only = false;
+  // optional (decode, one query per request, visible_only): per-wave sketch of each row for the
+  // one-launch long-row selection: [Q][sk_waves][8] (order key, entry) and [Q][sk_waves] bounds
+  uint2* sk_top = nullptr;
+  uint32_t* sk_bound = nullptr;
+  int64_t sk_waves = 0;
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
 
@@ -82,11 +90,20 @@ struct TopkArgs {
   const int32_t* page_table;
   int max_pages;
   int num_pages;
+  // sketch path only: the indexer's per-wave sketches of each row (see IndexerArgs)
+  const uint2* sk_top = nullptr;
+  const uint32_t* sk_bound = nullptr;
+  int64_t sk_waves = 0;
 };
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_single(const TopkArgs& a, hipStream_t s);
 bool topk_single_ok(int64_t max_n_vis, int k);
+// Long rows of a one-query-per-request decode: the indexer writes per-wave sketches (8 largest
+// scores of every 512 entries and a bound on the rest) and one block per query selects from them.
+hipError_t launch_topk_sketch(const TopkArgs& a, hipStream_t s);
+bool topk_sketch_ok(int64_t max_n_vis, int k);
+int64_t topk_sketch_waves(int64_t max_n_vis);   // sketches per row
 
 // Zero histograms / counters and write window indices (decode ring or causal prefill window).
 struct PrepArgs {

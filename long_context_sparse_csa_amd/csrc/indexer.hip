@@ -202,9 +202,79 @@ constexpr int kMaxSharedQueries = 4;   // multi-query decode: queries scored per
 template <bool FP4, int NQ>
 constexpr int kDecodeBufs = NQ > 1 ? 2 : kPageBufs<FP4>;
 
-template <int NHG, bool HIST, bool FP4, int NQ>
+// What the decode kernel leaves for the selection besides the scores: nothing, a per-row 12-bit
+// histogram of the scores (the multi-launch selection of rows of any length), or a per-wave sketch
+// (the one-launch selection of long rows; see sketch_wave below).
+enum SelOut : int { kSelNone = 0, kSelHist = 1, kSelSketch = 2 };
+
+// Per-wave sketch of a long row: the wave's 8 largest scores (order keys and entry indices, in
+// ascending index order) and the 9th largest order key, an upper bound for every entry of the wave
+// left out.  The selection takes the k largest of all waves' sketches; a wave whose bound reaches
+// the k-th of them may hide a selected entry, and only then are the full scores read back.
+//   Each lane holds one entry of each of the wave's 8 pages.  It sorts its 8 (key, page) pairs
+// (descending keys, a 19-exchange network), then 8 rounds take the wave's largest lane head (the
+// lowest lane on ties: within a wave the order of equal keys is immaterial, because a left-out entry
+// equal to a kept one makes the bound reach it) and that lane advances; a 9th round reads the
+// bound.  Entries past the visible prefix carry key 0 and page code 15 and give index -1.
+
+__device__ __forceinline__ void sketch_wave(const uint32_t* key8, uint32_t valid8, int64_t e_base, int lane,
+                                            uint2* top, uint32_t* bound) {
+  uint32_t k[8], pg[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool v = (valid8 >> i) & 1u;
+    k[i] = v ? key8[i] : 0u;
+    pg[i] = v ? (uint32_t)i : 15u;
+  }
+  auto cx = [&](int x, int y) {   // descending: larger key to x
+    const bool sw = k[y] > k[x];
+    const uint32_t kx = k[x], ky = k[y], px = pg[x], py = pg[y];
+    k[x] = sw ? ky : kx; k[y] = sw ? kx : ky;
+    pg[x] = sw ? py : px; pg[y] = sw ? px : py;
+  };
+  // Batcher's odd-even merge sort of 8
+  cx(0, 1); cx(2, 3); cx(4, 5); cx(6, 7);
+  cx(0, 2); cx(1, 3); cx(4, 6); cx(5, 7);
+  cx(1, 2); cx(5, 6);
+  cx(0, 4); cx(1, 5); cx(2, 6); cx(3, 7);
+  cx(2, 4); cx(3, 5);
+  cx(1, 2); cx(3, 4); cx(5, 6);
+  uint32_t my_key = 0u, my_idx = 0xFFFFFFFFu;
+#pragma unroll
+  for (int r = 0; r < kSketchTop; ++r) {
+    const uint32_t kmax = wave_umax(k[0]);
+    const int win = __builtin_ctzll(__ballot(k[0] == kmax));
+    const uint32_t cand = pg[0] < 8u ? (uint32_t)(e_base + (int64_t)pg[0] * kPage) : 0xFFFFFFFFu;
+    const uint32_t idx_r = (uint32_t)__builtin_amdgcn_readlane((int)cand, win);
+    my_key = lane == r ? kmax : my_key;
+    my_idx = lane == r ? idx_r : my_idx;
+    const bool adv = lane == win;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+      k[i] = adv ? k[i + 1] : k[i];
+      pg[i] = adv ? pg[i + 1] : pg[i];
+    }
+    k[7] = adv ? 0u : k[7];
+    pg[7] = adv ? 15u : pg[7];
+  }
+  const uint32_t bnd = wave_umax(k[0]);
+  // lanes 0-7 hold the kept entries; each lands at its rank by index (index -1, as unsigned, last)
+  int rank = 0;
+#pragma unroll
+  for (int s2 = 0; s2 < kSketchTop; ++s2) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)my_idx, s2);
+    rank += (o < my_idx || (o == my_idx && s2 < lane)) ? 1 : 0;
+  }
+  if (lane < kSketchTop) top[rank] = make_uint2(my_key, my_idx);
+  if (lane == 0) *bound = bnd;
+}
+
+template <int NHG, int SEL, bool FP4, int NQ>
 __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
+  constexpr bool HIST = SEL == kSelHist;
+  constexpr bool SK = SEL == kSelSketch && NQ == 1;
   constexpr int pages_per_wave = kPagesPerWave<FP4>;
+  static_assert(!SK || pages_per_wave * kPage == kSketchSpan, "a sketch covers one wave's pages");
   constexpr int nbuf = kDecodeBufs<FP4, NQ> < pages_per_wave ? kDecodeBufs<FP4, NQ> : pages_per_wave;
   const int q0 = blockIdx.x * NQ;   // queries vary fastest: a row's blocks share one XCD (and its L2)
   const int tid = threadIdx.x, lane = tid & 63;
@@ -266,6 +336,8 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
     for (int kg = 0; kg < 4; ++kg) kb[kg] = load_key_operand<FP4>(kp, kg);
   };
 
+  uint32_t skey[SK ? pages_per_wave : 1];   // sketch: order key of this lane's entry of page i
+  uint32_t svalid = 0u;                      // bit i: that entry is visible
   auto compute_page = [&](int i, const v8i* kb, int ksc) {
     const int64_t c0 = (p_first + i) * kPage;
     const bool mapped = page_ok(i);
@@ -273,12 +345,16 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const float score = score_page<NHG, FP4>(qa[j], qsc[j], wv[j], kb, ksc);
+      const float v = (mapped && c0 < nv[j] && c < nv[j]) ? score : -INFINITY;
       if (c < (a.visible_only ? nv[j] : a.max_n_vis)) {
-        const float v = (mapped && c0 < nv[j] && c < nv[j]) ? score : -INFINITY;
         a.logits[(int64_t)(q0 + j) * a.ld + c] = v;
         if constexpr (HIST) {
           if (c < nv[j]) atomicAdd(&lhist[j][order_key(v) >> kHistShift], 1u);
         }
+      }
+      if constexpr (SK) {
+        skey[i] = order_key(v);
+        svalid |= (c < nv[0] ? 1u : 0u) << i;
       }
     }
   };
@@ -296,6 +372,12 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
     for (int i = 0; i < pages_per_wave; ++i) {
       compute_page(i, kb[i % nbuf], ksc[i % nbuf]);
       if (i + nbuf < pages_per_wave) load_page(i + nbuf, kb[i % nbuf], ksc[i % nbuf]);
+    }
+    if constexpr (SK) {
+      // wave W of the row covers entries [W * kSketchSpan, (W + 1) * kSketchSpan)
+      const int64_t W = p_first / pages_per_wave;
+      const int64_t slot = (int64_t)q0 * a.sk_waves + W;
+      sketch_wave(skey, svalid, p_first * kPage + 4 * n + g, lane, a.sk_top + slot * kSketchTop, a.sk_bound + slot);
     }
   }
   if constexpr (HIST) {
@@ -476,6 +558,7 @@ __global__ __launch_bounds__(256) void indexer_f32_kernel(IndexerArgs a) {
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
   if (a.max_n_vis <= 0) return hipSuccess;
   const bool hist = a.hist != nullptr;
+  const bool sketch = a.sk_top != nullptr;
   if (a.dt == 0) {
     dim3 grid((unsigned)a.Q, (unsigned)((a.max_n_vis + kPage - 1) / kPage));
     ProfScope p("indexer_f32", s);
@@ -508,9 +591,10 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
   const int per_block = 4 * (fp4 ? kPagesPerWave<true> : kPagesPerWave<false>) * kPage;
   dim3 grid((unsigned)(a.Q / nq), (unsigned)((a.max_n_vis + per_block - 1) / per_block));
   ProfScope p(fp4 ? "indexer_fp4" : "indexer_fp8", s);
-#define CSA_IDX_LAUNCH(N, F, NQ)                                                                    \
-  if (hist) CSA_LAUNCH(p, (indexer_fp8_kernel<N, true, F, NQ>), grid, dim3(256), s, a); \
-  else CSA_LAUNCH(p, (indexer_fp8_kernel<N, false, F, NQ>), grid, dim3(256), s, a);
+#define CSA_IDX_LAUNCH(N, F, NQ)                                                                           \
+  if (hist) CSA_LAUNCH(p, (indexer_fp8_kernel<N, kSelHist, F, NQ>), grid, dim3(256), s, a);             \
+  else if (sketch && NQ == 1) CSA_LAUNCH(p, (indexer_fp8_kernel<N, kSelSketch, F, 1>), grid, dim3(256), s, a); \
+  else CSA_LAUNCH(p, (indexer_fp8_kernel<N, kSelNone, F, NQ>), grid, dim3(256), s, a);
 #define CSA_IDX_NQ(N, F)                          \
   switch (nq) {                                   \
     case 2: CSA_IDX_LAUNCH(N, F, 2) break;        \

@@ -60,34 +60,6 @@ __device__ __forceinline__ void write_window(const TopkArgs& a, int q) {
   a.idx[(int64_t)q * a.ld_idx - kWin + j] = v;
 }
 
-// Largest uint32 over the 64 lanes, with DPP moves inside each 16-lane row (quad permutations
-// for strides 1 and 2, row rotations for 4 and 8) and the cross-row lane swaps for 16 and 32: no
-// LDS-routed shuffle (a chain of those measured about a microsecond per block-wide reduction).
-__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
-  auto mx = [](uint32_t p, uint32_t q) { return p > q ? p : q; };
-  x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
-  x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
-  x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xf, 0xf, false));  // row_ror:4
-  x = mx(x, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false));  // row_ror:8
-  auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  x = mx(r[0], r[1]);
-  r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return mx(r[0], r[1]);
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (VALU only, no LDS crossbar):
-// shifts by 1, 2, 4, 8 inside each row of 16 lanes, then row 0's and row 2's totals broadcast into
-// rows 1 and 3, then the total of rows 0-1 into rows 2 and 3.  Lanes without a source add 0.
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, true);   // row_shr:1
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, true);   // row_shr:2
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, true);   // row_shr:4
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, true);   // row_shr:8
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return x;
-}
-
 // Exclusive prefix sum over the 256 threads of a block; *total receives the block sum.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -479,13 +451,14 @@ __global__ __launch_bounds__(256) void topk_finish_kernel(TopkArgs a) {
   for (int i = tid; i < k; i += 256) out[i] = sk[i] == 0x7FFFFFFF ? -1 : sk[i];
 }
 
-// ---- single-block selection for short rows (n_vis <= kSingleMax): one block per query keeps the
-// row in registers (16 consecutive entries per thread), so no global histogram, no zeroed
-// workspace and no second launch are needed.  Every barrier-separated phase costs on the order
-// of a microsecond at 16 waves, and a predicated LDS instruction costs its issue slot even when
-// few lanes are active, so the phases are few, the scans are done by a single wave and sparse
-// passes skip instructions no lane needs:
-//   1. a 4096-bin histogram of the scores over the row's value range gives the threshold bin b*
+// ---- single-block selection: one block per query keeps its entries in registers (PER consecutive
+// entries per thread, in index order), so no global histogram, no zeroed workspace and no second
+// launch are needed.  Two users: short rows (n_vis <= kSingleMax), whose entries are the row itself,
+// and long decode rows, whose entries are the indexer's per-wave sketches (see topk_sketch_kernel).
+// Every barrier-separated phase costs on the order of a microsecond at 16 waves, and a predicated
+// LDS instruction costs its issue slot even when few lanes are active, so the phases are few, the
+// scans are done by a single wave and sparse passes skip instructions no lane needs:
+//   1. a 4096-bin histogram of the scores over the entries' value range gives the threshold bin b*
 //      and the count above it; b*'s entries (normally a handful) go to an LDS candidate list and
 //      one wave ranks them by their full keys, giving the exact k-th largest key T and how many
 //      keys equal to T are taken;
@@ -537,12 +510,270 @@ __device__ __forceinline__ float key_value(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
-// NT threads cover rows of up to 16 NT entries; short rows take a small block so that several
-// rows share a CU (LDS: 16 KB of bins + 8 KB of candidate keys / selected indices + 4 B per thread).
+// LDS of the one-block selection (16 KB of bins + 8 KB of candidate keys / selected indices).
+template <int NT>
+struct SelShared {
+  uint32_t bins[kHistBins];
+  uint32_t scan[NT / 64];          // per-wave totals of the final scan
+  // order keys of the threshold bin's entries while the threshold is resolved, then the selected
+  // indices
+  uint32_t cand_sel[kCandMax > kSingleMaxK ? kCandMax : kSingleMaxK];
+  uint32_t s_digit, s_before, s_ncand, s_T, s_need;
+  uint32_t ext[2 * (NT / 64)];     // per-wave largest / smallest key
+};
+
+// Exact k-th largest order key T among the block's entries (thread t holds key[0..PER) with bit j
+// of vm set for a real entry) and how many entries equal to T are taken: sh.s_T, sh.s_need on
+// return (after a barrier).  The block holds at least k real entries.  On entry sh.bins is zeroed,
+// sh.s_ncand is 0 and a barrier has passed since.
+template <int NT, int PER>
+__device__ void block_threshold(const uint32_t* key, uint32_t vm, uint32_t k, SelShared<NT>& sh) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // extremes of the real keys: per wave, then across waves after the barrier
+  {
+    uint32_t kmx = 0u, kmn = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if ((vm >> j) & 1u) {
+        kmx = key[j] > kmx ? key[j] : kmx;
+        kmn = key[j] < kmn ? key[j] : kmn;
+      }
+    }
+    kmx = wave_umax(kmx);
+    kmn = ~wave_umax(~kmn);   // min through the max of complements
+    if (lane == 0) {
+      sh.ext[wave] = kmx;
+      sh.ext[NT / 64 + wave] = kmn;
+    }
+  }
+  __syncthreads();
+  // Level 1 on the value range: 4096 equal-width bins between the smallest and largest finite
+  // score.  Scores crowd a few of the fixed 12-bit key-prefix bins (the exponent and three
+  // mantissa bits), so LDS atomics collide and the threshold bin holds hundreds of entries; on the
+  // value range the bins hold a handful.  The bin index is a monotone function of the score
+  // (subtraction, multiplication by a positive scale and truncation all preserve order), so b*
+  // and the counts above it are exact.  When b* holds at most 64 entries one wave ranks them by
+  // their full keys; otherwise (ties, clusters, non-finite scores) the key-prefix levels run.
+  bool resolved = false;
+  {
+    uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+      kmax = sh.ext[w] > kmax ? sh.ext[w] : kmax;
+      kmin = sh.ext[NT / 64 + w] < kmin ? sh.ext[NT / 64 + w] : kmin;
+    }
+    const float vmin = key_value(kmin), vmax = key_value(kmax);
+    const float scale = 4096.f / (vmax - vmin);
+    // every real key is finite (NaN maps below -inf, infinities outside +-FLT_MAX) and spread
+    const bool adaptive = kmin >= order_key(-3.40282347e+38f) && kmax <= order_key(3.40282347e+38f) &&
+                          kmax > kmin && scale > 0.f && scale < 3.0e38f;
+    if (adaptive) {
+      uint32_t bin[PER];
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        const float x = (key_value(key[j]) - vmin) * scale;
+        // x >= 0 for real entries; the others (never counted) are clamped too
+        const uint32_t b = x < 4095.f ? (x > 0.f ? (uint32_t)x : 0u) : 4095u;
+        bin[j] = b;
+        if ((vm >> j) & 1u) atomicAdd(&sh.bins[b], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) wave_find_desc(sh.bins, kHistBins, k, &sh.s_digit, &sh.s_before);
+      __syncthreads();
+      const uint32_t bstar = sh.s_digit;
+      const uint32_t need1 = k - sh.s_before;
+      {
+        uint32_t hm = 0;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) hm |= (((vm >> j) & 1u) && bin[j] == bstar) ? (1u << j) : 0u;
+        const uint32_t hits = __popc(hm);
+        const uint32_t incl = wave_inclusive_scan(hits);
+        uint32_t base = 0;
+        if (lane == 63 && incl) base = atomicAdd(&sh.s_ncand, incl);
+        base = __builtin_amdgcn_readlane(base, 63);
+        uint32_t pos = base + incl - hits;
+        while (hm) {
+          const int j = __ffs((int)hm) - 1;
+          hm &= hm - 1u;
+          if (pos < 64u) sh.cand_sel[pos] = key[j];
+          ++pos;
+        }
+      }
+      __syncthreads();
+      const uint32_t n_cand = sh.s_ncand;
+      if (n_cand <= 64u) {
+        // rank the candidates by their keys: the threshold is the key with fewer than need1 keys
+        // above it and at least need1 at or above it
+        if (wave == 0) {
+          const uint32_t mine = lane < (int)n_cand ? sh.cand_sel[lane] : 0u;
+          uint32_t gt = 0, ge = 0;
+          for (int j = 0; j < (int)n_cand; ++j) {
+            const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, j);
+            gt += o > mine ? 1u : 0u;
+            ge += o >= mine ? 1u : 0u;
+          }
+          if (lane < (int)n_cand && gt < need1 && ge >= need1) {   // every such lane holds the same key
+            sh.s_T = mine;
+            sh.s_need = need1 - gt;
+          }
+        }
+        resolved = true;
+      } else {
+        for (int i = tid; i < kHistBins; i += NT) sh.bins[i] = 0u;
+        if (tid == 0) sh.s_ncand = 0u;
+        __syncthreads();
+      }
+    }
+  }
+  if (!resolved) {
+    // level 1: top 12 key bits of every entry (all lanes active: one LDS atomic instruction covers 64)
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if ((vm >> j) & 1u) atomicAdd(&sh.bins[key[j] >> kHistShift], 1u);
+    __syncthreads();
+    if (wave == 0) wave_find_desc(sh.bins, kHistBins, k, &sh.s_digit, &sh.s_before);
+    __syncthreads();
+    const uint32_t bstar = sh.s_digit;
+    const uint32_t need1 = k - sh.s_before;   // entries still to take from bin b* (>= 1)
+    // the entries of bin b* become candidates: their keys are appended to LDS with one atomic per
+    // wave, a lane's after those of the lanes below it
+    {
+      uint32_t hm = 0;   // bit j: entry j is in b*
+#pragma unroll
+      for (int j = 0; j < PER; ++j) hm |= (((vm >> j) & 1u) && (key[j] >> kHistShift) == bstar) ? (1u << j) : 0u;
+      const uint32_t hits = __popc(hm);
+      const uint32_t incl = wave_inclusive_scan(hits);
+      uint32_t base = 0;
+      if (lane == 63 && incl) base = atomicAdd(&sh.s_ncand, incl);
+      base = __builtin_amdgcn_readlane(base, 63);
+      uint32_t pos = base + incl - hits;
+      while (hm) {
+        const int j = __ffs((int)hm) - 1;
+        hm &= hm - 1u;
+        if (pos < (uint32_t)kCandMax) sh.cand_sel[pos] = key[j];
+        ++pos;
+      }
+    }
+    __syncthreads();
+    const uint32_t n_cand = sh.s_ncand;
+    if (n_cand <= (uint32_t)kCandMax) {
+      // wave 0 alone resolves the 20 low key bits among the candidates (two 10-bit levels in a
+      // wave-private histogram); LDS operations of one wave complete in order
+      if (wave == 0) {
+        uint32_t prefix = bstar, need = need1;
+#pragma unroll 1
+        for (int lvl = 0; lvl < 2; ++lvl) {
+          const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
+#pragma unroll
+          for (int i = 0; i < 1024; i += 256) *(uint4*)&sh.bins[i + 4 * lane] = make_uint4(0u, 0u, 0u, 0u);
+          __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+          __builtin_amdgcn_wave_barrier();
+          // four candidates per lane per pass: their reads are all in flight before the first atomic
+          for (uint32_t i0 = 0; i0 < n_cand; i0 += 256) {
+            uint32_t kk[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const uint32_t i = i0 + 64 * u + lane;
+              kk[u] = sh.cand_sel[i < n_cand ? i : 0];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const uint32_t i = i0 + 64 * u + lane;
+              if (i < n_cand && (kk[u] >> (shift + 10)) == prefix) atomicAdd(&sh.bins[(kk[u] >> shift) & 1023u], 1u);
+            }
+          }
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          __builtin_amdgcn_wave_barrier();
+          wave_find_desc(sh.bins, 1024, need, &sh.s_digit, &sh.s_before);
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          __builtin_amdgcn_wave_barrier();
+          prefix = (prefix << 10) | sh.s_digit;
+          need -= sh.s_before;
+        }
+        if (lane == 0) {
+          sh.s_T = prefix;
+          sh.s_need = need;
+        }
+      }
+    } else {
+      // many entries share b* (heavily tied scores): levels 2 and 3 over the whole block, ten more
+      // key bits each, counting only entries with the current prefix
+      uint32_t prefix = bstar, need = need1;
+#pragma unroll 1
+      for (int lvl = 0; lvl < 2; ++lvl) {
+        const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
+        for (int i = tid; i < 1024; i += NT) sh.bins[i] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const bool hit = ((vm >> j) & 1u) && (key[j] >> (shift + 10)) == prefix;
+          if (__any(hit) && hit) atomicAdd(&sh.bins[(key[j] >> shift) & 1023u], 1u);
+        }
+        __syncthreads();
+        if (wave == 0) wave_find_desc(sh.bins, 1024, need, &sh.s_digit, &sh.s_before);
+        __syncthreads();
+        prefix = (prefix << 10) | sh.s_digit;
+        need -= sh.s_before;
+      }
+      if (tid == 0) {
+        sh.s_T = prefix;
+        sh.s_need = need;
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// The selected entries' indices in ascending order into sh.cand_sel[0, k): every real entry above
+// T and the first `need` equal to T (index order), placed by one block scan of the per-thread
+// (greater, equal) counts packed in one word (both totals stay below 2^16).  idx_of(j) is the index
+// of this thread's entry j; thread t's entries precede thread t+1's in index order.  Ends with a
+// barrier.
+template <int NT, int PER, class IdxOf>
+__device__ void block_emit(const uint32_t* key, uint32_t vm, uint32_t T, uint32_t need, uint32_t k, IdxOf idx_of,
+                           SelShared<NT>& sh) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  uint32_t gm = 0, em = 0;       // bit j: entry j is above T / equal to T
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const bool ok = (vm >> j) & 1u;
+    gm |= (ok && key[j] > T) ? (1u << j) : 0u;
+    em |= (ok && key[j] == T) ? (1u << j) : 0u;
+  }
+  const uint32_t n_gt = __popc(gm), n_eq = __popc(em);
+  const uint32_t mine = (n_gt << 16) | n_eq;
+  const uint32_t incl = wave_inclusive_scan(mine);
+  if (lane == 63) sh.scan[wave] = incl;
+  __syncthreads();
+  uint32_t pre = incl - mine;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) pre += w < wave ? sh.scan[w] : 0u;
+  const uint32_t eq_before = pre & 0xFFFFu;
+  uint32_t pos = (pre >> 16) + (eq_before < need ? eq_before : need);
+  uint32_t take_eq = eq_before < need ? (need - eq_before < n_eq ? need - eq_before : n_eq) : 0u;
+  // the taken entries: all above T, and the lowest-index take_eq of those equal to T
+  uint32_t tm = gm;
+  for (uint32_t t = 0; t < take_eq; ++t) {
+    const uint32_t low = em & (0u - em);
+    tm |= low;
+    em ^= low;
+  }
+  int32_t* sel = (int32_t*)sh.cand_sel;
+  while (tm) {
+    const int j = __ffs((int)tm) - 1;
+    tm &= tm - 1u;
+    if (pos < k) sel[pos] = idx_of(j);
+    ++pos;
+  }
+  __syncthreads();
+}
+
+// NT threads cover rows of up to NT * PER entries; short rows take a small block so that several
+// rows share a CU.
 template <int NT, int PER>
 __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
   constexpr int kRowMax = NT * PER;
-  const int q = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int q = blockIdx.x, tid = threadIdx.x;
   const int64_t nv = topk_row_count(a, q);
   const int k = a.k;
   int32_t* out = a.idx + (int64_t)q * a.ld_idx;
@@ -562,19 +793,12 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
     // the request's page ids, loaded alongside the scores (rows >= 1: nv > k >= 1)
     for (int p = tid; p < (int)((nv + kPage - 1) / kPage); p += NT) pt_lds[p] = pt[p];
   }
-  __shared__ __align__(16) uint32_t bins[kHistBins];
-  __shared__ __align__(16) uint32_t scan[NT / 64];   // per-wave totals of the final scan
-  // order keys of the threshold bin's entries while the threshold is resolved, then the selected
-  // indices
-  __shared__ uint32_t cand_sel[kCandMax > kSingleMaxK ? kCandMax : kSingleMaxK];
-  uint32_t* cand_key = cand_sel;
-  int32_t* sel = (int32_t*)cand_sel;
-  __shared__ uint32_t s_digit, s_before, s_ncand, s_T, s_need;
-  __shared__ uint32_t ext[2 * (NT / 64)];   // per-wave largest / smallest visible key
+  __shared__ SelShared<NT> sh;
 
   const float* row = a.logits + (int64_t)q * a.ld;
   const int c0 = tid * PER;          // this thread owns entries [c0, c0+PER)
   uint32_t key[PER];
+  uint32_t vm = 0;
   {
     float v[PER];
 #pragma unroll
@@ -585,247 +809,203 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
       v[j] = x.x; v[j + 1] = x.y; v[j + 2] = x.z; v[j + 3] = x.w;
     }
     // cleared while the loads are in flight
-    for (int i = tid; i < kHistBins; i += NT) bins[i] = 0u;
-    if (tid == 0) s_ncand = 0u;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) key[j] = order_key(v[j]);   // entries past n_vis are never counted
-  }
-  __syncthreads();
-  // row extremes of the visible keys: per wave, then across waves after the barrier
-  {
-    uint32_t kmx = 0u, kmn = 0xFFFFFFFFu;
+    for (int i = tid; i < kHistBins; i += NT) sh.bins[i] = 0u;
+    if (tid == 0) sh.s_ncand = 0u;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-      if (c0 + j < nv) {
-        kmx = key[j] > kmx ? key[j] : kmx;
-        kmn = key[j] < kmn ? key[j] : kmn;
-      }
-    }
-    kmx = wave_umax(kmx);
-    kmn = ~wave_umax(~kmn);   // min through the max of complements
-    if (lane == 0) {
-      ext[wave] = kmx;
-      ext[NT / 64 + wave] = kmn;
+      key[j] = order_key(v[j]);
+      vm |= (c0 + j < nv ? 1u : 0u) << j;
     }
   }
   __syncthreads();
-  // Level 1 on the value range: 4096 equal-width bins between the row's smallest and largest
-  // finite score.  Scores crowd a few of the fixed 12-bit key-prefix bins (the exponent and three
-  // mantissa bits), so LDS atomics collide and the threshold bin holds hundreds of entries; on the
-  // value range the bins hold a handful.  The bin index is a monotone function of the score
-  // (subtraction, multiplication by a positive scale and truncation all preserve order), so b*
-  // and the counts above it are exact.  When b* holds at most 64 entries one wave ranks them by
-  // their full keys; otherwise (ties, clusters, non-finite scores) the key-prefix levels run.
-  bool resolved = false;
-  {
-    uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-      kmax = ext[w] > kmax ? ext[w] : kmax;
-      kmin = ext[NT / 64 + w] < kmin ? ext[NT / 64 + w] : kmin;
-    }
-    const float vmin = key_value(kmin), vmax = key_value(kmax);
-    const float scale = 4096.f / (vmax - vmin);
-    // every visible key is finite (NaN maps below -inf, infinities outside +-FLT_MAX) and spread
-    const bool adaptive = kmin >= order_key(-3.40282347e+38f) && kmax <= order_key(3.40282347e+38f) &&
-                          kmax > kmin && scale > 0.f && scale < 3.0e38f;
-    if (adaptive) {
-      uint32_t bin[PER];
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const float x = (key_value(key[j]) - vmin) * scale;
-        // x >= 0 for visible entries; entries past n_vis (never counted) are clamped too
-        const uint32_t b = x < 4095.f ? (x > 0.f ? (uint32_t)x : 0u) : 4095u;
-        bin[j] = b;
-        if (c0 + j < nv) atomicAdd(&bins[b], 1u);
-      }
-      __syncthreads();
-      if (wave == 0) wave_find_desc(bins, kHistBins, (uint32_t)k, &s_digit, &s_before);
-      __syncthreads();
-      const uint32_t bstar = s_digit;
-      const uint32_t need1 = (uint32_t)k - s_before;
-      {
-        uint32_t hm = 0;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) hm |= (c0 + j < nv && bin[j] == bstar) ? (1u << j) : 0u;
-        const uint32_t hits = __popc(hm);
-        const uint32_t incl = wave_inclusive_scan(hits);
-        uint32_t base = 0;
-        if (lane == 63 && incl) base = atomicAdd(&s_ncand, incl);
-        base = __builtin_amdgcn_readlane(base, 63);
-        uint32_t pos = base + incl - hits;
-        while (hm) {
-          const int j = __ffs((int)hm) - 1;
-          hm &= hm - 1u;
-          if (pos < 64u) cand_key[pos] = key[j];
-          ++pos;
-        }
-      }
-      __syncthreads();
-      const uint32_t n_cand = s_ncand;
-      if (n_cand <= 64u) {
-        // rank the candidates by their keys: the threshold is the key with fewer than need1 keys
-        // above it and at least need1 at or above it
-        if (wave == 0) {
-          const uint32_t mine = lane < (int)n_cand ? cand_key[lane] : 0u;
-          uint32_t gt = 0, ge = 0;
-          for (int j = 0; j < (int)n_cand; ++j) {
-            const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, j);
-            gt += o > mine ? 1u : 0u;
-            ge += o >= mine ? 1u : 0u;
-          }
-          if (lane < (int)n_cand && gt < need1 && ge >= need1) {   // every such lane holds the same key
-            s_T = mine;
-            s_need = need1 - gt;
-          }
-        }
-        resolved = true;
-      } else {
-        for (int i = tid; i < kHistBins; i += NT) bins[i] = 0u;
-        if (tid == 0) s_ncand = 0u;
-        __syncthreads();
-      }
-    }
-  }
-  if (!resolved) {
-    // level 1: top 12 key bits of every entry (all lanes active: one LDS atomic instruction covers 64)
-  #pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if (c0 + j < nv) atomicAdd(&bins[key[j] >> kHistShift], 1u);
-    __syncthreads();
-    if (wave == 0) wave_find_desc(bins, kHistBins, (uint32_t)k, &s_digit, &s_before);
-    __syncthreads();
-    const uint32_t bstar = s_digit;
-    const uint32_t need1 = (uint32_t)k - s_before;   // entries still to take from bin b* (>= 1)
-    // the entries of bin b* become candidates: their keys are appended to LDS with one atomic per
-    // wave, a lane's after those of the lanes below it
-    {
-      uint32_t hm = 0;   // bit j: entry c0 + j is in b*
-  #pragma unroll
-      for (int j = 0; j < PER; ++j) hm |= (c0 + j < nv && (key[j] >> kHistShift) == bstar) ? (1u << j) : 0u;
-      const uint32_t hits = __popc(hm);
-      const uint32_t incl = wave_inclusive_scan(hits);
-      uint32_t base = 0;
-      if (lane == 63 && incl) base = atomicAdd(&s_ncand, incl);
-      base = __builtin_amdgcn_readlane(base, 63);
-      uint32_t pos = base + incl - hits;
-      while (hm) {
-        const int j = __ffs((int)hm) - 1;
-        hm &= hm - 1u;
-        if (pos < (uint32_t)kCandMax) cand_key[pos] = key[j];
-        ++pos;
-      }
-    }
-    __syncthreads();
-    const uint32_t n_cand = s_ncand;
-    if (n_cand <= (uint32_t)kCandMax) {
-      // wave 0 alone resolves the 20 low key bits among the candidates (two 10-bit levels in a
-      // wave-private histogram); LDS operations of one wave complete in order
-      if (wave == 0) {
-        uint32_t prefix = bstar, need = need1;
-  #pragma unroll 1
-        for (int lvl = 0; lvl < 2; ++lvl) {
-          const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
-  #pragma unroll
-          for (int i = 0; i < 1024; i += 256) *(uint4*)&bins[i + 4 * lane] = make_uint4(0u, 0u, 0u, 0u);
-          __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-          __builtin_amdgcn_wave_barrier();
-          // four candidates per lane per pass: their reads are all in flight before the first atomic
-          for (uint32_t i0 = 0; i0 < n_cand; i0 += 256) {
-            uint32_t kk[4];
-  #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const uint32_t i = i0 + 64 * u + lane;
-              kk[u] = cand_key[i < n_cand ? i : 0];
-            }
-  #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const uint32_t i = i0 + 64 * u + lane;
-              if (i < n_cand && (kk[u] >> (shift + 10)) == prefix) atomicAdd(&bins[(kk[u] >> shift) & 1023u], 1u);
-            }
-          }
-          __builtin_amdgcn_s_waitcnt(0xc07f);
-          __builtin_amdgcn_wave_barrier();
-          wave_find_desc(bins, 1024, need, &s_digit, &s_before);
-          __builtin_amdgcn_s_waitcnt(0xc07f);
-          __builtin_amdgcn_wave_barrier();
-          prefix = (prefix << 10) | s_digit;
-          need -= s_before;
-        }
-        if (lane == 0) {
-          s_T = prefix;
-          s_need = need;
-        }
-      }
-    } else {
-      // many entries share b* (heavily tied scores): levels 2 and 3 over the whole block, ten more
-      // key bits each, counting only entries with the current prefix
-      uint32_t prefix = bstar, need = need1;
-  #pragma unroll 1
-      for (int lvl = 0; lvl < 2; ++lvl) {
-        const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
-        for (int i = tid; i < 1024; i += NT) bins[i] = 0u;
-        __syncthreads();
-  #pragma unroll
-        for (int j = 0; j < PER; ++j) {
-          const bool hit = c0 + j < nv && (key[j] >> (shift + 10)) == prefix;
-          if (__any(hit) && hit) atomicAdd(&bins[(key[j] >> shift) & 1023u], 1u);
-        }
-        __syncthreads();
-        if (wave == 0) wave_find_desc(bins, 1024, need, &s_digit, &s_before);
-        __syncthreads();
-        prefix = (prefix << 10) | s_digit;
-        need -= s_before;
-      }
-      if (tid == 0) {
-        s_T = prefix;
-        s_need = need;
-      }
-    }
-  }
-  __syncthreads();
-  const uint32_t T = s_T;        // exact k-th largest key
-  const uint32_t need = s_need;  // the first `need` entries equal to T (in index order) are taken
-  uint32_t gm = 0, em = 0;       // bit j: entry c0 + j is above T / equal to T
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const bool ok = c0 + j < nv;
-    gm |= (ok && key[j] > T) ? (1u << j) : 0u;
-    em |= (ok && key[j] == T) ? (1u << j) : 0u;
-  }
-  const uint32_t n_gt = __popc(gm), n_eq = __popc(em);
-  // exclusive scan of (n_gt << 16 | n_eq) over threads (both totals stay below 2^16): a DPP scan
-  // inside each wave, the wave totals through LDS, one barrier
-  const uint32_t mine = (n_gt << 16) | n_eq;
-  const uint32_t incl = wave_inclusive_scan(mine);
-  if (lane == 63) scan[wave] = incl;
-  __syncthreads();
-  uint32_t pre = incl - mine;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) pre += w < wave ? scan[w] : 0u;
-  const uint32_t eq_before = pre & 0xFFFFu;
-  uint32_t pos = (pre >> 16) + (eq_before < need ? eq_before : need);
-  uint32_t take_eq = eq_before < need ? (need - eq_before < n_eq ? need - eq_before : n_eq) : 0u;
-  // the taken entries: all above T, and the lowest-index take_eq of those equal to T
-  uint32_t tm = gm;
-  for (uint32_t t = 0; t < take_eq; ++t) {
-    const uint32_t low = em & (0u - em);
-    tm |= low;
-    em ^= low;
-  }
-  // selected entries land in LDS in ascending index order, then go out in coalesced stores
-  while (tm) {
-    const int j = __ffs((int)tm) - 1;
-    tm &= tm - 1u;
-    if (pos < (uint32_t)k) sel[pos] = c0 + j;
-    ++pos;
-  }
-  __syncthreads();
+  block_threshold<NT, PER>(key, vm, (uint32_t)k, sh);
+  block_emit<NT, PER>(key, vm, sh.s_T, sh.s_need, (uint32_t)k, [&](int j) { return c0 + j; }, sh);
+  const int32_t* sel = (const int32_t*)sh.cand_sel;
   for (int i = tid; i < k; i += NT) {
     const int c = sel[i];
     out[i] = c;
     if (a.rows) a.rows[(int64_t)q * a.ld_rows + i] = row_of(c, pt_lds[c >> 6]);
   }
+}
+
+// ---- long decode rows: selection from the indexer's per-wave sketches.  Wave W of a row (entries
+// [512 W, 512 W + 512)) left its 8 largest scores (ascending indices) and a bound on the rest, so
+// the sketches of a 262,144-entry row are 4,096 entries in index order.  One block of 1024
+// threads finds their exact k-th largest key T as the short-row selection does.  If every wave's
+// bound lies below T, no entry left out of the sketches can reach T and the sketches' top k is the
+// row's; otherwise (ties at T, or a wave holding more than 8 of the row's top entries) the block
+// selects from the full score row instead (select_streamed).
+constexpr int kSketchMaxWaves = 2048;   // rows up to 2^20 entries
+
+// Exact selection over a whole score row by one block: three radix levels (12, 10, 10 bits of the
+// order key) over the row, then one pass in index order that places the selected entries with
+// block scans.  Reads the row four times; the fallback of the sketch path.
+template <int NT>
+__device__ void select_streamed(const TopkArgs& a, int q, int64_t nv, uint32_t k, SelShared<NT>& sh,
+                                int32_t* out, int32_t* rows_out, const int32_t* pt) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const float* row = a.logits + (int64_t)q * a.ld;
+  uint32_t prefix = 0u, need = k;
+  int pbits = 0;
+#pragma unroll 1
+  for (int lvl = 0; lvl < 3; ++lvl) {
+    const int wdt = lvl == 0 ? 12 : 10;
+    const int nb = 1 << wdt;
+    const int shift = 32 - pbits - wdt;
+    for (int i = tid; i < nb; i += NT) sh.bins[i] = 0u;
+    __syncthreads();
+    for (int64_t c = (int64_t)tid * 4; c < nv; c += (int64_t)NT * 4) {
+      // rows are 16-byte aligned and ld is a multiple of 64, so the 4-entry load stays in the row
+      const float4 x = *(const float4*)(row + c);
+      const float v[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = order_key(v[e]);
+        if (c + e < nv && (pbits == 0 || (key >> (32 - pbits)) == prefix))
+          atomicAdd(&sh.bins[(key >> shift) & (uint32_t)(nb - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) wave_find_desc(sh.bins, nb, need, &sh.s_digit, &sh.s_before);
+    __syncthreads();
+    prefix = (prefix << wdt) | sh.s_digit;
+    pbits += wdt;
+    need -= sh.s_before;
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  // placement in index order, 4 consecutive entries per thread and NT * 4 per pass
+  uint32_t gt_run = 0u, eq_run = 0u;   // selected-above / equal counts of earlier passes
+  for (int64_t base = 0; base < nv; base += (int64_t)NT * 4) {
+    const int64_t c0 = base + (int64_t)tid * 4;
+    uint32_t gm = 0u, em = 0u;
+    if (c0 < nv) {
+      const float4 x = *(const float4*)(row + c0);
+      const float v[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t key = order_key(v[e]);
+        const bool ok = c0 + e < nv;
+        gm |= (ok && key > T) ? (1u << e) : 0u;
+        em |= (ok && key == T) ? (1u << e) : 0u;
+      }
+    }
+    const uint32_t n_gt = __popc(gm), n_eq = __popc(em);
+    const uint32_t mine = (n_gt << 16) | n_eq;
+    const uint32_t incl = wave_inclusive_scan(mine);
+    if (lane == 63) sh.scan[wave] = incl;
+    __syncthreads();
+    uint32_t pre = incl - mine, tot = 0u;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+      pre += w < wave ? sh.scan[w] : 0u;
+      tot += sh.scan[w];
+    }
+    __syncthreads();   // sh.scan is rewritten by the next pass
+    const uint32_t eq_before = eq_run + (pre & 0xFFFFu);
+    uint32_t pos = gt_run + (pre >> 16) + (eq_before < need ? eq_before : need);
+    uint32_t take_eq = eq_before < need ? (need - eq_before < n_eq ? need - eq_before : n_eq) : 0u;
+    uint32_t tm = gm;
+    for (uint32_t t = 0; t < take_eq; ++t) {
+      const uint32_t low = em & (0u - em);
+      tm |= low;
+      em ^= low;
+    }
+    while (tm) {
+      const int e = __ffs((int)tm) - 1;
+      tm &= tm - 1u;
+      if (pos < k) {
+        const int c = (int)(c0 + e);
+        out[pos] = c;
+        if (rows_out) {
+          const int pg = pt[c >> 6];
+          rows_out[pos] = (unsigned)pg < (unsigned)a.num_pages ? pg * kPage + (c & (kPage - 1)) : -1;
+        }
+      }
+      ++pos;
+    }
+    gt_run += tot >> 16;
+    eq_run += tot & 0xFFFFu;
+    if (gt_run + (eq_run < need ? eq_run : need) >= k) break;   // block-uniform
+  }
+}
+
+template <int PER>
+__global__ __launch_bounds__(1024) void topk_sketch_kernel(TopkArgs a) {
+  constexpr int NT = 1024;
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const int64_t nv = topk_row_count(a, q);
+  const int k = a.k;
+  int32_t* out = a.idx + (int64_t)q * a.ld_idx;
+  int32_t* rows_out = a.rows ? a.rows + (int64_t)q * a.ld_rows : nullptr;
+  if (a.win_mode) write_window(a, q);
+  const int r = q / a.q_per_req;
+  const int32_t* pt = a.page_table + (int64_t)r * a.max_pages;
+  auto row_of = [&](int c) {
+    const int pg = pt[c >> 6];
+    return (unsigned)pg < (unsigned)a.num_pages ? pg * kPage + (c & (kPage - 1)) : -1;
+  };
+  if (nv <= k) {
+    for (int i = tid; i < k; i += NT) {
+      out[i] = i < nv ? i : -1;
+      if (rows_out) rows_out[i] = i < nv ? row_of(i) : -1;
+    }
+    return;
+  }
+  __shared__ SelShared<NT> sh;
+  const int64_t n_w = (nv + kSketchSpan - 1) / kSketchSpan;
+  const int64_t n_u = n_w * kSketchTop;               // sketch entries of the row (<= NT * PER)
+  const uint2* top = a.sk_top + (int64_t)q * a.sk_waves * kSketchTop;
+  const uint32_t* bound = a.sk_bound + (int64_t)q * a.sk_waves;
+  uint32_t key[PER];
+  uint32_t idx[PER];
+  uint32_t vm = 0u;
+  const int64_t u0 = (int64_t)tid * PER;            // this thread's sketch entries [u0, u0 + PER)
+#pragma unroll
+  for (int j = 0; j < PER; j += 2) {
+    const int64_t u = u0 + j;
+    const uint4 x = *(const uint4*)&top[u < n_u ? u : 0];   // two entries; n_u is a multiple of 8
+    key[j] = x.x; idx[j] = x.y; key[j + 1] = x.z; idx[j + 1] = x.w;
+  }
+  uint32_t bnd[(kSketchMaxWaves + NT - 1) / NT];
+#pragma unroll
+  for (int i = 0; i < (kSketchMaxWaves + NT - 1) / NT; ++i) {
+    const int64_t W = tid + (int64_t)i * NT;
+    bnd[i] = W < n_w ? bound[W] : 0u;
+  }
+  for (int i = tid; i < kHistBins; i += NT) sh.bins[i] = 0u;
+  if (tid == 0) sh.s_ncand = 0u;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) vm |= (u0 + j < n_u && idx[j] != 0xFFFFFFFFu ? 1u : 0u) << j;
+  {
+    const uint32_t wsum = wave_inclusive_scan(__popc(vm));   // lane 63 holds the wave's count
+    if ((tid & 63) == 63) sh.scan[tid >> 6] = wsum;
+  }
+  __syncthreads();
+  uint32_t n_real = 0u;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) n_real += sh.scan[w];
+  // a row whose sketches hold fewer than k entries is selected from its full scores
+  bool from_sketch = n_real >= (uint32_t)k;
+  if (from_sketch) {
+    block_threshold<NT, PER>(key, vm, (uint32_t)k, sh);
+    const uint32_t T = sh.s_T;
+    bool reach = false;
+#pragma unroll
+    for (int i = 0; i < (kSketchMaxWaves + NT - 1) / NT; ++i) reach |= tid + (int64_t)i * NT < n_w && bnd[i] >= T;
+    from_sketch = !__syncthreads_or(reach);
+  }
+  if (from_sketch) {
+    block_emit<NT, PER>(key, vm, sh.s_T, sh.s_need, (uint32_t)k, [&](int j) { return (int32_t)idx[j]; }, sh);
+    const int32_t* sel = (const int32_t*)sh.cand_sel;
+    for (int i = tid; i < k; i += NT) {
+      const int c = sel[i];
+      out[i] = c;
+      if (rows_out) rows_out[i] = row_of(c);
+    }
+    return;
+  }
+  select_streamed<NT>(a, q, nv, (uint32_t)k, sh, out, rows_out, pt);
 }
 
 hipError_t launch_topk_single(const TopkArgs& a, hipStream_t s) {
@@ -842,6 +1022,24 @@ hipError_t launch_topk_single(const TopkArgs& a, hipStream_t s) {
 }
 
 bool topk_single_ok(int64_t max_n_vis, int k) { return max_n_vis <= kSingleMax && k <= kSingleMax; }
+
+// Long rows of a one-query-per-request decode take the sketches when every row of the longest
+// length has at least 4 k of them (so the k-th largest lies well inside), up to 2^20 entries.
+bool topk_sketch_ok(int64_t max_n_vis, int k) {
+  const int64_t waves = (max_n_vis + kSketchSpan - 1) / kSketchSpan;
+  return k <= kSingleMaxK && waves <= kSketchMaxWaves && waves * kSketchTop >= 4 * (int64_t)k;
+}
+
+int64_t topk_sketch_waves(int64_t max_n_vis) { return (max_n_vis + kSketchSpan - 1) / kSketchSpan; }
+
+hipError_t launch_topk_sketch(const TopkArgs& a, hipStream_t s) {
+  const int64_t entries = topk_sketch_waves(a.max_n_vis) * kSketchTop;
+  ProfScope p("topk_sketch", s);
+  if (entries <= 1024 * 4) CSA_LAUNCH(p, (topk_sketch_kernel<4>), dim3((unsigned)a.Q), dim3(1024), s, a);
+  else if (entries <= 1024 * 8) CSA_LAUNCH(p, (topk_sketch_kernel<8>), dim3((unsigned)a.Q), dim3(1024), s, a);
+  else CSA_LAUNCH(p, (topk_sketch_kernel<16>), dim3((unsigned)a.Q), dim3(1024), s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s) {
   if (a.max_n_vis <= a.k) return hipSuccess;

@@ -1,0 +1,90 @@
+"""Long-context decode at and near its full size (rows of 131,072 to 262,144 compressed entries),
+through csa_decode as the benchmark runs it: the indexer leaves a per-wave sketch of each row and
+one block per query selects from the sketches, falling back to the full score row when a wave may
+hide a selected entry.  Acceptance as everywhere: band-tolerant top-k against the oracle's scores,
+then the oracle evaluated on the GPU's own index set."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from oracle import csa_oracle as O
+from tests.helpers import BF16_TOL, check_attention, check_topk_row
+from workloads import configs
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import long_context_sparse_csa_amd as csa
+    csa.lib()
+    return "cuda"
+
+
+def _say(msg):
+    print(f"[gpu] {msg}", flush=True)
+
+
+def _decode_and_check(wl, dev, empty_rows=()):
+    from workloads import run, torch_io
+    out, idx = run.decode(wl, torch_io.to_device(wl, dev))
+    out, idx = torch_io.out_to_numpy(out), idx.cpu().numpy()
+    errs = []
+    for qi in range(wl.Q):
+        nv = int(wl.n_vis[qi])
+        assert idx[qi, :128].tolist() == O.query_window(wl, qi).tolist(), f"query {qi}: window indices differ"
+        check_topk_row(idx[qi, 128:], O.query_scores(wl, qi), nv, wl.topk, f"query {qi}")
+        ref = O.attend(wl, qi, idx[qi, :128], idx[qi, 128:])
+        errs.append(check_attention(out[qi], ref, BF16_TOL, f"query {qi}"))
+    for r in empty_rows:
+        assert np.all(out[r] == 0.0), f"row {r} must be exact zero"
+    return out, idx, max(errs)
+
+
+def test_decode_long_full_size(dev):
+    """Two requests of the long-context workload at full size: 1,048,576 tokens, 262,144 entries in
+    4,096 pages, 1% planted; every query checked, and the selection lies inside the planted set."""
+    wl = configs.long_decode(B=2)
+    _say("decode long full size (B=2, T=1048576, H=64, fp8)")
+    _, idx, err = _decode_and_check(wl, dev)
+    for b in range(wl.B):
+        assert set(idx[b, 128:].tolist()) <= set(wl.planted[b].tolist())
+    _say(f"max err {err:.2e}")
+
+
+def test_decode_long_clustered_planted(dev):
+    """1% planted entries in one run of consecutive entries: the row's top 512 fill a few waves, so
+    those waves' sketches cannot hold them and the selection reads the full score row."""
+    wl = configs.make_decode("long_cluster", [1 << 19, 1 << 19], H=16, HI=64, seed=3, planted_frac=0.01,
+                             planted_contiguous=True)
+    _say("decode long clustered planted (B=2, T=524288)")
+    _, idx, err = _decode_and_check(wl, dev)
+    for b in range(wl.B):
+        assert set(idx[b, 128:].tolist()) <= set(wl.planted[b].tolist())
+    _say(f"max err {err:.2e}")
+
+
+def test_decode_long_all_scores_tied(dev):
+    """Every indexer key zero, so every score is exactly 0: the first 512 entries are selected (ties
+    go to the lower index), through the full-row fallback."""
+    base = configs.make_decode("long_tied", [1 << 19], H=16, HI=64, seed=5)
+    wl = dataclasses.replace(base, ik_keys=np.zeros_like(base.ik_keys))
+    _say("decode long, all scores tied (T=524288)")
+    _, idx, _ = _decode_and_check(wl, dev)
+    assert idx[0, 128:].tolist() == list(range(512))
+
+
+def test_decode_long_ragged_batch(dev):
+    """A long row beside short ones in one call: the long row takes the sketches; a row with fewer
+    sketch entries than k, one shorter than k and empty rows take the full-row and short-row
+    paths of the same launch."""
+    ctx = [1 << 19, 20000, 0, 3, 2052, (1 << 19) - 77]
+    wl = configs.make_decode("long_ragged", ctx, H=16, HI=64, seed=6, planted_frac=0.01)
+    _say(f"decode long ragged ctx={ctx}")
+    _, _, err = _decode_and_check(wl, dev, empty_rows=(2,))
+    _say(f"max err {err:.2e}")

@@ -395,3 +395,21 @@ def test_gather_rows_drops_negative_out_of_range_and_unmapped_slots():
     # an all-dropped list attends to nothing: exact zeros
     out = O.attend(wl, r, np.array([-1, wr]), np.array([-2, limit, 2 * 64]))
     assert np.all(out == 0.0)
+
+
+def test_long_context_planted_rows_keep_the_row_scale():
+    """Planted KV rows lean on the queries' summed direction yet keep the scale of the N(0, 1) rows
+    around them (expected squared norm 512), so outputs stay of order one as with unplanted rows."""
+    from workloads import codec
+    wl = configs.make_decode("t", [65536], H=8, HI=16, seed=2, planted_frac=0.01, kv_fmt=configs.KV_F32)
+    n = wl.planted[0]
+    rows = np.stack([O.kv_row_values(wl.kv_pool[wl.page_table[0, c // 64], c % 64], wl.kv_fmt) for c in n])
+    others = np.stack([O.kv_row_values(wl.kv_pool[wl.page_table[0, c // 64], c % 64], wl.kv_fmt)
+                       for c in np.setdiff1d(np.arange(2000), n)[:200]])
+    d = O.q_values(wl.q[0], wl.q_dt).sum(axis=0)
+    d /= np.linalg.norm(d)
+    assert codec.ROW_BYTES[wl.kv_fmt] == 2048
+    assert abs(np.mean(np.sum(rows ** 2, axis=1)) / 512 - 1.0) < 0.05
+    assert abs(np.mean(np.sum(others ** 2, axis=1)) / 512 - 1.0) < 0.05
+    cos = rows @ d / np.linalg.norm(rows, axis=1)
+    assert 0.85 < cos.mean() < 0.93

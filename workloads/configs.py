@@ -186,13 +186,14 @@ def _indexer_queries(g: np.random.Generator, Q: int, HI: int, idx_dt: int):
 def make_decode(name: str, ctx_len, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_BF16,
                 idx_dt=DT_FP8, kv_fmt=KV_FP8, win_fmt=None, seed: int = 0,
                 planted_frac: float = 0.0, topk: int = TOPK, ratio: int = COMPRESS,
-                q_per_req: int = 1) -> Workload:
+                q_per_req: int = 1, planted_contiguous: bool = False) -> Workload:
     """``q_per_req`` queries per request: the last tokens of a context of ``ctx_len[b]`` raw tokens
     (query b*q_per_req + j sits at position ctx_len[b] - q_per_req + j).  The window ring holds
     128 + q_per_req - 1 slots, so the earliest query's window is still in it.
 
     Sub-streams, spawned in this order: page permutation, q, sink, indexer q, w, indexer key pool,
-    KV pool, window ring, planted entries.
+    KV pool, window ring, planted entries.  ``planted_contiguous`` puts each request's planted
+    entries in one run of consecutive entries at a seeded offset instead of spreading them.
     """
     win_fmt = kv_fmt if win_fmt is None else win_fmt
     ctx_len = np.asarray(ctx_len, dtype=np.int32)
@@ -218,7 +219,11 @@ def make_decode(name: str, ctx_len, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_
         pg = g[8]
         for b in range(B):
             n_plant = int(round(planted_frac * n_c[b]))
-            planted.append(np.sort(pg.choice(n_c[b], size=n_plant, replace=False)).astype(np.int64))
+            if planted_contiguous:
+                start = int(pg.integers(0, n_c[b] - n_plant + 1))
+                planted.append(np.arange(start, start + n_plant, dtype=np.int64))
+            else:
+                planted.append(np.sort(pg.choice(n_c[b], size=n_plant, replace=False)).astype(np.int64))
 
         def key_override(codes, scales):
             # planted indexer key = alpha * u_b + 0.25 * N(0, I), where u_b is the unit vector whose
@@ -249,7 +254,10 @@ def make_decode(name: str, ctx_len, H: int, HI: int, *, q_dt=DT_BF16, out_dt=DT_
             n = planted[b]
             d = q_f[b * S + S - 1].astype(np.float64).sum(axis=0)
             d /= np.linalg.norm(d)
-            x = (2.0 * math.sqrt(512) * d[None, :] + g[8].standard_normal((n.size, 512))).astype(np.float32)
+            # a planted row leans on the queries' summed direction (cosine about 0.89) and keeps the
+            # scale of the N(0, 1) rows around it: (2 sqrt(512) d + N(0, I)) / sqrt(5) has the same
+            # expected squared norm, 512, as an N(0, I) row
+            x = ((2.0 * math.sqrt(512) * d[None, :] + g[8].standard_normal((n.size, 512))) / math.sqrt(5.0)).astype(np.float32)
             rows = page_table[b, n // PAGE].astype(np.int64) * PAGE + (n % PAGE)
             kv_pool[rows] = codec.pack_kv_rows(x, kv_fmt)
     kv_pool = kv_pool.reshape(total_pages, PAGE, -1)
