@@ -52,7 +52,8 @@ typedef enum {
   CSA_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned                                 */
   CSA_ERR_WORKSPACE = -5,   /* ws is NULL or smaller than the *_workspace_bytes query            */
   CSA_ERR_UNSUPPORTED = -6, /* a valid combination the library does not implement             */
-  CSA_ERR_HIP = -7          /* a HIP launch failed; csa_last_hip_error() holds the hipError_t   */
+  CSA_ERR_HIP = -7,         /* a HIP launch failed; csa_last_hip_error() holds the hipError_t   */
+  CSA_ERR_SCRATCH = -8      /* csa_decode_noalloc: the call needs more than its static scratch  */
 } csa_status;
 
 /* Element types of q, out and the indexer operands. */
@@ -197,6 +198,30 @@ csa_status csa_decode(int32_t B, int32_t H, int32_t HI, int32_t k,
                       void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * csa_decode_noalloc - csa_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same arguments and
+ * result, minus the workspace, which comes from a static device array of CSA_NOALLOC_SCRATCH_BYTES
+ * compiled into the library (each device the library runs on holds its own copy until the
+ * process ends).  The call allocates nothing and calls no allocating routine.
+ *   Limit: calls whose csa_decode_workspace_bytes(B, H, HI, max_ctx, k) exceeds
+ *   CSA_NOALLOC_SCRATCH_BYTES return CSA_ERR_SCRATCH before anything is enqueued.
+ *   The stream must belong to the current device.  Every call on a device shares that device's
+ *   array, which keeps the last call's contents: calls that overlap on one device (different
+ *   streams or host threads without ordering between them) race and must not be issued.
+ * Errors as csa_decode, plus CSA_ERR_SCRATCH, and CSA_ERR_HIP if the array's address cannot be
+ * obtained on the current device.
+ * ------------------------------------------------------------------------------------------- */
+#define CSA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+csa_status csa_decode_noalloc(int32_t B, int32_t H, int32_t HI, int32_t k,
+                              const void* q, int32_t q_dt, const float* sink,
+                              const void* qI, const uint8_t* qI_scale, int32_t qI_dt, const float* w,
+                              const csa_paged_idx* keys, const csa_paged_kv* comp,
+                              const void* win_ring, int32_t win_fmt,
+                              const int32_t* ctx_len, int64_t max_ctx,
+                              float softmax_scale, void* out, int32_t out_dt, int32_t* idx_out,
+                              hipStream_t stream);
+
+/* ---------------------------------------------------------------------------------------------
  * csa_decode_multi - a decode step that takes the last S tokens of each of B requests at once
  * (multi-token prediction / speculative decoding: [P1] section 2.17 MTPBlock, [P2]'s NextN
  * variant), through the same path as csa_decode.  Query b*S + j sits at position T_b - S + j and
@@ -323,8 +348,8 @@ csa_status csa_compress_index_keys(const void* kv_proj, const void* score_proj, 
  *                       `kernel` (e.g. "indexer_fp8"), the summed duration in ms and the number
  *                       of launches since the last reset; unknown names return 0 launches.
  *   csa_profile_reset   forgets all recorded events.
- * Profiling state is process-wide (a diagnostic, the library's only mutable state), guarded by a
- * mutex.
+ * Profiling state is process-wide (a diagnostic, the library's only mutable state apart from the
+ * scratch array of csa_decode_noalloc), guarded by a mutex.
  * ------------------------------------------------------------------------------------------- */
 const char* csa_status_string(int32_t status);
 int32_t csa_last_hip_error(void);

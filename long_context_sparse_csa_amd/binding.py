@@ -14,7 +14,8 @@ HEADER = os.path.join(os.path.dirname(HERE), "include", "csa.h")
 CSA_F32, CSA_BF16, CSA_FP8_E4M3FN, CSA_FP4_E2M1 = 0, 1, 2, 3
 CSA_KV_F32, CSA_KV_BF16, CSA_KV_FP8NOPE_BF16ROPE = 0, 1, 2
 STATUS = {0: "CSA_OK", -1: "CSA_ERR_NULL", -2: "CSA_ERR_SHAPE", -3: "CSA_ERR_DTYPE", -4: "CSA_ERR_ALIGN",
-          -5: "CSA_ERR_WORKSPACE", -6: "CSA_ERR_UNSUPPORTED", -7: "CSA_ERR_HIP"}
+          -5: "CSA_ERR_WORKSPACE", -6: "CSA_ERR_UNSUPPORTED", -7: "CSA_ERR_HIP", -8: "CSA_ERR_SCRATCH"}
+NOALLOC_SCRATCH_BYTES = 32 << 20   # CSA_NOALLOC_SCRATCH_BYTES of include/csa.h
 
 
 class CsaError(RuntimeError):
@@ -46,6 +47,8 @@ _SIGS = {
     "csa_decode_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I64, _I32]),
     "csa_decode": (_I32, [_I32, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _I32, _P, ctypes.POINTER(PagedIdx),
                           ctypes.POINTER(PagedKV), _P, _I32, _P, _I64, _F32, _P, _I32, _P, _P, _SZ, _P]),
+    "csa_decode_noalloc": (_I32, [_I32, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _I32, _P, ctypes.POINTER(PagedIdx),
+                                  ctypes.POINTER(PagedKV), _P, _I32, _P, _I64, _F32, _P, _I32, _P, _P]),
     "csa_decode_multi_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I64, _I32]),
     "csa_decode_multi": (_I32, [_I32, _I32, _I32, _I32, _I32, _P, _I32, _P, _P, _P, _I32, _P,
                                 ctypes.POINTER(PagedIdx), ctypes.POINTER(PagedKV), _P, _I32, _I32, _P, _I64, _F32,
@@ -164,6 +167,14 @@ def csa_decode(B, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys: PagedId
         B, H, HI, k, _ptr(q), q_dt, _ptr(sink), _ptr(qI), _ptr(qI_scale), qI_dt, _ptr(w), ctypes.byref(keys),
         ctypes.byref(comp), _ptr(win_ring), win_fmt, _ptr(ctx_len), max_ctx, softmax_scale, _ptr(out), out_dt,
         _ptr(idx_out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def csa_decode_noalloc(B, H, HI, k, q, q_dt, sink, qI, qI_scale, qI_dt, w, keys: PagedIdx, comp: PagedKV, win_ring,
+                       win_fmt, ctx_len, max_ctx, softmax_scale, out, out_dt, idx_out, stream=None):
+    _check("csa_decode_noalloc", lib().csa_decode_noalloc(
+        B, H, HI, k, _ptr(q), q_dt, _ptr(sink), _ptr(qI), _ptr(qI_scale), qI_dt, _ptr(w), ctypes.byref(keys),
+        ctypes.byref(comp), _ptr(win_ring), win_fmt, _ptr(ctx_len), max_ctx, softmax_scale, _ptr(out), out_dt,
+        _ptr(idx_out), _stream(stream)))
 
 
 def csa_decode_multi_workspace_bytes(B, S, H, HI, max_ctx, k) -> int:

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libcsa.so")
-SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "compressor.hip", "api.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "attention.hip", "compressor.hip", "noalloc.hip", "api.cpp"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

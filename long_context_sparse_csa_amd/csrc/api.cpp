@@ -215,6 +215,7 @@ const char* csa_status_string(int32_t s) {
     case CSA_ERR_WORKSPACE: return "workspace missing or too small";
     case CSA_ERR_UNSUPPORTED: return "unsupported combination";
     case CSA_ERR_HIP: return "HIP launch failed";
+    case CSA_ERR_SCRATCH: return "the call needs more than the static scratch array holds";
     default: return "unknown status";
   }
 }

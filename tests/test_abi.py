@@ -35,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(-7, 1):
+    for s in range(-8, 1):
         assert csa.csa_status_string(s) != "unknown status"
     assert csa.csa_status_string(5) == "unknown status"
     assert csa.csa_last_hip_error() == 0
