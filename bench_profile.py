@@ -78,8 +78,8 @@ def traffic(fetch_csv, write_csv, copy_bytes, config, out, cmd):
         fb = sum(f[k]) / len(f[k]) * 1024.0 * f_scale
         wb = sum(w.get(k, [0.0])) / max(1, len(w.get(k, []))) * 1024.0 * w_scale
         res["kernels"][k] = {"fetch_bytes": int(fb), "write_bytes": int(wb), "dispatches": len(f[k])}
-    # the last indexer kernel to appear is the one bench.py's roofline launches time back to back
-    idx = [k for k in res["kernels"] if "indexer_fp8" in k]
+    # the decode indexer the fused step runs (the roofline kernel of the decode workloads)
+    idx = [k for k in res["kernels"] if ("indexer_fp8" in k or "indexer_fp4" in k) and "prefill" not in k]
     if idx:
         k = idx[-1]
         res["bytes_per_launch"] = res["kernels"][k]["fetch_bytes"] + res["kernels"][k]["write_bytes"]

@@ -348,11 +348,18 @@ csa_status csa_compress_index_keys(const void* kv_proj, const void* score_proj, 
  *                       `kernel` (e.g. "indexer_fp8"), the summed duration in ms and the number
  *                       of launches since the last reset; unknown names return 0 launches.
  *   csa_profile_reset   forgets all recorded events.
+ *   csa_debug_violations  debug builds (compiled with -DCSA_DEBUG_CHECKS): the number of device-
+ *                       resident values the kernels masked as invalid since the last call (an
+ *                       index that is not -1 but lies at or past its source or on an unmapped page,
+ *                       a visible indexer page with no page id in the pool), then clears it; read
+ *                       after the work is complete (synchronise first).  Release builds return
+ *                       CSA_ERR_UNSUPPORTED with *count = 0.
  * Profiling state is process-wide (a diagnostic, the library's only mutable state apart from the
- * scratch array of csa_decode_noalloc), guarded by a mutex.
+ * scratch array of csa_decode_noalloc and the debug counters), guarded by a mutex.
  * ------------------------------------------------------------------------------------------- */
 const char* csa_status_string(int32_t status);
 int32_t csa_last_hip_error(void);
+csa_status csa_debug_violations(uint64_t* count);
 csa_status csa_profile_enable(int32_t on);
 csa_status csa_profile_collect(const char* kernel, double* total_ms, int64_t* launches);
 csa_status csa_profile_reset(void);

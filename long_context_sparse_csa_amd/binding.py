@@ -8,7 +8,9 @@ import os
 import re
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libcsa.so")
+# CSA_LIB names another build of the library to load instead (the host-only sanitizer build the
+# CPU ABI tests run against); by default the in-tree gfx950 build
+LIB_PATH = os.environ.get("CSA_LIB") or os.path.join(HERE, "libcsa.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "csa.h")
 
 CSA_F32, CSA_BF16, CSA_FP8_E4M3FN, CSA_FP4_E2M1 = 0, 1, 2, 3
@@ -68,6 +70,7 @@ _SIGS = {
                                        _I32, _I32, _P, _I32, _P]),
     "csa_status_string": (ctypes.c_char_p, [_I32]),
     "csa_last_hip_error": (_I32, []),
+    "csa_debug_violations": (_I32, [ctypes.POINTER(ctypes.c_uint64)]),
     "csa_profile_enable": (_I32, [_I32]),
     "csa_profile_collect": (_I32, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "csa_profile_reset": (_I32, []),
@@ -247,6 +250,13 @@ def csa_status_string(status: int) -> str:
 
 def csa_last_hip_error() -> int:
     return int(lib().csa_last_hip_error())
+
+
+def csa_debug_violations() -> int:
+    """Masked-value count of a debug build since the last call (raises on release builds)."""
+    n = ctypes.c_uint64(0)
+    _check("csa_debug_violations", lib().csa_debug_violations(ctypes.byref(n)))
+    return int(n.value)
 
 
 def csa_profile_enable(on: bool):

@@ -2,6 +2,7 @@
 // Every check runs on the host before anything is enqueued; kernels never see an argument that
 // could send them out of bounds (device-resident values are masked inside the kernels).
 #include <cmath>
+#include <cstdlib>
 #include <cstdint>
 #include <cstring>
 #include <mutex>
@@ -157,6 +158,23 @@ csa_status check_attn_common(const void* q, int32_t q_dt, int32_t H, const float
   return CSA_OK;
 }
 
+// CSA_FAULT_INJECT=launch (read once per process): every entry point fails as a kernel launch
+// would, with CSA_ERR_HIP and hipErrorLaunchFailure, after validating its arguments and before
+// enqueuing anything.  For tests of callers' error handling; off by default.
+bool fault_inject_launch() {
+  static const bool on = [] {
+    const char* e = getenv("CSA_FAULT_INJECT");
+    return e != nullptr && strcmp(e, "launch") == 0;
+  }();
+  return on;
+}
+
+csa_status injected_fault() {
+  if (!fault_inject_launch()) return CSA_OK;
+  g_last_hip = (int32_t)hipErrorLaunchFailure;
+  return CSA_ERR_HIP;
+}
+
 #define CSA_TRY(x)                      \
   do {                                  \
     csa_status _s = (x);                \
@@ -222,6 +240,24 @@ const char* csa_status_string(int32_t s) {
 
 int32_t csa_last_hip_error(void) { return g_last_hip; }
 
+csa_status csa_debug_violations(uint64_t* count) {
+  if (!count) return CSA_ERR_NULL;
+#ifdef CSA_DEBUG_CHECKS
+  const uint64_t parts[3] = {csa::debug_take_violations_attention(), csa::debug_take_violations_indexer(),
+                             csa::debug_take_violations_topk()};
+  uint64_t n = 0;
+  for (uint64_t p : parts) {
+    if (p == ~0ull) return (csa_status)csa::record_hip_error(hipErrorInvalidSymbol);
+    n += p;
+  }
+  *count = n;
+  return CSA_OK;
+#else
+  *count = 0;
+  return CSA_ERR_UNSUPPORTED;
+#endif
+}
+
 csa_status csa_profile_enable(int32_t on) {
   std::lock_guard<std::mutex> lk(g_prof_mu);
   g_prof_on = on != 0;
@@ -276,6 +312,7 @@ csa_status csa_indexer_logits(const void* qI, const uint8_t* qI_scale, int32_t q
   a.page_table = keys->page_table; a.max_pages = keys->max_pages;
   a.q_req = q_req; a.n_req = n_req; a.n_vis = n_vis; a.Q = Q; a.HI = HI;
   a.max_n_vis = max_n_vis; a.logits = logits; a.ld = ld; a.hist = nullptr;
+  CSA_TRY(injected_fault());
   return hip_status(csa::launch_indexer(a, stream));
 }
 
@@ -295,6 +332,7 @@ csa_status csa_topk(const float* logits, int64_t ld, const int32_t* n_vis, int32
   const size_t need = csa_topk_workspace_bytes(Q, max_n_vis, k);
   if (!ws || ws_bytes < need) return CSA_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return CSA_ERR_ALIGN;
+  CSA_TRY(injected_fault());
   Carver c(ws);
   TopkWs w = carve_topk(c, Q, max_n_vis, k);
   if (csa::topk_single_ok(max_n_vis, k) && ld % 4 == 0 && aligned(logits, 16)) {
@@ -355,6 +393,7 @@ csa_status csa_sparse_attn(const void* q, int32_t q_dt, int32_t Q, int32_t H, co
   a.n_split = csa::attn_uses_matrix_cores(q_dt, a.win_fmt, a.comp_fmt, n_win, n_comp)
                   ? csa::plan_attn_split(Q, H, n_idx, q_dt) : 1;
   a.part = (float*)ws;
+  CSA_TRY(injected_fault());
   return hip_status(csa::launch_attention(a, stream));
 }
 
@@ -374,6 +413,7 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   if (!ws || ws_bytes < sizer.off) return CSA_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return CSA_ERR_ALIGN;
   if (idx_out && !aligned(idx_out, 4)) return CSA_ERR_ALIGN;
+  CSA_TRY(injected_fault());
   Carver c(ws);
   PathWs pw = carve_path(c, rows, H, n_query, k, path);
   int32_t* idx = idx_out ? idx_out : pw.idx;
@@ -554,6 +594,7 @@ csa_status run_hca(int mode, int32_t rows, int32_t H, const void* q, int32_t q_d
   HcaWs w = carve_hca(c, rows, H, n_comp);
   if (!ws || ws_bytes < c.off) return CSA_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return CSA_ERR_ALIGN;
+  CSA_TRY(injected_fault());
   const int64_t ld_idx = kWin + n_comp;
   csa::PrepArgs p{};
   p.mode = mode; p.rows = rows; p.ctx_len = ctx_len; p.max_ctx = max_ctx; p.pos0 = pos0;
@@ -642,6 +683,7 @@ csa_status csa_compress_kv(const void* kv_proj, const void* score_proj, int32_t 
   if (!kv_fmt_ok(pool_fmt)) return CSA_ERR_DTYPE;
   if (!aligned(pool_rows, 16)) return CSA_ERR_ALIGN;
   a.out = (uint8_t*)pool_rows; a.out_fmt = pool_fmt;
+  CSA_TRY(injected_fault());
   return hip_status(csa::launch_compress(a, stream));
 }
 
@@ -658,6 +700,7 @@ csa_status csa_compress_index_keys(const void* kv_proj, const void* score_proj, 
   if (key_dt != CSA_FP8_E4M3FN && key_dt != CSA_FP4_E2M1) return CSA_ERR_DTYPE;
   if (!aligned(keys, 16)) return CSA_ERR_ALIGN;
   a.out = (uint8_t*)keys; a.out_fmt = key_dt; a.out_scales = scales;
+  CSA_TRY(injected_fault());
   return hip_status(csa::launch_compress(a, stream));
 }
 

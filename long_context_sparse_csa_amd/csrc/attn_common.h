@@ -6,7 +6,6 @@
 
 namespace csa {
 
-constexpr int kTile = 32;
 constexpr int kKrStride = 528;   // bf16 per row of the row-major tile (1056 B, 16-B aligned)
 constexpr float kRescaleLog2 = 8.f;
 
@@ -79,6 +78,7 @@ __device__ __forceinline__ void slot_codes4(const AttnArgs& a, int q, int r, con
         o = has_pt && v[k] < n_entries && (unsigned)pg[k] < (unsigned)a.comp_num_pages;
         if (o) c = (uint64_t)(uintptr_t)(a.comp + ((int64_t)pg[k] * kPage + (v[k] & 63)) * comp_rb) | kCodeComp;
       }
+      CSA_DBG_COUNT(!o);   // an index that is not -1 yet has no row
     }
     code[k] = c;
     ok[k] = o;

@@ -1,7 +1,18 @@
 // Device-side helpers shared by the CSA kernels (gfx950 / CDNA4, wave64).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "csa_internal.h"
+
+// Launch kernel K on stream S; while profiling is on, the scope P's events are attached to the
+// dispatch itself (hipExtLaunchKernelGGL), so they bracket the kernel's execution.
+#define CSA_LAUNCH(P, K, GRID, BLOCK, S, ...)                                               \
+  do {                                                                                      \
+    (P).mark();                                                                             \
+    hipExtLaunchKernelGGL(K, GRID, BLOCK, 0, S, (P).ev0, (P).ev1, 0, __VA_ARGS__);          \
+  } while (0)
 
 namespace csa {
 
@@ -17,13 +28,35 @@ constexpr int kPage = 64;       // compressed entries per page
 constexpr int kWin = 128;       // sliding window
 constexpr int kHistBins = 4096; // top-k coarse histogram: top 12 bits of the order key
 constexpr int kHistShift = 20;
-constexpr int kSketchTop = 8;       // long-row sketch: largest scores kept per wave of the indexer
-constexpr int kSketchSpan = 512;    // entries scored by one indexer wave (8 pages)
+
+// Debug builds (-DCSA_DEBUG_CHECKS) count the device-resident values the kernels mask as invalid
+// (an index at or past its source, a page id outside the pool) into one counter per translation
+// unit, read and cleared by csa_debug_violations; release builds compile the counting away.
+#ifdef CSA_DEBUG_CHECKS
+static __device__ unsigned long long csa_dbg_violations;
+#define CSA_DBG_COUNT(cond)                                     \
+  do {                                                          \
+    if (cond) atomicAdd(&csa_dbg_violations, 1ull);             \
+  } while (0)
+#define CSA_DBG_ACCESSOR(NAME)                                                                            \
+  uint64_t NAME() {                                                                                       \
+    unsigned long long v = 0, z = 0;                                                                      \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(csa_dbg_violations), sizeof v, 0, hipMemcpyDeviceToHost) !=    \
+        hipSuccess)                                                                                       \
+      return ~0ull;                                                                                       \
+    (void)hipMemcpyToSymbol(HIP_SYMBOL(csa_dbg_violations), &z, sizeof z, 0, hipMemcpyHostToDevice);     \
+    return v;                                                                                             \
+  }
+#else
+#define CSA_DBG_COUNT(cond) \
+  do {                      \
+  } while (0)
+#define CSA_DBG_ACCESSOR(NAME)
+#endif
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kNegBig = -1.0e30f;   // finite running-max start: an all-invalid row yields 0
 
-enum RowFmt : int { kRowF32 = 0, kRowBF16 = 1, kRowFP8 = 2 };
 
 __host__ __device__ constexpr int row_bytes(int fmt) {
   return fmt == kRowF32 ? 2048 : (fmt == kRowBF16 ? 1024 : 608);

@@ -1,16 +1,33 @@
 // Internal host-side interface between the C ABI layer (api.cpp) and the kernel launchers.
 #pragma once
-#include <hip/hip_ext.h>
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
+#include <hip/hip_vector_types.h>
 #include <stdint.h>
 
 namespace csa {
+
+// Sizes and codes the kernels and the host planners (plan.cpp) share.
+enum RowFmt : int { kRowF32 = 0, kRowBF16 = 1, kRowFP8 = 2 };   // KV row formats (CSA_KV_* codes)
+constexpr int kSketchTop = 8;            // long-row sketch: largest scores kept per indexer wave
+constexpr int kSketchSpan = 512;         // entries scored by one indexer wave (8 pages)
+constexpr int kTile = 32;                // attention: slots per tile
+constexpr int kMaxSlots = 1024;          // attention: slots of one block; longer lists are split
+constexpr int kMaxSplit = 32;            // attention: key-range splits of one query
+constexpr int kSingleMax = 1024 * 32;    // one-block selection: longest row (1024 threads of 32)
+constexpr int kSingleMaxK = 2048;        // one-block selection: largest k
+constexpr int kSketchMaxWaves = 2048;    // sketch selection: rows up to 2^20 entries
+constexpr int kRowD = 512;               // head dim
+
+// Debug builds only (-DCSA_DEBUG_CHECKS): masked-value counters of each kernel file, read and cleared.
+uint64_t debug_take_violations_attention();
+uint64_t debug_take_violations_indexer();
+uint64_t debug_take_violations_topk();
 
 // Records e as the calling thread's last HIP error and returns CSA_ERR_HIP.
 int32_t record_hip_error(hipError_t e);
 
 // Per-launch timing while profiling is on (see csa_profile_enable): the scope owns two events that
-// CSA_LAUNCH attaches to the kernel's own dispatch, so they bracket its execution on the GPU, not
+// CSA_LAUNCH (csa_device.h) attaches to the kernel's own dispatch, so they bracket its execution on the GPU, not
 // its enqueue.  With profiling off both events are null and the launch is an ordinary one.
 struct ProfScope {
   ProfScope(const char* name, hipStream_t s);
@@ -19,11 +36,6 @@ struct ProfScope {
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
 };
 
-#define CSA_LAUNCH(P, K, GRID, BLOCK, S, ...)                                               \
-  do {                                                                                      \
-    (P).mark();                                                                             \
-    hipExtLaunchKernelGGL(K, GRID, BLOCK, 0, S, (P).ev0, (P).ev1, 0, __VA_ARGS__);          \
-  } while (0)
 
 struct IndexerArgs {
   const void* qI;             // [Q][HI][128] fp8 bytes or fp32
@@ -186,6 +198,7 @@ struct CompressArgs {
 hipError_t launch_compress(const CompressArgs& a, hipStream_t s);
 
 int plan_attn_split(int Q, int H, int n_idx, int q_dt);
+int attn_head_block(int Q, int H, int n_idx);   // 16 or 64 heads per block of the matrix-core kernels
 // true when the BF16 matrix-core kernel serves this call (bf16 q, BF16/FP8 rows); else the fp32 kernel
 bool attn_uses_matrix_cores(int q_dt, int win_fmt, int comp_fmt, int n_win, int n_comp);
 size_t attn_partial_bytes(int Q, int H, int n_idx);

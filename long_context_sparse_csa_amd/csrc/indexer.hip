@@ -342,6 +342,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
     const int64_t c0 = (p_first + i) * kPage;
     const bool mapped = page_ok(i);
     const int64_t c = c0 + 4 * n + g;
+    CSA_DBG_COUNT(lane == 0 && !mapped && c0 < nv_max);   // a visible page with no page id in the pool
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       const float score = score_page<NHG, FP4>(qa[j], qsc[j], wv[j], kb, ksc);
@@ -615,5 +616,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
 #undef CSA_IDX_LAUNCH
   return hipGetLastError();
 }
+
+CSA_DBG_ACCESSOR(debug_take_violations_indexer)
 
 }  // namespace csa

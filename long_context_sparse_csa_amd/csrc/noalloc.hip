@@ -5,6 +5,8 @@
 // with that device current) and only that address is ever handed to kernels or copies.
 #include <mutex>
 
+#include <hip/hip_runtime.h>
+
 #include "../../include/csa.h"
 #include "csa_internal.h"
 

@@ -470,10 +470,8 @@ __global__ __launch_bounds__(256) void topk_finish_kernel(TopkArgs a) {
 //      indices in ascending order (equal keys at T in index order) in LDS, from where they are
 //      written with coalesced stores.
 constexpr int kSinglePer = 16;      // entries per thread, in index order (32 for the longest rows)
-constexpr int kSingleMax = 1024 * 32;   // longest row: 1024 threads of 32 entries
 constexpr int kCandMax = 2048;      // entries of the threshold bin resolved by one wave; more take
                                     // the block-wide path
-constexpr int kSingleMaxK = 2048;   // largest k
 
 // One wave scans `nb` bins (64 to 4096, a multiple of 256) from the top and finds the bin where
 // the running count first reaches `need` (1 <= need <= total): *digit, *before (count strictly
@@ -824,7 +822,11 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
   for (int i = tid; i < k; i += NT) {
     const int c = sel[i];
     out[i] = c;
-    if (a.rows) a.rows[(int64_t)q * a.ld_rows + i] = row_of(c, pt_lds[c >> 6]);
+    if (a.rows) {
+      const int rw = row_of(c, pt_lds[c >> 6]);
+      CSA_DBG_COUNT(rw < 0);   // a selected entry on a page with no page id in the pool
+      a.rows[(int64_t)q * a.ld_rows + i] = rw;
+    }
   }
 }
 
@@ -835,7 +837,6 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
 // bound lies below T, no entry left out of the sketches can reach T and the sketches' top k is the
 // row's; otherwise (ties at T, or a wave holding more than 8 of the row's top entries) the block
 // selects from the full score row instead (select_streamed).
-constexpr int kSketchMaxWaves = 2048;   // rows up to 2^20 entries
 
 // Exact selection over a whole score row by one block: three radix levels (12, 10, 10 bits of the
 // order key) over the row, then one pass in index order that places the selected entries with
@@ -1001,7 +1002,11 @@ __global__ __launch_bounds__(1024) void topk_sketch_kernel(TopkArgs a) {
     for (int i = tid; i < k; i += NT) {
       const int c = sel[i];
       out[i] = c;
-      if (rows_out) rows_out[i] = row_of(c);
+      if (rows_out) {
+        const int rw = row_of(c);
+        CSA_DBG_COUNT(rw < 0);
+        rows_out[i] = rw;
+      }
     }
     return;
   }
@@ -1020,17 +1025,6 @@ hipError_t launch_topk_single(const TopkArgs& a, hipStream_t s) {
     CSA_LAUNCH(p, (topk_single_kernel<1024, 32>), dim3((unsigned)a.Q), dim3(1024), s, a);
   return hipGetLastError();
 }
-
-bool topk_single_ok(int64_t max_n_vis, int k) { return max_n_vis <= kSingleMax && k <= kSingleMax; }
-
-// Long rows of a one-query-per-request decode take the sketches when every row of the longest
-// length has at least 4 k of them (so the k-th largest lies well inside), up to 2^20 entries.
-bool topk_sketch_ok(int64_t max_n_vis, int k) {
-  const int64_t waves = (max_n_vis + kSketchSpan - 1) / kSketchSpan;
-  return k <= kSingleMaxK && waves <= kSketchMaxWaves && waves * kSketchTop >= 4 * (int64_t)k;
-}
-
-int64_t topk_sketch_waves(int64_t max_n_vis) { return (max_n_vis + kSketchSpan - 1) / kSketchSpan; }
 
 hipError_t launch_topk_sketch(const TopkArgs& a, hipStream_t s) {
   const int64_t entries = topk_sketch_waves(a.max_n_vis) * kSketchTop;
@@ -1116,5 +1110,7 @@ hipError_t launch_prep(const PrepArgs& a, hipStream_t s) {
   CSA_LAUNCH(p, prep_kernel, dim3((unsigned)blocks), dim3(256), s, a);
   return hipGetLastError();
 }
+
+CSA_DBG_ACCESSOR(debug_take_violations_topk)
 
 }  // namespace csa

@@ -264,3 +264,10 @@ def test_profile_toggle_without_launches():
     assert csa.csa_profile_collect("indexer_fp8") == (0.0, 0)
     csa.csa_profile_enable(False)
     csa.csa_profile_reset()
+
+
+def test_debug_counter_is_a_debug_build_feature():
+    import ctypes
+    n = ctypes.c_uint64(7)
+    assert csa.lib().csa_debug_violations(ctypes.byref(n)) == -6 and n.value == 0
+    assert csa.lib().csa_debug_violations(None) == -1
