@@ -3,11 +3,17 @@
   python bench_profile.py trace   <kernel_trace.csv> <out.txt> "<command>"
   python bench_profile.py traffic <fetch_counter_collection.csv> <write_counter_collection.csv>
                                   <copy_bytes> <config> <out.json> "<command>"
+  python bench_profile.py mfma    <counter_collection.csv> <out.json> "<command>"
 
 `traffic` scales the per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of each csa kernel by what the same
 counters read for the plain device copy of `copy_bytes` bytes that bench.py --calibrate-copy runs
 (each copy reads and writes copy_bytes), and records the indexer kernel source hash so bench.py can
 tell whether the figure still describes the current kernel.
+
+`mfma` averages every counter of each csa kernel over its dispatches and derives matrix-core use:
+GRBM_GUI_ACTIVE sums the eight XCDs' busy cycles, SQ_VALU_MFMA_BUSY_CYCLES the busy cycles of all
+1,024 SIMDs, so busy / (1024 * GRBM_GUI_ACTIVE / 8) is the share of SIMD time the matrix cores
+worked; SQ_INSTS_VALU_MFMA_MOPS_BF16 * 512 is the bf16 FLOP count of the dispatch.
 """
 import collections
 import csv
@@ -89,10 +95,34 @@ def traffic(fetch_csv, write_csv, copy_bytes, config, out, cmd):
     print(json.dumps(res, indent=1))
 
 
+def mfma(csv_path, out, cmd, xcds=8, simds=1024):
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(csv_path)):
+        k = _short(r["Kernel_Name"])
+        if "csa::" in k:
+            vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    res = {"command": cmd, "kernels": {}}
+    for k, d in vals.items():
+        avg = {c: sum(v) / len(v) for c, v in d.items()}
+        e = {"dispatches": max(len(v) for v in d.values()),
+             "counters": {c: int(round(v)) for c, v in avg.items()}}
+        if "GRBM_GUI_ACTIVE" in avg and "SQ_VALU_MFMA_BUSY_CYCLES" in avg and avg["GRBM_GUI_ACTIVE"] > 0:
+            e["mfma_busy_frac"] = round(avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (simds * avg["GRBM_GUI_ACTIVE"] / xcds), 4)
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
+            e["bf16_gflop"] = round(avg["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e9, 2)
+        if "SQ_INSTS_VALU" in avg and avg.get("SQ_INSTS_MFMA"):
+            e["valu_per_mfma"] = round(avg["SQ_INSTS_VALU"] / avg["SQ_INSTS_MFMA"], 2)
+        res["kernels"][k] = e
+    open(out, "w").write(json.dumps(res, indent=1) + "\n")
+    print(json.dumps(res, indent=1))
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "trace":
         trace(*sys.argv[2:5])
     elif sys.argv[1] == "traffic":
         traffic(*sys.argv[2:8])
+    elif sys.argv[1] == "mfma":
+        mfma(*sys.argv[2:5])
     else:
         sys.exit(__doc__)

@@ -119,6 +119,11 @@ typedef struct {
  *             position t: (t+1)/4).  Clamped to [0, min(max_n_vis, 64*max_pages)].
  *   logits    [Q][ld] fp32 out: s[c] for c < n_vis[q], -INFINITY for n_vis[q] <= c < max_n_vis;
  *             columns >= max_n_vis are not written.
+ * Arithmetic: every product of two dequantised codes is exact and the dot products accumulate in
+ * fp32 (FP8 codes are converted exactly to bf16 with their block scales folded in; E2M1 products
+ * are exact on the FP4 matrix cores), then ReLU, the weights and the head sum in fp32.  FP8 scale
+ * bytes must lie in [10, 245] (an FP8 value times its scale is then a normal bf16); 0xFF (NaN)
+ * is not supported.
  * Ranges: 1 <= Q, 1 <= HI <= 64, 0 <= max_n_vis <= ld, n_req >= 1.
  * ------------------------------------------------------------------------------------------- */
 csa_status csa_indexer_logits(const void* qI, const uint8_t* qI_scale, int32_t qI_dt,

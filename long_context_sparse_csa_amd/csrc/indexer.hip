@@ -5,24 +5,35 @@
 //     s[c] = sum_h w[h] * max(0, qI[h] . kI[c])
 // with FP8 E4M3FN or FP4 E2M1 operands that carry one E8M0 scale per 32 elements.
 //
-// FP8 path: one v_mfma_scale_f32_16x16x128_f8f6f4 covers 16 heads x 16 entries x all 128 dims, and
-// its per-lane E8M0 scale operands are exactly the stored per-32 block scales, so dequantisation
-// costs nothing.  Operand layout (measured on gfx950): lane l = m + 16*g holds row m, bytes 0..15
-// -> k in [16g, 16g+16), bytes 16..31 -> k in [64+16g, 64+16g+16); its scale byte scales row m's
-// 32-element block g.  A wave scores one page (64 entries) per step: MFMA column n of key group kg
-// is slot 4n+kg, so lane l's scale dword is word l of the page's [4 blocks][64 slots] scale array
-// and the key group picks the byte (opsel).  The epilogue applies ReLU and the head weights, then a
-// 2-step reduce-scatter over the four lane groups leaves lane l with the full score of slot
-// 4*(l%16) + l/16.  Decode: keys stream straight from HBM into VGPRs (no LDS), each lane loads
-// 2 x 16 B per key group, and each page is read exactly once.  Causal prefill, where all queries
-// share one request's keys, stages key pages in LDS per block of queries instead (see below).
+// FP8 path: the scores go through the bf16 matrix cores (v_mfma_f32_16x16x32_bf16), not the
+// FP8 ones.  Measured on gfx950, the FP8 instructions (v_mfma_f32_16x16x32_fp8_fp8 and the scaled
+// v_mfma_scale_f32_16x16x128_f8f6f4) sum each run of eight products on a fixed-point grid about
+// 16 bits below the largest of them: 448*448 + 1.75 comes back as 448*448, and
+// 448*448 - 448*448 + 0.125 as 0.  On random E4M3 operands the error reaches 1.4e-4 of the sum
+// of |products|, and on the 8192-token causal prefill it moved scores by up to 5.8e-5, enough to
+// swap the 512th and 513th entries of rows whose cut falls near a score of zero.  The bf16
+// instruction keeps every product exact and rounds like fp32 (2.6e-7 of the sum of |products|
+// on the same operands).  Every E4M3 value times a power-of-two scale is a bf16 value, so
+// v_cvt_scalef32_pk_bf16_fp8 converts two codes per instruction exactly, folding the E8M0 block
+// scale in (scale bytes 10..245 keep every converted value a normal bf16).  Operand layout: lane
+// l = n + 16*g holds bytes [16g, 16g+16) and [64+16g, 64+16g+16) of row n (the query head, or
+// the key 4n+kg of key group kg), i.e. elements of scale blocks g/2 and 2 + g/2; the four
+// 16x16x32 MFMAs of a key group take the lane's bytes eight at a time, and A and B use the same
+// layout, so codes pair up element by element.  A wave scores one page (64 entries) per step:
+// MFMA column n of key group kg is slot 4n+kg.  The epilogue applies ReLU and the head weights,
+// then a 2-step reduce-scatter over the four lane groups leaves lane l with the full score of
+// slot 4*(l%16) + l/16.  Decode: keys stream straight from HBM into VGPRs (no LDS), each lane
+// loads 2 x 16 B per key group, and each page is read exactly once.  Causal prefill, where all
+// queries share one request's keys, stages key pages in LDS per block of queries instead (see
+// below).
 //
-// FP4 path (two E2M1 codes per byte, element 2i in the low nibble): the same instruction with both
-// operand formats set to FP4 reads four registers per lane, and lane l = m + 16*g's 32 codes all
-// fall in scale block g (measured on gfx950).  Lane (m, g) therefore loads the one contiguous
-// 16-byte chunk of row m that holds elements [32g, 32g+32), and the scale operands are exactly the
-// FP8 path's.  A and B use the same lane layout, so codes pair up element by element.  Rows are
-// 64 bytes, a key page 4 KB: half the FP8 key traffic, at the same matrix-core cost per page.
+// FP4 path (two E2M1 codes per byte, element 2i in the low nibble): the scaled instruction
+// v_mfma_scale_f32_16x16x128_f8f6f4 with both operand formats set to FP4, which reads four
+// registers per lane.  Lane l = m + 16*g's 32 codes all fall in scale block g (measured on gfx950),
+// so lane (m, g) loads the one contiguous 16-byte chunk of row m that holds elements [32g, 32g+32)
+// and its scale operands are the stored block scales.  E2M1 products are multiples of 1/4 below
+// 36, so every run of them is exact on the instruction's grid (measured: no error on random
+// operands).  Rows are 64 bytes, a key page 4 KB: half the FP8 key traffic.
 #include <cstdlib>
 
 #include "csa_device.h"
@@ -34,10 +45,34 @@ namespace csa {
 template <bool FP4>
 constexpr int kRowB = FP4 ? kDI / 2 : kDI;
 
-template <int HG, int KG, bool FP4>
-__device__ __forceinline__ v4f mma_scaled(const v8i& a, const v8i& b, int sa, int sb, v4f c) {
-  constexpr int fmt = FP4 ? 4 : 0;   // operand format code: 0 = fp8 e4m3, 4 = fp4 e2m1
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, fmt, fmt, HG, sa, KG, sb);
+template <int HG, int KG>
+__device__ __forceinline__ v4f mma_fp4(const v8i& a, const v8i& b, int sa, int sb, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, HG, sa, KG, sb);
+}
+
+__device__ __forceinline__ v4f mma_bf16x32(const v8bf& a, const v8bf& b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// E8M0 scale byte e -> 2^(e - 127) (bytes 1..254)
+__device__ __forceinline__ float e8m0_float(uint32_t e) { return __uint_as_float(e << 23); }
+
+// eight E4M3FN codes (two dwords) times the power of two s, as bf16 (exact)
+__device__ __forceinline__ v8bf fp8x8_bf16(uint32_t w0, uint32_t w1, float s) {
+  const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, false);
+  const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, s, true);
+  const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, false);
+  const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, s, true);
+  return v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// A lane's FP8 operand (bytes [16g, +16) scaled by s_lo, bytes [64+16g, +16) by s_hi) as the
+// B/A operands of four 16x16x32 bf16 MFMAs
+__device__ __forceinline__ void fp8_operand_bf16(const v8i& r, float s_lo, float s_hi, v8bf* o) {
+  o[0] = fp8x8_bf16((uint32_t)r[0], (uint32_t)r[1], s_lo);
+  o[1] = fp8x8_bf16((uint32_t)r[2], (uint32_t)r[3], s_lo);
+  o[2] = fp8x8_bf16((uint32_t)r[4], (uint32_t)r[5], s_hi);
+  o[3] = fp8x8_bf16((uint32_t)r[6], (uint32_t)r[7], s_hi);
 }
 
 // max(x, 0) as one integer max on the bit pattern: every negative float (and -0) is a negative
@@ -76,16 +111,16 @@ __device__ __forceinline__ v8i load_row_operand(const uint8_t* row, int g) {
 // of the page, so every load instruction of a page reads one contiguous kilobyte (a row-major
 // page would touch sixteen 128-byte lines per quarter-wave instead of two).  `lane_base` is the
 // page address plus 16·lane; loads are non-temporal.
-template <bool FP4>
+template <bool FP4, bool NT = true>
 __device__ __forceinline__ v8i load_key_operand(const uint8_t* lane_base, int kg) {
   constexpr int halves = FP4 ? 1 : 2;
-  const v4u lo = load16<true>(lane_base + kg * halves * 1024);
+  const v4u lo = load16<NT>(lane_base + kg * halves * 1024);
   v8i r;
   r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
   if constexpr (FP4) {
     r[4] = 0; r[5] = 0; r[6] = 0; r[7] = 0;
   } else {
-    const v4u hi = load16<true>(lane_base + (kg * halves + 1) * 1024);
+    const v4u hi = load16<NT>(lane_base + (kg * halves + 1) * 1024);
     r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
   }
   return r;
@@ -119,34 +154,100 @@ __device__ __forceinline__ void flush_hist(uint32_t* lhist, uint32_t* ghist, int
   }
 }
 
-// The query's indexer heads as scaled-MFMA A operands (padded heads zeroed), their E8M0 block
-// scales packed one byte per head group, and the head weights of this lane's output rows.
-template <int NHG, bool FP4>
-__device__ __forceinline__ void load_query(const IndexerArgs& a, int q, int n, int g, v8i* qa, int& qsc,
-                                           float (*wv)[4]) {
-  const uint8_t* qb = (const uint8_t*)a.qI + (int64_t)q * a.HI * kRowB<FP4>;
-  qsc = 0;
+// One query's indexer heads as MFMA A operands (padded heads zeroed) and the head weights of this
+// lane's output rows.  FP4: the codes and their E8M0 block scales, one byte per head group.  FP8:
+// converted to bf16 once (RES, the operands stay resident) or kept as codes with the lane's two
+// block scales and converted per page (multi-query decode, where NQ resident copies would not
+// fit in the register file).
+template <int NHG, bool FP4, bool RES>
+struct QueryOps {
+  static constexpr bool kConv = !FP4 && RES;
+  v8i raw[kConv ? 1 : NHG];
+  v8bf bf[kConv ? NHG : 1][4];
+  float s[FP4 || RES ? 1 : NHG][2];
+  int qsc;
+  float wv[NHG][4];
+};
+
+// The loads of an FP8 query (codes, the lane's two block scales, head weights), apart from the
+// conversion, so that the causal prefill can have the next query's loads in flight while it
+// scores the current one.
+template <int NHG>
+struct QueryRawFp8 {
+  v8i raw[NHG];
+  uint32_t sc[NHG];     // scale bytes of blocks g/2 (bits 0-7) and 2 + g/2 (bits 8-15)
+  float wv[NHG][4];
+};
+
+template <int NHG>
+__device__ __forceinline__ void fetch_query_fp8(const IndexerArgs& a, int q, int n, int g, QueryRawFp8<NHG>& R) {
+  const uint8_t* qb = (const uint8_t*)a.qI + (int64_t)q * a.HI * kDI;
 #pragma unroll
   for (int hg = 0; hg < NHG; ++hg) {
     const int h = 16 * hg + n;
     const int hc = h < a.HI ? h : a.HI - 1;
-    const v8i v = load_row_operand<FP4>(qb + hc * kRowB<FP4>, g);
-    const int sb = (int)a.qI_scale[((int64_t)q * a.HI + hc) * 4 + g];
+    const v8i v = load_row_operand<false>(qb + hc * kDI, g);
+    const uint8_t* sp = a.qI_scale + ((int64_t)q * a.HI + hc) * 4;
     const bool ok = h < a.HI;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qa[hg][e] = ok ? v[e] : 0;
-    qsc |= (ok ? sb : 127) << (8 * hg);
+    for (int e = 0; e < 8; ++e) R.raw[hg][e] = ok ? v[e] : 0;
+    R.sc[hg] = (uint32_t)sp[g >> 1] | ((uint32_t)sp[2 + (g >> 1)] << 8);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int hh = 16 * hg + 4 * g + i;
       const float x = a.w[(int64_t)q * a.HI + (hh < a.HI ? hh : a.HI - 1)];
-      wv[hg][i] = hh < a.HI ? x : 0.f;
+      R.wv[hg][i] = hh < a.HI ? x : 0.f;
     }
   }
 }
 
-// Score of one page (64 entries) for one query: 4 x NHG scaled MFMAs, ReLU and head weights, then
-// a reduce-scatter over the four lane groups leaves lane (n, g) with the score of slot 4n + g.
+template <int NHG, bool RES>
+__device__ __forceinline__ void set_query_fp8(const QueryRawFp8<NHG>& R, QueryOps<NHG, false, RES>& Q) {
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg) {
+    const float s_lo = e8m0_float(R.sc[hg] & 0xFFu), s_hi = e8m0_float((R.sc[hg] >> 8) & 0xFFu);
+    if constexpr (RES) {
+      fp8_operand_bf16(R.raw[hg], s_lo, s_hi, Q.bf[hg]);
+    } else {
+      Q.raw[hg] = R.raw[hg];
+      Q.s[hg][0] = s_lo;
+      Q.s[hg][1] = s_hi;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Q.wv[hg][i] = R.wv[hg][i];
+  }
+}
+
+template <int NHG, bool FP4, bool RES>
+__device__ __forceinline__ void load_query(const IndexerArgs& a, int q, int n, int g, QueryOps<NHG, FP4, RES>& Q) {
+  if constexpr (FP4) {
+    const uint8_t* qb = (const uint8_t*)a.qI + (int64_t)q * a.HI * kRowB<true>;
+    Q.qsc = 0;
+#pragma unroll
+    for (int hg = 0; hg < NHG; ++hg) {
+      const int h = 16 * hg + n;
+      const int hc = h < a.HI ? h : a.HI - 1;
+      const v8i v = load_row_operand<true>(qb + hc * kRowB<true>, g);
+      const bool ok = h < a.HI;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Q.raw[hg][e] = ok ? v[e] : 0;
+      Q.qsc |= (ok ? (int)a.qI_scale[((int64_t)q * a.HI + hc) * 4 + g] : 127) << (8 * hg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int hh = 16 * hg + 4 * g + i;
+        const float x = a.w[(int64_t)q * a.HI + (hh < a.HI ? hh : a.HI - 1)];
+        Q.wv[hg][i] = hh < a.HI ? x : 0.f;
+      }
+    }
+  } else {
+    QueryRawFp8<NHG> R;
+    fetch_query_fp8<NHG>(a, q, n, g, R);
+    set_query_fp8(R, Q);
+  }
+}
+
+// Score of one page (64 entries) for one query: 4 x NHG MFMAs (FP4: scaled 16x16x128; FP8: four
+// 16x16x32 bf16 per key group and head group), ReLU and head weights, then a reduce-scatter over the four lane groups leaves lane (n, g) with the score of slot 4n + g.
 // The reduce-scatter uses the cross-half lane swaps (v_permlane32_swap: upper half of the first
 // operand <-> lower half of the second; v_permlane16_swap: odd 16-lane rows of the first <-> even
 // rows of the second), so the sum of the two swapped registers holds, in each half (row), the
@@ -160,40 +261,109 @@ __device__ __forceinline__ float swap_sum16(float keep_even, float keep_odd) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int NHG, bool FP4>
-__device__ __forceinline__ float score_page(const v8i* qa, int qsc, const float (*wv)[4], const v8i* kb, int ksc) {
-  v4f acc[NHG][4];
-  static_for<0, NHG>::run([&](auto HGc) {
-    constexpr int HG = decltype(HGc)::value;
-    static_for<0, 4>::run([&](auto KGc) {
-      constexpr int KG = decltype(KGc)::value;
-      acc[HG][KG] = mma_scaled<HG, KG, FP4>(qa[HG], kb[KG], qsc, ksc, v4f{0.f, 0.f, 0.f, 0.f});
-    });
-  });
-  float part[4];
+// One key group of a page against one query (bf16 operands): NHG x 4 MFMAs, then ReLU and the
+// head weights summed over this lane's four output rows of every head group.
+template <int NHG, class QOp>
+__device__ __forceinline__ float key_group_bf16(QOp qop, const float (*wv)[4], const v8bf* kf) {
+  v4f acc[NHG];
 #pragma unroll
-  for (int kg = 0; kg < 4; ++kg) {
-    float sacc = 0.f;
+  for (int hg = 0; hg < NHG; ++hg) acc[hg] = v4f{0.f, 0.f, 0.f, 0.f};
+  // j outer, heads inner: consecutive MFMAs are independent
 #pragma unroll
-    for (int hg = 0; hg < NHG; ++hg)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sacc = fmaf(wv[hg][e], relu(acc[hg][kg][e]), sacc);
-    part[kg] = sacc;
-  }
-  // lanes 0-31 keep key groups 0 and 1, lanes 32-63 key groups 2 and 3; then even rows keep the
-  // first of the pair and odd rows the second
+    for (int hg = 0; hg < NHG; ++hg) acc[hg] = mma_bf16x32(qop(hg, j), kf[j], acc[hg]);
+  float sacc = 0.f;
+#pragma unroll
+  for (int hg = 0; hg < NHG; ++hg)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sacc = fmaf(wv[hg][e], relu(acc[hg][e]), sacc);
+  return sacc;
+}
+
+// lanes 0-31 keep key groups 0 and 1, lanes 32-63 key groups 2 and 3; then even rows keep the
+// first of the pair and odd rows the second: lane (n, g) ends with the score of slot 4n + g
+__device__ __forceinline__ float reduce_key_groups(const float* part) {
   const float k0 = swap_sum32(part[0], part[2]);
   const float k1 = swap_sum32(part[1], part[3]);
   return swap_sum16(k0, k1);
 }
 
+// ks_lo / ks_hi: the page's scale words this lane needs.  FP4: word l of the page's [4 blocks]
+// [64 slots] scale array (block g of slots 4n..4n+3; the key group picks the byte).  FP8: words
+// 16*(g/2) + n and 16*(2 + g/2) + n (blocks g/2 and 2 + g/2 of the same slots).
+template <int NHG, bool FP4, bool RES>
+__device__ __forceinline__ float score_page(const QueryOps<NHG, FP4, RES>& Q, const v8i* kb, uint32_t ks_lo,
+                                            uint32_t ks_hi) {
+  float part[4];
+  if constexpr (FP4) {
+    v4f acc[NHG][4];
+    static_for<0, NHG>::run([&](auto HGc) {
+      constexpr int HG = decltype(HGc)::value;
+      static_for<0, 4>::run([&](auto KGc) {
+        constexpr int KG = decltype(KGc)::value;
+        acc[HG][KG] = mma_fp4<HG, KG>(Q.raw[HG], kb[KG], Q.qsc, (int)ks_lo, v4f{0.f, 0.f, 0.f, 0.f});
+      });
+    });
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      float sacc = 0.f;
+#pragma unroll
+      for (int hg = 0; hg < NHG; ++hg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sacc = fmaf(Q.wv[hg][e], relu(acc[hg][kg][e]), sacc);
+      part[kg] = sacc;
+    }
+  } else {
+    // per-page conversion of the query operands (multi-query decode); the empty asm hides that the
+    // codes are the same on every page, so the compiler cannot hoist all queries' conversions out
+    // of the page loop and run out of registers
+    v8bf qc[RES ? 1 : NHG][4];
+    if constexpr (!RES) {
+#pragma unroll
+      for (int hg = 0; hg < NHG; ++hg) {
+        v8i r = Q.raw[hg];
+        asm volatile("" : "+v"(r));
+        fp8_operand_bf16(r, Q.s[hg][0], Q.s[hg][1], qc[hg]);
+      }
+    }
+    auto qop = [&](int hg, int j) -> const v8bf& {
+      if constexpr (RES) return Q.bf[hg][j];
+      else return qc[hg][j];
+    };
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      v8bf kf[4];
+      fp8_operand_bf16(kb[kg], e8m0_float((ks_lo >> (8 * kg)) & 0xFFu), e8m0_float((ks_hi >> (8 * kg)) & 0xFFu), kf);
+      part[kg] = key_group_bf16<NHG>(qop, Q.wv, kf);
+    }
+  }
+  return reduce_key_groups(part);
+}
+
+// The scale words of one key page that lane (n, g) needs (see score_page)
+template <bool FP4>
+__device__ __forceinline__ void page_scale_words(const uint8_t* page_scales, int n, int g, uint32_t& lo, uint32_t& hi) {
+  const uint32_t* w = (const uint32_t*)page_scales;
+  if constexpr (FP4) {
+    lo = w[n + 16 * g];
+    hi = 0u;
+  } else {
+    lo = w[n + 16 * (g >> 1)];
+    hi = w[n + 16 * (2 + (g >> 1))];
+  }
+}
+
 // Pages (64 entries each) scored by one wave, and page buffers in flight per wave.  Measured on the
-// batched and long-context decode workloads with FP8 keys: 2 pages per wave is 15% slower than 4;
-// 8 matches 4 on the first and is 4% faster on the second.
+// batched and long-context decode workloads: 2 pages per wave is 15% slower than 4, 8 matches 4 on
+// the first and is 4% faster on the second (and 4 pages per wave for rows without a sketch is no
+// faster with the bf16 FP8 path either).  The FP8 path's resident bf16 query operands leave room
+// for two page buffers at two waves per SIMD (about 200 VGPRs; three buffers measured 2-7% slower,
+// and three waves per SIMD need spills that cost a third more time).
 template <bool FP4>
 constexpr int kPagesPerWave = FP4 ? 8 : 8;
 template <bool FP4>
-constexpr int kPageBufs = FP4 ? 3 : 3;
+constexpr int kPageBufs = FP4 ? 3 : 2;
 constexpr int kMaxSharedQueries = 4;   // multi-query decode: queries scored per key page
 
 // NQ > 1 (multi-query decode): the block scores the NQ queries of one request, the last NQ tokens
@@ -276,6 +446,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   constexpr int pages_per_wave = kPagesPerWave<FP4>;
   static_assert(!SK || pages_per_wave * kPage == kSketchSpan, "a sketch covers one wave's pages");
   constexpr int nbuf = kDecodeBufs<FP4, NQ> < pages_per_wave ? kDecodeBufs<FP4, NQ> : pages_per_wave;
+  constexpr bool kQRes = NQ == 1;   // FP8: bf16 query operands resident (else converted per page)
   const int q0 = blockIdx.x * NQ;   // queries vary fastest: a row's blocks share one XCD (and its L2)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -304,11 +475,9 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
 
   // A operands: the queries' indexer heads, resident in VGPRs.  Loads are unconditional (clamped
   // addresses, padded heads zeroed by select) so nothing waits before the first key page.
-  v8i qa[NQ][NHG];
-  int qsc[NQ];
-  float wv[NQ][NHG][4];
+  QueryOps<NHG, FP4, kQRes> qo[NQ];
 #pragma unroll
-  for (int j = 0; j < NQ; ++j) load_query<NHG, FP4>(a, q0 + j, n, g, qa[j], qsc[j], wv[j]);
+  for (int j = 0; j < NQ; ++j) load_query<NHG, FP4, kQRes>(a, q0 + j, n, g, qo[j]);
 
   const uint8_t* keys = (const uint8_t*)a.keys;
   const int32_t* pt = a.page_table + (int64_t)(r < 0 ? 0 : r) * a.max_pages;
@@ -327,25 +496,25 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
     const int pid = __builtin_amdgcn_readlane(my_pid, i);
     return (unsigned)pid < (unsigned)a.num_pages;
   };
-  auto load_page = [&](int i, v8i* kb, int& ksc) {
+  auto load_page = [&](int i, v8i* kb, uint32_t& ks_lo, uint32_t& ks_hi) {
     int pid = __builtin_amdgcn_readlane(my_pid, i);
     pid = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
     const uint8_t* kp = keys + (int64_t)pid * (kPage * kRowB<FP4>) + 16 * lane;
-    ksc = *(const int*)(a.kscale + (int64_t)pid * 256 + 4 * lane);
+    page_scale_words<FP4>(a.kscale + (int64_t)pid * 256, n, g, ks_lo, ks_hi);
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) kb[kg] = load_key_operand<FP4>(kp, kg);
   };
 
   uint32_t skey[SK ? pages_per_wave : 1];   // sketch: order key of this lane's entry of page i
   uint32_t svalid = 0u;                      // bit i: that entry is visible
-  auto compute_page = [&](int i, const v8i* kb, int ksc) {
+  auto compute_page = [&](int i, const v8i* kb, uint32_t ks_lo, uint32_t ks_hi) {
     const int64_t c0 = (p_first + i) * kPage;
     const bool mapped = page_ok(i);
     const int64_t c = c0 + 4 * n + g;
     CSA_DBG_COUNT(lane == 0 && !mapped && c0 < nv_max);   // a visible page with no page id in the pool
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
-      const float score = score_page<NHG, FP4>(qa[j], qsc[j], wv[j], kb, ksc);
+      const float score = score_page<NHG, FP4, kQRes>(qo[j], kb, ks_lo, ks_hi);
       const float v = (mapped && c0 < nv[j] && c < nv[j]) ? score : -INFINITY;
       if (c < (a.visible_only ? nv[j] : a.max_n_vis)) {
         a.logits[(int64_t)(q0 + j) * a.ld + c] = v;
@@ -366,13 +535,13 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   // and store nothing.
   if (!(a.visible_only && p_first * kPage >= nv_max)) {
     v8i kb[nbuf][4];
-    int ksc[nbuf];
+    uint32_t ks_lo[nbuf], ks_hi[nbuf];
 #pragma unroll
-    for (int i = 0; i < nbuf; ++i) load_page(i, kb[i], ksc[i]);
+    for (int i = 0; i < nbuf; ++i) load_page(i, kb[i], ks_lo[i], ks_hi[i]);
 #pragma unroll
     for (int i = 0; i < pages_per_wave; ++i) {
-      compute_page(i, kb[i % nbuf], ksc[i % nbuf]);
-      if (i + nbuf < pages_per_wave) load_page(i + nbuf, kb[i % nbuf], ksc[i % nbuf]);
+      compute_page(i, kb[i % nbuf], ks_lo[i % nbuf], ks_hi[i % nbuf]);
+      if (i + nbuf < pages_per_wave) load_page(i + nbuf, kb[i % nbuf], ks_lo[i % nbuf], ks_hi[i % nbuf]);
     }
     if constexpr (SK) {
       // wave W of the row covers entries [W * kSketchSpan, (W + 1) * kSketchSpan)
@@ -395,18 +564,21 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
 }
 
 // Causal prefill: every query scores the keys of request 0, so keys are shared across queries.  A
-// block stages kPfPages key pages (48 KB) and their scale words in LDS once and scores kPfQueries
-// consecutive queries against them (four per wave), instead of every query streaming every page.
-// The staged layout is the operand order, [page][key group kg][half][lane][16 B]: lane (n, g)'s
-// operand for key group kg is row 4n + kg, bytes 16g .. (half 0) and 64 + 16g .. (half 1), so every
-// LDS read of an operand half is 64 lanes x 16 contiguous bytes.  Staging uses direct global-to-LDS
-// loads (each lane fetches the chunk that belongs at its 16-byte slot), so no registers hold keys
-// in transit.  The kernel is bound by the matrix-core / VALU pair of each page score (16 scaled
-// MFMAs and 128 ReLU/weight operations), and one wave alone leaves both units half idle, so the
-// block is sized for three waves per SIMD: about 160 VGPRs and 50 KB of LDS (measured on the 8192-token
-// causal prefill: 8 pages at two waves per SIMD, with next-query prefetch and double-buffered key
-// operands, is 18% slower).  Query blocks are issued heaviest (latest) first.  Only the visible
-// prefix of each row is written: the selection reads nothing past it.
+// block stages a few key pages in LDS once and scores kPfQueries consecutive queries against them
+// (four per wave), instead of every query streaming every page.  Query blocks are issued heaviest
+// (latest) first, and only the visible prefix of each row is written: the selection reads nothing
+// past it.
+//   FP4 keys (indexer_fp4_prefill_kernel): kPfPages pages (24 KB) and their scale words are staged
+// in operand order, [page][key group kg][lane][16 B], with direct global-to-LDS loads (each lane
+// fetches the chunk that belongs at its 16-byte slot, so no registers hold keys in transit), and
+// every LDS read of an operand is 64 lanes x 16 contiguous bytes.  The kernel is bound by the
+// matrix-core / VALU pair of each page score (16 scaled MFMAs and 128 ReLU/weight operations);
+// one wave alone leaves both units half idle, so the block is sized for three waves per SIMD
+// (measured with FP8 keys on the 8192-token causal prefill before FP8 moved to bf16: 8 pages at
+// two waves per SIMD, with next-query prefetch and double-buffered key operands, was 18% slower).
+//   FP8 keys (indexer_fp8_prefill_kernel): each wave converts one page to its bf16 operands while
+// staging it, [page][key group][MFMA j][lane][16 B] (16 KB a page), so the per-query work is the
+// 64 MFMAs and the epilogue, with no conversion.
 constexpr int kPfPages = 6;
 constexpr int kPfQueries = 16;
 
@@ -420,8 +592,9 @@ __device__ __forceinline__ int64_t prefill_visible(const IndexerArgs& a, int q) 
   return a.n_req < 1 ? 0 : (nv > lim ? lim : nv);
 }
 
+
 template <int NHG, bool FP4>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void indexer_fp8_prefill_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void indexer_fp4_prefill_kernel(
     IndexerArgs a) {
   constexpr int kHalves = FP4 ? 1 : 2;                            // 16-byte chunks per lane operand
   constexpr int kRow = kRowB<FP4>;
@@ -480,13 +653,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const int64_t vis_end = nv - p0 * kPage;
     const int np = vis_end <= 0 ? 0 : (int)min<int64_t>((vis_end + kPage - 1) / kPage, kPfPages);
     if (np == 0) continue;
-    v8i qa[NHG];
-    int qsc;
-    float wv[NHG][4];
-    load_query<NHG, FP4>(a, q, n, g, qa, qsc, wv);
+    QueryOps<NHG, FP4, true> qo;
+    load_query<NHG, FP4, true>(a, q, n, g, qo);
     for (int pi = 0; pi < np; ++pi) {
       v8i kb[4];
-      const int ksc = (int)sl[pi][lane];
+      uint32_t ks_lo, ks_hi;
+      page_scale_words<FP4>((const uint8_t*)&sl[pi][0], n, g, ks_lo, ks_hi);
 #pragma unroll
       for (int kg = 0; kg < 4; ++kg) {
         const uint4 lo = *(const uint4*)&kl[pi][kg][0][lane][0];
@@ -499,7 +671,92 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         }
       }
       const bool live = (live_bits >> pi) & 1u;
-      const float score = score_page<NHG, FP4>(qa, qsc, wv, kb, ksc);
+      const float score = score_page<NHG, FP4, true>(qo, kb, ks_lo, ks_hi);
+      const int64_t c = (p0 + pi) * kPage + 4 * n + g;
+      if (c < a.max_n_vis) lrow[c] = (live && c < nv) ? score : -INFINITY;
+    }
+  }
+}
+
+// FP8 prefill block: kPfWavesBf waves share kPfPagesBf staged pages (64 KB of bf16 operands, two
+// blocks per CU) and score kPfQpwBf queries each.  Measured on the 8192-token causal prefill, all
+// within 5% of this shape and none faster: 8 pages with 8 waves, 2 pages, 2 or 1 queries per wave,
+// 3 pages at three waves per SIMD, and next-query prefetch.  The kernel runs at about 43% of the
+// bf16 matrix-core peak (64 MFMAs and 128 ReLU/weight operations per query and page).
+constexpr int kPfPagesBf = 4;
+constexpr int kPfWavesBf = 4;
+constexpr int kPfQpwBf = 4;   // queries per wave
+constexpr int kPfQueriesBf = kPfQpwBf * kPfWavesBf;
+
+template <int NHG>
+__global__ __launch_bounds__(64 * kPfWavesBf) __attribute__((amdgpu_waves_per_eu(2, 2))) void indexer_fp8_prefill_kernel(
+    IndexerArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, g = lane >> 4;
+  const int nbx = (a.Q + kPfQueriesBf - 1) / kPfQueriesBf;
+  const int q0 = (nbx - 1 - (int)blockIdx.x) * kPfQueriesBf;     // heaviest query blocks first
+  const int64_t p0 = (int64_t)blockIdx.y * kPfPagesBf;
+  if (p0 * kPage >= a.max_n_vis) return;
+  __shared__ v4u kbf[kPfPagesBf][4][4][64];                       // [page][kg][j][lane] bf16 operands
+  __shared__ int pid_s[kPfPagesBf];
+
+  const int qw = q0 + kPfQpwBf * wave;                            // this wave's first query
+  const int nq = min(kPfQpwBf, a.Q - qw);                         // its query count (may be <= 0)
+  const int qlast = min(q0 + kPfQueriesBf, a.Q) - 1;
+  const int64_t nv_last = prefill_visible(a, qlast);              // the largest prefix of the block
+  if (p0 * kPage >= nv_last) return;   // no query of the block sees these pages
+
+  if (tid < kPfPagesBf) {
+    const int64_t pp = p0 + tid;
+    int pid = -1;
+    if (pp * kPage < nv_last) pid = a.page_table[pp];
+    pid_s[tid] = pid;
+  }
+  __syncthreads();
+  // wave w converts page w (keys are read through the caches: every query block reads them)
+  for (int pg = wave; pg < kPfPagesBf; pg += kPfWavesBf) {
+    int pid = pid_s[pg];
+    pid = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
+    const uint8_t* kp = (const uint8_t*)a.keys + (int64_t)pid * (kPage * kDI) + 16 * lane;
+    uint32_t ks_lo, ks_hi;
+    page_scale_words<false>(a.kscale + (int64_t)pid * 256, n, g, ks_lo, ks_hi);
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      const v8i r = load_key_operand<false, false>(kp, kg);
+      v8bf o[4];
+      fp8_operand_bf16(r, e8m0_float((ks_lo >> (8 * kg)) & 0xFFu), e8m0_float((ks_hi >> (8 * kg)) & 0xFFu), o);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kbf[pg][kg][j][lane] = __builtin_bit_cast(v4u, o[j]);
+    }
+  }
+  __syncthreads();
+  uint32_t live_bits = 0;   // bit i: staged page i is mapped (wave-uniform)
+#pragma unroll
+  for (int i = 0; i < kPfPagesBf; ++i) live_bits |= ((unsigned)pid_s[i] < (unsigned)a.num_pages ? 1u : 0u) << i;
+  live_bits = __builtin_amdgcn_readfirstlane(live_bits);
+
+  for (int j = 0; j < nq; ++j) {
+    const int q = qw + j;
+    const int64_t nv = prefill_visible(a, q);
+    float* lrow = a.logits + (int64_t)q * a.ld;
+    const int64_t vis_end = nv - p0 * kPage;
+    const int np = vis_end <= 0 ? 0 : (int)min<int64_t>((vis_end + kPage - 1) / kPage, kPfPagesBf);
+    if (np == 0) continue;
+    QueryOps<NHG, false, true> qo;
+    load_query<NHG, false, true>(a, q, n, g, qo);
+    auto qop = [&](int hg, int jj) -> const v8bf& { return qo.bf[hg][jj]; };
+    for (int pi = 0; pi < np; ++pi) {
+      float part[4];
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg) {
+        v8bf kf[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) kf[jj] = __builtin_bit_cast(v8bf, kbf[pi][kg][jj][lane]);
+        part[kg] = key_group_bf16<NHG>(qop, qo.wv, kf);
+      }
+      const float score = reduce_key_groups(part);
+      const bool live = (live_bits >> pi) & 1u;
       const int64_t c = (p0 + pi) * kPage + 4 * n + g;
       if (c < a.max_n_vis) lrow[c] = (live && c < nv) ? score : -INFINITY;
     }
@@ -571,12 +828,13 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
   const bool fp4 = a.dt == 3;
   if (a.vis_mode == 2 && !hist) {
     // causal prefill: keys shared by all queries, staged once per block of queries
-    dim3 grid((unsigned)((a.Q + kPfQueries - 1) / kPfQueries),
-              (unsigned)((a.max_n_vis + kPfPages * kPage - 1) / (kPfPages * kPage)));
+    const int pages = fp4 ? kPfPages : kPfPagesBf, queries = fp4 ? kPfQueries : kPfQueriesBf;
+    const dim3 block(fp4 ? 256 : 64 * kPfWavesBf);
+    dim3 grid((unsigned)((a.Q + queries - 1) / queries), (unsigned)((a.max_n_vis + pages * kPage - 1) / (pages * kPage)));
     ProfScope p(fp4 ? "indexer_fp4_prefill" : "indexer_fp8_prefill", s);
 #define CSA_PF_LAUNCH(N)                                                                    \
-  if (fp4) CSA_LAUNCH(p, (indexer_fp8_prefill_kernel<N, true>), grid, dim3(256), s, a); \
-  else CSA_LAUNCH(p, (indexer_fp8_prefill_kernel<N, false>), grid, dim3(256), s, a);
+  if (fp4) CSA_LAUNCH(p, (indexer_fp4_prefill_kernel<N, true>), grid, block, s, a); \
+  else CSA_LAUNCH(p, (indexer_fp8_prefill_kernel<N>), grid, block, s, a);
     switch (nhg) {
       case 1: CSA_PF_LAUNCH(1) break;
       case 2: CSA_PF_LAUNCH(2) break;

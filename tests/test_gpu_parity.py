@@ -1,5 +1,6 @@
 """GPU parity of the HIP path against the CPU oracle, at sizes the oracle finishes in seconds that
 still span several tiles, pages and blocks with ragged tails.  Every call goes through the C ABI."""
+import dataclasses
 import math
 
 import numpy as np
@@ -53,6 +54,47 @@ def test_indexer_scores(dev, HI, idx_dt):
         if nv:
             _say(f"query {qi}: max err {err.max():.2e}, max err/bound {(err / bound).max():.3f}")
         assert np.all(np.isneginf(logits[qi, nv:wl.max_n_vis])), f"query {qi}: tail not -inf"
+
+
+def test_indexer_fp8_products_exact_under_cancellation(dev):
+    """FP8 operands whose products cancel inside one run of eight elements: 448*448 + v and
+    448*448 - 448*448 + v for small v, in the same 32-element scale block and across blocks.  A
+    matrix core that sums each run of products on a grid tied to the largest of them returns
+    448*448 and 0 here; the scores must instead meet the fp32 bound of exact products."""
+    run, tio = _run()
+    base = configs.make_decode("idx_cancel", [256], H=16, HI=16, seed=1)
+    qI = np.zeros_like(base.qI)
+    keys = base.ik_keys.copy()
+    w = np.zeros_like(base.w)
+    w[0, 0] = 1.0
+    E448, N448, ONE = 0x7E, 0xFE, 0x38      # e4m3fn codes of 448, -448 and 1
+    qI[0, 0, [0, 2]] = E448
+    qI[0, 0, [1, 65]] = ONE
+    pg = int(base.page_table[0, 0])
+    keys[pg] = 0
+    for c in range(64):
+        code = 0x20 + 2 * (c % 16)          # 0.125 ... 0.84
+        keys[pg, c, 0] = E448
+        if c < 16:
+            keys[pg, c, 1] = code            # 448^2 + v, one run of eight
+        elif c < 32:
+            keys[pg, c, 65] = code           # 448^2 + v, v in another scale block
+        elif c < 48:
+            keys[pg, c, [1, 2]] = [code, N448]   # 448^2 - 448^2 + v
+        else:
+            keys[pg, c, [2, 1, 3]] = [N448, code, code]
+    wl = dataclasses.replace(base, qI=qI, qI_scale=np.full_like(base.qI_scale, 127), ik_keys=keys,
+                             ik_scales=np.full_like(base.ik_scales, 127), w=w)
+    logits = run.indexer(wl, tio.to_device(wl, dev)).cpu().numpy()[0, :64].astype(np.float64)
+    ref = O.query_scores(wl, 0)
+    assert ref[32] == 0.125 and ref[0] == 448.0 ** 2 + 0.125
+    err = np.abs(logits - ref)
+    bound = _fp32_score_bound(wl, 0)
+    _say(f"cancelling fp8 products: max err {err.max():.3e}")
+    assert np.all(err <= bound), f"max err {err.max():.3e} at entry {int(err.argmax())}"
+    # every v is a multiple of 2^-6, so each exact sum is an fp32 value: exact products and fp32
+    # accumulation reproduce them bit for bit
+    assert np.all(logits == ref), f"inexact at entries {np.nonzero(logits != ref)[0][:8].tolist()}"
 
 
 @pytest.mark.parametrize("key_dt", [configs.DT_FP8, configs.DT_FP4])
