@@ -469,6 +469,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
     }
     __syncthreads();
     for (int p = 0; p <= nt + 1; ++p) {
+      // staging first: its VALU work and waits overlap the score waves' matrix-core burst at the
+      // start of the phase, and P.V then runs while the score waves do their softmax
+      if (p + 1 < nt) {
+        gather_stage<WF, CF>(Kr[(p + 1) & 3], rb, raw, rc, lane);
+        if (p + 2 < nt) gather_fetch<WF, CF, NTG>(p + 2, cw_lo, cw_hi, lane, raw, rc);
+      }
       if (p >= 2) {
         const int t = p - 2;
         const int pb = t & 1;
@@ -499,10 +505,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
 #pragma unroll
           for (int hg = 0; hg < 4; ++hg) acc[hg][dt] = mma_bf16(vv, pf[hg], acc[hg][dt]);
         }
-      }
-      if (p + 1 < nt) {
-        gather_stage<WF, CF>(Kr[(p + 1) & 3], rb, raw, rc, lane);
-        if (p + 2 < nt) gather_fetch<WF, CF, NTG>(p + 2, cw_lo, cw_hi, lane, raw, rc);
       }
       __syncthreads();
     }
