@@ -156,15 +156,11 @@ __device__ __forceinline__ void flush_hist(uint32_t* lhist, uint32_t* ghist, int
 
 // One query's indexer heads as MFMA A operands (padded heads zeroed) and the head weights of this
 // lane's output rows.  FP4: the codes and their E8M0 block scales, one byte per head group.  FP8:
-// converted to bf16 once (RES, the operands stay resident) or kept as codes with the lane's two
-// block scales and converted per page (multi-query decode, where NQ resident copies would not
-// fit in the register file).
-template <int NHG, bool FP4, bool RES>
+// converted to bf16 once, with the lane's two block scales folded in.
+template <int NHG, bool FP4>
 struct QueryOps {
-  static constexpr bool kConv = !FP4 && RES;
-  v8i raw[kConv ? 1 : NHG];
-  v8bf bf[kConv ? NHG : 1][4];
-  float s[FP4 || RES ? 1 : NHG][2];
+  v8i raw[FP4 ? NHG : 1];
+  v8bf bf[FP4 ? 1 : NHG][4];
   int qsc;
   float wv[NHG][4];
 };
@@ -201,25 +197,19 @@ __device__ __forceinline__ void fetch_query_fp8(const IndexerArgs& a, int q, int
   }
 }
 
-template <int NHG, bool RES>
-__device__ __forceinline__ void set_query_fp8(const QueryRawFp8<NHG>& R, QueryOps<NHG, false, RES>& Q) {
+template <int NHG>
+__device__ __forceinline__ void set_query_fp8(const QueryRawFp8<NHG>& R, QueryOps<NHG, false>& Q) {
 #pragma unroll
   for (int hg = 0; hg < NHG; ++hg) {
     const float s_lo = e8m0_float(R.sc[hg] & 0xFFu), s_hi = e8m0_float((R.sc[hg] >> 8) & 0xFFu);
-    if constexpr (RES) {
-      fp8_operand_bf16(R.raw[hg], s_lo, s_hi, Q.bf[hg]);
-    } else {
-      Q.raw[hg] = R.raw[hg];
-      Q.s[hg][0] = s_lo;
-      Q.s[hg][1] = s_hi;
-    }
+    fp8_operand_bf16(R.raw[hg], s_lo, s_hi, Q.bf[hg]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) Q.wv[hg][i] = R.wv[hg][i];
   }
 }
 
-template <int NHG, bool FP4, bool RES>
-__device__ __forceinline__ void load_query(const IndexerArgs& a, int q, int n, int g, QueryOps<NHG, FP4, RES>& Q) {
+template <int NHG, bool FP4>
+__device__ __forceinline__ void load_query(const IndexerArgs& a, int q, int n, int g, QueryOps<NHG, FP4>& Q) {
   if constexpr (FP4) {
     const uint8_t* qb = (const uint8_t*)a.qI + (int64_t)q * a.HI * kRowB<true>;
     Q.qsc = 0;
@@ -292,8 +282,8 @@ __device__ __forceinline__ float reduce_key_groups(const float* part) {
 // ks_lo / ks_hi: the page's scale words this lane needs.  FP4: word l of the page's [4 blocks]
 // [64 slots] scale array (block g of slots 4n..4n+3; the key group picks the byte).  FP8: words
 // 16*(g/2) + n and 16*(2 + g/2) + n (blocks g/2 and 2 + g/2 of the same slots).
-template <int NHG, bool FP4, bool RES>
-__device__ __forceinline__ float score_page(const QueryOps<NHG, FP4, RES>& Q, const v8i* kb, uint32_t ks_lo,
+template <int NHG, bool FP4>
+__device__ __forceinline__ float score_page(const QueryOps<NHG, FP4>& Q, const v8i* kb, uint32_t ks_lo,
                                             uint32_t ks_hi) {
   float part[4];
   if constexpr (FP4) {
@@ -315,22 +305,7 @@ __device__ __forceinline__ float score_page(const QueryOps<NHG, FP4, RES>& Q, co
       part[kg] = sacc;
     }
   } else {
-    // per-page conversion of the query operands (multi-query decode); the empty asm hides that the
-    // codes are the same on every page, so the compiler cannot hoist all queries' conversions out
-    // of the page loop and run out of registers
-    v8bf qc[RES ? 1 : NHG][4];
-    if constexpr (!RES) {
-#pragma unroll
-      for (int hg = 0; hg < NHG; ++hg) {
-        v8i r = Q.raw[hg];
-        asm volatile("" : "+v"(r));
-        fp8_operand_bf16(r, Q.s[hg][0], Q.s[hg][1], qc[hg]);
-      }
-    }
-    auto qop = [&](int hg, int j) -> const v8bf& {
-      if constexpr (RES) return Q.bf[hg][j];
-      else return qc[hg][j];
-    };
+    auto qop = [&](int hg, int j) -> const v8bf& { return Q.bf[hg][j]; };
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
       v8bf kf[4];
@@ -364,13 +339,18 @@ template <bool FP4>
 constexpr int kPagesPerWave = FP4 ? 8 : 8;
 template <bool FP4>
 constexpr int kPageBufs = FP4 ? 3 : 2;
-constexpr int kMaxSharedQueries = 4;   // multi-query decode: queries scored per key page
+constexpr int kMaxSharedQueries = 4;   // multi-query decode: queries sharing a block's key pages
 
-// NQ > 1 (multi-query decode): the block scores the NQ queries of one request, the last NQ tokens
-// of its context, so each key page is read from HBM once for all of them instead of once per
-// query.  Page buffers drop to two to make room for the extra query operands.
-template <bool FP4, int NQ>
-constexpr int kDecodeBufs = NQ > 1 ? 2 : kPageBufs<FP4>;
+// NQ > 1 (multi-query decode): the block takes the NQ queries of one request (the last NQ tokens
+// of its context).  Wave w scores query w % NQ over page group w / NQ, so every wave does the
+// one-query work with the one-query registers, and the NQ waves of a page group read the same
+// key pages at the same time: the first read comes from HBM, the others from the caches (the key
+// loads keep their lines for NQ > 1).  A block has 4 / NQ page groups (3 waves for NQ = 3).
+// Scoring all NQ queries in each wave instead (one key read per page) needs NQ sets of bf16 query
+// operands, 256 VGPRs at one wave per SIMD: measured on batched decode with 64 heads, S = 4 took
+// 43.8 us that way against 37.2 us this way, S = 2 25.2 against 23.8 us.
+template <int NQ>
+constexpr int kQGroups = 4 / NQ;
 
 // What the decode kernel leaves for the selection besides the scores: nothing, a per-row 12-bit
 // histogram of the scores (the multi-launch selection of rows of any length), or a per-wave sketch
@@ -445,44 +425,45 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   constexpr bool SK = SEL == kSelSketch && NQ == 1;
   constexpr int pages_per_wave = kPagesPerWave<FP4>;
   static_assert(!SK || pages_per_wave * kPage == kSketchSpan, "a sketch covers one wave's pages");
-  constexpr int nbuf = kDecodeBufs<FP4, NQ> < pages_per_wave ? kDecodeBufs<FP4, NQ> : pages_per_wave;
-  constexpr bool kQRes = NQ == 1;   // FP8: bf16 query operands resident (else converted per page)
+  constexpr int nbuf = kPageBufs<FP4> < pages_per_wave ? kPageBufs<FP4> : pages_per_wave;
+  constexpr int kGroups = kQGroups<NQ>;
   const int q0 = blockIdx.x * NQ;   // queries vary fastest: a row's blocks share one XCD (and its L2)
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int jq = wave % NQ, grp = wave / NQ;   // this wave's query and page group
   const int n = lane & 15, g = lane >> 4;
   __shared__ uint32_t lhist[HIST ? NQ : 1][HIST ? kHistBins : 1];
 
-  const int64_t c_begin = (int64_t)blockIdx.y * 4 * pages_per_wave * kPage;
+  const int64_t c_begin = (int64_t)blockIdx.y * kGroups * pages_per_wave * kPage;
   if (c_begin >= a.max_n_vis) return;
   int r;
-  int64_t nv[NQ];
-  int64_t nv_max = 0;
+  int64_t nv = 0, nv_max = 0;   // visible entries of this wave's query, and the block's largest
 #pragma unroll
   for (int j = 0; j < NQ; ++j) {
-    nv[j] = visible_count(a, q0 + j, r);   // one request: every j gives the same r
-    nv_max = nv[j] > nv_max ? nv[j] : nv_max;
+    const int64_t v = visible_count(a, q0 + j, r);   // one request: every j gives the same r
+    nv_max = v > nv_max ? v : nv_max;
+    nv = j == jq ? v : nv;
   }
   // inside a fused path the selection reads only the visible prefix of each row, so a block (or
   // a wave, below) past it has nothing to do; short rows of a ragged batch then cost nothing
   if (a.visible_only && c_begin >= nv_max) return;
   if constexpr (HIST) {
-    // every wave adds into every part of the histogram, so all clears must land before the first
-    // add (both returns above are block-uniform, so every wave reaches this barrier)
-    for (int i = tid; i < NQ * kHistBins; i += 256) lhist[i / kHistBins][i % kHistBins] = 0u;
+    // the waves of a query add into its part of the histogram, so all clears must land before
+    // the first add (both returns above are block-uniform, so every wave reaches this barrier)
+    for (int i = tid; i < NQ * kHistBins; i += (int)blockDim.x) lhist[i / kHistBins][i % kHistBins] = 0u;
     __syncthreads();
   }
 
-  // A operands: the queries' indexer heads, resident in VGPRs.  Loads are unconditional (clamped
+  // A operands: the query's indexer heads, resident in VGPRs.  Loads are unconditional (clamped
   // addresses, padded heads zeroed by select) so nothing waits before the first key page.
-  QueryOps<NHG, FP4, kQRes> qo[NQ];
-#pragma unroll
-  for (int j = 0; j < NQ; ++j) load_query<NHG, FP4, kQRes>(a, q0 + j, n, g, qo[j]);
+  const int q = q0 + jq;
+  QueryOps<NHG, FP4> qo;
+  load_query<NHG, FP4>(a, q, n, g, qo);
 
   const uint8_t* keys = (const uint8_t*)a.keys;
   const int32_t* pt = a.page_table + (int64_t)(r < 0 ? 0 : r) * a.max_pages;
-  const int64_t p_first = (c_begin >> 6) + (int64_t)wave * pages_per_wave;   // this wave's first page
-  const int64_t vis_pages = (nv_max + kPage - 1) / kPage;
+  const int64_t p_first = (c_begin >> 6) + (int64_t)grp * pages_per_wave;   // this wave's first page
+  const int64_t vis_pages = (nv + kPage - 1) / kPage;
 
   // page ids of this wave's pages, one per lane, then read into scalars as needed
   int my_pid = -1;
@@ -502,7 +483,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
     const uint8_t* kp = keys + (int64_t)pid * (kPage * kRowB<FP4>) + 16 * lane;
     page_scale_words<FP4>(a.kscale + (int64_t)pid * 256, n, g, ks_lo, ks_hi);
 #pragma unroll
-    for (int kg = 0; kg < 4; ++kg) kb[kg] = load_key_operand<FP4>(kp, kg);
+    for (int kg = 0; kg < 4; ++kg) kb[kg] = load_key_operand<FP4, NQ == 1>(kp, kg);
   };
 
   uint32_t skey[SK ? pages_per_wave : 1];   // sketch: order key of this lane's entry of page i
@@ -511,21 +492,18 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
     const int64_t c0 = (p_first + i) * kPage;
     const bool mapped = page_ok(i);
     const int64_t c = c0 + 4 * n + g;
-    CSA_DBG_COUNT(lane == 0 && !mapped && c0 < nv_max);   // a visible page with no page id in the pool
-#pragma unroll
-    for (int j = 0; j < NQ; ++j) {
-      const float score = score_page<NHG, FP4, kQRes>(qo[j], kb, ks_lo, ks_hi);
-      const float v = (mapped && c0 < nv[j] && c < nv[j]) ? score : -INFINITY;
-      if (c < (a.visible_only ? nv[j] : a.max_n_vis)) {
-        a.logits[(int64_t)(q0 + j) * a.ld + c] = v;
-        if constexpr (HIST) {
-          if (c < nv[j]) atomicAdd(&lhist[j][order_key(v) >> kHistShift], 1u);
-        }
+    CSA_DBG_COUNT(lane == 0 && !mapped && c0 < nv);   // a visible page with no page id in the pool
+    const float score = score_page<NHG, FP4>(qo, kb, ks_lo, ks_hi);
+    const float v = (mapped && c0 < nv && c < nv) ? score : -INFINITY;
+    if (c < (a.visible_only ? nv : a.max_n_vis)) {
+      a.logits[(int64_t)q * a.ld + c] = v;
+      if constexpr (HIST) {
+        if (c < nv) atomicAdd(&lhist[jq][order_key(v) >> kHistShift], 1u);
       }
-      if constexpr (SK) {
-        skey[i] = order_key(v);
-        svalid |= (c < nv[0] ? 1u : 0u) << i;
-      }
+    }
+    if constexpr (SK) {
+      skey[i] = order_key(v);
+      svalid |= (c < nv ? 1u : 0u) << i;
     }
   };
 
@@ -533,7 +511,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   // i + nbuf as soon as page i is scored, so up to nbuf pages are in flight and every wait is for
   // exactly the page about to be scored.  Pages past the wave's range load page 0 (always mapped)
   // and store nothing.
-  if (!(a.visible_only && p_first * kPage >= nv_max)) {
+  if (!(a.visible_only && p_first * kPage >= nv)) {
     v8i kb[nbuf][4];
     uint32_t ks_lo[nbuf], ks_hi[nbuf];
 #pragma unroll
@@ -555,7 +533,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
 #pragma unroll
     for (int j = 0; j < NQ; ++j) {
       uint32_t* gh = a.hist + (int64_t)(q0 + j) * kHistBins;
-      for (int i = tid; i < kHistBins; i += 256) {
+      for (int i = tid; i < kHistBins; i += (int)blockDim.x) {
         const uint32_t v = lhist[j][i];
         if (v) atomicAdd(&gh[i], v);
       }
@@ -653,8 +631,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const int64_t vis_end = nv - p0 * kPage;
     const int np = vis_end <= 0 ? 0 : (int)min<int64_t>((vis_end + kPage - 1) / kPage, kPfPages);
     if (np == 0) continue;
-    QueryOps<NHG, FP4, true> qo;
-    load_query<NHG, FP4, true>(a, q, n, g, qo);
+    QueryOps<NHG, FP4> qo;
+    load_query<NHG, FP4>(a, q, n, g, qo);
     for (int pi = 0; pi < np; ++pi) {
       v8i kb[4];
       uint32_t ks_lo, ks_hi;
@@ -671,7 +649,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         }
       }
       const bool live = (live_bits >> pi) & 1u;
-      const float score = score_page<NHG, FP4, true>(qo, kb, ks_lo, ks_hi);
+      const float score = score_page<NHG, FP4>(qo, kb, ks_lo, ks_hi);
       const int64_t c = (p0 + pi) * kPage + 4 * n + g;
       if (c < a.max_n_vis) lrow[c] = (live && c < nv) ? score : -INFINITY;
     }
@@ -743,8 +721,8 @@ __global__ __launch_bounds__(64 * kPfWavesBf) __attribute__((amdgpu_waves_per_eu
     const int64_t vis_end = nv - p0 * kPage;
     const int np = vis_end <= 0 ? 0 : (int)min<int64_t>((vis_end + kPage - 1) / kPage, kPfPagesBf);
     if (np == 0) continue;
-    QueryOps<NHG, false, true> qo;
-    load_query<NHG, false, true>(a, q, n, g, qo);
+    QueryOps<NHG, false> qo;
+    load_query<NHG, false>(a, q, n, g, qo);
     auto qop = [&](int hg, int jj) -> const v8bf& { return qo.bf[hg][jj]; };
     for (int pi = 0; pi < np; ++pi) {
       float part[4];
@@ -847,13 +825,15 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
   // kPagesPerWave pages per wave, four waves per block; a multi-query decode (2 to 4 queries per
   // request, derived visibility) gives each block all queries of one request
   const int nq = (a.vis_mode == 1 && a.q_per_req >= 2 && a.q_per_req <= kMaxSharedQueries) ? a.q_per_req : 1;
-  const int per_block = 4 * (fp4 ? kPagesPerWave<true> : kPagesPerWave<false>) * kPage;
+  const int groups = 4 / nq;   // kQGroups<nq>: page groups per block, nq waves each
+  const int per_block = groups * (fp4 ? kPagesPerWave<true> : kPagesPerWave<false>) * kPage;
   dim3 grid((unsigned)(a.Q / nq), (unsigned)((a.max_n_vis + per_block - 1) / per_block));
+  const dim3 block((unsigned)(64 * nq * groups));
   ProfScope p(fp4 ? "indexer_fp4" : "indexer_fp8", s);
 #define CSA_IDX_LAUNCH(N, F, NQ)                                                                           \
-  if (hist) CSA_LAUNCH(p, (indexer_fp8_kernel<N, kSelHist, F, NQ>), grid, dim3(256), s, a);             \
-  else if (sketch && NQ == 1) CSA_LAUNCH(p, (indexer_fp8_kernel<N, kSelSketch, F, 1>), grid, dim3(256), s, a); \
-  else CSA_LAUNCH(p, (indexer_fp8_kernel<N, kSelNone, F, NQ>), grid, dim3(256), s, a);
+  if (hist) CSA_LAUNCH(p, (indexer_fp8_kernel<N, kSelHist, F, NQ>), grid, block, s, a);             \
+  else if (sketch && NQ == 1) CSA_LAUNCH(p, (indexer_fp8_kernel<N, kSelSketch, F, 1>), grid, block, s, a); \
+  else CSA_LAUNCH(p, (indexer_fp8_kernel<N, kSelNone, F, NQ>), grid, block, s, a);
 #define CSA_IDX_NQ(N, F)                          \
   switch (nq) {                                   \
     case 2: CSA_IDX_LAUNCH(N, F, 2) break;        \
