@@ -316,18 +316,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   // instead of four; the partial scores of head group w ^ 1 go to wave w ^ 1 through LDS.  q stays
   // in registers as the QK B operand: qo[ks] / qx[ks] hold dims 256 (w & 1) + 32ks + 8g .. +7 of
   // head n of group w / w ^ 1.  Padded heads read head 0's row; their results are never written.
-  v8bf qo[8], qx[8];
-  if (wave < 4) {
-    const int ho = h_base + 16 * wave + n, hx = h_base + 16 * (wave ^ 1) + n;
-    const int d0 = 256 * (wave & 1) + 8 * g;
-    const uint16_t* qpo = (const uint16_t*)a.q + ((int64_t)q * a.H + (ho < a.H ? ho : 0)) * kD + d0;
-    const uint16_t* qpx = (const uint16_t*)a.q + ((int64_t)q * a.H + (hx < a.H ? hx : 0)) * kD + d0;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      qo[ks] = *(const v8bf*)(qpo + 32 * ks);
-      qx[ks] = *(const v8bf*)(qpx + 32 * ks);
-    }
-  }
+  v8bf qo[8], qx[8];   // loaded by the score waves after their slot codes (below)
   float m = kNegBig, lsum = 0.f;   // score-wave softmax state of head h_base + 16 wave + n
   v4f acc[4][8];                   // value waves: O^T[128 dw + 16 dt + 4 g + i][h_base + 16 hg + n]
 #pragma unroll
@@ -343,6 +332,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
     const int rb = 8 * wave;   // gathered rows rb .. rb+3 of every tile
     uint32_t cw_lo[2], cw_hi[2];
     gather_codes(a, q, r, s_begin, nt, n_idx, rb, lane, cw_lo, cw_hi, &vm8[0][0], wave);
+    // q after the codes: the codes' index loads then do not wait behind the 32 q loads
+    {
+      const int ho = h_base + 16 * wave + n, hx = h_base + 16 * (wave ^ 1) + n;
+      const int d0 = 256 * (wave & 1) + 8 * g;
+      const uint16_t* qpo = (const uint16_t*)a.q + ((int64_t)q * a.H + (ho < a.H ? ho : 0)) * kD + d0;
+      const uint16_t* qpx = (const uint16_t*)a.q + ((int64_t)q * a.H + (hx < a.H ? hx : 0)) * kD + d0;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        qo[ks] = *(const v8bf*)(qpo + 32 * ks);
+        qx[ks] = *(const v8bf*)(qpx + 32 * ks);
+      }
+    }
     RawChunk raw[kScoreDepth][4];
     uint64_t rc[kScoreDepth][4];
     auto fetch = [&](int t, RawChunk* rw, uint64_t* c4) { gather_fetch<WF, CF, NTG>(t, cw_lo, cw_hi, lane, rw, c4); };
@@ -631,14 +632,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs
   const int kb = wave & 1, dh = wave >> 1;   // consumer roles (waves 0-3)
   // q as the QK B operand: lane (n, g) holds dims 256 dh + 32ks + 8g .. +7 of head h (padded heads
   // read head 0's row; their results are never written)
+  // loaded after the slot codes are resolved: the barrier that publishes the codes waits for every
+  // outstanding load, and the producers' first gathers should not wait for q
   v8bf qop[8];
+  resolve_codes<kAttnThreads>(a, q, r, t_begin * kTile, nt * kTile, codes, vmask, tid);
+  __syncthreads();
   if (wave < 4) {
     const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)q * a.H + (h < a.H ? h : 0)) * kD + 256 * dh + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qop[ks] = *(const v8bf*)(qp + 32 * ks);
   }
-  resolve_codes<kAttnThreads>(a, q, r, t_begin * kTile, nt * kTile, codes, vmask, tid);
-  __syncthreads();
 
   float m = kNegBig, lsum = 0.f;   // softmax state of head h (identical in the four consumers)
   v4f acc[8];                      // O^T[128 wave + 16 dt + 4 g + i][head h]
@@ -942,8 +945,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   else if (wf == kRowFP8) CSA_LAUNCH(p, (K<kRowFP8, kRowBF16, NTG>), grid, dim3(kAttnThreads), s, a);           \
   else if (cf == kRowFP8) CSA_LAUNCH(p, (K<kRowBF16, kRowFP8, NTG>), grid, dim3(kAttnThreads), s, a);           \
   else CSA_LAUNCH(p, (K<kRowBF16, kRowBF16, NTG>), grid, dim3(kAttnThreads), s, a);
+    // rows are streamed (non-temporal) only when one block gathers each of them: with several head
+    // blocks per query, the later blocks' gathers of a row hit the copy the first one left in L2
+    const bool stream = a.stream_rows && hchunks == 1;
 #define CSA_ATTN_LAUNCH(K) \
-  if (a.stream_rows) { CSA_ATTN_FMT(K, true) } else { CSA_ATTN_FMT(K, false) }
+  if (stream) { CSA_ATTN_FMT(K, true) } else { CSA_ATTN_FMT(K, false) }
     if (hb == 16) {
       CSA_ATTN_LAUNCH(attn_bf16_h16_kernel)
     } else {
