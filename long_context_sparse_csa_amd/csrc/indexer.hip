@@ -656,88 +656,94 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   }
 }
 
-// FP8 prefill block: kPfWavesBf waves share kPfPagesBf staged pages (64 KB of bf16 operands, two
-// blocks per CU) and score kPfQpwBf queries each.  Measured on the 8192-token causal prefill, all
-// within 5% of this shape and none faster: 8 pages with 8 waves, 2 pages, 2 or 1 queries per wave,
-// 3 pages at three waves per SIMD, and next-query prefetch.  The kernel runs at about 43% of the
-// bf16 matrix-core peak (64 MFMAs and 128 ReLU/weight operations per query and page).
-constexpr int kPfPagesBf = 4;
-constexpr int kPfWavesBf = 4;
-constexpr int kPfQpwBf = 4;   // queries per wave
-constexpr int kPfQueriesBf = kPfQpwBf * kPfWavesBf;
+// FP8 prefill, query-major: a block of four waves takes four consecutive queries, one per wave,
+// and walks the pages they see in chunks of kPqChunk pages.  The four waves convert the next chunk
+// to bf16 operands into an LDS double buffer (its loads issued before the current chunk is
+// scored, the conversion after) while each wave scores the current chunk for its query, so a
+// query's operands are loaded and converted once per block.  Measured on the 8,192-token causal
+// prefill: 108 us at one page per chunk and three waves per SIMD (32 KB of LDS a block), 114 us
+// at two pages and two waves per SIMD, 130 us for the page-major shape this replaces (a block
+// staging four pages for sixteen queries, each query's operands loaded once per page block).
+constexpr int kPqChunk = 1;
 
 template <int NHG>
-__global__ __launch_bounds__(64 * kPfWavesBf) __attribute__((amdgpu_waves_per_eu(2, 2))) void indexer_fp8_prefill_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void indexer_fp8_prefill_kernel(
     IndexerArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int nbx = (a.Q + kPfQueriesBf - 1) / kPfQueriesBf;
-  const int q0 = (nbx - 1 - (int)blockIdx.x) * kPfQueriesBf;     // heaviest query blocks first
-  const int64_t p0 = (int64_t)blockIdx.y * kPfPagesBf;
-  if (p0 * kPage >= a.max_n_vis) return;
-  __shared__ v4u kbf[kPfPagesBf][4][4][64];                       // [page][kg][j][lane] bf16 operands
-  __shared__ int pid_s[kPfPagesBf];
+  const int nb = (a.Q + 3) / 4;
+  const int q0 = (nb - 1 - (int)blockIdx.x) * 4;   // heaviest (latest) query blocks first
+  const int q = q0 + wave;
+  const bool has_q = q < a.Q;
+  const int64_t nv_last = prefill_visible(a, min(q0 + 3, a.Q - 1));   // the block's largest prefix
+  const int64_t n_pages = (nv_last + kPage - 1) / kPage;
+  if (n_pages == 0) return;   // block-uniform: no query of the block sees an entry
+  const int n_chunks = (int)((n_pages + kPqChunk - 1) / kPqChunk);
+  __shared__ v4u kbf[2][kPqChunk][4][4][64];   // [buffer][page][kg][j][lane] bf16 operands
+  __shared__ int pid_s[2][kPqChunk];
 
-  const int qw = q0 + kPfQpwBf * wave;                            // this wave's first query
-  const int nq = min(kPfQpwBf, a.Q - qw);                         // its query count (may be <= 0)
-  const int qlast = min(q0 + kPfQueriesBf, a.Q) - 1;
-  const int64_t nv_last = prefill_visible(a, qlast);              // the largest prefix of the block
-  if (p0 * kPage >= nv_last) return;   // no query of the block sees these pages
+  // the query's operands first: their loads overlap the first chunk's
+  QueryOps<NHG, false> qo;
+  if (has_q) load_query<NHG, false>(a, q, n, g, qo);
+  const int64_t nv = has_q ? prefill_visible(a, q) : 0;
+  float* lrow = a.logits + (int64_t)(has_q ? q : 0) * a.ld;
 
-  if (tid < kPfPagesBf) {
-    const int64_t pp = p0 + tid;
-    int pid = -1;
-    if (pp * kPage < nv_last) pid = a.page_table[pp];
-    pid_s[tid] = pid;
-  }
-  __syncthreads();
-  // wave w converts page w (keys are read through the caches: every query block reads them)
-  for (int pg = wave; pg < kPfPagesBf; pg += kPfWavesBf) {
-    int pid = pid_s[pg];
-    pid = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
-    const uint8_t* kp = (const uint8_t*)a.keys + (int64_t)pid * (kPage * kDI) + 16 * lane;
-    uint32_t ks_lo, ks_hi;
-    page_scale_words<false>(a.kscale + (int64_t)pid * 256, n, g, ks_lo, ks_hi);
+  // staging: chunk c's (page, key group) pairs t = wave, wave + 4 (kPqChunk * 4 = 8 pairs)
+  constexpr int kPairs = kPqChunk * 4 / 4;
+  v8i sraw[kPairs];
+  uint32_t slo[kPairs], shi[kPairs];
+  auto stage_issue = [&](int c, int buf) {
 #pragma unroll
-    for (int kg = 0; kg < 4; ++kg) {
-      const v8i r = load_key_operand<false, false>(kp, kg);
+    for (int u = 0; u < kPairs; ++u) {
+      const int t = wave + 4 * u, i = t >> 2, kg = t & 3;
+      const int64_t pp = (int64_t)c * kPqChunk + i;
+      int pid = pp < n_pages ? a.page_table[pp] : -1;
+      if (kg == 0 && lane == 0) pid_s[buf][i] = pid;
+      pid = (unsigned)pid < (unsigned)a.num_pages ? pid : 0;
+      const uint8_t* kp = (const uint8_t*)a.keys + (int64_t)pid * (kPage * kDI) + 16 * lane;
+      sraw[u] = load_key_operand<false, false>(kp, kg);
+      page_scale_words<false>(a.kscale + (int64_t)pid * 256, n, g, slo[u], shi[u]);
+    }
+  };
+  auto stage_finish = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < kPairs; ++u) {
+      const int t = wave + 4 * u, i = t >> 2, kg = t & 3;
       v8bf o[4];
-      fp8_operand_bf16(r, e8m0_float((ks_lo >> (8 * kg)) & 0xFFu), e8m0_float((ks_hi >> (8 * kg)) & 0xFFu), o);
+      fp8_operand_bf16(sraw[u], e8m0_float((slo[u] >> (8 * kg)) & 0xFFu), e8m0_float((shi[u] >> (8 * kg)) & 0xFFu), o);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kbf[pg][kg][j][lane] = __builtin_bit_cast(v4u, o[j]);
+      for (int j = 0; j < 4; ++j) kbf[buf][i][kg][j][lane] = __builtin_bit_cast(v4u, o[j]);
     }
-  }
+  };
+  stage_issue(0, 0);
+  stage_finish(0);
   __syncthreads();
-  uint32_t live_bits = 0;   // bit i: staged page i is mapped (wave-uniform)
+  auto qop = [&](int hg, int jj) -> const v8bf& { return qo.bf[hg][jj]; };
+  for (int c = 0; c < n_chunks; ++c) {
+    const int buf = c & 1;
+    // the other buffer was last read in chunk c - 1, before the barrier that ended it
+    if (c + 1 < n_chunks) stage_issue(c + 1, buf ^ 1);
 #pragma unroll
-  for (int i = 0; i < kPfPagesBf; ++i) live_bits |= ((unsigned)pid_s[i] < (unsigned)a.num_pages ? 1u : 0u) << i;
-  live_bits = __builtin_amdgcn_readfirstlane(live_bits);
-
-  for (int j = 0; j < nq; ++j) {
-    const int q = qw + j;
-    const int64_t nv = prefill_visible(a, q);
-    float* lrow = a.logits + (int64_t)q * a.ld;
-    const int64_t vis_end = nv - p0 * kPage;
-    const int np = vis_end <= 0 ? 0 : (int)min<int64_t>((vis_end + kPage - 1) / kPage, kPfPagesBf);
-    if (np == 0) continue;
-    QueryOps<NHG, false> qo;
-    load_query<NHG, false>(a, q, n, g, qo);
-    auto qop = [&](int hg, int jj) -> const v8bf& { return qo.bf[hg][jj]; };
-    for (int pi = 0; pi < np; ++pi) {
-      float part[4];
+    for (int i = 0; i < kPqChunk; ++i) {
+      const int64_t p = (int64_t)c * kPqChunk + i;
+      if (p * kPage < nv) {   // wave-uniform: pages holding visible entries of this query
+        float part[4];
 #pragma unroll
-      for (int kg = 0; kg < 4; ++kg) {
-        v8bf kf[4];
+        for (int kg = 0; kg < 4; ++kg) {
+          v8bf kf[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) kf[jj] = __builtin_bit_cast(v8bf, kbf[pi][kg][jj][lane]);
-        part[kg] = key_group_bf16<NHG>(qop, qo.wv, kf);
+          for (int jj = 0; jj < 4; ++jj) kf[jj] = __builtin_bit_cast(v8bf, kbf[buf][i][kg][jj][lane]);
+          part[kg] = key_group_bf16<NHG>(qop, qo.wv, kf);
+        }
+        const float score = reduce_key_groups(part);
+        const bool live = (unsigned)pid_s[buf][i] < (unsigned)a.num_pages;
+        const int64_t e = p * kPage + 4 * n + g;
+        if (e < a.max_n_vis) lrow[e] = (live && e < nv) ? score : -INFINITY;
       }
-      const float score = reduce_key_groups(part);
-      const bool live = (live_bits >> pi) & 1u;
-      const int64_t c = (p0 + pi) * kPage + 4 * n + g;
-      if (c < a.max_n_vis) lrow[c] = (live && c < nv) ? score : -INFINITY;
     }
+    if (c + 1 < n_chunks) stage_finish(buf ^ 1);
+    __syncthreads();
   }
 }
 
@@ -806,9 +812,11 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
   const bool fp4 = a.dt == 3;
   if (a.vis_mode == 2 && !hist) {
     // causal prefill: keys shared by all queries, staged once per block of queries
-    const int pages = fp4 ? kPfPages : kPfPagesBf, queries = fp4 ? kPfQueries : kPfQueriesBf;
-    const dim3 block(fp4 ? 256 : 64 * kPfWavesBf);
-    dim3 grid((unsigned)((a.Q + queries - 1) / queries), (unsigned)((a.max_n_vis + pages * kPage - 1) / (pages * kPage)));
+    // FP4: page-major blocks (kPfPages pages, kPfQueries queries); FP8: query-major blocks of 4
+    const dim3 block(256);
+    dim3 grid = fp4 ? dim3((unsigned)((a.Q + kPfQueries - 1) / kPfQueries),
+                           (unsigned)((a.max_n_vis + kPfPages * kPage - 1) / (kPfPages * kPage)))
+                    : dim3((unsigned)((a.Q + 3) / 4));
     ProfScope p(fp4 ? "indexer_fp4_prefill" : "indexer_fp8_prefill", s);
 #define CSA_PF_LAUNCH(N)                                                                    \
   if (fp4) CSA_LAUNCH(p, (indexer_fp4_prefill_kernel<N, true>), grid, block, s, a); \
