@@ -444,7 +444,12 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   ia.max_n_vis = max_n_vis; ia.logits = pw.logits; ia.ld = pw.ld; ia.hist = one_block ? nullptr : pw.tk.hist;
   ia.vis_mode = one_block ? mode : 0; ia.ctx_len = ctx_len; ia.max_ctx = max_ctx; ia.pos0 = pos0; ia.q_per_req = S;
   ia.visible_only = true;
-  if (sketch) { ia.sk_top = pw.sk_top; ia.sk_bound = pw.sk_bound; ia.sk_waves = pw.sk_waves; }
+  if (sketch) {
+    ia.sk_top = pw.sk_top; ia.sk_bound = pw.sk_bound; ia.sk_waves = pw.sk_waves;
+    // rows of at least 64k entries hold k real sketch entries (8 per 512-entry span): they store
+    // no scores, and the selection rescores one when its sketches cannot decide it
+    ia.sk_rescore_from = csa::sketch_rescore_from(k);
+  }
   CSA_HIP(csa::launch_indexer(ia, stream));
 
   csa::TopkArgs t{};
@@ -459,7 +464,7 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
     t.rows = pw.rows; t.ld_rows = k; t.page_table = comp->page_table; t.max_pages = comp->max_pages;
     t.num_pages = comp->num_pages;
   }
-  if (sketch) { t.sk_top = pw.sk_top; t.sk_bound = pw.sk_bound; t.sk_waves = pw.sk_waves; }
+  if (sketch) { t.sk_top = pw.sk_top; t.sk_bound = pw.sk_bound; t.sk_waves = pw.sk_waves; t.ia = ia; }
   CSA_HIP(single ? csa::launch_topk_single(t, stream)
                  : (sketch ? csa::launch_topk_sketch(t, stream) : csa::launch_topk_select(t, stream)));
 

@@ -70,6 +70,10 @@ struct IndexerArgs {
   uint2* sk_top = nullptr;
   uint32_t* sk_bound = nullptr;
   int64_t sk_waves = 0;
+  // sketch rows with at least this many visible entries (> 0) store no scores: their sketches hold
+  // at least k real entries, and the selection rescores such a row when the sketches cannot
+  // decide it (rescore_span).  0: every row stores its scores.
+  int64_t sk_rescore_from = 0;
 };
 hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s);
 
@@ -106,6 +110,9 @@ struct TopkArgs {
   const uint2* sk_top = nullptr;
   const uint32_t* sk_bound = nullptr;
   int64_t sk_waves = 0;
+  // sketch path only: the indexer launch of this decode; rows with at least ia.sk_rescore_from
+  // visible entries (> 0) have no stored scores and are rescored when their sketches cannot decide
+  IndexerArgs ia{};
 };
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
@@ -116,6 +123,8 @@ bool topk_single_ok(int64_t max_n_vis, int k);
 hipError_t launch_topk_sketch(const TopkArgs& a, hipStream_t s);
 bool topk_sketch_ok(int64_t max_n_vis, int k);
 int64_t topk_sketch_waves(int64_t max_n_vis);   // sketches per row
+// visible entries from which a sketch row is sure to hold k real sketch entries
+int64_t sketch_rescore_from(int k);
 
 // Zero histograms / counters and write window indices (decode ring or causal prefill window).
 struct PrepArgs {

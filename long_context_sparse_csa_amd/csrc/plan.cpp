@@ -76,4 +76,6 @@ bool topk_sketch_ok(int64_t max_n_vis, int k) {
 
 int64_t topk_sketch_waves(int64_t max_n_vis) { return (max_n_vis + kSketchSpan - 1) / kSketchSpan; }
 
+int64_t sketch_rescore_from(int k) { return (int64_t)((k + kSketchTop - 1) / kSketchTop) * kSketchSpan; }
+
 }  // namespace csa

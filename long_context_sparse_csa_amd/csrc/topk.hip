@@ -17,6 +17,7 @@
 // a launch, so no device-scope fence (an L2 write-back on this part) is needed.
 #include "csa_device.h"
 #include "csa_internal.h"
+#include "indexer_score.h"
 
 namespace csa {
 
@@ -1009,6 +1010,30 @@ __global__ __launch_bounds__(1024) void topk_sketch_kernel(TopkArgs a) {
       }
     }
     return;
+  }
+  if (a.ia.sk_rescore_from > 0 && nv >= a.ia.sk_rescore_from) {
+    // the indexer stored no scores for this row: rescore it, each wave a span at a time
+    const int wave = tid >> 6, lane = tid & 63;
+    const int64_t n_span = (nv + kSketchSpan - 1) / kSketchSpan;
+    const int nhg = (a.ia.HI + 15) / 16;
+    for (int64_t W = wave; W < n_span; W += NT / 64) {
+      if (a.ia.dt == 3) {
+        switch (nhg) {
+          case 1: rescore_span<1, true>(a.ia, q, W, lane); break;
+          case 2: rescore_span<2, true>(a.ia, q, W, lane); break;
+          case 3: rescore_span<3, true>(a.ia, q, W, lane); break;
+          default: rescore_span<4, true>(a.ia, q, W, lane); break;
+        }
+      } else {
+        switch (nhg) {
+          case 1: rescore_span<1, false>(a.ia, q, W, lane); break;
+          case 2: rescore_span<2, false>(a.ia, q, W, lane); break;
+          case 3: rescore_span<3, false>(a.ia, q, W, lane); break;
+          default: rescore_span<4, false>(a.ia, q, W, lane); break;
+        }
+      }
+    }
+    __syncthreads();   // the block reads the rescored row next (workgroup scope: one L1)
   }
   select_streamed<NT>(a, q, nv, (uint32_t)k, sh, out, rows_out, pt);
 }
