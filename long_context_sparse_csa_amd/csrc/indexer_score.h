@@ -325,8 +325,8 @@ __device__ __forceinline__ void page_scale_words(const uint8_t* page_scales, int
 // store its scores (its selection works from the per-wave sketches); when the sketches cannot
 // decide a row's top k, the selection rescores the row with this.  Same operands, the same matrix-
 // core chains and the same fp32 sums in the same order as score_page, so the same scores; but a
-// page at a time with one head group's query operands at a time (reloaded through the caches for
-// every page), which fits in far fewer registers than the decode kernel's resident operands.
+// page, a head group and a key group at a time (query and key operands reloaded through the caches
+// as needed), which fits in far fewer registers than the decode kernel's resident operands.
 template <int NHG, bool FP4>
 __device__ __forceinline__ void rescore_span(const IndexerArgs& a, int q, int64_t span, int lane) {
   constexpr int kSpanPages = kSketchSpan / kPage;
@@ -350,9 +350,6 @@ __device__ __forceinline__ void rescore_span(const IndexerArgs& a, int q, int64_
     const uint8_t* kp = keys + (int64_t)pid * (kPage * kRowB<FP4>) + 16 * lane;
     uint32_t ks_lo, ks_hi;
     page_scale_words<FP4>(a.kscale + (int64_t)pid * 256, n, g, ks_lo, ks_hi);
-    v8i kb[4];
-#pragma unroll
-    for (int kg = 0; kg < 4; ++kg) kb[kg] = load_key_operand<FP4, false>(kp, kg);
     float sacc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int hg = 0; hg < NHG; ++hg) {
@@ -386,12 +383,14 @@ __device__ __forceinline__ void rescore_span(const IndexerArgs& a, int q, int64_
       }
       static_for<0, 4>::run([&](auto KGc) {
         constexpr int kg = decltype(KGc)::value;
+        // the key group's operand bytes, reloaded (through the caches) for every head group
+        const v8i kb = load_key_operand<FP4, false>(kp + z, kg);
         v4f acc;
         if constexpr (FP4) {
-          acc = mma_fp4<0, kg>(raw, kb[kg], qsc, (int)lo, v4f{0.f, 0.f, 0.f, 0.f});
+          acc = mma_fp4<0, kg>(raw, kb, qsc, (int)lo, v4f{0.f, 0.f, 0.f, 0.f});
         } else {
           v8bf kf[4];
-          fp8_operand_bf16(kb[kg], e8m0_float((lo >> (8 * kg)) & 0xFFu), e8m0_float((hi >> (8 * kg)) & 0xFFu), kf);
+          fp8_operand_bf16(kb, e8m0_float((lo >> (8 * kg)) & 0xFFu), e8m0_float((hi >> (8 * kg)) & 0xFFu), kf);
           acc = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int j = 0; j < 4; ++j) acc = mma_bf16x32(qb[j], kf[j], acc);

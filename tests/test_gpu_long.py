@@ -69,6 +69,24 @@ def test_decode_long_clustered_planted(dev):
     _say(f"max err {err:.2e}")
 
 
+def test_decode_long_rescored_rows_match_stored_scores(dev):
+    """Long rows store no scores inside csa_decode; when their sketches cannot decide them the
+    selection rescores them.  The rescored scores must be the indexer's own, bit for bit: the
+    decode's selection on clustered-planted rows (which take that path) equals csa_topk over the
+    scores csa_indexer_logits stores for the same queries, index for index."""
+    from workloads import run, torch_io
+    wl = configs.make_decode("long_cluster", [1 << 19, 1 << 19], H=16, HI=64, seed=3, planted_frac=0.01,
+                             planted_contiguous=True)
+    _say("decode long clustered planted: rescored selection vs stored-score selection")
+    d = torch_io.to_device(wl, dev)
+    _, idx = run.decode(wl, d)
+    logits = run.indexer(wl, d)
+    ref = run.topk(logits, d.n_vis, wl.max_n_vis, wl.topk).cpu().numpy()
+    got = idx.cpu().numpy()[:, 128:]
+    for qi in range(wl.Q):
+        assert got[qi].tolist() == ref[qi].tolist(), f"query {qi}: rescored selection differs"
+
+
 def test_decode_long_all_scores_tied(dev):
     """Every indexer key zero, so every score is exactly 0: the first 512 entries are selected (ties
     go to the lower index), through the full-row fallback."""
