@@ -31,7 +31,7 @@ def _short(name):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("indexer.hip", "csa_device.h"):
+    for f in ("indexer.hip", "indexer_score.h", "csa_device.h"):
         h.update(open(os.path.join(ROOT, "long_context_sparse_csa_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
