@@ -87,6 +87,25 @@ def test_decode_long_rescored_rows_match_stored_scores(dev):
         assert got[qi].tolist() == ref[qi].tolist(), f"query {qi}: rescored selection differs"
 
 
+def test_decode_long_store_threshold_rows(dev):
+    """Rows just below, at and above the length from which the decode stores no scores (64k = 32,768
+    entries at k = 512), beside a long row that puts the batch on the sketch path.  Clustered planted
+    entries send every row to the full-row fallback: the shortest from its stored scores, the others
+    rescored.  Oracle acceptance on every row, and the same selection as csa_topk over the stored
+    scores of csa_indexer_logits."""
+    from workloads import run, torch_io
+    ctx = [4 * 32767, 4 * 32768, 4 * 32769 + 3, 1 << 19]
+    wl = configs.make_decode("long_store_edge", ctx, H=16, HI=64, seed=8, planted_frac=0.02,
+                             planted_contiguous=True)
+    _say(f"decode long, store-threshold rows ctx={ctx}")
+    _, idx, err = _decode_and_check(wl, dev)
+    d = torch_io.to_device(wl, dev)
+    ref = run.topk(run.indexer(wl, d), d.n_vis, wl.max_n_vis, wl.topk).cpu().numpy()
+    for qi in range(wl.Q):
+        assert idx[qi, 128:].tolist() == ref[qi].tolist(), f"query {qi}: selection differs from stored scores"
+    _say(f"max err {err:.2e}")
+
+
 def test_decode_long_all_scores_tied(dev):
     """Every indexer key zero, so every score is exactly 0: the first 512 entries are selected (ties
     go to the lower index), through the full-row fallback."""
