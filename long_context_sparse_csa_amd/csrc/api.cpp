@@ -92,14 +92,14 @@ struct PathWs {
 
 // Which selection a fused call runs, from the visible-entry bound its workspace was sized for:
 // one block per query over the whole row (short rows), one block per query over the indexer's
-// per-wave sketches (long rows of a one-query-per-request decode), or the multi-launch histogram
+// per-wave sketches (long rows of a decode, one or several queries per request), or the multi-launch histogram
 // selection (everything else).  The workspace layout depends on it, so a call and its workspace
 // query decide it from the same numbers.
 enum SelPath { kPathSingle, kPathSketch, kPathMulti };
 
 SelPath sel_path(int mode, int32_t S, int64_t n, int32_t k) {
   if (csa::topk_single_ok(n, k)) return kPathSingle;
-  if (mode == 1 && S == 1 && csa::topk_sketch_ok(n, k)) return kPathSketch;
+  if (mode == 1 && csa::topk_sketch_ok(n, k)) return kPathSketch;
   return kPathMulti;
 }
 
@@ -419,8 +419,8 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   int32_t* idx = idx_out ? idx_out : pw.idx;
   const int64_t ld_idx = kWin + k;
   // Short rows: the indexer and a one-block-per-query selection derive visibility from ctx_len /
-  // pos0 themselves, so no preparation launch and no zeroed histogram are needed.  Long rows of a
-  // one-query-per-request decode likewise: the indexer leaves per-wave sketches and one block per
+  // pos0 themselves, so no preparation launch and no zeroed histogram are needed.  Long decode
+  // rows likewise: the indexer leaves per-wave sketches and one block per
   // query selects from them.
   const bool single = path == kPathSingle;
   const bool sketch = path == kPathSketch;

@@ -118,7 +118,7 @@ hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_single(const TopkArgs& a, hipStream_t s);
 bool topk_single_ok(int64_t max_n_vis, int k);
-// Long rows of a one-query-per-request decode: the indexer writes per-wave sketches (8 largest
+// Long rows of a decode (one or several queries per request): the indexer writes per-wave sketches (8 largest
 // scores of every 512 entries and a bound on the rest) and one block per query selects from them.
 hipError_t launch_topk_sketch(const TopkArgs& a, hipStream_t s);
 bool topk_sketch_ok(int64_t max_n_vis, int k);

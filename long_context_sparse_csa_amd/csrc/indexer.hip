@@ -113,7 +113,7 @@ __device__ __forceinline__ void sketch_wave(const uint32_t* key8, uint32_t valid
 template <int NHG, int SEL, bool FP4, int NQ>
 __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
   constexpr bool HIST = SEL == kSelHist;
-  constexpr bool SK = SEL == kSelSketch && NQ == 1;
+  constexpr bool SK = SEL == kSelSketch;
   constexpr int pages_per_wave = kPagesPerWave<FP4>;
   static_assert(!SK || pages_per_wave * kPage == kSketchSpan, "a sketch covers one wave's pages");
   constexpr int nbuf = kPageBufs<FP4> < pages_per_wave ? kPageBufs<FP4> : pages_per_wave;
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) void indexer_fp8_kernel(IndexerArgs a) {
     if constexpr (SK) {
       // wave W of the row covers entries [W * kSketchSpan, (W + 1) * kSketchSpan)
       const int64_t W = p_first / pages_per_wave;
-      const int64_t slot = (int64_t)q0 * a.sk_waves + W;
+      const int64_t slot = (int64_t)q * a.sk_waves + W;
       sketch_wave(skey, svalid, p_first * kPage + 4 * n + g, lane, a.sk_top + slot * kSketchTop, a.sk_bound + slot);
     }
   }
@@ -533,7 +533,7 @@ hipError_t launch_indexer(const IndexerArgs& a, hipStream_t s) {
   ProfScope p(fp4 ? "indexer_fp4" : "indexer_fp8", s);
 #define CSA_IDX_LAUNCH(N, F, NQ)                                                                           \
   if (hist) CSA_LAUNCH(p, (indexer_fp8_kernel<N, kSelHist, F, NQ>), grid, block, s, a);             \
-  else if (sketch && NQ == 1) CSA_LAUNCH(p, (indexer_fp8_kernel<N, kSelSketch, F, 1>), grid, block, s, a); \
+  else if (sketch) CSA_LAUNCH(p, (indexer_fp8_kernel<N, kSelSketch, F, NQ>), grid, block, s, a);  \
   else CSA_LAUNCH(p, (indexer_fp8_kernel<N, kSelNone, F, NQ>), grid, block, s, a);
 #define CSA_IDX_NQ(N, F)                          \
   switch (nq) {                                   \

@@ -67,7 +67,7 @@ bool attn_uses_matrix_cores(int q_dt, int win_fmt, int comp_fmt, int n_win, int 
 
 bool topk_single_ok(int64_t max_n_vis, int k) { return max_n_vis <= kSingleMax && k <= kSingleMax; }
 
-// Long rows of a one-query-per-request decode take the sketches when every row of the longest
+// Long rows of a decode take the sketches when every row of the longest
 // length has at least 4 k of them (so the k-th largest lies well inside), up to 2^20 entries.
 bool topk_sketch_ok(int64_t max_n_vis, int k) {
   const int64_t waves = (max_n_vis + kSketchSpan - 1) / kSketchSpan;
