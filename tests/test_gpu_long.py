@@ -106,17 +106,19 @@ def test_decode_long_store_threshold_rows(dev):
     _say(f"max err {err:.2e}")
 
 
-@pytest.mark.parametrize("S,contiguous", [(2, False), (3, True)])
-def test_decode_long_multi_query(dev, S, contiguous):
-    """Several queries per request on long rows: the multi-query indexer (the S queries of a
-    request share each block's key pages) leaves a sketch per query and wave, and the rows take the
-    sketch selection; clustered planted entries send them through the rescoring fallback, whose
-    selection must equal csa_topk over the stored scores of csa_indexer_logits."""
+@pytest.mark.parametrize("S,contiguous,idx_dt", [(2, False, configs.DT_FP8), (3, True, configs.DT_FP8),
+                                                   (2, True, configs.DT_FP4), (5, True, configs.DT_FP8)])
+def test_decode_long_multi_query(dev, S, contiguous, idx_dt):
+    """Several queries per request on long rows: the multi-query indexer (2 to 4 queries of a
+    request share each block's key pages; 5 take blocks of their own) leaves a sketch per query and
+    wave, and the rows take the sketch selection; clustered planted entries send them through the
+    rescoring fallback, whose selection must equal csa_topk over the stored scores of
+    csa_indexer_logits."""
     from workloads import run, torch_io
     ctx = [1 << 19, (1 << 19) - 5]
     wl = configs.make_decode(f"long_multi_{S}", ctx, H=16, HI=64, seed=9 + S, planted_frac=0.01,
-                             planted_contiguous=contiguous, q_per_req=S)
-    _say(f"decode long multi-query S={S} contiguous={contiguous} ctx={ctx}")
+                             planted_contiguous=contiguous, q_per_req=S, idx_dt=idx_dt)
+    _say(f"decode long multi-query S={S} contiguous={contiguous} idx_dt={idx_dt} ctx={ctx}")
     _, idx, err = _decode_and_check(wl, dev)
     d = torch_io.to_device(wl, dev)
     ref = run.topk(run.indexer(wl, d), d.n_vis, wl.max_n_vis, wl.topk).cpu().numpy()
