@@ -375,7 +375,8 @@ def main():
     csa.csa_profile_enable(False)
     kernels = {}
     for name in ("prep", "indexer_fp8", "indexer_fp8_prefill", "indexer_fp4", "indexer_fp4_prefill", "indexer_f32",
-                 "topk_single", "topk_sketch", "topk_hist", "topk_collect", "topk_finish", "attn_bf16", "attn_combine",
+                 "topk_single", "topk_sketch", "topk_hist", "topk_collect", "topk_finish", "attn_select", "attn_bf16",
+                 "attn_combine",
                  "attn_f32"):
         tot, n = csa.csa_profile_collect(name)
         if n:

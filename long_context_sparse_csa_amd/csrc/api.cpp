@@ -465,8 +465,12 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
     t.num_pages = comp->num_pages;
   }
   if (sketch) { t.sk_top = pw.sk_top; t.sk_bound = pw.sk_bound; t.sk_waves = pw.sk_waves; t.ia = ia; }
-  CSA_HIP(single ? csa::launch_topk_single(t, stream)
-                 : (sketch ? csa::launch_topk_sketch(t, stream) : csa::launch_topk_select(t, stream)));
+  // one query per request with one-block rows: the attention launch runs the selection (inside its
+  // own blocks when it can, else as its own launch first)
+  const bool sel_in_attn = single && mode == 1 && S == 1;
+  if (!sel_in_attn)
+    CSA_HIP(single ? csa::launch_topk_single(t, stream)
+                   : (sketch ? csa::launch_topk_sketch(t, stream) : csa::launch_topk_select(t, stream)));
 
   csa::AttnArgs a{};
   a.q = q; a.q_dt = q_dt; a.Q = rows; a.H = H; a.sink = sink;
@@ -482,6 +486,7 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
   if (mode == 2) { a.trim_ratio = 4; a.pos0 = pos0; }   // selection pads past min(n_vis, k) with -1
   a.stream_rows = mode == 1 && S == 1;   // one query per request: each row is gathered once
   if (one_block) { a.rows = pw.rows; a.ld_rows = k; }
+  if (sel_in_attn) a.sel = &t;
   return hip_status(csa::launch_attention(a, stream));
 }
 

@@ -29,6 +29,7 @@
 #include <cstdlib>
 
 #include "attn_common.h"
+#include "select_block.h"
 
 namespace csa {
 
@@ -159,7 +160,8 @@ __device__ __forceinline__ uint4 raw_to_bf16(const RawChunk& r, uint64_t code, i
 // bytes in LDS.
 __device__ __forceinline__ void gather_codes(const AttnArgs& a, int q, int r, int s_begin, int nt, int n_idx,
                                              int rb, int lane, uint32_t* cw_lo, uint32_t* cw_hi, uint8_t* vm8,
-                                             int vm_slot) {
+                                             int vm_slot, const int32_t* idx_list = nullptr,
+                                             const int32_t* rows_list = nullptr) {
   int sl[4];
   bool in[4], ok[4];
   uint64_t c[4];
@@ -169,7 +171,7 @@ __device__ __forceinline__ void gather_codes(const AttnArgs& a, int q, int r, in
     sl[j] = s_begin + (e >> 2) * kTile + rb + (e & 3);
     in[j] = j < 2 && e < 4 * nt && sl[j] < n_idx;
   }
-  slot_codes4(a, q, r, sl, in, c, ok);
+  slot_codes4(a, q, r, sl, in, c, ok, idx_list, rows_list);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     cw_lo[j] = (uint32_t)c[j];
@@ -282,8 +284,87 @@ __device__ __forceinline__ void produce_tiles(const uint64_t* codes, uint16_t (*
   for (int j = nt + 1; j < nbar; ++j) __syncthreads();
 }
 
-template <int WF, int CF, bool NTG>
-__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) {
+// Selection inside the attention blocks (SEL): every block of a query first selects the query's
+// k rows itself, exactly as topk_single_kernel does (its block_threshold / block_emit with this
+// block's 512 threads, PER entries each), into LDS borrowed from tile slots 1-3 of the ring (no
+// tile is staged there before the first barrier of the tile loop).  Its slot codes then come from
+// LDS: the step saves the selection launch and the global round trip of the index list.  The
+// blocks of split 0 also write the index list and rows for the caller.
+constexpr int kSelPer = 32;                                           // entries per thread
+constexpr int kSelRowMax = kAttnThreads * kSelPer;                    // 16,384 entries
+constexpr int kSelOff = kTile * kKrStride * 2;                        // byte offset: tile slot 1
+constexpr int kSelListOff = kSelOff + 32768;                          // after SelShared (< 32 KB)
+constexpr int kSelRowsOff = kSelListOff + 4 * kMaxSlots;
+constexpr int kSelPtOff = kSelRowsOff + 4 * kMaxSlots;
+static_assert(sizeof(SelShared<kAttnThreads>) <= 32768, "selection LDS fits its space");
+static_assert(kSelPtOff + 4 * (kSelRowMax / kPage) <= 4 * kTile * kKrStride * 2, "selection LDS fits the ring");
+
+// Selects query q's rows into LDS: idx_list[0 .. n_win + k) (the ring window, then the k entries in
+// ascending order, -1 past the visible ones) and rows_list[0 .. k) (their pool rows, -1 if none).
+__device__ __forceinline__ void select_rows(const TopkArgs& t, int q, uint8_t* lds, bool write_out) {
+  const int tid = threadIdx.x;
+  SelShared<kAttnThreads>& sh = *(SelShared<kAttnThreads>*)(lds + kSelOff);
+  int32_t* idx_list = (int32_t*)(lds + kSelListOff);
+  int32_t* rows_list = (int32_t*)(lds + kSelRowsOff);
+  int32_t* pt_lds = (int32_t*)(lds + kSelPtOff);
+  const int k = t.k;
+  int r;
+  const int64_t seen = decode_seen(t.ctx_len, t.max_ctx, 1, q, r);
+  const int64_t nv = topk_row_count(t, q);
+  const int32_t* pt = t.page_table + (int64_t)r * t.max_pages;
+  auto row_of = [&](int c, int pg) { return (unsigned)pg < (unsigned)t.num_pages ? pg * kPage + (c & (kPage - 1)) : -1; };
+  if (tid < kWin) {
+    const int64_t p = seen - kWin + tid;
+    idx_list[tid] = p >= 0 ? (int32_t)(p % t.ring) : -1;
+  }
+  if (nv <= k) {
+    for (int i = tid; i < k; i += kAttnThreads) {
+      idx_list[kWin + i] = i < nv ? i : -1;
+      rows_list[i] = i < nv ? row_of(i, pt[i >> 6]) : -1;
+    }
+  } else {
+    for (int p = tid; p < (int)((nv + kPage - 1) / kPage); p += kAttnThreads) pt_lds[p] = pt[p];
+    const float* row = t.logits + (int64_t)q * t.ld;
+    const int c0 = tid * kSelPer;
+    uint32_t key[kSelPer];
+    uint32_t vm = 0;
+    {
+      float v[kSelPer];
+#pragma unroll
+      for (int j = 0; j < kSelPer; j += 4) {
+        const int c = c0 + j;
+        const float4 x = *(const float4*)(row + (c < nv ? c : 0));
+        v[j] = x.x; v[j + 1] = x.y; v[j + 2] = x.z; v[j + 3] = x.w;
+      }
+      for (int i = tid; i < kHistBins; i += kAttnThreads) sh.bins[i] = 0u;
+      if (tid == 0) sh.s_ncand = 0u;
+#pragma unroll
+      for (int j = 0; j < kSelPer; ++j) {
+        key[j] = order_key(v[j]);
+        vm |= (c0 + j < nv ? 1u : 0u) << j;
+      }
+    }
+    __syncthreads();
+    block_threshold<kAttnThreads, kSelPer>(key, vm, (uint32_t)k, sh);
+    block_emit<kAttnThreads, kSelPer>(key, vm, sh.s_T, sh.s_need, (uint32_t)k, [&](int j) { return c0 + j; }, sh);
+    const int32_t* sel = (const int32_t*)sh.cand_sel;
+    for (int i = tid; i < k; i += kAttnThreads) {
+      const int c = sel[i];
+      const int rw = row_of(c, pt_lds[c >> 6]);
+      CSA_DBG_COUNT(rw < 0);   // a selected entry on a page with no page id in the pool
+      idx_list[kWin + i] = c;
+      rows_list[i] = rw;
+    }
+  }
+  __syncthreads();
+  if (write_out) {
+    for (int i = tid; i < kWin + k; i += kAttnThreads) t.idx[(int64_t)q * t.ld_idx - kWin + i] = idx_list[i];
+    for (int i = tid; i < k; i += kAttnThreads) t.rows[(int64_t)q * t.ld_rows + i] = rows_list[i];
+  }
+}
+
+template <int WF, int CF, bool NTG, bool SEL = false>
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a, TopkArgs t) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -310,13 +391,34 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   const int nt = attn_block_tiles(a, q, n_tiles, t_begin, tps);   // tiles of this block
   const int r = a.req_mode == 1 ? q / a.q_per_req : (a.req_mode == 2 ? 0 : a.q_req[q]);
   const int s_begin = t_begin * kTile;
-
+  const int32_t* idx_list = nullptr;
+  const int32_t* rows_list = nullptr;
   // score waves: wave w computes the scores of head groups w and w ^ 1 over dims [256 (w & 1),
   // +256), so every K fragment it reads feeds two MFMAs and each K element is read by two waves
   // instead of four; the partial scores of head group w ^ 1 go to wave w ^ 1 through LDS.  q stays
   // in registers as the QK B operand: qo[ks] / qx[ks] hold dims 256 (w & 1) + 32ks + 8g .. +7 of
   // head n of group w / w ^ 1.  Padded heads read head 0's row; their results are never written.
-  v8bf qo[8], qx[8];   // loaded by the score waves after their slot codes (below)
+  v8bf qo[8], qx[8];
+  auto load_q = [&] {
+    const int ho = h_base + 16 * wave + n, hx = h_base + 16 * (wave ^ 1) + n;
+    const int d0 = 256 * (wave & 1) + 8 * g;
+    const uint16_t* qpo = (const uint16_t*)a.q + ((int64_t)q * a.H + (ho < a.H ? ho : 0)) * kD + d0;
+    const uint16_t* qpx = (const uint16_t*)a.q + ((int64_t)q * a.H + (hx < a.H ? hx : 0)) * kD + d0;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qo[ks] = *(const v8bf*)(qpo + 32 * ks);
+      qx[ks] = *(const v8bf*)(qpx + 32 * ks);
+    }
+  };
+  if constexpr (SEL) {
+    // q does not depend on the selection: its loads overlap it
+    if (wave < 4) load_q();
+    uint8_t* lds = (uint8_t*)&Kr[0][0];
+    select_rows(t, q, lds, split == 0 && blockIdx.y == 0);
+    idx_list = (const int32_t*)(lds + kSelListOff);
+    rows_list = (const int32_t*)(lds + kSelRowsOff);
+  }
+
   float m = kNegBig, lsum = 0.f;   // score-wave softmax state of head h_base + 16 wave + n
   v4f acc[4][8];                   // value waves: O^T[128 dw + 16 dt + 4 g + i][h_base + 16 hg + n]
 #pragma unroll
@@ -331,19 +433,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
   if (wave < 4) {
     const int rb = 8 * wave;   // gathered rows rb .. rb+3 of every tile
     uint32_t cw_lo[2], cw_hi[2];
-    gather_codes(a, q, r, s_begin, nt, n_idx, rb, lane, cw_lo, cw_hi, &vm8[0][0], wave);
+    gather_codes(a, q, r, s_begin, nt, n_idx, rb, lane, cw_lo, cw_hi, &vm8[0][0], wave, idx_list, rows_list);
     // q after the codes: the codes' index loads then do not wait behind the 32 q loads
-    {
-      const int ho = h_base + 16 * wave + n, hx = h_base + 16 * (wave ^ 1) + n;
-      const int d0 = 256 * (wave & 1) + 8 * g;
-      const uint16_t* qpo = (const uint16_t*)a.q + ((int64_t)q * a.H + (ho < a.H ? ho : 0)) * kD + d0;
-      const uint16_t* qpx = (const uint16_t*)a.q + ((int64_t)q * a.H + (hx < a.H ? hx : 0)) * kD + d0;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        qo[ks] = *(const v8bf*)(qpo + 32 * ks);
-        qx[ks] = *(const v8bf*)(qpx + 32 * ks);
-      }
-    }
+    if constexpr (!SEL) load_q();
     RawChunk raw[kScoreDepth][4];
     uint64_t rc[kScoreDepth][4];
     auto fetch = [&](int t, RawChunk* rw, uint64_t* c4) { gather_fetch<WF, CF, NTG>(t, cw_lo, cw_hi, lane, rw, c4); };
@@ -458,7 +550,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a) 
     const int dw = wave - 4;   // output dims [128 dw, 128 dw + 128)
     const int rb = 8 * dw + 4;   // gathered rows rb .. rb+3 of every tile
     uint32_t cw_lo[2], cw_hi[2];
-    gather_codes(a, q, r, s_begin, nt, n_idx, rb, lane, cw_lo, cw_hi, &vm8[0][0], 4 + dw);
+    gather_codes(a, q, r, s_begin, nt, n_idx, rb, lane, cw_lo, cw_hi, &vm8[0][0], 4 + dw, idx_list, rows_list);
     // one tile of gathers in flight: the value waves' own work is the shorter of the two roles, so
     // they can wait for a gather without lengthening the phase
     RawChunk raw[4];
@@ -924,38 +1016,63 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
+// The selection runs inside the 64-head attention blocks when its rows fit one block of them
+// (at most 16,384 visible entries, the index list at most kMaxSlots slots).
+static bool attn_select_fused(const AttnArgs& a, int hb) {
+  static const int mode = [] {
+    const char* e = getenv("CSA_ATTN_SELECT");   // tuning override: 0 = separate selection launch
+    return e ? atoi(e) : -1;
+  }();
+  const TopkArgs* t = a.sel;
+  return mode != 0 && t != nullptr && hb == 64 && t->win_mode == 1 && t->q_per_req == 1 &&
+         t->max_n_vis <= kSelRowMax && t->k <= kSingleMaxK && a.n_win == kWin && a.n_comp == t->k &&
+         a.n_win + a.n_comp <= kMaxSlots && t->rows != nullptr;
+}
+
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
-  if (!attn_uses_matrix_cores(a.q_dt, a.win_fmt, a.comp_fmt, a.n_win, a.n_comp)) {
+  const bool mc = attn_uses_matrix_cores(a.q_dt, a.win_fmt, a.comp_fmt, a.n_win, a.n_comp);
+  const int Hpad = (a.H + 15) & ~15;
+  const int hb = attn_head_block(a.Q, a.H, a.n_win + a.n_comp);
+  const int hchunks = (Hpad + hb - 1) / hb;
+  const bool fuse = mc && attn_select_fused(a, hb);
+  if (a.sel && !fuse) {
+    const hipError_t e = launch_topk_single(*a.sel, s);
+    if (e != hipSuccess) return e;
+  }
+  if (!mc) {
     ProfScope p("attn_f32", s);
     if (a.q_dt == 1) CSA_LAUNCH(p, attn_f32_kernel<true>, dim3((unsigned)a.Q, (unsigned)a.H), dim3(256), s, a);
     else CSA_LAUNCH(p, attn_f32_kernel<false>, dim3((unsigned)a.Q, (unsigned)a.H), dim3(256), s, a);
     return hipGetLastError();
   }
-  const int Hpad = (a.H + 15) & ~15;
-  const int hb = attn_head_block(a.Q, a.H, a.n_win + a.n_comp);
-  const int hchunks = (Hpad + hb - 1) / hb;
   // a source with no slots takes the other source's format (its loads are never issued)
   const int wf = a.n_win > 0 ? a.win_fmt : a.comp_fmt;
   const int cf = a.n_comp > 0 ? a.comp_fmt : wf;
   {
-    ProfScope p("attn_bf16", s);
+    ProfScope p(fuse ? "attn_select" : "attn_bf16", s);
     const dim3 grid((unsigned)(a.Q * a.n_split), (unsigned)hchunks);
-#define CSA_ATTN_FMT(K, NTG)                                                                                          \
-  if (wf == kRowFP8 && cf == kRowFP8) CSA_LAUNCH(p, (K<kRowFP8, kRowFP8, NTG>), grid, dim3(kAttnThreads), s, a); \
-  else if (wf == kRowFP8) CSA_LAUNCH(p, (K<kRowFP8, kRowBF16, NTG>), grid, dim3(kAttnThreads), s, a);           \
-  else if (cf == kRowFP8) CSA_LAUNCH(p, (K<kRowBF16, kRowFP8, NTG>), grid, dim3(kAttnThreads), s, a);           \
-  else CSA_LAUNCH(p, (K<kRowBF16, kRowBF16, NTG>), grid, dim3(kAttnThreads), s, a);
+    const TopkArgs t = fuse ? *a.sel : TopkArgs{};
     // rows are streamed (non-temporal) only when one block gathers each of them: with several head
     // blocks per query, the later blocks' gathers of a row hit the copy the first one left in L2
     const bool stream = a.stream_rows && hchunks == 1;
-#define CSA_ATTN_LAUNCH(K) \
-  if (stream) { CSA_ATTN_FMT(K, true) } else { CSA_ATTN_FMT(K, false) }
+#define CSA_ATTN_FMT(K, ...)                                                                                       \
+  if (wf == kRowFP8 && cf == kRowFP8) CSA_LAUNCH(p, (K<kRowFP8, kRowFP8, __VA_ARGS__>), grid, dim3(kAttnThreads), s, ARGS); \
+  else if (wf == kRowFP8) CSA_LAUNCH(p, (K<kRowFP8, kRowBF16, __VA_ARGS__>), grid, dim3(kAttnThreads), s, ARGS);           \
+  else if (cf == kRowFP8) CSA_LAUNCH(p, (K<kRowBF16, kRowFP8, __VA_ARGS__>), grid, dim3(kAttnThreads), s, ARGS);           \
+  else CSA_LAUNCH(p, (K<kRowBF16, kRowBF16, __VA_ARGS__>), grid, dim3(kAttnThreads), s, ARGS);
     if (hb == 16) {
-      CSA_ATTN_LAUNCH(attn_bf16_h16_kernel)
+#define ARGS a
+      if (stream) { CSA_ATTN_FMT(attn_bf16_h16_kernel, true) } else { CSA_ATTN_FMT(attn_bf16_h16_kernel, false) }
+#undef ARGS
     } else {
-      CSA_ATTN_LAUNCH(attn_bf16_kernel)
+#define ARGS a, t
+      if (fuse) {
+        if (stream) { CSA_ATTN_FMT(attn_bf16_kernel, true, true) } else { CSA_ATTN_FMT(attn_bf16_kernel, false, true) }
+      } else {
+        if (stream) { CSA_ATTN_FMT(attn_bf16_kernel, true, false) } else { CSA_ATTN_FMT(attn_bf16_kernel, false, false) }
+      }
+#undef ARGS
     }
-#undef CSA_ATTN_LAUNCH
 #undef CSA_ATTN_FMT
   }
   hipError_t e = hipGetLastError();

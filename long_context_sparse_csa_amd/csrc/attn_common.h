@@ -33,16 +33,19 @@ static __device__ __attribute__((aligned(256))) const uint8_t kZeroRow[1024] = {
 
 // Codes of four slots of query q (absolute slot indices s[k]; in[k] = the slot exists): all index
 // loads, then all page-table loads, are issued before any is used.  ok[k] = the slot has a row.
+// idx_list / rows_list, when given, replace the query's row of a.idx (slot-indexed) and of a.rows
+// (indexed by compressed slot): a block that selected its own rows keeps them in LDS.
 __device__ __forceinline__ void slot_codes4(const AttnArgs& a, int q, int r, const int* s, const bool* in,
-                                            uint64_t* code, bool* ok) {
+                                            uint64_t* code, bool* ok, const int32_t* idx_list = nullptr,
+                                            const int32_t* rows_list = nullptr) {
   const bool r_ok = r >= 0 && r < a.n_req;
   const int rr = r_ok ? r : 0;
   const bool has_win = a.win != nullptr;
   const bool has_pt = a.comp != nullptr && a.page_table != nullptr && a.max_pages > 0;
   const int64_t n_entries = (int64_t)a.max_pages * kPage;
-  const int32_t* idx_row = a.idx + (int64_t)q * a.ld_idx;
-  const int32_t* rows_row = a.rows ? a.rows + (int64_t)q * a.ld_rows - a.n_win : nullptr;
-  const bool rows_in = a.rows != nullptr && a.comp != nullptr;   // compressed rows arrive resolved
+  const int32_t* idx_row = idx_list ? idx_list : a.idx + (int64_t)q * a.ld_idx;
+  const int32_t* rows_row = rows_list ? rows_list : (a.rows ? a.rows + (int64_t)q * a.ld_rows : nullptr);
+  const bool rows_in = rows_row != nullptr && a.comp != nullptr;   // compressed rows arrive resolved
   const uint64_t zero = (uint64_t)(uintptr_t)kZeroRow;
   const int64_t win_rb = row_bytes(a.win_fmt), comp_rb = row_bytes(a.comp_fmt);
   int v[4], pg[4];
@@ -51,7 +54,7 @@ __device__ __forceinline__ void slot_codes4(const AttnArgs& a, int q, int r, con
   for (int k = 0; k < 4; ++k) {
     live[k] = r_ok && in[k];
     const int sk = live[k] ? s[k] : 0;
-    v[k] = (rows_in && sk >= a.n_win) ? rows_row[sk] : idx_row[sk];
+    v[k] = (rows_in && sk >= a.n_win) ? rows_row[sk - a.n_win] : idx_row[sk];
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) pg[k] = -1;

@@ -182,6 +182,11 @@ struct AttnArgs {
   // already resolved through the page table; null = resolve idx through the page table
   const int32_t* rows;
   int64_t ld_rows;
+  // host side only, optional (one-query-per-request decode with one-block rows): the selection of
+  // this step.  launch_attention either runs it inside the 64-head attention blocks (each block
+  // selects its query's rows into LDS, and the blocks of split 0 also write idx / rows) or launches
+  // it first.
+  const struct TopkArgs* sel = nullptr;
 };
 struct CompressArgs {
   const void* kv;            // token projections, row (tok - tok0) at kv + row * ld: [n_tok][coff * D]

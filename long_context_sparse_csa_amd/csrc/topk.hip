@@ -18,48 +18,12 @@
 #include "csa_device.h"
 #include "csa_internal.h"
 #include "indexer_score.h"
+#include "select_block.h"
 
 namespace csa {
 
 constexpr int kSelChunk = 4096;     // scores scanned per block
 constexpr int kCandLds = 4096;      // candidates resolved from LDS; more fall back to global memory
-
-__device__ __forceinline__ int64_t clamp_nv(const TopkArgs& a, int q) {
-  int64_t nv = a.n_vis[q];
-  return nv < 0 ? 0 : (nv > a.max_n_vis ? a.max_n_vis : nv);
-}
-
-// Visible count of row q: from the n_vis array, or derived (decode: ctx_len/4, prefill: (t+1)/4).
-__device__ __forceinline__ int64_t topk_row_count(const TopkArgs& a, int q) {
-  int64_t nv;
-  if (a.win_mode == 1) {
-    int r;
-    nv = decode_seen(a.ctx_len, a.max_ctx, a.q_per_req, q, r) / 4;
-  } else if (a.win_mode == 2) {
-    nv = (a.pos0 + q + 1) / 4;
-  } else {
-    nv = a.n_vis[q];
-  }
-  return nv < 0 ? 0 : (nv > a.max_n_vis ? a.max_n_vis : nv);
-}
-
-// Window part of the index list: decode ring slots (position % ring) of the 128 positions up to
-// the query's, or prefill positions t-127..t; -1 before position 0.  Written to columns [-128, 0)
-// relative to a.idx.
-__device__ __forceinline__ void write_window(const TopkArgs& a, int q) {
-  const int j = threadIdx.x;
-  if (j >= kWin) return;
-  int32_t v;
-  if (a.win_mode == 1) {
-    int r;
-    const int64_t p = decode_seen(a.ctx_len, a.max_ctx, a.q_per_req, q, r) - kWin + j;
-    v = p >= 0 ? (int32_t)(p % a.ring) : -1;
-  } else {
-    const int64_t p = a.pos0 + q - (kWin - 1) + j;
-    v = p >= 0 ? (int32_t)p : -1;
-  }
-  a.idx[(int64_t)q * a.ld_idx - kWin + j] = v;
-}
 
 // Exclusive prefix sum over the 256 threads of a block; *total receives the block sum.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s_wave, uint32_t* total) {
@@ -450,321 +414,6 @@ __global__ __launch_bounds__(256) void topk_finish_kernel(TopkArgs a) {
     }
   }
   for (int i = tid; i < k; i += 256) out[i] = sk[i] == 0x7FFFFFFF ? -1 : sk[i];
-}
-
-// ---- single-block selection: one block per query keeps its entries in registers (PER consecutive
-// entries per thread, in index order), so no global histogram, no zeroed workspace and no second
-// launch are needed.  Two users: short rows (n_vis <= kSingleMax), whose entries are the row itself,
-// and long decode rows, whose entries are the indexer's per-wave sketches (see topk_sketch_kernel).
-// Every barrier-separated phase costs on the order of a microsecond at 16 waves, and a predicated
-// LDS instruction costs its issue slot even when few lanes are active, so the phases are few, the
-// scans are done by a single wave and sparse passes skip instructions no lane needs:
-//   1. a 4096-bin histogram of the scores over the entries' value range gives the threshold bin b*
-//      and the count above it; b*'s entries (normally a handful) go to an LDS candidate list and
-//      one wave ranks them by their full keys, giving the exact k-th largest key T and how many
-//      keys equal to T are taken;
-//   2. when b* holds more than 64 entries (ties, clusters) or a score is not finite, the levels run
-//      on key prefixes instead: a 12-bit histogram of every key gives b*, and the keys of its
-//      entries are resolved by one wave (two 10-bit levels of the remaining 20 bits, no block
-//      barrier), or by two block-wide levels when more than kCandMax entries share b*;
-//   3. one block scan of the per-thread (greater, equal) counts, packed in one word, places the k
-//      indices in ascending order (equal keys at T in index order) in LDS, from where they are
-//      written with coalesced stores.
-constexpr int kSinglePer = 16;      // entries per thread, in index order (32 for the longest rows)
-constexpr int kCandMax = 2048;      // entries of the threshold bin resolved by one wave; more take
-                                    // the block-wide path
-
-// One wave scans `nb` bins (64 to 4096, a multiple of 256) from the top and finds the bin where
-// the running count first reaches `need` (1 <= need <= total): *digit, *before (count strictly
-// above it).  Two rounds, no serial search: per-lane sums and a shuffle scan pick the lane whose
-// range crosses `need`, then the 64 lanes read that range's bins one each and a second scan picks
-// the bin.  Lanes of other waves do nothing; the caller puts barriers around it.
-__device__ __forceinline__ void wave_find_desc(const uint32_t* bins, int nb, uint32_t need, uint32_t* digit,
-                                               uint32_t* before) {
-  const int lane = threadIdx.x & 63;
-  const int per = nb / 64;              // bins per lane: lane l owns [nb - per (l+1), nb - per l)
-  const int hi = nb - per * lane;       // exclusive top of this lane's range
-  uint32_t sum = 0;
-  for (int j = 0; j < per; j += 4) {
-    const uint4 c = *(const uint4*)&bins[hi - per + j];
-    sum += c.x + c.y + c.z + c.w;
-  }
-  const uint32_t inc = wave_inclusive_scan(sum);
-  const uint64_t cross = __ballot(inc - sum < need && inc >= need);
-  const int x = cross ? __ffsll((long long)cross) - 1 : 63;
-  const uint32_t pre_x = __builtin_amdgcn_readlane(inc - sum, x);
-  const int top = nb - per * x;         // lane j looks at bin top - 1 - j
-  const uint32_t c = lane < per ? bins[top - 1 - lane] : 0u;
-  const uint32_t cinc = wave_inclusive_scan(c);
-  const uint64_t hit = __ballot(lane < per && pre_x + cinc >= need);
-  const int y = hit ? __ffsll((long long)hit) - 1 : 0;
-  if (lane == y) {
-    *digit = (uint32_t)(top - 1 - y);
-    *before = pre_x + cinc - c;
-  }
-}
-
-// the score of an order key (the inverse of order_key; -0.0 comes back as +0.0)
-__device__ __forceinline__ float key_value(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
-}
-
-// LDS of the one-block selection (16 KB of bins + 8 KB of candidate keys / selected indices).
-template <int NT>
-struct SelShared {
-  uint32_t bins[kHistBins];
-  uint32_t scan[NT / 64];          // per-wave totals of the final scan
-  // order keys of the threshold bin's entries while the threshold is resolved, then the selected
-  // indices
-  uint32_t cand_sel[kCandMax > kSingleMaxK ? kCandMax : kSingleMaxK];
-  uint32_t s_digit, s_before, s_ncand, s_T, s_need;
-  uint32_t ext[2 * (NT / 64)];     // per-wave largest / smallest key
-};
-
-// Exact k-th largest order key T among the block's entries (thread t holds key[0..PER) with bit j
-// of vm set for a real entry) and how many entries equal to T are taken: sh.s_T, sh.s_need on
-// return (after a barrier).  The block holds at least k real entries.  On entry sh.bins is zeroed,
-// sh.s_ncand is 0 and a barrier has passed since.
-template <int NT, int PER>
-__device__ void block_threshold(const uint32_t* key, uint32_t vm, uint32_t k, SelShared<NT>& sh) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  // extremes of the real keys: per wave, then across waves after the barrier
-  {
-    uint32_t kmx = 0u, kmn = 0xFFFFFFFFu;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if ((vm >> j) & 1u) {
-        kmx = key[j] > kmx ? key[j] : kmx;
-        kmn = key[j] < kmn ? key[j] : kmn;
-      }
-    }
-    kmx = wave_umax(kmx);
-    kmn = ~wave_umax(~kmn);   // min through the max of complements
-    if (lane == 0) {
-      sh.ext[wave] = kmx;
-      sh.ext[NT / 64 + wave] = kmn;
-    }
-  }
-  __syncthreads();
-  // Level 1 on the value range: 4096 equal-width bins between the smallest and largest finite
-  // score.  Scores crowd a few of the fixed 12-bit key-prefix bins (the exponent and three
-  // mantissa bits), so LDS atomics collide and the threshold bin holds hundreds of entries; on the
-  // value range the bins hold a handful.  The bin index is a monotone function of the score
-  // (subtraction, multiplication by a positive scale and truncation all preserve order), so b*
-  // and the counts above it are exact.  When b* holds at most 64 entries one wave ranks them by
-  // their full keys; otherwise (ties, clusters, non-finite scores) the key-prefix levels run.
-  bool resolved = false;
-  {
-    uint32_t kmax = 0u, kmin = 0xFFFFFFFFu;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-      kmax = sh.ext[w] > kmax ? sh.ext[w] : kmax;
-      kmin = sh.ext[NT / 64 + w] < kmin ? sh.ext[NT / 64 + w] : kmin;
-    }
-    const float vmin = key_value(kmin), vmax = key_value(kmax);
-    const float scale = 4096.f / (vmax - vmin);
-    // every real key is finite (NaN maps below -inf, infinities outside +-FLT_MAX) and spread
-    const bool adaptive = kmin >= order_key(-3.40282347e+38f) && kmax <= order_key(3.40282347e+38f) &&
-                          kmax > kmin && scale > 0.f && scale < 3.0e38f;
-    if (adaptive) {
-      uint32_t bin[PER];
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        const float x = (key_value(key[j]) - vmin) * scale;
-        // x >= 0 for real entries; the others (never counted) are clamped too
-        const uint32_t b = x < 4095.f ? (x > 0.f ? (uint32_t)x : 0u) : 4095u;
-        bin[j] = b;
-        if ((vm >> j) & 1u) atomicAdd(&sh.bins[b], 1u);
-      }
-      __syncthreads();
-      if (wave == 0) wave_find_desc(sh.bins, kHistBins, k, &sh.s_digit, &sh.s_before);
-      __syncthreads();
-      const uint32_t bstar = sh.s_digit;
-      const uint32_t need1 = k - sh.s_before;
-      {
-        uint32_t hm = 0;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) hm |= (((vm >> j) & 1u) && bin[j] == bstar) ? (1u << j) : 0u;
-        const uint32_t hits = __popc(hm);
-        const uint32_t incl = wave_inclusive_scan(hits);
-        uint32_t base = 0;
-        if (lane == 63 && incl) base = atomicAdd(&sh.s_ncand, incl);
-        base = __builtin_amdgcn_readlane(base, 63);
-        uint32_t pos = base + incl - hits;
-        while (hm) {
-          const int j = __ffs((int)hm) - 1;
-          hm &= hm - 1u;
-          if (pos < 64u) sh.cand_sel[pos] = key[j];
-          ++pos;
-        }
-      }
-      __syncthreads();
-      const uint32_t n_cand = sh.s_ncand;
-      if (n_cand <= 64u) {
-        // rank the candidates by their keys: the threshold is the key with fewer than need1 keys
-        // above it and at least need1 at or above it
-        if (wave == 0) {
-          const uint32_t mine = lane < (int)n_cand ? sh.cand_sel[lane] : 0u;
-          uint32_t gt = 0, ge = 0;
-          for (int j = 0; j < (int)n_cand; ++j) {
-            const uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)mine, j);
-            gt += o > mine ? 1u : 0u;
-            ge += o >= mine ? 1u : 0u;
-          }
-          if (lane < (int)n_cand && gt < need1 && ge >= need1) {   // every such lane holds the same key
-            sh.s_T = mine;
-            sh.s_need = need1 - gt;
-          }
-        }
-        resolved = true;
-      } else {
-        for (int i = tid; i < kHistBins; i += NT) sh.bins[i] = 0u;
-        if (tid == 0) sh.s_ncand = 0u;
-        __syncthreads();
-      }
-    }
-  }
-  if (!resolved) {
-    // level 1: top 12 key bits of every entry (all lanes active: one LDS atomic instruction covers 64)
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if ((vm >> j) & 1u) atomicAdd(&sh.bins[key[j] >> kHistShift], 1u);
-    __syncthreads();
-    if (wave == 0) wave_find_desc(sh.bins, kHistBins, k, &sh.s_digit, &sh.s_before);
-    __syncthreads();
-    const uint32_t bstar = sh.s_digit;
-    const uint32_t need1 = k - sh.s_before;   // entries still to take from bin b* (>= 1)
-    // the entries of bin b* become candidates: their keys are appended to LDS with one atomic per
-    // wave, a lane's after those of the lanes below it
-    {
-      uint32_t hm = 0;   // bit j: entry j is in b*
-#pragma unroll
-      for (int j = 0; j < PER; ++j) hm |= (((vm >> j) & 1u) && (key[j] >> kHistShift) == bstar) ? (1u << j) : 0u;
-      const uint32_t hits = __popc(hm);
-      const uint32_t incl = wave_inclusive_scan(hits);
-      uint32_t base = 0;
-      if (lane == 63 && incl) base = atomicAdd(&sh.s_ncand, incl);
-      base = __builtin_amdgcn_readlane(base, 63);
-      uint32_t pos = base + incl - hits;
-      while (hm) {
-        const int j = __ffs((int)hm) - 1;
-        hm &= hm - 1u;
-        if (pos < (uint32_t)kCandMax) sh.cand_sel[pos] = key[j];
-        ++pos;
-      }
-    }
-    __syncthreads();
-    const uint32_t n_cand = sh.s_ncand;
-    if (n_cand <= (uint32_t)kCandMax) {
-      // wave 0 alone resolves the 20 low key bits among the candidates (two 10-bit levels in a
-      // wave-private histogram); LDS operations of one wave complete in order
-      if (wave == 0) {
-        uint32_t prefix = bstar, need = need1;
-#pragma unroll 1
-        for (int lvl = 0; lvl < 2; ++lvl) {
-          const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
-#pragma unroll
-          for (int i = 0; i < 1024; i += 256) *(uint4*)&sh.bins[i + 4 * lane] = make_uint4(0u, 0u, 0u, 0u);
-          __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-          __builtin_amdgcn_wave_barrier();
-          // four candidates per lane per pass: their reads are all in flight before the first atomic
-          for (uint32_t i0 = 0; i0 < n_cand; i0 += 256) {
-            uint32_t kk[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const uint32_t i = i0 + 64 * u + lane;
-              kk[u] = sh.cand_sel[i < n_cand ? i : 0];
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const uint32_t i = i0 + 64 * u + lane;
-              if (i < n_cand && (kk[u] >> (shift + 10)) == prefix) atomicAdd(&sh.bins[(kk[u] >> shift) & 1023u], 1u);
-            }
-          }
-          __builtin_amdgcn_s_waitcnt(0xc07f);
-          __builtin_amdgcn_wave_barrier();
-          wave_find_desc(sh.bins, 1024, need, &sh.s_digit, &sh.s_before);
-          __builtin_amdgcn_s_waitcnt(0xc07f);
-          __builtin_amdgcn_wave_barrier();
-          prefix = (prefix << 10) | sh.s_digit;
-          need -= sh.s_before;
-        }
-        if (lane == 0) {
-          sh.s_T = prefix;
-          sh.s_need = need;
-        }
-      }
-    } else {
-      // many entries share b* (heavily tied scores): levels 2 and 3 over the whole block, ten more
-      // key bits each, counting only entries with the current prefix
-      uint32_t prefix = bstar, need = need1;
-#pragma unroll 1
-      for (int lvl = 0; lvl < 2; ++lvl) {
-        const int shift = kHistShift - 10 * (lvl + 1);   // 10, then 0
-        for (int i = tid; i < 1024; i += NT) sh.bins[i] = 0u;
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-          const bool hit = ((vm >> j) & 1u) && (key[j] >> (shift + 10)) == prefix;
-          if (__any(hit) && hit) atomicAdd(&sh.bins[(key[j] >> shift) & 1023u], 1u);
-        }
-        __syncthreads();
-        if (wave == 0) wave_find_desc(sh.bins, 1024, need, &sh.s_digit, &sh.s_before);
-        __syncthreads();
-        prefix = (prefix << 10) | sh.s_digit;
-        need -= sh.s_before;
-      }
-      if (tid == 0) {
-        sh.s_T = prefix;
-        sh.s_need = need;
-      }
-    }
-  }
-  __syncthreads();
-}
-
-// The selected entries' indices in ascending order into sh.cand_sel[0, k): every real entry above
-// T and the first `need` equal to T (index order), placed by one block scan of the per-thread
-// (greater, equal) counts packed in one word (both totals stay below 2^16).  idx_of(j) is the index
-// of this thread's entry j; thread t's entries precede thread t+1's in index order.  Ends with a
-// barrier.
-template <int NT, int PER, class IdxOf>
-__device__ void block_emit(const uint32_t* key, uint32_t vm, uint32_t T, uint32_t need, uint32_t k, IdxOf idx_of,
-                           SelShared<NT>& sh) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  uint32_t gm = 0, em = 0;       // bit j: entry j is above T / equal to T
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const bool ok = (vm >> j) & 1u;
-    gm |= (ok && key[j] > T) ? (1u << j) : 0u;
-    em |= (ok && key[j] == T) ? (1u << j) : 0u;
-  }
-  const uint32_t n_gt = __popc(gm), n_eq = __popc(em);
-  const uint32_t mine = (n_gt << 16) | n_eq;
-  const uint32_t incl = wave_inclusive_scan(mine);
-  if (lane == 63) sh.scan[wave] = incl;
-  __syncthreads();
-  uint32_t pre = incl - mine;
-#pragma unroll
-  for (int w = 0; w < NT / 64; ++w) pre += w < wave ? sh.scan[w] : 0u;
-  const uint32_t eq_before = pre & 0xFFFFu;
-  uint32_t pos = (pre >> 16) + (eq_before < need ? eq_before : need);
-  uint32_t take_eq = eq_before < need ? (need - eq_before < n_eq ? need - eq_before : n_eq) : 0u;
-  // the taken entries: all above T, and the lowest-index take_eq of those equal to T
-  uint32_t tm = gm;
-  for (uint32_t t = 0; t < take_eq; ++t) {
-    const uint32_t low = em & (0u - em);
-    tm |= low;
-    em ^= low;
-  }
-  int32_t* sel = (int32_t*)sh.cand_sel;
-  while (tm) {
-    const int j = __ffs((int)tm) - 1;
-    tm &= tm - 1u;
-    if (pos < k) sel[pos] = idx_of(j);
-    ++pos;
-  }
-  __syncthreads();
 }
 
 // NT threads cover rows of up to NT * PER entries; short rows take a small block so that several
