@@ -289,6 +289,21 @@ def test_decode_batched_full(dev):
         check_attention(out[qi], ref, BF16_TOL, f"query {qi}")
 
 
+def test_decode_selection_in_attention_short_and_long_rows(dev):
+    """More than 16 requests at 64 heads: the attention blocks select their own rows.  Contexts mix
+    rows with fewer visible entries than k (the list is every visible entry, then -1), rows at and
+    around 4k (k entries exactly), rows ending mid-page and rows of the full 16,384 entries; every
+    query's selection and output are checked against the oracle."""
+    run, tio = _run()
+    ctx = [0, 3, 700, 2047, 2048, 2052, 3001, 9000, 65536, 40000, 65535, 4100,
+           1, 130, 2600, 60000, 17, 33333, 5000, 64000]
+    wl = configs.make_decode("sel_attn", ctx, H=64, HI=64, seed=23)
+    _say(f"decode, selection inside the attention blocks (B={len(ctx)}, H=64, fp8)")
+    out, idx = run.decode(wl, tio.to_device(wl, dev))
+    err = _check_decode(wl, tio.out_to_numpy(out), idx.cpu().numpy(), BF16_TOL, empty_rows=(0,))
+    _say(f"max err {err:.2e}")
+
+
 def test_decode_fp4_indexer(dev):
     """Whole decode path with the MXFP4 indexer (E2M1 pairs, E8M0 per 32): 4 requests at 65,536
     tokens plus a ragged batch whose contexts end mid-page, with 40 indexer heads."""
