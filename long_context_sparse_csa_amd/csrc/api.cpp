@@ -465,9 +465,9 @@ static csa_status run_path(int mode, int32_t rows, int32_t H, int32_t HI, int32_
     t.num_pages = comp->num_pages;
   }
   if (sketch) { t.sk_top = pw.sk_top; t.sk_bound = pw.sk_bound; t.sk_waves = pw.sk_waves; t.ia = ia; }
-  // one query per request with one-block rows: the attention launch runs the selection (inside its
-  // own blocks when it can, else as its own launch first)
-  const bool sel_in_attn = single && mode == 1 && S == 1;
+  // one query per request with one-block or sketch rows: the attention launch runs the selection
+  // (inside its own blocks when it can, else as its own launch first)
+  const bool sel_in_attn = (single || sketch) && mode == 1 && S == 1;
   if (!sel_in_attn)
     CSA_HIP(single ? csa::launch_topk_single(t, stream)
                    : (sketch ? csa::launch_topk_sketch(t, stream) : csa::launch_topk_select(t, stream)));

@@ -29,6 +29,7 @@
 #include <cstdlib>
 
 #include "attn_common.h"
+#include "indexer_score.h"
 #include "select_block.h"
 
 namespace csa {
@@ -297,6 +298,8 @@ constexpr int kSelListOff = kSelOff + 32768;                          // after S
 constexpr int kSelRowsOff = kSelListOff + 4 * kMaxSlots;
 constexpr int kSelPtOff = kSelRowsOff + 4 * kMaxSlots;
 static_assert(sizeof(SelShared<kAttnThreads>) <= 32768, "selection LDS fits its space");
+constexpr int kSelSketchPer = 8;                                      // sketch entries per thread
+static_assert(kSelPtOff + 4 * (kSelRowMax / kPage) <= 3 * kTile * kKrStride * 2, "selection LDS fits the 16-head ring");
 static_assert(kSelPtOff + 4 * (kSelRowMax / kPage) <= 4 * kTile * kKrStride * 2, "selection LDS fits the ring");
 
 // Selects query q's rows into LDS: idx_list[0 .. n_win + k) (the ring window, then the k entries in
@@ -360,6 +363,121 @@ __device__ __forceinline__ void select_rows(const TopkArgs& t, int q, uint8_t* l
   if (write_out) {
     for (int i = tid; i < kWin + k; i += kAttnThreads) t.idx[(int64_t)q * t.ld_idx - kWin + i] = idx_list[i];
     for (int i = tid; i < k; i += kAttnThreads) t.rows[(int64_t)q * t.ld_rows + i] = rows_list[i];
+  }
+}
+
+// The same for long decode rows, from the indexer's per-wave sketches as topk_sketch_kernel
+// selects them (PER sketch entries per thread): the sketches' exact k-th largest key T decides the
+// row when every wave's bound lies below T; otherwise the block rescores the row if it has no
+// stored scores and selects from the full row (select_streamed), writing straight into the lists.
+template <int PER>
+__device__ __forceinline__ void select_rows_sketch(const TopkArgs& t, int q, uint8_t* lds, bool write_out) {
+  constexpr int NT = kAttnThreads;
+  const int tid = threadIdx.x;
+  SelShared<NT>& sh = *(SelShared<NT>*)(lds + kSelOff);
+  int32_t* idx_list = (int32_t*)(lds + kSelListOff);
+  int32_t* rows_list = (int32_t*)(lds + kSelRowsOff);
+  const int k = t.k;
+  int r;
+  const int64_t seen = decode_seen(t.ctx_len, t.max_ctx, 1, q, r);
+  const int64_t nv = topk_row_count(t, q);
+  const int32_t* pt = t.page_table + (int64_t)r * t.max_pages;
+  auto row_of = [&](int c) {
+    const int pg = pt[c >> 6];
+    return (unsigned)pg < (unsigned)t.num_pages ? pg * kPage + (c & (kPage - 1)) : -1;
+  };
+  if (tid < kWin) {
+    const int64_t p = seen - kWin + tid;
+    idx_list[tid] = p >= 0 ? (int32_t)(p % t.ring) : -1;
+  }
+  if (nv <= k) {
+    for (int i = tid; i < k; i += NT) {
+      idx_list[kWin + i] = i < nv ? i : -1;
+      rows_list[i] = i < nv ? row_of(i) : -1;
+    }
+  } else {
+    const int64_t n_w = (nv + kSketchSpan - 1) / kSketchSpan;
+    const int64_t n_u = n_w * kSketchTop;
+    const uint2* top = t.sk_top + (int64_t)q * t.sk_waves * kSketchTop;
+    const uint32_t* bound = t.sk_bound + (int64_t)q * t.sk_waves;
+    uint32_t key[PER], idx[PER], vm = 0u;
+    const int64_t u0 = (int64_t)tid * PER;
+#pragma unroll
+    for (int j = 0; j < PER; j += 2) {
+      const int64_t u = u0 + j;
+      const uint4 x = *(const uint4*)&top[u < n_u ? u : 0];
+      key[j] = x.x; idx[j] = x.y; key[j + 1] = x.z; idx[j + 1] = x.w;
+    }
+    constexpr int kBnd = (kSketchMaxWaves + NT - 1) / NT;
+    uint32_t bnd[kBnd];
+#pragma unroll
+    for (int i = 0; i < kBnd; ++i) {
+      const int64_t W = tid + (int64_t)i * NT;
+      bnd[i] = W < n_w ? bound[W] : 0u;
+    }
+    for (int i = tid; i < kHistBins; i += NT) sh.bins[i] = 0u;
+    if (tid == 0) sh.s_ncand = 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) vm |= (u0 + j < n_u && idx[j] != 0xFFFFFFFFu ? 1u : 0u) << j;
+    {
+      const uint32_t wsum = wave_inclusive_scan(__popc(vm));
+      if ((tid & 63) == 63) sh.scan[tid >> 6] = wsum;
+    }
+    __syncthreads();
+    uint32_t n_real = 0u;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) n_real += sh.scan[w];
+    bool from_sketch = n_real >= (uint32_t)k;
+    if (from_sketch) {
+      block_threshold<NT, PER>(key, vm, (uint32_t)k, sh);
+      const uint32_t T = sh.s_T;
+      bool reach = false;
+#pragma unroll
+      for (int i = 0; i < kBnd; ++i) reach |= tid + (int64_t)i * NT < n_w && bnd[i] >= T;
+      from_sketch = !__syncthreads_or(reach);
+    }
+    if (from_sketch) {
+      block_emit<NT, PER>(key, vm, sh.s_T, sh.s_need, (uint32_t)k, [&](int j) { return (int32_t)idx[j]; }, sh);
+      const int32_t* sel = (const int32_t*)sh.cand_sel;
+      for (int i = tid; i < k; i += NT) {
+        const int c = sel[i];
+        const int rw = row_of(c);
+        CSA_DBG_COUNT(rw < 0);
+        idx_list[kWin + i] = c;
+        rows_list[i] = rw;
+      }
+    } else {
+      if (t.ia.sk_rescore_from > 0 && nv >= t.ia.sk_rescore_from) {
+        // the indexer stored no scores for this row: rescore it, each wave a span at a time (every
+        // block of the query writes the same scores; each reads back only its own)
+        const int wave = tid >> 6, lane = tid & 63;
+        const int nhg = (t.ia.HI + 15) / 16;
+        for (int64_t W = wave; W < n_w; W += NT / 64) {
+          if (t.ia.dt == 3) {
+            switch (nhg) {
+              case 1: rescore_span<1, true>(t.ia, q, W, lane); break;
+              case 2: rescore_span<2, true>(t.ia, q, W, lane); break;
+              case 3: rescore_span<3, true>(t.ia, q, W, lane); break;
+              default: rescore_span<4, true>(t.ia, q, W, lane); break;
+            }
+          } else {
+            switch (nhg) {
+              case 1: rescore_span<1, false>(t.ia, q, W, lane); break;
+              case 2: rescore_span<2, false>(t.ia, q, W, lane); break;
+              case 3: rescore_span<3, false>(t.ia, q, W, lane); break;
+              default: rescore_span<4, false>(t.ia, q, W, lane); break;
+            }
+          }
+        }
+        __syncthreads();   // the block reads the rescored row next (workgroup scope: one L1)
+      }
+      select_streamed<NT>(t, q, nv, (uint32_t)k, sh, idx_list + kWin, rows_list, pt);
+    }
+  }
+  __syncthreads();
+  if (write_out) {
+    for (int i = tid; i < kWin + k; i += NT) t.idx[(int64_t)q * t.ld_idx - kWin + i] = idx_list[i];
+    for (int i = tid; i < k; i += NT) t.rows[(int64_t)q * t.ld_rows + i] = rows_list[i];
   }
 }
 
@@ -698,8 +816,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a, 
 // every consumer runs the same softmax on the summed scores, so P^T and the rescale factors never
 // cross waves.  Consumer c then accumulates output dims [128c, 128c+128).  One barrier per tile:
 // iteration k runs the softmax and P.V of tile k and the partial scores of tile k+1.
-template <int WF, int CF, bool NTG>
-__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs a) {
+template <int WF, int CF, bool NTG, bool SEL = false>
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs a, TopkArgs t) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
@@ -727,12 +845,26 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs
   // loaded after the slot codes are resolved: the barrier that publishes the codes waits for every
   // outstanding load, and the producers' first gathers should not wait for q
   v8bf qop[8];
-  resolve_codes<kAttnThreads>(a, q, r, t_begin * kTile, nt * kTile, codes, vmask, tid);
-  __syncthreads();
-  if (wave < 4) {
+  auto load_q = [&] {
     const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)q * a.H + (h < a.H ? h : 0)) * kD + 256 * dh + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) qop[ks] = *(const v8bf*)(qp + 32 * ks);
+  };
+  const int32_t* idx_list = nullptr;
+  const int32_t* rows_list = nullptr;
+  if constexpr (SEL) {
+    // the long rows' selection from the indexer's sketches, into LDS borrowed from ring slots 1-2;
+    // q does not depend on it, so its loads overlap it
+    if (wave < 4) load_q();
+    uint8_t* lds = (uint8_t*)&Kr[0][0];
+    select_rows_sketch<kSelSketchPer>(t, q, lds, split == 0 && blockIdx.y == 0);
+    idx_list = (const int32_t*)(lds + kSelListOff);
+    rows_list = (const int32_t*)(lds + kSelRowsOff);
+  }
+  resolve_codes<kAttnThreads>(a, q, r, t_begin * kTile, nt * kTile, codes, vmask, tid, idx_list, rows_list);
+  __syncthreads();
+  if constexpr (!SEL) {
+    if (wave < 4) load_q();
   }
 
   float m = kNegBig, lsum = 0.f;   // softmax state of head h (identical in the four consumers)
@@ -1024,9 +1156,12 @@ static bool attn_select_fused(const AttnArgs& a, int hb) {
     return e ? atoi(e) : -1;
   }();
   const TopkArgs* t = a.sel;
-  return mode != 0 && t != nullptr && hb == 64 && t->win_mode == 1 && t->q_per_req == 1 &&
-         t->max_n_vis <= kSelRowMax && t->k <= kSingleMaxK && a.n_win == kWin && a.n_comp == t->k &&
-         a.n_win + a.n_comp <= kMaxSlots && t->rows != nullptr;
+  if (mode == 0 || t == nullptr || t->win_mode != 1 || t->q_per_req != 1 || t->k > kSingleMaxK ||
+      a.n_win != kWin || a.n_comp != t->k || a.n_win + a.n_comp > kMaxSlots || t->rows == nullptr)
+    return false;
+  if (t->sk_top != nullptr)   // long rows: 16-head blocks select from the sketches
+    return hb == 16 && topk_sketch_waves(t->max_n_vis) * kSketchTop <= kAttnThreads * kSelSketchPer;
+  return hb == 64 && t->max_n_vis <= kSelRowMax;
 }
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
@@ -1036,7 +1171,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int hchunks = (Hpad + hb - 1) / hb;
   const bool fuse = mc && attn_select_fused(a, hb);
   if (a.sel && !fuse) {
-    const hipError_t e = launch_topk_single(*a.sel, s);
+    const hipError_t e = a.sel->sk_top ? launch_topk_sketch(*a.sel, s) : launch_topk_single(*a.sel, s);
     if (e != hipSuccess) return e;
   }
   if (!mc) {
@@ -1061,8 +1196,12 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   else if (cf == kRowFP8) CSA_LAUNCH(p, (K<kRowBF16, kRowFP8, __VA_ARGS__>), grid, dim3(kAttnThreads), s, ARGS);           \
   else CSA_LAUNCH(p, (K<kRowBF16, kRowBF16, __VA_ARGS__>), grid, dim3(kAttnThreads), s, ARGS);
     if (hb == 16) {
-#define ARGS a
-      if (stream) { CSA_ATTN_FMT(attn_bf16_h16_kernel, true) } else { CSA_ATTN_FMT(attn_bf16_h16_kernel, false) }
+#define ARGS a, t
+      if (fuse) {
+        if (stream) { CSA_ATTN_FMT(attn_bf16_h16_kernel, true, true) } else { CSA_ATTN_FMT(attn_bf16_h16_kernel, false, true) }
+      } else {
+        if (stream) { CSA_ATTN_FMT(attn_bf16_h16_kernel, true, false) } else { CSA_ATTN_FMT(attn_bf16_h16_kernel, false, false) }
+      }
 #undef ARGS
     } else {
 #define ARGS a, t

@@ -93,7 +93,8 @@ __device__ __forceinline__ void slot_codes4(const AttnArgs& a, int q, int r, con
 // consecutive slots per pass.
 template <int NT>
 __device__ __forceinline__ void resolve_codes(const AttnArgs& a, int q, int r, int s_begin, int s_count,
-                                              uint64_t* codes, uint32_t* vmask, int tid) {
+                                              uint64_t* codes, uint32_t* vmask, int tid,
+                                              const int32_t* idx_list = nullptr, const int32_t* rows_list = nullptr) {
   const int n_idx = a.n_win + a.n_comp;
   for (int b = 0; b < s_count; b += 4 * NT) {
     int sl[4];
@@ -105,7 +106,7 @@ __device__ __forceinline__ void resolve_codes(const AttnArgs& a, int q, int r, i
       sl[k] = s_begin + i;
       in[k] = i < s_count && s_begin + i < n_idx;
     }
-    slot_codes4(a, q, r, sl, in, c, ok);
+    slot_codes4(a, q, r, sl, in, c, ok, idx_list, rows_list);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int i = b + tid + NT * k;

@@ -488,99 +488,6 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
 // row's; otherwise (ties at T, or a wave holding more than 8 of the row's top entries) the block
 // selects from the full score row instead (select_streamed).
 
-// Exact selection over a whole score row by one block: three radix levels (12, 10, 10 bits of the
-// order key) over the row, then one pass in index order that places the selected entries with
-// block scans.  Reads the row four times; the fallback of the sketch path.
-template <int NT>
-__device__ void select_streamed(const TopkArgs& a, int q, int64_t nv, uint32_t k, SelShared<NT>& sh,
-                                int32_t* out, int32_t* rows_out, const int32_t* pt) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const float* row = a.logits + (int64_t)q * a.ld;
-  uint32_t prefix = 0u, need = k;
-  int pbits = 0;
-#pragma unroll 1
-  for (int lvl = 0; lvl < 3; ++lvl) {
-    const int wdt = lvl == 0 ? 12 : 10;
-    const int nb = 1 << wdt;
-    const int shift = 32 - pbits - wdt;
-    for (int i = tid; i < nb; i += NT) sh.bins[i] = 0u;
-    __syncthreads();
-    for (int64_t c = (int64_t)tid * 4; c < nv; c += (int64_t)NT * 4) {
-      // rows are 16-byte aligned and ld is a multiple of 64, so the 4-entry load stays in the row
-      const float4 x = *(const float4*)(row + c);
-      const float v[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t key = order_key(v[e]);
-        if (c + e < nv && (pbits == 0 || (key >> (32 - pbits)) == prefix))
-          atomicAdd(&sh.bins[(key >> shift) & (uint32_t)(nb - 1)], 1u);
-      }
-    }
-    __syncthreads();
-    if (wave == 0) wave_find_desc(sh.bins, nb, need, &sh.s_digit, &sh.s_before);
-    __syncthreads();
-    prefix = (prefix << wdt) | sh.s_digit;
-    pbits += wdt;
-    need -= sh.s_before;
-    __syncthreads();
-  }
-  const uint32_t T = prefix;
-  // placement in index order, 4 consecutive entries per thread and NT * 4 per pass
-  uint32_t gt_run = 0u, eq_run = 0u;   // selected-above / equal counts of earlier passes
-  for (int64_t base = 0; base < nv; base += (int64_t)NT * 4) {
-    const int64_t c0 = base + (int64_t)tid * 4;
-    uint32_t gm = 0u, em = 0u;
-    if (c0 < nv) {
-      const float4 x = *(const float4*)(row + c0);
-      const float v[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t key = order_key(v[e]);
-        const bool ok = c0 + e < nv;
-        gm |= (ok && key > T) ? (1u << e) : 0u;
-        em |= (ok && key == T) ? (1u << e) : 0u;
-      }
-    }
-    const uint32_t n_gt = __popc(gm), n_eq = __popc(em);
-    const uint32_t mine = (n_gt << 16) | n_eq;
-    const uint32_t incl = wave_inclusive_scan(mine);
-    if (lane == 63) sh.scan[wave] = incl;
-    __syncthreads();
-    uint32_t pre = incl - mine, tot = 0u;
-#pragma unroll
-    for (int w = 0; w < NT / 64; ++w) {
-      pre += w < wave ? sh.scan[w] : 0u;
-      tot += sh.scan[w];
-    }
-    __syncthreads();   // sh.scan is rewritten by the next pass
-    const uint32_t eq_before = eq_run + (pre & 0xFFFFu);
-    uint32_t pos = gt_run + (pre >> 16) + (eq_before < need ? eq_before : need);
-    uint32_t take_eq = eq_before < need ? (need - eq_before < n_eq ? need - eq_before : n_eq) : 0u;
-    uint32_t tm = gm;
-    for (uint32_t t = 0; t < take_eq; ++t) {
-      const uint32_t low = em & (0u - em);
-      tm |= low;
-      em ^= low;
-    }
-    while (tm) {
-      const int e = __ffs((int)tm) - 1;
-      tm &= tm - 1u;
-      if (pos < k) {
-        const int c = (int)(c0 + e);
-        out[pos] = c;
-        if (rows_out) {
-          const int pg = pt[c >> 6];
-          rows_out[pos] = (unsigned)pg < (unsigned)a.num_pages ? pg * kPage + (c & (kPage - 1)) : -1;
-        }
-      }
-      ++pos;
-    }
-    gt_run += tot >> 16;
-    eq_run += tot & 0xFFFFu;
-    if (gt_run + (eq_run < need ? eq_run : need) >= k) break;   // block-uniform
-  }
-}
-
 template <int PER>
 __global__ __launch_bounds__(1024) void topk_sketch_kernel(TopkArgs a) {
   constexpr int NT = 1024;
