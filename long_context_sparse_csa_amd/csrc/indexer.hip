@@ -110,12 +110,14 @@ __device__ __forceinline__ void sketch_wave(const uint32_t* key8, uint32_t valid
   if (lane == 0) *bound = bnd;
 }
 
-// Runs at two waves per SIMD (its resident query operands and two page buffers take about 190
-// VGPRs); stating that occupancy to the compiler (amdgpu_waves_per_eu) changes its schedule and
-// measured faster: long-context indexer 50.0 -> 48.2 us, batched 17.0 -> 16.5 us (interleaved, one
-// box).
+// FP8 operands run at two waves per SIMD (the resident query operands and two page buffers take
+// about 190 VGPRs); stating that occupancy to the compiler (amdgpu_waves_per_eu) changes its
+// schedule and measured faster: long-context indexer 50.0 -> 48.2 us, batched 17.0 -> 16.5 us
+// (interleaved, one box).  FP4 fits three waves (about 150 VGPRs), and capping it at two cost its
+// long-context launch 1.4 us, so its bound stays three.
 template <int NHG, int SEL, bool FP4, int NQ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void indexer_fp8_kernel(IndexerArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, FP4 ? 3 : 2))) void indexer_fp8_kernel(
+    IndexerArgs a) {
   constexpr bool HIST = SEL == kSelHist;
   constexpr bool SK = SEL == kSelSketch;
   constexpr int pages_per_wave = kPagesPerWave<FP4>;
