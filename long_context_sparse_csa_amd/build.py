@@ -87,7 +87,7 @@ def build_host_sanitized(verbose: bool = False) -> str:
     kernel launchers replaced by stubs that fail (launch_stubs.cpp): the CPU ABI tests run against
     it.  Not a GPU build; loading it in place of libcsa.so launches nothing."""
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
-    tmp = HOST_ASAN_LIB + ".tmp"
+    tmp = f"{HOST_ASAN_LIB}.tmp{os.getpid():x}"   # concurrent builders (test workers) each rename their own
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fno-omit-frame-pointer",
            "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-D__HIP_PLATFORM_AMD__",
            "-Wno-attributes", "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
