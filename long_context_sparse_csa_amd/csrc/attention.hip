@@ -304,50 +304,58 @@ static_assert(kSelPtOff + 4 * (kSelRowMax / kPage) <= 4 * kTile * kKrStride * 2,
 
 // Selects query q's rows into LDS: idx_list[0 .. n_win + k) (the ring window, then the k entries in
 // ascending order, -1 past the visible ones) and rows_list[0 .. k) (their pool rows, -1 if none).
-__device__ __forceinline__ void select_rows(const TopkArgs& t, int q, uint8_t* lds, bool write_out) {
+// Every load of the prologue (the context length, the first page ids, the scores up to the widest
+// row, all in bounds and masked once the row's length is known) is issued before the first wait: a
+// chain of dependent loads (length, then page ids, then scores) cost several memory round trips per
+// block.  issue_more() issues the caller's own loads after the first barrier, where nothing waits
+// for them until the selection is done (issued earlier, the waits for the scores would also wait for
+// them: the load counter drains in order).
+template <class IssueMore>
+__device__ __forceinline__ void select_rows(const TopkArgs& t, int q, uint8_t* lds, bool write_out, IssueMore issue_more) {
   const int tid = threadIdx.x;
   SelShared<kAttnThreads>& sh = *(SelShared<kAttnThreads>*)(lds + kSelOff);
   int32_t* idx_list = (int32_t*)(lds + kSelListOff);
   int32_t* rows_list = (int32_t*)(lds + kSelRowsOff);
   int32_t* pt_lds = (int32_t*)(lds + kSelPtOff);
   const int k = t.k;
-  int r;
-  const int64_t seen = decode_seen(t.ctx_len, t.max_ctx, 1, q, r);
-  const int64_t nv = topk_row_count(t, q);
-  const int32_t* pt = t.page_table + (int64_t)r * t.max_pages;
+  const int32_t word = row_extent_word(t, q);
+  const int32_t* pt = t.page_table + (int64_t)(q / t.q_per_req) * t.max_pages;
+  const int n_pt = t.max_pages < kSelRowMax / kPage ? t.max_pages : kSelRowMax / kPage;
+  const int32_t pg_mine = tid < n_pt ? pt[tid] : -1;
+  const float* row = t.logits + (int64_t)q * t.ld;
+  const int c0 = tid * kSelPer;
+  float v[kSelPer];
+#pragma unroll
+  for (int j = 0; j < kSelPer; j += 4) {
+    const int c = c0 + j;
+    const float4 x = *(const float4*)(row + (c < t.max_n_vis ? c : 0));   // ld >= max_n_vis, ld % 4 == 0
+    v[j] = x.x; v[j + 1] = x.y; v[j + 2] = x.z; v[j + 3] = x.w;
+  }
+  int64_t seen;
+  const int64_t nv = row_extent(t, q, word, seen);
   auto row_of = [&](int c, int pg) { return (unsigned)pg < (unsigned)t.num_pages ? pg * kPage + (c & (kPage - 1)) : -1; };
   if (tid < kWin) {
     const int64_t p = seen - kWin + tid;
-    idx_list[tid] = p >= 0 ? (int32_t)(p % t.ring) : -1;
+    idx_list[tid] = p >= 0 ? ring_slot(p, t.ring) : -1;
   }
+  if (tid < n_pt) pt_lds[tid] = pg_mine;
+  uint32_t key[kSelPer];
+  uint32_t vm = 0;
+  if (nv > k) {
+    for (int i = tid; i < kHistBins; i += kAttnThreads) sh.bins[i] = 0u;
+    if (tid == 0) sh.s_ncand = 0u;
+#pragma unroll
+    for (int j = 0; j < kSelPer; ++j) key[j] = order_key(v[j]);
+    vm = prefix_mask<kSelPer>(c0, nv);
+  }
+  __syncthreads();
+  issue_more();
   if (nv <= k) {
     for (int i = tid; i < k; i += kAttnThreads) {
       idx_list[kWin + i] = i < nv ? i : -1;
-      rows_list[i] = i < nv ? row_of(i, pt[i >> 6]) : -1;
+      rows_list[i] = i < nv ? row_of(i, pt_lds[i >> 6]) : -1;
     }
   } else {
-    for (int p = tid; p < (int)((nv + kPage - 1) / kPage); p += kAttnThreads) pt_lds[p] = pt[p];
-    const float* row = t.logits + (int64_t)q * t.ld;
-    const int c0 = tid * kSelPer;
-    uint32_t key[kSelPer];
-    uint32_t vm = 0;
-    {
-      float v[kSelPer];
-#pragma unroll
-      for (int j = 0; j < kSelPer; j += 4) {
-        const int c = c0 + j;
-        const float4 x = *(const float4*)(row + (c < nv ? c : 0));
-        v[j] = x.x; v[j + 1] = x.y; v[j + 2] = x.z; v[j + 3] = x.w;
-      }
-      for (int i = tid; i < kHistBins; i += kAttnThreads) sh.bins[i] = 0u;
-      if (tid == 0) sh.s_ncand = 0u;
-#pragma unroll
-      for (int j = 0; j < kSelPer; ++j) {
-        key[j] = order_key(v[j]);
-        vm |= (c0 + j < nv ? 1u : 0u) << j;
-      }
-    }
-    __syncthreads();
     block_threshold<kAttnThreads, kSelPer>(key, vm, (uint32_t)k, sh);
     block_emit<kAttnThreads, kSelPer>(key, vm, sh.s_T, sh.s_need, (uint32_t)k, [&](int j) { return c0 + j; }, sh);
     const int32_t* sel = (const int32_t*)sh.cand_sel;
@@ -370,60 +378,69 @@ __device__ __forceinline__ void select_rows(const TopkArgs& t, int q, uint8_t* l
 // selects them (PER sketch entries per thread): the sketches' exact k-th largest key T decides the
 // row when every wave's bound lies below T; otherwise the block rescores the row if it has no
 // stored scores and selects from the full row (select_streamed), writing straight into the lists.
-template <int PER>
-__device__ __forceinline__ void select_rows_sketch(const TopkArgs& t, int q, uint8_t* lds, bool write_out) {
+// The sketch entries and wave bounds are loaded with the context length, up to the widest row (in
+// bounds, masked once the row's length is known), before the first wait; issue_more() comes after
+// the first barrier (after the selection's own waits).
+template <int PER, class IssueMore>
+__device__ __forceinline__ void select_rows_sketch(const TopkArgs& t, int q, uint8_t* lds, bool write_out,
+                                                   IssueMore issue_more) {
   constexpr int NT = kAttnThreads;
   const int tid = threadIdx.x;
   SelShared<NT>& sh = *(SelShared<NT>*)(lds + kSelOff);
   int32_t* idx_list = (int32_t*)(lds + kSelListOff);
   int32_t* rows_list = (int32_t*)(lds + kSelRowsOff);
   const int k = t.k;
-  int r;
-  const int64_t seen = decode_seen(t.ctx_len, t.max_ctx, 1, q, r);
-  const int64_t nv = topk_row_count(t, q);
-  const int32_t* pt = t.page_table + (int64_t)r * t.max_pages;
+  const int32_t word = row_extent_word(t, q);
+  const uint2* top = t.sk_top + (int64_t)q * t.sk_waves * kSketchTop;
+  const uint32_t* bound = t.sk_bound + (int64_t)q * t.sk_waves;
+  const int64_t n_u_max = (int64_t)t.sk_waves * kSketchTop;
+  uint32_t key[PER], idx[PER];
+  const int64_t u0 = (int64_t)tid * PER;
+#pragma unroll
+  for (int j = 0; j < PER; j += 2) {
+    const int64_t u = u0 + j;
+    const uint4 x = *(const uint4*)&top[u < n_u_max ? u : 0];
+    key[j] = x.x; idx[j] = x.y; key[j + 1] = x.z; idx[j + 1] = x.w;
+  }
+  constexpr int kBnd = (kSketchMaxWaves + NT - 1) / NT;
+  uint32_t bnd[kBnd];
+#pragma unroll
+  for (int i = 0; i < kBnd; ++i) {
+    const int64_t W = tid + (int64_t)i * NT;
+    bnd[i] = W < t.sk_waves ? bound[W] : 0u;
+  }
+  int64_t seen;
+  const int64_t nv = row_extent(t, q, word, seen);
+  const int32_t* pt = t.page_table + (int64_t)(q / t.q_per_req) * t.max_pages;
   auto row_of = [&](int c) {
     const int pg = pt[c >> 6];
     return (unsigned)pg < (unsigned)t.num_pages ? pg * kPage + (c & (kPage - 1)) : -1;
   };
   if (tid < kWin) {
     const int64_t p = seen - kWin + tid;
-    idx_list[tid] = p >= 0 ? (int32_t)(p % t.ring) : -1;
+    idx_list[tid] = p >= 0 ? ring_slot(p, t.ring) : -1;
   }
-  if (nv <= k) {
+  const int64_t n_w = (nv + kSketchSpan - 1) / kSketchSpan;
+  const int64_t n_u = n_w * kSketchTop;
+  uint32_t vm = 0u;
+  if (nv > k) {
+#pragma unroll
+    for (int i = 0; i < kBnd; ++i) bnd[i] = tid + (int64_t)i * NT < n_w ? bnd[i] : 0u;
+    for (int i = tid; i < kHistBins; i += NT) sh.bins[i] = 0u;
+    if (tid == 0) sh.s_ncand = 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) vm |= (u0 + j < n_u && idx[j] != 0xFFFFFFFFu ? 1u : 0u) << j;
+    const uint32_t wsum = wave_inclusive_scan(__popc(vm));
+    if ((tid & 63) == 63) sh.scan[tid >> 6] = wsum;
+  }
+  __syncthreads();
+  issue_more();
+  if (nv <= k) {   // block-uniform
     for (int i = tid; i < k; i += NT) {
       idx_list[kWin + i] = i < nv ? i : -1;
       rows_list[i] = i < nv ? row_of(i) : -1;
     }
   } else {
-    const int64_t n_w = (nv + kSketchSpan - 1) / kSketchSpan;
-    const int64_t n_u = n_w * kSketchTop;
-    const uint2* top = t.sk_top + (int64_t)q * t.sk_waves * kSketchTop;
-    const uint32_t* bound = t.sk_bound + (int64_t)q * t.sk_waves;
-    uint32_t key[PER], idx[PER], vm = 0u;
-    const int64_t u0 = (int64_t)tid * PER;
-#pragma unroll
-    for (int j = 0; j < PER; j += 2) {
-      const int64_t u = u0 + j;
-      const uint4 x = *(const uint4*)&top[u < n_u ? u : 0];
-      key[j] = x.x; idx[j] = x.y; key[j + 1] = x.z; idx[j + 1] = x.w;
-    }
-    constexpr int kBnd = (kSketchMaxWaves + NT - 1) / NT;
-    uint32_t bnd[kBnd];
-#pragma unroll
-    for (int i = 0; i < kBnd; ++i) {
-      const int64_t W = tid + (int64_t)i * NT;
-      bnd[i] = W < n_w ? bound[W] : 0u;
-    }
-    for (int i = tid; i < kHistBins; i += NT) sh.bins[i] = 0u;
-    if (tid == 0) sh.s_ncand = 0u;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) vm |= (u0 + j < n_u && idx[j] != 0xFFFFFFFFu ? 1u : 0u) << j;
-    {
-      const uint32_t wsum = wave_inclusive_scan(__popc(vm));
-      if ((tid & 63) == 63) sh.scan[tid >> 6] = wsum;
-    }
-    __syncthreads();
     uint32_t n_real = 0u;
 #pragma unroll
     for (int w = 0; w < NT / 64; ++w) n_real += sh.scan[w];
@@ -529,10 +546,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a, 
     }
   };
   if constexpr (SEL) {
-    // q does not depend on the selection: its loads overlap it
-    if (wave < 4) load_q();
+    // q does not depend on the selection: its loads, issued behind the selection's, overlap it
     uint8_t* lds = (uint8_t*)&Kr[0][0];
-    select_rows(t, q, lds, split == 0 && blockIdx.y == 0);
+    select_rows(t, q, lds, split == 0 && blockIdx.y == 0, [&] {
+      if (wave < 4) load_q();
+    });
     idx_list = (const int32_t*)(lds + kSelListOff);
     rows_list = (const int32_t*)(lds + kSelRowsOff);
   }
@@ -857,7 +875,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs
     // q does not depend on it, so its loads overlap it
     if (wave < 4) load_q();
     uint8_t* lds = (uint8_t*)&Kr[0][0];
-    select_rows_sketch<kSelSketchPer>(t, q, lds, split == 0 && blockIdx.y == 0);
+    select_rows_sketch<kSelSketchPer>(t, q, lds, split == 0 && blockIdx.y == 0, [] {});
     idx_list = (const int32_t*)(lds + kSelListOff);
     rows_list = (const int32_t*)(lds + kSelRowsOff);
   }

@@ -165,12 +165,22 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
 // Decode with S queries per request: query q is token j = q % S of request r = q / S, one of the
 // last S tokens of that request's T = ctx_len[r] (clamped to [0, max_ctx]); it sits at position
 // T - S + j and sees the T - (S - 1 - j) tokens up to it (0 if that is negative).
+// Ring slot of decode position p >= 0 (32-bit division when p fits, as it does for any context a
+// ring serves; a 64-bit division is some 50 instructions).
+__device__ __forceinline__ int32_t ring_slot(int64_t p, int ring) {
+  return p <= 0x7FFFFFFF ? (int32_t)((uint32_t)p % (uint32_t)ring) : (int32_t)(p % ring);
+}
+
+// decode_seen_of takes T = ctx_len[q / S] already loaded.
+__device__ __forceinline__ int64_t decode_seen_of(int64_t T, int64_t max_ctx, int S, int q) {
+  T = T < 0 ? 0 : (T > max_ctx ? max_ctx : T);
+  T -= S - 1 - (q - (q / S) * S);
+  return T < 0 ? 0 : T;
+}
+
 __device__ __forceinline__ int64_t decode_seen(const int32_t* ctx_len, int64_t max_ctx, int S, int q, int& r) {
   r = q / S;
-  int64_t T = ctx_len[r];
-  T = T < 0 ? 0 : (T > max_ctx ? max_ctx : T);
-  T -= S - 1 - (q - r * S);
-  return T < 0 ? 0 : T;
+  return decode_seen_of(ctx_len[r], max_ctx, S, q);
 }
 
 template <int I, int N>

@@ -15,31 +15,44 @@ __device__ __forceinline__ int64_t clamp_nv(const TopkArgs& a, int q) {
   return nv < 0 ? 0 : (nv > a.max_n_vis ? a.max_n_vis : nv);
 }
 
-// Visible count of row q: from the n_vis array, or derived (decode: ctx_len/4, prefill: (t+1)/4).
-__device__ __forceinline__ int64_t topk_row_count(const TopkArgs& a, int q) {
+// The one word of memory row q's extent depends on: its request's context length (decode), its
+// n_vis entry, or none (causal prefill).  The selection prologues issue it with their other loads
+// and resolve the extent after one wait, instead of a chain of dependent loads.
+__device__ __forceinline__ int32_t row_extent_word(const TopkArgs& a, int q) {
+  return a.win_mode == 1 ? a.ctx_len[q / a.q_per_req] : (a.win_mode == 2 ? 0 : a.n_vis[q]);
+}
+
+// Visible count of row q from that word (decode: tokens seen / 4, prefill: (t+1)/4, else n_vis),
+// clamped to [0, max_n_vis]; `seen` gets the decode query's tokens seen (0 otherwise).
+__device__ __forceinline__ int64_t row_extent(const TopkArgs& a, int q, int32_t word, int64_t& seen) {
   int64_t nv;
+  seen = 0;
   if (a.win_mode == 1) {
-    int r;
-    nv = decode_seen(a.ctx_len, a.max_ctx, a.q_per_req, q, r) / 4;
+    seen = decode_seen_of(word, a.max_ctx, a.q_per_req, q);
+    nv = seen / 4;
   } else if (a.win_mode == 2) {
     nv = (a.pos0 + q + 1) / 4;
   } else {
-    nv = a.n_vis[q];
+    nv = word;
   }
   return nv < 0 ? 0 : (nv > a.max_n_vis ? a.max_n_vis : nv);
 }
 
+__device__ __forceinline__ int64_t topk_row_count(const TopkArgs& a, int q) {
+  int64_t seen;
+  return row_extent(a, q, row_extent_word(a, q), seen);
+}
+
 // Window part of the index list: decode ring slots (position % ring) of the 128 positions up to
-// the query's, or prefill positions t-127..t; -1 before position 0.  Written to columns [-128, 0)
-// relative to a.idx.
-__device__ __forceinline__ void write_window(const TopkArgs& a, int q) {
+// the query's (`seen` from row_extent), or prefill positions t-127..t; -1 before position 0.
+// Written to columns [-128, 0) relative to a.idx.
+__device__ __forceinline__ void write_window(const TopkArgs& a, int q, int64_t seen) {
   const int j = threadIdx.x;
   if (j >= kWin) return;
   int32_t v;
   if (a.win_mode == 1) {
-    int r;
-    const int64_t p = decode_seen(a.ctx_len, a.max_ctx, a.q_per_req, q, r) - kWin + j;
-    v = p >= 0 ? (int32_t)(p % a.ring) : -1;
+    const int64_t p = seen - kWin + j;
+    v = p >= 0 ? ring_slot(p, a.ring) : -1;
   } else {
     const int64_t p = a.pos0 + q - (kWin - 1) + j;
     v = p >= 0 ? (int32_t)p : -1;
@@ -121,17 +134,40 @@ struct SelShared {
 // of vm set for a real entry) and how many entries equal to T are taken: sh.s_T, sh.s_need on
 // return (after a barrier).  The block holds at least k real entries.  On entry sh.bins is zeroed,
 // sh.s_ncand is 0 and a barrier has passed since.
+// All PER entries of a thread real: the per-entry validity tests drop out (every thread but the
+// last of a row takes these paths, so the VALU work per entry, which bounds each phase, shrinks).
+template <int PER>
+__device__ __forceinline__ bool all_real(uint32_t vm) {
+  return vm == (PER >= 32 ? 0xFFFFFFFFu : ((1u << PER) - 1u));
+}
+
+// vm of a thread whose entries [c0, c0 + PER) are real below n: a prefix of them
+template <int PER>
+__device__ __forceinline__ uint32_t prefix_mask(int64_t c0, int64_t n) {
+  const int64_t m = n - c0;
+  return m >= PER ? (PER >= 32 ? 0xFFFFFFFFu : ((1u << PER) - 1u)) : (m <= 0 ? 0u : ((1u << (uint32_t)m) - 1u));
+}
+
 template <int NT, int PER>
 __device__ void block_threshold(const uint32_t* key, uint32_t vm, uint32_t k, SelShared<NT>& sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool full = all_real<PER>(vm);
   // extremes of the real keys: per wave, then across waves after the barrier
   {
     uint32_t kmx = 0u, kmn = 0xFFFFFFFFu;
+    if (full) {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if ((vm >> j) & 1u) {
+      for (int j = 0; j < PER; ++j) {
         kmx = key[j] > kmx ? key[j] : kmx;
         kmn = key[j] < kmn ? key[j] : kmn;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if ((vm >> j) & 1u) {
+          kmx = key[j] > kmx ? key[j] : kmx;
+          kmn = key[j] < kmn ? key[j] : kmn;
+        }
       }
     }
     kmx = wave_umax(kmx);
@@ -145,9 +181,9 @@ __device__ void block_threshold(const uint32_t* key, uint32_t vm, uint32_t k, Se
   // Level 1 on the value range: 4096 equal-width bins between the smallest and largest finite
   // score.  Scores crowd a few of the fixed 12-bit key-prefix bins (the exponent and three
   // mantissa bits), so LDS atomics collide and the threshold bin holds hundreds of entries; on the
-  // value range the bins hold a handful.  The bin index is a monotone function of the score
-  // (subtraction, multiplication by a positive scale and truncation all preserve order), so b*
-  // and the counts above it are exact.  When b* holds at most 64 entries one wave ranks them by
+  // value range the bins hold a handful.  The bin index is a monotone function of the score (one
+  // fused multiply-add with a positive scale, a clamp and truncation all preserve order) applied
+  // to every entry alike, so b* and the counts above it are exact.  When b* holds at most 64 entries one wave ranks them by
   // their full keys; otherwise (ties, clusters, non-finite scores) the key-prefix levels run.
   bool resolved = false;
   {
@@ -164,13 +200,22 @@ __device__ void block_threshold(const uint32_t* key, uint32_t vm, uint32_t k, Se
                           kmax > kmin && scale > 0.f && scale < 3.0e38f;
     if (adaptive) {
       uint32_t bin[PER];
+      const float off = -vmin * scale;
 #pragma unroll
       for (int j = 0; j < PER; ++j) {
-        const float x = (key_value(key[j]) - vmin) * scale;
-        // x >= 0 for real entries; the others (never counted) are clamped too
-        const uint32_t b = x < 4095.f ? (x > 0.f ? (uint32_t)x : 0u) : 4095u;
+        // about 0 at vmin and 4096 at vmax (finite for real entries; the others, never counted,
+        // are clamped too)
+        const float x = fmaf(key_value(key[j]), scale, off);
+        const uint32_t b = (uint32_t)fminf(fmaxf(x, 0.f), 4095.f);
         bin[j] = b;
-        if ((vm >> j) & 1u) atomicAdd(&sh.bins[b], 1u);
+      }
+      if (full) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) atomicAdd(&sh.bins[bin[j]], 1u);
+      } else {
+#pragma unroll
+        for (int j = 0; j < PER; ++j)
+          if ((vm >> j) & 1u) atomicAdd(&sh.bins[bin[j]], 1u);
       }
       __syncthreads();
       if (wave == 0) wave_find_desc(sh.bins, kHistBins, k, &sh.s_digit, &sh.s_before);
@@ -180,7 +225,8 @@ __device__ void block_threshold(const uint32_t* key, uint32_t vm, uint32_t k, Se
       {
         uint32_t hm = 0;
 #pragma unroll
-        for (int j = 0; j < PER; ++j) hm |= (((vm >> j) & 1u) && bin[j] == bstar) ? (1u << j) : 0u;
+        for (int j = 0; j < PER; ++j) hm |= bin[j] == bstar ? (1u << j) : 0u;
+        hm &= vm;
         const uint32_t hits = __popc(hm);
         const uint32_t incl = wave_inclusive_scan(hits);
         uint32_t base = 0;
@@ -331,10 +377,11 @@ __device__ void block_emit(const uint32_t* key, uint32_t vm, uint32_t T, uint32_
   uint32_t gm = 0, em = 0;       // bit j: entry j is above T / equal to T
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const bool ok = (vm >> j) & 1u;
-    gm |= (ok && key[j] > T) ? (1u << j) : 0u;
-    em |= (ok && key[j] == T) ? (1u << j) : 0u;
+    gm |= key[j] > T ? (1u << j) : 0u;
+    em |= key[j] == T ? (1u << j) : 0u;
   }
+  gm &= vm;
+  em &= vm;
   const uint32_t n_gt = __popc(gm), n_eq = __popc(em);
   const uint32_t mine = (n_gt << 16) | n_eq;
   const uint32_t incl = wave_inclusive_scan(mine);

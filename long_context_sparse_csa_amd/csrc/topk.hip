@@ -422,32 +422,28 @@ template <int NT, int PER>
 __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
   constexpr int kRowMax = NT * PER;
   const int q = blockIdx.x, tid = threadIdx.x;
-  const int64_t nv = topk_row_count(a, q);
   const int k = a.k;
   int32_t* out = a.idx + (int64_t)q * a.ld_idx;
-  if (a.win_mode) write_window(a, q);
+  // the row's extent word and the request's page ids are loaded together (one wait), then the
+  // scores up to the row's length: two memory round trips before the first barrier, not three
+  const int32_t word = row_extent_word(a, q);
   const int r = a.win_mode == 1 ? q / a.q_per_req : 0;   // request of this query (prefill: 0)
   const int32_t* pt = a.rows ? a.page_table + (int64_t)r * a.max_pages : nullptr;
+  static_assert(kRowMax / kPage <= NT, "one page id per thread");
+  const int n_pt = a.rows ? (a.max_pages < kRowMax / kPage ? a.max_pages : kRowMax / kPage) : 0;
+  const int32_t pg_mine = tid < n_pt ? pt[tid] : -1;
+  int64_t seen;
+  const int64_t nv = row_extent(a, q, word, seen);
+  if (a.win_mode) write_window(a, q, seen);
   auto row_of = [&](int c, int pg) { return (unsigned)pg < (unsigned)a.num_pages ? pg * kPage + (c & (kPage - 1)) : -1; };
-  if (nv <= k) {
-    for (int i = tid; i < k; i += NT) {
-      out[i] = i < nv ? i : -1;
-      if (a.rows) a.rows[(int64_t)q * a.ld_rows + i] = i < nv ? row_of(i, pt[i >> 6]) : -1;
-    }
-    return;
-  }
   __shared__ int32_t pt_lds[kRowMax / kPage];
-  if (a.rows) {
-    // the request's page ids, loaded alongside the scores (rows >= 1: nv > k >= 1)
-    for (int p = tid; p < (int)((nv + kPage - 1) / kPage); p += NT) pt_lds[p] = pt[p];
-  }
   __shared__ SelShared<NT> sh;
 
   const float* row = a.logits + (int64_t)q * a.ld;
   const int c0 = tid * PER;          // this thread owns entries [c0, c0+PER)
   uint32_t key[PER];
   uint32_t vm = 0;
-  {
+  if (nv > k) {
     float v[PER];
 #pragma unroll
     for (int j = 0; j < PER; j += 4) {
@@ -456,16 +452,26 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
       const float4 x = *(const float4*)(row + (c < nv ? c : 0));
       v[j] = x.x; v[j + 1] = x.y; v[j + 2] = x.z; v[j + 3] = x.w;
     }
+    // after the score loads in program order: the store waits for its page id, and the compiler
+    // keeps LDS stores and the scores' loads in order
+    if (tid < n_pt) pt_lds[tid] = pg_mine;
     // cleared while the loads are in flight
     for (int i = tid; i < kHistBins; i += NT) sh.bins[i] = 0u;
     if (tid == 0) sh.s_ncand = 0u;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      key[j] = order_key(v[j]);
-      vm |= (c0 + j < nv ? 1u : 0u) << j;
-    }
+    for (int j = 0; j < PER; ++j) key[j] = order_key(v[j]);
+    vm = prefix_mask<PER>(c0, nv);
+  } else if (tid < n_pt) {
+    pt_lds[tid] = pg_mine;
   }
   __syncthreads();
+  if (nv <= k) {   // block-uniform
+    for (int i = tid; i < k; i += NT) {
+      out[i] = i < nv ? i : -1;
+      if (a.rows) a.rows[(int64_t)q * a.ld_rows + i] = i < nv ? row_of(i, pt_lds[i >> 6]) : -1;
+    }
+    return;
+  }
   block_threshold<NT, PER>(key, vm, (uint32_t)k, sh);
   block_emit<NT, PER>(key, vm, sh.s_T, sh.s_need, (uint32_t)k, [&](int j) { return c0 + j; }, sh);
   const int32_t* sel = (const int32_t*)sh.cand_sel;
@@ -492,11 +498,33 @@ template <int PER>
 __global__ __launch_bounds__(1024) void topk_sketch_kernel(TopkArgs a) {
   constexpr int NT = 1024;
   const int q = blockIdx.x, tid = threadIdx.x;
-  const int64_t nv = topk_row_count(a, q);
   const int k = a.k;
   int32_t* out = a.idx + (int64_t)q * a.ld_idx;
   int32_t* rows_out = a.rows ? a.rows + (int64_t)q * a.ld_rows : nullptr;
-  if (a.win_mode) write_window(a, q);
+  // the row's extent word, its sketch entries and its wave bounds (over the whole sketch row: in
+  // bounds, masked once the row's length is known) are loaded together, before the first wait
+  const int32_t word = row_extent_word(a, q);
+  const uint2* top = a.sk_top + (int64_t)q * a.sk_waves * kSketchTop;
+  const uint32_t* bound = a.sk_bound + (int64_t)q * a.sk_waves;
+  const int64_t n_u_max = a.sk_waves * kSketchTop;
+  uint32_t key[PER];
+  uint32_t idx[PER];
+  const int64_t u0 = (int64_t)tid * PER;            // this thread's sketch entries [u0, u0 + PER)
+#pragma unroll
+  for (int j = 0; j < PER; j += 2) {
+    const int64_t u = u0 + j;
+    const uint4 x = *(const uint4*)&top[u < n_u_max ? u : 0];   // two entries; rows hold multiples of 8
+    key[j] = x.x; idx[j] = x.y; key[j + 1] = x.z; idx[j + 1] = x.w;
+  }
+  uint32_t bnd[(kSketchMaxWaves + NT - 1) / NT];
+#pragma unroll
+  for (int i = 0; i < (kSketchMaxWaves + NT - 1) / NT; ++i) {
+    const int64_t W = tid + (int64_t)i * NT;
+    bnd[i] = W < a.sk_waves ? bound[W] : 0u;
+  }
+  int64_t seen;
+  const int64_t nv = row_extent(a, q, word, seen);
+  if (a.win_mode) write_window(a, q, seen);
   const int r = q / a.q_per_req;
   const int32_t* pt = a.page_table + (int64_t)r * a.max_pages;
   auto row_of = [&](int c) {
@@ -513,24 +541,9 @@ __global__ __launch_bounds__(1024) void topk_sketch_kernel(TopkArgs a) {
   __shared__ SelShared<NT> sh;
   const int64_t n_w = (nv + kSketchSpan - 1) / kSketchSpan;
   const int64_t n_u = n_w * kSketchTop;               // sketch entries of the row (<= NT * PER)
-  const uint2* top = a.sk_top + (int64_t)q * a.sk_waves * kSketchTop;
-  const uint32_t* bound = a.sk_bound + (int64_t)q * a.sk_waves;
-  uint32_t key[PER];
-  uint32_t idx[PER];
   uint32_t vm = 0u;
-  const int64_t u0 = (int64_t)tid * PER;            // this thread's sketch entries [u0, u0 + PER)
 #pragma unroll
-  for (int j = 0; j < PER; j += 2) {
-    const int64_t u = u0 + j;
-    const uint4 x = *(const uint4*)&top[u < n_u ? u : 0];   // two entries; n_u is a multiple of 8
-    key[j] = x.x; idx[j] = x.y; key[j + 1] = x.z; idx[j + 1] = x.w;
-  }
-  uint32_t bnd[(kSketchMaxWaves + NT - 1) / NT];
-#pragma unroll
-  for (int i = 0; i < (kSketchMaxWaves + NT - 1) / NT; ++i) {
-    const int64_t W = tid + (int64_t)i * NT;
-    bnd[i] = W < n_w ? bound[W] : 0u;
-  }
+  for (int i = 0; i < (kSketchMaxWaves + NT - 1) / NT; ++i) bnd[i] = tid + (int64_t)i * NT < n_w ? bnd[i] : 0u;
   for (int i = tid; i < kHistBins; i += NT) sh.bins[i] = 0u;
   if (tid == 0) sh.s_ncand = 0u;
 #pragma unroll
@@ -661,7 +674,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs a) {
     if (a.mode == 1) {   // decode: ring slot of the j-th of the 128 positions up to the row's
       int r;
       const int64_t p = decode_seen(a.ctx_len, a.max_ctx, a.q_per_req, rrow, r) - kWin + j;
-      v = p >= 0 ? (int32_t)(p % a.ring) : -1;
+      v = p >= 0 ? ring_slot(p, a.ring) : -1;
     } else {             // causal prefill: raw position t-127+j
       const int64_t t = a.pos0 + rrow;
       const int64_t p = t - (kWin - 1) + j;
