@@ -302,6 +302,15 @@ constexpr int kSelSketchPer = 8;                                      // sketch 
 static_assert(kSelPtOff + 4 * (kSelRowMax / kPage) <= 3 * kTile * kKrStride * 2, "selection LDS fits the 16-head ring");
 static_assert(kSelPtOff + 4 * (kSelRowMax / kPage) <= 4 * kTile * kKrStride * 2, "selection LDS fits the ring");
 
+// Visible entries and tokens seen of a decode query that is its request's only query, from the
+// request's context length: row_extent for win_mode 1 with q_per_req 1, without its branches and
+// divisions (the prologue's scalar instructions are issued by every wave of the block).
+__device__ __forceinline__ int64_t decode1_extent(const TopkArgs& t, int32_t ctx, int64_t& seen) {
+  seen = ctx < 0 ? 0 : (ctx > t.max_ctx ? t.max_ctx : (int64_t)ctx);
+  const int64_t nv = seen / 4;
+  return nv > t.max_n_vis ? t.max_n_vis : nv;
+}
+
 // Selects query q's rows into LDS: idx_list[0 .. n_win + k) (the ring window, then the k entries in
 // ascending order, -1 past the visible ones) and rows_list[0 .. k) (their pool rows, -1 if none).
 // Every load of the prologue (the context length, the first page ids, the scores up to the widest
@@ -318,8 +327,8 @@ __device__ __forceinline__ void select_rows(const TopkArgs& t, int q, uint8_t* l
   int32_t* rows_list = (int32_t*)(lds + kSelRowsOff);
   int32_t* pt_lds = (int32_t*)(lds + kSelPtOff);
   const int k = t.k;
-  const int32_t word = row_extent_word(t, q);
-  const int32_t* pt = t.page_table + (int64_t)(q / t.q_per_req) * t.max_pages;
+  const int32_t ctx = t.ctx_len[q];   // decode, one query per request (attn_select_fused)
+  const int32_t* pt = t.page_table + (int64_t)q * t.max_pages;
   const int n_pt = t.max_pages < kSelRowMax / kPage ? t.max_pages : kSelRowMax / kPage;
   const int32_t pg_mine = tid < n_pt ? pt[tid] : -1;
   const float* row = t.logits + (int64_t)q * t.ld;
@@ -332,7 +341,7 @@ __device__ __forceinline__ void select_rows(const TopkArgs& t, int q, uint8_t* l
     v[j] = x.x; v[j + 1] = x.y; v[j + 2] = x.z; v[j + 3] = x.w;
   }
   int64_t seen;
-  const int64_t nv = row_extent(t, q, word, seen);
+  const int64_t nv = decode1_extent(t, ctx, seen);
   auto row_of = [&](int c, int pg) { return (unsigned)pg < (unsigned)t.num_pages ? pg * kPage + (c & (kPage - 1)) : -1; };
   if (tid < kWin) {
     const int64_t p = seen - kWin + tid;
@@ -390,7 +399,7 @@ __device__ __forceinline__ void select_rows_sketch(const TopkArgs& t, int q, uin
   int32_t* idx_list = (int32_t*)(lds + kSelListOff);
   int32_t* rows_list = (int32_t*)(lds + kSelRowsOff);
   const int k = t.k;
-  const int32_t word = row_extent_word(t, q);
+  const int32_t ctx = t.ctx_len[q];   // decode, one query per request (attn_select_fused)
   const uint2* top = t.sk_top + (int64_t)q * t.sk_waves * kSketchTop;
   const uint32_t* bound = t.sk_bound + (int64_t)q * t.sk_waves;
   const int64_t n_u_max = (int64_t)t.sk_waves * kSketchTop;
@@ -410,8 +419,8 @@ __device__ __forceinline__ void select_rows_sketch(const TopkArgs& t, int q, uin
     bnd[i] = W < t.sk_waves ? bound[W] : 0u;
   }
   int64_t seen;
-  const int64_t nv = row_extent(t, q, word, seen);
-  const int32_t* pt = t.page_table + (int64_t)(q / t.q_per_req) * t.max_pages;
+  const int64_t nv = decode1_extent(t, ctx, seen);
+  const int32_t* pt = t.page_table + (int64_t)q * t.max_pages;
   auto row_of = [&](int c) {
     const int pg = pt[c >> 6];
     return (unsigned)pg < (unsigned)t.num_pages ? pg * kPage + (c & (kPage - 1)) : -1;
@@ -503,9 +512,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  // queries vary fastest in the block index, so with Q a multiple of 8 every split of a query (and
-  // the combine blocks that read its partials) runs on the same XCD and shares its L2
-  const int q = blockIdx.x % a.Q, split = blockIdx.x / a.Q;
+  // grid (query, head block, split): queries vary fastest in the dispatch order, so with Q a
+  // multiple of 8 every split of a query (and the combine blocks that read its partials) runs on the
+  // same XCD and shares its L2
+  const int q = blockIdx.x, split = blockIdx.z;
   const int Hpad = (a.H + 15) & ~15;
   const int h_base = blockIdx.y * 64;
 
@@ -521,10 +531,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_kernel(AttnArgs a, 
 
   const int n_idx = a.n_win + a.n_comp;
   const int n_tiles = (n_idx + kTile - 1) / kTile;
-  const int tps = (n_tiles + a.n_split - 1) / a.n_split;
+  const int tps = a.tiles_per_split;
   const int t_begin = split * tps;
   const int nt = attn_block_tiles(a, q, n_tiles, t_begin, tps);   // tiles of this block
-  const int r = a.req_mode == 1 ? q / a.q_per_req : (a.req_mode == 2 ? 0 : a.q_req[q]);
+  // the fused selection runs only for decode with one query per request (attn_select_fused)
+  const int r = SEL ? q : (a.req_mode == 1 ? q / a.q_per_req : (a.req_mode == 2 ? 0 : a.q_req[q]));
   const int s_begin = t_begin * kTile;
   const int32_t* idx_list = nullptr;
   const int32_t* rows_list = nullptr;
@@ -839,7 +850,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, g = lane >> 4;
-  const int q = blockIdx.x % a.Q, split = blockIdx.x / a.Q;
+  const int q = blockIdx.x, split = blockIdx.z;   // grid (query, head block, split)
   const int Hpad = (a.H + 15) & ~15;
   const int h_base = blockIdx.y * 16;
   const int h = h_base + n;   // this lane's head
@@ -852,10 +863,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_bf16_h16_kernel(AttnArgs
 
   const int n_idx = a.n_win + a.n_comp;
   const int n_tiles = (n_idx + kTile - 1) / kTile;
-  const int tps = (n_tiles + a.n_split - 1) / a.n_split;
+  const int tps = a.tiles_per_split;
   const int t_begin = split * tps;
   const int nt = attn_block_tiles(a, q, n_tiles, t_begin, tps);
-  const int r = a.req_mode == 1 ? q / a.q_per_req : (a.req_mode == 2 ? 0 : a.q_req[q]);
+  // the fused selection runs only for decode with one query per request (attn_select_fused)
+  const int r = SEL ? q : (a.req_mode == 1 ? q / a.q_per_req : (a.req_mode == 2 ? 0 : a.q_req[q]));
 
   const int kb = wave & 1, dh = wave >> 1;   // consumer roles (waves 0-3)
   // q as the QK B operand: lane (n, g) holds dims 256 dh + 32ks + 8g .. +7 of head h (padded heads
@@ -1203,7 +1215,10 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   const int cf = a.n_comp > 0 ? a.comp_fmt : wf;
   {
     ProfScope p(fuse ? "attn_select" : "attn_bf16", s);
-    const dim3 grid((unsigned)(a.Q * a.n_split), (unsigned)hchunks);
+    const dim3 grid((unsigned)a.Q, (unsigned)hchunks, (unsigned)a.n_split);
+    AttnArgs ak = a;
+    const int n_tiles = (a.n_win + a.n_comp + kTile - 1) / kTile;
+    ak.tiles_per_split = (n_tiles + a.n_split - 1) / a.n_split;
     const TopkArgs t = fuse ? *a.sel : TopkArgs{};
     // rows are streamed (non-temporal) only when one block gathers each of them: with several head
     // blocks per query, the later blocks' gathers of a row hit the copy the first one left in L2
@@ -1214,7 +1229,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
   else if (cf == kRowFP8) CSA_LAUNCH(p, (K<kRowBF16, kRowFP8, __VA_ARGS__>), grid, dim3(kAttnThreads), s, ARGS);           \
   else CSA_LAUNCH(p, (K<kRowBF16, kRowBF16, __VA_ARGS__>), grid, dim3(kAttnThreads), s, ARGS);
     if (hb == 16) {
-#define ARGS a, t
+#define ARGS ak, t
       if (fuse) {
         if (stream) { CSA_ATTN_FMT(attn_bf16_h16_kernel, true, true) } else { CSA_ATTN_FMT(attn_bf16_h16_kernel, false, true) }
       } else {
@@ -1222,7 +1237,7 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t s) {
       }
 #undef ARGS
     } else {
-#define ARGS a, t
+#define ARGS ak, t
       if (fuse) {
         if (stream) { CSA_ATTN_FMT(attn_bf16_kernel, true, true) } else { CSA_ATTN_FMT(attn_bf16_kernel, false, true) }
       } else {

@@ -169,6 +169,7 @@ struct AttnArgs {
   int out_dt;                // 0 f32, 1 bf16
   float* part;               // split-K partials (may be null when n_split == 1)
   int n_split;               // chosen by plan_attn_split
+  int tiles_per_split = 0;   // 32-slot tiles per split (set by launch_attention)
   int req_mode;              // 0: q_req array; 1: request = query / q_per_req (decode); 2: request 0 (prefill)
   int q_per_req = 1;
   // causal prefill (req_mode 2) from a fused path: compressed slots at or past
