@@ -48,6 +48,13 @@ int plan_attn_split(int Q, int H, int n_idx, int q_dt) {
   if (s > kMaxSplit) s = kMaxSplit;
   if (s < min_s) s = min_s;
   if (s < 1) s = 1;
+  // as few splits as give each block the same number of tiles: 20 tiles over 8 splits are 3 tiles
+  // a block and an 8th block with none, which would still select and write an empty partial that
+  // the merge reads (7 splits here)
+  if (n_tiles > 0) {
+    const int tps = (n_tiles + s - 1) / s;
+    s = (n_tiles + tps - 1) / tps;
+  }
   return s;
 }
 
