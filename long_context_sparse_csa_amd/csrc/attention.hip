@@ -354,7 +354,7 @@ __device__ __forceinline__ void select_rows(const TopkArgs& t, int q, uint8_t* l
     for (int i = tid; i < kHistBins; i += kAttnThreads) sh.bins[i] = 0u;
     if (tid == 0) sh.s_ncand = 0u;
 #pragma unroll
-    for (int j = 0; j < kSelPer; ++j) key[j] = order_key(v[j]);
+    for (int j = 0; j < kSelPer; ++j) key[j] = order_key_raw(v[j]);
     vm = prefix_mask<kSelPer>(c0, nv);
   }
   __syncthreads();
@@ -365,7 +365,7 @@ __device__ __forceinline__ void select_rows(const TopkArgs& t, int q, uint8_t* l
       rows_list[i] = i < nv ? row_of(i, pt_lds[i >> 6]) : -1;
     }
   } else {
-    block_threshold<kAttnThreads, kSelPer>(key, vm, (uint32_t)k, sh);
+    block_threshold<kAttnThreads, kSelPer, true>(key, vm, (uint32_t)k, sh);
     block_emit<kAttnThreads, kSelPer>(key, vm, sh.s_T, sh.s_need, (uint32_t)k, [&](int j) { return c0 + j; }, sh);
     const int32_t* sel = (const int32_t*)sh.cand_sel;
     for (int i = tid; i < k; i += kAttnThreads) {

@@ -71,6 +71,20 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// order_key without its NaN test: the same order and ties (-0.0 folds onto +0.0: its negation is
+// +0.0's key), four operations instead of seven.  Negative scores map to the negation of their bits
+// (order_key's complement plus one), so the keys of [-inf, +inf] span [0x00800000, 0xFF800000]
+// and NaNs land outside that range; canonical_key maps them to 0 as order_key does.  For code that
+// ranks its own keys only (the one-block selection).
+__device__ __forceinline__ uint32_t order_key_raw(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? (0u - u) : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t canonical_key(uint32_t k) {
+  return (k < 0x00800000u || k > 0xFF800000u) ? 0u : k;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {

@@ -127,6 +127,7 @@ struct SelShared {
   // indices
   uint32_t cand_sel[kCandMax > kSingleMaxK ? kCandMax : kSingleMaxK];
   uint32_t s_digit, s_before, s_ncand, s_T, s_need;
+  uint32_t s_all_eq;               // 1: every real entry equal to T is taken (the k are those >= T)
   uint32_t ext[2 * (NT / 64)];     // per-wave largest / smallest key
 };
 
@@ -148,8 +149,11 @@ __device__ __forceinline__ uint32_t prefix_mask(int64_t c0, int64_t n) {
   return m >= PER ? (PER >= 32 ? 0xFFFFFFFFu : ((1u << PER) - 1u)) : (m <= 0 ? 0u : ((1u << (uint32_t)m) - 1u));
 }
 
-template <int NT, int PER>
-__device__ void block_threshold(const uint32_t* key, uint32_t vm, uint32_t k, SelShared<NT>& sh) {
+// RAW: the keys come from order_key_raw; the key-prefix levels then first map NaNs to 0 in place
+// (the value-range level never runs on rows with a non-finite key, and its bins only need a
+// monotone function of the key).
+template <int NT, int PER, bool RAW = false>
+__device__ void block_threshold(uint32_t* key, uint32_t vm, uint32_t k, SelShared<NT>& sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const bool full = all_real<PER>(vm);
   // extremes of the real keys: per wave, then across waves after the barrier
@@ -195,8 +199,11 @@ __device__ void block_threshold(const uint32_t* key, uint32_t vm, uint32_t k, Se
     }
     const float vmin = key_value(kmin), vmax = key_value(kmax);
     const float scale = 4096.f / (vmax - vmin);
-    // every real key is finite (NaN maps below -inf, infinities outside +-FLT_MAX) and spread
-    const bool adaptive = kmin >= order_key(-3.40282347e+38f) && kmax <= order_key(3.40282347e+38f) &&
+    // every real key is finite (NaN keys lie below -inf's, raw ones also above +inf's; infinities
+    // outside +-FLT_MAX) and spread
+    const uint32_t kfin_lo = RAW ? order_key_raw(-3.40282347e+38f) : order_key(-3.40282347e+38f);
+    const uint32_t kfin_hi = RAW ? order_key_raw(3.40282347e+38f) : order_key(3.40282347e+38f);
+    const bool adaptive = kmin >= kfin_lo && kmax <= kfin_hi &&
                           kmax > kmin && scale > 0.f && scale < 3.0e38f;
     if (adaptive) {
       uint32_t bin[PER];
@@ -256,6 +263,9 @@ __device__ void block_threshold(const uint32_t* key, uint32_t vm, uint32_t k, Se
           if (lane < (int)n_cand && gt < need1 && ge >= need1) {   // every such lane holds the same key
             sh.s_T = mine;
             sh.s_need = need1 - gt;
+            // entries equal to T share its bin, so all of them are candidates: ge == need1 means
+            // the entries at or above T are exactly k
+            sh.s_all_eq = ge == need1 ? 1u : 0u;
           }
         }
         resolved = true;
@@ -267,6 +277,10 @@ __device__ void block_threshold(const uint32_t* key, uint32_t vm, uint32_t k, Se
     }
   }
   if (!resolved) {
+    if constexpr (RAW) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j) key[j] = canonical_key(key[j]);
+    }
     // level 1: top 12 key bits of every entry (all lanes active: one LDS atomic instruction covers 64)
 #pragma unroll
     for (int j = 0; j < PER; ++j)
@@ -334,6 +348,7 @@ __device__ void block_threshold(const uint32_t* key, uint32_t vm, uint32_t k, Se
         if (lane == 0) {
           sh.s_T = prefix;
           sh.s_need = need;
+          sh.s_all_eq = 0u;
         }
       }
     } else {
@@ -359,6 +374,7 @@ __device__ void block_threshold(const uint32_t* key, uint32_t vm, uint32_t k, Se
       if (tid == 0) {
         sh.s_T = prefix;
         sh.s_need = need;
+        sh.s_all_eq = 0u;
       }
     }
   }
@@ -367,38 +383,54 @@ __device__ void block_threshold(const uint32_t* key, uint32_t vm, uint32_t k, Se
 
 // The selected entries' indices in ascending order into sh.cand_sel[0, k): every real entry above
 // T and the first `need` equal to T (index order), placed by one block scan of the per-thread
-// (greater, equal) counts packed in one word (both totals stay below 2^16).  idx_of(j) is the index
+// (greater, equal) counts packed in one word (both totals stay below 2^16); when block_threshold
+// found that every entry equal to T is taken (sh.s_all_eq), of the counts of entries at or above T.  idx_of(j) is the index
 // of this thread's entry j; thread t's entries precede thread t+1's in index order.  Ends with a
 // barrier.
 template <int NT, int PER, class IdxOf>
 __device__ void block_emit(const uint32_t* key, uint32_t vm, uint32_t T, uint32_t need, uint32_t k, IdxOf idx_of,
                            SelShared<NT>& sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  uint32_t gm = 0, em = 0;       // bit j: entry j is above T / equal to T
+  uint32_t tm, pos;   // bit j: entry j is taken; the output position of this thread's first one
+  if (sh.s_all_eq) {  // block-uniform: the taken entries are those at or above T, one compare each
+    uint32_t ge = 0;
 #pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    gm |= key[j] > T ? (1u << j) : 0u;
-    em |= key[j] == T ? (1u << j) : 0u;
-  }
-  gm &= vm;
-  em &= vm;
-  const uint32_t n_gt = __popc(gm), n_eq = __popc(em);
-  const uint32_t mine = (n_gt << 16) | n_eq;
-  const uint32_t incl = wave_inclusive_scan(mine);
-  if (lane == 63) sh.scan[wave] = incl;
-  __syncthreads();
-  uint32_t pre = incl - mine;
+    for (int j = 0; j < PER; ++j) ge |= key[j] >= T ? (1u << j) : 0u;
+    tm = ge & vm;
+    const uint32_t mine = __popc(tm);
+    const uint32_t incl = wave_inclusive_scan(mine);
+    if (lane == 63) sh.scan[wave] = incl;
+    __syncthreads();
+    pos = incl - mine;
 #pragma unroll
-  for (int w = 0; w < NT / 64; ++w) pre += w < wave ? sh.scan[w] : 0u;
-  const uint32_t eq_before = pre & 0xFFFFu;
-  uint32_t pos = (pre >> 16) + (eq_before < need ? eq_before : need);
-  uint32_t take_eq = eq_before < need ? (need - eq_before < n_eq ? need - eq_before : n_eq) : 0u;
-  // the taken entries: all above T, and the lowest-index take_eq of those equal to T
-  uint32_t tm = gm;
-  for (uint32_t t = 0; t < take_eq; ++t) {
-    const uint32_t low = em & (0u - em);
-    tm |= low;
-    em ^= low;
+    for (int w = 0; w < NT / 64; ++w) pos += w < wave ? sh.scan[w] : 0u;
+  } else {
+    uint32_t gm = 0, em = 0;       // bit j: entry j is above T / equal to T
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      gm |= key[j] > T ? (1u << j) : 0u;
+      em |= key[j] == T ? (1u << j) : 0u;
+    }
+    gm &= vm;
+    em &= vm;
+    const uint32_t n_gt = __popc(gm), n_eq = __popc(em);
+    const uint32_t mine = (n_gt << 16) | n_eq;
+    const uint32_t incl = wave_inclusive_scan(mine);
+    if (lane == 63) sh.scan[wave] = incl;
+    __syncthreads();
+    uint32_t pre = incl - mine;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) pre += w < wave ? sh.scan[w] : 0u;
+    const uint32_t eq_before = pre & 0xFFFFu;
+    pos = (pre >> 16) + (eq_before < need ? eq_before : need);
+    const uint32_t take_eq = eq_before < need ? (need - eq_before < n_eq ? need - eq_before : n_eq) : 0u;
+    // the taken entries: all above T, and the lowest-index take_eq of those equal to T
+    tm = gm;
+    for (uint32_t t = 0; t < take_eq; ++t) {
+      const uint32_t low = em & (0u - em);
+      tm |= low;
+      em ^= low;
+    }
   }
   int32_t* sel = (int32_t*)sh.cand_sel;
   while (tm) {
