@@ -158,9 +158,22 @@ _TOPK_LENGTHS = {
 }
 
 
-def _topk_cases(rng, size_class):
+def _topk_cases(rng, size_class, k=None):
     lengths, m = _TOPK_LENGTHS[size_class]
     cases = [rng.standard_normal(n_vis).astype(np.float32) for n_vis in lengths]
+    if k is not None and k < m:
+        # a pair tied at the k-th largest score in a spread row (the value-range level resolves the
+        # threshold bin; only the lower-index one of the pair is taken), and a pair tied at the k-1-th
+        # and k-th (both taken: the selection is exactly the entries at or above the threshold)
+        near = rng.standard_normal(m).astype(np.float32)
+        order = np.argsort(-near.astype(np.float64), kind="stable")
+        at = near.copy()
+        at[order[k]] = at[order[k - 1]]
+        cases.append(at)
+        if k >= 2:
+            above = near.copy()
+            above[order[k - 1]] = above[order[k - 2]]
+            cases.append(above)
     ties = rng.integers(0, 7, size=m).astype(np.float32)                   # heavy ties at the threshold
     cases.append(ties)
     flat = np.full(m * 2 // 3, 1.5, np.float32)                             # every score equal
@@ -185,7 +198,7 @@ def test_topk_exact(dev, k, size_class):
     entries (the tied rows) and block-wide otherwise (the all-equal rows)."""
     run, _ = _run()
     rng = np.random.default_rng(5 + k)
-    cases = _topk_cases(rng, size_class)
+    cases = _topk_cases(rng, size_class, k)
     n = [len(c) for c in cases]
     max_n = max(n)
     ld = (max_n + 63) // 64 * 64
