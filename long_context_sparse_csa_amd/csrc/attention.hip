@@ -356,6 +356,7 @@ __device__ __forceinline__ void select_rows(const TopkArgs& t, int q, uint8_t* l
 #pragma unroll
     for (int j = 0; j < kSelPer; ++j) key[j] = order_key_raw(v[j]);
     vm = prefix_mask<kSelPer>(c0, nv);
+    publish_extremes<kAttnThreads, kSelPer>(key, vm, sh);   // read after the barrier below
   }
   __syncthreads();
   issue_more();
@@ -365,7 +366,7 @@ __device__ __forceinline__ void select_rows(const TopkArgs& t, int q, uint8_t* l
       rows_list[i] = i < nv ? row_of(i, pt_lds[i >> 6]) : -1;
     }
   } else {
-    block_threshold<kAttnThreads, kSelPer, true>(key, vm, (uint32_t)k, sh);
+    block_threshold<kAttnThreads, kSelPer, true, true>(key, vm, (uint32_t)k, sh);
     block_emit<kAttnThreads, kSelPer>(key, vm, sh.s_T, sh.s_need, (uint32_t)k, [&](int j) { return c0 + j; }, sh);
     const int32_t* sel = (const int32_t*)sh.cand_sel;
     for (int i = tid; i < k; i += kAttnThreads) {

@@ -149,39 +149,48 @@ __device__ __forceinline__ uint32_t prefix_mask(int64_t c0, int64_t n) {
   return m >= PER ? (PER >= 32 ? 0xFFFFFFFFu : ((1u << PER) - 1u)) : (m <= 0 ? 0u : ((1u << (uint32_t)m) - 1u));
 }
 
-// RAW: the keys come from order_key_raw; the key-prefix levels then first map NaNs to 0 in place
-// (the value-range level never runs on rows with a non-finite key, and its bins only need a
-// monotone function of the key).
-template <int NT, int PER, bool RAW = false>
-__device__ void block_threshold(uint32_t* key, uint32_t vm, uint32_t k, SelShared<NT>& sh) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const bool full = all_real<PER>(vm);
-  // extremes of the real keys: per wave, then across waves after the barrier
-  {
-    uint32_t kmx = 0u, kmn = 0xFFFFFFFFu;
-    if (full) {
+// The extremes of the block's real keys, per wave into sh.ext (largest, then smallest), visible after
+// the caller's next barrier.  A caller that publishes them with its own keys' barrier saves
+// block_threshold a pass and a barrier (EXT = true).
+template <int NT, int PER>
+__device__ __forceinline__ void publish_extremes(const uint32_t* key, uint32_t vm, SelShared<NT>& sh) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t kmx = 0u, kmn = 0xFFFFFFFFu;
+  if (all_real<PER>(vm)) {
 #pragma unroll
-      for (int j = 0; j < PER; ++j) {
+    for (int j = 0; j < PER; ++j) {
+      kmx = key[j] > kmx ? key[j] : kmx;
+      kmn = key[j] < kmn ? key[j] : kmn;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if ((vm >> j) & 1u) {
         kmx = key[j] > kmx ? key[j] : kmx;
         kmn = key[j] < kmn ? key[j] : kmn;
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < PER; ++j) {
-        if ((vm >> j) & 1u) {
-          kmx = key[j] > kmx ? key[j] : kmx;
-          kmn = key[j] < kmn ? key[j] : kmn;
-        }
-      }
-    }
-    kmx = wave_umax(kmx);
-    kmn = ~wave_umax(~kmn);   // min through the max of complements
-    if (lane == 0) {
-      sh.ext[wave] = kmx;
-      sh.ext[NT / 64 + wave] = kmn;
     }
   }
-  __syncthreads();
+  kmx = wave_umax(kmx);
+  kmn = ~wave_umax(~kmn);   // min through the max of complements
+  if (lane == 0) {
+    sh.ext[wave] = kmx;
+    sh.ext[NT / 64 + wave] = kmn;
+  }
+}
+
+// RAW: the keys come from order_key_raw; the key-prefix levels then first map NaNs to 0 in place
+// (the value-range level never runs on rows with a non-finite key, and its bins only need a
+// monotone function of the key).  EXT: the caller published the extremes (publish_extremes) before
+// the barrier that precedes this call.
+template <int NT, int PER, bool RAW = false, bool EXT = false>
+__device__ void block_threshold(uint32_t* key, uint32_t vm, uint32_t k, SelShared<NT>& sh) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool full = all_real<PER>(vm);
+  if constexpr (!EXT) {
+    publish_extremes<NT, PER>(key, vm, sh);
+    __syncthreads();
+  }
   // Level 1 on the value range: 4096 equal-width bins between the smallest and largest finite
   // score.  Scores crowd a few of the fixed 12-bit key-prefix bins (the exponent and three
   // mantissa bits), so LDS atomics collide and the threshold bin holds hundreds of entries; on the

@@ -461,6 +461,7 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) key[j] = order_key_raw(v[j]);
     vm = prefix_mask<PER>(c0, nv);
+    publish_extremes<NT, PER>(key, vm, sh);   // read after the barrier below
   } else if (tid < n_pt) {
     pt_lds[tid] = pg_mine;
   }
@@ -472,7 +473,7 @@ __global__ __launch_bounds__(NT) void topk_single_kernel(TopkArgs a) {
     }
     return;
   }
-  block_threshold<NT, PER, true>(key, vm, (uint32_t)k, sh);
+  block_threshold<NT, PER, true, true>(key, vm, (uint32_t)k, sh);
   block_emit<NT, PER>(key, vm, sh.s_T, sh.s_need, (uint32_t)k, [&](int j) { return c0 + j; }, sh);
   const int32_t* sel = (const int32_t*)sh.cand_sel;
   for (int i = tid; i < k; i += NT) {
